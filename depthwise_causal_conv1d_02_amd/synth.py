@@ -1,0 +1,149 @@
+"""Seeded synthetic inputs for the depthwise causal conv1d.
+
+This module draws random numbers and nothing else: it holds none of the
+method's arithmetic.  The tests (for both the GPU path and the CPU oracle)
+and the benchmark use it so that both sides see the same inputs.
+
+Recipe (shapes and distributions of the Mamba-style mixer workloads):
+
+* one ``torch.Generator`` on the CPU, ``manual_seed(seed)``; tensors drawn in
+  the order they are listed; each drawn in float32 and rounded to bfloat16
+  (round to nearest even) unless stated otherwise;
+* N(0,1): ``randn``;  U(-0.5,0.5): ``rand - 0.5``;  bias: ``randn * 0.1``
+  (a standard deviation of 0.1);
+* "channel-last" inputs are drawn as ``[B,T,D]`` storage and exposed as the
+  ``[B,D,T]`` view ``storage.transpose(1, 2)``, which is how a model that owns
+  ``[B,T,D]`` storage hands them over (cuDNN FE "Causal Conv1d", the paragraph
+  on transpose views).
+"""
+import torch
+
+BF16 = torch.bfloat16
+
+
+def _normal(g, shape, scale=1.0):
+    t = torch.randn(*shape, generator=g, dtype=torch.float32)
+    if scale != 1.0:
+        t = t * scale
+    return t.to(BF16)
+
+
+def _uniform_half(g, shape, dtype=BF16):
+    return (torch.rand(*shape, generator=g, dtype=torch.float32) - 0.5).to(dtype)
+
+
+def activation_tensor(g, B, D, T, layout):
+    """x or dy: [B,D,T] logical view; layout 'cl' draws [B,T,D] storage."""
+    if layout == "cl":
+        return _normal(g, (B, T, D)).transpose(1, 2)
+    if layout == "tc":
+        return _normal(g, (B, D, T))
+    raise ValueError(layout)
+
+
+def weight_tensor(g, D, W=4, dtype=BF16):
+    return _uniform_half(g, (D, W), dtype)
+
+
+def bias_tensor(g, D):
+    return _normal(g, (D,), 0.1)
+
+
+def state_tensor(g, R, D, W=4):
+    return _normal(g, (R, D, W - 1))
+
+
+def packed_lengths(n_seq=16, lo=64, hi=4096, target=None, tol=0.01):
+    """Sequence lengths ~U[lo, hi] from a generator of their own.
+
+    The seed is the smallest one whose total lies within ``tol`` of the
+    expected total ``n_seq * (lo + hi) / 2`` (33,280 for 16 x U[64,4096]).
+    Returns (seed, lengths list).
+    """
+    if target is None:
+        target = n_seq * (lo + hi) / 2.0
+    seed = 0
+    while True:
+        g = torch.Generator().manual_seed(seed)
+        lens = torch.randint(lo, hi + 1, (n_seq,), generator=g)
+        if abs(int(lens.sum()) - target) <= tol * target:
+            return seed, [int(v) for v in lens]
+        seed += 1
+
+
+def cu_from_lengths(lengths):
+    cu = [0]
+    for n in lengths:
+        cu.append(cu[-1] + int(n))
+    return torch.tensor(cu, dtype=torch.int32)
+
+
+def random_inputs(seed, B, D, T, *, layout="cl", W=4, bias=True, init=False, dy=True,
+                  dfinal=False, weight_dtype=BF16, cu_seqlens=None):
+    """General seeded inputs for parity tests (CPU tensors).
+
+    Draw order: x, weight, bias, initial_states, dy, dfinal_states.
+    With ``cu_seqlens`` (B must be 1) the states have N = len(cu)-1 rows.
+    """
+    g = torch.Generator().manual_seed(seed)
+    R = B if cu_seqlens is None else int(cu_seqlens.numel()) - 1
+    out = {"x": activation_tensor(g, B, D, T, layout)}
+    out["weight"] = weight_tensor(g, D, W, weight_dtype)
+    out["bias"] = bias_tensor(g, D) if bias else None
+    out["initial_states"] = state_tensor(g, R, D, W) if init else None
+    out["dy"] = activation_tensor(g, B, D, T, layout) if dy else None
+    out["dfinal_states"] = state_tensor(g, R, D, W) if dfinal else None
+    out["cu_seqlens"] = cu_seqlens
+    return out
+
+
+# ---- the five named workloads ---------------------------------------------
+
+WORKLOADS = {
+    1: "tiny dense fwd: B=1 D=64 T=128, [B,D,T] contiguous, bf16 weight+bias, SiLU, "
+       "no initial state, final_states returned",
+    2: "dense fwd+bwd with state: B=4 D=4096 T=2048, channel-last, bf16 weight+bias, "
+       "initial_states, SiLU, final_states returned",
+    3: "packed varlen fwd+bwd: N=16 U[64,4096] lengths (T=33280), D=5120, channel-last, "
+       "fp32 weight, no bias, initial_states, SiLU",
+    4: "decode update: B=256 D=8192, 64 single-token steps, bf16 weight+bias, SiLU",
+    5: "large dense fwd+bwd: B=8 D=8192 T=8192, channel-last, bf16 weight, no bias, SiLU, "
+       "deterministic dweight",
+}
+
+
+def workload(idx):
+    """Inputs of workload ``idx`` (1..5) as CPU tensors, seed = idx."""
+    g = torch.Generator().manual_seed(idx)
+    if idx == 1:
+        B, D, T = 1, 64, 128
+        return dict(x=activation_tensor(g, B, D, T, "tc"), weight=weight_tensor(g, D),
+                    bias=bias_tensor(g, D), initial_states=None, dy=None, cu_seqlens=None,
+                    activation="silu", return_final_states=True, deterministic=False)
+    if idx == 2:
+        B, D, T = 4, 4096, 2048
+        return dict(x=activation_tensor(g, B, D, T, "cl"), weight=weight_tensor(g, D),
+                    bias=bias_tensor(g, D), initial_states=state_tensor(g, B, D),
+                    dy=activation_tensor(g, B, D, T, "cl"), cu_seqlens=None,
+                    activation="silu", return_final_states=True, deterministic=False)
+    if idx == 3:
+        _, lens = packed_lengths()
+        cu = cu_from_lengths(lens)
+        D, T = 5120, int(cu[-1])
+        N = len(lens)
+        return dict(x=activation_tensor(g, 1, D, T, "cl"),
+                    weight=weight_tensor(g, D, dtype=torch.float32), bias=None,
+                    initial_states=state_tensor(g, N, D), dy=activation_tensor(g, 1, D, T, "cl"),
+                    cu_seqlens=cu, activation="silu", return_final_states=True,
+                    deterministic=False)
+    if idx == 4:
+        B, D, steps = 256, 8192, 64
+        return dict(conv_state=_normal(g, (B, D, 3)), x_steps=_normal(g, (steps, B, D)),
+                    weight=weight_tensor(g, D), bias=bias_tensor(g, D), activation="silu")
+    if idx == 5:
+        B, D, T = 8, 8192, 8192
+        return dict(x=activation_tensor(g, B, D, T, "cl"), weight=weight_tensor(g, D),
+                    bias=None, initial_states=None, dy=activation_tensor(g, B, D, T, "cl"),
+                    cu_seqlens=None, activation="silu", return_final_states=False,
+                    deterministic=True)
+    raise ValueError("workload index must be 1..5")
