@@ -1,0 +1,470 @@
+// ccv_api.cpp — the C-ABI of libccv: host-side argument checks, the alias
+// and determinism rules, launch geometry, and the launches.  Nothing here
+// reads device memory or synchronises.
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "ccv.h"
+#include "ccv_internal.h"
+
+#ifndef CCV_TARGET_WAVES
+#define CCV_TARGET_WAVES 16384  // waves per channel-lane launch the chunk length aims for
+#endif
+#ifndef CCV_MIN_CHUNK
+#define CCV_MIN_CHUNK 16        // time steps per wave, at least
+#endif
+#ifndef CCV_MAX_CHUNK
+#define CCV_MAX_CHUNK 1024
+#endif
+
+namespace {
+
+using ccv::kWidth;
+
+bool present(const ccv_tensor *t) { return t != nullptr && t->data != nullptr; }
+
+int64_t elem_bytes(int32_t dt) {
+    switch (dt) {
+    case CCV_DTYPE_BF16: return 2;
+    case CCV_DTYPE_F32: return 4;
+    case CCV_DTYPE_I32: return 4;
+    default: return 0;
+    }
+}
+
+// Descriptor sanity: rank, dtype, non-negative sizes and strides.
+bool well_formed(const ccv_tensor *t, int ndim) {
+    if (t->ndim != ndim || elem_bytes(t->dtype) == 0) return false;
+    for (int i = 0; i < ndim; ++i)
+        if (t->shape[i] < 0 || t->stride[i] < 0) return false;
+    return true;
+}
+
+bool shape_is(const ccv_tensor *t, int64_t a, int64_t b = -1, int64_t c = -1) {
+    const int64_t want[3] = {a, b, c};
+    for (int i = 0; i < t->ndim; ++i)
+        if (t->shape[i] != want[i]) return false;
+    return true;
+}
+
+// Byte span [lo, hi) covered by a tensor (empty when any extent is 0).
+struct Span {
+    uintptr_t lo = 0, hi = 0;
+};
+
+Span span_of(const ccv_tensor *t) {
+    Span s;
+    if (!present(t)) return s;
+    int64_t last = 0;
+    for (int i = 0; i < t->ndim; ++i) {
+        if (t->shape[i] == 0) return s;
+        last += (t->shape[i] - 1) * t->stride[i];
+    }
+    const int64_t eb = elem_bytes(t->dtype);
+    s.lo = reinterpret_cast<uintptr_t>(t->data);
+    s.hi = s.lo + static_cast<uintptr_t>((last + 1) * eb);
+    return s;
+}
+
+Span span_raw(const void *p, size_t bytes) {
+    Span s;
+    if (p && bytes) {
+        s.lo = reinterpret_cast<uintptr_t>(p);
+        s.hi = s.lo + bytes;
+    }
+    return s;
+}
+
+bool overlaps(const Span &a, const Span &b) {
+    return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+// No two index tuples of an output may name the same element.  Dimensions
+// sorted by stride must each step over everything the smaller ones span.
+bool injective(const ccv_tensor *t) {
+    int64_t st[3], sh[3];
+    int n = 0;
+    for (int i = 0; i < t->ndim; ++i)
+        if (t->shape[i] > 1) { st[n] = t->stride[i]; sh[n] = t->shape[i]; ++n; }
+    for (int i = 0; i < n; ++i)
+        for (int j = i + 1; j < n; ++j)
+            if (st[j] < st[i]) { std::swap(st[i], st[j]); std::swap(sh[i], sh[j]); }
+    int64_t reach = 0;  // largest offset reachable with the smaller dims
+    for (int i = 0; i < n; ++i) {
+        if (st[i] <= reach) return false;
+        reach += (sh[i] - 1) * st[i];
+    }
+    return true;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// A [B,D,T] BF16 tensor the VEC = 8 lanes can read with 16-byte vectors.
+bool vec8_ok(const ccv_tensor *t) {
+    if (!present(t)) return true;
+    const int64_t B = t->shape[0], D = t->shape[1], T = t->shape[2];
+    return t->stride[1] == 1 && D % 8 == 0 && aligned16(t->data) &&
+           (B == 1 || t->stride[0] % 8 == 0) && (T == 1 || t->stride[2] % 8 == 0);
+}
+
+bool filter_vec(const ccv_tensor *w) {
+    return w->stride[1] == 1 && w->stride[0] == kWidth && aligned16(w->data);
+}
+
+ccv::Strided3 s3(const ccv_tensor *t) {
+    ccv::Strided3 s{nullptr, 0, 0, 0};
+    if (present(t)) {
+        s.ptr = t->data;
+        s.s0 = t->stride[0];
+        s.s1 = t->stride[1];
+        s.s2 = t->stride[2];
+    }
+    return s;
+}
+
+// Shared checks of the full-sequence calls (forward and backward inputs).
+struct Problem {
+    int64_t B = 0, D = 0, T = 0, N = 0, R = 0;
+    bool packed = false;
+};
+
+int check_inputs(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bias,
+                 const ccv_tensor *cu, const ccv_tensor *seq_idx, const ccv_tensor *init,
+                 int activation, const uint32_t *err_flag, Problem &p) {
+    if (!present(x) || !well_formed(x, 3) || x->dtype != CCV_DTYPE_BF16) return CCV_ERR_INVALID_ARG;
+    p.B = x->shape[0];
+    p.D = x->shape[1];
+    p.T = x->shape[2];
+    if (p.B < 1 || p.D < 1 || p.T < 1) return CCV_ERR_INVALID_ARG;
+    if (!present(weight) || !well_formed(weight, 2) || weight->shape[0] != p.D ||
+        weight->shape[1] < 1 ||
+        (weight->dtype != CCV_DTYPE_BF16 && weight->dtype != CCV_DTYPE_F32))
+        return CCV_ERR_INVALID_ARG;
+    if (present(bias) && (!well_formed(bias, 1) || !shape_is(bias, p.D) ||
+                          bias->dtype != CCV_DTYPE_BF16))
+        return CCV_ERR_INVALID_ARG;
+    // seq_idx and cu_seqlens are mutually exclusive; seq_idx alone is reserved.
+    if (present(seq_idx) && present(cu)) return CCV_ERR_INVALID_ARG;
+    if (present(cu)) {
+        if (!well_formed(cu, 1) || cu->dtype != CCV_DTYPE_I32 || cu->stride[0] != 1 ||
+            cu->shape[0] < 2 || p.B != 1 || err_flag == nullptr || cu->shape[0] - 1 > INT32_MAX)
+            return CCV_ERR_INVALID_ARG;
+        p.packed = true;
+        p.N = cu->shape[0] - 1;
+    }
+    p.R = p.packed ? p.N : p.B;
+    if (present(init) && (!well_formed(init, 3) || init->dtype != CCV_DTYPE_BF16 ||
+                          !shape_is(init, p.R, p.D, weight->shape[1] - 1)))
+        return CCV_ERR_INVALID_ARG;
+    // Declines: the reserved keyword, the width, FP32 filter with a bias,
+    // the activation set.
+    if (present(seq_idx)) return CCV_ERR_UNSUPPORTED;
+    if (weight->shape[1] != kWidth) return CCV_ERR_UNSUPPORTED;
+    if (weight->dtype == CCV_DTYPE_F32 && present(bias)) return CCV_ERR_UNSUPPORTED;
+    if (activation != CCV_ACT_NONE && activation != CCV_ACT_SILU) return CCV_ERR_UNSUPPORTED;
+    return CCV_OK;
+}
+
+int check_state_out(const ccv_tensor *t, const Problem &p) {
+    if (!present(t)) return CCV_OK;
+    if (!well_formed(t, 3) || t->dtype != CCV_DTYPE_BF16 || !shape_is(t, p.R, p.D, kWidth - 1) ||
+        !injective(t))
+        return CCV_ERR_INVALID_ARG;
+    return CCV_OK;
+}
+
+int check_act_tensor(const ccv_tensor *t, const Problem &p, bool output) {
+    if (!present(t) || !well_formed(t, 3) || t->dtype != CCV_DTYPE_BF16 ||
+        !shape_is(t, p.B, p.D, p.T))
+        return CCV_ERR_INVALID_ARG;
+    if (output && !injective(t)) return CCV_ERR_INVALID_ARG;
+    return CCV_OK;
+}
+
+// Every output span against every input span and every other output span.
+bool any_alias(const Span *outs, int n_out, const Span *ins, int n_in) {
+    for (int i = 0; i < n_out; ++i) {
+        for (int j = 0; j < n_in; ++j)
+            if (overlaps(outs[i], ins[j])) return true;
+        for (int j = i + 1; j < n_out; ++j)
+            if (overlaps(outs[i], outs[j])) return true;
+    }
+    return false;
+}
+
+// Time steps per wave: enough waves to fill 256 CUs several times over,
+// but never fewer than CCV_MIN_CHUNK steps per wave.
+struct Geometry {
+    int64_t L, n_chunk, n_tblk, n_group, n_block;
+};
+
+Geometry geometry(const Problem &p, int vec) {
+    Geometry g;
+    g.n_group = (p.D + ccv::kWaveSize * vec - 1) / (ccv::kWaveSize * vec);
+    const int64_t rows = p.packed ? 1 : p.B;
+    const int64_t work = rows * g.n_group * p.T;
+    int64_t L = (work + CCV_TARGET_WAVES - 1) / CCV_TARGET_WAVES;
+    L = (L + 7) / 8 * 8;
+    L = std::max<int64_t>(CCV_MIN_CHUNK, std::min<int64_t>(CCV_MAX_CHUNK, L));
+    g.L = L;
+    g.n_chunk = (p.T + L - 1) / L;
+    g.n_tblk = (g.n_chunk + ccv::kWavesPerBlock - 1) / ccv::kWavesPerBlock;
+    g.n_block = rows * g.n_group * g.n_tblk;
+    return g;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? CCV_OK : CCV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int ccv_abi_version(void) { return CCV_ABI_VERSION; }
+
+const char *ccv_status_string(int status) {
+    switch (status) {
+    case CCV_OK: return "CCV_OK";
+    case CCV_WARN_NONDETERMINISTIC: return "CCV_WARN_NONDETERMINISTIC";
+    case CCV_ERR_INVALID_ARG: return "CCV_ERR_INVALID_ARG";
+    case CCV_ERR_ALIAS: return "CCV_ERR_ALIAS";
+    case CCV_ERR_UNSUPPORTED: return "CCV_ERR_UNSUPPORTED";
+    case CCV_ERR_NONDETERMINISTIC: return "CCV_ERR_NONDETERMINISTIC";
+    case CCV_ERR_HIP: return "CCV_ERR_HIP";
+    default: return "CCV_UNKNOWN_STATUS";
+    }
+}
+
+int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bias,
+            const ccv_tensor *cu_seqlens, const ccv_tensor *seq_idx,
+            const ccv_tensor *initial_states, const ccv_tensor *y,
+            const ccv_tensor *final_states, int activation, uint32_t *err_flag,
+            hipStream_t stream) {
+    Problem p;
+    int rc = check_inputs(x, weight, bias, cu_seqlens, seq_idx, initial_states, activation,
+                          err_flag, p);
+    if (rc != CCV_OK) return rc;
+    if ((rc = check_act_tensor(y, p, true)) != CCV_OK) return rc;
+    if ((rc = check_state_out(final_states, p)) != CCV_OK) return rc;
+
+    const Span outs[] = {span_of(y), span_of(final_states),
+                         p.packed ? span_raw(err_flag, 4) : Span{}};
+    const Span ins[] = {span_of(x), span_of(weight), span_of(bias), span_of(cu_seqlens),
+                        span_of(initial_states)};
+    if (any_alias(outs, 3, ins, 5)) return CCV_ERR_ALIAS;
+
+    const int vec = (vec8_ok(x) && vec8_ok(y)) ? 8 : 1;
+    const Geometry g = geometry(p, vec);
+    ccv::FwdArgs a;
+    memset(&a, 0, sizeof(a));
+    a.x = s3(x);
+    a.y = s3(y);
+    a.init = s3(initial_states);
+    a.fin = s3(final_states);
+    a.w = weight->data;
+    a.w_sd = weight->stride[0];
+    a.w_sk = weight->stride[1];
+    a.w_f32 = weight->dtype == CCV_DTYPE_F32;
+    a.w_vec = filter_vec(weight);
+    a.bias = present(bias) ? bias->data : nullptr;
+    a.b_s = present(bias) ? bias->stride[0] : 0;
+    a.cu = p.packed ? static_cast<const int32_t *>(cu_seqlens->data) : nullptr;
+    a.n_seq = p.N;
+    a.err = p.packed ? err_flag : nullptr;
+    a.B = p.B;
+    a.D = p.D;
+    a.T = p.T;
+    a.L = g.L;
+    a.n_chunk = g.n_chunk;
+    a.n_tblk = g.n_tblk;
+    a.n_group = g.n_group;
+    a.n_block = g.n_block;
+    a.cu_in_lds = p.packed && p.N + 1 <= ccv::kLdsCuMax;
+    if (p.packed && !a.cu_in_lds) {
+        rc = hip_status(ccv::launch_validate(a.cu, p.N, p.T, err_flag, 0, stream));
+        if (rc != CCV_OK) return rc;
+    }
+    return hip_status(ccv::launch_fwd(a, vec, activation == CCV_ACT_SILU, p.packed, stream));
+}
+
+int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bias,
+            const ccv_tensor *cu_seqlens, const ccv_tensor *seq_idx,
+            const ccv_tensor *initial_states, const ccv_tensor *dy,
+            const ccv_tensor *dfinal_states, const ccv_tensor *dx,
+            const ccv_tensor *dweight, const ccv_tensor *dbias,
+            const ccv_tensor *dinitial_states, int activation, int deterministic,
+            int warn_only, void *workspace, size_t *workspace_bytes,
+            uint32_t *err_flag, hipStream_t stream) {
+    Problem p;
+    int rc = check_inputs(x, weight, bias, cu_seqlens, seq_idx, initial_states, activation,
+                          err_flag, p);
+    if (rc != CCV_OK) return rc;
+    if ((rc = check_act_tensor(dy, p, false)) != CCV_OK) return rc;
+    if ((rc = check_act_tensor(dx, p, true)) != CCV_OK) return rc;
+    if (present(dfinal_states) &&
+        (!well_formed(dfinal_states, 3) || dfinal_states->dtype != CCV_DTYPE_BF16 ||
+         !shape_is(dfinal_states, p.R, p.D, kWidth - 1)))
+        return CCV_ERR_INVALID_ARG;
+    if ((rc = check_state_out(dinitial_states, p)) != CCV_OK) return rc;
+    if (present(dinitial_states) && !present(initial_states)) return CCV_ERR_INVALID_ARG;
+    // dweight [D,W] and dbias [D]: FP32, contiguous.
+    if (!present(dweight) || !well_formed(dweight, 2) || dweight->dtype != CCV_DTYPE_F32 ||
+        !shape_is(dweight, p.D, kWidth) || dweight->stride[0] != kWidth || dweight->stride[1] != 1)
+        return CCV_ERR_INVALID_ARG;
+    if (present(bias) != present(dbias)) return CCV_ERR_INVALID_ARG;
+    if (present(dbias) && (!well_formed(dbias, 1) || dbias->dtype != CCV_DTYPE_F32 ||
+                           !shape_is(dbias, p.D) || dbias->stride[0] != 1))
+        return CCV_ERR_INVALID_ARG;
+
+    // Determinism policy (cuDNN FE "Causal Conv1d", the determinism paragraph).
+    int status = CCV_OK;
+    bool use_partials = false;
+    if (deterministic) {
+        if (present(bias)) {
+            if (!warn_only) return CCV_ERR_NONDETERMINISTIC;
+            status = CCV_WARN_NONDETERMINISTIC;
+        } else {
+            use_partials = true;
+        }
+    }
+    const int vec = (vec8_ok(x) && vec8_ok(dy) && vec8_ok(dx)) ? 8 : 1;
+    const Geometry g = geometry(p, vec);
+    const int64_t n_part = (p.packed ? 1 : p.B) * g.n_tblk;
+    const size_t need = use_partials
+                            ? static_cast<size_t>(n_part) * static_cast<size_t>(p.D) * kWidth * 4
+                            : 0;
+    if (workspace == nullptr && workspace_bytes != nullptr) {  // size query
+        *workspace_bytes = need;
+        return CCV_OK;
+    }
+    if (need > 0) {
+        if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+            return CCV_ERR_INVALID_ARG;
+        if (workspace_bytes != nullptr && *workspace_bytes < need) return CCV_ERR_INVALID_ARG;
+    }
+
+    const Span outs[] = {span_of(dx), span_of(dweight), span_of(dbias), span_of(dinitial_states),
+                         p.packed ? span_raw(err_flag, 4) : Span{}, span_raw(workspace, need)};
+    const Span ins[] = {span_of(x), span_of(weight), span_of(bias), span_of(cu_seqlens),
+                        span_of(initial_states), span_of(dy), span_of(dfinal_states)};
+    if (any_alias(outs, 6, ins, 7)) return CCV_ERR_ALIAS;
+
+    ccv::BwdArgs a;
+    memset(&a, 0, sizeof(a));
+    a.x = s3(x);
+    a.dy = s3(dy);
+    a.dx = s3(dx);
+    a.init = s3(initial_states);
+    a.dfin = s3(dfinal_states);
+    a.dinit = s3(dinitial_states);
+    a.w = weight->data;
+    a.w_sd = weight->stride[0];
+    a.w_sk = weight->stride[1];
+    a.w_f32 = weight->dtype == CCV_DTYPE_F32;
+    a.w_vec = filter_vec(weight);
+    a.bias = present(bias) ? bias->data : nullptr;
+    a.b_s = present(bias) ? bias->stride[0] : 0;
+    a.dw = static_cast<float *>(dweight->data);
+    a.db = present(dbias) ? static_cast<float *>(dbias->data) : nullptr;
+    a.partial = use_partials ? static_cast<float *>(workspace) : nullptr;
+    a.cu = p.packed ? static_cast<const int32_t *>(cu_seqlens->data) : nullptr;
+    a.n_seq = p.N;
+    a.err = p.packed ? err_flag : nullptr;
+    a.B = p.B;
+    a.D = p.D;
+    a.T = p.T;
+    a.L = g.L;
+    a.n_chunk = g.n_chunk;
+    a.n_tblk = g.n_tblk;
+    a.n_group = g.n_group;
+    a.n_block = g.n_block;
+    a.cu_in_lds = p.packed && p.N + 1 <= ccv::kLdsCuMax;
+
+    if (!use_partials) {
+        if ((rc = hip_status(ccv::launch_zero(a.dw, p.D * kWidth, stream))) != CCV_OK) return rc;
+        if (a.db && (rc = hip_status(ccv::launch_zero(a.db, p.D, stream))) != CCV_OK) return rc;
+    }
+    if (p.packed && !a.cu_in_lds) {
+        rc = hip_status(ccv::launch_validate(a.cu, p.N, p.T, err_flag, 0, stream));
+        if (rc != CCV_OK) return rc;
+    }
+    rc = hip_status(ccv::launch_bwd(a, vec, activation == CCV_ACT_SILU, p.packed, stream));
+    if (rc != CCV_OK) return rc;
+    if (use_partials) {
+        rc = hip_status(ccv::launch_dw_reduce(a.partial, n_part, p.D * kWidth, a.dw, stream));
+        if (rc != CCV_OK) return rc;
+    }
+    return status;
+}
+
+int ccv_update(const ccv_tensor *x, const ccv_tensor *conv_state, const ccv_tensor *weight,
+               const ccv_tensor *bias, const ccv_tensor *y, int activation,
+               hipStream_t stream) {
+    if (!present(x) || !well_formed(x, 2) || x->dtype != CCV_DTYPE_BF16) return CCV_ERR_INVALID_ARG;
+    const int64_t B = x->shape[0], D = x->shape[1];
+    if (B < 1 || D < 1) return CCV_ERR_INVALID_ARG;
+    if (!present(weight) || !well_formed(weight, 2) || weight->shape[0] != D ||
+        weight->shape[1] < 1 ||
+        (weight->dtype != CCV_DTYPE_BF16 && weight->dtype != CCV_DTYPE_F32))
+        return CCV_ERR_INVALID_ARG;
+    if (present(bias) && (!well_formed(bias, 1) || !shape_is(bias, D) ||
+                          bias->dtype != CCV_DTYPE_BF16))
+        return CCV_ERR_INVALID_ARG;
+    if (!present(conv_state) || !well_formed(conv_state, 3) ||
+        conv_state->dtype != CCV_DTYPE_BF16 ||
+        !shape_is(conv_state, B, D, weight->shape[1] - 1) || !injective(conv_state))
+        return CCV_ERR_INVALID_ARG;
+    if (!present(y) || !well_formed(y, 2) || y->dtype != CCV_DTYPE_BF16 || !shape_is(y, B, D) ||
+        !injective(y))
+        return CCV_ERR_INVALID_ARG;
+    if (weight->shape[1] != kWidth) return CCV_ERR_UNSUPPORTED;
+    if (weight->dtype == CCV_DTYPE_F32 && present(bias)) return CCV_ERR_UNSUPPORTED;
+    if (activation != CCV_ACT_NONE && activation != CCV_ACT_SILU) return CCV_ERR_UNSUPPORTED;
+    // conv_state is in/out by design; y and the state must not overlap any
+    // other argument.
+    const Span outs[] = {span_of(y), span_of(conv_state)};
+    const Span ins[] = {span_of(x), span_of(weight), span_of(bias)};
+    if (any_alias(outs, 2, ins, 3)) return CCV_ERR_ALIAS;
+
+    const bool vec = D % 8 == 0 && x->stride[1] == 1 && y->stride[1] == 1 &&
+                     conv_state->stride[2] == 1 && conv_state->stride[1] == kWidth - 1 &&
+                     aligned16(x->data) && aligned16(y->data) && aligned16(conv_state->data) &&
+                     (B == 1 || (x->stride[0] % 8 == 0 && y->stride[0] % 8 == 0 &&
+                                 conv_state->stride[0] % 8 == 0));
+    ccv::UpdArgs a;
+    memset(&a, 0, sizeof(a));
+    a.x = x->data;
+    a.x_sb = x->stride[0];
+    a.x_sd = x->stride[1];
+    a.state = conv_state->data;
+    a.s_sb = conv_state->stride[0];
+    a.s_sd = conv_state->stride[1];
+    a.s_sj = conv_state->stride[2];
+    a.w = weight->data;
+    a.w_sd = weight->stride[0];
+    a.w_sk = weight->stride[1];
+    a.w_f32 = weight->dtype == CCV_DTYPE_F32;
+    a.w_vec = filter_vec(weight);
+    a.bias = present(bias) ? bias->data : nullptr;
+    a.b_s = present(bias) ? bias->stride[0] : 0;
+    a.y = y->data;
+    a.y_sb = y->stride[0];
+    a.y_sd = y->stride[1];
+    a.B = B;
+    a.D = D;
+    a.n_lane_per_row = vec ? D / 8 : D;
+    return hip_status(ccv::launch_update(a, vec ? 8 : 1, activation == CCV_ACT_SILU, stream));
+}
+
+int ccv_validate_cu_seqlens(const int32_t *cu_seqlens, int64_t n_seqs, int64_t total_tokens,
+                            uint32_t *flags, hipStream_t stream) {
+    if (cu_seqlens == nullptr || flags == nullptr || n_seqs < 1 || total_tokens < 1 ||
+        n_seqs > INT32_MAX)
+        return CCV_ERR_INVALID_ARG;
+    if (overlaps(span_raw(cu_seqlens, static_cast<size_t>(n_seqs + 1) * 4), span_raw(flags, 4)))
+        return CCV_ERR_ALIAS;
+    return hip_status(ccv::launch_validate(cu_seqlens, n_seqs, total_tokens, flags, 1, stream));
+}
+
+}  // extern "C"

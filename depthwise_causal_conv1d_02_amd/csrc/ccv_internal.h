@@ -1,0 +1,86 @@
+// ccv_internal.h — argument blocks shared by the host layer (ccv_api.cpp)
+// and the gfx950 kernels (ccv_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace ccv {
+
+constexpr int kWidth = 4;          // the filter width the kernels are built for
+constexpr int kWaveSize = 64;      // CDNA wavefront
+constexpr int kWavesPerBlock = 4;  // channel-lane kernels: 4 waves share a channel group
+constexpr int kLdsCuMax = 4096;    // cu_seqlens entries staged in LDS (16 KB)
+
+// One BF16 activation-like tensor [B,D,T] (or [R,D,W-1] for states) in
+// element strides.  ptr == nullptr means absent.
+struct Strided3 {
+    const void *ptr;
+    int64_t s0, s1, s2;
+};
+
+struct FwdArgs {
+    Strided3 x, y, init, fin;  // y/fin are written through const_cast in the kernels
+    const void *w;             // [D,W], BF16 or FP32
+    int64_t w_sd, w_sk;
+    int w_f32, w_vec;          // w_vec: contiguous [D,W], 16-byte aligned
+    const void *bias;          // [D] BF16 or nullptr
+    int64_t b_s;
+    const int32_t *cu;         // packed offsets or nullptr
+    int64_t n_seq;             // N (packed) ; unused dense
+    uint32_t *err;             // flag word (packed) or nullptr
+    int64_t B, D, T;           // T = tokens per batch row (dense) or the packed total
+    int64_t L;                 // time steps per wave
+    int64_t n_chunk;           // ceil(T / L)
+    int64_t n_tblk;            // ceil(n_chunk / waves per block)
+    int64_t n_group;           // channel groups of 64*VEC channels
+    int64_t n_block;           // grid size
+    int cu_in_lds;             // stage + validate cu_seqlens in LDS
+};
+
+struct BwdArgs {
+    Strided3 x, dy, dx, init, dfin, dinit;
+    const void *w;
+    int64_t w_sd, w_sk;
+    int w_f32, w_vec;
+    const void *bias;
+    int64_t b_s;
+    float *dw;                 // [D,W] FP32 (atomic path) — contiguous
+    float *db;                 // [D] FP32 or nullptr
+    float *partial;            // deterministic path: [P][D][W] FP32, else nullptr
+    const int32_t *cu;
+    int64_t n_seq;
+    uint32_t *err;
+    int64_t B, D, T, L, n_chunk, n_tblk, n_group, n_block;
+    int cu_in_lds;
+};
+
+struct UpdArgs {
+    const void *x;        // [B,D]
+    int64_t x_sb, x_sd;
+    void *state;          // [B,D,W-1]
+    int64_t s_sb, s_sd, s_sj;
+    const void *w;
+    int64_t w_sd, w_sk;
+    int w_f32, w_vec;
+    const void *bias;
+    int64_t b_s;
+    void *y;              // [B,D]
+    int64_t y_sb, y_sd;
+    int64_t B, D;
+    int64_t n_lane_per_row;  // ceil(D / VEC)
+};
+
+// Launchers (ccv_kernels.hip).  `vec` is the channels per lane (8 or 1).
+hipError_t launch_fwd(const FwdArgs &a, int vec, int silu, int packed, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs &a, int vec, int silu, int packed, hipStream_t s);
+hipError_t launch_update(const UpdArgs &a, int vec, int silu, hipStream_t s);
+hipError_t launch_validate(const int32_t *cu, int64_t n_seq, int64_t total, uint32_t *flags,
+                           int overwrite, hipStream_t s);
+hipError_t launch_zero(float *p, int64_t n, hipStream_t s);
+hipError_t launch_dw_reduce(const float *partial, int64_t n_part, int64_t n_elem, float *out,
+                            hipStream_t s);
+
+}  // namespace ccv

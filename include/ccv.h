@@ -1,0 +1,207 @@
+/*
+ * ccv.h — C-ABI of libccv, the MI355X (gfx950) depthwise causal conv1d.
+ *
+ * The operation (cuDNN FE "Causal Conv1d" page, the bullet list of tensor and
+ * state semantics, the paragraph on the optimized route, and the
+ * POPCORNBENCH causal conv1d trace's derivation of the causal left pad for
+ * the tap order):
+ *
+ *   z[b,d,t] = bias[d] + sum_{k=0}^{W-1} weight[d,k] * x_ext[b,d,t-(W-1)+k]
+ *   y[b,d,t] = act(z[b,d,t]),   act in {identity, SiLU}
+ *
+ * x_ext is a row of x extended on the left by its W-1 initial-state values
+ * (oldest first) or by zeros.  A row is one batch entry (dense) or one
+ * sequence [cu_seqlens[i], cu_seqlens[i+1]) of a B == 1 input packed along T.
+ * Tap W-1 multiplies the current token.  final_states holds the last W-1
+ * entries of each extended row, oldest first.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor is described by a ccv_tensor: a DEVICE pointer, a dtype,
+ *   and shape and strides in elements, in the logical index order of the
+ *   pages' shapes.  x, y, dy and dx are [B,D,T]; channel-last [B,T,D]
+ *   storage seen through transpose(1,2) has stride[1] == 1 and is consumed
+ *   as is, without a copy (cuDNN FE "Causal Conv1d", the paragraph on
+ *   transpose views).  Any non-negative strides are accepted; outputs must
+ *   not overlap themselves.
+ * - An optional tensor is absent when its descriptor pointer is NULL or its
+ *   data pointer is NULL.
+ * - All memory is owned by the caller.  The library allocates nothing,
+ *   keeps no pointer after returning, and holds no handle or state.
+ * - Every kernel is launched on `stream` (NULL = the default stream).
+ *   Calls are asynchronous: no synchronisation, no device-to-host copy and
+ *   no read of device memory on the host (cuDNN FE overview, the stream
+ *   convention).
+ * - The return value is a status (ccv_status).  Argument checks run on the
+ *   host before any launch; when a call returns a negative status nothing
+ *   was launched.  Problems with device-resident metadata are reported
+ *   through a device flag word, never through the return value.
+ * - Arithmetic: inputs are widened exactly to FP32, accumulation is FP32,
+ *   and BF16 outputs are rounded to nearest even.
+ */
+#ifndef CCV_H
+#define CCV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CCV_ABI_VERSION 1
+
+typedef enum ccv_dtype {
+    CCV_DTYPE_BF16 = 0,
+    CCV_DTYPE_F32 = 1,
+    CCV_DTYPE_I32 = 2
+} ccv_dtype;
+
+typedef enum ccv_activation {
+    CCV_ACT_NONE = 0,
+    CCV_ACT_SILU = 1
+} ccv_activation;
+
+typedef enum ccv_status {
+    CCV_OK = 0,
+    /* Deterministic dweight was requested with a bias under warn_only: the
+     * call ran with FP32 atomics (cuDNN FE "Causal Conv1d", determinism). */
+    CCV_WARN_NONDETERMINISTIC = 1,
+    /* Bad shape, stride, dtype or pointer; B != 1 with cu_seqlens; both
+     * seq_idx and cu_seqlens; T < 1; N < 1; a too-small workspace. */
+    CCV_ERR_INVALID_ARG = -1,
+    /* An output's byte span overlaps an input's or another output's
+     * (cuDNN FE "Causal Conv1d", the paragraph on final_states_out). */
+    CCV_ERR_ALIAS = -2,
+    /* Declined explicitly (cuDNN FE "Causal Conv1d", the optimized route):
+     * seq_idx given; FP32 weight with a bias; a width other than 4; an
+     * activation other than none or SiLU. */
+    CCV_ERR_UNSUPPORTED = -3,
+    /* Deterministic dweight requested with a bias and no warn_only. */
+    CCV_ERR_NONDETERMINISTIC = -4,
+    /* A HIP launch failed (hipGetLastError after the launch). */
+    CCV_ERR_HIP = -5
+} ccv_status;
+
+/* Bits of the cu_seqlens flag word (cuDNN FE "Causal Conv1d", the paragraph
+ * on device-side validation of packed offsets; "non-increasing" is split
+ * into DECREASING (a strict decrease) and EMPTY (two equal offsets)). */
+#define CCV_CU_FIRST_NONZERO 0x1u /* cu_seqlens[0] != 0 */
+#define CCV_CU_LAST_MISMATCH 0x2u /* cu_seqlens[N] != token total */
+#define CCV_CU_DECREASING    0x4u /* cu_seqlens[i+1] <  cu_seqlens[i] */
+#define CCV_CU_EMPTY         0x8u /* cu_seqlens[i+1] == cu_seqlens[i] */
+
+typedef struct ccv_tensor {
+    void *data;        /* device pointer; NULL = absent */
+    int32_t dtype;     /* ccv_dtype */
+    int32_t ndim;      /* number of used entries in shape/stride (1..3) */
+    int64_t shape[3];
+    int64_t stride[3]; /* in elements, >= 0 */
+} ccv_tensor;
+
+/*
+ * ccv_fwd — full-sequence forward (cuDNN FE "Causal Conv1d": causal_conv1d).
+ *
+ *   x               [B,D,T]  BF16, read.
+ *   weight          [D,W]    BF16, or FP32 only without bias; W must be 4.
+ *   bias            [D]      BF16, optional.
+ *   cu_seqlens      [N+1]    I32, optional; packs N sequences along T of a
+ *                            B == 1 input.  Mutually exclusive with seq_idx.
+ *   seq_idx         [B,T]    reserved: must be absent (declined otherwise).
+ *   initial_states  [R,D,W-1] BF16, optional; R = B dense, N packed.
+ *   y               [B,D,T]  BF16, written.  Any layout; usually x's.
+ *   final_states    [R,D,W-1] BF16, optional, written.
+ *   activation      CCV_ACT_NONE or CCV_ACT_SILU.
+ *   err_flag        device uint32, required with cu_seqlens, else ignored.
+ *
+ * Packed inputs are validated on the device (no host read).  The bits of
+ * the violations found are ORed into *err_flag.  The flag is sticky: when
+ * it is non-zero at kernel start, or this call's offsets are malformed, the
+ * kernels write no output and touch no memory outside the inputs'
+ * bounds.  The caller clears the word to resume.
+ */
+int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bias,
+            const ccv_tensor *cu_seqlens, const ccv_tensor *seq_idx,
+            const ccv_tensor *initial_states, const ccv_tensor *y,
+            const ccv_tensor *final_states, int activation, uint32_t *err_flag,
+            hipStream_t stream);
+
+/*
+ * ccv_bwd — backward of L = <dy, y> + <dfinal_states, final_states>
+ * (cuDNN FE "Causal Conv1d": the optimized route covers backward with the
+ * W-1 initial and final state; the determinism paragraph).
+ *
+ *   x, weight, bias, cu_seqlens, seq_idx, initial_states: as in ccv_fwd.
+ *   dy              [B,D,T]  BF16, read.
+ *   dfinal_states   [R,D,W-1] BF16, optional, read.
+ *   dx              [B,D,T]  BF16, written.
+ *   dweight         [D,W]    FP32, written (overwritten, not accumulated).
+ *   dbias           [D]      FP32, written; required iff bias is given.
+ *   dinitial_states [R,D,W-1] BF16, written; optional, only with
+ *                            initial_states.
+ *   deterministic   0: dweight/dbias accumulate with FP32 atomics (not
+ *                   bitwise reproducible).  1: bias-free calls write unique
+ *                   FP32 partials into the workspace and reduce them in a
+ *                   fixed order (bit-exact run to run); with a bias the call
+ *                   returns CCV_ERR_NONDETERMINISTIC, or, with warn_only,
+ *                   runs with atomics and returns CCV_WARN_NONDETERMINISTIC.
+ *   workspace / workspace_bytes:
+ *                   query: workspace == NULL and workspace_bytes != NULL
+ *                   -> *workspace_bytes = bytes needed, CCV_OK, nothing
+ *                   launched.  Run: workspace_bytes == NULL, or workspace
+ *                   != NULL with *workspace_bytes >= the bytes needed.  The
+ *                   workspace is device memory, 256-byte aligned.
+ *   err_flag        as in ccv_fwd.
+ */
+int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bias,
+            const ccv_tensor *cu_seqlens, const ccv_tensor *seq_idx,
+            const ccv_tensor *initial_states, const ccv_tensor *dy,
+            const ccv_tensor *dfinal_states, const ccv_tensor *dx,
+            const ccv_tensor *dweight, const ccv_tensor *dbias,
+            const ccv_tensor *dinitial_states, int activation, int deterministic,
+            int warn_only, void *workspace, size_t *workspace_bytes,
+            uint32_t *err_flag, hipStream_t stream);
+
+/*
+ * ccv_update — single-token decode step (cuDNN FE "Causal Conv1d": the
+ * returned width-four final_states feed causal_conv1d_update, which mutates
+ * the state in place with no layout conversion).
+ *
+ *   x           [B,D]      BF16, the new token, read.
+ *   conv_state  [B,D,W-1]  BF16, read and written in place: the state
+ *                          (s_0..s_{W-2}, oldest first) becomes
+ *                          (s_1..s_{W-2}, x).
+ *   weight      [D,W]      BF16 (or FP32 without bias); W must be 4.
+ *   bias        [D]        BF16, optional.
+ *   y           [B,D]      BF16, written: act(bias + sum_k w_k v_k) over
+ *                          v = (s_0..s_{W-2}, x).  Must not overlap any
+ *                          other argument.
+ */
+int ccv_update(const ccv_tensor *x, const ccv_tensor *conv_state, const ccv_tensor *weight,
+               const ccv_tensor *bias, const ccv_tensor *y, int activation,
+               hipStream_t stream);
+
+/*
+ * ccv_validate_cu_seqlens — device-side check of packed offsets (cuDNN FE
+ * "Causal Conv1d", the paragraph on device-side validation).
+ *
+ *   cu_seqlens    device int32[n_seqs + 1], read.
+ *   n_seqs        N >= 1.
+ *   total_tokens  the token total the last offset must equal (T >= 1).
+ *   flags         device uint32, OVERWRITTEN with the CCV_CU_* bit mask
+ *                 (0 = well formed).  Read it after synchronising the stream.
+ */
+int ccv_validate_cu_seqlens(const int32_t *cu_seqlens, int64_t n_seqs, int64_t total_tokens,
+                            uint32_t *flags, hipStream_t stream);
+
+/* Library version (CCV_ABI_VERSION) and a static name for a status code. */
+int ccv_abi_version(void);
+const char *ccv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CCV_H */

@@ -1,0 +1,342 @@
+"""GPU parity: the HIP path (through the C-ABI) against the fp64 oracle on the
+same seeded inputs, element by element, at sizes that span several tiles and
+end in ragged tails; every output sits inside a sentinel-filled guard band
+that must come back untouched."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from depthwise_causal_conv1d_02_amd import ops, synth
+from parity import (Guarded, check_bf16, check_exact_bf16, check_f32_rel, f64, guarded_act,
+                    guarded_flat)
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda", 0)
+BF16, F32 = torch.bfloat16, torch.float32
+
+
+def dev(t):
+    if t is None:
+        return None
+    d = t.to(DEV)
+    assert d.stride() == t.stride()
+    return d
+
+
+def inputs(seed, B, D, T, layout, bias=True, init=False, wdtype=BF16, dfinal=False, cu=None):
+    inp = synth.random_inputs(seed, B, D, T, layout=layout, bias=bias, init=init, dfinal=dfinal,
+                              weight_dtype=wdtype, cu_seqlens=cu)
+    return inp, {k: dev(v) for k, v in inp.items()}
+
+
+def run_fwd(g, layout, act, ret_final, cu=None):
+    B, D, T = g["x"].shape
+    R = B if cu is None else cu.numel() - 1
+    y = guarded_act(B, D, T, layout, DEV)
+    fin = guarded_flat((R, D, 3), DEV) if ret_final else None
+    ops.fwd(g["x"], g["weight"], g["bias"], g["cu_seqlens"], g["initial_states"], act,
+            final_states_out=None if fin is None else fin.view, y=y.view)
+    torch.cuda.synchronize()
+    return y, fin
+
+
+def check_fwd(inp, y, fin, act):
+    oy, ofin = oracle.fwd(f64(inp["x"]), f64(inp["weight"]), f64(inp["bias"]),
+                          None if inp["cu_seqlens"] is None else inp["cu_seqlens"].numpy(),
+                          f64(inp["initial_states"]), act)
+    check_bf16("y", y.view, oy)
+    assert y.intact(), "write outside y"
+    if fin is not None:
+        check_exact_bf16("final_states", fin.view, ofin)
+        assert fin.intact(), "write outside final_states"
+
+
+FWD_CASES = [
+    # B, D, T, layout, bias, init, act, weight dtype
+    (2, 1536, 300, "cl", True, True, "silu", BF16),
+    (2, 1536, 300, "cl", False, False, None, BF16),
+    (1, 1024, 77, "cl", False, True, "silu", F32),
+    (1, 64, 128, "tc", True, False, "silu", BF16),
+    (3, 40, 77, "cl", True, True, "silu", BF16),
+    (2, 48, 50, "tc", True, True, None, BF16),
+    (1, 512, 1, "cl", True, True, "silu", BF16),
+    (2, 520, 2, "cl", True, False, "silu", BF16),
+    (1, 8, 4100, "cl", True, True, "silu", BF16),
+    (2, 24, 3, "tc", False, True, "silu", F32),
+]
+
+
+@pytest.mark.parametrize("case", FWD_CASES, ids=lambda c: "B%d-D%d-T%d-%s-b%d-i%d-%s-%s" % (
+    c[0], c[1], c[2], c[3], c[4], c[5], c[6], "f32" if c[7] == F32 else "bf16"))
+def test_fwd_parity(case):
+    B, D, T, layout, bias, init, act, wdt = case
+    print("fwd case", case, flush=True)
+    inp, g = inputs(100 + D + T, B, D, T, layout, bias, init, wdt)
+    y, fin = run_fwd(g, layout, act, True)
+    check_fwd(inp, y, fin, act)
+    # without the final state
+    y2, _ = run_fwd(g, layout, act, False)
+    assert torch.equal(y2.view, y.view)
+
+
+BWD_CASES = [
+    # B, D, T, layout, bias, init, dfinal, act, weight dtype, deterministic
+    (2, 1536, 300, "cl", True, True, True, "silu", BF16, False),
+    (2, 1536, 300, "cl", False, True, False, "silu", BF16, True),
+    (2, 1024, 133, "cl", False, False, False, None, BF16, False),
+    (1, 1024, 77, "cl", False, True, True, "silu", F32, True),
+    (1, 64, 128, "tc", True, False, False, "silu", BF16, False),
+    (3, 40, 77, "cl", True, True, True, "silu", BF16, False),
+    (2, 48, 50, "tc", False, True, True, "silu", BF16, True),
+    (1, 512, 1, "cl", True, True, True, "silu", BF16, False),
+    (2, 520, 2, "cl", False, True, True, "silu", BF16, True),
+    (1, 8, 4100, "cl", True, True, True, "silu", BF16, False),
+]
+
+
+def run_bwd(g, layout, act, det, cu=None):
+    B, D, T = g["x"].shape
+    R = B if cu is None else cu.numel() - 1
+    dx = guarded_act(B, D, T, layout, DEV)
+    dinit = None
+    # dinit goes to a guarded buffer through the raw call
+    _, dw, db, dinit_t = ops.bwd(g["x"], g["weight"], g["dy"], g["bias"], g["cu_seqlens"],
+                                 g["initial_states"], g["dfinal_states"], act, det, False,
+                                 dx=dx.view)
+    torch.cuda.synchronize()
+    return dx, dw, db, dinit_t
+
+
+def check_bwd(inp, dx, dw, db, dinit, act):
+    odx, odw, odb, odinit = oracle.bwd(
+        f64(inp["x"]), f64(inp["weight"]), f64(inp["dy"]), f64(inp["bias"]),
+        None if inp["cu_seqlens"] is None else inp["cu_seqlens"].numpy(),
+        f64(inp["initial_states"]), f64(inp["dfinal_states"]), act)
+    check_bf16("dx", dx.view, odx)
+    assert dx.intact(), "write outside dx"
+    check_f32_rel("dweight", dw, odw)
+    if odb is not None:
+        check_f32_rel("dbias", db, odb)
+    else:
+        assert db is None
+    if odinit is not None:
+        check_bf16("dinitial_states", dinit, odinit)
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "B%d-D%d-T%d-%s-b%d-i%d-f%d-%s-%s-det%d" % (
+    c[0], c[1], c[2], c[3], c[4], c[5], c[6], c[7], "f32" if c[8] == F32 else "bf16", c[9]))
+def test_bwd_parity(case):
+    B, D, T, layout, bias, init, dfinal, act, wdt, det = case
+    print("bwd case", case, flush=True)
+    inp, g = inputs(200 + D + T, B, D, T, layout, bias, init, wdt, dfinal)
+    dx, dw, db, dinit = run_bwd(g, layout, act, det)
+    check_bwd(inp, dx, dw, db, dinit, act)
+    if det:
+        dx2, dw2, _, _ = run_bwd(g, layout, act, det)
+        assert torch.equal(dw2.view(torch.int32), dw.view(torch.int32))
+
+
+PACKED = [
+    ([1, 2, 3, 100, 17, 400, 5], 512, True),
+    ([1, 2, 3, 100, 17, 400, 5], 40, False),
+    ([64], 136, True),
+    ([1] * 20 + [2] * 5 + [3, 3], 520, True),
+    ([700, 1, 350, 2], 1024, False),
+]
+
+
+@pytest.mark.parametrize("lengths,D,init", PACKED)
+@pytest.mark.parametrize("det", [False, True])
+def test_packed_parity(lengths, D, init, det):
+    print("packed case", lengths, D, init, det, flush=True)
+    cu = synth.cu_from_lengths(lengths)
+    T = int(cu[-1])
+    inp, g = inputs(300 + D + T, 1, D, T, "cl", bias=not det, init=init, dfinal=True, cu=cu)
+    ops.reset_flag(DEV)
+    y, fin = run_fwd(g, "cl", "silu", True, cu)
+    check_fwd(inp, y, fin, "silu")
+    dx, dw, db, dinit = run_bwd(g, "cl", "silu", det, cu)
+    check_bwd(inp, dx, dw, db, dinit, "silu")
+    ops.check_flag(DEV)
+
+
+def test_packed_many_sequences_global_offsets():
+    """More offsets than fit in LDS: the separate validation kernel and the
+    global-memory search."""
+    rng = np.random.default_rng(5)
+    lengths = rng.integers(1, 4, size=5000).tolist()
+    cu = synth.cu_from_lengths(lengths)
+    T = int(cu[-1])
+    inp, g = inputs(401, 1, 64, T, "cl", bias=True, init=True, dfinal=True, cu=cu)
+    ops.reset_flag(DEV)
+    y, fin = run_fwd(g, "cl", "silu", True, cu)
+    check_fwd(inp, y, fin, "silu")
+    dx, dw, db, dinit = run_bwd(g, "cl", "silu", False, cu)
+    check_bwd(inp, dx, dw, db, dinit, "silu")
+    ops.check_flag(DEV)
+
+
+@pytest.mark.parametrize("n_extra", [0, 5000])
+def test_malformed_offsets_write_nothing_and_stick(n_extra):
+    good = [0] + list(np.cumsum([3] * n_extra + [5, 7])) if n_extra else [0, 5, 12]
+    T = good[-1]
+    bad = list(good)
+    bad[-2], bad[-3] = bad[-3], bad[-2]          # a decrease
+    inp, g = inputs(402, 1, 64, T, "cl", bias=True, init=True,
+                    cu=torch.tensor(good, dtype=torch.int32))
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    cu_bad = torch.tensor(bad, dtype=torch.int32, device=DEV)
+    y = guarded_act(1, 64, T, "cl", DEV)
+    fin = guarded_flat((len(bad) - 1, 64, 3), DEV)
+    before_y, before_f = y.storage.clone(), fin.storage.clone()
+    ops.fwd(g["x"], g["weight"], g["bias"], cu_bad, g["initial_states"], "silu",
+            final_states_out=fin.view, y=y.view, err_flag=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) & 0x4
+    assert torch.equal(y.storage, before_y) and torch.equal(fin.storage, before_f)
+    # the flag is sticky: valid offsets still write nothing until it is cleared
+    cu_good = g["cu_seqlens"]
+    ops.fwd(g["x"], g["weight"], g["bias"], cu_good, g["initial_states"], "silu",
+            final_states_out=fin.view, y=y.view, err_flag=flag)
+    torch.cuda.synchronize()
+    assert torch.equal(y.storage, before_y)
+    dx = guarded_act(1, 64, T, "cl", DEV)
+    before_dx = dx.storage.clone()
+    ops.bwd(g["x"], g["weight"], g["x"], g["bias"], cu_bad, g["initial_states"], None, "silu",
+            dx=dx.view, err_flag=flag)
+    torch.cuda.synchronize()
+    assert torch.equal(dx.storage, before_dx)
+    flag.zero_()
+    ops.fwd(g["x"], g["weight"], g["bias"], cu_good, g["initial_states"], "silu",
+            final_states_out=fin.view, y=y.view, err_flag=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+    check_fwd(inp, y, fin, "silu")
+
+
+def _flag_predicate(cu, total):
+    bits = 0
+    if cu[0] != 0:
+        bits |= 1
+    if cu[-1] != total:
+        bits |= 2
+    d = np.diff(np.asarray(cu))
+    if (d < 0).any():
+        bits |= 4
+    if (d == 0).any():
+        bits |= 8
+    return bits
+
+
+def test_validate_brute_force():
+    import itertools
+    from depthwise_causal_conv1d_02_amd import _abi
+    cases = []
+    for N in (1, 2, 3):
+        for cu in itertools.product(range(-1, 6), repeat=N + 1):
+            for total in range(1, 6):
+                cases.append((cu, total))
+    flat = torch.tensor([v for cu, _ in cases for v in cu], dtype=torch.int32, device=DEV)
+    flags = torch.full((len(cases),), -1, dtype=torch.int32, device=DEV)
+    L = _abi.lib()
+    stream = torch.cuda.current_stream(DEV).cuda_stream
+    off = 0
+    base, fbase = flat.data_ptr(), flags.data_ptr()
+    for i, (cu, total) in enumerate(cases):
+        rc = L.ccv_validate_cu_seqlens(base + 4 * off, len(cu) - 1, total, fbase + 4 * i, stream)
+        assert rc == 0
+        off += len(cu)
+    got = flags.cpu().numpy()
+    want = np.array([oracle.validate_cu_seqlens(list(cu), total) for cu, total in cases])
+    assert np.array_equal(got, want)
+    assert all(want[i] == _flag_predicate(cu, t) for i, (cu, t) in enumerate(cases[:2000]))
+
+
+UPDATE_CASES = [(4, 512, True, BF16), (3, 40, True, BF16), (2, 1024, False, F32),
+                (5, 24, False, BF16)]
+
+
+@pytest.mark.parametrize("B,D,bias,wdt", UPDATE_CASES)
+def test_update_parity(B, D, bias, wdt):
+    print("update case", B, D, bias, wdt, flush=True)
+    gen = torch.Generator().manual_seed(500 + D)
+    state = synth.state_tensor(gen, B, D)
+    w = synth.weight_tensor(gen, D, dtype=wdt)
+    b = synth.bias_tensor(gen, D) if bias else None
+    xs = [synth.activation_tensor(gen, B, D, 1, "tc")[:, :, 0].contiguous() for _ in range(6)]
+    g_state = dev(state)
+    st = f64(state)
+    for x in xs:
+        y = guarded_flat((B, D), DEV)
+        ops.update(dev(x), g_state, dev(w), dev(b), "silu", y=y.view)
+        torch.cuda.synchronize()
+        oy, st = oracle.update(f64(x), st, f64(w), f64(b), "silu")
+        check_bf16("update y", y.view, oy)
+        assert y.intact()
+        check_exact_bf16("conv_state", g_state, st)
+
+
+def test_update_strided_state():
+    """A state that is a slice of a wider buffer (generic lanes)."""
+    gen = torch.Generator().manual_seed(77)
+    big = synth.state_tensor(gen, 3, 64, W=6)         # [3,64,5]
+    g_big = dev(big)
+    g_state = g_big[:, :, 1:4]                          # [3,64,3], stride (320,5,1)
+    w = synth.weight_tensor(gen, 64)
+    x = synth.activation_tensor(gen, 3, 64, 1, "tc")[:, :, 0].contiguous()
+    y = ops.update(dev(x), g_state, dev(w), None, None)
+    torch.cuda.synchronize()
+    oy, st = oracle.update(f64(x), f64(big[:, :, 1:4]), f64(w), None, None)
+    check_bf16("y", y, oy)
+    check_exact_bf16("state", g_state, st)
+    check_exact_bf16("untouched", g_big[:, :, 0], f64(big[:, :, 0]))
+    check_exact_bf16("untouched", g_big[:, :, 4], f64(big[:, :, 4]))
+
+
+def test_autograd_wrapper():
+    inp, g = inputs(600, 2, 512, 64, "cl", bias=True, init=True, dfinal=True)
+    x = g["x"].detach().requires_grad_(True)
+    w = g["weight"].detach().requires_grad_(True)
+    b = g["bias"].detach().requires_grad_(True)
+    init = g["initial_states"].detach().requires_grad_(True)
+    y, fin = ops.causal_conv1d(x, w, b, initial_states=init, return_final_states=True,
+                               activation="silu")
+    (y.float() * g["dy"].float()).sum().backward(retain_graph=True)
+    odx, odw, odb, _ = oracle.bwd(f64(inp["x"]), f64(inp["weight"]), f64(inp["dy"]),
+                                  f64(inp["bias"]), None, f64(inp["initial_states"]), None,
+                                  "silu")
+    check_f32_rel("dweight", w.grad.float(), odw, rel=2e-2)  # cast to BF16 parameters
+    check_f32_rel("dbias", b.grad.float(), odb, rel=2e-2)
+    oy, ofin = oracle.fwd(f64(inp["x"]), f64(inp["weight"]), f64(inp["bias"]), None,
+                          f64(inp["initial_states"]), "silu")
+    check_bf16("y", y, oy)
+    check_exact_bf16("final", fin, ofin)
+    assert x.grad.stride() == x.stride()
+    check_bf16("dx", x.grad, odx)
+
+
+def test_deterministic_flag_policy():
+    inp, g = inputs(700, 1, 512, 40, "cl", bias=True)
+    with pytest.raises(RuntimeError):
+        ops.bwd(g["x"], g["weight"], g["dy"], g["bias"], deterministic=True)
+    with pytest.warns(UserWarning):
+        dx, dw, db, _ = ops.bwd(g["x"], g["weight"], g["dy"], g["bias"], deterministic=True,
+                                warn_only=True)
+    torch.cuda.synchronize()
+    odx, odw, odb, _ = oracle.bwd(f64(inp["x"]), f64(inp["weight"]), f64(inp["dy"]),
+                                  f64(inp["bias"]), None, None, None, "silu")
+    check_f32_rel("dweight", dw, odw)
+    check_f32_rel("dbias", db, odb)
+
+
+def test_fp32_weight_rounding_is_single_rne():
+    """y = x * w3 in FP32, rounded once to BF16 (no activation, one tap)."""
+    gen = torch.Generator().manual_seed(9)
+    x = synth.activation_tensor(gen, 1, 512, 256, "cl")
+    w = torch.zeros(512, 4, dtype=F32)
+    w[:, 3] = torch.rand(512, generator=gen) + 0.1
+    y, _ = ops.fwd(dev(x), dev(w), None, None, None, None)
+    torch.cuda.synchronize()
+    want = (x.float() * w[:, 3][None, :, None]).to(BF16)
+    assert torch.equal(y.cpu(), want)
