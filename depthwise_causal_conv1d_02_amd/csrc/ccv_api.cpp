@@ -381,10 +381,6 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     a.n_block = g.n_block;
     a.cu_in_lds = p.packed && p.N + 1 <= ccv::kLdsCuMax;
 
-    if (!use_partials) {
-        if ((rc = hip_status(ccv::launch_zero(a.dw, p.D * kWidth, stream))) != CCV_OK) return rc;
-        if (a.db && (rc = hip_status(ccv::launch_zero(a.db, p.D, stream))) != CCV_OK) return rc;
-    }
     if (p.packed && !a.cu_in_lds) {
         rc = hip_status(ccv::launch_validate(a.cu, p.N, p.T, err_flag, 0, stream));
         if (rc != CCV_OK) return rc;

@@ -47,7 +47,7 @@ struct BwdArgs {
     int w_f32, w_vec;
     const void *bias;
     int64_t b_s;
-    float *dw;                 // [D,W] FP32 (atomic path) — contiguous
+    float *dw;                 // [D,W] FP32, contiguous, accumulated into
     float *db;                 // [D] FP32 or nullptr
     float *partial;            // deterministic path: [P][D][W] FP32, else nullptr
     const int32_t *cu;
@@ -79,7 +79,6 @@ hipError_t launch_bwd(const BwdArgs &a, int vec, int silu, int packed, hipStream
 hipError_t launch_update(const UpdArgs &a, int vec, int silu, hipStream_t s);
 hipError_t launch_validate(const int32_t *cu, int64_t n_seq, int64_t total, uint32_t *flags,
                            int overwrite, hipStream_t s);
-hipError_t launch_zero(float *p, int64_t n, hipStream_t s);
 hipError_t launch_dw_reduce(const float *partial, int64_t n_part, int64_t n_elem, float *out,
                             hipStream_t s);
 

@@ -699,13 +699,7 @@ __global__ __launch_bounds__(256) void k_validate(const int32_t *cu, int64_t n_s
     }
 }
 
-__global__ __launch_bounds__(256) void k_zero(float *p, int64_t n) {
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
-        p[i] = 0.0f;
-}
-
-// Fixed-order reduction of unique partials: out[e] = sum_{p=0}^{P-1} part[p][e],
+// Fixed-order reduction of unique partials: out[e] += sum_{p=0}^{P-1} part[p][e],
 // always in increasing p, so the result does not depend on scheduling.
 __global__ __launch_bounds__(256) void k_dw_reduce(const float *part, int64_t n_part,
                                                    int64_t n_elem, float *out) {
@@ -713,7 +707,7 @@ __global__ __launch_bounds__(256) void k_dw_reduce(const float *part, int64_t n_
     if (e >= n_elem) return;
     float acc = 0.0f;
     for (int64_t p = 0; p < n_part; ++p) acc += part[p * n_elem + e];
-    out[e] = acc;
+    out[e] += acc;
 }
 
 template <typename K, typename A>
@@ -762,14 +756,6 @@ hipError_t launch_update(const UpdArgs &a, int vec, int silu, hipStream_t s) {
 hipError_t launch_validate(const int32_t *cu, int64_t n_seq, int64_t total, uint32_t *flags,
                            int overwrite, hipStream_t s) {
     hipLaunchKernelGGL(k_validate, dim3(1), dim3(256), 0, s, cu, n_seq, total, flags, overwrite);
-    return hipGetLastError();
-}
-
-hipError_t launch_zero(float *p, int64_t n, hipStream_t s) {
-    if (n <= 0) return hipSuccess;
-    int64_t blocks = (n + 255) / 256;
-    if (blocks > 1024) blocks = 1024;
-    hipLaunchKernelGGL(k_zero, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p, n);
     return hipGetLastError();
 }
 

@@ -149,16 +149,20 @@ def fwd(x, weight, bias=None, cu_seqlens=None, initial_states=None, activation="
 
 def bwd(x, weight, dy, bias=None, cu_seqlens=None, initial_states=None, dfinal_states=None,
         activation="silu", deterministic=False, warn_only=False, dx=None, err_flag=None,
-        want_dinit=True, seq_idx=None, workspace=None):
+        want_dinit=True, seq_idx=None, workspace=None, dweight=None, dbias=None, dinit=None):
     """One ccv_bwd call.  Returns (dx, dweight_f32, dbias_f32 or None,
-    dinitial_states or None)."""
+    dinitial_states or None).  ``dweight``/``dbias`` (FP32) are accumulated
+    into when given, else freshly zeroed ones are used."""
     if dx is None:
         dx = torch.empty_like(x)
     D, W = weight.shape
-    dw = torch.empty(D, W, dtype=torch.float32, device=x.device)
-    db = torch.empty(D, dtype=torch.float32, device=x.device) if bias is not None else None
-    dinit = (torch.empty_like(initial_states) if (initial_states is not None and want_dinit)
-             else None)
+    dw = dweight if dweight is not None else torch.zeros(D, W, dtype=torch.float32,
+                                                          device=x.device)
+    db = None
+    if bias is not None:
+        db = dbias if dbias is not None else torch.zeros(D, dtype=torch.float32, device=x.device)
+    if dinit is None and initial_states is not None and want_dinit:
+        dinit = torch.empty_like(initial_states)
     flag = None
     if cu_seqlens is not None:
         flag = err_flag if err_flag is not None else flag_tensor(x.device)

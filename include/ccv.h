@@ -137,14 +137,17 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
  *   dy              [B,D,T]  BF16, read.
  *   dfinal_states   [R,D,W-1] BF16, optional, read.
  *   dx              [B,D,T]  BF16, written.
- *   dweight         [D,W]    FP32, written (overwritten, not accumulated).
- *   dbias           [D]      FP32, written; required iff bias is given.
+ *   dweight         [D,W]    FP32, ACCUMULATED into (+=), like an autograd
+ *                            .grad; zero it first for a plain gradient.
+ *   dbias           [D]      FP32, accumulated into; required iff bias is
+ *                            given.
  *   dinitial_states [R,D,W-1] BF16, written; optional, only with
  *                            initial_states.
  *   deterministic   0: dweight/dbias accumulate with FP32 atomics (not
  *                   bitwise reproducible).  1: bias-free calls write unique
- *                   FP32 partials into the workspace and reduce them in a
- *                   fixed order (bit-exact run to run); with a bias the call
+ *                   FP32 partials into the workspace and add their sum, taken
+ *                   in a fixed order, to dweight (bit-exact run to run for
+ *                   the same starting dweight); with a bias the call
  *                   returns CCV_ERR_NONDETERMINISTIC, or, with warn_only,
  *                   runs with atomics and returns CCV_WARN_NONDETERMINISTIC.
  *   workspace / workspace_bytes:
