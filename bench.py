@@ -33,6 +33,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+SPACER_CYCLES = 200000      # GPU spin before each timed op in the per-op pass
 METRIC = "achieved HBM GB/s (% of MI355X peak) for fwd, bwd and update at 1 GPU"
 
 
@@ -70,10 +71,12 @@ class Workload:
         self.ops = []
         if name == "decode":
             B, D = w["conv_state"].shape[:2]
-            self.shape = dict(B=B, D=D)
+            n_tok = w["x_steps"].shape[0]
+            self.shape = dict(B=B, D=D, tokens=n_tok)
             self.bytes = {"update": update_bytes(B, D, 2, True)}
-            self.desc = ("decode update: B=%d D=%d, one token per step (64 seeded tokens), "
-                         "bf16 weight+bias, SiLU, state mutated in place" % (B, D))
+            self.counts = {"update": n_tok}
+            self.desc = ("decode update: B=%d D=%d, %d single-token steps per step, bf16 "
+                         "weight+bias, SiLU, state mutated in place" % (B, D, n_tok))
             return
         x = w["x"]
         B, D, T = x.shape
@@ -88,6 +91,7 @@ class Workload:
             self.bytes["bwd"] = bwd_bytes(B, D, T, R, init, False, wb, bias)
         if name == "dense":
             self.bytes["update"] = update_bytes(B, D, 2, bias)
+        self.counts = {k: 1 for k in self.bytes}
         self.desc = synth.WORKLOADS[idx]
 
 
@@ -98,15 +102,17 @@ def make_step(wl, torch):
     g, dev = wl.g, wl.dev
     if wl.name == "decode":
         state = g["conv_state"].clone()
-        y = torch.empty_like(g["x_steps"][0])
-        n = [0]
+        xs = g["x_steps"]
+        ys = torch.empty_like(xs)
 
         def step(ev):
-            xt = g["x_steps"][n[0] % g["x_steps"].shape[0]]
-            n[0] += 1
-            ev.begin("update")
-            ops.update(xt, state, g["weight"], g["bias"], g["activation"], y=y)
-            ev.end("update")
+            # one step decodes the 64 seeded tokens in order, each in place on
+            # the same state
+            for s in range(xs.shape[0]):
+                ev.begin("update")
+                ops.update(xs[s], state, g["weight"], g["bias"], g["activation"], y=ys[s])
+                ev.end("update")
+        step.outputs = {"y": ys}
         return step
 
     x = g["x"]
@@ -117,13 +123,15 @@ def make_step(wl, torch):
     has_bwd = g["dy"] is not None
     if has_bwd:
         dx = torch.empty_like(x)
-        dw = torch.zeros(x.shape[1], 4, dtype=torch.float32, device=dev)
-        db = torch.zeros(x.shape[1], dtype=torch.float32, device=dev) if g["bias"] is not None else None
+        D = x.shape[1]
+        # dweight and dbias live in one buffer, cleared by a single fill per step
+        grads = torch.zeros(D * 5, dtype=torch.float32, device=dev)
+        dw = grads[:D * 4].view(D, 4)
+        db = grads[D * 4:] if g["bias"] is not None else None
         dinit = torch.empty_like(g["initial_states"]) if g["initial_states"] is not None else None
         ws = torch.empty(1 << 26, dtype=torch.uint8, device=dev) if g["deterministic"] else None
     flag = torch.zeros(1, dtype=torch.int32, device=dev)
     if wl.name == "dense":
-        state = torch.empty_like(fin)
         xt = g["x"][:, :, -1].contiguous()
         yt = torch.empty_like(xt)
 
@@ -133,32 +141,40 @@ def make_step(wl, torch):
                 final_states_out=fin, y=y, err_flag=flag)
         ev.end("fwd")
         if has_bwd:
-            dw.zero_()
-            if db is not None:
-                db.zero_()
+            grads.zero_()
             ev.begin("bwd")
             ops.bwd(x, g["weight"], g["dy"], g["bias"], g["cu_seqlens"], g["initial_states"], None,
                     g["activation"], g["deterministic"], False, dx=dx, err_flag=flag,
                     workspace=ws, dweight=dw, dbias=db, dinit=dinit)
             ev.end("bwd")
         if wl.name == "dense":
-            state.copy_(fin)
+            # decode the next token straight from the returned final states
+            # (updated in place; the next step's forward rewrites them)
             ev.begin("update")
-            ops.update(xt, state, g["weight"], g["bias"], g["activation"], y=yt)
+            ops.update(xt, fin, g["weight"], g["bias"], g["activation"], y=yt)
             ev.end("update")
+    step.outputs = {"y": y}
+    if has_bwd:
+        step.outputs.update(dx=dx, dw=dw)
     return step
 
 
 class Events:
-    """HIP events around each op on the current stream (the one the kernels use)."""
+    """HIP events around each op on the current stream (the one the kernels use).
 
-    def __init__(self, torch, on):
-        self.torch, self.on = torch, on
+    With `spacer`, a short GPU spin runs before each start event, so that the
+    host has queued the op before the GPU reaches it: the event pair then
+    brackets the op's kernels, not host launch latency."""
+
+    def __init__(self, torch, on, spacer=False):
+        self.torch, self.on, self.spacer = torch, on, spacer
         self.rec = {}
         self.open = {}
 
     def begin(self, name):
         if self.on:
+            if self.spacer:
+                self.torch.cuda._sleep(SPACER_CYCLES)
             e = self.torch.cuda.Event(enable_timing=True)
             e.record()
             self.open[name] = e
@@ -238,7 +254,11 @@ def main():
                     choices=["dense", "packed", "decode", "large", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-events", action="store_true",
-                    help="time the steps without per-op events")
+                    help="skip the per-op event pass")
+    ap.add_argument("--graph", dest="graph", action="store_true", default=True,
+                    help="replay the step as a captured HIP graph in the timed region (default)")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="launch every op eagerly in the timed region")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the workload, run a plain device copy of MIB MiB "
                          "(counter calibration for rocprofv3 --pmc)")
@@ -268,30 +288,62 @@ def main():
     print("bench: building workload %s" % args.workload, file=sys.stderr, flush=True)
     wl = Workload(args.workload, dev)
     step = make_step(wl, torch)
-    warm = Events(torch, False)
+    quiet = Events(torch, False)
     for _ in range(args.warmup):
-        step(warm)
-    ev = Events(torch, not args.no_events)
+        step(quiet)
+    torch.cuda.synchronize()
+
+    graph = None
+    if args.graph:
+        # The step's launches captured once and replayed: no host launch
+        # latency between kernels (HIP graph under torch.cuda.CUDAGraph).
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step(quiet)
+        graph.replay()
+        torch.cuda.synchronize()
+
+    # Timed region: exactly K steps between two synchronisations.
+    step_ev = Events(torch, graph is not None and not args.no_events)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(ev)
+        if graph is not None:
+            step_ev.begin("step")
+            graph.replay()
+            step_ev.end("step")
+        else:
+            step(quiet)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
-    step_bytes = sum(wl.bytes.values())
+    step_bytes = sum(wl.bytes[k] * wl.counts[k] for k in wl.bytes)
     value = step_bytes / (ms * 1e-3) / 1e9
-    print("bench: timed %d steps, %.4f ms/step" % (args.steps, ms), file=sys.stderr, flush=True)
+    print("bench: timed %d steps, %.4f ms/step (%s)" % (
+        args.steps, ms, "graph replay" if graph is not None else "eager"), file=sys.stderr,
+        flush=True)
 
     per_op = {}
     roof = None
     if not args.no_events:
+        # Per-op times: an eager pass with events around every op, on the
+        # stream the kernels run on.  A step of one op kind (decode) takes its
+        # per-launch time from the graph replays instead, where no host
+        # latency sits between launches.
+        ev = Events(torch, True, spacer=True)
+        for _ in range(args.steps):
+            step(ev)
+        torch.cuda.synchronize()
         means = ev.mean_ms()
+        if graph is not None and len(wl.bytes) == 1:
+            (k,) = wl.bytes
+            means[k] = step_ev.mean_ms()["step"] / wl.counts[k]
         for k, t in means.items():
             gbs = wl.bytes[k] / (t * 1e-3) / 1e9
             per_op[k] = {"ms": round(t, 5), "algorithmic_bytes": wl.bytes[k],
+                         "launches_per_step": wl.counts[k],
                          "GB_s": round(gbs, 1), "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2)}
-        dom = max(means, key=lambda k: means[k])
+        dom = max(means, key=lambda k: means[k] * wl.counts[k])
         kernel = {"fwd": "k_fwd_chan", "bwd": "k_bwd_chan", "update": "k_update"}[dom]
         ach = wl.bytes[dom] / (means[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": kernel, "op": dom, "achieved": round(ach, 1),
@@ -300,14 +352,15 @@ def main():
                 "avg_launch_ms": round(means[dom], 5)}
 
     shape = wl.shape
-    tc = shape["B"] * shape["D"] * shape.get("T", 1)
+    tc = shape["B"] * shape["D"] * shape.get("T", shape.get("tokens", 1))
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.desc, "io_dtype": "bf16", **shape,
-                   "ops_per_step": list(wl.bytes), "step_algorithmic_bytes": step_bytes},
+                   "ops_per_step": wl.counts, "step_algorithmic_bytes": step_bytes,
+                   "timing": "graph replay" if graph is not None else "eager launches"},
         "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "token_channels_per_s": round(tc / (ms * 1e-3), 1),
         "ops": per_op, "roofline": roof,

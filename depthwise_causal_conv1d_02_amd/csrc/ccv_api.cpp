@@ -9,14 +9,43 @@
 #include "ccv.h"
 #include "ccv_internal.h"
 
-#ifndef CCV_TARGET_WAVES
-#define CCV_TARGET_WAVES 16384  // waves per channel-lane launch the chunk length aims for
+// Launch geometry of the channel-lane kernels (measured on MI355X): the
+// chunk of time steps per wave aims for a number of waves per launch, within
+// [min, max] steps; lanes own VEC channels when the layout allows.
+#ifndef CCV_FWD_TARGET_WAVES
+#define CCV_FWD_TARGET_WAVES 16384
 #endif
-#ifndef CCV_MIN_CHUNK
-#define CCV_MIN_CHUNK 16        // time steps per wave, at least
+#ifndef CCV_FWD_MIN_CHUNK
+#define CCV_FWD_MIN_CHUNK 16
+#endif
+#ifndef CCV_BWD_TARGET_WAVES
+#define CCV_BWD_TARGET_WAVES 16384
+#endif
+#ifndef CCV_BWD_MIN_CHUNK
+#define CCV_BWD_MIN_CHUNK 16
 #endif
 #ifndef CCV_MAX_CHUNK
 #define CCV_MAX_CHUNK 1024
+#endif
+#ifndef CCV_FWD_ROUNDS
+#define CCV_FWD_ROUNDS 0        // 0: size the grid by target waves
+#endif
+#ifndef CCV_BWD_ROUNDS
+#define CCV_BWD_ROUNDS 1
+#endif
+#ifndef CCV_FWD_VEC
+#define CCV_FWD_VEC 8
+#endif
+// Bulk loads use the non-temporal policy once an op streams at least this
+// many input bytes (twice the 256 MB memory-side cache).
+#ifndef CCV_NT_LOAD_MIN_BYTES
+#define CCV_NT_LOAD_MIN_BYTES (int64_t(1) << 29)
+#endif
+#ifndef CCV_UPD_VEC
+#define CCV_UPD_VEC 8
+#endif
+#ifndef CCV_BWD_VEC
+#define CCV_BWD_VEC 4           // the backward kernels are built for 4 or 1
 #endif
 
 namespace {
@@ -101,16 +130,31 @@ bool injective(const ccv_tensor *t) {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// A [B,D,T] BF16 tensor the VEC = 8 lanes can read with 16-byte vectors.
-bool vec8_ok(const ccv_tensor *t) {
+// A [B,D,T] BF16 tensor that lanes owning `vec` channels can read with
+// vec*2-byte vectors: unit channel stride, and every row start aligned.
+bool vec_ok(const ccv_tensor *t, int vec) {
     if (!present(t)) return true;
     const int64_t B = t->shape[0], D = t->shape[1], T = t->shape[2];
-    return t->stride[1] == 1 && D % 8 == 0 && aligned16(t->data) &&
-           (B == 1 || t->stride[0] % 8 == 0) && (T == 1 || t->stride[2] % 8 == 0);
+    const uintptr_t a = reinterpret_cast<uintptr_t>(t->data);
+    return t->stride[1] == 1 && D % vec == 0 && a % (2 * vec) == 0 &&
+           (B == 1 || t->stride[0] % vec == 0) && (T == 1 || t->stride[2] % vec == 0);
 }
 
 bool filter_vec(const ccv_tensor *w) {
     return w->stride[1] == 1 && w->stride[0] == kWidth && aligned16(w->data);
+}
+
+// The widest lane width (preferred first, then 4, else 1) every tensor
+// allows.  Vector lanes also load the filter and bias as vectors.
+int pick_vec(int preferred, const ccv_tensor *weight, const ccv_tensor *bias,
+             const ccv_tensor *a, const ccv_tensor *b, const ccv_tensor *c) {
+    if (!filter_vec(weight) || (present(bias) && (bias->stride[0] != 1 || !aligned16(bias->data))))
+        return 1;
+    for (int v : {preferred, 4}) {
+        if (v <= 1) continue;
+        if (vec_ok(a, v) && vec_ok(b, v) && vec_ok(c, v)) return v;
+    }
+    return 1;
 }
 
 ccv::Strided3 s3(const ccv_tensor *t) {
@@ -194,20 +238,33 @@ bool any_alias(const Span *outs, int n_out, const Span *ins, int n_in) {
     return false;
 }
 
-// Time steps per wave: enough waves to fill 256 CUs several times over,
-// but never fewer than CCV_MIN_CHUNK steps per wave.
+// Time steps per wave (L).  With `rounds` > 0 and the device's resident
+// block capacity known, L makes the grid `rounds` whole rounds of resident
+// blocks, so that no last round runs partly empty.  Otherwise L aims for
+// `target_waves` waves.  Never fewer than `min_chunk` steps per wave.
 struct Geometry {
     int64_t L, n_chunk, n_tblk, n_group, n_block;
 };
 
-Geometry geometry(const Problem &p, int vec) {
+Geometry geometry(const Problem &p, int vec, int64_t capacity, int rounds, int64_t target_waves,
+                  int64_t min_chunk) {
     Geometry g;
     g.n_group = (p.D + ccv::kWaveSize * vec - 1) / (ccv::kWaveSize * vec);
     const int64_t rows = p.packed ? 1 : p.B;
     const int64_t work = rows * g.n_group * p.T;
-    int64_t L = (work + CCV_TARGET_WAVES - 1) / CCV_TARGET_WAVES;
-    L = (L + 7) / 8 * 8;
-    L = std::max<int64_t>(CCV_MIN_CHUNK, std::min<int64_t>(CCV_MAX_CHUNK, L));
+    int64_t L = 0;
+    if (capacity > 0 && rounds > 0) {
+        const int64_t per_row_group = capacity * rounds / (rows * g.n_group);
+        if (per_row_group >= 1) {
+            const int64_t chunks = per_row_group * ccv::kWavesPerBlock;
+            L = (p.T + chunks - 1) / chunks;
+        }
+    }
+    if (L == 0) {
+        L = (work + target_waves - 1) / target_waves;
+        L = (L + 7) / 8 * 8;
+    }
+    L = std::max<int64_t>(min_chunk, std::min<int64_t>(CCV_MAX_CHUNK, L));
     g.L = L;
     g.n_chunk = (p.T + L - 1) / L;
     g.n_tblk = (g.n_chunk + ccv::kWavesPerBlock - 1) / ccv::kWavesPerBlock;
@@ -254,8 +311,7 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
                         span_of(initial_states)};
     if (any_alias(outs, 3, ins, 5)) return CCV_ERR_ALIAS;
 
-    const int vec = (vec8_ok(x) && vec8_ok(y)) ? 8 : 1;
-    const Geometry g = geometry(p, vec);
+    const int vec = pick_vec(CCV_FWD_VEC, weight, bias, x, y, nullptr);
     ccv::FwdArgs a;
     memset(&a, 0, sizeof(a));
     a.x = s3(x);
@@ -272,6 +328,10 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     a.cu = p.packed ? static_cast<const int32_t *>(cu_seqlens->data) : nullptr;
     a.n_seq = p.N;
     a.err = p.packed ? err_flag : nullptr;
+    const int silu = activation == CCV_ACT_SILU;
+    const int64_t cap = CCV_FWD_ROUNDS > 0 ? ccv::fwd_resident_blocks(a, vec, silu, p.packed) : 0;
+    const Geometry g = geometry(p, vec, cap, CCV_FWD_ROUNDS, CCV_FWD_TARGET_WAVES,
+                                CCV_FWD_MIN_CHUNK);
     a.B = p.B;
     a.D = p.D;
     a.T = p.T;
@@ -281,11 +341,12 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     a.n_group = g.n_group;
     a.n_block = g.n_block;
     a.cu_in_lds = p.packed && p.N + 1 <= ccv::kLdsCuMax;
+    a.nt_load = p.B * p.D * p.T * 2 >= CCV_NT_LOAD_MIN_BYTES;
     if (p.packed && !a.cu_in_lds) {
         rc = hip_status(ccv::launch_validate(a.cu, p.N, p.T, err_flag, 0, stream));
         if (rc != CCV_OK) return rc;
     }
-    return hip_status(ccv::launch_fwd(a, vec, activation == CCV_ACT_SILU, p.packed, stream));
+    return hip_status(ccv::launch_fwd(a, vec, silu, p.packed, stream));
 }
 
 int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bias,
@@ -328,8 +389,11 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
             use_partials = true;
         }
     }
-    const int vec = (vec8_ok(x) && vec8_ok(dy) && vec8_ok(dx)) ? 8 : 1;
-    const Geometry g = geometry(p, vec);
+    const int vec = pick_vec(CCV_BWD_VEC, weight, bias, x, dy, dx);
+    // The partials of the deterministic route depend on the shape only (a
+    // grid sized by target waves); the atomic route sizes its grid by the
+    // device's resident capacity below.
+    Geometry g = geometry(p, vec, 0, 0, CCV_BWD_TARGET_WAVES, CCV_BWD_MIN_CHUNK);
     const int64_t n_part = (p.packed ? 1 : p.B) * g.n_tblk;
     const size_t need = use_partials
                             ? static_cast<size_t>(n_part) * static_cast<size_t>(p.D) * kWidth * 4
@@ -371,6 +435,10 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     a.cu = p.packed ? static_cast<const int32_t *>(cu_seqlens->data) : nullptr;
     a.n_seq = p.N;
     a.err = p.packed ? err_flag : nullptr;
+    const int silu = activation == CCV_ACT_SILU;
+    if (!use_partials && CCV_BWD_ROUNDS > 0)
+        g = geometry(p, vec, ccv::bwd_resident_blocks(a, vec, silu, p.packed), CCV_BWD_ROUNDS,
+                     CCV_BWD_TARGET_WAVES, CCV_BWD_MIN_CHUNK);
     a.B = p.B;
     a.D = p.D;
     a.T = p.T;
@@ -380,12 +448,13 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     a.n_group = g.n_group;
     a.n_block = g.n_block;
     a.cu_in_lds = p.packed && p.N + 1 <= ccv::kLdsCuMax;
+    a.nt_load = 2 * p.B * p.D * p.T * 2 >= CCV_NT_LOAD_MIN_BYTES;
 
     if (p.packed && !a.cu_in_lds) {
         rc = hip_status(ccv::launch_validate(a.cu, p.N, p.T, err_flag, 0, stream));
         if (rc != CCV_OK) return rc;
     }
-    rc = hip_status(ccv::launch_bwd(a, vec, activation == CCV_ACT_SILU, p.packed, stream));
+    rc = hip_status(ccv::launch_bwd(a, vec, silu, p.packed, stream));
     if (rc != CCV_OK) return rc;
     if (use_partials) {
         rc = hip_status(ccv::launch_dw_reduce(a.partial, n_part, p.D * kWidth, a.dw, stream));
@@ -423,11 +492,15 @@ int ccv_update(const ccv_tensor *x, const ccv_tensor *conv_state, const ccv_tens
     const Span ins[] = {span_of(x), span_of(weight), span_of(bias)};
     if (any_alias(outs, 2, ins, 3)) return CCV_ERR_ALIAS;
 
-    const bool vec = D % 8 == 0 && x->stride[1] == 1 && y->stride[1] == 1 &&
+    // 8-channel lanes need unit channel strides, a contiguous state, a
+    // contiguous filter and bias, and 16-byte aligned rows everywhere.
+    const bool vec = CCV_UPD_VEC == 8 && D % 8 == 0 && x->stride[1] == 1 && y->stride[1] == 1 &&
                      conv_state->stride[2] == 1 && conv_state->stride[1] == kWidth - 1 &&
                      aligned16(x->data) && aligned16(y->data) && aligned16(conv_state->data) &&
                      (B == 1 || (x->stride[0] % 8 == 0 && y->stride[0] % 8 == 0 &&
-                                 conv_state->stride[0] % 8 == 0));
+                                 conv_state->stride[0] % 8 == 0)) &&
+                     filter_vec(weight) &&
+                     (!present(bias) || (bias->stride[0] == 1 && aligned16(bias->data)));
     ccv::UpdArgs a;
     memset(&a, 0, sizeof(a));
     a.x = x->data;

@@ -38,6 +38,7 @@ struct FwdArgs {
     int64_t n_group;           // channel groups of 64*VEC channels
     int64_t n_block;           // grid size
     int cu_in_lds;             // stage + validate cu_seqlens in LDS
+    int nt_load;               // stream the bulk loads with the non-temporal policy
 };
 
 struct BwdArgs {
@@ -55,6 +56,7 @@ struct BwdArgs {
     uint32_t *err;
     int64_t B, D, T, L, n_chunk, n_tblk, n_group, n_block;
     int cu_in_lds;
+    int nt_load;
 };
 
 struct UpdArgs {
@@ -77,6 +79,10 @@ struct UpdArgs {
 hipError_t launch_fwd(const FwdArgs &a, int vec, int silu, int packed, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs &a, int vec, int silu, int packed, hipStream_t s);
 hipError_t launch_update(const UpdArgs &a, int vec, int silu, hipStream_t s);
+// Blocks of the kernel launch_fwd / launch_bwd would pick that fit on the
+// current device at once (0 if the runtime cannot tell).  Host queries only.
+int64_t fwd_resident_blocks(const FwdArgs &a, int vec, int silu, int packed);
+int64_t bwd_resident_blocks(const BwdArgs &a, int vec, int silu, int packed);
 hipError_t launch_validate(const int32_t *cu, int64_t n_seq, int64_t total, uint32_t *flags,
                            int overwrite, hipStream_t s);
 hipError_t launch_dw_reduce(const float *partial, int64_t n_part, int64_t n_elem, float *out,

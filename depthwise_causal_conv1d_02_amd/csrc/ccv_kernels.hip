@@ -22,6 +22,8 @@
 // by every block (no host read) and searched there.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "ccv_internal.h"
 
 namespace ccv {
@@ -32,10 +34,27 @@ constexpr uint32_t kFirstNonzero = 0x1u, kLastMismatch = 0x2u, kDecreasing = 0x4
                    kEmpty = 0x8u;
 
 #ifndef CCV_FWD_UNROLL
-#define CCV_FWD_UNROLL 8
+#define CCV_FWD_UNROLL 4
 #endif
 #ifndef CCV_BWD_UNROLL
 #define CCV_BWD_UNROLL 4
+#endif
+// Lower bound on resident waves per SIMD (register budget), measured best.
+#ifndef CCV_FWD_MIN_WAVES
+#define CCV_FWD_MIN_WAVES 4
+#endif
+#ifndef CCV_BWD_MIN_WAVES
+#define CCV_BWD_MIN_WAVES 3
+#endif
+#ifdef CCV_FWD_MIN_WAVES
+#define CCV_FWD_ATTR __attribute__((amdgpu_waves_per_eu(CCV_FWD_MIN_WAVES)))
+#else
+#define CCV_FWD_ATTR
+#endif
+#ifdef CCV_BWD_MIN_WAVES
+#define CCV_BWD_ATTR __attribute__((amdgpu_waves_per_eu(CCV_BWD_MIN_WAVES)))
+#else
+#define CCV_BWD_ATTR
 #endif
 
 // ---------------------------------------------------------------------------
@@ -59,55 +78,66 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float a) {
     return static_cast<uint16_t>(pack2_bf16(a, 0.0f) & 0xffffu);
 }
 
-// VEC channels of one token as raw BF16 bits.
+// VEC channels of one token as raw BF16 bits (clang vector types, so the
+// non-temporal builtins apply).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 template <int VEC> struct Raw;
-template <> struct Raw<8> { uint4 v; };
+template <> struct Raw<8> { u32x4_t v; };
+template <> struct Raw<4> { u32x2_t v; };
 template <> struct Raw<1> { uint16_t v; };
 
-template <int VEC>
-__device__ __forceinline__ Raw<VEC> load_raw(const uint16_t *p, int64_t sd);
-template <>
-__device__ __forceinline__ Raw<8> load_raw<8>(const uint16_t *p, int64_t) {
-    return Raw<8>{*reinterpret_cast<const uint4 *>(p)};
-}
-template <>
-__device__ __forceinline__ Raw<1> load_raw<1>(const uint16_t *p, int64_t) {
-    return Raw<1>{*p};
+// Loads and stores of one token's VEC channels.  STREAM selects the
+// non-temporal cache policy for data touched once (the bulk of x, dy, y and
+// dx); halo and state accesses use the default policy so that re-reads of a
+// neighbour chunk's tokens can hit in cache.
+#ifndef CCV_NT_LOAD
+#define CCV_NT_LOAD 1
+#endif
+#ifndef CCV_NT_STORE
+#define CCV_NT_STORE 1
+#endif
+
+template <int VEC, bool STREAM = false>
+__device__ __forceinline__ Raw<VEC> load_raw(const uint16_t *p, int64_t) {
+    using V = decltype(Raw<VEC>::v);
+    const V *q = reinterpret_cast<const V *>(p);
+    if constexpr (STREAM && CCV_NT_LOAD) return Raw<VEC>{__builtin_nontemporal_load(q)};
+    else return Raw<VEC>{*q};
 }
 
 template <int VEC>
-__device__ __forceinline__ void unpack(const Raw<VEC> &r, float (&v)[VEC]);
-template <>
-__device__ __forceinline__ void unpack<8>(const Raw<8> &r, float (&v)[8]) {
-    v[0] = lo_bf16(r.v.x); v[1] = hi_bf16(r.v.x);
-    v[2] = lo_bf16(r.v.y); v[3] = hi_bf16(r.v.y);
-    v[4] = lo_bf16(r.v.z); v[5] = hi_bf16(r.v.z);
-    v[6] = lo_bf16(r.v.w); v[7] = hi_bf16(r.v.w);
-}
-template <>
-__device__ __forceinline__ void unpack<1>(const Raw<1> &r, float (&v)[1]) {
-    v[0] = bf16_bits_to_f32(r.v);
+__device__ __forceinline__ void unpack(const Raw<VEC> &r, float (&v)[VEC]) {
+    if constexpr (VEC == 1) {
+        v[0] = bf16_bits_to_f32(r.v);
+    } else {
+#pragma unroll
+        for (int i = 0; i < VEC / 2; ++i) {
+            v[2 * i] = lo_bf16(r.v[i]);
+            v[2 * i + 1] = hi_bf16(r.v[i]);
+        }
+    }
 }
 
-template <int VEC>
-__device__ __forceinline__ void store_vec(uint16_t *p, int64_t sd, const float (&v)[VEC]);
-template <>
-__device__ __forceinline__ void store_vec<8>(uint16_t *p, int64_t, const float (&v)[8]) {
-    uint4 r;
-    r.x = pack2_bf16(v[0], v[1]);
-    r.y = pack2_bf16(v[2], v[3]);
-    r.z = pack2_bf16(v[4], v[5]);
-    r.w = pack2_bf16(v[6], v[7]);
-    *reinterpret_cast<uint4 *>(p) = r;
-}
-template <>
-__device__ __forceinline__ void store_vec<1>(uint16_t *p, int64_t, const float (&v)[1]) {
-    *p = to_bf16_bits(v[0]);
+template <int VEC, bool STREAM = false>
+__device__ __forceinline__ void store_vec(uint16_t *p, int64_t, const float (&v)[VEC]) {
+    using V = decltype(Raw<VEC>::v);
+    V r;
+    if constexpr (VEC == 1) {
+        r = to_bf16_bits(v[0]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < VEC / 2; ++i) r[i] = pack2_bf16(v[2 * i], v[2 * i + 1]);
+    }
+    V *q = reinterpret_cast<V *>(p);
+    if constexpr (STREAM && CCV_NT_STORE) __builtin_nontemporal_store(r, q);
+    else *q = r;
 }
 
 // ---------------------------------------------------------------------------
 // Activation and its slope.  SiLU(z) = z * s, s = 1 / (1 + e^-z);
-// SiLU'(z) = s * (1 + z (1 - s)).  One v_exp_f32 and one v_rcp_f32 each.
+// SiLU'(z) = s * (1 + z (1 - s)) = s + z (s - s^2).  One v_exp_f32 and one
+// v_rcp_f32 each.
 // ---------------------------------------------------------------------------
 template <bool SILU>
 __device__ __forceinline__ float act(float z) {
@@ -117,8 +147,8 @@ __device__ __forceinline__ float act(float z) {
 template <bool SILU>
 __device__ __forceinline__ float act_slope(float z) {
     if constexpr (SILU) {
-        float s = __builtin_amdgcn_rcpf(1.0f + __expf(-z));
-        return s * fmaf(z, 1.0f - s, 1.0f);
+        const float s = __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+        return fmaf(z, fmaf(-s, s, s), s);
     } else {
         return 1.0f;
     }
@@ -133,47 +163,62 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nb) {
     return x * q + (x < r ? x : r) + j;
 }
 
-// Filter taps and bias of a lane's VEC channels, widened to FP32.
-// `wvec`: the host found the filter contiguous [D,W] and 16-byte aligned.
-template <int VEC>
-__device__ __forceinline__ void load_filter(const void *wp, int64_t sd, int64_t sk, int wf32,
-                                            int wvec, const void *bp, int64_t bs, int64_t c0,
+// Filter kinds: the weight dtype and whether a bias is present.
+enum FilterKind { kBf16 = 0, kBf16Bias = 1, kF32 = 2 };
+
+// Filter taps and bias of a lane's VEC channels, widened to FP32.  With
+// VEC >= 4 the host has verified a contiguous [D,W] filter and a contiguous
+// bias, both 16-byte aligned: every load is a vector load, all issued before
+// the first conversion.
+template <int VEC, int FK>
+__device__ __forceinline__ void load_filter(const void *wp, int64_t sd, int64_t sk,
+                                            const void *bp, int64_t bs, int64_t c0,
                                             float (&w)[W][VEC], float (&bias)[VEC]) {
-    if (wf32) {
-        const float *p = static_cast<const float *>(wp);
-        if (VEC == 8 && wvec) {
-            const float4 *q = reinterpret_cast<const float4 *>(p + c0 * W);
+    if constexpr (VEC >= 4) {
+        constexpr int kWordsPerCh = W * (FK == kF32 ? 4 : 2) / 4;   // 32-bit words per channel
+        constexpr int kVecs = VEC * kWordsPerCh / 4;                  // 16-byte loads
+        const u32x4_t *q = reinterpret_cast<const u32x4_t *>(
+            static_cast<const char *>(wp) + c0 * W * (FK == kF32 ? 4 : 2));
+        u32x4_t wv[kVecs];
 #pragma unroll
-            for (int c = 0; c < VEC; ++c) {
-                float4 t = q[c];
-                w[0][c] = t.x; w[1][c] = t.y; w[2][c] = t.z; w[3][c] = t.w;
+        for (int i = 0; i < kVecs; ++i) wv[i] = q[i];
+        Raw<VEC> bv{};
+        if constexpr (FK == kBf16Bias)
+            bv = load_raw<VEC>(static_cast<const uint16_t *>(bp) + c0, 1);
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) {
+#pragma unroll
+            for (int k = 0; k < W; ++k) {
+                if constexpr (FK == kF32) {
+                    const int e2 = c * W + k;
+                    w[k][c] = __uint_as_float(wv[e2 / 4][e2 % 4]);
+                } else {
+                    const int e2 = c * W + k;  // BF16 element index
+                    const uint32_t word = wv[e2 / 8][(e2 % 8) / 2];
+                    w[k][c] = (e2 % 2) ? hi_bf16(word) : lo_bf16(word);
+                }
             }
+        }
+        if constexpr (FK == kBf16Bias) {
+            unpack<VEC>(bv, bias);
         } else {
 #pragma unroll
-            for (int c = 0; c < VEC; ++c)
-#pragma unroll
-                for (int k = 0; k < W; ++k) w[k][c] = p[(c0 + c) * sd + k * sk];
+            for (int c = 0; c < VEC; ++c) bias[c] = 0.0f;
         }
     } else {
-        const uint16_t *p = static_cast<const uint16_t *>(wp);
-        if (VEC == 8 && wvec) {
-            const uint2 *q = reinterpret_cast<const uint2 *>(p + c0 * W);
 #pragma unroll
-            for (int c = 0; c < VEC; ++c) {
-                uint2 t = q[c];
-                w[0][c] = lo_bf16(t.x); w[1][c] = hi_bf16(t.x);
-                w[2][c] = lo_bf16(t.y); w[3][c] = hi_bf16(t.y);
+        for (int c = 0; c < VEC; ++c) {
+#pragma unroll
+            for (int k = 0; k < W; ++k) {
+                const int64_t off = (c0 + c) * sd + k * sk;
+                w[k][c] = FK == kF32 ? static_cast<const float *>(wp)[off]
+                                     : bf16_bits_to_f32(static_cast<const uint16_t *>(wp)[off]);
             }
-        } else {
-#pragma unroll
-            for (int c = 0; c < VEC; ++c)
-#pragma unroll
-                for (int k = 0; k < W; ++k) w[k][c] = bf16_bits_to_f32(p[(c0 + c) * sd + k * sk]);
+            bias[c] = FK == kBf16Bias
+                          ? bf16_bits_to_f32(static_cast<const uint16_t *>(bp)[(c0 + c) * bs])
+                          : 0.0f;
         }
     }
-#pragma unroll
-    for (int c = 0; c < VEC; ++c)
-        bias[c] = bp ? bf16_bits_to_f32(static_cast<const uint16_t *>(bp)[(c0 + c) * bs]) : 0.0f;
 }
 
 // z = bias + sum_k w[k] * v[k] with v = (win[0..W-2], cur), FP32 fused.
@@ -199,24 +244,41 @@ __device__ __forceinline__ void shift_in(float (&win)[W - 1][VEC], const float (
 
 // Left halo of a piece that starts at position ta of the row [s, e) whose
 // state row is r: x_ext[ta-(W-1) .. ta-1] from the input where inside the
-// row, else from the initial state (slot p - s + W - 1), else zeros.
+// row, else from the initial state (slot p - s + W - 1), else zeros.  The
+// input loads use addresses clamped into the row, so they can be issued
+// early and together (issue_left_halo); finish_left_halo then replaces the
+// values that lie before the row.
 template <int VEC>
-__device__ __forceinline__ void load_left_halo(const uint16_t *xb, int64_t xs_d, int64_t xs_t,
-                                               const Strided3 &init, int64_t r, int64_t s,
-                                               int64_t ta, int64_t c0, float (&win)[W - 1][VEC]) {
+__device__ __forceinline__ void issue_left_halo(const uint16_t *xb, int64_t xs_d, int64_t xs_t,
+                                                int64_t s, int64_t ta, Raw<VEC> (&raw)[W - 1]) {
 #pragma unroll
     for (int j = 0; j < W - 1; ++j) {
         const int64_t p = ta - (W - 1) + j;
-        if (p >= s) {
-            unpack<VEC>(load_raw<VEC>(xb + p * xs_t, xs_d), win[j]);
-        } else if (init.ptr) {
-            const uint16_t *ip = static_cast<const uint16_t *>(init.ptr) + r * init.s0 +
-                                 c0 * init.s1 + (p - s + W - 1) * init.s2;
+        raw[j] = load_raw<VEC>(xb + (p >= s ? p : s) * xs_t, xs_d);
+    }
+}
+
+template <int VEC>
+__device__ __forceinline__ void finish_left_halo(const Raw<VEC> (&raw)[W - 1],
+                                                 const Strided3 &init, int64_t r, int64_t s,
+                                                 int64_t ta, int64_t c0,
+                                                 float (&win)[W - 1][VEC]) {
 #pragma unroll
-            for (int c = 0; c < VEC; ++c) win[j][c] = bf16_bits_to_f32(ip[c * init.s1]);
-        } else {
+    for (int j = 0; j < W - 1; ++j) unpack<VEC>(raw[j], win[j]);
+    if (ta - (W - 1) < s) {
 #pragma unroll
-            for (int c = 0; c < VEC; ++c) win[j][c] = 0.0f;
+        for (int j = 0; j < W - 1; ++j) {
+            const int64_t p = ta - (W - 1) + j;
+            if (p >= s) continue;
+            if (init.ptr) {
+                const uint16_t *ip = static_cast<const uint16_t *>(init.ptr) + r * init.s0 +
+                                     c0 * init.s1 + (p - s + W - 1) * init.s2;
+#pragma unroll
+                for (int c = 0; c < VEC; ++c) win[j][c] = bf16_bits_to_f32(ip[c * init.s1]);
+            } else {
+#pragma unroll
+                for (int c = 0; c < VEC; ++c) win[j][c] = 0.0f;
+            }
         }
     }
 }
@@ -270,7 +332,7 @@ __device__ __forceinline__ int64_t find_row(const int32_t *cu, int64_t n, int64_
 // ===========================================================================
 // Forward
 // ===========================================================================
-template <int VEC, bool SILU>
+template <int VEC, bool SILU, bool NTL>
 __device__ __forceinline__ void fwd_piece(const FwdArgs &a, int64_t b, int64_t r, int64_t s,
                                           int64_t e, int64_t ta, int64_t tb, int64_t c0,
                                           const float (&w)[W][VEC], const float (&bias)[VEC]) {
@@ -278,31 +340,47 @@ __device__ __forceinline__ void fwd_piece(const FwdArgs &a, int64_t b, int64_t r
     const uint16_t *xb = static_cast<const uint16_t *>(a.x.ptr) + b * a.x.s0 + c0 * a.x.s1;
     uint16_t *yb = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.y.ptr)) + b * a.y.s0 +
                    c0 * a.y.s1;
-    const int64_t xs_t = a.x.s2, ys_t = a.y.s2;
+    const int64_t xs_t = a.x.s2, ys_t = a.y.s2, xs_d = a.x.s1, ys_d = a.y.s1;
     float win[W - 1][VEC];
-    load_left_halo<VEC>(xb, a.x.s1, xs_t, a.init, r, s, ta, c0, win);
 
-    int64_t t = ta;
-    for (; t + U <= tb; t += U) {
-        Raw<VEC> raw[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) raw[u] = load_raw<VEC>(xb + (t + u) * xs_t, a.x.s1);
+    auto run_batch = [&](int64_t t, const Raw<VEC> (&raw)[U]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float cur[VEC], out[VEC];
             unpack<VEC>(raw[u], cur);
 #pragma unroll
             for (int c = 0; c < VEC; ++c) out[c] = act<SILU>(preact<VEC>(w, bias, win, cur, c));
-            store_vec<VEC>(yb + (t + u) * ys_t, a.y.s1, out);
+            store_vec<VEC, true>(yb + (t + u) * ys_t, ys_d, out);
             shift_in<VEC>(win, cur);
         }
+    };
+
+    // The halo loads go out together with the first batch's.
+    Raw<VEC> halo[W - 1];
+    issue_left_halo<VEC>(xb, xs_d, xs_t, s, ta, halo);
+    int64_t t = ta;
+    if (t + U <= tb) {
+        Raw<VEC> raw[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) raw[u] = load_raw<VEC, NTL>(xb + (t + u) * xs_t, xs_d);
+        finish_left_halo<VEC>(halo, a.init, r, s, ta, c0, win);
+        run_batch(t, raw);
+        t += U;
+    } else {
+        finish_left_halo<VEC>(halo, a.init, r, s, ta, c0, win);
+    }
+    for (; t + U <= tb; t += U) {
+        Raw<VEC> raw[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) raw[u] = load_raw<VEC, NTL>(xb + (t + u) * xs_t, xs_d);
+        run_batch(t, raw);
     }
     for (; t < tb; ++t) {
         float cur[VEC], out[VEC];
-        unpack<VEC>(load_raw<VEC>(xb + t * xs_t, a.x.s1), cur);
+        unpack<VEC>(load_raw<VEC, NTL>(xb + t * xs_t, xs_d), cur);
 #pragma unroll
         for (int c = 0; c < VEC; ++c) out[c] = act<SILU>(preact<VEC>(w, bias, win, cur, c));
-        store_vec<VEC>(yb + t * ys_t, a.y.s1, out);
+        store_vec<VEC, true>(yb + t * ys_t, ys_d, out);
         shift_in<VEC>(win, cur);
     }
     // The row ends inside this piece: its last W-1 extended tokens are the
@@ -318,8 +396,8 @@ __device__ __forceinline__ void fwd_piece(const FwdArgs &a, int64_t b, int64_t r
     }
 }
 
-template <int VEC, bool SILU, bool PACKED>
-__global__ __launch_bounds__(256) void k_fwd_chan(FwdArgs a) {
+template <int VEC, bool SILU, bool PACKED, int FK>
+__global__ __launch_bounds__(256) CCV_FWD_ATTR void k_fwd_chan(FwdArgs a) {
     __shared__ int32_t s_cu[PACKED ? kLdsCuMax : 1];
     __shared__ uint32_t s_bad;
     const int64_t tile = xcd_remap(blockIdx.x, a.n_block);
@@ -339,18 +417,25 @@ __global__ __launch_bounds__(256) void k_fwd_chan(FwdArgs a) {
     const int64_t t1 = min(t0 + a.L, a.T);
 
     float w[W][VEC], bias[VEC];
-    load_filter<VEC>(a.w, a.w_sd, a.w_sk, a.w_f32, a.w_vec, a.bias, a.b_s, c0, w, bias);
+    load_filter<VEC, FK>(a.w, a.w_sd, a.w_sk, a.bias, a.b_s, c0, w, bias);
 
-    if constexpr (!PACKED) {
-        fwd_piece<VEC, SILU>(a, b, b, 0, a.T, t0, t1, c0, w, bias);
-    } else {
-        const int32_t *cu = a.cu_in_lds ? s_cu : a.cu;
-        for (int64_t i = find_row(cu, a.n_seq, t0); i < a.n_seq; ++i) {
-            const int64_t s = cu[i], e = cu[i + 1];
-            if (s >= t1) break;
-            fwd_piece<VEC, SILU>(a, 0, i, s, e, s > t0 ? s : t0, e < t1 ? e : t1, c0, w, bias);
+    // Non-temporal loads only when the operands exceed what caches can keep.
+    auto run = [&](auto ntl) {
+        constexpr bool NTL = decltype(ntl)::value;
+        if constexpr (!PACKED) {
+            fwd_piece<VEC, SILU, NTL>(a, b, b, 0, a.T, t0, t1, c0, w, bias);
+        } else {
+            const int32_t *cu = a.cu_in_lds ? s_cu : a.cu;
+            for (int64_t i = find_row(cu, a.n_seq, t0); i < a.n_seq; ++i) {
+                const int64_t s = cu[i], e = cu[i + 1];
+                if (s >= t1) break;
+                fwd_piece<VEC, SILU, NTL>(a, 0, i, s, e, s > t0 ? s : t0, e < t1 ? e : t1, c0,
+                                          w, bias);
+            }
         }
-    }
+    };
+    if (a.nt_load) run(std::true_type{});
+    else run(std::false_type{});
 }
 
 // ===========================================================================
@@ -371,7 +456,7 @@ struct BwdLane {
     float dw[W][VEC], db[VEC];
 };
 
-template <int VEC, bool SILU, bool BIAS>
+template <int VEC, bool SILU, bool BIAS, bool NTL>
 __device__ __forceinline__ void bwd_piece(const BwdArgs &a, BwdLane<VEC, SILU, BIAS> &L,
                                           int64_t b, int64_t r, int64_t s, int64_t e,
                                           int64_t ta, int64_t tb, int64_t c0) {
@@ -384,7 +469,6 @@ __device__ __forceinline__ void bwd_piece(const BwdArgs &a, BwdLane<VEC, SILU, B
     const int64_t ds_d = a.dx.s1, ds_t = a.dx.s2;
 
     float xw[W - 1][VEC], gw[W - 1][VEC];
-    load_left_halo<VEC>(xb, xs_d, xs_t, a.init, r, s, ta, c0, xw);
 #pragma unroll
     for (int j = 0; j < W - 1; ++j)
 #pragma unroll
@@ -409,6 +493,7 @@ __device__ __forceinline__ void bwd_piece(const BwdArgs &a, BwdLane<VEC, SILU, B
         for (int c = 0; c < VEC; ++c) gw[W - 2][c] = gcur[c];
     };
     // g at tau from (xw, cur, dy); accumulates dW/dB when `count`.
+    // SiLU'(z) = s + z s (1 - s), with s (1 - s) formed as s - s^2.
     auto grad_step = [&](const float (&cur)[VEC], const float (&dyv)[VEC], float (&gcur)[VEC],
                          bool count) {
 #pragma unroll
@@ -426,13 +511,13 @@ __device__ __forceinline__ void bwd_piece(const BwdArgs &a, BwdLane<VEC, SILU, B
             }
         }
     };
-    // Fully checked step (head and tail of a piece).
-    auto generic_step = [&](int64_t tau) {
+    // Fully checked step (head and tail of a piece) on preloaded tokens.
+    auto generic_step = [&](int64_t tau, const Raw<VEC> &rxv, const Raw<VEC> &rdv) {
         float gcur[VEC];
         if (tau < e) {
             float cur[VEC], dyv[VEC];
-            unpack<VEC>(load_raw<VEC>(xb + tau * xs_t, xs_d), cur);
-            unpack<VEC>(load_raw<VEC>(dyb + tau * ys_t, ys_d), dyv);
+            unpack<VEC>(rxv, cur);
+            unpack<VEC>(rdv, dyv);
             grad_step(cur, dyv, gcur, tau < tb);
             shift_in<VEC>(xw, cur);
         } else {
@@ -462,20 +547,19 @@ __device__ __forceinline__ void bwd_piece(const BwdArgs &a, BwdLane<VEC, SILU, B
         }
         shift_g(gcur);
     };
-
-    // Head: tau in [ta, ta + W-1).
+    // x and dy of the W-1 steps from tau0, addresses clamped into the row so
+    // that the loads can be issued together (values past the row are unused).
+    auto load_steps = [&](int64_t tau0, Raw<VEC> (&rx)[W - 1], Raw<VEC> (&rd)[W - 1]) {
 #pragma unroll
-    for (int h = 0; h < W - 1; ++h) generic_step(ta + h);
-    // Body: tau in [ta + W-1, tb): inside the row, emits dx[tau-(W-1)] with
-    // no final-state term (tau - (W-1) < e - (W-1)).
-    int64_t tau = ta + (W - 1);
-    for (; tau + U <= tb; tau += U) {
-        Raw<VEC> rx[U], rd[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            rx[u] = load_raw<VEC>(xb + (tau + u) * xs_t, xs_d);
-            rd[u] = load_raw<VEC>(dyb + (tau + u) * ys_t, ys_d);
+        for (int h = 0; h < W - 1; ++h) {
+            const int64_t tc = tau0 + h < e ? tau0 + h : e - 1;
+            rx[h] = load_raw<VEC>(xb + tc * xs_t, xs_d);
+            rd[h] = load_raw<VEC>(dyb + tc * ys_t, ys_d);
         }
+    };
+    // Body step: inside the row, emits dx[tau-(W-1)] with no final-state
+    // term (tau - (W-1) < e - (W-1)).
+    auto body_batch = [&](int64_t tau, const Raw<VEC> (&rx)[U], const Raw<VEC> (&rd)[U]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float cur[VEC], dyv[VEC], gcur[VEC], v[VEC];
@@ -484,26 +568,66 @@ __device__ __forceinline__ void bwd_piece(const BwdArgs &a, BwdLane<VEC, SILU, B
             grad_step(cur, dyv, gcur, true);
             shift_in<VEC>(xw, cur);
             emit_value(gcur, v);
-            store_vec<VEC>(dxb + (tau + u - (W - 1)) * ds_t, ds_d, v);
+            store_vec<VEC, true>(dxb + (tau + u - (W - 1)) * ds_t, ds_d, v);
             shift_g(gcur);
         }
+    };
+    auto load_batch = [&](int64_t tau, Raw<VEC> (&rx)[U], Raw<VEC> (&rd)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            rx[u] = load_raw<VEC, NTL>(xb + (tau + u) * xs_t, xs_d);
+            rd[u] = load_raw<VEC, NTL>(dyb + (tau + u) * ys_t, ys_d);
+        }
+    };
+
+    // Prologue: the left halo, the head (tau in [ta, ta + W-1)) and the first
+    // body batch are all requested before anything waits.
+    Raw<VEC> halo[W - 1], hx[W - 1], hd[W - 1];
+    issue_left_halo<VEC>(xb, xs_d, xs_t, s, ta, halo);
+    load_steps(ta, hx, hd);
+    int64_t tau = ta + (W - 1);
+    if (tau + U <= tb) {
+        Raw<VEC> rx[U], rd[U];
+        load_batch(tau, rx, rd);
+        finish_left_halo<VEC>(halo, a.init, r, s, ta, c0, xw);
+#pragma unroll
+        for (int h = 0; h < W - 1; ++h) generic_step(ta + h, hx[h], hd[h]);
+        body_batch(tau, rx, rd);
+        tau += U;
+    } else {
+        finish_left_halo<VEC>(halo, a.init, r, s, ta, c0, xw);
+#pragma unroll
+        for (int h = 0; h < W - 1; ++h) generic_step(ta + h, hx[h], hd[h]);
+    }
+    for (; tau + U <= tb; tau += U) {
+        Raw<VEC> rx[U], rd[U];
+        load_batch(tau, rx, rd);
+        body_batch(tau, rx, rd);
     }
     for (; tau < tb; ++tau) {
         float cur[VEC], dyv[VEC], gcur[VEC], v[VEC];
-        unpack<VEC>(load_raw<VEC>(xb + tau * xs_t, xs_d), cur);
-        unpack<VEC>(load_raw<VEC>(dyb + tau * ys_t, ys_d), dyv);
+        unpack<VEC>(load_raw<VEC, NTL>(xb + tau * xs_t, xs_d), cur);
+        unpack<VEC>(load_raw<VEC, NTL>(dyb + tau * ys_t, ys_d), dyv);
         grad_step(cur, dyv, gcur, true);
         shift_in<VEC>(xw, cur);
         emit_value(gcur, v);
-        store_vec<VEC>(dxb + (tau - (W - 1)) * ds_t, ds_d, v);
+        store_vec<VEC, true>(dxb + (tau - (W - 1)) * ds_t, ds_d, v);
         shift_g(gcur);
     }
-    // Tail: tau in [max(tb, ta + W-1), tb + W-1).
-    for (tau = tb > ta + (W - 1) ? tb : ta + (W - 1); tau < tb + (W - 1); ++tau) generic_step(tau);
+    // Tail: tau in [max(tb, ta + W-1), tb + W-1): at most W-1 steps.
+    {
+        const int64_t tt = tb > ta + (W - 1) ? tb : ta + (W - 1);
+        Raw<VEC> rx[W - 1], rd[W - 1];
+        load_steps(tt, rx, rd);
+#pragma unroll
+        for (int h = 0; h < W - 1; ++h)
+            if (tt + h < tb + (W - 1)) generic_step(tt + h, rx[h], rd[h]);
+    }
 }
 
-template <int VEC, bool SILU, bool PACKED, bool BIAS>
-__global__ __launch_bounds__(256) void k_bwd_chan(BwdArgs a) {
+template <int VEC, bool SILU, bool PACKED, int FK>
+__global__ __launch_bounds__(256) CCV_BWD_ATTR void k_bwd_chan(BwdArgs a) {
+    constexpr bool BIAS = FK == kBf16Bias;
     constexpr int CH = kWaveSize * VEC;  // channels of a block
     // One LDS buffer: the staged offsets during the walk, then the dW/dB
     // reduction (a barrier separates the two uses).
@@ -536,17 +660,23 @@ __global__ __launch_bounds__(256) void k_bwd_chan(BwdArgs a) {
     }
     if (t0 < a.T && c0 < a.D) {
         const int64_t t1 = min(t0 + a.L, a.T);
-        load_filter<VEC>(a.w, a.w_sd, a.w_sk, a.w_f32, a.w_vec, a.bias, a.b_s, c0, L.w, L.bias);
-        if constexpr (!PACKED) {
-            bwd_piece<VEC, SILU, BIAS>(a, L, b, b, 0, a.T, t0, t1, c0);
-        } else {
-            const int32_t *cu = a.cu_in_lds ? s_cu : a.cu;
-            for (int64_t i = find_row(cu, a.n_seq, t0); i < a.n_seq; ++i) {
-                const int64_t s = cu[i], e = cu[i + 1];
-                if (s >= t1) break;
-                bwd_piece<VEC, SILU, BIAS>(a, L, 0, i, s, e, s > t0 ? s : t0, e < t1 ? e : t1, c0);
+        load_filter<VEC, FK>(a.w, a.w_sd, a.w_sk, a.bias, a.b_s, c0, L.w, L.bias);
+        auto run = [&](auto ntl) {
+            constexpr bool NTL = decltype(ntl)::value;
+            if constexpr (!PACKED) {
+                bwd_piece<VEC, SILU, BIAS, NTL>(a, L, b, b, 0, a.T, t0, t1, c0);
+            } else {
+                const int32_t *cu = a.cu_in_lds ? s_cu : a.cu;
+                for (int64_t i = find_row(cu, a.n_seq, t0); i < a.n_seq; ++i) {
+                    const int64_t s = cu[i], e = cu[i + 1];
+                    if (s >= t1) break;
+                    bwd_piece<VEC, SILU, BIAS, NTL>(a, L, 0, i, s, e, s > t0 ? s : t0,
+                                                    e < t1 ? e : t1, c0);
+                }
             }
-        }
+        };
+        if (a.nt_load) run(std::true_type{});
+        else run(std::false_type{});
     }
 
     // dW/dB: the block's waves cover the same channels over consecutive
@@ -584,50 +714,89 @@ __global__ __launch_bounds__(256) void k_bwd_chan(BwdArgs a) {
 
 // ===========================================================================
 // Single-token update (in place on the [B,D,W-1] state)
+//
+// One lane per VEC channels of one batch row.  With VEC = 8 the host has
+// verified unit channel strides, a contiguous [B,D,W-1] state, a contiguous
+// [D,W] filter and 16-byte alignment, so a lane's state is 3 x 16 contiguous
+// bytes and every load below is issued before the first wait.
 // ===========================================================================
-template <int VEC, bool SILU>
-__global__ __launch_bounds__(256) void k_update(UpdArgs a) {
+#ifndef CCV_UPD_MAX_WAVES
+#define CCV_UPD_MAX_WAVES 4
+#endif
+#ifndef CCV_UPD_NT
+#define CCV_UPD_NT 0
+#endif
+// The register budget of up to CCV_UPD_MAX_WAVES waves per SIMD leaves room
+// for every load of a lane to be in flight at once.
+template <int VEC, bool SILU, bool WF32, bool BIAS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, CCV_UPD_MAX_WAVES)))
+void k_update(UpdArgs a) {
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t b = gid / a.n_lane_per_row;
     if (b >= a.B) return;
     const int64_t c0 = (gid % a.n_lane_per_row) * VEC;
-
-    float w[W][VEC], bias[VEC];
-    load_filter<VEC>(a.w, a.w_sd, a.w_sk, a.w_f32, a.w_vec, a.bias, a.b_s, c0, w, bias);
     const uint16_t *xp = static_cast<const uint16_t *>(a.x) + b * a.x_sb + c0 * a.x_sd;
     uint16_t *sp = static_cast<uint16_t *>(a.state) + b * a.s_sb + c0 * a.s_sd;
     uint16_t *yp = static_cast<uint16_t *>(a.y) + b * a.y_sb + c0 * a.y_sd;
 
-    // Raw bits: the shifted state is a copy, never re-rounded.
+    // Raw bits: the shifted state is a copy of them, never re-rounded.
     uint16_t st[VEC][W - 1], xr[VEC];
-    // VEC == 8: the host verified unit channel strides, a contiguous
-    // [B,D,W-1] state and 16-byte alignment of every row.
+    float w[W][VEC], bias[VEC];
     if constexpr (VEC == 8) {
-        // The lane's VEC*(W-1) state values are contiguous: 3 x 16 bytes.
-        const uint4 *q = reinterpret_cast<const uint4 *>(sp);
-        uint32_t words[VEC * (W - 1) / 2];
+        constexpr int kStateVecs = VEC * (W - 1) / 8;      // 16-byte vectors of state
+        constexpr int kFilterVecs = VEC * W * (WF32 ? 4 : 2) / 16;
+        const u32x4_t *sq = reinterpret_cast<const u32x4_t *>(sp);
+        const u32x4_t *wq = reinterpret_cast<const u32x4_t *>(
+            static_cast<const char *>(a.w) + c0 * W * (WF32 ? 4 : 2));
+        u32x4_t sv[kStateVecs], wv[kFilterVecs], xv, bv;
 #pragma unroll
-        for (int i = 0; i < VEC * (W - 1) / 8; ++i) {
-            uint4 t = q[i];
-            words[4 * i] = t.x; words[4 * i + 1] = t.y; words[4 * i + 2] = t.z; words[4 * i + 3] = t.w;
-        }
+        for (int i = 0; i < kStateVecs; ++i) sv[i] = CCV_UPD_NT ? __builtin_nontemporal_load(sq + i) : sq[i];
+        xv = CCV_UPD_NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(xp))
+                        : *reinterpret_cast<const u32x4_t *>(xp);
+#pragma unroll
+        for (int i = 0; i < kFilterVecs; ++i) wv[i] = wq[i];
+        if constexpr (BIAS) bv = *reinterpret_cast<const u32x4_t *>(
+                                  static_cast<const uint16_t *>(a.bias) + c0);
 #pragma unroll
         for (int e2 = 0; e2 < VEC * (W - 1); ++e2)
-            st[e2 / (W - 1)][e2 % (W - 1)] = static_cast<uint16_t>(words[e2 / 2] >> (16 * (e2 % 2)));
+            st[e2 / (W - 1)][e2 % (W - 1)] =
+                static_cast<uint16_t>(sv[e2 / 8][(e2 % 8) / 2] >> (16 * (e2 % 2)));
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) xr[c] = static_cast<uint16_t>(xv[c / 2] >> (16 * (c % 2)));
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) {
+#pragma unroll
+            for (int k = 0; k < W; ++k) {
+                const int e2 = c * W + k;
+                if constexpr (WF32) {
+                    w[k][c] = __uint_as_float(wv[e2 / 4][e2 % 4]);
+                } else {
+                    const uint32_t word = wv[e2 / 8][(e2 % 8) / 2];
+                    w[k][c] = (e2 % 2) ? hi_bf16(word) : lo_bf16(word);
+                }
+            }
+            if constexpr (BIAS) {
+                const uint32_t word = bv[c / 2];
+                bias[c] = (c % 2) ? hi_bf16(word) : lo_bf16(word);
+            } else {
+                bias[c] = 0.0f;
+            }
+        }
     } else {
 #pragma unroll
-        for (int c = 0; c < VEC; ++c)
+        for (int c = 0; c < VEC; ++c) {
 #pragma unroll
             for (int j = 0; j < W - 1; ++j) st[c][j] = sp[c * a.s_sd + j * a.s_sj];
-    }
-    if constexpr (VEC == 8) {
-        uint4 t = *reinterpret_cast<const uint4 *>(xp);
-        const uint32_t words[4] = {t.x, t.y, t.z, t.w};
+            xr[c] = xp[c * a.x_sd];
 #pragma unroll
-        for (int c = 0; c < VEC; ++c) xr[c] = static_cast<uint16_t>(words[c / 2] >> (16 * (c % 2)));
-    } else {
-#pragma unroll
-        for (int c = 0; c < VEC; ++c) xr[c] = xp[c * a.x_sd];
+            for (int k = 0; k < W; ++k) {
+                const int64_t off = (c0 + c) * a.w_sd + k * a.w_sk;
+                w[k][c] = WF32 ? static_cast<const float *>(a.w)[off]
+                               : bf16_bits_to_f32(static_cast<const uint16_t *>(a.w)[off]);
+            }
+            bias[c] = BIAS ? bf16_bits_to_f32(static_cast<const uint16_t *>(a.bias)[(c0 + c) * a.b_s])
+                           : 0.0f;
+        }
     }
 
     float out[VEC];
@@ -639,12 +808,6 @@ __global__ __launch_bounds__(256) void k_update(UpdArgs a) {
         z = fmaf(w[W - 1][c], bf16_bits_to_f32(xr[c]), z);
         out[c] = act<SILU>(z);
     }
-    if constexpr (VEC == 8) {
-        store_vec<VEC>(yp, 1, out);
-    } else {
-#pragma unroll
-        for (int c = 0; c < VEC; ++c) yp[c * a.y_sd] = to_bf16_bits(out[c]);
-    }
     // New state (s_1 .. s_{W-2}, x).
     uint16_t ns[VEC][W - 1];
 #pragma unroll
@@ -654,22 +817,28 @@ __global__ __launch_bounds__(256) void k_update(UpdArgs a) {
         ns[c][W - 2] = xr[c];
     }
     if constexpr (VEC == 8) {
-        uint32_t words[VEC * (W - 1) / 2];
+        store_vec<VEC, true>(yp, 1, out);
+        constexpr int kStateVecs = VEC * (W - 1) / 8;
+        u32x4_t sv[kStateVecs];
 #pragma unroll
         for (int i = 0; i < VEC * (W - 1) / 2; ++i) {
             const int e0 = 2 * i, e1 = 2 * i + 1;
-            words[i] = static_cast<uint32_t>(ns[e0 / (W - 1)][e0 % (W - 1)]) |
-                       (static_cast<uint32_t>(ns[e1 / (W - 1)][e1 % (W - 1)]) << 16);
+            sv[i / 4][i % 4] = static_cast<uint32_t>(ns[e0 / (W - 1)][e0 % (W - 1)]) |
+                               (static_cast<uint32_t>(ns[e1 / (W - 1)][e1 % (W - 1)]) << 16);
         }
-        uint4 *q = reinterpret_cast<uint4 *>(sp);
+        u32x4_t *sq = reinterpret_cast<u32x4_t *>(sp);
 #pragma unroll
-        for (int i = 0; i < VEC * (W - 1) / 8; ++i)
-            q[i] = make_uint4(words[4 * i], words[4 * i + 1], words[4 * i + 2], words[4 * i + 3]);
+        for (int i = 0; i < kStateVecs; ++i) {
+            if (CCV_UPD_NT) __builtin_nontemporal_store(sv[i], sq + i);
+            else sq[i] = sv[i];
+        }
     } else {
 #pragma unroll
-        for (int c = 0; c < VEC; ++c)
+        for (int c = 0; c < VEC; ++c) {
+            yp[c * a.y_sd] = to_bf16_bits(out[c]);
 #pragma unroll
             for (int j = 0; j < W - 1; ++j) sp[c * a.s_sd + j * a.s_sj] = ns[c][j];
+        }
     }
 }
 
@@ -710,6 +879,9 @@ __global__ __launch_bounds__(256) void k_dw_reduce(const float *part, int64_t n_
     out[e] += acc;
 }
 
+// A stream value that never names a real stream: dispatch without launching.
+hipStream_t const kQueryStream = reinterpret_cast<hipStream_t>(~uintptr_t(0));
+
 template <typename K, typename A>
 hipError_t launch(K kernel, int64_t blocks, const A &args, hipStream_t s) {
     if (blocks <= 0) return hipSuccess;
@@ -719,37 +891,109 @@ hipError_t launch(K kernel, int64_t blocks, const A &args, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_fwd(const FwdArgs &a, int vec, int silu, int packed, hipStream_t s) {
-#define CCV_FWD(V, S, P) \
-    if (vec == V && !!silu == S && !!packed == P) return launch(k_fwd_chan<V, S, P>, a.n_block, a, s);
-    CCV_FWD(8, true, false) CCV_FWD(8, true, true) CCV_FWD(8, false, false) CCV_FWD(8, false, true)
-    CCV_FWD(1, true, false) CCV_FWD(1, true, true) CCV_FWD(1, false, false) CCV_FWD(1, false, true)
+// Filter kind of an argument block (see FilterKind).
+template <typename A>
+int filter_kind(const A &a) {
+    return a.w_f32 ? kF32 : (a.bias != nullptr ? kBf16Bias : kBf16);
+}
+
+// Resident blocks of a kernel on the current device (CUs x blocks per CU),
+// from the occupancy the compiled kernel allows; 0 when it cannot be told.
+int64_t resident_blocks(const void *kernel) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess)
+        return 0;
+    return static_cast<int64_t>(cus) * per_cu;
+}
+
+template <int V, bool S, bool P, int F>
+hipError_t fwd_one(const FwdArgs &a, hipStream_t s) {
+    if (s == kQueryStream) return hipSuccess;
+    return launch(k_fwd_chan<V, S, P, F>, a.n_block, a, s);
+}
+
+template <int V>
+hipError_t fwd_vec(const FwdArgs &a, int silu, int packed, int fk, hipStream_t s, int64_t *cap) {
+#define CCV_FWD(S, P, F)                                                                   \
+    if (!!silu == S && !!packed == P && fk == F) {                                         \
+        if (cap) *cap = resident_blocks(reinterpret_cast<const void *>(k_fwd_chan<V, S, P, F>)); \
+        return fwd_one<V, S, P, F>(a, s);                                                  \
+    }
+#define CCV_FWD_K(S, P) CCV_FWD(S, P, kBf16) CCV_FWD(S, P, kBf16Bias) CCV_FWD(S, P, kF32)
+    CCV_FWD_K(true, false) CCV_FWD_K(true, true) CCV_FWD_K(false, false) CCV_FWD_K(false, true)
+#undef CCV_FWD_K
 #undef CCV_FWD
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd(const BwdArgs &a, int vec, int silu, int packed, hipStream_t s) {
-    const bool bias = a.db != nullptr;
-#define CCV_BWD(V, S, P, B)                                            \
-    if (vec == V && !!silu == S && !!packed == P && bias == B) \
-        return launch(k_bwd_chan<V, S, P, B>, a.n_block, a, s);
-    CCV_BWD(8, true, false, true) CCV_BWD(8, true, false, false)
-    CCV_BWD(8, true, true, true) CCV_BWD(8, true, true, false)
-    CCV_BWD(8, false, false, true) CCV_BWD(8, false, false, false)
-    CCV_BWD(8, false, true, true) CCV_BWD(8, false, true, false)
-    CCV_BWD(1, true, false, true) CCV_BWD(1, true, false, false)
-    CCV_BWD(1, true, true, true) CCV_BWD(1, true, true, false)
-    CCV_BWD(1, false, false, true) CCV_BWD(1, false, false, false)
-    CCV_BWD(1, false, true, true) CCV_BWD(1, false, true, false)
+hipError_t launch_fwd(const FwdArgs &a, int vec, int silu, int packed, hipStream_t s) {
+    const int fk = filter_kind(a);
+    if (vec == 8) return fwd_vec<8>(a, silu, packed, fk, s, nullptr);
+    if (vec == 4) return fwd_vec<4>(a, silu, packed, fk, s, nullptr);
+    if (vec == 1) return fwd_vec<1>(a, silu, packed, fk, s, nullptr);
+    return hipErrorInvalidValue;
+}
+
+int64_t fwd_resident_blocks(const FwdArgs &a, int vec, int silu, int packed) {
+    const int fk = filter_kind(a);
+    int64_t cap = 0;
+    if (vec == 8) fwd_vec<8>(a, silu, packed, fk, kQueryStream, &cap);
+    if (vec == 4) fwd_vec<4>(a, silu, packed, fk, kQueryStream, &cap);
+    if (vec == 1) fwd_vec<1>(a, silu, packed, fk, kQueryStream, &cap);
+    return cap;
+}
+
+template <int V, bool S, bool P, int F>
+hipError_t bwd_one(const BwdArgs &a, hipStream_t s) {
+    if (s == kQueryStream) return hipSuccess;
+    return launch(k_bwd_chan<V, S, P, F>, a.n_block, a, s);
+}
+
+template <int V>
+hipError_t bwd_vec(const BwdArgs &a, int silu, int packed, int fk, hipStream_t s, int64_t *cap) {
+#define CCV_BWD(S, P, F)                                                                   \
+    if (!!silu == S && !!packed == P && fk == F) {                                         \
+        if (cap) *cap = resident_blocks(reinterpret_cast<const void *>(k_bwd_chan<V, S, P, F>)); \
+        return bwd_one<V, S, P, F>(a, s);                                                  \
+    }
+#define CCV_BWD_K(S, P) CCV_BWD(S, P, kBf16) CCV_BWD(S, P, kBf16Bias) CCV_BWD(S, P, kF32)
+    CCV_BWD_K(true, false) CCV_BWD_K(true, true) CCV_BWD_K(false, false) CCV_BWD_K(false, true)
+#undef CCV_BWD_K
 #undef CCV_BWD
     return hipErrorInvalidValue;
+}
+
+// Backward lanes own 4 channels (or 1): with 8, the window, gradient window
+// and dW accumulators leave too few registers for latency hiding.
+hipError_t launch_bwd(const BwdArgs &a, int vec, int silu, int packed, hipStream_t s) {
+    const int fk = filter_kind(a);
+    if (vec == 4) return bwd_vec<4>(a, silu, packed, fk, s, nullptr);
+    if (vec == 1) return bwd_vec<1>(a, silu, packed, fk, s, nullptr);
+    return hipErrorInvalidValue;
+}
+
+int64_t bwd_resident_blocks(const BwdArgs &a, int vec, int silu, int packed) {
+    const int fk = filter_kind(a);
+    int64_t cap = 0;
+    if (vec == 4) bwd_vec<4>(a, silu, packed, fk, kQueryStream, &cap);
+    if (vec == 1) bwd_vec<1>(a, silu, packed, fk, kQueryStream, &cap);
+    return cap;
 }
 
 hipError_t launch_update(const UpdArgs &a, int vec, int silu, hipStream_t s) {
     const int64_t lanes = a.B * a.n_lane_per_row;
     const int64_t blocks = (lanes + 255) / 256;
-    if (vec == 8) return silu ? launch(k_update<8, true>, blocks, a, s) : launch(k_update<8, false>, blocks, a, s);
-    if (vec == 1) return silu ? launch(k_update<1, true>, blocks, a, s) : launch(k_update<1, false>, blocks, a, s);
+    const bool wf32 = a.w_f32 != 0, bias = a.bias != nullptr;
+#define CCV_UPD(V, S, F, B) \
+    if (vec == V && !!silu == S && wf32 == F && bias == B) return launch(k_update<V, S, F, B>, blocks, a, s);
+    CCV_UPD(8, true, false, true) CCV_UPD(8, true, false, false) CCV_UPD(8, true, true, false)
+    CCV_UPD(8, false, false, true) CCV_UPD(8, false, false, false) CCV_UPD(8, false, true, false)
+    CCV_UPD(1, true, false, true) CCV_UPD(1, true, false, false) CCV_UPD(1, true, true, false)
+    CCV_UPD(1, false, false, true) CCV_UPD(1, false, false, false) CCV_UPD(1, false, true, false)
+#undef CCV_UPD
     return hipErrorInvalidValue;
 }
 
