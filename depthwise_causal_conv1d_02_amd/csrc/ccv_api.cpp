@@ -242,21 +242,23 @@ bool any_alias(const Span *outs, int n_out, const Span *ins, int n_in) {
 // block capacity known, L makes the grid `rounds` whole rounds of resident
 // blocks, so that no last round runs partly empty.  Otherwise L aims for
 // `target_waves` waves.  Never fewer than `min_chunk` steps per wave.
+// A block holds `wt` waves along time times `wc` waves along channel groups.
 struct Geometry {
-    int64_t L, n_chunk, n_tblk, n_group, n_block;
+    int64_t L, n_chunk, n_tblk, n_group, n_gblk, n_block;
 };
 
-Geometry geometry(const Problem &p, int vec, int64_t capacity, int rounds, int64_t target_waves,
-                  int64_t min_chunk) {
+Geometry geometry(const Problem &p, int vec, int wt, int wc, int64_t capacity, int rounds,
+                  int64_t target_waves, int64_t min_chunk) {
     Geometry g;
     g.n_group = (p.D + ccv::kWaveSize * vec - 1) / (ccv::kWaveSize * vec);
+    g.n_gblk = (g.n_group + wc - 1) / wc;
     const int64_t rows = p.packed ? 1 : p.B;
     const int64_t work = rows * g.n_group * p.T;
     int64_t L = 0;
     if (capacity > 0 && rounds > 0) {
-        const int64_t per_row_group = capacity * rounds / (rows * g.n_group);
-        if (per_row_group >= 1) {
-            const int64_t chunks = per_row_group * ccv::kWavesPerBlock;
+        const int64_t per_row_gblk = capacity * rounds / (rows * g.n_gblk);
+        if (per_row_gblk >= 1) {
+            const int64_t chunks = per_row_gblk * wt;
             L = (p.T + chunks - 1) / chunks;
         }
     }
@@ -267,8 +269,8 @@ Geometry geometry(const Problem &p, int vec, int64_t capacity, int rounds, int64
     L = std::max<int64_t>(min_chunk, std::min<int64_t>(CCV_MAX_CHUNK, L));
     g.L = L;
     g.n_chunk = (p.T + L - 1) / L;
-    g.n_tblk = (g.n_chunk + ccv::kWavesPerBlock - 1) / ccv::kWavesPerBlock;
-    g.n_block = rows * g.n_group * g.n_tblk;
+    g.n_tblk = (g.n_chunk + wt - 1) / wt;
+    g.n_block = rows * g.n_gblk * g.n_tblk;
     return g;
 }
 
@@ -330,8 +332,8 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     a.err = p.packed ? err_flag : nullptr;
     const int silu = activation == CCV_ACT_SILU;
     const int64_t cap = CCV_FWD_ROUNDS > 0 ? ccv::fwd_resident_blocks(a, vec, silu, p.packed) : 0;
-    const Geometry g = geometry(p, vec, cap, CCV_FWD_ROUNDS, CCV_FWD_TARGET_WAVES,
-                                CCV_FWD_MIN_CHUNK);
+    const Geometry g = geometry(p, vec, ccv::kFwdWavesT, ccv::kFwdWavesC, cap, CCV_FWD_ROUNDS,
+                                CCV_FWD_TARGET_WAVES, CCV_FWD_MIN_CHUNK);
     a.B = p.B;
     a.D = p.D;
     a.T = p.T;
@@ -339,6 +341,7 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     a.n_chunk = g.n_chunk;
     a.n_tblk = g.n_tblk;
     a.n_group = g.n_group;
+    a.n_gblk = g.n_gblk;
     a.n_block = g.n_block;
     a.cu_in_lds = p.packed && p.N + 1 <= ccv::kLdsCuMax;
     a.nt_load = p.B * p.D * p.T * 2 >= CCV_NT_LOAD_MIN_BYTES;
@@ -393,7 +396,8 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     // The partials of the deterministic route depend on the shape only (a
     // grid sized by target waves); the atomic route sizes its grid by the
     // device's resident capacity below.
-    Geometry g = geometry(p, vec, 0, 0, CCV_BWD_TARGET_WAVES, CCV_BWD_MIN_CHUNK);
+    Geometry g = geometry(p, vec, ccv::kWavesPerBlock, 1, 0, 0, CCV_BWD_TARGET_WAVES,
+                          CCV_BWD_MIN_CHUNK);
     const int64_t n_part = (p.packed ? 1 : p.B) * g.n_tblk;
     const size_t need = use_partials
                             ? static_cast<size_t>(n_part) * static_cast<size_t>(p.D) * kWidth * 4
@@ -437,8 +441,8 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     a.err = p.packed ? err_flag : nullptr;
     const int silu = activation == CCV_ACT_SILU;
     if (!use_partials && CCV_BWD_ROUNDS > 0)
-        g = geometry(p, vec, ccv::bwd_resident_blocks(a, vec, silu, p.packed), CCV_BWD_ROUNDS,
-                     CCV_BWD_TARGET_WAVES, CCV_BWD_MIN_CHUNK);
+        g = geometry(p, vec, ccv::kWavesPerBlock, 1, ccv::bwd_resident_blocks(a, vec, silu, p.packed),
+                     CCV_BWD_ROUNDS, CCV_BWD_TARGET_WAVES, CCV_BWD_MIN_CHUNK);
     a.B = p.B;
     a.D = p.D;
     a.T = p.T;
@@ -446,6 +450,7 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     a.n_chunk = g.n_chunk;
     a.n_tblk = g.n_tblk;
     a.n_group = g.n_group;
+    a.n_gblk = g.n_gblk;
     a.n_block = g.n_block;
     a.cu_in_lds = p.packed && p.N + 1 <= ccv::kLdsCuMax;
     a.nt_load = 2 * p.B * p.D * p.T * 2 >= CCV_NT_LOAD_MIN_BYTES;

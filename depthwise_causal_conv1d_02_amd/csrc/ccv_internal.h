@@ -11,7 +11,21 @@ namespace ccv {
 
 constexpr int kWidth = 4;          // the filter width the kernels are built for
 constexpr int kWaveSize = 64;      // CDNA wavefront
-constexpr int kWavesPerBlock = 4;  // channel-lane kernels: 4 waves share a channel group
+constexpr int kWavesPerBlock = 4;  // channel-lane kernels: 4 waves per block
+// Forward blocks: kFwdWavesT waves along time x kFwdWavesC along channel
+// groups.  Backward blocks put all 4 waves on one channel group (consecutive
+// chunks), so that their dW/dB partials can be summed in LDS.
+#ifndef CCV_FWD_WAVES_T
+#define CCV_FWD_WAVES_T 2
+#endif
+constexpr int kFwdWavesT = CCV_FWD_WAVES_T;
+constexpr int kFwdWavesC = kWavesPerBlock / kFwdWavesT;
+// Order of blocks in a launch: 0 = time blocks innermost (a block's
+// neighbours in time are its neighbours in dispatch order), 1 = channel
+// blocks innermost (concurrent blocks cover whole [B,T,D] rows).
+#ifndef CCV_TILE_ORDER
+#define CCV_TILE_ORDER 1
+#endif
 constexpr int kLdsCuMax = 4096;    // cu_seqlens entries staged in LDS (16 KB)
 
 // One BF16 activation-like tensor [B,D,T] (or [R,D,W-1] for states) in
@@ -34,8 +48,9 @@ struct FwdArgs {
     int64_t B, D, T;           // T = tokens per batch row (dense) or the packed total
     int64_t L;                 // time steps per wave
     int64_t n_chunk;           // ceil(T / L)
-    int64_t n_tblk;            // ceil(n_chunk / waves per block)
+    int64_t n_tblk;            // blocks along time: ceil(n_chunk / kFwdWavesT)
     int64_t n_group;           // channel groups of 64*VEC channels
+    int64_t n_gblk;            // blocks along channels: ceil(n_group / kFwdWavesC)
     int64_t n_block;           // grid size
     int cu_in_lds;             // stage + validate cu_seqlens in LDS
     int nt_load;               // stream the bulk loads with the non-temporal policy
@@ -54,7 +69,7 @@ struct BwdArgs {
     const int32_t *cu;
     int64_t n_seq;
     uint32_t *err;
-    int64_t B, D, T, L, n_chunk, n_tblk, n_group, n_block;
+    int64_t B, D, T, L, n_chunk, n_tblk, n_group, n_gblk, n_block;
     int cu_in_lds;
     int nt_load;
 };

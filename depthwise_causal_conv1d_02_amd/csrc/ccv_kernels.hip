@@ -163,6 +163,19 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nb) {
     return x * q + (x < r ? x : r) + j;
 }
 
+// Logical tile -> (row b, channel block, time block) in the CCV_TILE_ORDER.
+__device__ __forceinline__ void decode_tile(int64_t tile, int64_t n_t, int64_t n_c, int64_t &b,
+                                            int64_t &cb, int64_t &tb) {
+    if (CCV_TILE_ORDER == 0) {
+        tb = tile % n_t;
+        cb = (tile / n_t) % n_c;
+    } else {
+        cb = tile % n_c;
+        tb = (tile / n_c) % n_t;
+    }
+    b = tile / (n_t * n_c);
+}
+
 // Filter kinds: the weight dtype and whether a bias is present.
 enum FilterKind { kBf16 = 0, kBf16Bias = 1, kF32 = 2 };
 
@@ -400,10 +413,8 @@ template <int VEC, bool SILU, bool PACKED, int FK>
 __global__ __launch_bounds__(256) CCV_FWD_ATTR void k_fwd_chan(FwdArgs a) {
     __shared__ int32_t s_cu[PACKED ? kLdsCuMax : 1];
     __shared__ uint32_t s_bad;
-    const int64_t tile = xcd_remap(blockIdx.x, a.n_block);
-    const int64_t bt = tile % a.n_tblk;
-    const int64_t g = (tile / a.n_tblk) % a.n_group;
-    const int64_t b = tile / (a.n_tblk * a.n_group);
+    int64_t b, gb, bt;
+    decode_tile(xcd_remap(blockIdx.x, a.n_block), a.n_tblk, a.n_gblk, b, gb, bt);
     const int wave = threadIdx.x / kWaveSize, lane = threadIdx.x % kWaveSize;
 
     if constexpr (PACKED) {
@@ -411,7 +422,8 @@ __global__ __launch_bounds__(256) CCV_FWD_ATTR void k_fwd_chan(FwdArgs a) {
                                blockIdx.x == 0))
             return;  // malformed or sticky: write nothing
     }
-    const int64_t t0 = (bt * kWavesPerBlock + wave) * a.L;
+    const int64_t g = gb * kFwdWavesC + wave / kFwdWavesT;
+    const int64_t t0 = (bt * kFwdWavesT + wave % kFwdWavesT) * a.L;
     const int64_t c0 = g * (kWaveSize * VEC) + lane * VEC;
     if (t0 >= a.T || c0 >= a.D) return;
     const int64_t t1 = min(t0 + a.L, a.T);
@@ -637,10 +649,8 @@ __global__ __launch_bounds__(256) CCV_BWD_ATTR void k_bwd_chan(BwdArgs a) {
     __shared__ uint32_t s_bad;
     int32_t *s_cu = reinterpret_cast<int32_t *>(s_buf);
     float (*s_red)[W + 1][CH + 1] = reinterpret_cast<float (*)[W + 1][CH + 1]>(s_buf);
-    const int64_t tile = xcd_remap(blockIdx.x, a.n_block);
-    const int64_t bt = tile % a.n_tblk;
-    const int64_t g = (tile / a.n_tblk) % a.n_group;
-    const int64_t b = tile / (a.n_tblk * a.n_group);
+    int64_t b, g, bt;
+    decode_tile(xcd_remap(blockIdx.x, a.n_block), a.n_tblk, a.n_group, b, g, bt);
     const int wave = threadIdx.x / kWaveSize, lane = threadIdx.x % kWaveSize;
 
     if constexpr (PACKED) {
