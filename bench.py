@@ -37,6 +37,42 @@ SPACER_CYCLES = 200000      # GPU spin before each timed op in the per-op pass
 METRIC = "achieved HBM GB/s (% of MI355X peak) for fwd, bwd and update at 1 GPU"
 
 
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = [os.path.join(ROOT, "depthwise_causal_conv1d_02_amd", "csrc", f)
+                  for f in ("ccv_kernels.hip", "ccv_api.cpp", "ccv_internal.h")]
+OP_KERNEL = {"fwd": "k_fwd_chan", "bwd": "k_bwd_chan", "update": "k_update"}
+
+
+def source_hash():
+    """Hash of the kernel sources: counter figures taken from another version
+    of the kernels are not reported."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profile_path(kernel, workload):
+    return os.path.join(PROFILES, "%s_%s.md" % (kernel, workload))
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernels changed since it was taken."""
+    path = profile_path(kernel, workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("<!-- traffic "):
+                rec = json.loads(line[len("<!-- traffic "):].rsplit("-->", 1)[0])
+                if rec.get("source_hash") == source_hash():
+                    return rec
+    return None
+
+
 def act_bytes(B, D, T):
     return B * D * T * 2
 
@@ -95,8 +131,22 @@ class Workload:
         self.desc = synth.WORKLOADS[idx]
 
 
+class Step:
+    """One pass of the hot path: the ops of a step, run in order."""
+
+    def __init__(self, ops, outputs):
+        self.ops = ops            # [(op name, callable)]
+        self.outputs = outputs
+
+    def __call__(self, ev):
+        for name, fn in self.ops:
+            ev.begin(name)
+            fn()
+            ev.end(name)
+
+
 def make_step(wl, torch):
-    """Allocate every output once; return step() running all ops of one pass."""
+    """Allocate every output once; return the Step of this workload."""
     from depthwise_causal_conv1d_02_amd import ops
 
     g, dev = wl.g, wl.dev
@@ -104,24 +154,24 @@ def make_step(wl, torch):
         state = g["conv_state"].clone()
         xs = g["x_steps"]
         ys = torch.empty_like(xs)
-
-        def step(ev):
-            # one step decodes the 64 seeded tokens in order, each in place on
-            # the same state
-            for s in range(xs.shape[0]):
-                ev.begin("update")
-                ops.update(xs[s], state, g["weight"], g["bias"], g["activation"], y=ys[s])
-                ev.end("update")
-        step.outputs = {"y": ys}
-        return step
+        # one step decodes the seeded tokens in order, each in place on the
+        # same state
+        calls = [("update", (lambda s=s: ops.update(xs[s], state, g["weight"], g["bias"],
+                                                     g["activation"], y=ys[s])))
+                 for s in range(xs.shape[0])]
+        return Step(calls, {"y": ys})
 
     x = g["x"]
     y = torch.empty_like(x)
     fin = None
     if g["return_final_states"] or wl.name == "dense":
         fin = torch.empty(wl.shape["R"], x.shape[1], 3, dtype=x.dtype, device=dev)
-    has_bwd = g["dy"] is not None
-    if has_bwd:
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    calls = [("fwd", lambda: ops.fwd(x, g["weight"], g["bias"], g["cu_seqlens"],
+                                     g["initial_states"], g["activation"],
+                                     final_states_out=fin, y=y, err_flag=flag))]
+    outputs = {"y": y}
+    if g["dy"] is not None:
         dx = torch.empty_like(x)
         D = x.shape[1]
         # dweight and dbias live in one buffer, cleared by a single fill per step
@@ -130,33 +180,20 @@ def make_step(wl, torch):
         db = grads[D * 4:] if g["bias"] is not None else None
         dinit = torch.empty_like(g["initial_states"]) if g["initial_states"] is not None else None
         ws = torch.empty(1 << 26, dtype=torch.uint8, device=dev) if g["deterministic"] else None
-    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+        calls.append(("zero_grads", grads.zero_))
+        calls.append(("bwd", lambda: ops.bwd(x, g["weight"], g["dy"], g["bias"], g["cu_seqlens"],
+                                             g["initial_states"], None, g["activation"],
+                                             g["deterministic"], False, dx=dx, err_flag=flag,
+                                             workspace=ws, dweight=dw, dbias=db, dinit=dinit)))
+        outputs.update(dx=dx, dw=dw)
     if wl.name == "dense":
+        # decode the next token straight from the returned final states
+        # (updated in place; the next step's forward rewrites them)
         xt = g["x"][:, :, -1].contiguous()
         yt = torch.empty_like(xt)
-
-    def step(ev):
-        ev.begin("fwd")
-        ops.fwd(x, g["weight"], g["bias"], g["cu_seqlens"], g["initial_states"], g["activation"],
-                final_states_out=fin, y=y, err_flag=flag)
-        ev.end("fwd")
-        if has_bwd:
-            grads.zero_()
-            ev.begin("bwd")
-            ops.bwd(x, g["weight"], g["dy"], g["bias"], g["cu_seqlens"], g["initial_states"], None,
-                    g["activation"], g["deterministic"], False, dx=dx, err_flag=flag,
-                    workspace=ws, dweight=dw, dbias=db, dinit=dinit)
-            ev.end("bwd")
-        if wl.name == "dense":
-            # decode the next token straight from the returned final states
-            # (updated in place; the next step's forward rewrites them)
-            ev.begin("update")
-            ops.update(xt, fin, g["weight"], g["bias"], g["activation"], y=yt)
-            ev.end("update")
-    step.outputs = {"y": y}
-    if has_bwd:
-        step.outputs.update(dx=dx, dw=dw)
-    return step
+        calls.append(("update", lambda: ops.update(xt, fin, g["weight"], g["bias"],
+                                                   g["activation"], y=yt)))
+    return Step(calls, outputs)
 
 
 class Events:
@@ -187,6 +224,27 @@ class Events:
 
     def mean_ms(self):
         return {k: sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in self.rec.items()}
+
+
+def op_times(torch, step, wl, reps):
+    """Mean ms per launch of each op kind of the step (see main)."""
+    seen = {}
+    for name, fn in step.ops:
+        if name not in wl.bytes or name in seen:
+            continue
+        ts = []
+        for _ in range(3):
+            torch.cuda._sleep(SPACER_CYCLES)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) / reps)
+        seen[name] = sorted(ts)[1]
+    return seen
 
 
 def cpu_baseline(wl, budget_s=10.0):
@@ -245,6 +303,93 @@ def cpu_baseline(wl, budget_s=10.0):
                 seconds=round(dt, 3), token_channels_per_s=round(B * nch * T / dt, 1))
 
 
+def _kernel_rows(csv_path):
+    import csv
+    rows = list(csv.DictReader(open(csv_path)))
+    for r in rows:
+        n = r.get("Kernel_Name") or r.get("Name")
+        r["_short"] = n.replace("void ccv::(anonymous namespace)::", "").split("(ccv")[0]
+    return rows
+
+
+def _counter_per_launch(pmc_dir, counter, name_part):
+    """Mean of a counter over the dispatches whose kernel name contains name_part."""
+    import glob
+    vals = []
+    for f in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in _kernel_rows(f):
+            if r["Counter_Name"] == counter and name_part in r["_short"]:
+                vals.append(float(r["Counter_Value"]))
+    return sum(vals) / len(vals) if vals else None, len(vals)
+
+
+def summarize(args):
+    """Write profiles/<kernel>_<workload>.md from rocprofv3 output directories
+    (kernel trace, FETCH_SIZE pass, WRITE_SIZE pass, and the same two counters
+    for a plain copy of known size)."""
+    import glob
+    wl_bytes = {"dense": {"fwd": fwd_bytes(4, 4096, 2048, 4, True, True, 2, True),
+                          "bwd": bwd_bytes(4, 4096, 2048, 4, True, False, 2, True)},
+                "packed": {"fwd": fwd_bytes(1, 5120, 33280, 16, True, True, 4, False),
+                           "bwd": bwd_bytes(1, 5120, 33280, 16, True, False, 4, False)},
+                "large": {"fwd": fwd_bytes(8, 8192, 8192, 8, False, False, 2, False),
+                          "bwd": bwd_bytes(8, 8192, 8192, 8, False, False, 2, False)},
+                "decode": {"update": update_bytes(256, 8192, 2, True)}}[args.workload]
+    trace_dir, fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.summarize
+    stats = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
+    rows = _kernel_rows(stats)
+    copy_bytes = args.copy_calibration << 20
+    c_fetch, _ = _counter_per_launch(cfetch_dir, "FETCH_SIZE", "copyBuffer")
+    c_write, _ = _counter_per_launch(cwrite_dir, "WRITE_SIZE", "copyBuffer")
+    f_scale = copy_bytes / (c_fetch * 1024.0)   # counter KiB -> bytes read
+    w_scale = copy_bytes / (c_write * 1024.0)
+    h = source_hash()
+    for op, kernel in OP_KERNEL.items():
+        if op not in wl_bytes:
+            continue
+        mine = [r for r in rows if r["_short"].startswith(kernel)]
+        if not mine:
+            continue
+        fetch, nf = _counter_per_launch(fetch_dir, "FETCH_SIZE", kernel)
+        write, nw = _counter_per_launch(write_dir, "WRITE_SIZE", kernel)
+        hbm = int(fetch * 1024 * f_scale + write * 1024 * w_scale)
+        alg = wl_bytes[op]
+        lines = ["# %s on the %s workload" % (kernel, args.workload), "",
+                 "Commands (one MI355X, repository root as $REPO, `cd /tmp && export TMPDIR=/tmp` first):", "",
+                 "```"]
+        lines += args.commands.split(";;")
+        lines += ["```", "", "Kernel trace (`--kernel-trace --stats`):", "",
+                  "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+        for r in rows:
+            lines.append("| `%s` | %s | %.2f | %.2f | %.2f |" % (
+                r["_short"][:70], r["Calls"], float(r["AverageNs"]) / 1e3,
+                float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+        avg_us = sum(float(r["AverageNs"]) * int(r["Calls"]) for r in mine) / \
+            sum(int(r["Calls"]) for r in mine) / 1e3
+        lines += ["", "Counters per launch of `%s` (means over %d and %d dispatches):" % (kernel, nf, nw), "",
+                  "| quantity | value |", "|---|---|",
+                  "| FETCH_SIZE (KiB) | %.1f |" % fetch, "| WRITE_SIZE (KiB) | %.1f |" % write,
+                  "| copy calibration: %d MiB copy reads FETCH_SIZE KiB | %.1f (factor %.4f) |" % (
+                      args.copy_calibration, c_fetch, f_scale),
+                  "| copy calibration: %d MiB copy reads WRITE_SIZE KiB | %.1f (factor %.4f) |" % (
+                      args.copy_calibration, c_write, w_scale),
+                  "| HBM bytes per launch (scaled) | %d |" % hbm,
+                  "| algorithmic bytes per launch | %d |" % alg,
+                  "| traffic / algorithmic | %.4f |" % (hbm / alg),
+                  "| average kernel duration (us) | %.2f |" % avg_us,
+                  "| algorithmic bytes / average duration (GB/s) | %.1f |" % (alg / (avg_us * 1e-6) / 1e9),
+                  "",
+                  "<!-- traffic " + json.dumps({"kernel": kernel, "workload": args.workload,
+                                                 "hbm_bytes_per_launch": hbm,
+                                                 "algorithmic_bytes": alg,
+                                                 "avg_kernel_us": round(avg_us, 3),
+                                                 "source_hash": h}) + " -->"]
+        path = profile_path(kernel, args.workload)
+        with open(path, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print("wrote", path)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -255,6 +400,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-events", action="store_true",
                     help="skip the per-op event pass")
+    ap.add_argument("--op-reps", type=int, default=10,
+                    help="back-to-back launches per event pair in the per-op pass")
     ap.add_argument("--graph", dest="graph", action="store_true", default=True,
                     help="replay the step as a captured HIP graph in the timed region (default)")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
@@ -262,7 +409,14 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the workload, run a plain device copy of MIB MiB "
                          "(counter calibration for rocprofv3 --pmc)")
+    ap.add_argument("--summarize", nargs=5, metavar="DIR",
+                    help="(no GPU) write profiles/<kernel>_<workload>.md from rocprofv3 output: "
+                         "TRACE FETCH WRITE COPY_FETCH COPY_WRITE directories")
+    ap.add_argument("--commands", default="", help="with --summarize: the commands run, ';;'-separated")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the op shards with no communication over channels; see the design notes)",
@@ -326,15 +480,13 @@ def main():
     per_op = {}
     roof = None
     if not args.no_events:
-        # Per-op times: an eager pass with events around every op, on the
-        # stream the kernels run on.  A step of one op kind (decode) takes its
-        # per-launch time from the graph replays instead, where no host
-        # latency sits between launches.
-        ev = Events(torch, True, spacer=True)
-        for _ in range(args.steps):
-            step(ev)
-        torch.cuda.synchronize()
-        means = ev.mean_ms()
+        # Per-op times: for every op of the step, a GPU spin, then one event
+        # pair around `op_reps` back-to-back launches of that op, on the
+        # stream the kernels run on (the pair's own latency is spread over the
+        # launches, as a kernel trace would not count it).  A step of one op
+        # kind (decode) takes its per-launch time from the graph replays,
+        # where no host latency sits between launches.
+        means = op_times(torch, step, wl, args.op_reps)
         if graph is not None and len(wl.bytes) == 1:
             (k,) = wl.bytes
             means[k] = step_ev.mean_ms()["step"] / wl.counts[k]
@@ -344,12 +496,15 @@ def main():
                          "launches_per_step": wl.counts[k],
                          "GB_s": round(gbs, 1), "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2)}
         dom = max(means, key=lambda k: means[k] * wl.counts[k])
-        kernel = {"fwd": "k_fwd_chan", "bwd": "k_bwd_chan", "update": "k_update"}[dom]
+        kernel = OP_KERNEL[dom]
         ach = wl.bytes[dom] / (means[dom] * 1e-3) / 1e9
+        rec = recorded_traffic(kernel, wl.name)
         roof = {"bound": "hbm", "kernel": kernel, "op": dom, "achieved": round(ach, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                "traffic": None, "bytes_per_launch": wl.bytes[dom],
-                "avg_launch_ms": round(means[dom], 5)}
+                "traffic": None if rec is None else rec["hbm_bytes_per_launch"],
+                "bytes_per_launch": wl.bytes[dom], "avg_launch_ms": round(means[dom], 5)}
+        if rec is not None:
+            roof["traffic_over_algorithmic"] = round(rec["hbm_bytes_per_launch"] / wl.bytes[dom], 4)
 
     shape = wl.shape
     tc = shape["B"] * shape["D"] * shape.get("T", shape.get("tokens", 1))
