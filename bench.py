@@ -132,7 +132,8 @@ class Workload:
 
 
 class Step:
-    """One pass of the hot path: the ops of a step, run in order."""
+    """One pass of the hot path: the ops of a step, run in order on the
+    current stream."""
 
     def __init__(self, ops, outputs):
         self.ops = ops            # [(op name, callable)]

@@ -528,6 +528,8 @@ int ccv_update(const ccv_tensor *x, const ccv_tensor *conv_state, const ccv_tens
     a.B = B;
     a.D = D;
     a.n_lane_per_row = vec ? D / 8 : D;
+    const int64_t rpl = ccv::update_rows_per_lane();
+    a.n_row_groups = (B + rpl - 1) / rpl;
     return hip_status(ccv::launch_update(a, vec ? 8 : 1, activation == CCV_ACT_SILU, stream));
 }
 

@@ -87,13 +87,15 @@ struct UpdArgs {
     void *y;              // [B,D]
     int64_t y_sb, y_sd;
     int64_t B, D;
-    int64_t n_lane_per_row;  // ceil(D / VEC)
+    int64_t n_lane_per_row;  // D / VEC
+    int64_t n_row_groups;    // ceil(B / rows per lane), 8-channel lanes
 };
 
 // Launchers (ccv_kernels.hip).  `vec` is the channels per lane (8 or 1).
 hipError_t launch_fwd(const FwdArgs &a, int vec, int silu, int packed, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs &a, int vec, int silu, int packed, hipStream_t s);
 hipError_t launch_update(const UpdArgs &a, int vec, int silu, hipStream_t s);
+int update_rows_per_lane();  // batch rows an 8-channel update lane serves
 // Blocks of the kernel launch_fwd / launch_bwd would pick that fit on the
 // current device at once (0 if the runtime cannot tell).  Host queries only.
 int64_t fwd_resident_blocks(const FwdArgs &a, int vec, int silu, int packed);

@@ -736,120 +736,131 @@ __global__ __launch_bounds__(256) CCV_BWD_ATTR void k_bwd_chan(BwdArgs a) {
 #ifndef CCV_UPD_NT
 #define CCV_UPD_NT 0
 #endif
-// The register budget of up to CCV_UPD_MAX_WAVES waves per SIMD leaves room
-// for every load of a lane to be in flight at once.
-template <int VEC, bool SILU, bool WF32, bool BIAS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, CCV_UPD_MAX_WAVES)))
-void k_update(UpdArgs a) {
-    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    const int64_t b = gid / a.n_lane_per_row;
-    if (b >= a.B) return;
-    const int64_t c0 = (gid % a.n_lane_per_row) * VEC;
-    const uint16_t *xp = static_cast<const uint16_t *>(a.x) + b * a.x_sb + c0 * a.x_sd;
-    uint16_t *sp = static_cast<uint16_t *>(a.state) + b * a.s_sb + c0 * a.s_sd;
-    uint16_t *yp = static_cast<uint16_t *>(a.y) + b * a.y_sb + c0 * a.y_sd;
 
-    // Raw bits: the shifted state is a copy of them, never re-rounded.
-    uint16_t st[VEC][W - 1], xr[VEC];
+// The register budget of up to CCV_UPD_MAX_WAVES waves per SIMD leaves room
+// for every load of a lane to be in flight at once.  With 8 channels per lane
+// the host has verified unit channel strides, a contiguous [B,D,W-1] state, a
+// contiguous [D,W] filter and bias, and 16-byte alignment: a lane's state is
+// 3 x 16 contiguous bytes.  A lane serves RPL batch rows of the same
+// channels, so their filter and bias are loaded once.
+template <bool SILU, bool WF32, bool BIAS, int RPL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, CCV_UPD_MAX_WAVES)))
+void k_update_vec(UpdArgs a) {
+    constexpr int VEC = 8;
+    constexpr int kStateVecs = VEC * (W - 1) / 8;              // 16-byte vectors of state
+    constexpr int kFilterVecs = VEC * W * (WF32 ? 4 : 2) / 16;
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t rg = gid / a.n_lane_per_row;
+    if (rg >= a.n_row_groups) return;
+    const int64_t c0 = (gid % a.n_lane_per_row) * VEC;
+    const int64_t b0 = rg * RPL;
+
+    // Every load first: filter, bias, then each row's state and token.
+    const u32x4_t *wq = reinterpret_cast<const u32x4_t *>(
+        static_cast<const char *>(a.w) + c0 * W * (WF32 ? 4 : 2));
+    u32x4_t wv[kFilterVecs], bv = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < kFilterVecs; ++i) wv[i] = wq[i];
+    if constexpr (BIAS)
+        bv = *reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(a.bias) + c0);
+    u32x4_t sv[RPL][kStateVecs], xv[RPL];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+        if (b0 + r >= a.B) break;
+        const u32x4_t *sq = reinterpret_cast<const u32x4_t *>(
+            static_cast<const uint16_t *>(a.state) + (b0 + r) * a.s_sb + c0 * (W - 1));
+#pragma unroll
+        for (int i = 0; i < kStateVecs; ++i)
+            sv[r][i] = CCV_UPD_NT ? __builtin_nontemporal_load(sq + i) : sq[i];
+        const u32x4_t *xq = reinterpret_cast<const u32x4_t *>(
+            static_cast<const uint16_t *>(a.x) + (b0 + r) * a.x_sb + c0);
+        xv[r] = CCV_UPD_NT ? __builtin_nontemporal_load(xq) : *xq;
+    }
+
     float w[W][VEC], bias[VEC];
-    if constexpr (VEC == 8) {
-        constexpr int kStateVecs = VEC * (W - 1) / 8;      // 16-byte vectors of state
-        constexpr int kFilterVecs = VEC * W * (WF32 ? 4 : 2) / 16;
-        const u32x4_t *sq = reinterpret_cast<const u32x4_t *>(sp);
-        const u32x4_t *wq = reinterpret_cast<const u32x4_t *>(
-            static_cast<const char *>(a.w) + c0 * W * (WF32 ? 4 : 2));
-        u32x4_t sv[kStateVecs], wv[kFilterVecs], xv, bv;
 #pragma unroll
-        for (int i = 0; i < kStateVecs; ++i) sv[i] = CCV_UPD_NT ? __builtin_nontemporal_load(sq + i) : sq[i];
-        xv = CCV_UPD_NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(xp))
-                        : *reinterpret_cast<const u32x4_t *>(xp);
+    for (int c = 0; c < VEC; ++c) {
 #pragma unroll
-        for (int i = 0; i < kFilterVecs; ++i) wv[i] = wq[i];
-        if constexpr (BIAS) bv = *reinterpret_cast<const u32x4_t *>(
-                                  static_cast<const uint16_t *>(a.bias) + c0);
+        for (int k = 0; k < W; ++k) {
+            const int e2 = c * W + k;
+            if constexpr (WF32) {
+                w[k][c] = __uint_as_float(wv[e2 / 4][e2 % 4]);
+            } else {
+                const uint32_t word = wv[e2 / 8][(e2 % 8) / 2];
+                w[k][c] = (e2 % 2) ? hi_bf16(word) : lo_bf16(word);
+            }
+        }
+        bias[c] = (c % 2) ? hi_bf16(bv[c / 2]) : lo_bf16(bv[c / 2]);
+    }
+
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+        if (b0 + r >= a.B) break;
+        // Raw bits: the shifted state is a copy of them, never re-rounded.
+        uint16_t st[VEC][W - 1], xr[VEC];
 #pragma unroll
         for (int e2 = 0; e2 < VEC * (W - 1); ++e2)
             st[e2 / (W - 1)][e2 % (W - 1)] =
-                static_cast<uint16_t>(sv[e2 / 8][(e2 % 8) / 2] >> (16 * (e2 % 2)));
+                static_cast<uint16_t>(sv[r][e2 / 8][(e2 % 8) / 2] >> (16 * (e2 % 2)));
 #pragma unroll
-        for (int c = 0; c < VEC; ++c) xr[c] = static_cast<uint16_t>(xv[c / 2] >> (16 * (c % 2)));
-#pragma unroll
-        for (int c = 0; c < VEC; ++c) {
-#pragma unroll
-            for (int k = 0; k < W; ++k) {
-                const int e2 = c * W + k;
-                if constexpr (WF32) {
-                    w[k][c] = __uint_as_float(wv[e2 / 4][e2 % 4]);
-                } else {
-                    const uint32_t word = wv[e2 / 8][(e2 % 8) / 2];
-                    w[k][c] = (e2 % 2) ? hi_bf16(word) : lo_bf16(word);
-                }
-            }
-            if constexpr (BIAS) {
-                const uint32_t word = bv[c / 2];
-                bias[c] = (c % 2) ? hi_bf16(word) : lo_bf16(word);
-            } else {
-                bias[c] = 0.0f;
-            }
-        }
-    } else {
+        for (int c = 0; c < VEC; ++c)
+            xr[c] = static_cast<uint16_t>(xv[r][c / 2] >> (16 * (c % 2)));
+        float out[VEC];
 #pragma unroll
         for (int c = 0; c < VEC; ++c) {
+            float z = bias[c];
 #pragma unroll
-            for (int j = 0; j < W - 1; ++j) st[c][j] = sp[c * a.s_sd + j * a.s_sj];
-            xr[c] = xp[c * a.x_sd];
-#pragma unroll
-            for (int k = 0; k < W; ++k) {
-                const int64_t off = (c0 + c) * a.w_sd + k * a.w_sk;
-                w[k][c] = WF32 ? static_cast<const float *>(a.w)[off]
-                               : bf16_bits_to_f32(static_cast<const uint16_t *>(a.w)[off]);
-            }
-            bias[c] = BIAS ? bf16_bits_to_f32(static_cast<const uint16_t *>(a.bias)[(c0 + c) * a.b_s])
-                           : 0.0f;
+            for (int k = 0; k < W - 1; ++k) z = fmaf(w[k][c], bf16_bits_to_f32(st[c][k]), z);
+            z = fmaf(w[W - 1][c], bf16_bits_to_f32(xr[c]), z);
+            out[c] = act<SILU>(z);
         }
-    }
-
-    float out[VEC];
-#pragma unroll
-    for (int c = 0; c < VEC; ++c) {
-        float z = bias[c];
-#pragma unroll
-        for (int k = 0; k < W - 1; ++k) z = fmaf(w[k][c], bf16_bits_to_f32(st[c][k]), z);
-        z = fmaf(w[W - 1][c], bf16_bits_to_f32(xr[c]), z);
-        out[c] = act<SILU>(z);
-    }
-    // New state (s_1 .. s_{W-2}, x).
-    uint16_t ns[VEC][W - 1];
-#pragma unroll
-    for (int c = 0; c < VEC; ++c) {
-#pragma unroll
-        for (int j = 0; j < W - 2; ++j) ns[c][j] = st[c][j + 1];
-        ns[c][W - 2] = xr[c];
-    }
-    if constexpr (VEC == 8) {
-        store_vec<VEC, true>(yp, 1, out);
-        constexpr int kStateVecs = VEC * (W - 1) / 8;
-        u32x4_t sv[kStateVecs];
+        store_vec<VEC, true>(static_cast<uint16_t *>(a.y) + (b0 + r) * a.y_sb + c0, 1, out);
+        // New state (s_1 .. s_{W-2}, x), packed back into 16-byte vectors.
+        u32x4_t nv[kStateVecs];
 #pragma unroll
         for (int i = 0; i < VEC * (W - 1) / 2; ++i) {
-            const int e0 = 2 * i, e1 = 2 * i + 1;
-            sv[i / 4][i % 4] = static_cast<uint32_t>(ns[e0 / (W - 1)][e0 % (W - 1)]) |
-                               (static_cast<uint32_t>(ns[e1 / (W - 1)][e1 % (W - 1)]) << 16);
+            uint16_t h[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int e2 = 2 * i + q, c = e2 / (W - 1), j = e2 % (W - 1);
+                h[q] = j < W - 2 ? st[c][j + 1] : xr[c];
+            }
+            nv[i / 4][i % 4] = static_cast<uint32_t>(h[0]) | (static_cast<uint32_t>(h[1]) << 16);
         }
-        u32x4_t *sq = reinterpret_cast<u32x4_t *>(sp);
+        u32x4_t *sq = reinterpret_cast<u32x4_t *>(static_cast<uint16_t *>(a.state) +
+                                                  (b0 + r) * a.s_sb + c0 * (W - 1));
 #pragma unroll
         for (int i = 0; i < kStateVecs; ++i) {
-            if (CCV_UPD_NT) __builtin_nontemporal_store(sv[i], sq + i);
-            else sq[i] = sv[i];
-        }
-    } else {
-#pragma unroll
-        for (int c = 0; c < VEC; ++c) {
-            yp[c * a.y_sd] = to_bf16_bits(out[c]);
-#pragma unroll
-            for (int j = 0; j < W - 1; ++j) sp[c * a.s_sd + j * a.s_sj] = ns[c][j];
+            if (CCV_UPD_NT) __builtin_nontemporal_store(nv[i], sq + i);
+            else sq[i] = nv[i];
         }
     }
+}
+
+// Any strides: one lane per channel of one row.
+template <bool SILU, bool WF32, bool BIAS>
+__global__ __launch_bounds__(256) void k_update_any(UpdArgs a) {
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t b = gid / a.n_lane_per_row;
+    if (b >= a.B) return;
+    const int64_t c = gid % a.n_lane_per_row;
+    const uint16_t *xp = static_cast<const uint16_t *>(a.x) + b * a.x_sb + c * a.x_sd;
+    uint16_t *sp = static_cast<uint16_t *>(a.state) + b * a.s_sb + c * a.s_sd;
+    uint16_t st[W - 1];
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) st[j] = sp[j * a.s_sj];
+    const uint16_t xr = *xp;
+    float z = BIAS ? bf16_bits_to_f32(static_cast<const uint16_t *>(a.bias)[c * a.b_s]) : 0.0f;
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+        const int64_t off = c * a.w_sd + k * a.w_sk;
+        const float wk = WF32 ? static_cast<const float *>(a.w)[off]
+                              : bf16_bits_to_f32(static_cast<const uint16_t *>(a.w)[off]);
+        z = fmaf(wk, bf16_bits_to_f32(k < W - 1 ? st[k] : xr), z);
+    }
+    static_cast<uint16_t *>(a.y)[b * a.y_sb + c * a.y_sd] = to_bf16_bits(act<SILU>(z));
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) sp[j * a.s_sj] = j < W - 2 ? st[j + 1] : xr;
 }
 
 // ===========================================================================
@@ -993,19 +1004,31 @@ int64_t bwd_resident_blocks(const BwdArgs &a, int vec, int silu, int packed) {
     return cap;
 }
 
+#ifndef CCV_UPD_ROWS
+#define CCV_UPD_ROWS 2
+#endif
+
 hipError_t launch_update(const UpdArgs &a, int vec, int silu, hipStream_t s) {
-    const int64_t lanes = a.B * a.n_lane_per_row;
-    const int64_t blocks = (lanes + 255) / 256;
     const bool wf32 = a.w_f32 != 0, bias = a.bias != nullptr;
-#define CCV_UPD(V, S, F, B) \
-    if (vec == V && !!silu == S && wf32 == F && bias == B) return launch(k_update<V, S, F, B>, blocks, a, s);
-    CCV_UPD(8, true, false, true) CCV_UPD(8, true, false, false) CCV_UPD(8, true, true, false)
-    CCV_UPD(8, false, false, true) CCV_UPD(8, false, false, false) CCV_UPD(8, false, true, false)
-    CCV_UPD(1, true, false, true) CCV_UPD(1, true, false, false) CCV_UPD(1, true, true, false)
-    CCV_UPD(1, false, false, true) CCV_UPD(1, false, false, false) CCV_UPD(1, false, true, false)
+    if (vec == 8) {
+        const int64_t blocks = (a.n_row_groups * a.n_lane_per_row + 255) / 256;
+#define CCV_UPD(S, F, B) \
+        if (!!silu == S && wf32 == F && bias == B) return launch(k_update_vec<S, F, B, CCV_UPD_ROWS>, blocks, a, s);
+        CCV_UPD(true, false, true) CCV_UPD(true, false, false) CCV_UPD(true, true, false)
+        CCV_UPD(false, false, true) CCV_UPD(false, false, false) CCV_UPD(false, true, false)
 #undef CCV_UPD
+    } else if (vec == 1) {
+        const int64_t blocks = (a.B * a.n_lane_per_row + 255) / 256;
+#define CCV_UPD(S, F, B) \
+        if (!!silu == S && wf32 == F && bias == B) return launch(k_update_any<S, F, B>, blocks, a, s);
+        CCV_UPD(true, false, true) CCV_UPD(true, false, false) CCV_UPD(true, true, false)
+        CCV_UPD(false, false, true) CCV_UPD(false, false, false) CCV_UPD(false, true, false)
+#undef CCV_UPD
+    }
     return hipErrorInvalidValue;
 }
+
+int update_rows_per_lane() { return CCV_UPD_ROWS; }
 
 hipError_t launch_validate(const int32_t *cu, int64_t n_seq, int64_t total, uint32_t *flags,
                            int overwrite, hipStream_t s) {
