@@ -44,6 +44,11 @@
 #ifndef CCV_UPD_VEC
 #define CCV_UPD_VEC 8
 #endif
+// The forward software-pipelines its loads (fewer, fatter waves) from this
+// many input bytes on; smaller inputs keep more waves per SIMD instead.
+#ifndef CCV_FWD_PIPE_MIN_BYTES
+#define CCV_FWD_PIPE_MIN_BYTES (int64_t(1) << 28)
+#endif
 #ifndef CCV_BWD_VEC
 #define CCV_BWD_VEC 4           // the backward kernels are built for 4 or 1
 #endif
@@ -330,6 +335,7 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     a.cu = p.packed ? static_cast<const int32_t *>(cu_seqlens->data) : nullptr;
     a.n_seq = p.N;
     a.err = p.packed ? err_flag : nullptr;
+    a.pipe = p.B * p.D * p.T * 2 >= CCV_FWD_PIPE_MIN_BYTES;
     const int silu = activation == CCV_ACT_SILU;
     const int64_t cap = CCV_FWD_ROUNDS > 0 ? ccv::fwd_resident_blocks(a, vec, silu, p.packed) : 0;
     const Geometry g = geometry(p, vec, ccv::kFwdWavesT, ccv::kFwdWavesC, cap, CCV_FWD_ROUNDS,

@@ -54,6 +54,7 @@ struct FwdArgs {
     int64_t n_block;           // grid size
     int cu_in_lds;             // stage + validate cu_seqlens in LDS
     int nt_load;               // stream the bulk loads with the non-temporal policy
+    int pipe;                  // software-pipelined body (8-channel lanes, large inputs)
 };
 
 struct BwdArgs {

@@ -39,18 +39,22 @@ constexpr uint32_t kFirstNonzero = 0x1u, kLastMismatch = 0x2u, kDecreasing = 0x4
 #ifndef CCV_BWD_UNROLL
 #define CCV_BWD_UNROLL 4
 #endif
-// Lower bound on resident waves per SIMD (register budget), measured best.
+#ifndef CCV_BWD_PIPE
+#define CCV_BWD_PIPE 1
+#endif
+// Lower bound on resident waves per SIMD (register budget), measured best:
+// the forward keeps 4 waves, or 3 when it software-pipelines its loads.
 #ifndef CCV_FWD_MIN_WAVES
 #define CCV_FWD_MIN_WAVES 4
 #endif
+#ifndef CCV_FWD_PIPE_MIN_WAVES
+#define CCV_FWD_PIPE_MIN_WAVES 3
+#endif
 #ifndef CCV_BWD_MIN_WAVES
-#define CCV_BWD_MIN_WAVES 3
+#define CCV_BWD_MIN_WAVES 2
 #endif
-#ifdef CCV_FWD_MIN_WAVES
-#define CCV_FWD_ATTR __attribute__((amdgpu_waves_per_eu(CCV_FWD_MIN_WAVES)))
-#else
-#define CCV_FWD_ATTR
-#endif
+#define CCV_FWD_ATTR \
+    __attribute__((amdgpu_waves_per_eu(PIPE ? CCV_FWD_PIPE_MIN_WAVES : CCV_FWD_MIN_WAVES)))
 #ifdef CCV_BWD_MIN_WAVES
 #define CCV_BWD_ATTR __attribute__((amdgpu_waves_per_eu(CCV_BWD_MIN_WAVES)))
 #else
@@ -345,7 +349,7 @@ __device__ __forceinline__ int64_t find_row(const int32_t *cu, int64_t n, int64_
 // ===========================================================================
 // Forward
 // ===========================================================================
-template <int VEC, bool SILU, bool NTL>
+template <int VEC, bool SILU, bool NTL, bool PIPE>
 __device__ __forceinline__ void fwd_piece(const FwdArgs &a, int64_t b, int64_t r, int64_t s,
                                           int64_t e, int64_t ta, int64_t tb, int64_t c0,
                                           const float (&w)[W][VEC], const float (&bias)[VEC]) {
@@ -382,11 +386,31 @@ __device__ __forceinline__ void fwd_piece(const FwdArgs &a, int64_t b, int64_t r
     } else {
         finish_left_halo<VEC>(halo, a.init, r, s, ta, c0, win);
     }
-    for (; t + U <= tb; t += U) {
-        Raw<VEC> raw[U];
+    if constexpr (PIPE) {
+        // Software pipeline: the next batch's loads are in flight while the
+        // current batch computes.
+        if (t + U <= tb) {
+            Raw<VEC> cur_raw[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) raw[u] = load_raw<VEC, NTL>(xb + (t + u) * xs_t, xs_d);
-        run_batch(t, raw);
+            for (int u = 0; u < U; ++u) cur_raw[u] = load_raw<VEC, NTL>(xb + (t + u) * xs_t, xs_d);
+            for (; t + 2 * U <= tb; t += U) {
+                Raw<VEC> nxt[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) nxt[u] = load_raw<VEC, NTL>(xb + (t + U + u) * xs_t, xs_d);
+                run_batch(t, cur_raw);
+#pragma unroll
+                for (int u = 0; u < U; ++u) cur_raw[u] = nxt[u];
+            }
+            run_batch(t, cur_raw);
+            t += U;
+        }
+    } else {
+        for (; t + U <= tb; t += U) {
+            Raw<VEC> raw[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) raw[u] = load_raw<VEC, NTL>(xb + (t + u) * xs_t, xs_d);
+            run_batch(t, raw);
+        }
     }
     for (; t < tb; ++t) {
         float cur[VEC], out[VEC];
@@ -409,7 +433,7 @@ __device__ __forceinline__ void fwd_piece(const FwdArgs &a, int64_t b, int64_t r
     }
 }
 
-template <int VEC, bool SILU, bool PACKED, int FK>
+template <int VEC, bool SILU, bool PACKED, int FK, bool PIPE>
 __global__ __launch_bounds__(256) CCV_FWD_ATTR void k_fwd_chan(FwdArgs a) {
     __shared__ int32_t s_cu[PACKED ? kLdsCuMax : 1];
     __shared__ uint32_t s_bad;
@@ -435,14 +459,14 @@ __global__ __launch_bounds__(256) CCV_FWD_ATTR void k_fwd_chan(FwdArgs a) {
     auto run = [&](auto ntl) {
         constexpr bool NTL = decltype(ntl)::value;
         if constexpr (!PACKED) {
-            fwd_piece<VEC, SILU, NTL>(a, b, b, 0, a.T, t0, t1, c0, w, bias);
+            fwd_piece<VEC, SILU, NTL, PIPE>(a, b, b, 0, a.T, t0, t1, c0, w, bias);
         } else {
             const int32_t *cu = a.cu_in_lds ? s_cu : a.cu;
             for (int64_t i = find_row(cu, a.n_seq, t0); i < a.n_seq; ++i) {
                 const int64_t s = cu[i], e = cu[i + 1];
                 if (s >= t1) break;
-                fwd_piece<VEC, SILU, NTL>(a, 0, i, s, e, s > t0 ? s : t0, e < t1 ? e : t1, c0,
-                                          w, bias);
+                fwd_piece<VEC, SILU, NTL, PIPE>(a, 0, i, s, e, s > t0 ? s : t0, e < t1 ? e : t1,
+                                                c0, w, bias);
             }
         }
     };
@@ -611,10 +635,31 @@ __device__ __forceinline__ void bwd_piece(const BwdArgs &a, BwdLane<VEC, SILU, B
 #pragma unroll
         for (int h = 0; h < W - 1; ++h) generic_step(ta + h, hx[h], hd[h]);
     }
-    for (; tau + U <= tb; tau += U) {
-        Raw<VEC> rx[U], rd[U];
-        load_batch(tau, rx, rd);
-        body_batch(tau, rx, rd);
+    if constexpr (CCV_BWD_PIPE) {
+        // Software pipeline: the next batch's loads are in flight while the
+        // current batch computes.
+        if (tau + U <= tb) {
+            Raw<VEC> rx[U], rd[U];
+            load_batch(tau, rx, rd);
+            for (; tau + 2 * U <= tb; tau += U) {
+                Raw<VEC> nx[U], nd[U];
+                load_batch(tau + U, nx, nd);
+                body_batch(tau, rx, rd);
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    rx[u] = nx[u];
+                    rd[u] = nd[u];
+                }
+            }
+            body_batch(tau, rx, rd);
+            tau += U;
+        }
+    } else {
+        for (; tau + U <= tb; tau += U) {
+            Raw<VEC> rx[U], rd[U];
+            load_batch(tau, rx, rd);
+            body_batch(tau, rx, rd);
+        }
     }
     for (; tau < tb; ++tau) {
         float cur[VEC], dyv[VEC], gcur[VEC], v[VEC];
@@ -930,18 +975,19 @@ int64_t resident_blocks(const void *kernel) {
     return static_cast<int64_t>(cus) * per_cu;
 }
 
-template <int V, bool S, bool P, int F>
+template <int V, bool S, bool P, int F, bool Q>
 hipError_t fwd_one(const FwdArgs &a, hipStream_t s) {
     if (s == kQueryStream) return hipSuccess;
-    return launch(k_fwd_chan<V, S, P, F>, a.n_block, a, s);
+    return launch(k_fwd_chan<V, S, P, F, Q>, a.n_block, a, s);
 }
 
-template <int V>
+// The software-pipelined forward is built for 8-channel lanes only.
+template <int V, bool Q>
 hipError_t fwd_vec(const FwdArgs &a, int silu, int packed, int fk, hipStream_t s, int64_t *cap) {
-#define CCV_FWD(S, P, F)                                                                   \
-    if (!!silu == S && !!packed == P && fk == F) {                                         \
-        if (cap) *cap = resident_blocks(reinterpret_cast<const void *>(k_fwd_chan<V, S, P, F>)); \
-        return fwd_one<V, S, P, F>(a, s);                                                  \
+#define CCV_FWD(S, P, F)                                                                       \
+    if (!!silu == S && !!packed == P && fk == F) {                                             \
+        if (cap) *cap = resident_blocks(reinterpret_cast<const void *>(k_fwd_chan<V, S, P, F, Q>)); \
+        return fwd_one<V, S, P, F, Q>(a, s);                                                   \
     }
 #define CCV_FWD_K(S, P) CCV_FWD(S, P, kBf16) CCV_FWD(S, P, kBf16Bias) CCV_FWD(S, P, kF32)
     CCV_FWD_K(true, false) CCV_FWD_K(true, true) CCV_FWD_K(false, false) CCV_FWD_K(false, true)
@@ -950,20 +996,23 @@ hipError_t fwd_vec(const FwdArgs &a, int silu, int packed, int fk, hipStream_t s
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_fwd(const FwdArgs &a, int vec, int silu, int packed, hipStream_t s) {
+hipError_t fwd_dispatch(const FwdArgs &a, int vec, int silu, int packed, hipStream_t s,
+                        int64_t *cap) {
     const int fk = filter_kind(a);
-    if (vec == 8) return fwd_vec<8>(a, silu, packed, fk, s, nullptr);
-    if (vec == 4) return fwd_vec<4>(a, silu, packed, fk, s, nullptr);
-    if (vec == 1) return fwd_vec<1>(a, silu, packed, fk, s, nullptr);
+    if (vec == 8 && a.pipe) return fwd_vec<8, true>(a, silu, packed, fk, s, cap);
+    if (vec == 8) return fwd_vec<8, false>(a, silu, packed, fk, s, cap);
+    if (vec == 4) return fwd_vec<4, false>(a, silu, packed, fk, s, cap);
+    if (vec == 1) return fwd_vec<1, false>(a, silu, packed, fk, s, cap);
     return hipErrorInvalidValue;
 }
 
+hipError_t launch_fwd(const FwdArgs &a, int vec, int silu, int packed, hipStream_t s) {
+    return fwd_dispatch(a, vec, silu, packed, s, nullptr);
+}
+
 int64_t fwd_resident_blocks(const FwdArgs &a, int vec, int silu, int packed) {
-    const int fk = filter_kind(a);
     int64_t cap = 0;
-    if (vec == 8) fwd_vec<8>(a, silu, packed, fk, kQueryStream, &cap);
-    if (vec == 4) fwd_vec<4>(a, silu, packed, fk, kQueryStream, &cap);
-    if (vec == 1) fwd_vec<1>(a, silu, packed, fk, kQueryStream, &cap);
+    fwd_dispatch(a, vec, silu, packed, kQueryStream, &cap);
     return cap;
 }
 
