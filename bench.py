@@ -38,8 +38,7 @@ METRIC = "achieved HBM GB/s (% of MI355X peak) for fwd, bwd and update at 1 GPU"
 
 
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = [os.path.join(ROOT, "depthwise_causal_conv1d_02_amd", "csrc", f)
-                  for f in ("ccv_kernels.hip", "ccv_api.cpp", "ccv_internal.h")]
+CSRC = os.path.join(ROOT, "depthwise_causal_conv1d_02_amd", "csrc")
 OP_KERNEL = {"fwd": "k_fwd_chan", "bwd": "k_bwd_chan", "update": "k_update"}
 
 
@@ -48,9 +47,9 @@ def source_hash():
     of the kernels are not reported."""
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as fh:
+            h.update(name.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 

@@ -7,6 +7,7 @@ import ctypes
 import os
 import threading
 
+ABI_VERSION = 2  # CCV_ABI_VERSION of include/ccv.h
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libccv.so")
 
 CCV_DTYPE_BF16, CCV_DTYPE_F32, CCV_DTYPE_I32 = 0, 1, 2
@@ -19,6 +20,9 @@ CCV_ERR_ALIAS = -2
 CCV_ERR_UNSUPPORTED = -3
 CCV_ERR_NONDETERMINISTIC = -4
 CCV_ERR_HIP = -5
+
+# option bits of ccv_fwd / ccv_bwd / ccv_update
+CCV_OPT_F32_FILTER_BIAS, CCV_OPT_DETERMINISTIC_DBIAS = 0x1, 0x2
 
 CU_FIRST_NONZERO, CU_LAST_MISMATCH, CU_DECREASING, CU_EMPTY = 0x1, 0x2, 0x4, 0x8
 CU_BIT_NAMES = {CU_FIRST_NONZERO: "first offset is not zero",
@@ -46,12 +50,12 @@ class LibraryMissing(RuntimeError):
 
 
 def _declare(lib):
-    i, u32p, sz = ctypes.c_int, ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_size_t)
-    lib.ccv_fwd.argtypes = [P, P, P, P, P, P, P, P, i, _vp, _vp]
+    i, u32, sz = ctypes.c_int, ctypes.c_uint32, ctypes.POINTER(ctypes.c_size_t)
+    lib.ccv_fwd.argtypes = [P, P, P, P, P, P, P, P, i, u32, _vp, _vp]
     lib.ccv_fwd.restype = i
-    lib.ccv_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, i, i, i, _vp, sz, _vp, _vp]
+    lib.ccv_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, i, i, i, u32, _vp, sz, _vp, _vp]
     lib.ccv_bwd.restype = i
-    lib.ccv_update.argtypes = [P, P, P, P, P, i, _vp]
+    lib.ccv_update.argtypes = [P, P, P, P, P, i, u32, _vp]
     lib.ccv_update.restype = i
     lib.ccv_validate_cu_seqlens.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64, _vp, _vp]
     lib.ccv_validate_cu_seqlens.restype = i
@@ -59,7 +63,6 @@ def _declare(lib):
     lib.ccv_abi_version.restype = i
     lib.ccv_status_string.argtypes = [i]
     lib.ccv_status_string.restype = ctypes.c_char_p
-    del u32p
 
 
 def lib(path=None):
@@ -77,7 +80,7 @@ def lib(path=None):
                     % LIB_PATH)
             l = ctypes.CDLL(LIB_PATH)
             _declare(l)
-            if l.ccv_abi_version() != 1:
+            if l.ccv_abi_version() != ABI_VERSION:
                 raise LibraryMissing("libccv.so ABI version mismatch")
             _lib = l
     return _lib

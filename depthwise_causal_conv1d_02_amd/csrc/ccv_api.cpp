@@ -55,7 +55,8 @@
 
 namespace {
 
-using ccv::kWidth;
+constexpr uint32_t kKnownOptions = CCV_OPT_F32_FILTER_BIAS | CCV_OPT_DETERMINISTIC_DBIAS;
+
 
 bool present(const ccv_tensor *t) { return t != nullptr && t->data != nullptr; }
 
@@ -146,7 +147,7 @@ bool vec_ok(const ccv_tensor *t, int vec) {
 }
 
 bool filter_vec(const ccv_tensor *w) {
-    return w->stride[1] == 1 && w->stride[0] == kWidth && aligned16(w->data);
+    return w->stride[1] == 1 && w->stride[0] == w->shape[1] && aligned16(w->data);
 }
 
 // The widest lane width (preferred first, then 4, else 1) every tensor
@@ -175,13 +176,25 @@ ccv::Strided3 s3(const ccv_tensor *t) {
 
 // Shared checks of the full-sequence calls (forward and backward inputs).
 struct Problem {
-    int64_t B = 0, D = 0, T = 0, N = 0, R = 0;
+    int64_t B = 0, D = 0, T = 0, N = 0, R = 0, W = 0;
     bool packed = false;
 };
 
+// The filter and bias dtypes: a BF16 filter takes a BF16 bias; an FP32
+// filter takes no bias, or (with CCV_OPT_F32_FILTER_BIAS) an FP32 one.
+// Called after the shape checks; returns INVALID or the explicit decline.
+int check_filter_dtypes(const ccv_tensor *weight, const ccv_tensor *bias, uint32_t options) {
+    if (!present(bias)) return CCV_OK;
+    if (weight->dtype == CCV_DTYPE_BF16)
+        return bias->dtype == CCV_DTYPE_BF16 ? CCV_OK : CCV_ERR_INVALID_ARG;
+    if (bias->dtype != CCV_DTYPE_BF16 && bias->dtype != CCV_DTYPE_F32) return CCV_ERR_INVALID_ARG;
+    if (!(options & CCV_OPT_F32_FILTER_BIAS)) return CCV_ERR_UNSUPPORTED;
+    return bias->dtype == CCV_DTYPE_F32 ? CCV_OK : CCV_ERR_INVALID_ARG;
+}
+
 int check_inputs(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bias,
                  const ccv_tensor *cu, const ccv_tensor *seq_idx, const ccv_tensor *init,
-                 int activation, const uint32_t *err_flag, Problem &p) {
+                 int activation, const uint32_t *err_flag, uint32_t options, Problem &p) {
     if (!present(x) || !well_formed(x, 3) || x->dtype != CCV_DTYPE_BF16) return CCV_ERR_INVALID_ARG;
     p.B = x->shape[0];
     p.D = x->shape[1];
@@ -191,9 +204,9 @@ int check_inputs(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor
         weight->shape[1] < 1 ||
         (weight->dtype != CCV_DTYPE_BF16 && weight->dtype != CCV_DTYPE_F32))
         return CCV_ERR_INVALID_ARG;
-    if (present(bias) && (!well_formed(bias, 1) || !shape_is(bias, p.D) ||
-                          bias->dtype != CCV_DTYPE_BF16))
+    if (present(bias) && (!well_formed(bias, 1) || !shape_is(bias, p.D)))
         return CCV_ERR_INVALID_ARG;
+    if (options & ~kKnownOptions) return CCV_ERR_INVALID_ARG;
     // seq_idx and cu_seqlens are mutually exclusive; seq_idx alone is reserved.
     if (present(seq_idx) && present(cu)) return CCV_ERR_INVALID_ARG;
     if (present(cu)) {
@@ -207,18 +220,19 @@ int check_inputs(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor
     if (present(init) && (!well_formed(init, 3) || init->dtype != CCV_DTYPE_BF16 ||
                           !shape_is(init, p.R, p.D, weight->shape[1] - 1)))
         return CCV_ERR_INVALID_ARG;
-    // Declines: the reserved keyword, the width, FP32 filter with a bias,
-    // the activation set.
+    // Declines: the reserved keyword, the width, FP32 filter with a bias
+    // (unless opted in), the activation set.
     if (present(seq_idx)) return CCV_ERR_UNSUPPORTED;
-    if (weight->shape[1] != kWidth) return CCV_ERR_UNSUPPORTED;
-    if (weight->dtype == CCV_DTYPE_F32 && present(bias)) return CCV_ERR_UNSUPPORTED;
+    p.W = weight->shape[1];
+    if (p.W < ccv::kMinWidth || p.W > ccv::kMaxWidth) return CCV_ERR_UNSUPPORTED;
+    if (int rc = check_filter_dtypes(weight, bias, options)) return rc;
     if (activation != CCV_ACT_NONE && activation != CCV_ACT_SILU) return CCV_ERR_UNSUPPORTED;
     return CCV_OK;
 }
 
 int check_state_out(const ccv_tensor *t, const Problem &p) {
     if (!present(t)) return CCV_OK;
-    if (!well_formed(t, 3) || t->dtype != CCV_DTYPE_BF16 || !shape_is(t, p.R, p.D, kWidth - 1) ||
+    if (!well_formed(t, 3) || t->dtype != CCV_DTYPE_BF16 || !shape_is(t, p.R, p.D, p.W - 1) ||
         !injective(t))
         return CCV_ERR_INVALID_ARG;
     return CCV_OK;
@@ -303,11 +317,11 @@ const char *ccv_status_string(int status) {
 int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bias,
             const ccv_tensor *cu_seqlens, const ccv_tensor *seq_idx,
             const ccv_tensor *initial_states, const ccv_tensor *y,
-            const ccv_tensor *final_states, int activation, uint32_t *err_flag,
-            hipStream_t stream) {
+            const ccv_tensor *final_states, int activation, uint32_t options,
+            uint32_t *err_flag, hipStream_t stream) {
     Problem p;
     int rc = check_inputs(x, weight, bias, cu_seqlens, seq_idx, initial_states, activation,
-                          err_flag, p);
+                          err_flag, options, p);
     if (rc != CCV_OK) return rc;
     if ((rc = check_act_tensor(y, p, true)) != CCV_OK) return rc;
     if ((rc = check_state_out(final_states, p)) != CCV_OK) return rc;
@@ -321,6 +335,7 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     const int vec = pick_vec(CCV_FWD_VEC, weight, bias, x, y, nullptr);
     ccv::FwdArgs a;
     memset(&a, 0, sizeof(a));
+    a.width = static_cast<int>(p.W);
     a.x = s3(x);
     a.y = s3(y);
     a.init = s3(initial_states);
@@ -364,40 +379,43 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
             const ccv_tensor *dfinal_states, const ccv_tensor *dx,
             const ccv_tensor *dweight, const ccv_tensor *dbias,
             const ccv_tensor *dinitial_states, int activation, int deterministic,
-            int warn_only, void *workspace, size_t *workspace_bytes,
+            int warn_only, uint32_t options, void *workspace, size_t *workspace_bytes,
             uint32_t *err_flag, hipStream_t stream) {
     Problem p;
     int rc = check_inputs(x, weight, bias, cu_seqlens, seq_idx, initial_states, activation,
-                          err_flag, p);
+                          err_flag, options, p);
     if (rc != CCV_OK) return rc;
     if ((rc = check_act_tensor(dy, p, false)) != CCV_OK) return rc;
     if ((rc = check_act_tensor(dx, p, true)) != CCV_OK) return rc;
     if (present(dfinal_states) &&
         (!well_formed(dfinal_states, 3) || dfinal_states->dtype != CCV_DTYPE_BF16 ||
-         !shape_is(dfinal_states, p.R, p.D, kWidth - 1)))
+         !shape_is(dfinal_states, p.R, p.D, p.W - 1)))
         return CCV_ERR_INVALID_ARG;
     if ((rc = check_state_out(dinitial_states, p)) != CCV_OK) return rc;
     if (present(dinitial_states) && !present(initial_states)) return CCV_ERR_INVALID_ARG;
     // dweight [D,W] and dbias [D]: FP32, contiguous.
     if (!present(dweight) || !well_formed(dweight, 2) || dweight->dtype != CCV_DTYPE_F32 ||
-        !shape_is(dweight, p.D, kWidth) || dweight->stride[0] != kWidth || dweight->stride[1] != 1)
+        !shape_is(dweight, p.D, p.W) || dweight->stride[0] != p.W || dweight->stride[1] != 1)
         return CCV_ERR_INVALID_ARG;
     if (present(bias) != present(dbias)) return CCV_ERR_INVALID_ARG;
     if (present(dbias) && (!well_formed(dbias, 1) || dbias->dtype != CCV_DTYPE_F32 ||
                            !shape_is(dbias, p.D) || dbias->stride[0] != 1))
         return CCV_ERR_INVALID_ARG;
 
-    // Determinism policy (cuDNN FE "Causal Conv1d", the determinism paragraph).
+    // Determinism policy (cuDNN FE "Causal Conv1d", the determinism
+    // paragraph): a bias has no deterministic dbias route unless the caller
+    // opts into dbias partials (one more FP32 column per channel).
     int status = CCV_OK;
     bool use_partials = false;
     if (deterministic) {
-        if (present(bias)) {
+        if (present(bias) && !(options & CCV_OPT_DETERMINISTIC_DBIAS)) {
             if (!warn_only) return CCV_ERR_NONDETERMINISTIC;
             status = CCV_WARN_NONDETERMINISTIC;
         } else {
             use_partials = true;
         }
     }
+    const int64_t kp = p.W + (present(bias) ? 1 : 0);  // partial columns per channel
     const int vec = pick_vec(CCV_BWD_VEC, weight, bias, x, dy, dx);
     // The partials of the deterministic route depend on the shape only (a
     // grid sized by target waves); the atomic route sizes its grid by the
@@ -406,7 +424,7 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
                           CCV_BWD_MIN_CHUNK);
     const int64_t n_part = (p.packed ? 1 : p.B) * g.n_tblk;
     const size_t need = use_partials
-                            ? static_cast<size_t>(n_part) * static_cast<size_t>(p.D) * kWidth * 4
+                            ? static_cast<size_t>(n_part) * static_cast<size_t>(p.D * kp) * 4
                             : 0;
     if (workspace == nullptr && workspace_bytes != nullptr) {  // size query
         *workspace_bytes = need;
@@ -426,6 +444,7 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
 
     ccv::BwdArgs a;
     memset(&a, 0, sizeof(a));
+    a.width = static_cast<int>(p.W);
     a.x = s3(x);
     a.dy = s3(dy);
     a.dx = s3(dx);
@@ -442,6 +461,7 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     a.dw = static_cast<float *>(dweight->data);
     a.db = present(dbias) ? static_cast<float *>(dbias->data) : nullptr;
     a.partial = use_partials ? static_cast<float *>(workspace) : nullptr;
+    a.part_stride = static_cast<int>(kp);
     a.cu = p.packed ? static_cast<const int32_t *>(cu_seqlens->data) : nullptr;
     a.n_seq = p.N;
     a.err = p.packed ? err_flag : nullptr;
@@ -468,14 +488,15 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     rc = hip_status(ccv::launch_bwd(a, vec, silu, p.packed, stream));
     if (rc != CCV_OK) return rc;
     if (use_partials) {
-        rc = hip_status(ccv::launch_dw_reduce(a.partial, n_part, p.D * kWidth, a.dw, stream));
+        rc = hip_status(ccv::launch_dw_reduce(a.partial, n_part, p.D, static_cast<int>(p.W),
+                                              static_cast<int>(kp), a.dw, a.db, stream));
         if (rc != CCV_OK) return rc;
     }
     return status;
 }
 
 int ccv_update(const ccv_tensor *x, const ccv_tensor *conv_state, const ccv_tensor *weight,
-               const ccv_tensor *bias, const ccv_tensor *y, int activation,
+               const ccv_tensor *bias, const ccv_tensor *y, int activation, uint32_t options,
                hipStream_t stream) {
     if (!present(x) || !well_formed(x, 2) || x->dtype != CCV_DTYPE_BF16) return CCV_ERR_INVALID_ARG;
     const int64_t B = x->shape[0], D = x->shape[1];
@@ -484,9 +505,9 @@ int ccv_update(const ccv_tensor *x, const ccv_tensor *conv_state, const ccv_tens
         weight->shape[1] < 1 ||
         (weight->dtype != CCV_DTYPE_BF16 && weight->dtype != CCV_DTYPE_F32))
         return CCV_ERR_INVALID_ARG;
-    if (present(bias) && (!well_formed(bias, 1) || !shape_is(bias, D) ||
-                          bias->dtype != CCV_DTYPE_BF16))
+    if (present(bias) && (!well_formed(bias, 1) || !shape_is(bias, D)))
         return CCV_ERR_INVALID_ARG;
+    if (options & ~kKnownOptions) return CCV_ERR_INVALID_ARG;
     if (!present(conv_state) || !well_formed(conv_state, 3) ||
         conv_state->dtype != CCV_DTYPE_BF16 ||
         !shape_is(conv_state, B, D, weight->shape[1] - 1) || !injective(conv_state))
@@ -494,8 +515,9 @@ int ccv_update(const ccv_tensor *x, const ccv_tensor *conv_state, const ccv_tens
     if (!present(y) || !well_formed(y, 2) || y->dtype != CCV_DTYPE_BF16 || !shape_is(y, B, D) ||
         !injective(y))
         return CCV_ERR_INVALID_ARG;
-    if (weight->shape[1] != kWidth) return CCV_ERR_UNSUPPORTED;
-    if (weight->dtype == CCV_DTYPE_F32 && present(bias)) return CCV_ERR_UNSUPPORTED;
+    const int64_t W = weight->shape[1];
+    if (W < ccv::kMinWidth || W > ccv::kMaxWidth) return CCV_ERR_UNSUPPORTED;
+    if (int rc = check_filter_dtypes(weight, bias, options)) return rc;
     if (activation != CCV_ACT_NONE && activation != CCV_ACT_SILU) return CCV_ERR_UNSUPPORTED;
     // conv_state is in/out by design; y and the state must not overlap any
     // other argument.
@@ -506,7 +528,7 @@ int ccv_update(const ccv_tensor *x, const ccv_tensor *conv_state, const ccv_tens
     // 8-channel lanes need unit channel strides, a contiguous state, a
     // contiguous filter and bias, and 16-byte aligned rows everywhere.
     const bool vec = CCV_UPD_VEC == 8 && D % 8 == 0 && x->stride[1] == 1 && y->stride[1] == 1 &&
-                     conv_state->stride[2] == 1 && conv_state->stride[1] == kWidth - 1 &&
+                     conv_state->stride[2] == 1 && conv_state->stride[1] == W - 1 &&
                      aligned16(x->data) && aligned16(y->data) && aligned16(conv_state->data) &&
                      (B == 1 || (x->stride[0] % 8 == 0 && y->stride[0] % 8 == 0 &&
                                  conv_state->stride[0] % 8 == 0)) &&
@@ -514,6 +536,7 @@ int ccv_update(const ccv_tensor *x, const ccv_tensor *conv_state, const ccv_tens
                      (!present(bias) || (bias->stride[0] == 1 && aligned16(bias->data)));
     ccv::UpdArgs a;
     memset(&a, 0, sizeof(a));
+    a.width = static_cast<int>(W);
     a.x = x->data;
     a.x_sb = x->stride[0];
     a.x_sd = x->stride[1];

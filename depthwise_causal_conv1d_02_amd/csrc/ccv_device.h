@@ -1,4 +1,5 @@
-// ccv_kernels.hip — gfx950 kernels of the depthwise causal conv1d.
+// ccv_device.h — gfx950 device code of the depthwise causal conv1d (all
+// kernels as templates; ccv_width.hip and ccv_misc.hip instantiate them).
 //
 // Operation (cuDNN FE "Causal Conv1d", tensor/state semantics and the
 // optimized route; tap order from the POPCORNBENCH trace's causal left-pad
@@ -20,6 +21,8 @@
 // sequence starts and every piece restarts its window from that sequence's
 // initial state (or zeros).  The offsets are staged in LDS, validated there
 // by every block (no host read) and searched there.
+#pragma once
+
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -28,8 +31,6 @@
 
 namespace ccv {
 namespace {
-
-constexpr int W = kWidth;
 constexpr uint32_t kFirstNonzero = 0x1u, kLastMismatch = 0x2u, kDecreasing = 0x4u,
                    kEmpty = 0x8u;
 
@@ -181,36 +182,49 @@ __device__ __forceinline__ void decode_tile(int64_t tile, int64_t n_t, int64_t n
 }
 
 // Filter kinds: the weight dtype and whether a bias is present.
-enum FilterKind { kBf16 = 0, kBf16Bias = 1, kF32 = 2 };
+// Filter kinds: the weight dtype and whether a bias is present.  The bias
+// has the weight's dtype (an FP32 filter with an FP32 bias is an opt-in of
+// the boundary).
+enum FilterKind { kBf16 = 0, kBf16Bias = 1, kF32 = 2, kF32Bias = 3 };
+constexpr bool fk_f32(int fk) { return fk == kF32 || fk == kF32Bias; }
+constexpr bool fk_bias(int fk) { return fk == kBf16Bias || fk == kF32Bias; }
 
 // Filter taps and bias of a lane's VEC channels, widened to FP32.  With
 // VEC >= 4 the host has verified a contiguous [D,W] filter and a contiguous
 // bias, both 16-byte aligned: every load is a vector load, all issued before
 // the first conversion.
-template <int VEC, int FK>
+template <int W, int VEC, int FK>
 __device__ __forceinline__ void load_filter(const void *wp, int64_t sd, int64_t sk,
                                             const void *bp, int64_t bs, int64_t c0,
                                             float (&w)[W][VEC], float (&bias)[VEC]) {
-    if constexpr (VEC >= 4) {
-        constexpr int kWordsPerCh = W * (FK == kF32 ? 4 : 2) / 4;   // 32-bit words per channel
-        constexpr int kVecs = VEC * kWordsPerCh / 4;                  // 16-byte loads
+    constexpr int kEl = fk_f32(FK) ? 4 : 2;                     // bytes per tap / bias
+    constexpr int kBytes = VEC * W * kEl;                       // a lane's filter bytes
+    if constexpr (VEC >= 4 && kBytes % 16 == 0) {
+        constexpr int kVecs = kBytes / 16;                      // 16-byte loads
+        constexpr int kBiasVecs = (VEC * kEl + 15) / 16;
         const u32x4_t *q = reinterpret_cast<const u32x4_t *>(
-            static_cast<const char *>(wp) + c0 * W * (FK == kF32 ? 4 : 2));
+            static_cast<const char *>(wp) + c0 * W * kEl);
         u32x4_t wv[kVecs];
 #pragma unroll
         for (int i = 0; i < kVecs; ++i) wv[i] = q[i];
         Raw<VEC> bv{};
+        u32x4_t bf[kBiasVecs];
         if constexpr (FK == kBf16Bias)
             bv = load_raw<VEC>(static_cast<const uint16_t *>(bp) + c0, 1);
+        if constexpr (FK == kF32Bias) {
+            const u32x4_t *bq =
+                reinterpret_cast<const u32x4_t *>(static_cast<const float *>(bp) + c0);
+#pragma unroll
+            for (int i = 0; i < kBiasVecs; ++i) bf[i] = bq[i];
+        }
 #pragma unroll
         for (int c = 0; c < VEC; ++c) {
 #pragma unroll
             for (int k = 0; k < W; ++k) {
-                if constexpr (FK == kF32) {
-                    const int e2 = c * W + k;
+                const int e2 = c * W + k;
+                if constexpr (fk_f32(FK)) {
                     w[k][c] = __uint_as_float(wv[e2 / 4][e2 % 4]);
                 } else {
-                    const int e2 = c * W + k;  // BF16 element index
                     const uint32_t word = wv[e2 / 8][(e2 % 8) / 2];
                     w[k][c] = (e2 % 2) ? hi_bf16(word) : lo_bf16(word);
                 }
@@ -218,6 +232,9 @@ __device__ __forceinline__ void load_filter(const void *wp, int64_t sd, int64_t 
         }
         if constexpr (FK == kBf16Bias) {
             unpack<VEC>(bv, bias);
+        } else if constexpr (FK == kF32Bias) {
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) bias[c] = __uint_as_float(bf[c / 4][c % 4]);
         } else {
 #pragma unroll
             for (int c = 0; c < VEC; ++c) bias[c] = 0.0f;
@@ -228,18 +245,21 @@ __device__ __forceinline__ void load_filter(const void *wp, int64_t sd, int64_t 
 #pragma unroll
             for (int k = 0; k < W; ++k) {
                 const int64_t off = (c0 + c) * sd + k * sk;
-                w[k][c] = FK == kF32 ? static_cast<const float *>(wp)[off]
+                w[k][c] = fk_f32(FK) ? static_cast<const float *>(wp)[off]
                                      : bf16_bits_to_f32(static_cast<const uint16_t *>(wp)[off]);
             }
-            bias[c] = FK == kBf16Bias
-                          ? bf16_bits_to_f32(static_cast<const uint16_t *>(bp)[(c0 + c) * bs])
-                          : 0.0f;
+            if constexpr (FK == kBf16Bias)
+                bias[c] = bf16_bits_to_f32(static_cast<const uint16_t *>(bp)[(c0 + c) * bs]);
+            else if constexpr (FK == kF32Bias)
+                bias[c] = static_cast<const float *>(bp)[(c0 + c) * bs];
+            else
+                bias[c] = 0.0f;
         }
     }
 }
 
 // z = bias + sum_k w[k] * v[k] with v = (win[0..W-2], cur), FP32 fused.
-template <int VEC>
+template <int W, int VEC>
 __device__ __forceinline__ float preact(const float (&w)[W][VEC], const float (&bias)[VEC],
                                         const float (&win)[W - 1][VEC], const float (&cur)[VEC],
                                         int c) {
@@ -249,7 +269,7 @@ __device__ __forceinline__ float preact(const float (&w)[W][VEC], const float (&
     return fmaf(w[W - 1][c], cur[c], z);
 }
 
-template <int VEC>
+template <int W, int VEC>
 __device__ __forceinline__ void shift_in(float (&win)[W - 1][VEC], const float (&cur)[VEC]) {
 #pragma unroll
     for (int k = 0; k < W - 2; ++k)
@@ -265,7 +285,7 @@ __device__ __forceinline__ void shift_in(float (&win)[W - 1][VEC], const float (
 // input loads use addresses clamped into the row, so they can be issued
 // early and together (issue_left_halo); finish_left_halo then replaces the
 // values that lie before the row.
-template <int VEC>
+template <int W, int VEC>
 __device__ __forceinline__ void issue_left_halo(const uint16_t *xb, int64_t xs_d, int64_t xs_t,
                                                 int64_t s, int64_t ta, Raw<VEC> (&raw)[W - 1]) {
 #pragma unroll
@@ -275,7 +295,7 @@ __device__ __forceinline__ void issue_left_halo(const uint16_t *xb, int64_t xs_d
     }
 }
 
-template <int VEC>
+template <int W, int VEC>
 __device__ __forceinline__ void finish_left_halo(const Raw<VEC> (&raw)[W - 1],
                                                  const Strided3 &init, int64_t r, int64_t s,
                                                  int64_t ta, int64_t c0,
@@ -349,7 +369,7 @@ __device__ __forceinline__ int64_t find_row(const int32_t *cu, int64_t n, int64_
 // ===========================================================================
 // Forward
 // ===========================================================================
-template <int VEC, bool SILU, bool NTL, bool PIPE>
+template <int W, int VEC, bool SILU, bool NTL, bool PIPE>
 __device__ __forceinline__ void fwd_piece(const FwdArgs &a, int64_t b, int64_t r, int64_t s,
                                           int64_t e, int64_t ta, int64_t tb, int64_t c0,
                                           const float (&w)[W][VEC], const float (&bias)[VEC]) {
@@ -366,25 +386,25 @@ __device__ __forceinline__ void fwd_piece(const FwdArgs &a, int64_t b, int64_t r
             float cur[VEC], out[VEC];
             unpack<VEC>(raw[u], cur);
 #pragma unroll
-            for (int c = 0; c < VEC; ++c) out[c] = act<SILU>(preact<VEC>(w, bias, win, cur, c));
+            for (int c = 0; c < VEC; ++c) out[c] = act<SILU>(preact<W, VEC>(w, bias, win, cur, c));
             store_vec<VEC, true>(yb + (t + u) * ys_t, ys_d, out);
-            shift_in<VEC>(win, cur);
+            shift_in<W, VEC>(win, cur);
         }
     };
 
     // The halo loads go out together with the first batch's.
     Raw<VEC> halo[W - 1];
-    issue_left_halo<VEC>(xb, xs_d, xs_t, s, ta, halo);
+    issue_left_halo<W, VEC>(xb, xs_d, xs_t, s, ta, halo);
     int64_t t = ta;
     if (t + U <= tb) {
         Raw<VEC> raw[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) raw[u] = load_raw<VEC, NTL>(xb + (t + u) * xs_t, xs_d);
-        finish_left_halo<VEC>(halo, a.init, r, s, ta, c0, win);
+        finish_left_halo<W, VEC>(halo, a.init, r, s, ta, c0, win);
         run_batch(t, raw);
         t += U;
     } else {
-        finish_left_halo<VEC>(halo, a.init, r, s, ta, c0, win);
+        finish_left_halo<W, VEC>(halo, a.init, r, s, ta, c0, win);
     }
     if constexpr (PIPE) {
         // Software pipeline: the next batch's loads are in flight while the
@@ -416,9 +436,9 @@ __device__ __forceinline__ void fwd_piece(const FwdArgs &a, int64_t b, int64_t r
         float cur[VEC], out[VEC];
         unpack<VEC>(load_raw<VEC, NTL>(xb + t * xs_t, xs_d), cur);
 #pragma unroll
-        for (int c = 0; c < VEC; ++c) out[c] = act<SILU>(preact<VEC>(w, bias, win, cur, c));
+        for (int c = 0; c < VEC; ++c) out[c] = act<SILU>(preact<W, VEC>(w, bias, win, cur, c));
         store_vec<VEC, true>(yb + t * ys_t, ys_d, out);
-        shift_in<VEC>(win, cur);
+        shift_in<W, VEC>(win, cur);
     }
     // The row ends inside this piece: its last W-1 extended tokens are the
     // window (cuDNN FE "Causal Conv1d": returned final_states).
@@ -433,7 +453,7 @@ __device__ __forceinline__ void fwd_piece(const FwdArgs &a, int64_t b, int64_t r
     }
 }
 
-template <int VEC, bool SILU, bool PACKED, int FK, bool PIPE>
+template <int W, int VEC, bool SILU, bool PACKED, int FK, bool PIPE>
 __global__ __launch_bounds__(256) CCV_FWD_ATTR void k_fwd_chan(FwdArgs a) {
     __shared__ int32_t s_cu[PACKED ? kLdsCuMax : 1];
     __shared__ uint32_t s_bad;
@@ -453,19 +473,19 @@ __global__ __launch_bounds__(256) CCV_FWD_ATTR void k_fwd_chan(FwdArgs a) {
     const int64_t t1 = min(t0 + a.L, a.T);
 
     float w[W][VEC], bias[VEC];
-    load_filter<VEC, FK>(a.w, a.w_sd, a.w_sk, a.bias, a.b_s, c0, w, bias);
+    load_filter<W, VEC, FK>(a.w, a.w_sd, a.w_sk, a.bias, a.b_s, c0, w, bias);
 
     // Non-temporal loads only when the operands exceed what caches can keep.
     auto run = [&](auto ntl) {
         constexpr bool NTL = decltype(ntl)::value;
         if constexpr (!PACKED) {
-            fwd_piece<VEC, SILU, NTL, PIPE>(a, b, b, 0, a.T, t0, t1, c0, w, bias);
+            fwd_piece<W, VEC, SILU, NTL, PIPE>(a, b, b, 0, a.T, t0, t1, c0, w, bias);
         } else {
             const int32_t *cu = a.cu_in_lds ? s_cu : a.cu;
             for (int64_t i = find_row(cu, a.n_seq, t0); i < a.n_seq; ++i) {
                 const int64_t s = cu[i], e = cu[i + 1];
                 if (s >= t1) break;
-                fwd_piece<VEC, SILU, NTL, PIPE>(a, 0, i, s, e, s > t0 ? s : t0, e < t1 ? e : t1,
+                fwd_piece<W, VEC, SILU, NTL, PIPE>(a, 0, i, s, e, s > t0 ? s : t0, e < t1 ? e : t1,
                                                 c0, w, bias);
             }
         }
@@ -486,14 +506,14 @@ __global__ __launch_bounds__(256) CCV_FWD_ATTR void k_fwd_chan(FwdArgs a) {
 // emits dx_ext[tau-(W-1)] from the W-1 previous g's held in registers.
 // Emission before ta happens only when the piece starts the row (dinit).
 // ===========================================================================
-template <int VEC, bool SILU, bool BIAS>
+template <int W, int VEC, bool SILU, bool BIAS>
 struct BwdLane {
     float w[W][VEC], bias[VEC];
     float dw[W][VEC], db[VEC];
 };
 
-template <int VEC, bool SILU, bool BIAS, bool NTL>
-__device__ __forceinline__ void bwd_piece(const BwdArgs &a, BwdLane<VEC, SILU, BIAS> &L,
+template <int W, int VEC, bool SILU, bool BIAS, bool NTL>
+__device__ __forceinline__ void bwd_piece(const BwdArgs &a, BwdLane<W, VEC, SILU, BIAS> &L,
                                           int64_t b, int64_t r, int64_t s, int64_t e,
                                           int64_t ta, int64_t tb, int64_t c0) {
     constexpr int U = CCV_BWD_UNROLL;
@@ -534,7 +554,7 @@ __device__ __forceinline__ void bwd_piece(const BwdArgs &a, BwdLane<VEC, SILU, B
                          bool count) {
 #pragma unroll
         for (int c = 0; c < VEC; ++c) {
-            const float z = preact<VEC>(L.w, L.bias, xw, cur, c);
+            const float z = preact<W, VEC>(L.w, L.bias, xw, cur, c);
             gcur[c] = dyv[c] * act_slope<SILU>(z);
         }
         if (count) {
@@ -555,7 +575,7 @@ __device__ __forceinline__ void bwd_piece(const BwdArgs &a, BwdLane<VEC, SILU, B
             unpack<VEC>(rxv, cur);
             unpack<VEC>(rdv, dyv);
             grad_step(cur, dyv, gcur, tau < tb);
-            shift_in<VEC>(xw, cur);
+            shift_in<W, VEC>(xw, cur);
         } else {
 #pragma unroll
             for (int c = 0; c < VEC; ++c) gcur[c] = 0.0f;
@@ -602,7 +622,7 @@ __device__ __forceinline__ void bwd_piece(const BwdArgs &a, BwdLane<VEC, SILU, B
             unpack<VEC>(rx[u], cur);
             unpack<VEC>(rd[u], dyv);
             grad_step(cur, dyv, gcur, true);
-            shift_in<VEC>(xw, cur);
+            shift_in<W, VEC>(xw, cur);
             emit_value(gcur, v);
             store_vec<VEC, true>(dxb + (tau + u - (W - 1)) * ds_t, ds_d, v);
             shift_g(gcur);
@@ -619,19 +639,19 @@ __device__ __forceinline__ void bwd_piece(const BwdArgs &a, BwdLane<VEC, SILU, B
     // Prologue: the left halo, the head (tau in [ta, ta + W-1)) and the first
     // body batch are all requested before anything waits.
     Raw<VEC> halo[W - 1], hx[W - 1], hd[W - 1];
-    issue_left_halo<VEC>(xb, xs_d, xs_t, s, ta, halo);
+    issue_left_halo<W, VEC>(xb, xs_d, xs_t, s, ta, halo);
     load_steps(ta, hx, hd);
     int64_t tau = ta + (W - 1);
     if (tau + U <= tb) {
         Raw<VEC> rx[U], rd[U];
         load_batch(tau, rx, rd);
-        finish_left_halo<VEC>(halo, a.init, r, s, ta, c0, xw);
+        finish_left_halo<W, VEC>(halo, a.init, r, s, ta, c0, xw);
 #pragma unroll
         for (int h = 0; h < W - 1; ++h) generic_step(ta + h, hx[h], hd[h]);
         body_batch(tau, rx, rd);
         tau += U;
     } else {
-        finish_left_halo<VEC>(halo, a.init, r, s, ta, c0, xw);
+        finish_left_halo<W, VEC>(halo, a.init, r, s, ta, c0, xw);
 #pragma unroll
         for (int h = 0; h < W - 1; ++h) generic_step(ta + h, hx[h], hd[h]);
     }
@@ -666,7 +686,7 @@ __device__ __forceinline__ void bwd_piece(const BwdArgs &a, BwdLane<VEC, SILU, B
         unpack<VEC>(load_raw<VEC, NTL>(xb + tau * xs_t, xs_d), cur);
         unpack<VEC>(load_raw<VEC, NTL>(dyb + tau * ys_t, ys_d), dyv);
         grad_step(cur, dyv, gcur, true);
-        shift_in<VEC>(xw, cur);
+        shift_in<W, VEC>(xw, cur);
         emit_value(gcur, v);
         store_vec<VEC, true>(dxb + (tau - (W - 1)) * ds_t, ds_d, v);
         shift_g(gcur);
@@ -682,9 +702,9 @@ __device__ __forceinline__ void bwd_piece(const BwdArgs &a, BwdLane<VEC, SILU, B
     }
 }
 
-template <int VEC, bool SILU, bool PACKED, int FK>
+template <int W, int VEC, bool SILU, bool PACKED, int FK>
 __global__ __launch_bounds__(256) CCV_BWD_ATTR void k_bwd_chan(BwdArgs a) {
-    constexpr bool BIAS = FK == kBf16Bias;
+    constexpr bool BIAS = fk_bias(FK);
     constexpr int CH = kWaveSize * VEC;  // channels of a block
     // One LDS buffer: the staged offsets during the walk, then the dW/dB
     // reduction (a barrier separates the two uses).
@@ -706,7 +726,7 @@ __global__ __launch_bounds__(256) CCV_BWD_ATTR void k_bwd_chan(BwdArgs a) {
     const int64_t t0 = (bt * kWavesPerBlock + wave) * a.L;
     const int64_t c0 = g * CH + lane * VEC;
 
-    BwdLane<VEC, SILU, BIAS> L;
+    BwdLane<W, VEC, SILU, BIAS> L;
 #pragma unroll
     for (int c = 0; c < VEC; ++c) {
 #pragma unroll
@@ -715,17 +735,17 @@ __global__ __launch_bounds__(256) CCV_BWD_ATTR void k_bwd_chan(BwdArgs a) {
     }
     if (t0 < a.T && c0 < a.D) {
         const int64_t t1 = min(t0 + a.L, a.T);
-        load_filter<VEC, FK>(a.w, a.w_sd, a.w_sk, a.bias, a.b_s, c0, L.w, L.bias);
+        load_filter<W, VEC, FK>(a.w, a.w_sd, a.w_sk, a.bias, a.b_s, c0, L.w, L.bias);
         auto run = [&](auto ntl) {
             constexpr bool NTL = decltype(ntl)::value;
             if constexpr (!PACKED) {
-                bwd_piece<VEC, SILU, BIAS, NTL>(a, L, b, b, 0, a.T, t0, t1, c0);
+                bwd_piece<W, VEC, SILU, BIAS, NTL>(a, L, b, b, 0, a.T, t0, t1, c0);
             } else {
                 const int32_t *cu = a.cu_in_lds ? s_cu : a.cu;
                 for (int64_t i = find_row(cu, a.n_seq, t0); i < a.n_seq; ++i) {
                     const int64_t s = cu[i], e = cu[i + 1];
                     if (s >= t1) break;
-                    bwd_piece<VEC, SILU, BIAS, NTL>(a, L, 0, i, s, e, s > t0 ? s : t0,
+                    bwd_piece<W, VEC, SILU, BIAS, NTL>(a, L, 0, i, s, e, s > t0 ? s : t0,
                                                     e < t1 ? e : t1, c0);
                 }
             }
@@ -747,14 +767,27 @@ __global__ __launch_bounds__(256) CCV_BWD_ATTR void k_bwd_chan(BwdArgs a) {
     __syncthreads();
     const int64_t ch0 = g * CH;
     const int64_t pidx = b * a.n_tblk + bt;
+    if (a.partial) {
+        // One unique partial row per block: [channel][tap] (+ the bias slot
+        // when dbias goes through the deterministic route too).
+        const int kp = a.part_stride;
+        for (int i = threadIdx.x; i < CH * kp; i += blockDim.x) {
+            const int ch = i / kp, k = i % kp;
+            if (ch0 + ch >= a.D) continue;
+            float v = s_red[0][k][ch];
+#pragma unroll
+            for (int q = 1; q < kWavesPerBlock; ++q) v += s_red[q][k][ch];
+            a.partial[(pidx * a.D + ch0 + ch) * kp + k] = v;
+        }
+        return;
+    }
     for (int i = threadIdx.x; i < CH * W; i += blockDim.x) {
         const int ch = i / W, k = i % W;
         if (ch0 + ch >= a.D) continue;
         float v = s_red[0][k][ch];
 #pragma unroll
         for (int q = 1; q < kWavesPerBlock; ++q) v += s_red[q][k][ch];
-        if (a.partial) a.partial[(pidx * a.D + ch0 + ch) * W + k] = v;
-        else atomicAdd(a.dw + (ch0 + ch) * W + k, v);
+        atomicAdd(a.dw + (ch0 + ch) * W + k, v);
     }
     if constexpr (BIAS) {
         for (int ch = threadIdx.x; ch < CH; ch += blockDim.x) {
@@ -781,6 +814,9 @@ __global__ __launch_bounds__(256) CCV_BWD_ATTR void k_bwd_chan(BwdArgs a) {
 #ifndef CCV_UPD_NT
 #define CCV_UPD_NT 0
 #endif
+#ifndef CCV_UPD_ROWS
+#define CCV_UPD_ROWS 2          // batch rows an 8-channel update lane serves
+#endif
 
 // The register budget of up to CCV_UPD_MAX_WAVES waves per SIMD leaves room
 // for every load of a lane to be in flight at once.  With 8 channels per lane
@@ -788,7 +824,7 @@ __global__ __launch_bounds__(256) CCV_BWD_ATTR void k_bwd_chan(BwdArgs a) {
 // contiguous [D,W] filter and bias, and 16-byte alignment: a lane's state is
 // 3 x 16 contiguous bytes.  A lane serves RPL batch rows of the same
 // channels, so their filter and bias are loaded once.
-template <bool SILU, bool WF32, bool BIAS, int RPL>
+template <int W, bool SILU, bool WF32, bool BIAS, int RPL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, CCV_UPD_MAX_WAVES)))
 void k_update_vec(UpdArgs a) {
     constexpr int VEC = 8;
@@ -803,11 +839,19 @@ void k_update_vec(UpdArgs a) {
     // Every load first: filter, bias, then each row's state and token.
     const u32x4_t *wq = reinterpret_cast<const u32x4_t *>(
         static_cast<const char *>(a.w) + c0 * W * (WF32 ? 4 : 2));
-    u32x4_t wv[kFilterVecs], bv = {0u, 0u, 0u, 0u};
+    // The bias has the filter's dtype: 8 BF16 values (one vector) or 8 FP32.
+    constexpr int kBiasVecs = WF32 ? 2 : 1;
+    u32x4_t wv[kFilterVecs], bv[kBiasVecs];
 #pragma unroll
     for (int i = 0; i < kFilterVecs; ++i) wv[i] = wq[i];
-    if constexpr (BIAS)
-        bv = *reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(a.bias) + c0);
+#pragma unroll
+    for (int i = 0; i < kBiasVecs; ++i) bv[i] = u32x4_t{0u, 0u, 0u, 0u};
+    if constexpr (BIAS) {
+        const u32x4_t *bq = reinterpret_cast<const u32x4_t *>(
+            static_cast<const char *>(a.bias) + c0 * (WF32 ? 4 : 2));
+#pragma unroll
+        for (int i = 0; i < kBiasVecs; ++i) bv[i] = bq[i];
+    }
     u32x4_t sv[RPL][kStateVecs], xv[RPL];
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
@@ -835,7 +879,8 @@ void k_update_vec(UpdArgs a) {
                 w[k][c] = (e2 % 2) ? hi_bf16(word) : lo_bf16(word);
             }
         }
-        bias[c] = (c % 2) ? hi_bf16(bv[c / 2]) : lo_bf16(bv[c / 2]);
+        if constexpr (WF32) bias[c] = __uint_as_float(bv[c / 4][c % 4]);
+        else bias[c] = (c % 2) ? hi_bf16(bv[0][c / 2]) : lo_bf16(bv[0][c / 2]);
     }
 
 #pragma unroll
@@ -883,7 +928,7 @@ void k_update_vec(UpdArgs a) {
 }
 
 // Any strides: one lane per channel of one row.
-template <bool SILU, bool WF32, bool BIAS>
+template <int W, bool SILU, bool WF32, bool BIAS>
 __global__ __launch_bounds__(256) void k_update_any(UpdArgs a) {
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t b = gid / a.n_lane_per_row;
@@ -895,7 +940,10 @@ __global__ __launch_bounds__(256) void k_update_any(UpdArgs a) {
 #pragma unroll
     for (int j = 0; j < W - 1; ++j) st[j] = sp[j * a.s_sj];
     const uint16_t xr = *xp;
-    float z = BIAS ? bf16_bits_to_f32(static_cast<const uint16_t *>(a.bias)[c * a.b_s]) : 0.0f;
+    float z = 0.0f;
+    if constexpr (BIAS)
+        z = WF32 ? static_cast<const float *>(a.bias)[c * a.b_s]
+                 : bf16_bits_to_f32(static_cast<const uint16_t *>(a.bias)[c * a.b_s]);
 #pragma unroll
     for (int k = 0; k < W; ++k) {
         const int64_t off = c * a.w_sd + k * a.w_sk;
@@ -934,15 +982,21 @@ __global__ __launch_bounds__(256) void k_validate(const int32_t *cu, int64_t n_s
     }
 }
 
-// Fixed-order reduction of unique partials: out[e] += sum_{p=0}^{P-1} part[p][e],
-// always in increasing p, so the result does not depend on scheduling.
+// Fixed-order reduction of unique partials [P][D][kp]: the sum over
+// p = 0..P-1, always in increasing p (so the result does not depend on
+// scheduling), is added to dw[d][k] for k < W and, with kp = W+1, to db[d].
 __global__ __launch_bounds__(256) void k_dw_reduce(const float *part, int64_t n_part,
-                                                   int64_t n_elem, float *out) {
+                                                   int64_t n_ch, int w, int kp, float *dw,
+                                                   float *db) {
     const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t n_elem = n_ch * kp;
     if (e >= n_elem) return;
     float acc = 0.0f;
     for (int64_t p = 0; p < n_part; ++p) acc += part[p * n_elem + e];
-    out[e] += acc;
+    const int64_t ch = e / kp;
+    const int k = static_cast<int>(e % kp);
+    if (k < w) dw[ch * w + k] += acc;
+    else db[ch] += acc;
 }
 
 // A stream value that never names a real stream: dispatch without launching.
@@ -956,141 +1010,4 @@ hipError_t launch(K kernel, int64_t blocks, const A &args, hipStream_t s) {
 }
 
 }  // namespace
-
-// Filter kind of an argument block (see FilterKind).
-template <typename A>
-int filter_kind(const A &a) {
-    return a.w_f32 ? kF32 : (a.bias != nullptr ? kBf16Bias : kBf16);
-}
-
-// Resident blocks of a kernel on the current device (CUs x blocks per CU),
-// from the occupancy the compiled kernel allows; 0 when it cannot be told.
-int64_t resident_blocks(const void *kernel) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess)
-        return 0;
-    return static_cast<int64_t>(cus) * per_cu;
-}
-
-template <int V, bool S, bool P, int F, bool Q>
-hipError_t fwd_one(const FwdArgs &a, hipStream_t s) {
-    if (s == kQueryStream) return hipSuccess;
-    return launch(k_fwd_chan<V, S, P, F, Q>, a.n_block, a, s);
-}
-
-// The software-pipelined forward is built for 8-channel lanes only.
-template <int V, bool Q>
-hipError_t fwd_vec(const FwdArgs &a, int silu, int packed, int fk, hipStream_t s, int64_t *cap) {
-#define CCV_FWD(S, P, F)                                                                       \
-    if (!!silu == S && !!packed == P && fk == F) {                                             \
-        if (cap) *cap = resident_blocks(reinterpret_cast<const void *>(k_fwd_chan<V, S, P, F, Q>)); \
-        return fwd_one<V, S, P, F, Q>(a, s);                                                   \
-    }
-#define CCV_FWD_K(S, P) CCV_FWD(S, P, kBf16) CCV_FWD(S, P, kBf16Bias) CCV_FWD(S, P, kF32)
-    CCV_FWD_K(true, false) CCV_FWD_K(true, true) CCV_FWD_K(false, false) CCV_FWD_K(false, true)
-#undef CCV_FWD_K
-#undef CCV_FWD
-    return hipErrorInvalidValue;
-}
-
-hipError_t fwd_dispatch(const FwdArgs &a, int vec, int silu, int packed, hipStream_t s,
-                        int64_t *cap) {
-    const int fk = filter_kind(a);
-    if (vec == 8 && a.pipe) return fwd_vec<8, true>(a, silu, packed, fk, s, cap);
-    if (vec == 8) return fwd_vec<8, false>(a, silu, packed, fk, s, cap);
-    if (vec == 4) return fwd_vec<4, false>(a, silu, packed, fk, s, cap);
-    if (vec == 1) return fwd_vec<1, false>(a, silu, packed, fk, s, cap);
-    return hipErrorInvalidValue;
-}
-
-hipError_t launch_fwd(const FwdArgs &a, int vec, int silu, int packed, hipStream_t s) {
-    return fwd_dispatch(a, vec, silu, packed, s, nullptr);
-}
-
-int64_t fwd_resident_blocks(const FwdArgs &a, int vec, int silu, int packed) {
-    int64_t cap = 0;
-    fwd_dispatch(a, vec, silu, packed, kQueryStream, &cap);
-    return cap;
-}
-
-template <int V, bool S, bool P, int F>
-hipError_t bwd_one(const BwdArgs &a, hipStream_t s) {
-    if (s == kQueryStream) return hipSuccess;
-    return launch(k_bwd_chan<V, S, P, F>, a.n_block, a, s);
-}
-
-template <int V>
-hipError_t bwd_vec(const BwdArgs &a, int silu, int packed, int fk, hipStream_t s, int64_t *cap) {
-#define CCV_BWD(S, P, F)                                                                   \
-    if (!!silu == S && !!packed == P && fk == F) {                                         \
-        if (cap) *cap = resident_blocks(reinterpret_cast<const void *>(k_bwd_chan<V, S, P, F>)); \
-        return bwd_one<V, S, P, F>(a, s);                                                  \
-    }
-#define CCV_BWD_K(S, P) CCV_BWD(S, P, kBf16) CCV_BWD(S, P, kBf16Bias) CCV_BWD(S, P, kF32)
-    CCV_BWD_K(true, false) CCV_BWD_K(true, true) CCV_BWD_K(false, false) CCV_BWD_K(false, true)
-#undef CCV_BWD_K
-#undef CCV_BWD
-    return hipErrorInvalidValue;
-}
-
-// Backward lanes own 4 channels (or 1): with 8, the window, gradient window
-// and dW accumulators leave too few registers for latency hiding.
-hipError_t launch_bwd(const BwdArgs &a, int vec, int silu, int packed, hipStream_t s) {
-    const int fk = filter_kind(a);
-    if (vec == 4) return bwd_vec<4>(a, silu, packed, fk, s, nullptr);
-    if (vec == 1) return bwd_vec<1>(a, silu, packed, fk, s, nullptr);
-    return hipErrorInvalidValue;
-}
-
-int64_t bwd_resident_blocks(const BwdArgs &a, int vec, int silu, int packed) {
-    const int fk = filter_kind(a);
-    int64_t cap = 0;
-    if (vec == 4) bwd_vec<4>(a, silu, packed, fk, kQueryStream, &cap);
-    if (vec == 1) bwd_vec<1>(a, silu, packed, fk, kQueryStream, &cap);
-    return cap;
-}
-
-#ifndef CCV_UPD_ROWS
-#define CCV_UPD_ROWS 2
-#endif
-
-hipError_t launch_update(const UpdArgs &a, int vec, int silu, hipStream_t s) {
-    const bool wf32 = a.w_f32 != 0, bias = a.bias != nullptr;
-    if (vec == 8) {
-        const int64_t blocks = (a.n_row_groups * a.n_lane_per_row + 255) / 256;
-#define CCV_UPD(S, F, B) \
-        if (!!silu == S && wf32 == F && bias == B) return launch(k_update_vec<S, F, B, CCV_UPD_ROWS>, blocks, a, s);
-        CCV_UPD(true, false, true) CCV_UPD(true, false, false) CCV_UPD(true, true, false)
-        CCV_UPD(false, false, true) CCV_UPD(false, false, false) CCV_UPD(false, true, false)
-#undef CCV_UPD
-    } else if (vec == 1) {
-        const int64_t blocks = (a.B * a.n_lane_per_row + 255) / 256;
-#define CCV_UPD(S, F, B) \
-        if (!!silu == S && wf32 == F && bias == B) return launch(k_update_any<S, F, B>, blocks, a, s);
-        CCV_UPD(true, false, true) CCV_UPD(true, false, false) CCV_UPD(true, true, false)
-        CCV_UPD(false, false, true) CCV_UPD(false, false, false) CCV_UPD(false, true, false)
-#undef CCV_UPD
-    }
-    return hipErrorInvalidValue;
-}
-
-int update_rows_per_lane() { return CCV_UPD_ROWS; }
-
-hipError_t launch_validate(const int32_t *cu, int64_t n_seq, int64_t total, uint32_t *flags,
-                           int overwrite, hipStream_t s) {
-    hipLaunchKernelGGL(k_validate, dim3(1), dim3(256), 0, s, cu, n_seq, total, flags, overwrite);
-    return hipGetLastError();
-}
-
-hipError_t launch_dw_reduce(const float *partial, int64_t n_part, int64_t n_elem, float *out,
-                            hipStream_t s) {
-    const int64_t blocks = (n_elem + 255) / 256;
-    hipLaunchKernelGGL(k_dw_reduce, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, partial,
-                       n_part, n_elem, out);
-    return hipGetLastError();
-}
-
 }  // namespace ccv

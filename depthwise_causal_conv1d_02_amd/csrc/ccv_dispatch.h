@@ -1,0 +1,109 @@
+// ccv_dispatch.h — host-side selection of the kernel instance for one filter
+// width W (a template argument here; ccv_width.hip instantiates it for each
+// width the library is built for).
+#pragma once
+
+#include "ccv_device.h"
+
+namespace ccv {
+namespace {
+
+// Filter kind of an argument block (see FilterKind).
+template <typename A>
+int filter_kind(const A &a) {
+    if (a.w_f32) return a.bias != nullptr ? kF32Bias : kF32;
+    return a.bias != nullptr ? kBf16Bias : kBf16;
+}
+
+template <typename K>
+int64_t capacity_of(K kernel) {
+    return resident_blocks(reinterpret_cast<const void *>(kernel));
+}
+
+template <int W, int V, bool S, bool P, int F, bool Q>
+hipError_t fwd_one(const FwdArgs &a, hipStream_t s, int64_t *cap) {
+    if (cap) *cap = capacity_of(k_fwd_chan<W, V, S, P, F, Q>);
+    if (s == kQueryStream) return hipSuccess;
+    return launch(k_fwd_chan<W, V, S, P, F, Q>, a.n_block, a, s);
+}
+
+template <int W, int V, bool Q>
+hipError_t fwd_vec(const FwdArgs &a, int silu, int packed, int fk, hipStream_t s, int64_t *cap) {
+#define CCV_FWD(S, P, F) \
+    if (!!silu == S && !!packed == P && fk == F) return fwd_one<W, V, S, P, F, Q>(a, s, cap);
+#define CCV_FWD_K(S, P) \
+    CCV_FWD(S, P, kBf16) CCV_FWD(S, P, kBf16Bias) CCV_FWD(S, P, kF32) CCV_FWD(S, P, kF32Bias)
+    CCV_FWD_K(true, false) CCV_FWD_K(true, true) CCV_FWD_K(false, false) CCV_FWD_K(false, true)
+#undef CCV_FWD_K
+#undef CCV_FWD
+    return hipErrorInvalidValue;
+}
+
+// The software-pipelined forward is built for 8-channel lanes only.
+template <int W>
+hipError_t fwd_dispatch(const FwdArgs &a, int vec, int silu, int packed, hipStream_t s,
+                        int64_t *cap) {
+    const int fk = filter_kind(a);
+    if (vec == 8 && a.pipe) return fwd_vec<W, 8, true>(a, silu, packed, fk, s, cap);
+    if (vec == 8) return fwd_vec<W, 8, false>(a, silu, packed, fk, s, cap);
+    if (vec == 4) return fwd_vec<W, 4, false>(a, silu, packed, fk, s, cap);
+    if (vec == 1) return fwd_vec<W, 1, false>(a, silu, packed, fk, s, cap);
+    return hipErrorInvalidValue;
+}
+
+template <int W, int V, bool S, bool P, int F>
+hipError_t bwd_one(const BwdArgs &a, hipStream_t s, int64_t *cap) {
+    if (cap) *cap = capacity_of(k_bwd_chan<W, V, S, P, F>);
+    if (s == kQueryStream) return hipSuccess;
+    return launch(k_bwd_chan<W, V, S, P, F>, a.n_block, a, s);
+}
+
+template <int W, int V>
+hipError_t bwd_vec(const BwdArgs &a, int silu, int packed, int fk, hipStream_t s, int64_t *cap) {
+#define CCV_BWD(S, P, F) \
+    if (!!silu == S && !!packed == P && fk == F) return bwd_one<W, V, S, P, F>(a, s, cap);
+#define CCV_BWD_K(S, P) \
+    CCV_BWD(S, P, kBf16) CCV_BWD(S, P, kBf16Bias) CCV_BWD(S, P, kF32) CCV_BWD(S, P, kF32Bias)
+    CCV_BWD_K(true, false) CCV_BWD_K(true, true) CCV_BWD_K(false, false) CCV_BWD_K(false, true)
+#undef CCV_BWD_K
+#undef CCV_BWD
+    return hipErrorInvalidValue;
+}
+
+// Backward lanes own 4 channels (or 1): with 8, the window, gradient window
+// and dW accumulators leave too few registers for latency hiding.
+template <int W>
+hipError_t bwd_dispatch(const BwdArgs &a, int vec, int silu, int packed, hipStream_t s,
+                        int64_t *cap) {
+    const int fk = filter_kind(a);
+    if (vec == 4) return bwd_vec<W, 4>(a, silu, packed, fk, s, cap);
+    if (vec == 1) return bwd_vec<W, 1>(a, silu, packed, fk, s, cap);
+    return hipErrorInvalidValue;
+}
+
+template <int W>
+hipError_t update_dispatch(const UpdArgs &a, int vec, int silu, hipStream_t s) {
+    const bool wf32 = a.w_f32 != 0, bias = a.bias != nullptr;
+    if (vec == 8) {
+        const int64_t blocks = (a.n_row_groups * a.n_lane_per_row + 255) / 256;
+#define CCV_UPD(S, F, B)                                                                      \
+        if (!!silu == S && wf32 == F && bias == B)                                            \
+            return launch(k_update_vec<W, S, F, B, CCV_UPD_ROWS>, blocks, a, s);
+        CCV_UPD(true, false, true) CCV_UPD(true, false, false) CCV_UPD(true, true, false)
+        CCV_UPD(true, true, true) CCV_UPD(false, false, true) CCV_UPD(false, false, false)
+        CCV_UPD(false, true, false) CCV_UPD(false, true, true)
+#undef CCV_UPD
+    } else if (vec == 1) {
+        const int64_t blocks = (a.B * a.n_lane_per_row + 255) / 256;
+#define CCV_UPD(S, F, B) \
+        if (!!silu == S && wf32 == F && bias == B) return launch(k_update_any<W, S, F, B>, blocks, a, s);
+        CCV_UPD(true, false, true) CCV_UPD(true, false, false) CCV_UPD(true, true, false)
+        CCV_UPD(true, true, true) CCV_UPD(false, false, true) CCV_UPD(false, false, false)
+        CCV_UPD(false, true, false) CCV_UPD(false, true, true)
+#undef CCV_UPD
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+}  // namespace ccv

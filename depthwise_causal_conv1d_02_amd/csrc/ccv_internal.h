@@ -9,7 +9,7 @@
 
 namespace ccv {
 
-constexpr int kWidth = 4;          // the filter width the kernels are built for
+constexpr int kMinWidth = 2, kMaxWidth = 4;  // filter widths the kernels are built for
 constexpr int kWaveSize = 64;      // CDNA wavefront
 constexpr int kWavesPerBlock = 4;  // channel-lane kernels: 4 waves per block
 // Forward blocks: kFwdWavesT waves along time x kFwdWavesC along channel
@@ -36,6 +36,7 @@ struct Strided3 {
 };
 
 struct FwdArgs {
+    int width;                 // filter taps W (2..4)
     Strided3 x, y, init, fin;  // y/fin are written through const_cast in the kernels
     const void *w;             // [D,W], BF16 or FP32
     int64_t w_sd, w_sk;
@@ -58,6 +59,7 @@ struct FwdArgs {
 };
 
 struct BwdArgs {
+    int width;
     Strided3 x, dy, dx, init, dfin, dinit;
     const void *w;
     int64_t w_sd, w_sk;
@@ -66,7 +68,8 @@ struct BwdArgs {
     int64_t b_s;
     float *dw;                 // [D,W] FP32, contiguous, accumulated into
     float *db;                 // [D] FP32 or nullptr
-    float *partial;            // deterministic path: [P][D][W] FP32, else nullptr
+    float *partial;            // deterministic path: [P][D][part_stride] FP32, else nullptr
+    int part_stride;           // W, or W+1 when dbias is reduced deterministically too
     const int32_t *cu;
     int64_t n_seq;
     uint32_t *err;
@@ -76,6 +79,7 @@ struct BwdArgs {
 };
 
 struct UpdArgs {
+    int width;
     const void *x;        // [B,D]
     int64_t x_sb, x_sd;
     void *state;          // [B,D,W-1]
@@ -92,7 +96,8 @@ struct UpdArgs {
     int64_t n_row_groups;    // ceil(B / rows per lane), 8-channel lanes
 };
 
-// Launchers (ccv_kernels.hip).  `vec` is the channels per lane (8 or 1).
+// Launchers (ccv_misc.hip).  `vec` is the channels per lane (8, 4 or 1); the
+// filter width comes from the argument block.
 hipError_t launch_fwd(const FwdArgs &a, int vec, int silu, int packed, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs &a, int vec, int silu, int packed, hipStream_t s);
 hipError_t launch_update(const UpdArgs &a, int vec, int silu, hipStream_t s);
@@ -103,7 +108,22 @@ int64_t fwd_resident_blocks(const FwdArgs &a, int vec, int silu, int packed);
 int64_t bwd_resident_blocks(const BwdArgs &a, int vec, int silu, int packed);
 hipError_t launch_validate(const int32_t *cu, int64_t n_seq, int64_t total, uint32_t *flags,
                            int overwrite, hipStream_t s);
-hipError_t launch_dw_reduce(const float *partial, int64_t n_part, int64_t n_elem, float *out,
-                            hipStream_t s);
+hipError_t launch_dw_reduce(const float *partial, int64_t n_part, int64_t n_ch, int w, int kp,
+                            float *dw, float *db, hipStream_t s);
+int64_t resident_blocks(const void *kernel);
+
+// Per-width kernel selection (ccv_width.hip, built once per width).  With
+// `cap` set, the resident-block capacity of the selected kernel is stored
+// there; the stream kQueryStream selects without launching.
+#define CCV_DECLARE_WIDTH(W)                                                                   \
+    hipError_t fwd_dispatch_w##W(const FwdArgs &a, int vec, int silu, int packed, hipStream_t s, \
+                                 int64_t *cap);                                                \
+    hipError_t bwd_dispatch_w##W(const BwdArgs &a, int vec, int silu, int packed, hipStream_t s, \
+                                 int64_t *cap);                                                \
+    hipError_t update_dispatch_w##W(const UpdArgs &a, int vec, int silu, hipStream_t s);
+CCV_DECLARE_WIDTH(2)
+CCV_DECLARE_WIDTH(3)
+CCV_DECLARE_WIDTH(4)
+#undef CCV_DECLARE_WIDTH
 
 }  // namespace ccv

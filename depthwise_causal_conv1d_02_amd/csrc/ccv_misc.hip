@@ -1,0 +1,87 @@
+// ccv_misc.hip — width-independent launches (offset validation, the fixed-
+// order dW reduction) and the switch from a call's filter width to the
+// kernels built for it.
+#include "ccv_device.h"
+
+namespace ccv {
+
+// Resident blocks of a kernel on the current device (CUs x blocks per CU),
+// from the occupancy the compiled kernel allows; 0 when it cannot be told.
+int64_t resident_blocks(const void *kernel) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess)
+        return 0;
+    return static_cast<int64_t>(cus) * per_cu;
+}
+
+hipError_t launch_fwd(const FwdArgs &a, int vec, int silu, int packed, hipStream_t s) {
+    switch (a.width) {
+    case 2: return fwd_dispatch_w2(a, vec, silu, packed, s, nullptr);
+    case 3: return fwd_dispatch_w3(a, vec, silu, packed, s, nullptr);
+    case 4: return fwd_dispatch_w4(a, vec, silu, packed, s, nullptr);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+int64_t fwd_resident_blocks(const FwdArgs &a, int vec, int silu, int packed) {
+    int64_t cap = 0;
+    hipError_t e = hipErrorInvalidValue;
+    switch (a.width) {
+    case 2: e = fwd_dispatch_w2(a, vec, silu, packed, kQueryStream, &cap); break;
+    case 3: e = fwd_dispatch_w3(a, vec, silu, packed, kQueryStream, &cap); break;
+    case 4: e = fwd_dispatch_w4(a, vec, silu, packed, kQueryStream, &cap); break;
+    default: break;
+    }
+    return e == hipSuccess ? cap : 0;
+}
+
+hipError_t launch_bwd(const BwdArgs &a, int vec, int silu, int packed, hipStream_t s) {
+    switch (a.width) {
+    case 2: return bwd_dispatch_w2(a, vec, silu, packed, s, nullptr);
+    case 3: return bwd_dispatch_w3(a, vec, silu, packed, s, nullptr);
+    case 4: return bwd_dispatch_w4(a, vec, silu, packed, s, nullptr);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+int64_t bwd_resident_blocks(const BwdArgs &a, int vec, int silu, int packed) {
+    int64_t cap = 0;
+    hipError_t e = hipErrorInvalidValue;
+    switch (a.width) {
+    case 2: e = bwd_dispatch_w2(a, vec, silu, packed, kQueryStream, &cap); break;
+    case 3: e = bwd_dispatch_w3(a, vec, silu, packed, kQueryStream, &cap); break;
+    case 4: e = bwd_dispatch_w4(a, vec, silu, packed, kQueryStream, &cap); break;
+    default: break;
+    }
+    return e == hipSuccess ? cap : 0;
+}
+
+hipError_t launch_update(const UpdArgs &a, int vec, int silu, hipStream_t s) {
+    switch (a.width) {
+    case 2: return update_dispatch_w2(a, vec, silu, s);
+    case 3: return update_dispatch_w3(a, vec, silu, s);
+    case 4: return update_dispatch_w4(a, vec, silu, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+int update_rows_per_lane() { return CCV_UPD_ROWS; }
+
+hipError_t launch_validate(const int32_t *cu, int64_t n_seq, int64_t total, uint32_t *flags,
+                           int overwrite, hipStream_t s) {
+    hipLaunchKernelGGL(k_validate, dim3(1), dim3(256), 0, s, cu, n_seq, total, flags, overwrite);
+    return hipGetLastError();
+}
+
+hipError_t launch_dw_reduce(const float *partial, int64_t n_part, int64_t n_ch, int w, int kp,
+                            float *dw, float *db, hipStream_t s) {
+    const int64_t blocks = (n_ch * kp + 255) / 256;
+    hipLaunchKernelGGL(k_dw_reduce, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, partial,
+                       n_part, n_ch, w, kp, dw, db);
+    return hipGetLastError();
+}
+
+}  // namespace ccv

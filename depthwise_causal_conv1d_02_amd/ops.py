@@ -126,8 +126,14 @@ def _rows(x, cu_seqlens):
     return x.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
 
 
+def _options(fp32_weight_bias=False, deterministic_dbias=False):
+    return ((_abi.CCV_OPT_F32_FILTER_BIAS if fp32_weight_bias else 0) |
+            (_abi.CCV_OPT_DETERMINISTIC_DBIAS if deterministic_dbias else 0))
+
+
 def fwd(x, weight, bias=None, cu_seqlens=None, initial_states=None, activation="silu",
-        return_final_states=False, final_states_out=None, y=None, err_flag=None, seq_idx=None):
+        return_final_states=False, final_states_out=None, y=None, err_flag=None, seq_idx=None,
+        options=0):
     """One ccv_fwd call.  Returns (y, final_states or None)."""
     if y is None:
         y = torch.empty_like(x)
@@ -141,15 +147,16 @@ def fwd(x, weight, bias=None, cu_seqlens=None, initial_states=None, activation="
     rc = _abi.lib().ccv_fwd(_ref(_desc(x)), _ref(_desc(weight)), _ref(_desc(bias)),
                             _ref(_desc(cu_seqlens)), _ref(_desc(seq_idx)),
                             _ref(_desc(initial_states)), _ref(_desc(y)), _ref(_desc(fin)),
-                            _act(activation), None if flag is None else flag.data_ptr(),
-                            _stream(x))
+                            _act(activation), int(options),
+                            None if flag is None else flag.data_ptr(), _stream(x))
     _check(rc, "causal_conv1d")
     return y, fin
 
 
 def bwd(x, weight, dy, bias=None, cu_seqlens=None, initial_states=None, dfinal_states=None,
         activation="silu", deterministic=False, warn_only=False, dx=None, err_flag=None,
-        want_dinit=True, seq_idx=None, workspace=None, dweight=None, dbias=None, dinit=None):
+        want_dinit=True, seq_idx=None, workspace=None, dweight=None, dbias=None, dinit=None,
+        options=0):
     """One ccv_bwd call.  Returns (dx, dweight_f32, dbias_f32 or None,
     dinitial_states or None).  ``dweight``/``dbias`` (FP32) are accumulated
     into when given, else freshly zeroed ones are used."""
@@ -171,7 +178,7 @@ def bwd(x, weight, dy, bias=None, cu_seqlens=None, initial_states=None, dfinal_s
                  _ref(_desc(seq_idx)), _ref(_desc(initial_states)), _ref(_desc(dy)),
                  _ref(_desc(dfinal_states)), _ref(_desc(dx)), _ref(_desc(dw)), _ref(_desc(db)),
                  _ref(_desc(dinit)), _act(activation), int(bool(deterministic)),
-                 int(bool(warn_only)))
+                 int(bool(warn_only)), int(options))
     flag_ptr = None if flag is None else flag.data_ptr()
     need = ctypes.c_size_t(0)
     rc = L.ccv_bwd(*args_head, None, ctypes.byref(need), flag_ptr, _stream(x))
@@ -187,12 +194,13 @@ def bwd(x, weight, dy, bias=None, cu_seqlens=None, initial_states=None, dfinal_s
     return dx, dw, db, dinit
 
 
-def update(x, conv_state, weight, bias=None, activation="silu", y=None):
+def update(x, conv_state, weight, bias=None, activation="silu", y=None, options=0):
     """One ccv_update call (conv_state is mutated in place).  Returns y."""
     if y is None:
         y = torch.empty_like(x)
     rc = _abi.lib().ccv_update(_ref(_desc(x)), _ref(_desc(conv_state)), _ref(_desc(weight)),
-                               _ref(_desc(bias)), _ref(_desc(y)), _act(activation), _stream(x))
+                               _ref(_desc(bias)), _ref(_desc(y)), _act(activation), int(options),
+                               _stream(x))
     _check(rc, "causal_conv1d_update")
     return y
 
@@ -202,14 +210,15 @@ def update(x, conv_state, weight, bias=None, activation="silu", y=None):
 class _CausalConv1dFn(torch.autograd.Function):
     @staticmethod
     def forward(ctx, x, weight, bias, cu_seqlens, initial_states, final_states_out, activation,
-                return_final_states, deterministic):
+                return_final_states, deterministic, options):
         y, fin = fwd(x, weight, bias, cu_seqlens, initial_states, activation,
-                     return_final_states, final_states_out)
+                     return_final_states, final_states_out, options=options)
         # Inputs are saved for backward; the final state is written after the
         # forward (cuDNN FE "Causal Conv1d", the aliasing paragraph).
         ctx.save_for_backward(x, weight, bias, cu_seqlens, initial_states)
         ctx.activation = activation
         ctx.deterministic = deterministic
+        ctx.options = options
         ctx.has_fin = fin is not None
         if final_states_out is not None:
             ctx.mark_dirty(final_states_out)
@@ -230,14 +239,14 @@ class _CausalConv1dFn(torch.autograd.Function):
         need_dinit = init is not None and ctx.needs_input_grad[4]
         dx, dw, db, dinit = bwd(x, weight, dy, bias, cu_seqlens, init,
                                 dfin if ctx.has_fin else None, ctx.activation, det, warn_only,
-                                want_dinit=need_dinit)
+                                want_dinit=need_dinit, options=ctx.options)
         return (dx, dw.to(weight.dtype), None if db is None else db.to(bias.dtype), None,
-                dinit, None, None, None, None)
+                dinit, None, None, None, None, None)
 
 
 def causal_conv1d(x, weight, bias=None, seq_idx=None, cu_seqlens=None, initial_states=None,
                   return_final_states=False, final_states_out=None, activation=None,
-                  deterministic=None):
+                  deterministic=None, fp32_weight_bias=False, deterministic_dbias=False):
     """y = act(bias + depthwise causal conv of x with weight), x [B,D,T].
 
     ``x`` may be a [B,T,D] storage seen through ``transpose(1, 2)``; it is
@@ -245,6 +254,11 @@ def causal_conv1d(x, weight, bias=None, seq_idx=None, cu_seqlens=None, initial_s
     input; their metadata is validated on the device and malformed offsets
     set the device flag (see :func:`check_flag`) instead of trapping.
     Returns ``y`` or ``(y, final_states)``.
+
+    Two opt-ins widen what the pages' route declines: ``fp32_weight_bias``
+    admits an FP32 weight with an FP32 bias, and ``deterministic_dbias``
+    lets a deterministic backward with a bias reduce dbias in a fixed order
+    instead of failing (or warning and using atomics).
     """
     if seq_idx is not None:
         if cu_seqlens is not None:
@@ -254,17 +268,20 @@ def causal_conv1d(x, weight, bias=None, seq_idx=None, cu_seqlens=None, initial_s
         return_final_states = True
     needs_grad = torch.is_grad_enabled() and any(
         t is not None and t.requires_grad for t in (x, weight, bias, initial_states))
+    opts = _options(fp32_weight_bias, deterministic_dbias)
     if needs_grad:
         y, fin = _CausalConv1dFn.apply(x, weight, bias, cu_seqlens, initial_states,
                                        final_states_out, activation, return_final_states,
-                                       deterministic)
+                                       deterministic, opts)
     else:
         y, fin = fwd(x, weight, bias, cu_seqlens, initial_states, activation,
-                     return_final_states, final_states_out)
+                     return_final_states, final_states_out, options=opts)
     return (y, fin) if return_final_states else y
 
 
-def causal_conv1d_update(x, conv_state, weight, bias=None, activation=None):
+def causal_conv1d_update(x, conv_state, weight, bias=None, activation=None,
+                         fp32_weight_bias=False):
     """One decode token: x [B,D]; conv_state [B,D,W-1] is mutated in place
     (it becomes the last W-1 tokens).  Returns y [B,D]."""
-    return update(x, conv_state, weight, bias, activation)
+    return update(x, conv_state, weight, bias, activation,
+                  options=_options(fp32_weight_bias))

@@ -45,8 +45,10 @@ def weight_tensor(g, D, W=4, dtype=BF16):
     return _uniform_half(g, (D, W), dtype)
 
 
-def bias_tensor(g, D):
-    return _normal(g, (D,), 0.1)
+def bias_tensor(g, D, dtype=BF16):
+    """randn * 0.1, rounded to BF16, or kept in FP32 for an FP32 filter."""
+    t = torch.randn(D, generator=g, dtype=torch.float32) * 0.1
+    return t.to(dtype)
 
 
 def state_tensor(g, R, D, W=4):
@@ -84,12 +86,13 @@ def random_inputs(seed, B, D, T, *, layout="cl", W=4, bias=True, init=False, dy=
 
     Draw order: x, weight, bias, initial_states, dy, dfinal_states.
     With ``cu_seqlens`` (B must be 1) the states have N = len(cu)-1 rows.
+    The bias takes the weight's dtype.
     """
     g = torch.Generator().manual_seed(seed)
     R = B if cu_seqlens is None else int(cu_seqlens.numel()) - 1
     out = {"x": activation_tensor(g, B, D, T, layout)}
     out["weight"] = weight_tensor(g, D, W, weight_dtype)
-    out["bias"] = bias_tensor(g, D) if bias else None
+    out["bias"] = bias_tensor(g, D, weight_dtype) if bias else None
     out["initial_states"] = state_tensor(g, R, D, W) if init else None
     out["dy"] = activation_tensor(g, B, D, T, layout) if dy else None
     out["dfinal_states"] = state_tensor(g, R, D, W) if dfinal else None

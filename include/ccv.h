@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define CCV_ABI_VERSION 1
+#define CCV_ABI_VERSION 2
 
 typedef enum ccv_dtype {
     CCV_DTYPE_BF16 = 0,
@@ -76,10 +76,12 @@ typedef enum ccv_status {
      * (cuDNN FE "Causal Conv1d", the paragraph on final_states_out). */
     CCV_ERR_ALIAS = -2,
     /* Declined explicitly (cuDNN FE "Causal Conv1d", the optimized route):
-     * seq_idx given; FP32 weight with a bias; a width other than 4; an
-     * activation other than none or SiLU. */
+     * seq_idx given; FP32 weight with a bias (without
+     * CCV_OPT_F32_FILTER_BIAS); a width outside 2..4; an activation other
+     * than none or SiLU. */
     CCV_ERR_UNSUPPORTED = -3,
-    /* Deterministic dweight requested with a bias and no warn_only. */
+    /* Deterministic dweight requested with a bias, without warn_only and
+     * without CCV_OPT_DETERMINISTIC_DBIAS. */
     CCV_ERR_NONDETERMINISTIC = -4,
     /* A HIP launch failed (hipGetLastError after the launch). */
     CCV_ERR_HIP = -5
@@ -93,6 +95,21 @@ typedef enum ccv_status {
 #define CCV_CU_DECREASING    0x4u /* cu_seqlens[i+1] <  cu_seqlens[i] */
 #define CCV_CU_EMPTY         0x8u /* cu_seqlens[i+1] == cu_seqlens[i] */
 
+/* Option bits (the `options` argument).  Both widen what the pages' route
+ * declines (cuDNN FE "Causal Conv1d", the paragraph on the optimized route
+ * and the determinism paragraph), so each is opt-in; any other bit is
+ * CCV_ERR_INVALID_ARG.
+ *   CCV_OPT_F32_FILTER_BIAS      admit an FP32 weight together with an FP32
+ *                                bias (ccv_fwd, ccv_bwd, ccv_update).  The
+ *                                bias is then FP32 too; a BF16 bias with an
+ *                                FP32 weight stays invalid.
+ *   CCV_OPT_DETERMINISTIC_DBIAS  (ccv_bwd) with deterministic = 1 and a
+ *                                bias, reduce dbias through the workspace
+ *                                partials as well, in the same fixed order
+ *                                as dweight. */
+#define CCV_OPT_F32_FILTER_BIAS     0x1u
+#define CCV_OPT_DETERMINISTIC_DBIAS 0x2u
+
 typedef struct ccv_tensor {
     void *data;        /* device pointer; NULL = absent */
     int32_t dtype;     /* ccv_dtype */
@@ -105,8 +122,12 @@ typedef struct ccv_tensor {
  * ccv_fwd — full-sequence forward (cuDNN FE "Causal Conv1d": causal_conv1d).
  *
  *   x               [B,D,T]  BF16, read.
- *   weight          [D,W]    BF16, or FP32 only without bias; W must be 4.
- *   bias            [D]      BF16, optional.
+ *   weight          [D,W]    BF16, or FP32 (with a bias only under
+ *                            CCV_OPT_F32_FILTER_BIAS); W in 2..4 (the page's
+ *                            optimized route is W = 4; 2 and 3 use the same
+ *                            kernels built for their width).
+ *   bias            [D]      optional; BF16, or FP32 with an FP32 weight
+ *                            under CCV_OPT_F32_FILTER_BIAS.
  *   cu_seqlens      [N+1]    I32, optional; packs N sequences along T of a
  *                            B == 1 input.  Mutually exclusive with seq_idx.
  *   seq_idx         [B,T]    reserved: must be absent (declined otherwise).
@@ -114,6 +135,7 @@ typedef struct ccv_tensor {
  *   y               [B,D,T]  BF16, written.  Any layout; usually x's.
  *   final_states    [R,D,W-1] BF16, optional, written.
  *   activation      CCV_ACT_NONE or CCV_ACT_SILU.
+ *   options         CCV_OPT_* bits (0 = the pages' route).
  *   err_flag        device uint32, required with cu_seqlens, else ignored.
  *
  * Packed inputs are validated on the device (no host read).  The bits of
@@ -125,8 +147,8 @@ typedef struct ccv_tensor {
 int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bias,
             const ccv_tensor *cu_seqlens, const ccv_tensor *seq_idx,
             const ccv_tensor *initial_states, const ccv_tensor *y,
-            const ccv_tensor *final_states, int activation, uint32_t *err_flag,
-            hipStream_t stream);
+            const ccv_tensor *final_states, int activation, uint32_t options,
+            uint32_t *err_flag, hipStream_t stream);
 
 /*
  * ccv_bwd — backward of L = <dy, y> + <dfinal_states, final_states>
@@ -149,7 +171,10 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
  *                   in a fixed order, to dweight (bit-exact run to run for
  *                   the same starting dweight); with a bias the call
  *                   returns CCV_ERR_NONDETERMINISTIC, or, with warn_only,
- *                   runs with atomics and returns CCV_WARN_NONDETERMINISTIC.
+ *                   runs with atomics and returns CCV_WARN_NONDETERMINISTIC,
+ *                   or, under CCV_OPT_DETERMINISTIC_DBIAS, reduces dbias
+ *                   through the partials too (W+1 columns per channel).
+ *   options         CCV_OPT_* bits.
  *   workspace / workspace_bytes:
  *                   query: workspace == NULL and workspace_bytes != NULL
  *                   -> *workspace_bytes = bytes needed, CCV_OK, nothing
@@ -164,7 +189,7 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
             const ccv_tensor *dfinal_states, const ccv_tensor *dx,
             const ccv_tensor *dweight, const ccv_tensor *dbias,
             const ccv_tensor *dinitial_states, int activation, int deterministic,
-            int warn_only, void *workspace, size_t *workspace_bytes,
+            int warn_only, uint32_t options, void *workspace, size_t *workspace_bytes,
             uint32_t *err_flag, hipStream_t stream);
 
 /*
@@ -176,14 +201,15 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
  *   conv_state  [B,D,W-1]  BF16, read and written in place: the state
  *                          (s_0..s_{W-2}, oldest first) becomes
  *                          (s_1..s_{W-2}, x).
- *   weight      [D,W]      BF16 (or FP32 without bias); W must be 4.
- *   bias        [D]        BF16, optional.
+ *   weight      [D,W]      BF16 or FP32; W in 2..4.
+ *   bias        [D]        optional; as in ccv_fwd (FP32 with an FP32
+ *                          weight under CCV_OPT_F32_FILTER_BIAS).
  *   y           [B,D]      BF16, written: act(bias + sum_k w_k v_k) over
  *                          v = (s_0..s_{W-2}, x).  Must not overlap any
  *                          other argument.
  */
 int ccv_update(const ccv_tensor *x, const ccv_tensor *conv_state, const ccv_tensor *weight,
-               const ccv_tensor *bias, const ccv_tensor *y, int activation,
+               const ccv_tensor *bias, const ccv_tensor *y, int activation, uint32_t options,
                hipStream_t stream);
 
 /*

@@ -55,8 +55,13 @@ def L():
     return _abi.lib()
 
 
-def fwd(L, x, w, b=None, cu=None, seq=None, init=None, y=None, fin=None, act=1, flag=None):
-    return L.ccv_fwd(R(x), R(w), R(b), R(cu), R(seq), R(init), R(y), R(fin), act, flag, None)
+F32FB, DETDB = _abi.CCV_OPT_F32_FILTER_BIAS, _abi.CCV_OPT_DETERMINISTIC_DBIAS
+
+
+def fwd(L, x, w, b=None, cu=None, seq=None, init=None, y=None, fin=None, act=1, flag=None,
+        opt=0):
+    return L.ccv_fwd(R(x), R(w), R(b), R(cu), R(seq), R(init), R(y), R(fin), act, opt, flag,
+                     None)
 
 
 def test_exports_every_declared_symbol(L):
@@ -68,7 +73,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.ccv_abi_version() == 1
+    assert L.ccv_abi_version() == _abi.ABI_VERSION == 2
     assert _abi.status_name(0) == "CCV_OK"
     assert _abi.status_name(-2) == "CCV_ERR_ALIAS"
     assert _abi.status_name(99) == "CCV_UNKNOWN_STATUS"
@@ -91,7 +96,9 @@ def test_fwd_rejects(L):
     assert fwd(L, x, w, y=None) == INVALID
     assert fwd(L, x, w, y=T([2, 64, 31])) == INVALID                # shape
     assert fwd(L, x, w, y=T([2, 64, 32], F32)) == INVALID          # dtype
-    assert fwd(L, x, T([64, 3]), y=y) == UNSUP                     # width
+    assert fwd(L, x, T([64, 5]), y=y) == UNSUP                     # width
+    assert fwd(L, x, T([64, 1]), y=y) == UNSUP
+    assert fwd(L, x, T([64, 3]), y=y, fin=T([2, 64, 3])) == INVALID  # W-1 state slots
     assert fwd(L, x, T([64, 4], F32), b=T([64]), y=y) == UNSUP     # FP32 filter + bias
     assert fwd(L, x, w, y=y, act=2) == UNSUP                       # activation
     assert fwd(L, x, w, y=y, seq=T([2, 32], I32)) == UNSUP         # seq_idx reserved
@@ -110,6 +117,24 @@ def test_fwd_rejects(L):
     assert fwd(L, x, w, y=y, fin=T([2, 64, 3], stride=[3, 1, 1])) == INVALID
     # bias dtype
     assert fwd(L, x, w, b=T([64], F32), y=y) == INVALID
+    assert fwd(L, x, w, b=T([64], F32), y=y, opt=F32FB) == INVALID  # BF16 filter, FP32 bias
+    # unknown option bits
+    assert fwd(L, x, w, y=y, opt=0x4) == INVALID
+    assert fwd(L, x, w, y=y, opt=0x80000000) == INVALID
+
+
+def test_fp32_filter_bias_option(L):
+    """FP32 weight with a bias: declined by default, admitted (FP32 bias only)
+    under the opt-in."""
+    x, _, y = dense()
+    w32 = T([64, 4], F32)
+    assert fwd(L, x, w32, b=T([64], F32), y=y) == UNSUP
+    assert fwd(L, x, w32, b=T([64]), y=y) == UNSUP
+    assert fwd(L, x, w32, b=T([64]), y=y, opt=F32FB) == INVALID     # BF16 bias
+    assert fwd(L, x, w32, b=T([64], I32), y=y, opt=F32FB) == INVALID
+    # aliasing is still checked under the option (returns before any launch)
+    b32 = T([64], F32)
+    assert fwd(L, x, w32, b=b32, y=T([2, 64, 32], data=b32.data), opt=F32FB) == ALIAS
 
 
 def test_fwd_alias(L):
@@ -128,9 +153,9 @@ def test_fwd_alias(L):
 
 
 def bwd(L, x, w, dy, dx, dw, b=None, db=None, init=None, dinit=None, dfin=None, cu=None,
-        det=0, warn=0, ws=None, wsb=None, flag=None, act=1, seq=None):
+        det=0, warn=0, ws=None, wsb=None, flag=None, act=1, seq=None, opt=0):
     return L.ccv_bwd(R(x), R(w), R(b), R(cu), R(seq), R(init), R(dy), R(dfin), R(dx), R(dw),
-                     R(db), R(dinit), act, det, warn, ws, wsb, flag, None)
+                     R(db), R(dinit), act, det, warn, opt, ws, wsb, flag, None)
 
 
 def test_bwd_rejects_and_policy(L):
@@ -166,16 +191,51 @@ def test_bwd_rejects_and_policy(L):
     ws = addr(q.value)
     assert bwd(L, x, w, dy, dx, dw, det=1, ws=ws, wsb=ctypes.byref(ctypes.c_size_t(q.value)),
                dfin=T([2, 64, 3], data=ws)) == ALIAS
+    assert bwd(L, x, w, dy, dx, dw, opt=0x8) == INVALID
+
+
+def test_deterministic_dbias_option(L):
+    """With the opt-in, a deterministic call with a bias takes the partials
+    route: the workspace gains one column per channel (P * D * (W+1) * 4
+    bytes, the same P as without a bias)."""
+    x, w, _ = dense()
+    dy, dx, dw = T([2, 64, 32]), T([2, 64, 32]), T([64, 4], F32)
+    b, db = T([64]), T([64], F32)
+    q0, q1 = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert bwd(L, x, w, dy, dx, dw, det=1, wsb=ctypes.byref(q0)) == 0
+    assert bwd(L, x, w, dy, dx, dw, b=b, db=db, det=1, opt=DETDB, wsb=ctypes.byref(q1)) == 0
+    assert q0.value > 0 and q1.value * 4 == q0.value * 5
+    # the opt-in changes nothing without deterministic (atomics, no workspace)
+    q2 = ctypes.c_size_t(7)
+    assert bwd(L, x, w, dy, dx, dw, b=b, db=db, opt=DETDB, wsb=ctypes.byref(q2)) == 0
+    assert q2.value == 0
+    # a too-small workspace is still rejected
+    ws = addr(q1.value)
+    assert bwd(L, x, w, dy, dx, dw, b=b, db=db, det=1, opt=DETDB, ws=ws,
+               wsb=ctypes.byref(ctypes.c_size_t(q0.value))) == INVALID
+    # both options together (FP32 filter + FP32 bias, deterministic dbias)
+    w32, b32 = T([64, 4], F32), T([64], F32)
+    q3 = ctypes.c_size_t(0)
+    assert bwd(L, x, w32, dy, dx, dw, b=b32, db=db, det=1, opt=DETDB,
+               wsb=ctypes.byref(q3)) == UNSUP
+    assert bwd(L, x, w32, dy, dx, dw, b=b32, db=db, det=1, opt=DETDB | F32FB,
+               wsb=ctypes.byref(q3)) == 0
+    assert q3.value == q1.value
 
 
 def test_update_rejects(L):
     x, st, w, y = T([4, 64]), T([4, 64, 3]), T([64, 4]), T([4, 64])
     up = lambda **k: L.ccv_update(R(k.get("x", x)), R(k.get("st", st)), R(k.get("w", w)),
-                                  R(k.get("b")), R(k.get("y", y)), k.get("act", 1), None)
+                                  R(k.get("b")), R(k.get("y", y)), k.get("act", 1),
+                                  k.get("opt", 0), None)
     assert up(x=None) == INVALID
     assert up(st=T([4, 64, 2])) == INVALID
-    assert up(w=T([64, 3]), st=T([4, 64, 2])) == UNSUP
+    assert up(w=T([64, 5]), st=T([4, 64, 4])) == UNSUP
+    assert up(w=T([64, 3]), st=T([4, 64, 3])) == INVALID
     assert up(w=T([64, 4], F32), b=T([64])) == UNSUP
+    assert up(w=T([64, 4], F32), b=T([64], F32)) == UNSUP
+    assert up(w=T([64, 4], F32), b=T([64]), opt=F32FB) == INVALID
+    assert up(opt=0x10) == INVALID
     assert up(act=7) == UNSUP
     assert up(y=T([4, 64], data=x.data)) == ALIAS
     assert up(y=T([4, 64], data=st.data + 2)) == ALIAS

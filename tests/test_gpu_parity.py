@@ -7,13 +7,15 @@ import pytest
 import torch
 
 import oracle
-from depthwise_causal_conv1d_02_amd import ops, synth
+from depthwise_causal_conv1d_02_amd import _abi, ops, synth
 from parity import (Guarded, check_bf16, check_exact_bf16, check_f32_rel, f64, guarded_act,
                     guarded_flat)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda", 0)
 BF16, F32 = torch.bfloat16, torch.float32
+OPT_F32 = _abi.CCV_OPT_F32_FILTER_BIAS
+OPT_DETDB = _abi.CCV_OPT_DETERMINISTIC_DBIAS
 
 
 def dev(t):
@@ -24,19 +26,20 @@ def dev(t):
     return d
 
 
-def inputs(seed, B, D, T, layout, bias=True, init=False, wdtype=BF16, dfinal=False, cu=None):
-    inp = synth.random_inputs(seed, B, D, T, layout=layout, bias=bias, init=init, dfinal=dfinal,
-                              weight_dtype=wdtype, cu_seqlens=cu)
+def inputs(seed, B, D, T, layout, bias=True, init=False, wdtype=BF16, dfinal=False, cu=None, W=4):
+    inp = synth.random_inputs(seed, B, D, T, layout=layout, W=W, bias=bias, init=init,
+                              dfinal=dfinal, weight_dtype=wdtype, cu_seqlens=cu)
     return inp, {k: dev(v) for k, v in inp.items()}
 
 
-def run_fwd(g, layout, act, ret_final, cu=None):
+def run_fwd(g, layout, act, ret_final, cu=None, options=0):
     B, D, T = g["x"].shape
     R = B if cu is None else cu.numel() - 1
+    W = g["weight"].shape[1]
     y = guarded_act(B, D, T, layout, DEV)
-    fin = guarded_flat((R, D, 3), DEV) if ret_final else None
+    fin = guarded_flat((R, D, W - 1), DEV) if ret_final else None
     ops.fwd(g["x"], g["weight"], g["bias"], g["cu_seqlens"], g["initial_states"], act,
-            final_states_out=None if fin is None else fin.view, y=y.view)
+            final_states_out=None if fin is None else fin.view, y=y.view, options=options)
     torch.cuda.synchronize()
     return y, fin
 
@@ -95,7 +98,7 @@ BWD_CASES = [
 ]
 
 
-def run_bwd(g, layout, act, det, cu=None):
+def run_bwd(g, layout, act, det, cu=None, options=0, dweight=None, dbias=None):
     B, D, T = g["x"].shape
     R = B if cu is None else cu.numel() - 1
     dx = guarded_act(B, D, T, layout, DEV)
@@ -103,20 +106,25 @@ def run_bwd(g, layout, act, det, cu=None):
     # dinit goes to a guarded buffer through the raw call
     _, dw, db, dinit_t = ops.bwd(g["x"], g["weight"], g["dy"], g["bias"], g["cu_seqlens"],
                                  g["initial_states"], g["dfinal_states"], act, det, False,
-                                 dx=dx.view)
+                                 dx=dx.view, options=options, dweight=dweight, dbias=dbias)
     torch.cuda.synchronize()
     return dx, dw, db, dinit_t
 
 
-def check_bwd(inp, dx, dw, db, dinit, act):
+def check_bwd(inp, dx, dw, db, dinit, act, dw0=None, db0=None):
+    """dw0/db0: the starting values the gradients were accumulated into."""
     odx, odw, odb, odinit = oracle.bwd(
         f64(inp["x"]), f64(inp["weight"]), f64(inp["dy"]), f64(inp["bias"]),
         None if inp["cu_seqlens"] is None else inp["cu_seqlens"].numpy(),
         f64(inp["initial_states"]), f64(inp["dfinal_states"]), act)
     check_bf16("dx", dx.view, odx)
     assert dx.intact(), "write outside dx"
+    if dw0 is not None:
+        odw = odw + f64(dw0)
     check_f32_rel("dweight", dw, odw)
     if odb is not None:
+        if db0 is not None:
+            odb = odb + f64(db0)
         check_f32_rel("dbias", db, odb)
     else:
         assert db is None
@@ -254,23 +262,28 @@ def test_validate_brute_force():
     assert all(want[i] == _flag_predicate(cu, t) for i, (cu, t) in enumerate(cases[:2000]))
 
 
-UPDATE_CASES = [(4, 512, True, BF16), (3, 40, True, BF16), (2, 1024, False, F32),
-                (5, 24, False, BF16)]
+UPDATE_CASES = [(4, 512, True, BF16, 4), (3, 40, True, BF16, 4), (2, 1024, False, F32, 4),
+                (5, 24, False, BF16, 4), (3, 512, True, BF16, 3), (4, 64, True, BF16, 2),
+                (1, 1024, False, F32, 3), (2, 40, True, BF16, 2)]
 
 
-@pytest.mark.parametrize("B,D,bias,wdt", UPDATE_CASES)
-def test_update_parity(B, D, bias, wdt):
-    print("update case", B, D, bias, wdt, flush=True)
+UPDATE_CASES += [(4, 512, True, F32, 4), (3, 40, True, F32, 3), (2, 64, True, F32, 2)]
+
+
+@pytest.mark.parametrize("B,D,bias,wdt,W", UPDATE_CASES)
+def test_update_parity(B, D, bias, wdt, W):
+    print("update case", B, D, bias, wdt, W, flush=True)
     gen = torch.Generator().manual_seed(500 + D)
-    state = synth.state_tensor(gen, B, D)
-    w = synth.weight_tensor(gen, D, dtype=wdt)
-    b = synth.bias_tensor(gen, D) if bias else None
+    state = synth.state_tensor(gen, B, D, W)
+    w = synth.weight_tensor(gen, D, W, dtype=wdt)
+    b = synth.bias_tensor(gen, D, wdt) if bias else None
+    opts = OPT_F32 if (bias and wdt == F32) else 0
     xs = [synth.activation_tensor(gen, B, D, 1, "tc")[:, :, 0].contiguous() for _ in range(6)]
     g_state = dev(state)
     st = f64(state)
     for x in xs:
         y = guarded_flat((B, D), DEV)
-        ops.update(dev(x), g_state, dev(w), dev(b), "silu", y=y.view)
+        ops.update(dev(x), g_state, dev(w), dev(b), "silu", y=y.view, options=opts)
         torch.cuda.synchronize()
         oy, st = oracle.update(f64(x), st, f64(w), f64(b), "silu")
         check_bf16("update y", y.view, oy)
@@ -341,3 +354,141 @@ def test_fp32_weight_rounding_is_single_rne():
     torch.cuda.synchronize()
     want = (x.float() * w[:, 3][None, :, None]).to(BF16)
     assert torch.equal(y.cpu(), want)
+
+
+WIDTH_CASES = [
+    # W, B, D, T, layout, bias, init, dfinal, weight dtype, deterministic, packed lengths
+    (2, 2, 1024, 150, "cl", True, True, True, BF16, False, None),
+    (3, 2, 1024, 150, "cl", False, True, True, BF16, True, None),
+    (3, 1, 520, 77, "cl", True, False, False, BF16, False, None),
+    (2, 2, 40, 33, "tc", False, True, True, F32, False, None),
+    (3, 1, 512, None, "cl", True, True, True, BF16, False, [1, 2, 3, 60, 1, 100]),
+    (2, 1, 136, None, "cl", False, True, True, F32, True, [2, 1, 40, 1]),
+]
+
+
+@pytest.mark.parametrize("case", WIDTH_CASES, ids=lambda c: "W%d-B%d-D%d-%s-%s" % (
+    c[0], c[1], c[2], c[4], "packed" if c[10] else "dense"))
+def test_other_widths(case):
+    W, B, D, T, layout, bias, init, dfinal, wdt, det, lengths = case
+    print("width case", case, flush=True)
+    cu = None
+    if lengths is not None:
+        cu = synth.cu_from_lengths(lengths)
+        T = int(cu[-1])
+    inp, g = inputs(900 + W + D, B, D, T, layout, bias, init, wdt, dfinal, cu, W=W)
+    ops.reset_flag(DEV)
+    y, fin = run_fwd(g, layout, "silu", True, cu)
+    check_fwd(inp, y, fin, "silu")
+    dx, dw, db, dinit = run_bwd(g, layout, "silu", det, cu)
+    check_bwd(inp, dx, dw, db, dinit, "silu")
+    ops.check_flag(DEV)
+
+
+# ---- opt-ins beyond the pages' route -------------------------------------------
+
+F32_BIAS_CASES = [
+    # W, B, D, T, layout, init, dfinal, deterministic, packed lengths, misaligned bias
+    (4, 2, 1536, 300, "cl", True, True, False, None, False),
+    (4, 3, 40, 77, "cl", True, True, True, None, False),
+    (4, 2, 1024, 64, "cl", False, False, False, None, True),
+    (3, 2, 48, 50, "tc", True, False, False, None, False),
+    (2, 1, 512, None, "cl", True, True, True, [1, 2, 3, 60, 1, 100], False),
+]
+
+
+@pytest.mark.parametrize("case", F32_BIAS_CASES, ids=lambda c: "W%d-B%d-D%d-%s-det%d-%s%s" % (
+    c[0], c[1], c[2], c[4], c[7], "packed" if c[8] else "dense", "-misaligned" if c[9] else ""))
+def test_fp32_weight_with_bias(case):
+    """An FP32 filter with an FP32 bias (declined by default) under the
+    opt-in: fwd and bwd against the oracle, on 8-, 4- and 1-channel lanes."""
+    W, B, D, T, layout, init, dfinal, det, lengths, misaligned = case
+    print("fp32 filter+bias case", case, flush=True)
+    cu = None
+    if lengths is not None:
+        cu = synth.cu_from_lengths(lengths)
+        T = int(cu[-1])
+    inp, g = inputs(1100 + W + D, B, D, T, layout, True, init, F32, dfinal, cu, W=W)
+    assert g["bias"].dtype == F32
+    if misaligned:
+        # a bias view 4 bytes into a buffer: not 16-byte aligned
+        holder = torch.zeros(D + 1, dtype=F32, device=DEV)
+        holder[1:].copy_(g["bias"])
+        g["bias"] = holder[1:]
+    with pytest.raises(NotImplementedError):
+        ops.fwd(g["x"], g["weight"], g["bias"], g["cu_seqlens"], g["initial_states"], "silu")
+    ops.reset_flag(DEV)
+    y, fin = run_fwd(g, layout, "silu", True, cu, options=OPT_F32)
+    check_fwd(inp, y, fin, "silu")
+    opts = OPT_F32 | (OPT_DETDB if det else 0)
+    dx, dw, db, dinit = run_bwd(g, layout, "silu", det, cu, options=opts)
+    assert db.dtype == F32
+    check_bwd(inp, dx, dw, db, dinit, "silu")
+    if det:
+        _, dw2, db2, _ = run_bwd(g, layout, "silu", det, cu, options=opts)
+        assert torch.equal(dw2.view(torch.int32), dw.view(torch.int32))
+        assert torch.equal(db2.view(torch.int32), db.view(torch.int32))
+    ops.check_flag(DEV)
+
+
+DET_DBIAS_CASES = [
+    # W, B, D, T, layout, packed lengths
+    (4, 2, 1536, 300, "cl", None),
+    (4, 1, 520, 2100, "cl", None),
+    (3, 3, 40, 77, "cl", None),
+    (4, 2, 48, 50, "tc", None),
+    (4, 1, 512, None, "cl", [1, 2, 3, 100, 17, 400, 5]),
+]
+
+
+@pytest.mark.parametrize("case", DET_DBIAS_CASES, ids=lambda c: "W%d-B%d-D%d-%s-%s" % (
+    c[0], c[1], c[2], c[4], "packed" if c[5] else "dense"))
+def test_deterministic_dbias(case):
+    """Deterministic dweight and dbias with a BF16 bias under the opt-in:
+    accumulated into non-zero gradients, equal to start + the oracle's, and
+    bit-identical over repeated runs."""
+    W, B, D, T, layout, lengths = case
+    print("deterministic dbias case", case, flush=True)
+    cu = None
+    if lengths is not None:
+        cu = synth.cu_from_lengths(lengths)
+        T = int(cu[-1])
+    inp, g = inputs(1200 + W + D, B, D, T, layout, True, True, BF16, True, cu, W=W)
+    gen = torch.Generator().manual_seed(1201)
+    dw0 = torch.randn(D, W, generator=gen)
+    db0 = torch.randn(D, generator=gen)
+    ops.reset_flag(DEV)
+    runs = []
+    for _ in range(3):
+        dw, db = dev(dw0.clone()), dev(db0.clone())
+        dx, dw, db, dinit = run_bwd(g, layout, "silu", True, cu, options=OPT_DETDB,
+                                    dweight=dw, dbias=db)
+        runs.append((dw.view(torch.int32).clone(), db.view(torch.int32).clone()))
+    check_bwd(inp, dx, dw, db, dinit, "silu", dw0=dw0, db0=db0)
+    for rw, rb in runs[1:]:
+        assert torch.equal(rw, runs[0][0]) and torch.equal(rb, runs[0][1])
+    ops.check_flag(DEV)
+
+
+def test_deterministic_dbias_autograd():
+    """The autograd surface: deterministic=True with a bias fails by default
+    and runs the fixed-order reduction under deterministic_dbias."""
+    inp, g = inputs(1300, 2, 512, 96, "cl", bias=True)
+    x = g["x"].detach().requires_grad_(True)
+    w = g["weight"].detach().requires_grad_(True)
+    b = g["bias"].detach().requires_grad_(True)
+    y = ops.causal_conv1d(x, w, b, activation="silu", deterministic=True)
+    with pytest.raises(RuntimeError):
+        (y.float() * g["dy"].float()).sum().backward()
+    grads = []
+    for _ in range(2):
+        x.grad = w.grad = b.grad = None
+        y = ops.causal_conv1d(x, w, b, activation="silu", deterministic=True,
+                              deterministic_dbias=True)
+        y.backward(g["dy"])
+        grads.append((w.grad.clone(), b.grad.clone()))
+    assert torch.equal(grads[0][0], grads[1][0]) and torch.equal(grads[0][1], grads[1][1])
+    _, odw, odb, _ = oracle.bwd(f64(inp["x"]), f64(inp["weight"]), f64(inp["dy"]),
+                                f64(inp["bias"]), None, None, None, "silu")
+    check_f32_rel("dweight", w.grad.float(), odw, rel=2e-2)
+    check_f32_rel("dbias", b.grad.float(), odb, rel=2e-2)
