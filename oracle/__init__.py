@@ -55,6 +55,11 @@ class _Oracle:
         lib.oracle_bwd.argtypes = [i64, i64, i64, i64, dp, dp, dp, ip, i64, dp, dp, dp,
                                    ctypes.c_int, dp, dp, dp, dp]
         lib.oracle_bwd.restype = ctypes.c_int
+        lib.oracle_fwd_seq.argtypes = [i64, i64, i64, i64, dp, dp, dp, ip, ctypes.c_int, dp]
+        lib.oracle_fwd_seq.restype = ctypes.c_int
+        lib.oracle_bwd_seq.argtypes = [i64, i64, i64, i64, dp, dp, dp, ip, dp, ctypes.c_int,
+                                       dp, dp, dp]
+        lib.oracle_bwd_seq.restype = ctypes.c_int
         lib.oracle_update.argtypes = [i64, i64, i64, dp, dp, dp, dp, ctypes.c_int, dp]
         lib.oracle_update.restype = ctypes.c_int
         lib.oracle_validate_cu_seqlens.argtypes = [ip, i64, i64]
@@ -183,6 +188,38 @@ def bwd(x, w, dy, bias=None, cu_seqlens=None, initial_states=None, dfinal_states
     if rc:
         raise ValueError("oracle_bwd rejected the arguments (%d)" % rc)
     return dx, dw, db, dinit
+
+
+def fwd_seq(x, w, seq_idx, bias=None, activation="silu"):
+    """Forward with per-token sequence ids seq_idx [B,T]: returns y [B,D,T]."""
+    x, w, bias, seq = _f64(x), _f64(w), _f64(bias), _i32(seq_idx)
+    B, D, T = x.shape
+    W = w.shape[1]
+    if seq.shape != (B, T):
+        raise ValueError("seq_idx must be [B,T]")
+    y = np.empty((B, D, T), np.float64)
+    rc = _L().oracle_fwd_seq(B, D, T, W, _ptr(x), _ptr(w), _ptr(bias), _ptr(seq),
+                             _act(activation), _ptr(y))
+    if rc:
+        raise ValueError("oracle_fwd_seq rejected the arguments (%d)" % rc)
+    return y
+
+
+def bwd_seq(x, w, dy, seq_idx, bias=None, activation="silu"):
+    """Backward of <dy, y> for fwd_seq: returns (dx, dw, dbias or None)."""
+    x, w, bias, dy, seq = _f64(x), _f64(w), _f64(bias), _f64(dy), _i32(seq_idx)
+    B, D, T = x.shape
+    W = w.shape[1]
+    if seq.shape != (B, T):
+        raise ValueError("seq_idx must be [B,T]")
+    dx = np.empty((B, D, T), np.float64)
+    dw = np.empty((D, W), np.float64)
+    db = np.empty((D,), np.float64) if bias is not None else None
+    rc = _L().oracle_bwd_seq(B, D, T, W, _ptr(x), _ptr(w), _ptr(bias), _ptr(seq), _ptr(dy),
+                             _act(activation), _ptr(dx), _ptr(dw), _ptr(db))
+    if rc:
+        raise ValueError("oracle_bwd_seq rejected the arguments (%d)" % rc)
+    return dx, dw, db
 
 
 def update(x, state, w, bias=None, activation="silu"):

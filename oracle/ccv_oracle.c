@@ -247,6 +247,99 @@ int oracle_bwd(int64_t B, int64_t D, int64_t T, int64_t W,
     return 0;
 }
 
+/* ---- per-token sequence ids (seq_idx) ----------------------------------- */
+/*
+ * cuDNN FE "Causal Conv1d": the tensor list names a seq_idx[B, T] keyword,
+ * kept for compatibility and mutually exclusive with cu_seqlens, i.e. a
+ * second way to pack several sequences into one row: seq[b][t] is the id of
+ * the sequence that token t of row b belongs to.  The page gives no further
+ * semantics; the reading taken here is the plainest one: tap k of output t
+ * sees input position p = t-(W-1)+k only when p >= 0 and seq[b][p] ==
+ * seq[b][t]; any other tap sees zero.  With ids that are constant over
+ * contiguous runs this is the packed route with zero initial states, one
+ * sequence per run.  No state tensors go with seq_idx.
+ */
+
+/* x at position p as seen from output position t (row b, channel d). */
+static double x_seen(const double *x, const int32_t *seq, int64_t b, int64_t d,
+                     int64_t p, int64_t t, int64_t D, int64_t T)
+{
+    if (p < 0 || seq[b * T + p] != seq[b * T + t])
+        return 0.0;
+    return x[(b * D + d) * T + p];
+}
+
+static double pre_act_seq(const double *x, const double *w, const double *bias,
+                          const int32_t *seq, int64_t b, int64_t d, int64_t t,
+                          int64_t D, int64_t T, int64_t W)
+{
+    double acc = 0.0;
+    for (int64_t k = 0; k < W; ++k)
+        acc += w[d * W + k] * x_seen(x, seq, b, d, t - (W - 1) + k, t, D, T);
+    if (bias)
+        acc += bias[d];
+    return acc;
+}
+
+int oracle_fwd_seq(int64_t B, int64_t D, int64_t T, int64_t W,
+                   const double *x, const double *w, const double *bias,
+                   const int32_t *seq, int act, double *y)
+{
+    if (B < 1 || D < 1 || T < 0 || W < 1 || !seq)
+        return -1;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t d = 0; d < D; ++d)
+            for (int64_t t = 0; t < T; ++t)
+                y[(b * D + d) * T + t] =
+                    act_value(act, pre_act_seq(x, w, bias, seq, b, d, t, D, T, W));
+    return 0;
+}
+
+/* Gradient of L = sum dy * y for the forward above:
+ *   g[t]     = dy[t] * act'(z[t])
+ *   dx[p]    = sum_k w[d,k] * g[t] over t = p + (W-1) - k < T with
+ *              seq[t] == seq[p]   (the taps that saw x[p])
+ *   dw[d,k]  = sum_t g[t] * (x[t-(W-1)+k] as seen from t)
+ *   dbias[d] = sum_t g[t]                                                   */
+int oracle_bwd_seq(int64_t B, int64_t D, int64_t T, int64_t W,
+                   const double *x, const double *w, const double *bias,
+                   const int32_t *seq, const double *dy, int act,
+                   double *dx, double *dw, double *dbias)
+{
+    if (B < 1 || D < 1 || T < 0 || W < 1 || !seq)
+        return -1;
+    for (int64_t d = 0; d < D; ++d) {
+        for (int64_t k = 0; k < W; ++k)
+            dw[d * W + k] = 0.0;
+        if (dbias)
+            dbias[d] = 0.0;
+    }
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t d = 0; d < D; ++d)
+            for (int64_t p = 0; p < T; ++p) {
+                double acc = 0.0;
+                for (int64_t k = 0; k < W; ++k) {
+                    int64_t t = p + (W - 1) - k;
+                    if (t < T && seq[b * T + t] == seq[b * T + p]) {
+                        double z = pre_act_seq(x, w, bias, seq, b, d, t, D, T, W);
+                        acc += w[d * W + k] * dy[(b * D + d) * T + t] * act_slope(act, z);
+                    }
+                }
+                dx[(b * D + d) * T + p] = acc;
+            }
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t d = 0; d < D; ++d)
+            for (int64_t t = 0; t < T; ++t) {
+                double z = pre_act_seq(x, w, bias, seq, b, d, t, D, T, W);
+                double g = dy[(b * D + d) * T + t] * act_slope(act, z);
+                for (int64_t k = 0; k < W; ++k)
+                    dw[d * W + k] += g * x_seen(x, seq, b, d, t - (W - 1) + k, t, D, T);
+                if (dbias)
+                    dbias[d] += g;
+            }
+    return 0;
+}
+
 /* ---- single-token update ------------------------------------------------ */
 
 /* cuDNN FE "Causal Conv1d", the paragraph on causal_conv1d_update: the state

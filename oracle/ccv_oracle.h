@@ -32,6 +32,15 @@ int oracle_bwd(int64_t B, int64_t D, int64_t T, int64_t W,
                const double *dy, const double *dfinal, int act,
                double *dx, double *dw, double *dbias, double *dinit);
 
+int oracle_fwd_seq(int64_t B, int64_t D, int64_t T, int64_t W,
+                   const double *x, const double *w, const double *bias,
+                   const int32_t *seq, int act, double *y);
+
+int oracle_bwd_seq(int64_t B, int64_t D, int64_t T, int64_t W,
+                   const double *x, const double *w, const double *bias,
+                   const int32_t *seq, const double *dy, int act,
+                   double *dx, double *dw, double *dbias);
+
 int oracle_update(int64_t B, int64_t D, int64_t W,
                   const double *x, double *state, const double *w,
                   const double *bias, int act, double *y);

@@ -406,6 +406,134 @@ def test_O11_flags_brute_force():
 
 
 # ---------------------------------------------------------------------------
+# O12 per-token sequence ids (seq_idx)
+# ---------------------------------------------------------------------------
+
+def _seq_problem(seed, B, D, T, W=4, bias=True):
+    r = _rng(seed)
+    return dict(x=r.standard_normal((B, D, T)), w=r.uniform(-0.5, 0.5, (D, W)),
+                bias=r.standard_normal(D) * 0.1 if bias else None,
+                dy=r.standard_normal((B, D, T)))
+
+
+def _runs_to_ids(lengths, first_id=0):
+    return np.concatenate([np.full(n, first_id + i, np.int32) for i, n in enumerate(lengths)])
+
+
+@pytest.mark.parametrize("W", [2, 3, 4])
+def test_O12_constant_ids_are_the_dense_route(W):
+    """One id per row: the library conv1d (float64, autograd) exactly as the
+    dense route with zero initial state."""
+    p = _seq_problem(21, 2, 3, 9, W)
+    seq = np.array([[5] * 9, [-2] * 9], np.int32)
+    y = oracle.fwd_seq(p["x"], p["w"], seq, p["bias"], "silu")
+    dx, dw, db = oracle.bwd_seq(p["x"], p["w"], p["dy"], seq, p["bias"], "silu")
+    xt = torch.tensor(p["x"], requires_grad=True)
+    wt = torch.tensor(p["w"], requires_grad=True)
+    bt = torch.tensor(p["bias"], requires_grad=True)
+    yt = F.silu(F.conv1d(F.pad(xt, (W - 1, 0)), wt[:, None, :], bt, groups=3))
+    (yt * torch.tensor(p["dy"])).sum().backward()
+    np.testing.assert_allclose(y, yt.detach().numpy(), rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(dx, xt.grad.numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dw, wt.grad.numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(db, bt.grad.numpy(), rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("lengths", [[1, 2, 3, 5, 8], [4, 1, 1, 13], [19]])
+def test_O12_contiguous_runs_are_the_packed_route(lengths):
+    """Ids constant over contiguous runs: every run is an independent
+    sequence, i.e. the packed route (cu_seqlens from the runs, no states), and
+    per-run library conv1d."""
+    T = sum(lengths)
+    p = _seq_problem(22, 1, 3, T)
+    seq = _runs_to_ids(lengths, first_id=7)[None, :]
+    y = oracle.fwd_seq(p["x"], p["w"], seq, p["bias"], "silu")
+    dx, dw, db = oracle.bwd_seq(p["x"], p["w"], p["dy"], seq, p["bias"], "silu")
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    yp, _ = oracle.fwd(p["x"], p["w"], p["bias"], cu, None, "silu")
+    dxp, dwp, dbp, _ = oracle.bwd(p["x"], p["w"], p["dy"], p["bias"], cu, None, None, "silu")
+    assert np.array_equal(y, yp)
+    np.testing.assert_allclose(dx, dxp, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(dw, dwp, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(db, dbp, rtol=1e-12, atol=1e-13)
+    for s, e in zip(cu[:-1], cu[1:]):
+        xt = torch.tensor(p["x"][:, :, s:e])
+        ref = F.silu(F.conv1d(F.pad(xt, (3, 0)), torch.tensor(p["w"])[:, None, :],
+                              torch.tensor(p["bias"]), groups=3))
+        np.testing.assert_allclose(y[:, :, s:e], ref.numpy(), rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("m", [2, 3])
+@pytest.mark.parametrize("W", [3, 4])
+def test_O12_periodic_ids_reduce_to_a_sparse_filter(m, W):
+    """ids[t] = t mod m: output t sees only positions t - j with j a multiple
+    of m, so the route equals the dense library conv1d with the other taps
+    zeroed (their dW is exactly zero); two rows, both activations."""
+    T = 11
+    p = _seq_problem(23, 2, 3, T, W)
+    seq = np.tile((np.arange(T) % m).astype(np.int32), (2, 1))
+    keep = np.array([(W - 1 - k) % m == 0 for k in range(W)])
+    for act in ("silu", None):
+        y = oracle.fwd_seq(p["x"], p["w"], seq, p["bias"], act)
+        dx, dw, db = oracle.bwd_seq(p["x"], p["w"], p["dy"], seq, p["bias"], act)
+        xt = torch.tensor(p["x"], requires_grad=True)
+        wt = torch.tensor(p["w"] * keep, requires_grad=True)
+        bt = torch.tensor(p["bias"], requires_grad=True)
+        z = F.conv1d(F.pad(xt, (W - 1, 0)), wt[:, None, :], bt, groups=3)
+        yt = F.silu(z) if act else z
+        (yt * torch.tensor(p["dy"])).sum().backward()
+        np.testing.assert_allclose(y, yt.detach().numpy(), rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(dx, xt.grad.numpy(), rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(dw[:, keep], wt.grad.numpy()[:, keep], rtol=1e-12,
+                                   atol=1e-13)
+        assert np.all(dw[:, ~keep] == 0.0)
+        np.testing.assert_allclose(db, bt.grad.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def _seq_loss(p, seq, act):
+    return float(np.sum(p["dy"] * oracle.fwd_seq(p["x"], p["w"], seq, p["bias"], act)))
+
+
+@pytest.mark.parametrize("act", ["silu", None])
+def test_O12_finite_differences_recurring_ids(act):
+    """Ids that recur within the window (no run structure): the backward is
+    the gradient of the forward, by central differences."""
+    p = _seq_problem(24, 2, 2, 9)
+    seq = np.array([[0, 1, 0, 0, 2, 1, 1, 2, 2], [3, 3, 4, 3, 4, 4, 3, 3, 3]], np.int32)
+    dx, dw, db = oracle.bwd_seq(p["x"], p["w"], p["dy"], seq, p["bias"], act)
+    h = 1e-6
+    for name, grad in (("x", dx), ("w", dw), ("bias", db)):
+        base = p[name]
+        num = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            plus, minus = base.copy(), base.copy()
+            plus[idx] += h
+            minus[idx] -= h
+            num[idx] = (_seq_loss(dict(p, **{name: plus}), seq, act) -
+                        _seq_loss(dict(p, **{name: minus}), seq, act)) / (2 * h)
+        np.testing.assert_allclose(grad, num, rtol=1e-7, atol=1e-7, err_msg=name)
+
+
+def test_O12_relabelling_and_row_isolation():
+    """Only equality of ids matters (a bijective relabelling changes nothing,
+    bit for bit), and rows never see each other."""
+    p = _seq_problem(25, 2, 3, 10)
+    seq = np.array([[0, 0, 1, 1, 1, 0, 2, 2, 1, 1], [4, 4, 4, 5, 5, 4, 4, 6, 6, 6]], np.int32)
+    relabel = {0: 100, 1: -3, 2: 7, 4: 0, 5: 2**31 - 1, 6: -2**31}
+    seq2 = np.vectorize(relabel.get)(seq).astype(np.int32)
+    y = oracle.fwd_seq(p["x"], p["w"], seq, p["bias"], "silu")
+    assert np.array_equal(y, oracle.fwd_seq(p["x"], p["w"], seq2, p["bias"], "silu"))
+    g1 = oracle.bwd_seq(p["x"], p["w"], p["dy"], seq, p["bias"], "silu")
+    g2 = oracle.bwd_seq(p["x"], p["w"], p["dy"], seq2, p["bias"], "silu")
+    for a, b in zip(g1, g2):
+        assert np.array_equal(a, b)
+    x2 = p["x"].copy()
+    x2[1] += 5.0
+    y2 = oracle.fwd_seq(x2, p["w"], seq, p["bias"], "silu")
+    assert np.array_equal(y[0], y2[0]) and not np.array_equal(y[1], y2[1])
+
+
+# ---------------------------------------------------------------------------
 # The pins catch planted mistakes
 # ---------------------------------------------------------------------------
 
@@ -417,7 +545,10 @@ MUTANTS = [
      "int64_t j = p - row.s + (W - 1);", "int64_t j = row.s - 1 - p;"),
     ("SiLU slope sign",
      "return s * (1.0 + z * (1.0 - s));", "return s * (1.0 - z * (1.0 - s));"),
-    ("bias dropped", "        acc += bias[d];\n    return acc;", "    return acc;"),
+    ("bias dropped",
+     "row, D, T, W);\n    if (bias)\n        acc += bias[d];", "row, D, T, W);"),
+    ("seq_idx bias dropped",
+     "t, D, T);\n    if (bias)\n        acc += bias[d];", "t, D, T);"),
     ("dfinal slot off by one",
      "int64_t j = tau - (row.e - (W - 1));", "int64_t j = tau - (row.e - W);"),
     ("packed row lookup off by one",
@@ -434,6 +565,16 @@ MUTANTS = [
     ("dx misses the in-row bound", "if (t >= row.s && t < row.e)", "if (t >= row.s)"),
     ("dinit taken at the wrong place",
      "row.s - (W - 1) + j, row, D, T, W);", "row.s - W + j, row, D, T, W);"),
+    ("seq_idx mask ignored",
+     "if (p < 0 || seq[b * T + p] != seq[b * T + t])", "if (p < 0)"),
+    ("seq_idx dx ignores the ids",
+     "if (t < T && seq[b * T + t] == seq[b * T + p]) {", "if (t < T) {"),
+    ("seq_idx dW unmasked",
+     "dw[d * W + k] += g * x_seen(x, seq, b, d, t - (W - 1) + k, t, D, T);",
+     "dw[d * W + k] += g * x_seen(x, seq, b, d, t - (W - 1) + k, t - (W - 1) + k, D, T);"),
+    ("seq_idx tap order reversed",
+     "acc += w[d * W + k] * x_seen(x, seq, b, d, t - (W - 1) + k, t, D, T);",
+     "acc += w[d * W + (W - 1 - k)] * x_seen(x, seq, b, d, t - (W - 1) + k, t, D, T);"),
 ]
 
 PIN_BATTERY = [
@@ -445,6 +586,9 @@ PIN_BATTERY = [
     lambda: test_O3_packed_equals_dense([1, 2, 3, 5, 8], True),
     lambda: test_O4_update_steps_reproduce_forward(2, True),
     test_O11_flags_brute_force,
+    lambda: test_O12_contiguous_runs_are_the_packed_route([1, 2, 3, 5, 8]),
+    lambda: test_O12_periodic_ids_reduce_to_a_sparse_filter(2, 4),
+    lambda: test_O12_finite_differences_recurring_ids("silu"),
 ]
 
 
