@@ -16,6 +16,8 @@ input already resident in HBM:
                     (the 64 seeded tokens are cycled).
   large             B=8 D=8192 T=8192, no bias: forward + deterministic backward.
   tiny              B=1 D=64 T=128 [B,D,T]: forward (launch-bound).
+  seqidx            the dense shape with sequences of U[64,1024] tokens per row
+                    marked by seq_idx (no states): forward + backward.
 
 The value is algorithmic bytes (every compulsory input read once, every output
 written once) per step divided by the wall time per step.  Per-op times come
@@ -99,7 +101,7 @@ class Workload:
 
         self.name, self.dev = name, dev
         to = lambda t: None if t is None else t.to(dev)
-        idx = {"tiny": 1, "dense": 2, "packed": 3, "decode": 4, "large": 5}[name]
+        idx = {"tiny": 1, "dense": 2, "packed": 3, "decode": 4, "large": 5, "seqidx": 6}[name]
         self.cpu = synth.workload(idx)
         w = self.cpu
         self.g = {k: to(v) if isinstance(v, torch.Tensor) else v for k, v in w.items()}
@@ -121,9 +123,11 @@ class Workload:
         bias = w["bias"] is not None
         init = w["initial_states"] is not None
         self.shape = dict(B=B, D=D, T=T, R=R)
-        self.bytes = {"fwd": fwd_bytes(B, D, T, R, init, w["return_final_states"], wb, bias)}
+        seq = B * T * 4 if w.get("seq_idx") is not None else 0   # the int32 ids
+        self.bytes = {"fwd": fwd_bytes(B, D, T, R, init, w["return_final_states"], wb, bias)
+                      + seq}
         if w["dy"] is not None:
-            self.bytes["bwd"] = bwd_bytes(B, D, T, R, init, False, wb, bias)
+            self.bytes["bwd"] = bwd_bytes(B, D, T, R, init, False, wb, bias) + seq
         if name == "dense":
             self.bytes["update"] = update_bytes(B, D, 2, bias)
         self.counts = {k: 1 for k in self.bytes}
@@ -167,9 +171,10 @@ def make_step(wl, torch):
     if g["return_final_states"] or wl.name == "dense":
         fin = torch.empty(wl.shape["R"], x.shape[1], 3, dtype=x.dtype, device=dev)
     flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    seq = g.get("seq_idx")
     calls = [("fwd", lambda: ops.fwd(x, g["weight"], g["bias"], g["cu_seqlens"],
                                      g["initial_states"], g["activation"],
-                                     final_states_out=fin, y=y, err_flag=flag))]
+                                     final_states_out=fin, y=y, err_flag=flag, seq_idx=seq))]
     outputs = {"y": y}
     if g["dy"] is not None:
         dx = torch.empty_like(x)
@@ -184,7 +189,8 @@ def make_step(wl, torch):
         calls.append(("bwd", lambda: ops.bwd(x, g["weight"], g["dy"], g["bias"], g["cu_seqlens"],
                                              g["initial_states"], None, g["activation"],
                                              g["deterministic"], False, dx=dx, err_flag=flag,
-                                             workspace=ws, dweight=dw, dbias=db, dinit=dinit)))
+                                             workspace=ws, dweight=dw, dbias=db, dinit=dinit,
+                                             seq_idx=seq)))
         outputs.update(dx=dx, dw=dw)
     if wl.name == "dense":
         # decode the next token straight from the returned final states
@@ -284,12 +290,19 @@ def cpu_baseline(wl, budget_s=10.0):
         sub = lambda t: None if t is None else f(t[:, :nch] if t.dim() == 3 else t[:nch])
         xs, ws_, bs = sub(x), sub(w["weight"]), sub(w["bias"])
         init, dy = sub(w["initial_states"]), sub(w["dy"])
+        seq = w.get("seq_idx")
         t0 = time.perf_counter()
-        oracle.fwd(xs, ws_, bs, cun, init, "silu", return_final_states=True)
-        if has_bwd:
-            oracle.bwd(xs, ws_, dy, bs, cun, init, None, "silu")
+        if seq is not None:
+            oracle.fwd_seq(xs, ws_, seq.numpy(), bs, "silu")
+            if has_bwd:
+                oracle.bwd_seq(xs, ws_, dy, seq.numpy(), bs, "silu")
+        else:
+            oracle.fwd(xs, ws_, bs, cun, init, "silu", return_final_states=True)
+            if has_bwd:
+                oracle.bwd(xs, ws_, dy, bs, cun, init, None, "silu")
         dt = time.perf_counter() - t0
-        nbytes = fwd_bytes(B, nch, T, R, init is not None, True, wb, bs is not None)
+        fin = w["return_final_states"]
+        nbytes = fwd_bytes(B, nch, T, R, init is not None, fin, wb, bs is not None)
         if has_bwd:
             nbytes += bwd_bytes(B, nch, T, R, init is not None, False, wb, bs is not None)
         return dt, nbytes
@@ -396,7 +409,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense",
-                    choices=["dense", "packed", "decode", "large", "tiny"])
+                    choices=["dense", "packed", "decode", "large", "tiny", "seqidx"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-events", action="store_true",
                     help="skip the per-op event pass")

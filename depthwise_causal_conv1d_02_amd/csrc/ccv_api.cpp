@@ -177,7 +177,9 @@ ccv::Strided3 s3(const ccv_tensor *t) {
 // Shared checks of the full-sequence calls (forward and backward inputs).
 struct Problem {
     int64_t B = 0, D = 0, T = 0, N = 0, R = 0, W = 0;
-    bool packed = false;
+    bool packed = false;  // rows packed by cu_seqlens
+    bool seq = false;     // tokens carry seq_idx sequence ids
+    int rows() const { return packed ? 1 : (seq ? 2 : 0); }  // the kernels' row mode
 };
 
 // The filter and bias dtypes: a BF16 filter takes a BF16 bias; an FP32
@@ -207,8 +209,14 @@ int check_inputs(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor
     if (present(bias) && (!well_formed(bias, 1) || !shape_is(bias, p.D)))
         return CCV_ERR_INVALID_ARG;
     if (options & ~kKnownOptions) return CCV_ERR_INVALID_ARG;
-    // seq_idx and cu_seqlens are mutually exclusive; seq_idx alone is reserved.
+    // seq_idx and cu_seqlens are mutually exclusive.
     if (present(seq_idx) && present(cu)) return CCV_ERR_INVALID_ARG;
+    if (present(seq_idx)) {
+        if (!well_formed(seq_idx, 2) || seq_idx->dtype != CCV_DTYPE_I32 ||
+            !shape_is(seq_idx, p.B, p.T))
+            return CCV_ERR_INVALID_ARG;
+        p.seq = true;
+    }
     if (present(cu)) {
         if (!well_formed(cu, 1) || cu->dtype != CCV_DTYPE_I32 || cu->stride[0] != 1 ||
             cu->shape[0] < 2 || p.B != 1 || err_flag == nullptr || cu->shape[0] - 1 > INT32_MAX)
@@ -220,9 +228,9 @@ int check_inputs(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor
     if (present(init) && (!well_formed(init, 3) || init->dtype != CCV_DTYPE_BF16 ||
                           !shape_is(init, p.R, p.D, weight->shape[1] - 1)))
         return CCV_ERR_INVALID_ARG;
-    // Declines: the reserved keyword, the width, FP32 filter with a bias
-    // (unless opted in), the activation set.
-    if (present(seq_idx)) return CCV_ERR_UNSUPPORTED;
+    // Declines: states with seq_idx (undefined there), the width, FP32 filter
+    // with a bias (unless opted in), the activation set.
+    if (p.seq && present(init)) return CCV_ERR_UNSUPPORTED;
     p.W = weight->shape[1];
     if (p.W < ccv::kMinWidth || p.W > ccv::kMaxWidth) return CCV_ERR_UNSUPPORTED;
     if (int rc = check_filter_dtypes(weight, bias, options)) return rc;
@@ -244,6 +252,14 @@ int check_act_tensor(const ccv_tensor *t, const Problem &p, bool output) {
         return CCV_ERR_INVALID_ARG;
     if (output && !injective(t)) return CCV_ERR_INVALID_ARG;
     return CCV_OK;
+}
+
+// The seq_idx fields of an argument block.
+template <typename A>
+void set_seq(A &a, const ccv_tensor *seq_idx, const Problem &p) {
+    a.seq = p.seq ? static_cast<const int32_t *>(seq_idx->data) : nullptr;
+    a.seq_sb = p.seq ? seq_idx->stride[0] : 0;
+    a.seq_st = p.seq ? seq_idx->stride[1] : 0;
 }
 
 // Every output span against every input span and every other output span.
@@ -325,12 +341,13 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     if (rc != CCV_OK) return rc;
     if ((rc = check_act_tensor(y, p, true)) != CCV_OK) return rc;
     if ((rc = check_state_out(final_states, p)) != CCV_OK) return rc;
+    if (p.seq && present(final_states)) return CCV_ERR_UNSUPPORTED;
 
     const Span outs[] = {span_of(y), span_of(final_states),
                          p.packed ? span_raw(err_flag, 4) : Span{}};
     const Span ins[] = {span_of(x), span_of(weight), span_of(bias), span_of(cu_seqlens),
-                        span_of(initial_states)};
-    if (any_alias(outs, 3, ins, 5)) return CCV_ERR_ALIAS;
+                        span_of(initial_states), span_of(seq_idx)};
+    if (any_alias(outs, 3, ins, 6)) return CCV_ERR_ALIAS;
 
     const int vec = pick_vec(CCV_FWD_VEC, weight, bias, x, y, nullptr);
     ccv::FwdArgs a;
@@ -350,9 +367,10 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     a.cu = p.packed ? static_cast<const int32_t *>(cu_seqlens->data) : nullptr;
     a.n_seq = p.N;
     a.err = p.packed ? err_flag : nullptr;
+    set_seq(a, seq_idx, p);
     a.pipe = p.B * p.D * p.T * 2 >= CCV_FWD_PIPE_MIN_BYTES;
     const int silu = activation == CCV_ACT_SILU;
-    const int64_t cap = CCV_FWD_ROUNDS > 0 ? ccv::fwd_resident_blocks(a, vec, silu, p.packed) : 0;
+    const int64_t cap = CCV_FWD_ROUNDS > 0 ? ccv::fwd_resident_blocks(a, vec, silu, p.rows()) : 0;
     const Geometry g = geometry(p, vec, ccv::kFwdWavesT, ccv::kFwdWavesC, cap, CCV_FWD_ROUNDS,
                                 CCV_FWD_TARGET_WAVES, CCV_FWD_MIN_CHUNK);
     a.B = p.B;
@@ -370,7 +388,7 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
         rc = hip_status(ccv::launch_validate(a.cu, p.N, p.T, err_flag, 0, stream));
         if (rc != CCV_OK) return rc;
     }
-    return hip_status(ccv::launch_fwd(a, vec, silu, p.packed, stream));
+    return hip_status(ccv::launch_fwd(a, vec, silu, p.rows(), stream));
 }
 
 int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bias,
@@ -393,6 +411,7 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
         return CCV_ERR_INVALID_ARG;
     if ((rc = check_state_out(dinitial_states, p)) != CCV_OK) return rc;
     if (present(dinitial_states) && !present(initial_states)) return CCV_ERR_INVALID_ARG;
+    if (p.seq && present(dfinal_states)) return CCV_ERR_UNSUPPORTED;
     // dweight [D,W] and dbias [D]: FP32, contiguous.
     if (!present(dweight) || !well_formed(dweight, 2) || dweight->dtype != CCV_DTYPE_F32 ||
         !shape_is(dweight, p.D, p.W) || dweight->stride[0] != p.W || dweight->stride[1] != 1)
@@ -439,8 +458,9 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     const Span outs[] = {span_of(dx), span_of(dweight), span_of(dbias), span_of(dinitial_states),
                          p.packed ? span_raw(err_flag, 4) : Span{}, span_raw(workspace, need)};
     const Span ins[] = {span_of(x), span_of(weight), span_of(bias), span_of(cu_seqlens),
-                        span_of(initial_states), span_of(dy), span_of(dfinal_states)};
-    if (any_alias(outs, 6, ins, 7)) return CCV_ERR_ALIAS;
+                        span_of(initial_states), span_of(dy), span_of(dfinal_states),
+                        span_of(seq_idx)};
+    if (any_alias(outs, 6, ins, 8)) return CCV_ERR_ALIAS;
 
     ccv::BwdArgs a;
     memset(&a, 0, sizeof(a));
@@ -465,9 +485,10 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     a.cu = p.packed ? static_cast<const int32_t *>(cu_seqlens->data) : nullptr;
     a.n_seq = p.N;
     a.err = p.packed ? err_flag : nullptr;
+    set_seq(a, seq_idx, p);
     const int silu = activation == CCV_ACT_SILU;
     if (!use_partials && CCV_BWD_ROUNDS > 0)
-        g = geometry(p, vec, ccv::kWavesPerBlock, 1, ccv::bwd_resident_blocks(a, vec, silu, p.packed),
+        g = geometry(p, vec, ccv::kWavesPerBlock, 1, ccv::bwd_resident_blocks(a, vec, silu, p.rows()),
                      CCV_BWD_ROUNDS, CCV_BWD_TARGET_WAVES, CCV_BWD_MIN_CHUNK);
     a.B = p.B;
     a.D = p.D;
@@ -485,7 +506,7 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
         rc = hip_status(ccv::launch_validate(a.cu, p.N, p.T, err_flag, 0, stream));
         if (rc != CCV_OK) return rc;
     }
-    rc = hip_status(ccv::launch_bwd(a, vec, silu, p.packed, stream));
+    rc = hip_status(ccv::launch_bwd(a, vec, silu, p.rows(), stream));
     if (rc != CCV_OK) return rc;
     if (use_partials) {
         rc = hip_status(ccv::launch_dw_reduce(a.partial, n_part, p.D, static_cast<int>(p.W),

@@ -54,12 +54,29 @@ constexpr uint32_t kFirstNonzero = 0x1u, kLastMismatch = 0x2u, kDecreasing = 0x4
 #ifndef CCV_BWD_MIN_WAVES
 #define CCV_BWD_MIN_WAVES 2
 #endif
-#define CCV_FWD_ATTR \
-    __attribute__((amdgpu_waves_per_eu(PIPE ? CCV_FWD_PIPE_MIN_WAVES : CCV_FWD_MIN_WAVES)))
+// Variants that would spill under the 4-wave budget (no activation, seq_idx
+// rows, packed rows with a bias) take the pipelined budget instead.
+#define CCV_FWD_ATTR                                                                 \
+    __attribute__((amdgpu_waves_per_eu(                                              \
+        (PIPE || !SILU || ROWS == kRowsSeq || (ROWS == kRowsPacked && fk_bias(FK)))  \
+            ? CCV_FWD_PIPE_MIN_WAVES                                                 \
+            : CCV_FWD_MIN_WAVES)))
 #ifdef CCV_BWD_MIN_WAVES
 #define CCV_BWD_ATTR __attribute__((amdgpu_waves_per_eu(CCV_BWD_MIN_WAVES)))
 #else
 #define CCV_BWD_ATTR
+#endif
+// Dynamic LDS (bytes) given to the backward and to the pipelined forward to
+// cap their blocks per CU (0: the registers alone decide).
+#ifndef CCV_BWD_DYN_LDS
+#define CCV_BWD_DYN_LDS 0
+#endif
+#ifndef CCV_FWD_PIPE_DYN_LDS
+#define CCV_FWD_PIPE_DYN_LDS 0
+#endif
+// Wave index through readfirstlane in the seq_idx kernels.
+#ifndef CCV_WAVE_UNIFORM
+#define CCV_WAVE_UNIFORM 1
 #endif
 
 // ---------------------------------------------------------------------------
@@ -181,11 +198,13 @@ __device__ __forceinline__ void decode_tile(int64_t tile, int64_t n_t, int64_t n
     b = tile / (n_t * n_c);
 }
 
-// Filter kinds: the weight dtype and whether a bias is present.
 // Filter kinds: the weight dtype and whether a bias is present.  The bias
 // has the weight's dtype (an FP32 filter with an FP32 bias is an opt-in of
 // the boundary).
 enum FilterKind { kBf16 = 0, kBf16Bias = 1, kF32 = 2, kF32Bias = 3 };
+// Row modes: dense batch rows, rows packed by cu_seqlens, or rows whose
+// tokens carry sequence ids (seq_idx).
+enum RowMode { kRowsDense = 0, kRowsPacked = 1, kRowsSeq = 2 };
 constexpr bool fk_f32(int fk) { return fk == kF32 || fk == kF32Bias; }
 constexpr bool fk_bias(int fk) { return fk == kBf16Bias || fk == kF32Bias; }
 
@@ -453,13 +472,102 @@ __device__ __forceinline__ void fwd_piece(const FwdArgs &a, int64_t b, int64_t r
     }
 }
 
-template <int W, int VEC, bool SILU, bool PACKED, int FK, bool PIPE>
+// ---------------------------------------------------------------------------
+// seq_idx rows (per-token sequence ids; no states).  Tap k of output t sees
+// x[t-(W-1)+k] only when that token carries t's id, so the window keeps the
+// ids of its W-1 tokens next to their values.  An id is the same for every
+// lane of a wave (one token of one row), so its load is a single broadcast.
+// ---------------------------------------------------------------------------
+template <int W>
+__device__ __forceinline__ void shift_id(int32_t (&idw)[W - 1], int32_t id) {
+#pragma unroll
+    for (int k = 0; k < W - 2; ++k) idw[k] = idw[k + 1];
+    idw[W - 2] = id;
+}
+
+// Ids of the W-1 positions before ta (0 before the row start, where the
+// values are zeros and the id is never used).
+template <int W>
+__device__ __forceinline__ void load_id_halo(const int32_t *sq, int64_t st, int64_t ta,
+                                             int32_t (&idw)[W - 1]) {
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) {
+        const int64_t p = ta - (W - 1) + j;
+        idw[j] = p >= 0 ? sq[p * st] : 0;
+    }
+}
+
+// z with the taps of other sequences masked: the same FP32 chain as preact
+// with a zero in place of a masked value.
+template <int W, int VEC>
+__device__ __forceinline__ float preact_seq(const float (&w)[W][VEC], const float (&bias)[VEC],
+                                            const float (&win)[W - 1][VEC],
+                                            const int32_t (&idw)[W - 1], int32_t id,
+                                            const float (&cur)[VEC], int c) {
+    float z = bias[c];
+#pragma unroll
+    for (int k = 0; k < W - 1; ++k) z = fmaf(w[k][c], idw[k] == id ? win[k][c] : 0.0f, z);
+    return fmaf(w[W - 1][c], cur[c], z);
+}
+
+template <int W, int VEC, bool SILU, bool NTL>
+__device__ __forceinline__ void fwd_seq_piece(const FwdArgs &a, int64_t b, int64_t ta,
+                                              int64_t tb, int64_t c0, const float (&w)[W][VEC],
+                                              const float (&bias)[VEC]) {
+    constexpr int U = CCV_FWD_UNROLL;
+    const uint16_t *xb = static_cast<const uint16_t *>(a.x.ptr) + b * a.x.s0 + c0 * a.x.s1;
+    uint16_t *yb = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.y.ptr)) + b * a.y.s0 +
+                   c0 * a.y.s1;
+    const int32_t *sq = a.seq + b * a.seq_sb;
+    const int64_t xs_t = a.x.s2, ys_t = a.y.s2, xs_d = a.x.s1, ys_d = a.y.s1, st = a.seq_st;
+    float win[W - 1][VEC];
+    int32_t idw[W - 1];
+    {
+        Raw<VEC> halo[W - 1];
+        issue_left_halo<W, VEC>(xb, xs_d, xs_t, 0, ta, halo);
+        load_id_halo<W>(sq, st, ta, idw);
+        finish_left_halo<W, VEC>(halo, a.init, b, 0, ta, c0, win);  // no state: zeros
+    }
+    auto step = [&](int64_t t, const Raw<VEC> &raw, int32_t id) {
+        float cur[VEC], out[VEC];
+        unpack<VEC>(raw, cur);
+#pragma unroll
+        for (int c = 0; c < VEC; ++c)
+            out[c] = act<SILU>(preact_seq<W, VEC>(w, bias, win, idw, id, cur, c));
+        store_vec<VEC, true>(yb + t * ys_t, ys_d, out);
+        shift_in<W, VEC>(win, cur);
+        shift_id<W>(idw, id);
+    };
+    int64_t t = ta;
+    for (; t + U <= tb; t += U) {
+        Raw<VEC> raw[U];
+        int32_t ids[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            raw[u] = load_raw<VEC, NTL>(xb + (t + u) * xs_t, xs_d);
+            ids[u] = sq[(t + u) * st];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) step(t + u, raw[u], ids[u]);
+    }
+    for (; t < tb; ++t) step(t, load_raw<VEC, NTL>(xb + t * xs_t, xs_d), sq[t * st]);
+}
+
+template <int W, int VEC, bool SILU, int ROWS, int FK, bool PIPE>
 __global__ __launch_bounds__(256) CCV_FWD_ATTR void k_fwd_chan(FwdArgs a) {
+    constexpr bool PACKED = ROWS == kRowsPacked;
     __shared__ int32_t s_cu[PACKED ? kLdsCuMax : 1];
     __shared__ uint32_t s_bad;
     int64_t b, gb, bt;
     decode_tile(xcd_remap(blockIdx.x, a.n_block), a.n_tblk, a.n_gblk, b, gb, bt);
-    const int wave = threadIdx.x / kWaveSize, lane = threadIdx.x % kWaveSize;
+    // The wave index is uniform over the wave; readfirstlane tells the
+    // compiler so, which keeps the time bounds and row offsets in scalars.
+    // Measured: it frees the registers the seq_idx walk needs, but slows
+    // the dense and packed streams on large inputs, so only seq_idx uses it.
+    const int wave = (ROWS == kRowsSeq && CCV_WAVE_UNIFORM)
+                         ? __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize)
+                         : static_cast<int>(threadIdx.x / kWaveSize);
+    const int lane = threadIdx.x % kWaveSize;
 
     if constexpr (PACKED) {
         if (stage_and_validate(a.cu, a.n_seq, a.T, a.err, s_cu, &s_bad, a.cu_in_lds,
@@ -478,7 +586,9 @@ __global__ __launch_bounds__(256) CCV_FWD_ATTR void k_fwd_chan(FwdArgs a) {
     // Non-temporal loads only when the operands exceed what caches can keep.
     auto run = [&](auto ntl) {
         constexpr bool NTL = decltype(ntl)::value;
-        if constexpr (!PACKED) {
+        if constexpr (ROWS == kRowsSeq) {
+            fwd_seq_piece<W, VEC, SILU, NTL>(a, b, t0, t1, c0, w, bias);
+        } else if constexpr (!PACKED) {
             fwd_piece<W, VEC, SILU, NTL, PIPE>(a, b, b, 0, a.T, t0, t1, c0, w, bias);
         } else {
             const int32_t *cu = a.cu_in_lds ? s_cu : a.cu;
@@ -702,8 +812,119 @@ __device__ __forceinline__ void bwd_piece(const BwdArgs &a, BwdLane<W, VEC, SILU
     }
 }
 
-template <int W, int VEC, bool SILU, bool PACKED, int FK>
+// seq_idx rows: the walk of bwd_piece (tau over [ta, tb + W-1), g[tau] in
+// registers, dx[tau-(W-1)] emitted) with the ids of the window's tokens kept
+// beside their values.  x[p] reaches output t only when id[p] == id[t], in
+// the forward (z), in dW, and in dx[p] = sum_k w[k] g[p+W-1-k] [same id].
+template <int W, int VEC, bool SILU, bool BIAS, bool NTL>
+__device__ __forceinline__ void bwd_seq_piece(const BwdArgs &a, BwdLane<W, VEC, SILU, BIAS> &L,
+                                              int64_t b, int64_t ta, int64_t tb, int64_t c0) {
+    constexpr int U = CCV_BWD_UNROLL;
+    const uint16_t *xb = static_cast<const uint16_t *>(a.x.ptr) + b * a.x.s0 + c0 * a.x.s1;
+    const uint16_t *dyb = static_cast<const uint16_t *>(a.dy.ptr) + b * a.dy.s0 + c0 * a.dy.s1;
+    uint16_t *dxb = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.dx.ptr)) +
+                    b * a.dx.s0 + c0 * a.dx.s1;
+    const int32_t *sq = a.seq + b * a.seq_sb;
+    const int64_t xs_d = a.x.s1, xs_t = a.x.s2, ys_d = a.dy.s1, ys_t = a.dy.s2;
+    const int64_t ds_d = a.dx.s1, ds_t = a.dx.s2, st = a.seq_st;
+
+    float xw[W - 1][VEC], gw[W - 1][VEC];
+    int32_t idw[W - 1];
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j)
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) gw[j][c] = 0.0f;
+    {
+        Raw<VEC> halo[W - 1];
+        issue_left_halo<W, VEC>(xb, xs_d, xs_t, 0, ta, halo);
+        load_id_halo<W>(sq, st, ta, idw);
+        finish_left_halo<W, VEC>(halo, a.init, b, 0, ta, c0, xw);  // no state: zeros
+    }
+    // One step at tau: g[tau] (zero past the row end), dW/dB when `count`,
+    // dx[tau-(W-1)] when `emit`.
+    auto step = [&](int64_t tau, const Raw<VEC> &rxv, const Raw<VEC> &rdv, int32_t id,
+                    bool in_row, bool count, bool emit, bool stream) {
+        float cur[VEC], gcur[VEC];
+        if (in_row) {
+            float dyv[VEC];
+            unpack<VEC>(rxv, cur);
+            unpack<VEC>(rdv, dyv);
+#pragma unroll
+            for (int c = 0; c < VEC; ++c)
+                gcur[c] = dyv[c] * act_slope<SILU>(preact_seq<W, VEC>(L.w, L.bias, xw, idw, id,
+                                                                      cur, c));
+            if (count) {
+#pragma unroll
+                for (int c = 0; c < VEC; ++c) {
+#pragma unroll
+                    for (int k = 0; k < W - 1; ++k)
+                        L.dw[k][c] = fmaf(gcur[c], idw[k] == id ? xw[k][c] : 0.0f, L.dw[k][c]);
+                    L.dw[W - 1][c] = fmaf(gcur[c], cur[c], L.dw[W - 1][c]);
+                    if constexpr (BIAS) L.db[c] += gcur[c];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) cur[c] = gcur[c] = 0.0f;
+        }
+        if (emit) {
+            // dx at p = tau-(W-1): its id is the window's oldest, idw[0].
+            const int32_t idp = idw[0];
+            float v[VEC];
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) {
+                float acc = L.w[0][c] * (id == idp ? gcur[c] : 0.0f);
+#pragma unroll
+                for (int j = W - 2; j >= 0; --j)
+                    acc = fmaf(L.w[W - 1 - j][c], idw[j] == idp ? gw[j][c] : 0.0f, acc);
+                v[c] = acc;
+            }
+            if (stream) store_vec<VEC, true>(dxb + (tau - (W - 1)) * ds_t, ds_d, v);
+            else store_vec<VEC>(dxb + (tau - (W - 1)) * ds_t, ds_d, v);
+        }
+        shift_in<W, VEC>(xw, cur);
+        shift_id<W>(idw, id);
+#pragma unroll
+        for (int k = 0; k < W - 2; ++k)
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) gw[k][c] = gw[k + 1][c];
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) gw[W - 2][c] = gcur[c];
+    };
+    // Fully checked step: head (no emission yet), right halo past tb.
+    auto generic = [&](int64_t tau) {
+        const bool in_row = tau < a.T;
+        Raw<VEC> rx{}, rd{};
+        int32_t id = 0;
+        if (in_row) {
+            rx = load_raw<VEC>(xb + tau * xs_t, xs_d);
+            rd = load_raw<VEC>(dyb + tau * ys_t, ys_d);
+            id = sq[tau * st];
+        }
+        step(tau, rx, rd, id, in_row, tau < tb, tau - (W - 1) >= ta, false);
+    };
+    const int64_t end = tb + (W - 1);
+    const int64_t head_end = ta + (W - 1) < end ? ta + (W - 1) : end;
+    int64_t tau = ta;
+    for (; tau < head_end; ++tau) generic(tau);
+    for (; tau + U <= tb; tau += U) {
+        Raw<VEC> rx[U], rd[U];
+        int32_t ids[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            rx[u] = load_raw<VEC, NTL>(xb + (tau + u) * xs_t, xs_d);
+            rd[u] = load_raw<VEC, NTL>(dyb + (tau + u) * ys_t, ys_d);
+            ids[u] = sq[(tau + u) * st];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) step(tau + u, rx[u], rd[u], ids[u], true, true, true, true);
+    }
+    for (; tau < end; ++tau) generic(tau);
+}
+
+template <int W, int VEC, bool SILU, int ROWS, int FK>
 __global__ __launch_bounds__(256) CCV_BWD_ATTR void k_bwd_chan(BwdArgs a) {
+    constexpr bool PACKED = ROWS == kRowsPacked;
     constexpr bool BIAS = fk_bias(FK);
     constexpr int CH = kWaveSize * VEC;  // channels of a block
     // One LDS buffer: the staged offsets during the walk, then the dW/dB
@@ -716,7 +937,14 @@ __global__ __launch_bounds__(256) CCV_BWD_ATTR void k_bwd_chan(BwdArgs a) {
     float (*s_red)[W + 1][CH + 1] = reinterpret_cast<float (*)[W + 1][CH + 1]>(s_buf);
     int64_t b, g, bt;
     decode_tile(xcd_remap(blockIdx.x, a.n_block), a.n_tblk, a.n_group, b, g, bt);
-    const int wave = threadIdx.x / kWaveSize, lane = threadIdx.x % kWaveSize;
+    // The wave index is uniform over the wave; readfirstlane tells the
+    // compiler so, which keeps the time bounds and row offsets in scalars.
+    // Measured: it frees the registers the seq_idx walk needs, but slows
+    // the dense and packed streams on large inputs, so only seq_idx uses it.
+    const int wave = (ROWS == kRowsSeq && CCV_WAVE_UNIFORM)
+                         ? __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize)
+                         : static_cast<int>(threadIdx.x / kWaveSize);
+    const int lane = threadIdx.x % kWaveSize;
 
     if constexpr (PACKED) {
         if (stage_and_validate(a.cu, a.n_seq, a.T, a.err, s_cu, &s_bad, a.cu_in_lds,
@@ -738,7 +966,9 @@ __global__ __launch_bounds__(256) CCV_BWD_ATTR void k_bwd_chan(BwdArgs a) {
         load_filter<W, VEC, FK>(a.w, a.w_sd, a.w_sk, a.bias, a.b_s, c0, L.w, L.bias);
         auto run = [&](auto ntl) {
             constexpr bool NTL = decltype(ntl)::value;
-            if constexpr (!PACKED) {
+            if constexpr (ROWS == kRowsSeq) {
+                bwd_seq_piece<W, VEC, SILU, BIAS, NTL>(a, L, b, t0, t1, c0);
+            } else if constexpr (!PACKED) {
                 bwd_piece<W, VEC, SILU, BIAS, NTL>(a, L, b, b, 0, a.T, t0, t1, c0);
             } else {
                 const int32_t *cu = a.cu_in_lds ? s_cu : a.cu;
@@ -1002,10 +1232,12 @@ __global__ __launch_bounds__(256) void k_dw_reduce(const float *part, int64_t n_
 // A stream value that never names a real stream: dispatch without launching.
 hipStream_t const kQueryStream = reinterpret_cast<hipStream_t>(~uintptr_t(0));
 
+// `lds` bytes of dynamic LDS (unused by the kernel) cap the blocks that fit
+// on one CU, i.e. the kernel's occupancy.
 template <typename K, typename A>
-hipError_t launch(K kernel, int64_t blocks, const A &args, hipStream_t s) {
+hipError_t launch(K kernel, int64_t blocks, const A &args, hipStream_t s, unsigned lds = 0) {
     if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, args);
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), lds, s, args);
     return hipGetLastError();
 }
 

@@ -16,55 +16,67 @@ int filter_kind(const A &a) {
 }
 
 template <typename K>
-int64_t capacity_of(K kernel) {
-    return resident_blocks(reinterpret_cast<const void *>(kernel));
+int64_t capacity_of(K kernel, unsigned lds) {
+    return resident_blocks(reinterpret_cast<const void *>(kernel), lds);
 }
 
-template <int W, int V, bool S, bool P, int F, bool Q>
+template <int W, int V, bool S, int P, int F, bool Q>
 hipError_t fwd_one(const FwdArgs &a, hipStream_t s, int64_t *cap) {
-    if (cap) *cap = capacity_of(k_fwd_chan<W, V, S, P, F, Q>);
-    if (s == kQueryStream) return hipSuccess;
-    return launch(k_fwd_chan<W, V, S, P, F, Q>, a.n_block, a, s);
+    if constexpr (P == kRowsSeq && Q) {
+        return hipErrorInvalidValue;  // seq_idx rows have no pipelined body
+    } else {
+        constexpr unsigned lds = Q ? CCV_FWD_PIPE_DYN_LDS : 0;
+        if (cap) *cap = capacity_of(k_fwd_chan<W, V, S, P, F, Q>, lds);
+        if (s == kQueryStream) return hipSuccess;
+        return launch(k_fwd_chan<W, V, S, P, F, Q>, a.n_block, a, s, lds);
+    }
 }
 
 template <int W, int V, bool Q>
-hipError_t fwd_vec(const FwdArgs &a, int silu, int packed, int fk, hipStream_t s, int64_t *cap) {
+hipError_t fwd_vec(const FwdArgs &a, int silu, int rows, int fk, hipStream_t s, int64_t *cap) {
 #define CCV_FWD(S, P, F) \
-    if (!!silu == S && !!packed == P && fk == F) return fwd_one<W, V, S, P, F, Q>(a, s, cap);
+    if (!!silu == S && rows == P && fk == F) return fwd_one<W, V, S, P, F, Q>(a, s, cap);
 #define CCV_FWD_K(S, P) \
     CCV_FWD(S, P, kBf16) CCV_FWD(S, P, kBf16Bias) CCV_FWD(S, P, kF32) CCV_FWD(S, P, kF32Bias)
-    CCV_FWD_K(true, false) CCV_FWD_K(true, true) CCV_FWD_K(false, false) CCV_FWD_K(false, true)
+    CCV_FWD_K(true, kRowsDense) CCV_FWD_K(true, kRowsPacked) CCV_FWD_K(false, kRowsDense)
+    CCV_FWD_K(false, kRowsPacked)
+    if constexpr (!Q) {
+        CCV_FWD_K(true, kRowsSeq) CCV_FWD_K(false, kRowsSeq)
+    }
 #undef CCV_FWD_K
 #undef CCV_FWD
     return hipErrorInvalidValue;
 }
 
-// The software-pipelined forward is built for 8-channel lanes only.
+// The software-pipelined forward is built for 8-channel lanes of dense and
+// packed rows only.
 template <int W>
-hipError_t fwd_dispatch(const FwdArgs &a, int vec, int silu, int packed, hipStream_t s,
+hipError_t fwd_dispatch(const FwdArgs &a, int vec, int silu, int rows, hipStream_t s,
                         int64_t *cap) {
     const int fk = filter_kind(a);
-    if (vec == 8 && a.pipe) return fwd_vec<W, 8, true>(a, silu, packed, fk, s, cap);
-    if (vec == 8) return fwd_vec<W, 8, false>(a, silu, packed, fk, s, cap);
-    if (vec == 4) return fwd_vec<W, 4, false>(a, silu, packed, fk, s, cap);
-    if (vec == 1) return fwd_vec<W, 1, false>(a, silu, packed, fk, s, cap);
+    if (vec == 8 && a.pipe && rows != kRowsSeq)
+        return fwd_vec<W, 8, true>(a, silu, rows, fk, s, cap);
+    if (vec == 8) return fwd_vec<W, 8, false>(a, silu, rows, fk, s, cap);
+    if (vec == 4) return fwd_vec<W, 4, false>(a, silu, rows, fk, s, cap);
+    if (vec == 1) return fwd_vec<W, 1, false>(a, silu, rows, fk, s, cap);
     return hipErrorInvalidValue;
 }
 
-template <int W, int V, bool S, bool P, int F>
+template <int W, int V, bool S, int P, int F>
 hipError_t bwd_one(const BwdArgs &a, hipStream_t s, int64_t *cap) {
-    if (cap) *cap = capacity_of(k_bwd_chan<W, V, S, P, F>);
+    if (cap) *cap = capacity_of(k_bwd_chan<W, V, S, P, F>, CCV_BWD_DYN_LDS);
     if (s == kQueryStream) return hipSuccess;
-    return launch(k_bwd_chan<W, V, S, P, F>, a.n_block, a, s);
+    return launch(k_bwd_chan<W, V, S, P, F>, a.n_block, a, s, CCV_BWD_DYN_LDS);
 }
 
 template <int W, int V>
-hipError_t bwd_vec(const BwdArgs &a, int silu, int packed, int fk, hipStream_t s, int64_t *cap) {
+hipError_t bwd_vec(const BwdArgs &a, int silu, int rows, int fk, hipStream_t s, int64_t *cap) {
 #define CCV_BWD(S, P, F) \
-    if (!!silu == S && !!packed == P && fk == F) return bwd_one<W, V, S, P, F>(a, s, cap);
+    if (!!silu == S && rows == P && fk == F) return bwd_one<W, V, S, P, F>(a, s, cap);
 #define CCV_BWD_K(S, P) \
     CCV_BWD(S, P, kBf16) CCV_BWD(S, P, kBf16Bias) CCV_BWD(S, P, kF32) CCV_BWD(S, P, kF32Bias)
-    CCV_BWD_K(true, false) CCV_BWD_K(true, true) CCV_BWD_K(false, false) CCV_BWD_K(false, true)
+    CCV_BWD_K(true, kRowsDense) CCV_BWD_K(true, kRowsPacked) CCV_BWD_K(true, kRowsSeq)
+    CCV_BWD_K(false, kRowsDense) CCV_BWD_K(false, kRowsPacked) CCV_BWD_K(false, kRowsSeq)
 #undef CCV_BWD_K
 #undef CCV_BWD
     return hipErrorInvalidValue;
@@ -73,11 +85,11 @@ hipError_t bwd_vec(const BwdArgs &a, int silu, int packed, int fk, hipStream_t s
 // Backward lanes own 4 channels (or 1): with 8, the window, gradient window
 // and dW accumulators leave too few registers for latency hiding.
 template <int W>
-hipError_t bwd_dispatch(const BwdArgs &a, int vec, int silu, int packed, hipStream_t s,
+hipError_t bwd_dispatch(const BwdArgs &a, int vec, int silu, int rows, hipStream_t s,
                         int64_t *cap) {
     const int fk = filter_kind(a);
-    if (vec == 4) return bwd_vec<W, 4>(a, silu, packed, fk, s, cap);
-    if (vec == 1) return bwd_vec<W, 1>(a, silu, packed, fk, s, cap);
+    if (vec == 4) return bwd_vec<W, 4>(a, silu, rows, fk, s, cap);
+    if (vec == 1) return bwd_vec<W, 1>(a, silu, rows, fk, s, cap);
     return hipErrorInvalidValue;
 }
 

@@ -1,5 +1,5 @@
 // ccv_internal.h — argument blocks shared by the host layer (ccv_api.cpp)
-// and the gfx950 kernels (ccv_kernels.hip).  Not part of the public ABI.
+// and the gfx950 kernels (ccv_device.h).  Not part of the public ABI.
 #pragma once
 
 #include <stddef.h>
@@ -45,6 +45,8 @@ struct FwdArgs {
     int64_t b_s;
     const int32_t *cu;         // packed offsets or nullptr
     int64_t n_seq;             // N (packed) ; unused dense
+    const int32_t *seq;        // seq_idx [B,T] or nullptr
+    int64_t seq_sb, seq_st;
     uint32_t *err;             // flag word (packed) or nullptr
     int64_t B, D, T;           // T = tokens per batch row (dense) or the packed total
     int64_t L;                 // time steps per wave
@@ -72,6 +74,8 @@ struct BwdArgs {
     int part_stride;           // W, or W+1 when dbias is reduced deterministically too
     const int32_t *cu;
     int64_t n_seq;
+    const int32_t *seq;        // seq_idx [B,T] or nullptr
+    int64_t seq_sb, seq_st;
     uint32_t *err;
     int64_t B, D, T, L, n_chunk, n_tblk, n_group, n_gblk, n_block;
     int cu_in_lds;
@@ -97,28 +101,29 @@ struct UpdArgs {
 };
 
 // Launchers (ccv_misc.hip).  `vec` is the channels per lane (8, 4 or 1); the
-// filter width comes from the argument block.
-hipError_t launch_fwd(const FwdArgs &a, int vec, int silu, int packed, hipStream_t s);
-hipError_t launch_bwd(const BwdArgs &a, int vec, int silu, int packed, hipStream_t s);
+// filter width comes from the argument block; `rows` is the row mode
+// (0 dense, 1 packed by cu_seqlens, 2 seq_idx).
+hipError_t launch_fwd(const FwdArgs &a, int vec, int silu, int rows, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs &a, int vec, int silu, int rows, hipStream_t s);
 hipError_t launch_update(const UpdArgs &a, int vec, int silu, hipStream_t s);
 int update_rows_per_lane();  // batch rows an 8-channel update lane serves
 // Blocks of the kernel launch_fwd / launch_bwd would pick that fit on the
 // current device at once (0 if the runtime cannot tell).  Host queries only.
-int64_t fwd_resident_blocks(const FwdArgs &a, int vec, int silu, int packed);
-int64_t bwd_resident_blocks(const BwdArgs &a, int vec, int silu, int packed);
+int64_t fwd_resident_blocks(const FwdArgs &a, int vec, int silu, int rows);
+int64_t bwd_resident_blocks(const BwdArgs &a, int vec, int silu, int rows);
 hipError_t launch_validate(const int32_t *cu, int64_t n_seq, int64_t total, uint32_t *flags,
                            int overwrite, hipStream_t s);
 hipError_t launch_dw_reduce(const float *partial, int64_t n_part, int64_t n_ch, int w, int kp,
                             float *dw, float *db, hipStream_t s);
-int64_t resident_blocks(const void *kernel);
+int64_t resident_blocks(const void *kernel, unsigned dyn_lds);
 
 // Per-width kernel selection (ccv_width.hip, built once per width).  With
 // `cap` set, the resident-block capacity of the selected kernel is stored
 // there; the stream kQueryStream selects without launching.
 #define CCV_DECLARE_WIDTH(W)                                                                   \
-    hipError_t fwd_dispatch_w##W(const FwdArgs &a, int vec, int silu, int packed, hipStream_t s, \
+    hipError_t fwd_dispatch_w##W(const FwdArgs &a, int vec, int silu, int rows, hipStream_t s, \
                                  int64_t *cap);                                                \
-    hipError_t bwd_dispatch_w##W(const BwdArgs &a, int vec, int silu, int packed, hipStream_t s, \
+    hipError_t bwd_dispatch_w##W(const BwdArgs &a, int vec, int silu, int rows, hipStream_t s, \
                                  int64_t *cap);                                                \
     hipError_t update_dispatch_w##W(const UpdArgs &a, int vec, int silu, hipStream_t s);
 CCV_DECLARE_WIDTH(2)

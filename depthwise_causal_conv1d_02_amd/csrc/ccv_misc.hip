@@ -7,53 +7,53 @@ namespace ccv {
 
 // Resident blocks of a kernel on the current device (CUs x blocks per CU),
 // from the occupancy the compiled kernel allows; 0 when it cannot be told.
-int64_t resident_blocks(const void *kernel) {
+int64_t resident_blocks(const void *kernel, unsigned dyn_lds) {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, dyn_lds) != hipSuccess)
         return 0;
     return static_cast<int64_t>(cus) * per_cu;
 }
 
-hipError_t launch_fwd(const FwdArgs &a, int vec, int silu, int packed, hipStream_t s) {
+hipError_t launch_fwd(const FwdArgs &a, int vec, int silu, int rows, hipStream_t s) {
     switch (a.width) {
-    case 2: return fwd_dispatch_w2(a, vec, silu, packed, s, nullptr);
-    case 3: return fwd_dispatch_w3(a, vec, silu, packed, s, nullptr);
-    case 4: return fwd_dispatch_w4(a, vec, silu, packed, s, nullptr);
+    case 2: return fwd_dispatch_w2(a, vec, silu, rows, s, nullptr);
+    case 3: return fwd_dispatch_w3(a, vec, silu, rows, s, nullptr);
+    case 4: return fwd_dispatch_w4(a, vec, silu, rows, s, nullptr);
     default: return hipErrorInvalidValue;
     }
 }
 
-int64_t fwd_resident_blocks(const FwdArgs &a, int vec, int silu, int packed) {
+int64_t fwd_resident_blocks(const FwdArgs &a, int vec, int silu, int rows) {
     int64_t cap = 0;
     hipError_t e = hipErrorInvalidValue;
     switch (a.width) {
-    case 2: e = fwd_dispatch_w2(a, vec, silu, packed, kQueryStream, &cap); break;
-    case 3: e = fwd_dispatch_w3(a, vec, silu, packed, kQueryStream, &cap); break;
-    case 4: e = fwd_dispatch_w4(a, vec, silu, packed, kQueryStream, &cap); break;
+    case 2: e = fwd_dispatch_w2(a, vec, silu, rows, kQueryStream, &cap); break;
+    case 3: e = fwd_dispatch_w3(a, vec, silu, rows, kQueryStream, &cap); break;
+    case 4: e = fwd_dispatch_w4(a, vec, silu, rows, kQueryStream, &cap); break;
     default: break;
     }
     return e == hipSuccess ? cap : 0;
 }
 
-hipError_t launch_bwd(const BwdArgs &a, int vec, int silu, int packed, hipStream_t s) {
+hipError_t launch_bwd(const BwdArgs &a, int vec, int silu, int rows, hipStream_t s) {
     switch (a.width) {
-    case 2: return bwd_dispatch_w2(a, vec, silu, packed, s, nullptr);
-    case 3: return bwd_dispatch_w3(a, vec, silu, packed, s, nullptr);
-    case 4: return bwd_dispatch_w4(a, vec, silu, packed, s, nullptr);
+    case 2: return bwd_dispatch_w2(a, vec, silu, rows, s, nullptr);
+    case 3: return bwd_dispatch_w3(a, vec, silu, rows, s, nullptr);
+    case 4: return bwd_dispatch_w4(a, vec, silu, rows, s, nullptr);
     default: return hipErrorInvalidValue;
     }
 }
 
-int64_t bwd_resident_blocks(const BwdArgs &a, int vec, int silu, int packed) {
+int64_t bwd_resident_blocks(const BwdArgs &a, int vec, int silu, int rows) {
     int64_t cap = 0;
     hipError_t e = hipErrorInvalidValue;
     switch (a.width) {
-    case 2: e = bwd_dispatch_w2(a, vec, silu, packed, kQueryStream, &cap); break;
-    case 3: e = bwd_dispatch_w3(a, vec, silu, packed, kQueryStream, &cap); break;
-    case 4: e = bwd_dispatch_w4(a, vec, silu, packed, kQueryStream, &cap); break;
+    case 2: e = bwd_dispatch_w2(a, vec, silu, rows, kQueryStream, &cap); break;
+    case 3: e = bwd_dispatch_w3(a, vec, silu, rows, kQueryStream, &cap); break;
+    case 4: e = bwd_dispatch_w4(a, vec, silu, rows, kQueryStream, &cap); break;
     default: break;
     }
     return e == hipSuccess ? cap : 0;

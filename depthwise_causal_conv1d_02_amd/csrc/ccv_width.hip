@@ -11,14 +11,14 @@
 
 namespace ccv {
 
-hipError_t CCV_CAT(fwd_dispatch_w, CCV_WIDTH)(const FwdArgs &a, int vec, int silu, int packed,
+hipError_t CCV_CAT(fwd_dispatch_w, CCV_WIDTH)(const FwdArgs &a, int vec, int silu, int rows,
                                                hipStream_t s, int64_t *cap) {
-    return fwd_dispatch<CCV_WIDTH>(a, vec, silu, packed, s, cap);
+    return fwd_dispatch<CCV_WIDTH>(a, vec, silu, rows, s, cap);
 }
 
-hipError_t CCV_CAT(bwd_dispatch_w, CCV_WIDTH)(const BwdArgs &a, int vec, int silu, int packed,
+hipError_t CCV_CAT(bwd_dispatch_w, CCV_WIDTH)(const BwdArgs &a, int vec, int silu, int rows,
                                                hipStream_t s, int64_t *cap) {
-    return bwd_dispatch<CCV_WIDTH>(a, vec, silu, packed, s, cap);
+    return bwd_dispatch<CCV_WIDTH>(a, vec, silu, rows, s, cap);
 }
 
 hipError_t CCV_CAT(update_dispatch_w, CCV_WIDTH)(const UpdArgs &a, int vec, int silu,

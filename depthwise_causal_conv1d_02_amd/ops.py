@@ -209,13 +209,13 @@ def update(x, conv_state, weight, bias=None, activation="silu", y=None, options=
 
 class _CausalConv1dFn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, x, weight, bias, cu_seqlens, initial_states, final_states_out, activation,
-                return_final_states, deterministic, options):
+    def forward(ctx, x, weight, bias, seq_idx, cu_seqlens, initial_states, final_states_out,
+                activation, return_final_states, deterministic, options):
         y, fin = fwd(x, weight, bias, cu_seqlens, initial_states, activation,
-                     return_final_states, final_states_out, options=options)
+                     return_final_states, final_states_out, seq_idx=seq_idx, options=options)
         # Inputs are saved for backward; the final state is written after the
         # forward (cuDNN FE "Causal Conv1d", the aliasing paragraph).
-        ctx.save_for_backward(x, weight, bias, cu_seqlens, initial_states)
+        ctx.save_for_backward(x, weight, bias, seq_idx, cu_seqlens, initial_states)
         ctx.activation = activation
         ctx.deterministic = deterministic
         ctx.options = options
@@ -226,7 +226,7 @@ class _CausalConv1dFn(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, dy, dfin):
-        x, weight, bias, cu_seqlens, init = ctx.saved_tensors
+        x, weight, bias, seq_idx, cu_seqlens, init = ctx.saved_tensors
         if dy is None:
             dy = torch.zeros_like(x)
         elif dy.stride() != x.stride():
@@ -236,11 +236,11 @@ class _CausalConv1dFn(torch.autograd.Function):
         if det is None:
             det = torch.are_deterministic_algorithms_enabled()
         warn_only = torch.is_deterministic_algorithms_warn_only_enabled()
-        need_dinit = init is not None and ctx.needs_input_grad[4]
+        need_dinit = init is not None and ctx.needs_input_grad[5]
         dx, dw, db, dinit = bwd(x, weight, dy, bias, cu_seqlens, init,
                                 dfin if ctx.has_fin else None, ctx.activation, det, warn_only,
-                                want_dinit=need_dinit, options=ctx.options)
-        return (dx, dw.to(weight.dtype), None if db is None else db.to(bias.dtype), None,
+                                want_dinit=need_dinit, seq_idx=seq_idx, options=ctx.options)
+        return (dx, dw.to(weight.dtype), None if db is None else db.to(bias.dtype), None, None,
                 dinit, None, None, None, None, None)
 
 
@@ -255,27 +255,29 @@ def causal_conv1d(x, weight, bias=None, seq_idx=None, cu_seqlens=None, initial_s
     set the device flag (see :func:`check_flag`) instead of trapping.
     Returns ``y`` or ``(y, final_states)``.
 
+    ``seq_idx`` [B,T] (int32) gives each token the id of its sequence: a tap
+    contributes only when its token has the output token's id.  It excludes
+    ``cu_seqlens`` and the state tensors.
+
     Two opt-ins widen what the pages' route declines: ``fp32_weight_bias``
     admits an FP32 weight with an FP32 bias, and ``deterministic_dbias``
     lets a deterministic backward with a bias reduce dbias in a fixed order
     instead of failing (or warning and using atomics).
     """
-    if seq_idx is not None:
-        if cu_seqlens is not None:
-            raise ValueError("seq_idx and cu_seqlens are mutually exclusive")
-        raise NotImplementedError("seq_idx is reserved and declined")
+    if seq_idx is not None and cu_seqlens is not None:
+        raise ValueError("seq_idx and cu_seqlens are mutually exclusive")
     if final_states_out is not None:
         return_final_states = True
     needs_grad = torch.is_grad_enabled() and any(
         t is not None and t.requires_grad for t in (x, weight, bias, initial_states))
     opts = _options(fp32_weight_bias, deterministic_dbias)
     if needs_grad:
-        y, fin = _CausalConv1dFn.apply(x, weight, bias, cu_seqlens, initial_states,
+        y, fin = _CausalConv1dFn.apply(x, weight, bias, seq_idx, cu_seqlens, initial_states,
                                        final_states_out, activation, return_final_states,
                                        deterministic, opts)
     else:
         y, fin = fwd(x, weight, bias, cu_seqlens, initial_states, activation,
-                     return_final_states, final_states_out, options=opts)
+                     return_final_states, final_states_out, seq_idx=seq_idx, options=opts)
     return (y, fin) if return_final_states else y
 
 

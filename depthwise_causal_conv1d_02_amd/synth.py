@@ -73,6 +73,30 @@ def packed_lengths(n_seq=16, lo=64, hi=4096, target=None, tol=0.01):
         seed += 1
 
 
+def seq_idx_tensor(g, B, T, kind="runs", max_run=64, n_ids=3, min_run=1):
+    """seq_idx [B,T] int32 ids: 'runs' = contiguous runs of U[min_run, max_run]
+    tokens with increasing ids (packed sequences), 'random' = iid ids from
+    {0..n_ids-1} (ids recur inside the window), 'periodic' = t mod n_ids,
+    'constant' = 0."""
+    if kind == "runs":
+        rows = []
+        for _ in range(B):
+            ids, cur = [], 0
+            while len(ids) < T:
+                n = int(torch.randint(min_run, max_run + 1, (1,), generator=g))
+                ids.extend([cur] * n)
+                cur += 1
+            rows.append(ids[:T])
+        return torch.tensor(rows, dtype=torch.int32)
+    if kind == "random":
+        return torch.randint(0, n_ids, (B, T), generator=g, dtype=torch.int32)
+    if kind == "periodic":
+        return (torch.arange(T, dtype=torch.int32) % n_ids).repeat(B, 1)
+    if kind == "constant":
+        return torch.zeros(B, T, dtype=torch.int32)
+    raise ValueError(kind)
+
+
 def cu_from_lengths(lengths):
     cu = [0]
     for n in lengths:
@@ -112,11 +136,13 @@ WORKLOADS = {
     4: "decode update: B=256 D=8192, 64 single-token steps, bf16 weight+bias, SiLU",
     5: "large dense fwd+bwd: B=8 D=8192 T=8192, channel-last, bf16 weight, no bias, SiLU, "
        "deterministic dweight",
+    6: "seq_idx fwd+bwd: B=4 D=4096 T=2048, channel-last, bf16 weight+bias, SiLU, each row "
+       "packs sequences of U[64,1024] tokens marked by seq_idx (no states)",
 }
 
 
 def workload(idx):
-    """Inputs of workload ``idx`` (1..5) as CPU tensors, seed = idx."""
+    """Inputs of workload ``idx`` (1..6) as CPU tensors, seed = idx."""
     g = torch.Generator().manual_seed(idx)
     if idx == 1:
         B, D, T = 1, 64, 128
@@ -149,4 +175,12 @@ def workload(idx):
                     bias=None, initial_states=None, dy=activation_tensor(g, B, D, T, "cl"),
                     cu_seqlens=None, activation="silu", return_final_states=False,
                     deterministic=True)
-    raise ValueError("workload index must be 1..5")
+    if idx == 6:
+        B, D, T = 4, 4096, 2048
+        x = activation_tensor(g, B, D, T, "cl")
+        weight, bias = weight_tensor(g, D), bias_tensor(g, D)
+        dy = activation_tensor(g, B, D, T, "cl")
+        return dict(x=x, weight=weight, bias=bias, initial_states=None, dy=dy, cu_seqlens=None,
+                    seq_idx=seq_idx_tensor(g, B, T, "runs", max_run=1024, min_run=64),
+                    activation="silu", return_final_states=False, deterministic=False)
+    raise ValueError("workload index must be 1..6")

@@ -76,7 +76,7 @@ typedef enum ccv_status {
      * (cuDNN FE "Causal Conv1d", the paragraph on final_states_out). */
     CCV_ERR_ALIAS = -2,
     /* Declined explicitly (cuDNN FE "Causal Conv1d", the optimized route):
-     * seq_idx given; FP32 weight with a bias (without
+     * state tensors together with seq_idx; FP32 weight with a bias (without
      * CCV_OPT_F32_FILTER_BIAS); a width outside 2..4; an activation other
      * than none or SiLU. */
     CCV_ERR_UNSUPPORTED = -3,
@@ -130,7 +130,13 @@ typedef struct ccv_tensor {
  *                            under CCV_OPT_F32_FILTER_BIAS.
  *   cu_seqlens      [N+1]    I32, optional; packs N sequences along T of a
  *                            B == 1 input.  Mutually exclusive with seq_idx.
- *   seq_idx         [B,T]    reserved: must be absent (declined otherwise).
+ *   seq_idx         [B,T]    I32, optional: the id of the sequence each token
+ *                            belongs to; tap k of output t sees position
+ *                            t-(W-1)+k only when that token has t's id (a
+ *                            reading of the page's compatibility keyword: only
+ *                            equality of ids matters).  Mutually exclusive
+ *                            with cu_seqlens; with it, initial_states and
+ *                            final_states are declined.
  *   initial_states  [R,D,W-1] BF16, optional; R = B dense, N packed.
  *   y               [B,D,T]  BF16, written.  Any layout; usually x's.
  *   final_states    [R,D,W-1] BF16, optional, written.
@@ -155,7 +161,8 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
  * (cuDNN FE "Causal Conv1d": the optimized route covers backward with the
  * W-1 initial and final state; the determinism paragraph).
  *
- *   x, weight, bias, cu_seqlens, seq_idx, initial_states: as in ccv_fwd.
+ *   x, weight, bias, cu_seqlens, seq_idx, initial_states: as in ccv_fwd
+ *                   (with seq_idx, dfinal_states is declined).
  *   dy              [B,D,T]  BF16, read.
  *   dfinal_states   [R,D,W-1] BF16, optional, read.
  *   dx              [B,D,T]  BF16, written.

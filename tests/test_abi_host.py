@@ -101,7 +101,13 @@ def test_fwd_rejects(L):
     assert fwd(L, x, T([64, 3]), y=y, fin=T([2, 64, 3])) == INVALID  # W-1 state slots
     assert fwd(L, x, T([64, 4], F32), b=T([64]), y=y) == UNSUP     # FP32 filter + bias
     assert fwd(L, x, w, y=y, act=2) == UNSUP                       # activation
-    assert fwd(L, x, w, y=y, seq=T([2, 32], I32)) == UNSUP         # seq_idx reserved
+    seq = T([2, 32], I32)
+    assert fwd(L, x, w, y=y, seq=seq, init=T([2, 64, 3])) == UNSUP     # states with seq_idx
+    assert fwd(L, x, w, y=y, seq=seq, fin=T([2, 64, 3])) == UNSUP
+    assert fwd(L, x, w, y=y, seq=T([2, 32])) == INVALID            # seq_idx dtype
+    assert fwd(L, x, w, y=y, seq=T([2, 31], I32)) == INVALID       # seq_idx shape
+    assert fwd(L, x, w, y=y, seq=T([2, 32, 1], I32)) == INVALID    # seq_idx rank
+    assert fwd(L, x, w, y=T([2, 64, 32], data=seq.data), seq=seq) == ALIAS
     cu = T([3], I32)
     assert fwd(L, x, w, y=y, seq=T([2, 32], I32), cu=cu, flag=addr(4)) == INVALID  # exclusive
     assert fwd(L, x, w, y=y, cu=cu, flag=addr(4)) == INVALID       # packed needs B == 1
@@ -192,6 +198,10 @@ def test_bwd_rejects_and_policy(L):
     assert bwd(L, x, w, dy, dx, dw, det=1, ws=ws, wsb=ctypes.byref(ctypes.c_size_t(q.value)),
                dfin=T([2, 64, 3], data=ws)) == ALIAS
     assert bwd(L, x, w, dy, dx, dw, opt=0x8) == INVALID
+    # seq_idx: no final-state gradient, and the ids are an input (alias)
+    seq = T([2, 32], I32)
+    assert bwd(L, x, w, dy, dx, dw, seq=seq, dfin=T([2, 64, 3])) == UNSUP
+    assert bwd(L, x, w, dy, T([2, 64, 32], data=seq.data), dw, seq=seq) == ALIAS
 
 
 def test_deterministic_dbias_option(L):
@@ -259,7 +269,7 @@ def test_python_surface_refuses_cpu_tensors():
     w = torch.zeros(8, 4, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU only"):
         causal_conv1d(x, w)
-    with pytest.raises(NotImplementedError):
+    with pytest.raises(ValueError, match="GPU only"):
         causal_conv1d(x, w, seq_idx=torch.zeros(1, 4, dtype=torch.int32))
     with pytest.raises(ValueError):
         causal_conv1d(x, w, seq_idx=torch.zeros(1, 4, dtype=torch.int32),

@@ -492,3 +492,99 @@ def test_deterministic_dbias_autograd():
                                 f64(inp["bias"]), None, None, None, "silu")
     check_f32_rel("dweight", w.grad.float(), odw, rel=2e-2)
     check_f32_rel("dbias", b.grad.float(), odb, rel=2e-2)
+
+
+# ---- seq_idx rows (per-token sequence ids) ------------------------------------
+
+SEQ_CASES = [
+    # W, B, D, T, layout, bias, act, id kind, weight dtype, deterministic
+    (4, 2, 1536, 300, "cl", True, "silu", "runs", BF16, False),
+    (4, 2, 1024, 257, "cl", False, "silu", "random", BF16, True),
+    (4, 3, 40, 77, "cl", True, None, "periodic", BF16, False),
+    (4, 2, 48, 50, "tc", True, "silu", "random", BF16, False),
+    (4, 1, 512, 4100, "cl", True, "silu", "runs", BF16, False),
+    (3, 2, 520, 130, "cl", True, "silu", "random", BF16, False),
+    (2, 2, 1024, 99, "cl", False, "silu", "runs", F32, True),
+    (4, 2, 512, 64, "cl", False, "silu", "constant", F32, False),
+]
+
+
+@pytest.mark.parametrize("case", SEQ_CASES, ids=lambda c: "W%d-B%d-D%d-T%d-%s-%s-%s%s" % (
+    c[0], c[1], c[2], c[3], c[4], c[7], "f32" if c[8] == F32 else "bf16",
+    "-det" if c[9] else ""))
+def test_seq_idx_parity(case):
+    W, B, D, T, layout, bias, act, kind, wdt, det = case
+    print("seq_idx case", case, flush=True)
+    inp, g = inputs(1400 + W + D + T, B, D, T, layout, bias, False, wdt, W=W)
+    gen = torch.Generator().manual_seed(1401 + T)
+    seq = synth.seq_idx_tensor(gen, B, T, kind)
+    gseq = dev(seq)
+    y = guarded_act(B, D, T, layout, DEV)
+    ops.fwd(g["x"], g["weight"], g["bias"], None, None, act, y=y.view, seq_idx=gseq)
+    torch.cuda.synchronize()
+    oy = oracle.fwd_seq(f64(inp["x"]), f64(inp["weight"]), seq.numpy(), f64(inp["bias"]), act)
+    check_bf16("y", y.view, oy)
+    assert y.intact(), "write outside y"
+    dx = guarded_act(B, D, T, layout, DEV)
+    _, dw, db, _ = ops.bwd(g["x"], g["weight"], g["dy"], g["bias"], None, None, None, act, det,
+                           False, dx=dx.view, seq_idx=gseq)
+    torch.cuda.synchronize()
+    odx, odw, odb = oracle.bwd_seq(f64(inp["x"]), f64(inp["weight"]), f64(inp["dy"]),
+                                   seq.numpy(), f64(inp["bias"]), act)
+    check_bf16("dx", dx.view, odx)
+    assert dx.intact(), "write outside dx"
+    check_f32_rel("dweight", dw, odw)
+    if odb is not None:
+        check_f32_rel("dbias", db, odb)
+    if det:
+        _, dw2, _, _ = ops.bwd(g["x"], g["weight"], g["dy"], g["bias"], None, None, None, act,
+                               det, False, seq_idx=gseq)
+        torch.cuda.synchronize()
+        assert torch.equal(dw2.view(torch.int32), dw.view(torch.int32))
+
+
+def test_seq_idx_strided_ids_and_runs_equal_packed():
+    """Ids read through a strided view ([T,B] storage transposed); ids that
+    form contiguous runs give exactly the packed route's y (same kernels'
+    arithmetic per token), checked against the oracle too."""
+    B, D, T = 1, 512, 333
+    inp, g = inputs(1500, B, D, T, "cl", True, False, BF16)
+    lengths = [5, 1, 100, 2, 77, 148]
+    cu = synth.cu_from_lengths(lengths)
+    ids = torch.repeat_interleave(torch.arange(len(lengths), dtype=torch.int32),
+                                  torch.tensor(lengths))[None, :]
+    store = torch.zeros(T, 3, dtype=torch.int32)
+    store[:, 1] = ids[0]
+    gseq = dev(store).t()[1:2]                        # [1,T], stride (1, 3)
+    assert gseq.stride() == (1, 3)
+    y_seq, _ = ops.fwd(g["x"], g["weight"], g["bias"], None, None, "silu", seq_idx=gseq)
+    ops.reset_flag(DEV)
+    y_pk, _ = ops.fwd(g["x"], g["weight"], g["bias"], dev(cu), None, "silu")
+    torch.cuda.synchronize()
+    ops.check_flag(DEV)
+    oy = oracle.fwd_seq(f64(inp["x"]), f64(inp["weight"]), ids.numpy(), f64(inp["bias"]),
+                        "silu")
+    check_bf16("y", y_seq, oy)
+    assert torch.equal(y_seq, y_pk)
+
+
+def test_seq_idx_autograd_and_declines():
+    B, D, T = 2, 512, 96
+    inp, g = inputs(1600, B, D, T, "cl", True, True, BF16)
+    seq = synth.seq_idx_tensor(torch.Generator().manual_seed(1601), B, T, "runs", max_run=20)
+    gseq = dev(seq)
+    x = g["x"].detach().requires_grad_(True)
+    w = g["weight"].detach().requires_grad_(True)
+    b = g["bias"].detach().requires_grad_(True)
+    y = ops.causal_conv1d(x, w, b, seq_idx=gseq, activation="silu")
+    y.backward(g["dy"])
+    odx, odw, odb = oracle.bwd_seq(f64(inp["x"]), f64(inp["weight"]), f64(inp["dy"]),
+                                   seq.numpy(), f64(inp["bias"]), "silu")
+    check_bf16("dx", x.grad, odx)
+    check_f32_rel("dweight", w.grad.float(), odw, rel=2e-2)
+    check_f32_rel("dbias", b.grad.float(), odb, rel=2e-2)
+    with pytest.raises(NotImplementedError):
+        ops.causal_conv1d(g["x"], g["weight"], g["bias"], seq_idx=gseq,
+                          initial_states=g["initial_states"])
+    with pytest.raises(NotImplementedError):
+        ops.causal_conv1d(g["x"], g["weight"], g["bias"], seq_idx=gseq, return_final_states=True)

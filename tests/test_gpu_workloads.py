@@ -41,13 +41,15 @@ def run_workload(idx):
     B, D, T = x.shape
     R = B if w["cu_seqlens"] is None else w["cu_seqlens"].numel() - 1
     flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    seq = g.get("seq_idx")
     y, fin = ops.fwd(x, g["weight"], g["bias"], g["cu_seqlens"], g["initial_states"],
-                     g["activation"], return_final_states=w["return_final_states"], err_flag=flag)
+                     g["activation"], return_final_states=w["return_final_states"], err_flag=flag,
+                     seq_idx=seq)
     out = {"y": y, "fin": fin}
     if g["dy"] is not None:
         dx, dw, db, dinit = ops.bwd(x, g["weight"], g["dy"], g["bias"], g["cu_seqlens"],
                                     g["initial_states"], None, g["activation"], g["deterministic"],
-                                    False, err_flag=flag)
+                                    False, err_flag=flag, seq_idx=seq)
         out.update(dx=dx, dw=dw, db=db, dinit=dinit)
     torch.cuda.synchronize()
     assert int(flag.item()) == 0
@@ -134,3 +136,17 @@ def test_workload_5_large_deterministic():
                               True, False, dx=dx)
         torch.cuda.synchronize()
         assert torch.equal(dw.view(torch.int32), ref)
+
+
+def test_workload_6_seq_idx_fwd_bwd():
+    w, g, out = run_workload(6)
+    D = w["x"].shape[1]
+    sel = sample_channels(D)
+    seq = w["seq_idx"].numpy()
+    xs, ws, bs = f(sub(w["x"], sel)), f(sub(w["weight"], sel)), f(sub(w["bias"], sel))
+    oy = oracle.fwd_seq(xs, ws, seq, bs, "silu")
+    check_bf16("y", out["y"][:, sel], oy)
+    odx, odw, odb = oracle.bwd_seq(xs, ws, f(sub(w["dy"], sel)), seq, bs, "silu")
+    check_bf16("dx", out["dx"][:, sel], odx)
+    check_f32_rel("dweight", out["dw"][sel], odw)
+    check_f32_rel("dbias", out["db"][sel], odb)
