@@ -42,6 +42,12 @@ METRIC = "achieved HBM GB/s (% of MI355X peak) for fwd, bwd and update at 1 GPU"
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "depthwise_causal_conv1d_02_amd", "csrc")
 OP_KERNEL = {"fwd": "k_fwd_chan", "bwd": "k_bwd_chan", "update": "k_update"}
+OP_KERNEL_TIME = {"fwd": "k_fwd_tc", "bwd": "k_bwd_tc", "update": "k_update"}
+
+
+def op_kernels(workload):
+    """op -> kernel name prefix of a workload (time-lane kernels for *_tc)."""
+    return OP_KERNEL_TIME if workload.endswith("_tc") else OP_KERNEL
 
 
 def source_hash():
@@ -100,13 +106,19 @@ class Workload:
         from depthwise_causal_conv1d_02_amd import synth
 
         self.name, self.dev = name, dev
+        # "<workload>_tc": the same data in [B,D,T] storage (unit time stride)
+        self.kind = name[:-3] if name.endswith("_tc") else name
         to = lambda t: None if t is None else t.to(dev)
-        idx = {"tiny": 1, "dense": 2, "packed": 3, "decode": 4, "large": 5, "seqidx": 6}[name]
+        idx = {"tiny": 1, "dense": 2, "packed": 3, "decode": 4, "large": 5,
+               "seqidx": 6}[self.kind]
         self.cpu = synth.workload(idx)
+        if name.endswith("_tc"):
+            self.cpu = dict(self.cpu, x=self.cpu["x"].contiguous(),
+                            dy=None if self.cpu["dy"] is None else self.cpu["dy"].contiguous())
         w = self.cpu
         self.g = {k: to(v) if isinstance(v, torch.Tensor) else v for k, v in w.items()}
         self.ops = []
-        if name == "decode":
+        if self.kind == "decode":
             B, D = w["conv_state"].shape[:2]
             n_tok = w["x_steps"].shape[0]
             self.shape = dict(B=B, D=D, tokens=n_tok)
@@ -128,10 +140,12 @@ class Workload:
                       + seq}
         if w["dy"] is not None:
             self.bytes["bwd"] = bwd_bytes(B, D, T, R, init, False, wb, bias) + seq
-        if name == "dense":
+        if self.kind == "dense":
             self.bytes["update"] = update_bytes(B, D, 2, bias)
         self.counts = {k: 1 for k in self.bytes}
         self.desc = synth.WORKLOADS[idx]
+        if name.endswith("_tc"):
+            self.desc = self.desc.replace("channel-last", "[B,D,T] time-contiguous")
 
 
 class Step:
@@ -154,7 +168,7 @@ def make_step(wl, torch):
     from depthwise_causal_conv1d_02_amd import ops
 
     g, dev = wl.g, wl.dev
-    if wl.name == "decode":
+    if wl.kind == "decode":
         state = g["conv_state"].clone()
         xs = g["x_steps"]
         ys = torch.empty_like(xs)
@@ -168,7 +182,7 @@ def make_step(wl, torch):
     x = g["x"]
     y = torch.empty_like(x)
     fin = None
-    if g["return_final_states"] or wl.name == "dense":
+    if g["return_final_states"] or wl.kind == "dense":
         fin = torch.empty(wl.shape["R"], x.shape[1], 3, dtype=x.dtype, device=dev)
     flag = torch.zeros(1, dtype=torch.int32, device=dev)
     seq = g.get("seq_idx")
@@ -192,7 +206,7 @@ def make_step(wl, torch):
                                              workspace=ws, dweight=dw, dbias=db, dinit=dinit,
                                              seq_idx=seq)))
         outputs.update(dx=dx, dw=dw)
-    if wl.name == "dense":
+    if wl.kind == "dense":
         # decode the next token straight from the returned final states
         # (updated in place; the next step's forward rewrites them)
         xt = g["x"][:, :, -1].contiguous()
@@ -259,7 +273,7 @@ def cpu_baseline(wl, budget_s=10.0):
 
     w = wl.cpu
     f = lambda t: None if t is None else t.double().numpy()
-    if wl.name == "decode":
+    if wl.kind == "decode":
         B, D = w["conv_state"].shape[:2]
         nb = 16
         st = f(w["conv_state"][:nb])
@@ -341,8 +355,13 @@ def summarize(args):
     (kernel trace, FETCH_SIZE pass, WRITE_SIZE pass, and the same two counters
     for a plain copy of known size)."""
     import glob
-    wl_bytes = {"dense": {"fwd": fwd_bytes(4, 4096, 2048, 4, True, True, 2, True),
-                          "bwd": bwd_bytes(4, 4096, 2048, 4, True, False, 2, True)},
+    dense = {"fwd": fwd_bytes(4, 4096, 2048, 4, True, True, 2, True),
+             "bwd": bwd_bytes(4, 4096, 2048, 4, True, False, 2, True)}
+    large = {"fwd": fwd_bytes(8, 8192, 8192, 8, False, False, 2, False),
+             "bwd": bwd_bytes(8, 8192, 8192, 8, False, False, 2, False)}
+    wl_bytes = {"dense": dense, "dense_tc": dense, "large_tc": large,
+                "seqidx": {"fwd": fwd_bytes(4, 4096, 2048, 4, False, False, 2, True) + 4 * 2048 * 4,
+                           "bwd": bwd_bytes(4, 4096, 2048, 4, False, False, 2, True) + 4 * 2048 * 4},
                 "packed": {"fwd": fwd_bytes(1, 5120, 33280, 16, True, True, 4, False),
                            "bwd": bwd_bytes(1, 5120, 33280, 16, True, False, 4, False)},
                 "large": {"fwd": fwd_bytes(8, 8192, 8192, 8, False, False, 2, False),
@@ -357,7 +376,7 @@ def summarize(args):
     f_scale = copy_bytes / (c_fetch * 1024.0)   # counter KiB -> bytes read
     w_scale = copy_bytes / (c_write * 1024.0)
     h = source_hash()
-    for op, kernel in OP_KERNEL.items():
+    for op, kernel in op_kernels(args.workload).items():
         if op not in wl_bytes:
             continue
         mine = [r for r in rows if r["_short"].startswith(kernel)]
@@ -409,7 +428,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense",
-                    choices=["dense", "packed", "decode", "large", "tiny", "seqidx"])
+                    choices=["dense", "packed", "decode", "large", "tiny", "seqidx", "dense_tc",
+                             "large_tc"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-events", action="store_true",
                     help="skip the per-op event pass")
@@ -509,7 +529,7 @@ def main():
                          "launches_per_step": wl.counts[k],
                          "GB_s": round(gbs, 1), "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2)}
         dom = max(means, key=lambda k: means[k] * wl.counts[k])
-        kernel = OP_KERNEL[dom]
+        kernel = op_kernels(wl.name)[dom]
         ach = wl.bytes[dom] / (means[dom] * 1e-3) / 1e9
         rec = recorded_traffic(kernel, wl.name)
         roof = {"bound": "hbm", "kernel": kernel, "op": dom, "achieved": round(ach, 1),

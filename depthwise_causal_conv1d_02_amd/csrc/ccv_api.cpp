@@ -163,6 +163,18 @@ int pick_vec(int preferred, const ccv_tensor *weight, const ccv_tensor *bias,
     return 1;
 }
 
+// Time lanes (unit stride along T): every activation tensor has unit time
+// stride and 16-byte aligned row starts; dense rows only.
+bool time_lanes_ok(const ccv_tensor *a, const ccv_tensor *b, const ccv_tensor *c) {
+    for (const ccv_tensor *t : {a, b, c}) {
+        if (t == nullptr) continue;
+        if (t->stride[2] != 1 || t->stride[0] % 8 != 0 || t->stride[1] % 8 != 0 ||
+            !aligned16(t->data))
+            return false;
+    }
+    return true;
+}
+
 ccv::Strided3 s3(const ccv_tensor *t) {
     ccv::Strided3 s{nullptr, 0, 0, 0};
     if (present(t)) {
@@ -309,6 +321,18 @@ Geometry geometry(const Problem &p, int vec, int wt, int wc, int64_t capacity, i
     return g;
 }
 
+// Time-lane geometry: one wave per (row, chunk of kTcTiles tiles).
+Geometry time_geometry(const Problem &p) {
+    Geometry g;
+    g.L = static_cast<int64_t>(ccv::kTcTiles) * ccv::kTcTile;
+    g.n_chunk = (p.T + g.L - 1) / g.L;
+    g.n_tblk = g.n_chunk;  // partials per batch row: one per chunk
+    g.n_group = p.D;
+    g.n_gblk = p.D;
+    g.n_block = (p.B * p.D * g.n_chunk + ccv::kWavesPerBlock - 1) / ccv::kWavesPerBlock;
+    return g;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? CCV_OK : CCV_ERR_HIP; }
 
 }  // namespace
@@ -349,7 +373,8 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
                         span_of(initial_states), span_of(seq_idx)};
     if (any_alias(outs, 3, ins, 6)) return CCV_ERR_ALIAS;
 
-    const int vec = pick_vec(CCV_FWD_VEC, weight, bias, x, y, nullptr);
+    const bool time_lanes = !p.packed && !p.seq && time_lanes_ok(x, y, nullptr);
+    const int vec = time_lanes ? ccv::kVecTime : pick_vec(CCV_FWD_VEC, weight, bias, x, y, nullptr);
     ccv::FwdArgs a;
     memset(&a, 0, sizeof(a));
     a.width = static_cast<int>(p.W);
@@ -370,9 +395,13 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     set_seq(a, seq_idx, p);
     a.pipe = p.B * p.D * p.T * 2 >= CCV_FWD_PIPE_MIN_BYTES;
     const int silu = activation == CCV_ACT_SILU;
-    const int64_t cap = CCV_FWD_ROUNDS > 0 ? ccv::fwd_resident_blocks(a, vec, silu, p.rows()) : 0;
-    const Geometry g = geometry(p, vec, ccv::kFwdWavesT, ccv::kFwdWavesC, cap, CCV_FWD_ROUNDS,
-                                CCV_FWD_TARGET_WAVES, CCV_FWD_MIN_CHUNK);
+    const int64_t cap = CCV_FWD_ROUNDS > 0 && !time_lanes
+                            ? ccv::fwd_resident_blocks(a, vec, silu, p.rows())
+                            : 0;
+    const Geometry g = time_lanes ? time_geometry(p)
+                                  : geometry(p, vec, ccv::kFwdWavesT, ccv::kFwdWavesC, cap,
+                                             CCV_FWD_ROUNDS, CCV_FWD_TARGET_WAVES,
+                                             CCV_FWD_MIN_CHUNK);
     a.B = p.B;
     a.D = p.D;
     a.T = p.T;
@@ -435,12 +464,14 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
         }
     }
     const int64_t kp = p.W + (present(bias) ? 1 : 0);  // partial columns per channel
-    const int vec = pick_vec(CCV_BWD_VEC, weight, bias, x, dy, dx);
+    const bool time_lanes = !p.packed && !p.seq && time_lanes_ok(x, dy, dx);
+    const int vec = time_lanes ? ccv::kVecTime : pick_vec(CCV_BWD_VEC, weight, bias, x, dy, dx);
     // The partials of the deterministic route depend on the shape only (a
     // grid sized by target waves); the atomic route sizes its grid by the
     // device's resident capacity below.
-    Geometry g = geometry(p, vec, ccv::kWavesPerBlock, 1, 0, 0, CCV_BWD_TARGET_WAVES,
-                          CCV_BWD_MIN_CHUNK);
+    Geometry g = time_lanes ? time_geometry(p)
+                            : geometry(p, vec, ccv::kWavesPerBlock, 1, 0, 0,
+                                       CCV_BWD_TARGET_WAVES, CCV_BWD_MIN_CHUNK);
     const int64_t n_part = (p.packed ? 1 : p.B) * g.n_tblk;
     const size_t need = use_partials
                             ? static_cast<size_t>(n_part) * static_cast<size_t>(p.D * kp) * 4
@@ -487,7 +518,7 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     a.err = p.packed ? err_flag : nullptr;
     set_seq(a, seq_idx, p);
     const int silu = activation == CCV_ACT_SILU;
-    if (!use_partials && CCV_BWD_ROUNDS > 0)
+    if (!use_partials && CCV_BWD_ROUNDS > 0 && !time_lanes)
         g = geometry(p, vec, ccv::kWavesPerBlock, 1, ccv::bwd_resident_blocks(a, vec, silu, p.rows()),
                      CCV_BWD_ROUNDS, CCV_BWD_TARGET_WAVES, CCV_BWD_MIN_CHUNK);
     a.B = p.B;

@@ -1031,6 +1031,320 @@ __global__ __launch_bounds__(256) CCV_BWD_ATTR void k_bwd_chan(BwdArgs a) {
 }
 
 // ===========================================================================
+// Time-contiguous rows (unit stride along T, e.g. a contiguous [B,D,T]).
+//
+// Lanes run along time: a lane owns kTcE = 8 consecutive tokens of one
+// (b, d) row (one 16-byte vector), a wave one tile of 512 consecutive tokens,
+// and a wave walks a chunk of kTcTiles tiles in order, all of whose loads are
+// issued before the first use.  The W-1 tokens before a lane's first token
+// come from the lane before (a cross-lane shift); lane 0 takes them from the
+// previous tile's lane 63, or at the chunk start from memory (the input, the
+// initial state, or zeros).  The filter taps and the bias belong to the row,
+// so they are wave-uniform.
+// ===========================================================================
+__device__ __forceinline__ float lane_up(float v) { return __shfl_up(v, 1, kWaveSize); }
+__device__ __forceinline__ float lane_down(float v) { return __shfl_down(v, 1, kWaveSize); }
+__device__ __forceinline__ float from_lane(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = kWaveSize / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWaveSize);
+    return v;
+}
+
+// A lane's kTcE tokens from t on a unit-stride row; the tokens at or past
+// `end` read as zeros.  Whole vectors when they fit (the host has checked
+// 16-byte aligned row starts).
+template <bool NTL>
+__device__ __forceinline__ Raw<8> tc_load(const uint16_t *row, int64_t t, int64_t end) {
+    if (t + kTcE <= end) return load_raw<8, NTL>(row + t, 1);
+    Raw<8> r;
+    r.v = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < kTcE; ++i)
+        if (t + i < end) r.v[i / 2] |= static_cast<uint32_t>(row[t + i]) << (16 * (i % 2));
+    return r;
+}
+
+template <bool STREAM>
+__device__ __forceinline__ void tc_store(uint16_t *row, int64_t t, int64_t end,
+                                         const float (&v)[kTcE]) {
+    if (t + kTcE <= end) {
+        store_vec<8, STREAM>(row + t, 1, v);
+    } else {
+#pragma unroll
+        for (int i = 0; i < kTcE; ++i)
+            if (t + i < end) row[t + i] = to_bf16_bits(v[i]);
+    }
+}
+
+// x_ext at a position p < T of row (b, d): the input for p >= 0, else the
+// initial state slot p + W-1, else zero.
+template <int W>
+__device__ __forceinline__ float tc_x_ext(const uint16_t *xr, const Strided3 &init, int64_t b,
+                                          int64_t d, int64_t p) {
+    if (p >= 0) return bf16_bits_to_f32(xr[p]);
+    if (!init.ptr) return 0.0f;
+    return bf16_bits_to_f32(static_cast<const uint16_t *>(
+        init.ptr)[b * init.s0 + d * init.s1 + (p + W - 1) * init.s2]);
+}
+
+// Work item of a time-lane wave: row (b, d) and chunk [t0, t1).
+struct TcItem {
+    int64_t b, d, chunk, t0, t1;
+};
+template <typename A>
+__device__ __forceinline__ bool tc_item(const A &a, TcItem &it) {
+    const int64_t wid = xcd_remap(blockIdx.x, a.n_block) * kWavesPerBlock +
+                        __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
+    if (wid >= a.B * a.D * a.n_chunk) return false;
+    const int64_t row = wid / a.n_chunk;
+    it.chunk = wid % a.n_chunk;
+    it.b = row / a.D;
+    it.d = row % a.D;
+    it.t0 = it.chunk * a.L;
+    it.t1 = min(it.t0 + a.L, a.T);
+    return true;
+}
+
+template <int W, bool SILU, int FK, bool NTL>
+__device__ __forceinline__ void fwd_tc_chunk(const FwdArgs &a, const TcItem &it) {
+    const int lane = threadIdx.x % kWaveSize;
+    const uint16_t *xr = static_cast<const uint16_t *>(a.x.ptr) + it.b * a.x.s0 + it.d * a.x.s1;
+    uint16_t *yr = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.y.ptr)) +
+                   it.b * a.y.s0 + it.d * a.y.s1;
+    Raw<8> raw[kTcTiles];
+#pragma unroll
+    for (int c = 0; c < kTcTiles; ++c) {
+        const int64_t t = it.t0 + c * kTcTile + lane * kTcE;
+        if (t < it.t1) raw[c] = tc_load<NTL>(xr, t, it.t1);
+        else raw[c].v = u32x4_t{0u, 0u, 0u, 0u};
+    }
+    float w[W][1], bias[1];
+    load_filter<W, 1, FK>(a.w, a.w_sd, a.w_sk, a.bias, a.b_s, it.d, w, bias);
+    float carry[W - 1];  // x_ext of the W-1 tokens before the current tile
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) carry[j] = tc_x_ext<W>(xr, a.init, it.b, it.d, it.t0 - (W - 1) + j);
+
+#pragma unroll
+    for (int c = 0; c < kTcTiles; ++c) {
+        const int64_t tt = it.t0 + c * kTcTile;
+        if (tt >= it.t1) break;
+        float v[kTcE], xe[W - 1 + kTcE], out[kTcE];
+        unpack<8>(raw[c], v);
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) {
+            const float up = lane_up(v[kTcE - (W - 1) + j]);
+            xe[j] = lane == 0 ? carry[j] : up;
+        }
+#pragma unroll
+        for (int i = 0; i < kTcE; ++i) xe[W - 1 + i] = v[i];
+#pragma unroll
+        for (int i = 0; i < kTcE; ++i) {
+            float z = bias[0];
+#pragma unroll
+            for (int k = 0; k < W; ++k) z = fmaf(w[k][0], xe[i + k], z);
+            out[i] = act<SILU>(z);
+        }
+        const int64_t t = tt + lane * kTcE;
+        if (t < it.t1) tc_store<true>(yr, t, it.t1, out);
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) carry[j] = from_lane(v[kTcE - (W - 1) + j], kWaveSize - 1);
+    }
+    // The chunk that ends the row writes its final state: the last W-1
+    // extended tokens, copied bit for bit.
+    if (it.t1 == a.T && a.fin.ptr && lane < W - 1) {
+        const int64_t p = a.T - (W - 1) + lane;
+        uint16_t bits = 0;
+        if (p >= 0) bits = xr[p];
+        else if (a.init.ptr)
+            bits = static_cast<const uint16_t *>(a.init.ptr)[it.b * a.init.s0 + it.d * a.init.s1 +
+                                                             (p + W - 1) * a.init.s2];
+        const_cast<uint16_t *>(static_cast<const uint16_t *>(a.fin.ptr))
+            [it.b * a.fin.s0 + it.d * a.fin.s1 + lane * a.fin.s2] = bits;
+    }
+}
+
+template <int W, bool SILU, int FK>
+__global__ __launch_bounds__(256) void k_fwd_tc(FwdArgs a) {
+    TcItem it;
+    if (!tc_item(a, it)) return;
+    if (a.nt_load) fwd_tc_chunk<W, SILU, FK, true>(a, it);
+    else fwd_tc_chunk<W, SILU, FK, false>(a, it);
+}
+
+// Backward on time lanes.  Per tile: z and g = dy * act'(z) for the lane's
+// tokens, dW/dB accumulated per lane; dx[p] = sum_k w[k] g[p+W-1-k] needs
+// the next W-1 g's, from the next lane or, for lane 63, from the next tile,
+// so a tile's dx is emitted once the next tile's g is known.  After the
+// chunk's last tile the W-1 g's past the chunk are computed directly (the
+// right halo).  dW/dB: one wave sum per chunk, then an atomic or a unique
+// partial.
+template <int W, bool SILU, int FK, bool NTL>
+__device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it) {
+    constexpr bool BIAS = fk_bias(FK);
+    const int lane = threadIdx.x % kWaveSize;
+    const uint16_t *xr = static_cast<const uint16_t *>(a.x.ptr) + it.b * a.x.s0 + it.d * a.x.s1;
+    const uint16_t *dyr = static_cast<const uint16_t *>(a.dy.ptr) + it.b * a.dy.s0 + it.d * a.dy.s1;
+    uint16_t *dxr = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.dx.ptr)) +
+                    it.b * a.dx.s0 + it.d * a.dx.s1;
+    Raw<8> rx[kTcTiles], rd[kTcTiles];
+#pragma unroll
+    for (int c = 0; c < kTcTiles; ++c) {
+        const int64_t t = it.t0 + c * kTcTile + lane * kTcE;
+        if (t < it.t1) {
+            rx[c] = tc_load<NTL>(xr, t, it.t1);
+            rd[c] = tc_load<NTL>(dyr, t, it.t1);
+        } else {
+            rx[c].v = u32x4_t{0u, 0u, 0u, 0u};
+            rd[c].v = u32x4_t{0u, 0u, 0u, 0u};
+        }
+    }
+    float w[W][1], bias[1];
+    load_filter<W, 1, FK>(a.w, a.w_sd, a.w_sk, a.bias, a.b_s, it.d, w, bias);
+    float carry[W - 1];
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) carry[j] = tc_x_ext<W>(xr, a.init, it.b, it.d, it.t0 - (W - 1) + j);
+    float dwacc[W], dbacc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < W; ++k) dwacc[k] = 0.0f;
+    const int64_t fin0 = a.T - (W - 1);  // first position a final-state gradient reaches
+
+    // dx of the lane's tokens of the tile at tt from its g and the W-1 g's
+    // that follow the lane (gn: the next lane's, or `after` for lane 63).
+    auto emit = [&](int64_t tt, const float (&g)[kTcE], const float (&after)[W - 1]) {
+        float ge[kTcE + W - 1], v[kTcE];
+#pragma unroll
+        for (int i = 0; i < kTcE; ++i) ge[i] = g[i];
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) {
+            const float dn = lane_down(g[j]);
+            ge[kTcE + j] = lane == kWaveSize - 1 ? after[j] : dn;
+        }
+        const int64_t t = tt + lane * kTcE;
+#pragma unroll
+        for (int i = 0; i < kTcE; ++i) {
+            float acc = w[0][0] * ge[i + W - 1];
+#pragma unroll
+            for (int j = W - 2; j >= 0; --j) acc = fmaf(w[W - 1 - j][0], ge[i + j], acc);
+            v[i] = acc;
+        }
+        if (a.dfin.ptr && t + kTcE > fin0) {
+#pragma unroll
+            for (int i = 0; i < kTcE; ++i) {
+                const int64_t p = t + i;
+                if (p >= fin0 && p < a.T)
+                    v[i] += bf16_bits_to_f32(static_cast<const uint16_t *>(a.dfin.ptr)
+                                                 [it.b * a.dfin.s0 + it.d * a.dfin.s1 +
+                                                  (p - fin0) * a.dfin.s2]);
+            }
+        }
+        if (t < it.t1) tc_store<true>(dxr, t, it.t1, v);
+    };
+
+    float gprev[kTcE];
+    int64_t tprev = -1;
+#pragma unroll
+    for (int c = 0; c < kTcTiles; ++c) {
+        const int64_t tt = it.t0 + c * kTcTile;
+        if (tt >= it.t1) break;
+        float v[kTcE], dyv[kTcE], xe[W - 1 + kTcE], g[kTcE];
+        unpack<8>(rx[c], v);
+        unpack<8>(rd[c], dyv);
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) {
+            const float up = lane_up(v[kTcE - (W - 1) + j]);
+            xe[j] = lane == 0 ? carry[j] : up;
+        }
+#pragma unroll
+        for (int i = 0; i < kTcE; ++i) xe[W - 1 + i] = v[i];
+#pragma unroll
+        for (int i = 0; i < kTcE; ++i) {
+            float z = bias[0];
+#pragma unroll
+            for (int k = 0; k < W; ++k) z = fmaf(w[k][0], xe[i + k], z);
+            g[i] = dyv[i] * act_slope<SILU>(z);  // zero past the chunk (dy reads 0)
+#pragma unroll
+            for (int k = 0; k < W; ++k) dwacc[k] = fmaf(g[i], xe[i + k], dwacc[k]);
+            if constexpr (BIAS) dbacc += g[i];
+        }
+        if (tprev >= 0) {
+            float after[W - 1];
+#pragma unroll
+            for (int j = 0; j < W - 1; ++j) after[j] = from_lane(g[j], 0);
+            emit(tprev, gprev, after);
+        }
+        // The gradient of the initial state: dx_ext at -(W-1)..-1 from the
+        // row's first g's (lane 0 of the first tile).
+        if (tt == 0 && a.dinit.ptr && lane == 0) {
+#pragma unroll
+            for (int j = 0; j < W - 1; ++j) {
+                const int64_t p = j - (W - 1);
+                float acc = w[0][0] * (p + W - 1 < kTcE ? g[p + W - 1] : 0.0f);
+#pragma unroll
+                for (int m = W - 2; m >= 0; --m)
+                    acc = fmaf(w[W - 1 - m][0], p + m >= 0 ? g[p + m] : 0.0f, acc);
+                if (a.dfin.ptr && p >= fin0)
+                    acc += bf16_bits_to_f32(static_cast<const uint16_t *>(a.dfin.ptr)
+                                                [it.b * a.dfin.s0 + it.d * a.dfin.s1 +
+                                                 (p - fin0) * a.dfin.s2]);
+                const_cast<uint16_t *>(static_cast<const uint16_t *>(a.dinit.ptr))
+                    [it.b * a.dinit.s0 + it.d * a.dinit.s1 + j * a.dinit.s2] = to_bf16_bits(acc);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kTcE; ++i) gprev[i] = g[i];
+        tprev = tt;
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) carry[j] = from_lane(v[kTcE - (W - 1) + j], kWaveSize - 1);
+    }
+    // Right halo: g at t1 .. t1+W-2 (inside the row) for the last tile's
+    // lane 63; lane j computes position t1 + j.  (A chunk that does not end
+    // the row is a whole number of tiles, so t1 - (W-1) >= 0 here.)
+    {
+        float gh = 0.0f;
+        const int64_t p = it.t1 + lane;
+        if (lane < W - 1 && p < a.T) {
+            float z = bias[0];
+#pragma unroll
+            for (int k = 0; k < W; ++k)
+                z = fmaf(w[k][0], bf16_bits_to_f32(xr[p - (W - 1) + k]), z);
+            gh = bf16_bits_to_f32(dyr[p]) * act_slope<SILU>(z);
+        }
+        float after[W - 1];
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) after[j] = from_lane(gh, j);
+        emit(tprev, gprev, after);
+    }
+    // dW/dB of the chunk: a wave sum, then one atomic or one partial per tap.
+#pragma unroll
+    for (int k = 0; k < W; ++k) dwacc[k] = wave_sum(dwacc[k]);
+    if constexpr (BIAS) dbacc = wave_sum(dbacc);
+    if (lane == 0) {
+        if (a.partial) {
+            const int64_t pidx = it.b * a.n_chunk + it.chunk;
+            float *pr = a.partial + (pidx * a.D + it.d) * a.part_stride;
+#pragma unroll
+            for (int k = 0; k < W; ++k) pr[k] = dwacc[k];
+            if (a.part_stride > W) pr[W] = dbacc;
+        } else {
+#pragma unroll
+            for (int k = 0; k < W; ++k) atomicAdd(a.dw + it.d * W + k, dwacc[k]);
+            if constexpr (BIAS) atomicAdd(a.db + it.d, dbacc);
+        }
+    }
+}
+
+template <int W, bool SILU, int FK>
+__global__ __launch_bounds__(256) void k_bwd_tc(BwdArgs a) {
+    TcItem it;
+    if (!tc_item(a, it)) return;
+    if (a.nt_load) bwd_tc_chunk<W, SILU, FK, true>(a, it);
+    else bwd_tc_chunk<W, SILU, FK, false>(a, it);
+}
+
+// ===========================================================================
 // Single-token update (in place on the [B,D,W-1] state)
 //
 // One lane per VEC channels of one batch row.  With VEC = 8 the host has

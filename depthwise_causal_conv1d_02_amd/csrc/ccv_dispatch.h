@@ -50,10 +50,36 @@ hipError_t fwd_vec(const FwdArgs &a, int silu, int rows, int fk, hipStream_t s, 
 
 // The software-pipelined forward is built for 8-channel lanes of dense and
 // packed rows only.
+// Time-lane kernels: dense rows only.
+template <int W>
+hipError_t fwd_tc(const FwdArgs &a, int silu, int fk, hipStream_t s) {
+#define CCV_TC(S, F) \
+    if (!!silu == S && fk == F) return launch(k_fwd_tc<W, S, F>, a.n_block, a, s);
+    CCV_TC(true, kBf16) CCV_TC(true, kBf16Bias) CCV_TC(true, kF32) CCV_TC(true, kF32Bias)
+    CCV_TC(false, kBf16) CCV_TC(false, kBf16Bias) CCV_TC(false, kF32) CCV_TC(false, kF32Bias)
+#undef CCV_TC
+    return hipErrorInvalidValue;
+}
+
+template <int W>
+hipError_t bwd_tc(const BwdArgs &a, int silu, int fk, hipStream_t s) {
+#define CCV_TC(S, F) \
+    if (!!silu == S && fk == F) return launch(k_bwd_tc<W, S, F>, a.n_block, a, s);
+    CCV_TC(true, kBf16) CCV_TC(true, kBf16Bias) CCV_TC(true, kF32) CCV_TC(true, kF32Bias)
+    CCV_TC(false, kBf16) CCV_TC(false, kBf16Bias) CCV_TC(false, kF32) CCV_TC(false, kF32Bias)
+#undef CCV_TC
+    return hipErrorInvalidValue;
+}
+
 template <int W>
 hipError_t fwd_dispatch(const FwdArgs &a, int vec, int silu, int rows, hipStream_t s,
                         int64_t *cap) {
     const int fk = filter_kind(a);
+    if (vec == kVecTime) {
+        if (cap) *cap = 0;
+        if (s == kQueryStream) return hipSuccess;
+        return rows == kRowsDense ? fwd_tc<W>(a, silu, fk, s) : hipErrorInvalidValue;
+    }
     if (vec == 8 && a.pipe && rows != kRowsSeq)
         return fwd_vec<W, 8, true>(a, silu, rows, fk, s, cap);
     if (vec == 8) return fwd_vec<W, 8, false>(a, silu, rows, fk, s, cap);
@@ -88,6 +114,11 @@ template <int W>
 hipError_t bwd_dispatch(const BwdArgs &a, int vec, int silu, int rows, hipStream_t s,
                         int64_t *cap) {
     const int fk = filter_kind(a);
+    if (vec == kVecTime) {
+        if (cap) *cap = 0;
+        if (s == kQueryStream) return hipSuccess;
+        return rows == kRowsDense ? bwd_tc<W>(a, silu, fk, s) : hipErrorInvalidValue;
+    }
     if (vec == 4) return bwd_vec<W, 4>(a, silu, rows, fk, s, cap);
     if (vec == 1) return bwd_vec<W, 1>(a, silu, rows, fk, s, cap);
     return hipErrorInvalidValue;

@@ -27,6 +27,16 @@ constexpr int kFwdWavesC = kWavesPerBlock / kFwdWavesT;
 #define CCV_TILE_ORDER 1
 #endif
 constexpr int kLdsCuMax = 4096;    // cu_seqlens entries staged in LDS (16 KB)
+// Time-lane kernels (unit stride along T): tokens per lane, per wave step
+// (a tile), and tiles per wave chunk.
+constexpr int kTcE = 8;
+constexpr int kTcTile = kWaveSize * kTcE;
+#ifndef CCV_TC_TILES
+#define CCV_TC_TILES 4
+#endif
+constexpr int kTcTiles = CCV_TC_TILES;
+// `vec` value that selects the time-lane kernels.
+constexpr int kVecTime = 0;
 
 // One BF16 activation-like tensor [B,D,T] (or [R,D,W-1] for states) in
 // element strides.  ptr == nullptr means absent.

@@ -588,3 +588,68 @@ def test_seq_idx_autograd_and_declines():
                           initial_states=g["initial_states"])
     with pytest.raises(NotImplementedError):
         ops.causal_conv1d(g["x"], g["weight"], g["bias"], seq_idx=gseq, return_final_states=True)
+
+
+# ---- time-contiguous rows (time lanes) ----------------------------------------
+
+def padded_tc(t, pad_to=8):
+    """A [B,D,T] copy whose rows start on 16-byte boundaries (row stride
+    rounded up to a multiple of 8 elements), on the device."""
+    B, D, T = t.shape
+    Tp = (T + pad_to - 1) // pad_to * pad_to + pad_to
+    st = torch.zeros(B, D, Tp, dtype=t.dtype, device=DEV)
+    view = st[:, :, :T]
+    view.copy_(t.to(DEV))
+    return view
+
+
+TC_CASES = [
+    # W, B, D, T, bias, init, dfinal, act, weight dtype, deterministic, padded rows
+    (4, 2, 64, 4616, True, True, True, "silu", BF16, False, False),   # 3 chunks, last partial
+    (4, 3, 40, 2048, True, False, False, "silu", BF16, True, False),  # exactly one chunk
+    (4, 2, 24, 512, False, True, True, None, BF16, False, False),     # one tile
+    (4, 1, 16, 8, True, True, True, "silu", BF16, False, False),      # one lane
+    (4, 2, 16, 77, True, True, True, "silu", BF16, False, True),      # partial lanes
+    (4, 2, 16, 2, True, True, True, "silu", BF16, False, True),       # T < W-1
+    (3, 2, 32, 2600, True, True, True, "silu", BF16, True, False),
+    (2, 2, 32, 1000, False, True, True, "silu", F32, False, True),
+    (4, 2, 32, 2056, True, True, False, "silu", F32, True, False),    # FP32 filter + bias
+]
+
+
+@pytest.mark.parametrize("case", TC_CASES, ids=lambda c: "W%d-B%d-D%d-T%d-%s%s%s" % (
+    c[0], c[1], c[2], c[3], "f32" if c[8] == F32 else "bf16", "-det" if c[9] else "",
+    "-padded" if c[10] else ""))
+def test_time_lanes_parity(case):
+    """Unit-stride time rows go to the time-lane kernels: forward (with the
+    final state), backward (dx, dinit with dfinal, dW/dB atomics or
+    deterministic partials) against the oracle, inside guard bands."""
+    W, B, D, T, bias, init, dfinal, act, wdt, det, padded = case
+    print("time-lane case", case, flush=True)
+    inp, g = inputs(1700 + W + D + T, B, D, T, "tc", bias, init, wdt, dfinal, W=W)
+    if padded:
+        g["x"], g["dy"] = padded_tc(inp["x"]), padded_tc(inp["dy"])
+    opts = (OPT_F32 if (bias and wdt == F32) else 0) | (OPT_DETDB if (bias and det) else 0)
+    y, fin = run_fwd(g, "tc", act, True, options=opts)
+    check_fwd(inp, y, fin, act)
+    dx, dw, db, dinit = run_bwd(g, "tc", act, det, options=opts)
+    check_bwd(inp, dx, dw, db, dinit, act)
+    if det:
+        _, dw2, db2, _ = run_bwd(g, "tc", act, det, options=opts)
+        assert torch.equal(dw2.view(torch.int32), dw.view(torch.int32))
+        if bias:
+            assert torch.equal(db2.view(torch.int32), db.view(torch.int32))
+
+
+def test_time_lanes_match_channel_lanes():
+    """The same data in both layouts: time lanes and channel lanes agree to
+    the rounding of their (identical) per-token arithmetic."""
+    B, D, T = 2, 512, 3000
+    inp, g = inputs(1800, B, D, T, "tc", True, True, BF16, True)
+    y_tc, fin_tc = ops.fwd(g["x"], g["weight"], g["bias"], None, g["initial_states"], "silu",
+                           return_final_states=True)
+    x_cl = g["x"].transpose(1, 2).contiguous().transpose(1, 2)
+    y_cl, fin_cl = ops.fwd(x_cl, g["weight"], g["bias"], None, g["initial_states"], "silu",
+                           return_final_states=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y_tc, y_cl) and torch.equal(fin_tc, fin_cl)
