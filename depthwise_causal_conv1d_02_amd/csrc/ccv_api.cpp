@@ -550,9 +550,13 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
 int ccv_update(const ccv_tensor *x, const ccv_tensor *conv_state, const ccv_tensor *weight,
                const ccv_tensor *bias, const ccv_tensor *y, int activation, uint32_t options,
                hipStream_t stream) {
-    if (!present(x) || !well_formed(x, 2) || x->dtype != CCV_DTYPE_BF16) return CCV_ERR_INVALID_ARG;
-    const int64_t B = x->shape[0], D = x->shape[1];
-    if (B < 1 || D < 1) return CCV_ERR_INVALID_ARG;
+    // x and y: [B,D] (one token) or [B,D,L] (L tokens in order).
+    if (!present(x) || (x->ndim != 2 && x->ndim != 3) || !well_formed(x, x->ndim) ||
+        x->dtype != CCV_DTYPE_BF16)
+        return CCV_ERR_INVALID_ARG;
+    const int nd = x->ndim;
+    const int64_t B = x->shape[0], D = x->shape[1], L = nd == 3 ? x->shape[2] : 1;
+    if (B < 1 || D < 1 || L < 1) return CCV_ERR_INVALID_ARG;
     if (!present(weight) || !well_formed(weight, 2) || weight->shape[0] != D ||
         weight->shape[1] < 1 ||
         (weight->dtype != CCV_DTYPE_BF16 && weight->dtype != CCV_DTYPE_F32))
@@ -564,8 +568,8 @@ int ccv_update(const ccv_tensor *x, const ccv_tensor *conv_state, const ccv_tens
         conv_state->dtype != CCV_DTYPE_BF16 ||
         !shape_is(conv_state, B, D, weight->shape[1] - 1) || !injective(conv_state))
         return CCV_ERR_INVALID_ARG;
-    if (!present(y) || !well_formed(y, 2) || y->dtype != CCV_DTYPE_BF16 || !shape_is(y, B, D) ||
-        !injective(y))
+    if (!present(y) || !well_formed(y, nd) || y->dtype != CCV_DTYPE_BF16 ||
+        !shape_is(y, B, D, nd == 3 ? L : -1) || !injective(y))
         return CCV_ERR_INVALID_ARG;
     const int64_t W = weight->shape[1];
     if (W < ccv::kMinWidth || W > ccv::kMaxWidth) return CCV_ERR_UNSUPPORTED;
@@ -579,11 +583,13 @@ int ccv_update(const ccv_tensor *x, const ccv_tensor *conv_state, const ccv_tens
 
     // 8-channel lanes need unit channel strides, a contiguous state, a
     // contiguous filter and bias, and 16-byte aligned rows everywhere.
+    // With several tokens, their strides keep the rows aligned too.
     const bool vec = CCV_UPD_VEC == 8 && D % 8 == 0 && x->stride[1] == 1 && y->stride[1] == 1 &&
                      conv_state->stride[2] == 1 && conv_state->stride[1] == W - 1 &&
                      aligned16(x->data) && aligned16(y->data) && aligned16(conv_state->data) &&
                      (B == 1 || (x->stride[0] % 8 == 0 && y->stride[0] % 8 == 0 &&
                                  conv_state->stride[0] % 8 == 0)) &&
+                     (L == 1 || (x->stride[2] % 8 == 0 && y->stride[2] % 8 == 0)) &&
                      filter_vec(weight) &&
                      (!present(bias) || (bias->stride[0] == 1 && aligned16(bias->data)));
     ccv::UpdArgs a;
@@ -606,6 +612,9 @@ int ccv_update(const ccv_tensor *x, const ccv_tensor *conv_state, const ccv_tens
     a.y = y->data;
     a.y_sb = y->stride[0];
     a.y_sd = y->stride[1];
+    a.L = L;
+    a.x_st = nd == 3 ? x->stride[2] : 0;
+    a.y_st = nd == 3 ? y->stride[2] : 0;
     a.B = B;
     a.D = D;
     a.n_lane_per_row = vec ? D / 8 : D;

@@ -1471,7 +1471,8 @@ void k_update_vec(UpdArgs a) {
     }
 }
 
-// Any strides: one lane per channel of one row.
+// Any strides: one lane per channel of one row; the row's L tokens in
+// order, the state in registers until the end.
 template <int W, bool SILU, bool WF32, bool BIAS>
 __global__ __launch_bounds__(256) void k_update_any(UpdArgs a) {
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -1479,25 +1480,90 @@ __global__ __launch_bounds__(256) void k_update_any(UpdArgs a) {
     if (b >= a.B) return;
     const int64_t c = gid % a.n_lane_per_row;
     const uint16_t *xp = static_cast<const uint16_t *>(a.x) + b * a.x_sb + c * a.x_sd;
+    uint16_t *yp = static_cast<uint16_t *>(a.y) + b * a.y_sb + c * a.y_sd;
     uint16_t *sp = static_cast<uint16_t *>(a.state) + b * a.s_sb + c * a.s_sd;
     uint16_t st[W - 1];
 #pragma unroll
     for (int j = 0; j < W - 1; ++j) st[j] = sp[j * a.s_sj];
-    const uint16_t xr = *xp;
-    float z = 0.0f;
-    if constexpr (BIAS)
-        z = WF32 ? static_cast<const float *>(a.bias)[c * a.b_s]
-                 : bf16_bits_to_f32(static_cast<const uint16_t *>(a.bias)[c * a.b_s]);
+    float w[W], bias = 0.0f;
 #pragma unroll
     for (int k = 0; k < W; ++k) {
         const int64_t off = c * a.w_sd + k * a.w_sk;
-        const float wk = WF32 ? static_cast<const float *>(a.w)[off]
-                              : bf16_bits_to_f32(static_cast<const uint16_t *>(a.w)[off]);
-        z = fmaf(wk, bf16_bits_to_f32(k < W - 1 ? st[k] : xr), z);
+        w[k] = WF32 ? static_cast<const float *>(a.w)[off]
+                    : bf16_bits_to_f32(static_cast<const uint16_t *>(a.w)[off]);
     }
-    static_cast<uint16_t *>(a.y)[b * a.y_sb + c * a.y_sd] = to_bf16_bits(act<SILU>(z));
+    if constexpr (BIAS)
+        bias = WF32 ? static_cast<const float *>(a.bias)[c * a.b_s]
+                    : bf16_bits_to_f32(static_cast<const uint16_t *>(a.bias)[c * a.b_s]);
+    for (int64_t l = 0; l < a.L; ++l) {
+        const uint16_t xr = xp[l * a.x_st];
+        float z = bias;
 #pragma unroll
-    for (int j = 0; j < W - 1; ++j) sp[j * a.s_sj] = j < W - 2 ? st[j + 1] : xr;
+        for (int k = 0; k < W; ++k) z = fmaf(w[k], bf16_bits_to_f32(k < W - 1 ? st[k] : xr), z);
+        yp[l * a.y_st] = to_bf16_bits(act<SILU>(z));
+#pragma unroll
+        for (int j = 0; j < W - 2; ++j) st[j] = st[j + 1];
+        st[W - 2] = xr;
+    }
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) sp[j * a.s_sj] = st[j];
+}
+
+// Several tokens per row (x [B,D,L], L > 1) on 8-channel lanes: the state
+// window stays in registers (raw bits) across the row's tokens, whose loads
+// go out in batches of 4; the state is written once at the end.
+template <int W, bool SILU, bool WF32, bool BIAS>
+__global__ __launch_bounds__(256) void k_update_tokens(UpdArgs a) {
+    constexpr int VEC = 8, U = 4;
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t b = gid / a.n_lane_per_row;
+    if (b >= a.B) return;
+    const int64_t c0 = (gid % a.n_lane_per_row) * VEC;
+    const uint16_t *xb = static_cast<const uint16_t *>(a.x) + b * a.x_sb + c0;
+    uint16_t *yb = static_cast<uint16_t *>(a.y) + b * a.y_sb + c0;
+    uint16_t *sb = static_cast<uint16_t *>(a.state) + b * a.s_sb + c0 * (W - 1);
+    float w[W][VEC], bias[VEC];
+    load_filter<W, VEC, WF32 ? (BIAS ? kF32Bias : kF32) : (BIAS ? kBf16Bias : kBf16)>(
+        a.w, a.w_sd, a.w_sk, a.bias, a.b_s, c0, w, bias);
+    uint16_t st[VEC][W - 1];
+#pragma unroll
+    for (int c = 0; c < VEC; ++c)
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) st[c][j] = sb[c * (W - 1) + j];
+    auto step = [&](int64_t l, const Raw<VEC> &raw) {
+        uint16_t xr[VEC];
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) xr[c] = static_cast<uint16_t>(raw.v[c / 2] >> (16 * (c % 2)));
+        float out[VEC];
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) {
+            float z = bias[c];
+#pragma unroll
+            for (int k = 0; k < W - 1; ++k) z = fmaf(w[k][c], bf16_bits_to_f32(st[c][k]), z);
+            z = fmaf(w[W - 1][c], bf16_bits_to_f32(xr[c]), z);
+            out[c] = act<SILU>(z);
+        }
+        store_vec<VEC>(yb + l * a.y_st, 1, out);
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) {
+#pragma unroll
+            for (int j = 0; j < W - 2; ++j) st[c][j] = st[c][j + 1];
+            st[c][W - 2] = xr[c];
+        }
+    };
+    int64_t l = 0;
+    for (; l + U <= a.L; l += U) {
+        Raw<VEC> raw[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) raw[u] = load_raw<VEC>(xb + (l + u) * a.x_st, 1);
+#pragma unroll
+        for (int u = 0; u < U; ++u) step(l + u, raw[u]);
+    }
+    for (; l < a.L; ++l) step(l, load_raw<VEC>(xb + l * a.x_st, 1));
+#pragma unroll
+    for (int c = 0; c < VEC; ++c)
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) sb[c * (W - 1) + j] = st[c][j];
 }
 
 // ===========================================================================

@@ -127,7 +127,15 @@ hipError_t bwd_dispatch(const BwdArgs &a, int vec, int silu, int rows, hipStream
 template <int W>
 hipError_t update_dispatch(const UpdArgs &a, int vec, int silu, hipStream_t s) {
     const bool wf32 = a.w_f32 != 0, bias = a.bias != nullptr;
-    if (vec == 8) {
+    if (vec == 8 && a.L > 1) {
+        const int64_t blocks = (a.B * a.n_lane_per_row + 255) / 256;
+#define CCV_UPD(S, F, B) \
+        if (!!silu == S && wf32 == F && bias == B) return launch(k_update_tokens<W, S, F, B>, blocks, a, s);
+        CCV_UPD(true, false, true) CCV_UPD(true, false, false) CCV_UPD(true, true, false)
+        CCV_UPD(true, true, true) CCV_UPD(false, false, true) CCV_UPD(false, false, false)
+        CCV_UPD(false, true, false) CCV_UPD(false, true, true)
+#undef CCV_UPD
+    } else if (vec == 8) {
         const int64_t blocks = (a.n_row_groups * a.n_lane_per_row + 255) / 256;
 #define CCV_UPD(S, F, B)                                                                      \
         if (!!silu == S && wf32 == F && bias == B)                                            \

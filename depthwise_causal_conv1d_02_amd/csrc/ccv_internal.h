@@ -94,7 +94,7 @@ struct BwdArgs {
 
 struct UpdArgs {
     int width;
-    const void *x;        // [B,D]
+    const void *x;        // [B,D] or [B,D,L]
     int64_t x_sb, x_sd;
     void *state;          // [B,D,W-1]
     int64_t s_sb, s_sd, s_sj;
@@ -103,8 +103,10 @@ struct UpdArgs {
     int w_f32, w_vec;
     const void *bias;
     int64_t b_s;
-    void *y;              // [B,D]
+    void *y;              // [B,D] or [B,D,L]
     int64_t y_sb, y_sd;
+    int64_t L;            // tokens per row (1: x and y are [B,D])
+    int64_t x_st, y_st;   // token strides when L > 1
     int64_t B, D;
     int64_t n_lane_per_row;  // D / VEC
     int64_t n_row_groups;    // ceil(B / rows per lane), 8-channel lanes

@@ -195,7 +195,8 @@ def bwd(x, weight, dy, bias=None, cu_seqlens=None, initial_states=None, dfinal_s
 
 
 def update(x, conv_state, weight, bias=None, activation="silu", y=None, options=0):
-    """One ccv_update call (conv_state is mutated in place).  Returns y."""
+    """One ccv_update call (conv_state is mutated in place).  x is [B,D] (one
+    token) or [B,D,L] (L tokens in order).  Returns y (x's shape)."""
     if y is None:
         y = torch.empty_like(x)
     rc = _abi.lib().ccv_update(_ref(_desc(x)), _ref(_desc(conv_state)), _ref(_desc(weight)),
@@ -283,7 +284,8 @@ def causal_conv1d(x, weight, bias=None, seq_idx=None, cu_seqlens=None, initial_s
 
 def causal_conv1d_update(x, conv_state, weight, bias=None, activation=None,
                          fp32_weight_bias=False):
-    """One decode token: x [B,D]; conv_state [B,D,W-1] is mutated in place
-    (it becomes the last W-1 tokens).  Returns y [B,D]."""
+    """Decode: x [B,D] (one token) or [B,D,L] (L tokens in order);
+    conv_state [B,D,W-1] is mutated in place (it becomes the last W-1
+    tokens).  Returns y with x's shape."""
     return update(x, conv_state, weight, bias, activation,
                   options=_options(fp32_weight_bias))

@@ -200,20 +200,23 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
             uint32_t *err_flag, hipStream_t stream);
 
 /*
- * ccv_update — single-token decode step (cuDNN FE "Causal Conv1d": the
- * returned width-four final_states feed causal_conv1d_update, which mutates
- * the state in place with no layout conversion).
+ * ccv_update — decode step (cuDNN FE "Causal Conv1d": the returned
+ * width-four final_states feed causal_conv1d_update, which mutates the state
+ * in place with no layout conversion).  One token, or L tokens in order
+ * (exactly L single-token steps).
  *
- *   x           [B,D]      BF16, the new token, read.
+ *   x           [B,D]      BF16, the new token, read; or [B,D,L], L >= 1
+ *                          tokens (oldest first), read.
  *   conv_state  [B,D,W-1]  BF16, read and written in place: the state
  *                          (s_0..s_{W-2}, oldest first) becomes
- *                          (s_1..s_{W-2}, x).
+ *                          (s_1..s_{W-2}, x): the last W-1 entries of
+ *                          (state, tokens).
  *   weight      [D,W]      BF16 or FP32; W in 2..4.
  *   bias        [D]        optional; as in ccv_fwd (FP32 with an FP32
  *                          weight under CCV_OPT_F32_FILTER_BIAS).
- *   y           [B,D]      BF16, written: act(bias + sum_k w_k v_k) over
- *                          v = (s_0..s_{W-2}, x).  Must not overlap any
- *                          other argument.
+ *   y           x's shape, BF16, written: act(bias + sum_k w_k v_k) over
+ *                          v = (s_0..s_{W-2}, x) for each token in turn.
+ *                          Must not overlap any other argument.
  */
 int ccv_update(const ccv_tensor *x, const ccv_tensor *conv_state, const ccv_tensor *weight,
                const ccv_tensor *bias, const ccv_tensor *y, int activation, uint32_t options,

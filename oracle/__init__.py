@@ -236,6 +236,17 @@ def update(x, state, w, bias=None, activation="silu"):
     return y, st
 
 
+def update_tokens(x, state, w, bias=None, activation="silu"):
+    """L decode tokens x [B,D,L] in order: L single-token steps (the
+    definition of a multi-token update).  Returns (y [B,D,L], new state)."""
+    x = _f64(x)
+    st = np.array(state, dtype=np.float64, copy=True, order="C")
+    y = np.empty(x.shape, np.float64)
+    for l in range(x.shape[2]):
+        y[:, :, l], st = update(x[:, :, l], st, w, bias, activation)
+    return y, st
+
+
 def validate_cu_seqlens(cu_seqlens, total):
     """Bit mask of the four malformed-metadata conditions (uint32)."""
     cu = _i32(cu_seqlens)

@@ -251,6 +251,12 @@ def test_update_rejects(L):
     assert up(y=T([4, 64], data=st.data + 2)) == ALIAS
     assert up(st=T([4, 64, 3], data=w.data)) == ALIAS
     assert up(y=T([4, 64], stride=[0, 1])) == INVALID
+    # several tokens: x and y [B,D,L] alike, L >= 1
+    x3 = T([4, 64, 5])
+    assert up(x=x3, y=T([4, 64])) == INVALID
+    assert up(x=x3, y=T([4, 64, 4])) == INVALID
+    assert up(x=T([4, 64, 0]), y=T([4, 64, 0])) == INVALID
+    assert up(x=x3, y=T([4, 64, 5], data=x3.data + 16)) == ALIAS
 
 
 def test_validate_rejects(L):

@@ -653,3 +653,44 @@ def test_time_lanes_match_channel_lanes():
                            return_final_states=True)
     torch.cuda.synchronize()
     assert torch.equal(y_tc, y_cl) and torch.equal(fin_tc, fin_cl)
+
+
+# ---- multi-token update ---------------------------------------------------------
+
+MULTI_CASES = [
+    # B, D, L, W, bias, weight dtype, layout of x/y
+    (4, 512, 5, 4, True, BF16, "cl"),
+    (3, 1024, 16, 4, False, BF16, "cl"),
+    (2, 64, 2, 3, True, BF16, "cl"),
+    (2, 64, 9, 2, True, F32, "cl"),
+    (3, 40, 6, 4, True, BF16, "cl"),       # D % 8 != 0: one-channel lanes
+    (2, 64, 7, 4, True, BF16, "tc"),       # [B,D,L] contiguous: one-channel lanes
+    (5, 256, 1, 4, True, BF16, "cl"),      # L = 1 through the [B,D,L] form
+]
+
+
+@pytest.mark.parametrize("B,D,L,W,bias,wdt,layout", MULTI_CASES)
+def test_update_several_tokens(B, D, L, W, bias, wdt, layout):
+    """L tokens in one call == L single-token steps of the oracle; then a
+    single-token call continues from the state it left."""
+    print("multi-token update case", B, D, L, W, bias, wdt, layout, flush=True)
+    gen = torch.Generator().manual_seed(1900 + D + L)
+    state = synth.state_tensor(gen, B, D, W)
+    w = synth.weight_tensor(gen, D, W, dtype=wdt)
+    b = synth.bias_tensor(gen, D, wdt) if bias else None
+    x = synth.activation_tensor(gen, B, D, L, layout)
+    opts = OPT_F32 if (bias and wdt == F32) else 0
+    g_state = dev(state)
+    y = guarded_act(B, D, L, layout, DEV)
+    ops.update(dev(x), g_state, dev(w), dev(b), "silu", y=y.view, options=opts)
+    torch.cuda.synchronize()
+    oy, ost = oracle.update_tokens(f64(x), f64(state), f64(w), f64(b), "silu")
+    check_bf16("y", y.view, oy)
+    assert y.intact()
+    check_exact_bf16("conv_state", g_state, ost)
+    xt = synth.activation_tensor(gen, B, D, 1, "tc")[:, :, 0].contiguous()
+    yt = ops.update(dev(xt), g_state, dev(w), dev(b), "silu", options=opts)
+    torch.cuda.synchronize()
+    oyt, ost = oracle.update(f64(xt), ost, f64(w), f64(b), "silu")
+    check_bf16("next token y", yt, oyt)
+    check_exact_bf16("conv_state after", g_state, ost)

@@ -282,6 +282,23 @@ def test_O4_update_steps_reproduce_forward(T0, bias):
     assert np.array_equal(state, fin_full)
 
 
+@pytest.mark.parametrize("W", [2, 3, 4])
+@pytest.mark.parametrize("L", [1, 2, 7])
+def test_O4_multi_token_update_is_forward_from_the_state(W, L):
+    """L tokens at once == the forward over those tokens with the state as
+    its initial state (outputs and final state, exactly), and == the
+    library conv1d of the state followed by the tokens."""
+    p = _rand_problem(14, 3, 4, L, W=W, bias=True, init=True)
+    y, st = oracle.update_tokens(p["x"], p["init"], p["w"], p["bias"], "silu")
+    yf, ff = oracle.fwd(p["x"], p["w"], p["bias"], None, p["init"], "silu")
+    assert np.array_equal(y, yf) and np.array_equal(st, ff)
+    full = torch.tensor(np.concatenate([p["init"], p["x"]], axis=2))
+    ref = F.silu(F.conv1d(F.pad(full, (W - 1, 0)), torch.tensor(p["w"])[:, None, :],
+                          torch.tensor(p["bias"]), groups=4))[:, :, W - 1:]
+    np.testing.assert_allclose(y, ref.numpy(), rtol=1e-13, atol=1e-14)
+    np.testing.assert_array_equal(st, np.concatenate([p["init"], p["x"]], axis=2)[:, :, -(W - 1):])
+
+
 # ---------------------------------------------------------------------------
 # O5 central finite differences on tiny inputs
 # ---------------------------------------------------------------------------
