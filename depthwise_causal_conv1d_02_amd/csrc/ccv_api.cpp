@@ -30,6 +30,15 @@
 #ifndef CCV_FWD_ROUNDS
 #define CCV_FWD_ROUNDS 0        // 0: size the grid by target waves
 #endif
+#ifndef CCV_FWD_PACKED_MIN_CHUNK
+#define CCV_FWD_PACKED_MIN_CHUNK CCV_FWD_MIN_CHUNK
+#endif
+#ifndef CCV_FWD_PACKED_TARGET_WAVES
+#define CCV_FWD_PACKED_TARGET_WAVES CCV_FWD_TARGET_WAVES
+#endif
+#ifndef CCV_BWD_PACKED_ROUNDS
+#define CCV_BWD_PACKED_ROUNDS CCV_BWD_ROUNDS
+#endif
 #ifndef CCV_BWD_ROUNDS
 #define CCV_BWD_ROUNDS 1
 #endif
@@ -400,8 +409,11 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
                             : 0;
     const Geometry g = time_lanes ? time_geometry(p)
                                   : geometry(p, vec, ccv::kFwdWavesT, ccv::kFwdWavesC, cap,
-                                             CCV_FWD_ROUNDS, CCV_FWD_TARGET_WAVES,
-                                             CCV_FWD_MIN_CHUNK);
+                                             CCV_FWD_ROUNDS,
+                                             p.packed ? CCV_FWD_PACKED_TARGET_WAVES
+                                                      : CCV_FWD_TARGET_WAVES,
+                                             p.packed ? CCV_FWD_PACKED_MIN_CHUNK
+                                                      : CCV_FWD_MIN_CHUNK);
     a.B = p.B;
     a.D = p.D;
     a.T = p.T;
@@ -518,9 +530,10 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     a.err = p.packed ? err_flag : nullptr;
     set_seq(a, seq_idx, p);
     const int silu = activation == CCV_ACT_SILU;
-    if (!use_partials && CCV_BWD_ROUNDS > 0 && !time_lanes)
+    const int rounds = p.packed ? CCV_BWD_PACKED_ROUNDS : CCV_BWD_ROUNDS;
+    if (!use_partials && rounds > 0 && !time_lanes)
         g = geometry(p, vec, ccv::kWavesPerBlock, 1, ccv::bwd_resident_blocks(a, vec, silu, p.rows()),
-                     CCV_BWD_ROUNDS, CCV_BWD_TARGET_WAVES, CCV_BWD_MIN_CHUNK);
+                     rounds, CCV_BWD_TARGET_WAVES, CCV_BWD_MIN_CHUNK);
     a.B = p.B;
     a.D = p.D;
     a.T = p.T;

@@ -40,6 +40,17 @@ constexpr uint32_t kFirstNonzero = 0x1u, kLastMismatch = 0x2u, kDecreasing = 0x4
 #ifndef CCV_BWD_UNROLL
 #define CCV_BWD_UNROLL 4
 #endif
+// Measured per row mode: packed rows do best with batches of 2 (their
+// pieces restart often), seq_idx rows (not software-pipelined) with 8.
+#ifndef CCV_BWD_UNROLL_PACKED
+#define CCV_BWD_UNROLL_PACKED 2
+#endif
+#ifndef CCV_BWD_UNROLL_SEQ
+#define CCV_BWD_UNROLL_SEQ 8
+#endif
+#ifndef CCV_TC_BWD_WAVES
+#define CCV_TC_BWD_WAVES 8      // time-lane backward: waves per SIMD it must fit
+#endif
 #ifndef CCV_BWD_PIPE
 #define CCV_BWD_PIPE 1
 #endif
@@ -622,11 +633,10 @@ struct BwdLane {
     float dw[W][VEC], db[VEC];
 };
 
-template <int W, int VEC, bool SILU, bool BIAS, bool NTL>
+template <int W, int VEC, bool SILU, bool BIAS, bool NTL, int U>
 __device__ __forceinline__ void bwd_piece(const BwdArgs &a, BwdLane<W, VEC, SILU, BIAS> &L,
                                           int64_t b, int64_t r, int64_t s, int64_t e,
                                           int64_t ta, int64_t tb, int64_t c0) {
-    constexpr int U = CCV_BWD_UNROLL;
     const uint16_t *xb = static_cast<const uint16_t *>(a.x.ptr) + b * a.x.s0 + c0 * a.x.s1;
     const uint16_t *dyb = static_cast<const uint16_t *>(a.dy.ptr) + b * a.dy.s0 + c0 * a.dy.s1;
     uint16_t *dxb = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.dx.ptr)) +
@@ -816,10 +826,9 @@ __device__ __forceinline__ void bwd_piece(const BwdArgs &a, BwdLane<W, VEC, SILU
 // registers, dx[tau-(W-1)] emitted) with the ids of the window's tokens kept
 // beside their values.  x[p] reaches output t only when id[p] == id[t], in
 // the forward (z), in dW, and in dx[p] = sum_k w[k] g[p+W-1-k] [same id].
-template <int W, int VEC, bool SILU, bool BIAS, bool NTL>
+template <int W, int VEC, bool SILU, bool BIAS, bool NTL, int U>
 __device__ __forceinline__ void bwd_seq_piece(const BwdArgs &a, BwdLane<W, VEC, SILU, BIAS> &L,
                                               int64_t b, int64_t ta, int64_t tb, int64_t c0) {
-    constexpr int U = CCV_BWD_UNROLL;
     const uint16_t *xb = static_cast<const uint16_t *>(a.x.ptr) + b * a.x.s0 + c0 * a.x.s1;
     const uint16_t *dyb = static_cast<const uint16_t *>(a.dy.ptr) + b * a.dy.s0 + c0 * a.dy.s1;
     uint16_t *dxb = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.dx.ptr)) +
@@ -967,16 +976,16 @@ __global__ __launch_bounds__(256) CCV_BWD_ATTR void k_bwd_chan(BwdArgs a) {
         auto run = [&](auto ntl) {
             constexpr bool NTL = decltype(ntl)::value;
             if constexpr (ROWS == kRowsSeq) {
-                bwd_seq_piece<W, VEC, SILU, BIAS, NTL>(a, L, b, t0, t1, c0);
+                bwd_seq_piece<W, VEC, SILU, BIAS, NTL, CCV_BWD_UNROLL_SEQ>(a, L, b, t0, t1, c0);
             } else if constexpr (!PACKED) {
-                bwd_piece<W, VEC, SILU, BIAS, NTL>(a, L, b, b, 0, a.T, t0, t1, c0);
+                bwd_piece<W, VEC, SILU, BIAS, NTL, CCV_BWD_UNROLL>(a, L, b, b, 0, a.T, t0, t1, c0);
             } else {
                 const int32_t *cu = a.cu_in_lds ? s_cu : a.cu;
                 for (int64_t i = find_row(cu, a.n_seq, t0); i < a.n_seq; ++i) {
                     const int64_t s = cu[i], e = cu[i + 1];
                     if (s >= t1) break;
-                    bwd_piece<W, VEC, SILU, BIAS, NTL>(a, L, 0, i, s, e, s > t0 ? s : t0,
-                                                    e < t1 ? e : t1, c0);
+                    bwd_piece<W, VEC, SILU, BIAS, NTL, CCV_BWD_UNROLL_PACKED>(
+                        a, L, 0, i, s, e, s > t0 ? s : t0, e < t1 ? e : t1, c0);
                 }
             }
         };
@@ -1337,7 +1346,8 @@ __device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it)
 }
 
 template <int W, bool SILU, int FK>
-__global__ __launch_bounds__(256) void k_bwd_tc(BwdArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CCV_TC_BWD_WAVES)))
+void k_bwd_tc(BwdArgs a) {
     TcItem it;
     if (!tc_item(a, it)) return;
     if (a.nt_load) bwd_tc_chunk<W, SILU, FK, true>(a, it);
