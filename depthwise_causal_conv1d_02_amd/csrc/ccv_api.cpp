@@ -45,6 +45,14 @@
 #ifndef CCV_FWD_VEC
 #define CCV_FWD_VEC 8
 #endif
+// Small dense forwards (whose 8-channel geometry would already sit at the
+// minimum chunk) measured faster on 4-channel lanes with 32-step chunks.
+#ifndef CCV_FWD_SMALL_VEC
+#define CCV_FWD_SMALL_VEC 4
+#endif
+#ifndef CCV_FWD_SMALL_CHUNK
+#define CCV_FWD_SMALL_CHUNK 32
+#endif
 // Bulk loads use the non-temporal policy once an op streams at least this
 // many input bytes (twice the 256 MB memory-side cache).
 #ifndef CCV_NT_LOAD_MIN_BYTES
@@ -383,7 +391,13 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     if (any_alias(outs, 3, ins, 6)) return CCV_ERR_ALIAS;
 
     const bool time_lanes = !p.packed && !p.seq && time_lanes_ok(x, y, nullptr);
-    const int vec = time_lanes ? ccv::kVecTime : pick_vec(CCV_FWD_VEC, weight, bias, x, y, nullptr);
+    const bool pipe = p.B * p.D * p.T * 2 >= CCV_FWD_PIPE_MIN_BYTES;
+    const int64_t groups8 = (p.D + ccv::kWaveSize * 8 - 1) / (ccv::kWaveSize * 8);
+    const bool small_dense = !p.packed && !p.seq && !pipe &&
+                             p.B * groups8 * p.T <= int64_t(CCV_FWD_TARGET_WAVES) * CCV_FWD_MIN_CHUNK;
+    const int vec = time_lanes ? ccv::kVecTime
+                               : pick_vec(small_dense ? CCV_FWD_SMALL_VEC : CCV_FWD_VEC, weight,
+                                          bias, x, y, nullptr);
     ccv::FwdArgs a;
     memset(&a, 0, sizeof(a));
     a.width = static_cast<int>(p.W);
@@ -402,7 +416,7 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     a.n_seq = p.N;
     a.err = p.packed ? err_flag : nullptr;
     set_seq(a, seq_idx, p);
-    a.pipe = p.B * p.D * p.T * 2 >= CCV_FWD_PIPE_MIN_BYTES;
+    a.pipe = pipe;
     const int silu = activation == CCV_ACT_SILU;
     const int64_t cap = CCV_FWD_ROUNDS > 0 && !time_lanes
                             ? ccv::fwd_resident_blocks(a, vec, silu, p.rows())
@@ -413,7 +427,9 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
                                              p.packed ? CCV_FWD_PACKED_TARGET_WAVES
                                                       : CCV_FWD_TARGET_WAVES,
                                              p.packed ? CCV_FWD_PACKED_MIN_CHUNK
-                                                      : CCV_FWD_MIN_CHUNK);
+                                             : small_dense && vec == CCV_FWD_SMALL_VEC
+                                                 ? CCV_FWD_SMALL_CHUNK
+                                                 : CCV_FWD_MIN_CHUNK);
     a.B = p.B;
     a.D = p.D;
     a.T = p.T;
