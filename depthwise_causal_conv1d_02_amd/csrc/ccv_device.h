@@ -931,7 +931,10 @@ __device__ __forceinline__ void bwd_seq_piece(const BwdArgs &a, BwdLane<W, VEC, 
     for (; tau < end; ++tau) generic(tau);
 }
 
-template <int W, int VEC, bool SILU, int ROWS, int FK>
+// WU: the wave index through readfirstlane (addresses in scalars: fewer
+// registers, so 3 waves per SIMD instead of 2).  Measured faster for inputs
+// that stay in cache-sized streams, slower for the non-temporal ones.
+template <int W, int VEC, bool SILU, int ROWS, int FK, bool WU = false>
 __global__ __launch_bounds__(256) CCV_BWD_ATTR void k_bwd_chan(BwdArgs a) {
     constexpr bool PACKED = ROWS == kRowsPacked;
     constexpr bool BIAS = fk_bias(FK);
@@ -950,7 +953,7 @@ __global__ __launch_bounds__(256) CCV_BWD_ATTR void k_bwd_chan(BwdArgs a) {
     // compiler so, which keeps the time bounds and row offsets in scalars.
     // Measured: it frees the registers the seq_idx walk needs, but slows
     // the dense and packed streams on large inputs, so only seq_idx uses it.
-    const int wave = (ROWS == kRowsSeq && CCV_WAVE_UNIFORM)
+    const int wave = ((ROWS == kRowsSeq || WU) && CCV_WAVE_UNIFORM)
                          ? __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize)
                          : static_cast<int>(threadIdx.x / kWaveSize);
     const int lane = threadIdx.x % kWaveSize;
