@@ -35,6 +35,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+MALL_BYTES = 256 << 20      # MI355X memory-side (Infinity) cache
+DECODE_STATES = 16          # decode: states rotated over, so each launch finds its state in HBM
 SPACER_CYCLES = 200000      # GPU spin before each timed op in the per-op pass
 METRIC = "achieved HBM GB/s (% of MI355X peak) for fwd, bwd and update at 1 GPU"
 
@@ -125,7 +127,8 @@ class Workload:
             self.bytes = {"update": update_bytes(B, D, 2, True)}
             self.counts = {"update": n_tok}
             self.desc = ("decode update: B=%d D=%d, %d single-token steps per step, bf16 "
-                         "weight+bias, SiLU, state mutated in place" % (B, D, n_tok))
+                         "weight+bias, SiLU, state mutated in place (rotating over %d states)"
+                         % (B, D, n_tok, DECODE_STATES))
             return
         x = w["x"]
         B, D, T = x.shape
@@ -146,6 +149,23 @@ class Workload:
         self.desc = synth.WORKLOADS[idx]
         if name.endswith("_tc"):
             self.desc = self.desc.replace("channel-last", "[B,D,T] time-contiguous")
+
+    def step_bytes(self):
+        return sum(self.bytes[k] * self.counts[k] for k in self.bytes)
+
+    def clone(self):
+        """The same workload on fresh device copies of its tensors (strides
+        kept), for timing with operands that are not in any cache."""
+        import copy
+        c = copy.copy(self)
+        c.g = {k: (v.clone() if getattr(v, "is_cuda", False) else v) for k, v in self.g.items()}
+        return c
+
+
+def rotation_count(wl):
+    """Operand copies to rotate over: between two uses of one copy, at least
+    three times the memory-side cache of other traffic."""
+    return max(2, min(16, -(-4 * MALL_BYTES // max(1, wl.step_bytes()))))
 
 
 class Step:
@@ -169,13 +189,14 @@ def make_step(wl, torch):
 
     g, dev = wl.g, wl.dev
     if wl.kind == "decode":
-        state = g["conv_state"].clone()
+        states = [g["conv_state"].clone() for _ in range(DECODE_STATES)]
         xs = g["x_steps"]
         ys = torch.empty_like(xs)
-        # one step decodes the seeded tokens in order, each in place on the
-        # same state
-        calls = [("update", (lambda s=s: ops.update(xs[s], state, g["weight"], g["bias"],
-                                                     g["activation"], y=ys[s])))
+        # one step decodes the seeded tokens in order, each in place on a
+        # state; the states rotate so that no launch finds its state cached
+        calls = [("update", (lambda s=s: ops.update(xs[s], states[s % DECODE_STATES],
+                                                     g["weight"], g["bias"], g["activation"],
+                                                     y=ys[s])))
                  for s in range(xs.shape[0])]
         return Step(calls, {"y": ys})
 
@@ -246,25 +267,49 @@ class Events:
         return {k: sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in self.rec.items()}
 
 
+def _graph_launch_ms(torch, fns, n):
+    """Mean ms per launch of n back-to-back launches cycling through fns,
+    captured in one HIP graph (no host latency between launches) and timed
+    by one event pair after a GPU spin; the median over three replays."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fns[i % len(fns)]()
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(3):
+        torch.cuda._sleep(SPACER_CYCLES)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) / n)
+    del g
+    return sorted(ts)[1]
+
+
 def op_times(torch, step, wl, reps):
-    """Mean ms per launch of each op kind of the step (see main)."""
+    """Warm per-op times: `reps` back-to-back launches of each op kind on the
+    same operands (the memory-side cache may serve part of them)."""
     seen = {}
     for name, fn in step.ops:
-        if name not in wl.bytes or name in seen:
-            continue
-        ts = []
-        for _ in range(3):
-            torch.cuda._sleep(SPACER_CYCLES)
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record()
-            for _ in range(reps):
-                fn()
-            b.record()
-            torch.cuda.synchronize()
-            ts.append(a.elapsed_time(b) / reps)
-        seen[name] = sorted(ts)[1]
+        if name in wl.bytes and name not in seen:
+            seen[name] = _graph_launch_ms(torch, [fn], reps)
     return seen
+
+
+def rotated_op_times(torch, steps, wl, rounds):
+    """Cold per-op times: back-to-back launches of each op kind rotating over
+    the workload's operand copies (one Step per copy), so every launch finds
+    its operands in HBM, not in the memory-side cache."""
+    res = {}
+    for name in wl.bytes:
+        fns = [fn for st in steps for (n, fn) in st.ops if n == name]
+        res[name] = _graph_launch_ms(torch, fns, max(rounds * len(steps), len(fns)))
+    return res
 
 
 def cpu_baseline(wl, budget_s=10.0):
@@ -435,6 +480,8 @@ def main():
                     help="skip the per-op event pass")
     ap.add_argument("--op-reps", type=int, default=10,
                     help="back-to-back launches per event pair in the per-op pass")
+    ap.add_argument("--no-warm-pass", action="store_true",
+                    help="skip the warm per-op pass (same operands every launch)")
     ap.add_argument("--graph", dest="graph", action="store_true", default=True,
                     help="replay the step as a captured HIP graph in the timed region (default)")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
@@ -474,70 +521,89 @@ def main():
 
     print("bench: building workload %s" % args.workload, file=sys.stderr, flush=True)
     wl = Workload(args.workload, dev)
-    step = make_step(wl, torch)
+    # R copies of every operand; the timed steps and the cold per-op pass
+    # rotate over them, so that no launch finds its operands in the 256 MB
+    # memory-side cache (HBM-bound, "cold" timing).
+    n_rot = rotation_count(wl)
+    wls = [wl] + [wl.clone() for _ in range(n_rot - 1)]
+    steps = [make_step(w, torch) for w in wls]
     quiet = Events(torch, False)
     for _ in range(args.warmup):
-        step(quiet)
+        for st in steps:
+            st(quiet)
     torch.cuda.synchronize()
 
-    graph = None
+    graphs = None
     if args.graph:
-        # The step's launches captured once and replayed: no host launch
-        # latency between kernels (HIP graph under torch.cuda.CUDAGraph).
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step(quiet)
-        graph.replay()
+        # Each copy's step captured once and replayed: no host launch latency
+        # between kernels (HIP graphs under torch.cuda.CUDAGraph).
+        graphs = []
+        for st in steps:
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                st(quiet)
+            gr.replay()
+            graphs.append(gr)
         torch.cuda.synchronize()
 
-    # Timed region: exactly K steps between two synchronisations.
-    step_ev = Events(torch, graph is not None and not args.no_events)
+    # Timed region: exactly K steps between two synchronisations; step i runs
+    # on operand copy i mod R.
+    step_ev = Events(torch, graphs is not None and not args.no_events)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        if graph is not None:
+    for i in range(args.steps):
+        if graphs is not None:
             step_ev.begin("step")
-            graph.replay()
+            graphs[i % n_rot].replay()
             step_ev.end("step")
         else:
-            step(quiet)
+            steps[i % n_rot](quiet)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
-    step_bytes = sum(wl.bytes[k] * wl.counts[k] for k in wl.bytes)
+    step_bytes = wl.step_bytes()
     value = step_bytes / (ms * 1e-3) / 1e9
-    print("bench: timed %d steps, %.4f ms/step (%s)" % (
-        args.steps, ms, "graph replay" if graph is not None else "eager"), file=sys.stderr,
-        flush=True)
+    print("bench: timed %d steps, %.4f ms/step (%s over %d operand copies)" % (
+        args.steps, ms, "graph replay" if graphs is not None else "eager", n_rot),
+        file=sys.stderr, flush=True)
 
     per_op = {}
     roof = None
     if not args.no_events:
-        # Per-op times: for every op of the step, a GPU spin, then one event
-        # pair around `op_reps` back-to-back launches of that op, on the
-        # stream the kernels run on (the pair's own latency is spread over the
-        # launches, as a kernel trace would not count it).  A step of one op
-        # kind (decode) takes its per-launch time from the graph replays,
-        # where no host latency sits between launches.
-        means = op_times(torch, step, wl, args.op_reps)
-        if graph is not None and len(wl.bytes) == 1:
-            (k,) = wl.bytes
-            means[k] = step_ev.mean_ms()["step"] / wl.counts[k]
-        for k, t in means.items():
+        # Per-op times, on the stream the kernels run on, each from one event
+        # pair around many back-to-back launches replayed from a HIP graph
+        # after a GPU spin (the pair's own latency is spread over the
+        # launches, as a kernel trace would not count it).  Cold: the
+        # launches rotate over the operand copies (the headline, HBM-bound).
+        # Warm: the same operands every launch, so the memory-side cache can
+        # serve part of them (reported beside it).
+        cold = rotated_op_times(torch, steps, wl, args.op_reps)
+        warm = {} if args.no_warm_pass else op_times(torch, steps[0], wl, args.op_reps)
+        for k, t in cold.items():
             gbs = wl.bytes[k] / (t * 1e-3) / 1e9
             per_op[k] = {"ms": round(t, 5), "algorithmic_bytes": wl.bytes[k],
                          "launches_per_step": wl.counts[k],
-                         "GB_s": round(gbs, 1), "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2)}
-        dom = max(means, key=lambda k: means[k] * wl.counts[k])
+                         "GB_s": round(gbs, 1), "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+                         "timing": "cold (rotating over %d operand copies)" % n_rot}
+            if k in warm:
+                wg = wl.bytes[k] / (warm[k] * 1e-3) / 1e9
+                per_op[k].update(warm_ms=round(warm[k], 5), warm_GB_s=round(wg, 1),
+                                 warm_pct_of_peak=round(100 * wg / PEAK_HBM_GBS, 2))
+        dom = max(cold, key=lambda k: cold[k] * wl.counts[k])
         kernel = op_kernels(wl.name)[dom]
-        ach = wl.bytes[dom] / (means[dom] * 1e-3) / 1e9
+        ach = wl.bytes[dom] / (cold[dom] * 1e-3) / 1e9
         rec = recorded_traffic(kernel, wl.name)
         roof = {"bound": "hbm", "kernel": kernel, "op": dom, "achieved": round(ach, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
                 "traffic": None if rec is None else rec["hbm_bytes_per_launch"],
-                "bytes_per_launch": wl.bytes[dom], "avg_launch_ms": round(means[dom], 5)}
+                "bytes_per_launch": wl.bytes[dom], "avg_launch_ms": round(cold[dom], 5),
+                "timing": "cold: back-to-back launches rotating over %d operand copies" % n_rot}
         if rec is not None:
             roof["traffic_over_algorithmic"] = round(rec["hbm_bytes_per_launch"] / wl.bytes[dom], 4)
+        if dom in warm:
+            ach_w = wl.bytes[dom] / (warm[dom] * 1e-3) / 1e9
+            roof.update(achieved_warm=round(ach_w, 1), frac_warm=round(ach_w / PEAK_HBM_GBS, 4),
+                        avg_launch_ms_warm=round(warm[dom], 5))
 
     shape = wl.shape
     tc = shape["B"] * shape["D"] * shape.get("T", shape.get("tokens", 1))
@@ -548,7 +614,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.desc, "io_dtype": "bf16", **shape,
                    "ops_per_step": wl.counts, "step_algorithmic_bytes": step_bytes,
-                   "timing": "graph replay" if graph is not None else "eager launches"},
+                   "timing": ("graph replay" if graphs is not None else "eager launches") +
+                             " rotating over %d operand copies (cold caches)" % n_rot},
         "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "token_channels_per_s": round(tc / (ms * 1e-3), 1),
         "ops": per_op, "roofline": roof,

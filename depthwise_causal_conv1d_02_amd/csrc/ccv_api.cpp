@@ -45,10 +45,6 @@
 #ifndef CCV_FWD_VEC
 #define CCV_FWD_VEC 8
 #endif
-// Dense backward below the non-temporal size: the wave-uniform variant.
-#ifndef CCV_BWD_DENSE_UNIFORM
-#define CCV_BWD_DENSE_UNIFORM 1
-#endif
 // Small dense forwards (whose 8-channel geometry would already sit at the
 // minimum chunk) measured faster on 4-channel lanes with 32-step chunks.
 #ifndef CCV_FWD_SMALL_VEC
@@ -58,9 +54,14 @@
 #define CCV_FWD_SMALL_CHUNK 32
 #endif
 // Bulk loads use the non-temporal policy once an op streams at least this
-// many input bytes (twice the 256 MB memory-side cache).
+// many input bytes.  Measured with cold caches (the operands in HBM, not in
+// the memory-side cache): from the first byte for dense and packed rows;
+// seq_idx rows from twice the 256 MB memory-side cache.
 #ifndef CCV_NT_LOAD_MIN_BYTES
-#define CCV_NT_LOAD_MIN_BYTES (int64_t(1) << 29)
+#define CCV_NT_LOAD_MIN_BYTES 0
+#endif
+#ifndef CCV_NT_LOAD_MIN_BYTES_SEQ
+#define CCV_NT_LOAD_MIN_BYTES_SEQ (int64_t(1) << 29)
 #endif
 #ifndef CCV_UPD_VEC
 #define CCV_UPD_VEC 8
@@ -444,7 +445,8 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     a.n_gblk = g.n_gblk;
     a.n_block = g.n_block;
     a.cu_in_lds = p.packed && p.N + 1 <= ccv::kLdsCuMax;
-    a.nt_load = p.B * p.D * p.T * 2 >= CCV_NT_LOAD_MIN_BYTES;
+    a.nt_load = p.B * p.D * p.T * 2 >=
+                (p.seq ? CCV_NT_LOAD_MIN_BYTES_SEQ : CCV_NT_LOAD_MIN_BYTES);
     if (p.packed && !a.cu_in_lds) {
         rc = hip_status(ccv::launch_validate(a.cu, p.N, p.T, err_flag, 0, stream));
         if (rc != CCV_OK) return rc;
@@ -549,8 +551,8 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     a.n_seq = p.N;
     a.err = p.packed ? err_flag : nullptr;
     set_seq(a, seq_idx, p);
-    a.nt_load = 2 * p.B * p.D * p.T * 2 >= CCV_NT_LOAD_MIN_BYTES;
-    a.wave_uniform = CCV_BWD_DENSE_UNIFORM && !p.packed && !p.seq && !time_lanes && !a.nt_load;
+    a.nt_load = 2 * p.B * p.D * p.T * 2 >=
+                (p.seq ? CCV_NT_LOAD_MIN_BYTES_SEQ : CCV_NT_LOAD_MIN_BYTES);
     const int silu = activation == CCV_ACT_SILU;
     const int rounds = p.packed ? CCV_BWD_PACKED_ROUNDS : CCV_BWD_ROUNDS;
     if (!use_partials && rounds > 0 && !time_lanes)

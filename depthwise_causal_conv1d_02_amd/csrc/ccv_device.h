@@ -37,6 +37,11 @@ constexpr uint32_t kFirstNonzero = 0x1u, kLastMismatch = 0x2u, kDecreasing = 0x4
 #ifndef CCV_FWD_UNROLL
 #define CCV_FWD_UNROLL 4
 #endif
+// Dense rows on 4-channel lanes (the small-input forward): longer batches,
+// more loads in flight from HBM (measured with cold caches).
+#ifndef CCV_FWD_SMALL_UNROLL
+#define CCV_FWD_SMALL_UNROLL 16
+#endif
 #ifndef CCV_BWD_UNROLL
 #define CCV_BWD_UNROLL 4
 #endif
@@ -399,11 +404,10 @@ __device__ __forceinline__ int64_t find_row(const int32_t *cu, int64_t n, int64_
 // ===========================================================================
 // Forward
 // ===========================================================================
-template <int W, int VEC, bool SILU, bool NTL, bool PIPE>
+template <int W, int VEC, bool SILU, bool NTL, bool PIPE, int U>
 __device__ __forceinline__ void fwd_piece(const FwdArgs &a, int64_t b, int64_t r, int64_t s,
                                           int64_t e, int64_t ta, int64_t tb, int64_t c0,
                                           const float (&w)[W][VEC], const float (&bias)[VEC]) {
-    constexpr int U = CCV_FWD_UNROLL;
     const uint16_t *xb = static_cast<const uint16_t *>(a.x.ptr) + b * a.x.s0 + c0 * a.x.s1;
     uint16_t *yb = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.y.ptr)) + b * a.y.s0 +
                    c0 * a.y.s1;
@@ -600,14 +604,15 @@ __global__ __launch_bounds__(256) CCV_FWD_ATTR void k_fwd_chan(FwdArgs a) {
         if constexpr (ROWS == kRowsSeq) {
             fwd_seq_piece<W, VEC, SILU, NTL>(a, b, t0, t1, c0, w, bias);
         } else if constexpr (!PACKED) {
-            fwd_piece<W, VEC, SILU, NTL, PIPE>(a, b, b, 0, a.T, t0, t1, c0, w, bias);
+            constexpr int U = (VEC == 4 && !PIPE) ? CCV_FWD_SMALL_UNROLL : CCV_FWD_UNROLL;
+            fwd_piece<W, VEC, SILU, NTL, PIPE, U>(a, b, b, 0, a.T, t0, t1, c0, w, bias);
         } else {
             const int32_t *cu = a.cu_in_lds ? s_cu : a.cu;
             for (int64_t i = find_row(cu, a.n_seq, t0); i < a.n_seq; ++i) {
                 const int64_t s = cu[i], e = cu[i + 1];
                 if (s >= t1) break;
-                fwd_piece<W, VEC, SILU, NTL, PIPE>(a, 0, i, s, e, s > t0 ? s : t0, e < t1 ? e : t1,
-                                                c0, w, bias);
+                fwd_piece<W, VEC, SILU, NTL, PIPE, CCV_FWD_UNROLL>(
+                    a, 0, i, s, e, s > t0 ? s : t0, e < t1 ? e : t1, c0, w, bias);
             }
         }
     };
@@ -931,10 +936,7 @@ __device__ __forceinline__ void bwd_seq_piece(const BwdArgs &a, BwdLane<W, VEC, 
     for (; tau < end; ++tau) generic(tau);
 }
 
-// WU: the wave index through readfirstlane (addresses in scalars: fewer
-// registers, so 3 waves per SIMD instead of 2).  Measured faster for inputs
-// that stay in cache-sized streams, slower for the non-temporal ones.
-template <int W, int VEC, bool SILU, int ROWS, int FK, bool WU = false>
+template <int W, int VEC, bool SILU, int ROWS, int FK>
 __global__ __launch_bounds__(256) CCV_BWD_ATTR void k_bwd_chan(BwdArgs a) {
     constexpr bool PACKED = ROWS == kRowsPacked;
     constexpr bool BIAS = fk_bias(FK);
@@ -953,7 +955,7 @@ __global__ __launch_bounds__(256) CCV_BWD_ATTR void k_bwd_chan(BwdArgs a) {
     // compiler so, which keeps the time bounds and row offsets in scalars.
     // Measured: it frees the registers the seq_idx walk needs, but slows
     // the dense and packed streams on large inputs, so only seq_idx uses it.
-    const int wave = ((ROWS == kRowsSeq || WU) && CCV_WAVE_UNIFORM)
+    const int wave = (ROWS == kRowsSeq && CCV_WAVE_UNIFORM)
                          ? __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize)
                          : static_cast<int>(threadIdx.x / kWaveSize);
     const int lane = threadIdx.x % kWaveSize;
@@ -1605,21 +1607,41 @@ __global__ __launch_bounds__(256) void k_validate(const int32_t *cu, int64_t n_s
     }
 }
 
-// Fixed-order reduction of unique partials [P][D][kp]: the sum over
-// p = 0..P-1, always in increasing p (so the result does not depend on
-// scheduling), is added to dw[d][k] for k < W and, with kp = W+1, to db[d].
+// Fixed-order reduction of unique partials [P][D][kp] into dw[d][k] (k < W)
+// and, with kp = W+1, db[d].  A block takes 64 consecutive elements (one per
+// lane) and splits the P partials into 16 groups (4 waves x 4 accumulators):
+// group q sums p = q, q+16, q+32, ... in increasing p, then the 16 group sums
+// are added in increasing q.  The order depends on P only, never on
+// scheduling, so the result is the same bits run to run.
 __global__ __launch_bounds__(256) void k_dw_reduce(const float *part, int64_t n_part,
                                                    int64_t n_ch, int w, int kp, float *dw,
                                                    float *db) {
-    const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    constexpr int kAcc = 4, kGroups = kWavesPerBlock * kAcc;
+    __shared__ float s_acc[kGroups][kWaveSize];
+    const int lane = threadIdx.x % kWaveSize, wave = threadIdx.x / kWaveSize;
     const int64_t n_elem = n_ch * kp;
-    if (e >= n_elem) return;
-    float acc = 0.0f;
-    for (int64_t p = 0; p < n_part; ++p) acc += part[p * n_elem + e];
+    const int64_t e = static_cast<int64_t>(blockIdx.x) * kWaveSize + lane;
+    float acc[kAcc] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (e < n_elem) {
+        for (int64_t p0 = 0; p0 < n_part; p0 += kGroups) {
+#pragma unroll
+            for (int j = 0; j < kAcc; ++j) {
+                const int64_t p = p0 + wave * kAcc + j;
+                if (p < n_part) acc[j] += part[p * n_elem + e];
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kAcc; ++j) s_acc[wave * kAcc + j][lane] = acc[j];
+    __syncthreads();
+    if (wave != 0 || e >= n_elem) return;
+    float sum = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kGroups; ++q) sum += s_acc[q][lane];
     const int64_t ch = e / kp;
     const int k = static_cast<int>(e % kp);
-    if (k < w) dw[ch * w + k] += acc;
-    else db[ch] += acc;
+    if (k < w) dw[ch * w + k] += sum;
+    else db[ch] += sum;
 }
 
 // A stream value that never names a real stream: dispatch without launching.

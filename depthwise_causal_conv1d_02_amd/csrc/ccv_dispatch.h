@@ -88,20 +88,17 @@ hipError_t fwd_dispatch(const FwdArgs &a, int vec, int silu, int rows, hipStream
     return hipErrorInvalidValue;
 }
 
-template <int W, int V, bool S, int P, int F, bool U = false>
+template <int W, int V, bool S, int P, int F>
 hipError_t bwd_one(const BwdArgs &a, hipStream_t s, int64_t *cap) {
-    if (cap) *cap = capacity_of(k_bwd_chan<W, V, S, P, F, U>, CCV_BWD_DYN_LDS);
+    if (cap) *cap = capacity_of(k_bwd_chan<W, V, S, P, F>, CCV_BWD_DYN_LDS);
     if (s == kQueryStream) return hipSuccess;
-    return launch(k_bwd_chan<W, V, S, P, F, U>, a.n_block, a, s, CCV_BWD_DYN_LDS);
+    return launch(k_bwd_chan<W, V, S, P, F>, a.n_block, a, s, CCV_BWD_DYN_LDS);
 }
 
 template <int W, int V>
 hipError_t bwd_vec(const BwdArgs &a, int silu, int rows, int fk, hipStream_t s, int64_t *cap) {
-#define CCV_BWD(S, P, F)                                                         \
-    if (!!silu == S && rows == P && fk == F) {                                   \
-        if (P == kRowsDense && a.wave_uniform) return bwd_one<W, V, S, P, F, true>(a, s, cap); \
-        return bwd_one<W, V, S, P, F>(a, s, cap);                                \
-    }
+#define CCV_BWD(S, P, F) \
+    if (!!silu == S && rows == P && fk == F) return bwd_one<W, V, S, P, F>(a, s, cap);
 #define CCV_BWD_K(S, P) \
     CCV_BWD(S, P, kBf16) CCV_BWD(S, P, kBf16Bias) CCV_BWD(S, P, kF32) CCV_BWD(S, P, kF32Bias)
     CCV_BWD_K(true, kRowsDense) CCV_BWD_K(true, kRowsPacked) CCV_BWD_K(true, kRowsSeq)

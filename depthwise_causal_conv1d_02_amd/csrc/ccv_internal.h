@@ -90,7 +90,6 @@ struct BwdArgs {
     int64_t B, D, T, L, n_chunk, n_tblk, n_group, n_gblk, n_block;
     int cu_in_lds;
     int nt_load;
-    int wave_uniform;          // dense rows: the wave-uniform kernel variant
 };
 
 struct UpdArgs {

@@ -78,7 +78,7 @@ hipError_t launch_validate(const int32_t *cu, int64_t n_seq, int64_t total, uint
 
 hipError_t launch_dw_reduce(const float *partial, int64_t n_part, int64_t n_ch, int w, int kp,
                             float *dw, float *db, hipStream_t s) {
-    const int64_t blocks = (n_ch * kp + 255) / 256;
+    const int64_t blocks = (n_ch * kp + kWaveSize - 1) / kWaveSize;  // 64 elements per block
     hipLaunchKernelGGL(k_dw_reduce, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, partial,
                        n_part, n_ch, w, kp, dw, db);
     return hipGetLastError();
