@@ -61,7 +61,14 @@
 #define CCV_NT_LOAD_MIN_BYTES 0
 #endif
 #ifndef CCV_NT_LOAD_MIN_BYTES_SEQ
-#define CCV_NT_LOAD_MIN_BYTES_SEQ (int64_t(1) << 29)
+#define CCV_NT_LOAD_MIN_BYTES_SEQ (int64_t(1) << 29)    // forward
+#endif
+#ifndef CCV_NT_LOAD_MIN_BYTES_SEQ_BWD
+#define CCV_NT_LOAD_MIN_BYTES_SEQ_BWD 0
+#endif
+// The small-input forward geometry for seq_idx rows too.
+#ifndef CCV_FWD_SMALL_SEQ
+#define CCV_FWD_SMALL_SEQ 1
 #endif
 #ifndef CCV_UPD_VEC
 #define CCV_UPD_VEC 8
@@ -398,7 +405,7 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     const bool time_lanes = !p.packed && !p.seq && time_lanes_ok(x, y, nullptr);
     const bool pipe = p.B * p.D * p.T * 2 >= CCV_FWD_PIPE_MIN_BYTES;
     const int64_t groups8 = (p.D + ccv::kWaveSize * 8 - 1) / (ccv::kWaveSize * 8);
-    const bool small_dense = !p.packed && !p.seq && !pipe &&
+    const bool small_dense = !p.packed && (!p.seq || CCV_FWD_SMALL_SEQ) && !pipe &&
                              p.B * groups8 * p.T <= int64_t(CCV_FWD_TARGET_WAVES) * CCV_FWD_MIN_CHUNK;
     const int vec = time_lanes ? ccv::kVecTime
                                : pick_vec(small_dense ? CCV_FWD_SMALL_VEC : CCV_FWD_VEC, weight,
@@ -552,7 +559,7 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     a.err = p.packed ? err_flag : nullptr;
     set_seq(a, seq_idx, p);
     a.nt_load = 2 * p.B * p.D * p.T * 2 >=
-                (p.seq ? CCV_NT_LOAD_MIN_BYTES_SEQ : CCV_NT_LOAD_MIN_BYTES);
+                (p.seq ? CCV_NT_LOAD_MIN_BYTES_SEQ_BWD : CCV_NT_LOAD_MIN_BYTES);
     const int silu = activation == CCV_ACT_SILU;
     const int rounds = p.packed ? CCV_BWD_PACKED_ROUNDS : CCV_BWD_ROUNDS;
     if (!use_partials && rounds > 0 && !time_lanes)

@@ -525,11 +525,10 @@ __device__ __forceinline__ float preact_seq(const float (&w)[W][VEC], const floa
     return fmaf(w[W - 1][c], cur[c], z);
 }
 
-template <int W, int VEC, bool SILU, bool NTL>
+template <int W, int VEC, bool SILU, bool NTL, int U>
 __device__ __forceinline__ void fwd_seq_piece(const FwdArgs &a, int64_t b, int64_t ta,
                                               int64_t tb, int64_t c0, const float (&w)[W][VEC],
                                               const float (&bias)[VEC]) {
-    constexpr int U = CCV_FWD_UNROLL;
     const uint16_t *xb = static_cast<const uint16_t *>(a.x.ptr) + b * a.x.s0 + c0 * a.x.s1;
     uint16_t *yb = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.y.ptr)) + b * a.y.s0 +
                    c0 * a.y.s1;
@@ -602,7 +601,8 @@ __global__ __launch_bounds__(256) CCV_FWD_ATTR void k_fwd_chan(FwdArgs a) {
     auto run = [&](auto ntl) {
         constexpr bool NTL = decltype(ntl)::value;
         if constexpr (ROWS == kRowsSeq) {
-            fwd_seq_piece<W, VEC, SILU, NTL>(a, b, t0, t1, c0, w, bias);
+            constexpr int U = VEC == 4 ? CCV_FWD_SMALL_UNROLL : CCV_FWD_UNROLL;
+            fwd_seq_piece<W, VEC, SILU, NTL, U>(a, b, t0, t1, c0, w, bias);
         } else if constexpr (!PACKED) {
             constexpr int U = (VEC == 4 && !PIPE) ? CCV_FWD_SMALL_UNROLL : CCV_FWD_UNROLL;
             fwd_piece<W, VEC, SILU, NTL, PIPE, U>(a, b, b, 0, a.T, t0, t1, c0, w, bias);
