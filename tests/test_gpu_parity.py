@@ -694,3 +694,35 @@ def test_update_several_tokens(B, D, L, W, bias, wdt, layout):
     oyt, ost = oracle.update(f64(xt), ost, f64(w), f64(b), "silu")
     check_bf16("next token y", yt, oyt)
     check_exact_bf16("conv_state after", g_state, ost)
+
+
+def test_packed_and_seq_idx_time_contiguous_layout():
+    """Packed offsets and seq_idx ids on a [B,D,T]-contiguous input (the
+    one-channel lanes): forward and backward against the oracle."""
+    lengths = [5, 1, 40, 3, 77]
+    cu = synth.cu_from_lengths(lengths)
+    T = int(cu[-1])
+    inp, g = inputs(2000, 1, 48, T, "tc", True, True, BF16, True, cu)
+    ops.reset_flag(DEV)
+    y, fin = run_fwd(g, "tc", "silu", True, cu)
+    check_fwd(inp, y, fin, "silu")
+    dx, dw, db, dinit = run_bwd(g, "tc", "silu", False, cu)
+    check_bwd(inp, dx, dw, db, dinit, "silu")
+    ops.check_flag(DEV)
+
+    inp, g = inputs(2001, 2, 40, 96, "tc", True, False, BF16)
+    seq = synth.seq_idx_tensor(torch.Generator().manual_seed(2002), 2, 96, "random")
+    y = guarded_act(2, 40, 96, "tc", DEV)
+    ops.fwd(g["x"], g["weight"], g["bias"], None, None, "silu", y=y.view, seq_idx=dev(seq))
+    dx = guarded_act(2, 40, 96, "tc", DEV)
+    _, dw, db, _ = ops.bwd(g["x"], g["weight"], g["dy"], g["bias"], None, None, None, "silu",
+                           False, False, dx=dx.view, seq_idx=dev(seq))
+    torch.cuda.synchronize()
+    oy = oracle.fwd_seq(f64(inp["x"]), f64(inp["weight"]), seq.numpy(), f64(inp["bias"]), "silu")
+    odx, odw, odb = oracle.bwd_seq(f64(inp["x"]), f64(inp["weight"]), f64(inp["dy"]),
+                                   seq.numpy(), f64(inp["bias"]), "silu")
+    check_bf16("y", y.view, oy)
+    check_bf16("dx", dx.view, odx)
+    check_f32_rel("dweight", dw, odw)
+    check_f32_rel("dbias", db, odb)
+    assert y.intact() and dx.intact()

@@ -150,3 +150,52 @@ def test_workload_6_seq_idx_fwd_bwd():
     check_bf16("dx", out["dx"][:, sel], odx)
     check_f32_rel("dweight", out["dw"][sel], odw)
     check_f32_rel("dbias", out["db"][sel], odb)
+
+
+def test_more_than_2_pow_31_elements():
+    """64-bit indexing: x [1, 8, 2^28 + 37] (2.1 G elements, 4.3 GB) in
+    channel-last storage, forward with final states, checked on sampled
+    positions (each from its own 4-token window through the oracle) across
+    the 2^31-element boundary and at both ends; then backward dx on samples
+    with dy zero except at the sampled tokens."""
+    T = (1 << 28) + 37
+    D = 8
+    gen = torch.Generator(device=DEV).manual_seed(31)
+    x = torch.randn(1, T, D, generator=gen, device=DEV).to(torch.bfloat16).transpose(1, 2)
+    w = (torch.rand(D, 4, generator=gen, device=DEV) - 0.5).to(torch.bfloat16)
+    b = (torch.randn(D, generator=gen, device=DEV) * 0.1).to(torch.bfloat16)
+    y, fin = ops.fwd(x, w, b, None, None, "silu", return_final_states=True)
+    torch.cuda.synchronize()
+    wf, bf = f(w), f(b)
+    edge = (1 << 31) // D          # first token whose element index passes 2^31
+    for t in (0, 1, 2, 3, edge - 2, edge - 1, edge, edge + 1, T // 2, T - 2, T - 1):
+        lo = max(0, t - 3)
+        win = f(x[:, :, lo:t + 1])
+        oy, _ = oracle.fwd(win, wf, bf, None, None, "silu")
+        check_bf16("y[%d]" % t, y[:, :, t:t + 1], oy[:, :, -1:])
+    check_exact_bf16("final_states", fin, f(x[:, :, T - 3:]))
+    # backward: dy nonzero only at a few tokens, so dx there has a local closed
+    # window in the oracle
+    dy = torch.zeros_like(x)
+    picks = (edge, T - 1)
+    for t in picks:
+        dy[:, :, t] = 1.0
+    dx, dwt, dbt, _ = ops.bwd(x, w, dy, b, None, None, None, "silu")
+    torch.cuda.synchronize()
+    for t in picks:
+        lo, hi = t - 6, min(T, t + 4)
+        xs, dys = f(x[:, :, lo:hi]), f(dy[:, :, lo:hi])
+        # the window's leading tokens act as its past: use them as initial state
+        odx, odw, odb, _ = oracle.bwd(xs[:, :, 3:], wf, dys[:, :, 3:], bf, None, xs[:, :, :3],
+                                      None, "silu")
+        check_bf16("dx near %d" % t, dx[:, :, lo + 3:hi], odx)
+    # dW/dB: only the picked tokens contribute
+    ow, ob = np.zeros((D, 4)), np.zeros(D)
+    for t in picks:
+        xs = f(x[:, :, t - 3:t + 1])
+        _, odw, odb, _ = oracle.bwd(xs[:, :, 3:], wf, f(dy[:, :, t:t + 1]), bf, None,
+                                    xs[:, :, :3], None, "silu")
+        ow += odw
+        ob += odb
+    check_f32_rel("dweight", dwt, ow)
+    check_f32_rel("dbias", dbt, ob)
