@@ -1376,58 +1376,26 @@ void k_bwd_tc(BwdArgs a) {
 #ifndef CCV_UPD_ROWS
 #define CCV_UPD_ROWS 2          // batch rows an 8-channel update lane serves
 #endif
+#ifndef CCV_UPD_STAGED
+#define CCV_UPD_STAGED 1        // coalesced (LDS-staged) update when D % 512 == 0
+#endif
 
-// The register budget of up to CCV_UPD_MAX_WAVES waves per SIMD leaves room
-// for every load of a lane to be in flight at once.  With 8 channels per lane
-// the host has verified unit channel strides, a contiguous [B,D,W-1] state, a
-// contiguous [D,W] filter and bias, and 16-byte alignment: a lane's state is
-// 3 x 16 contiguous bytes.  A lane serves RPL batch rows of the same
-// channels, so their filter and bias are loaded once.
-template <int W, bool SILU, bool WF32, bool BIAS, int RPL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, CCV_UPD_MAX_WAVES)))
-void k_update_vec(UpdArgs a) {
-    constexpr int VEC = 8;
-    constexpr int kStateVecs = VEC * (W - 1) / 8;              // 16-byte vectors of state
-    constexpr int kFilterVecs = VEC * W * (WF32 ? 4 : 2) / 16;
-    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    const int64_t rg = gid / a.n_lane_per_row;
-    if (rg >= a.n_row_groups) return;
-    const int64_t c0 = (gid % a.n_lane_per_row) * VEC;
-    const int64_t b0 = rg * RPL;
+// Per-lane pieces of the 8-channel update, shared by both kernels below.
+// Filter taps and bias of 8 channels from their raw 16-byte vectors (the
+// bias has the filter's dtype).
+template <int W, bool WF32>
+struct UpdVecs {
+    static constexpr int kState = 8 * (W - 1) / 8;           // 16-byte vectors of state
+    static constexpr int kFilter = 8 * W * (WF32 ? 4 : 2) / 16;
+    static constexpr int kBias = WF32 ? 2 : 1;
+};
 
-    // Every load first: filter, bias, then each row's state and token.
-    const u32x4_t *wq = reinterpret_cast<const u32x4_t *>(
-        static_cast<const char *>(a.w) + c0 * W * (WF32 ? 4 : 2));
-    // The bias has the filter's dtype: 8 BF16 values (one vector) or 8 FP32.
-    constexpr int kBiasVecs = WF32 ? 2 : 1;
-    u32x4_t wv[kFilterVecs], bv[kBiasVecs];
+template <int W, bool WF32>
+__device__ __forceinline__ void upd_unpack_filter(
+    const u32x4_t (&wv)[UpdVecs<W, WF32>::kFilter], const u32x4_t (&bv)[UpdVecs<W, WF32>::kBias],
+    float (&w)[W][8], float (&bias)[8]) {
 #pragma unroll
-    for (int i = 0; i < kFilterVecs; ++i) wv[i] = wq[i];
-#pragma unroll
-    for (int i = 0; i < kBiasVecs; ++i) bv[i] = u32x4_t{0u, 0u, 0u, 0u};
-    if constexpr (BIAS) {
-        const u32x4_t *bq = reinterpret_cast<const u32x4_t *>(
-            static_cast<const char *>(a.bias) + c0 * (WF32 ? 4 : 2));
-#pragma unroll
-        for (int i = 0; i < kBiasVecs; ++i) bv[i] = bq[i];
-    }
-    u32x4_t sv[RPL][kStateVecs], xv[RPL];
-#pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-        if (b0 + r >= a.B) break;
-        const u32x4_t *sq = reinterpret_cast<const u32x4_t *>(
-            static_cast<const uint16_t *>(a.state) + (b0 + r) * a.s_sb + c0 * (W - 1));
-#pragma unroll
-        for (int i = 0; i < kStateVecs; ++i)
-            sv[r][i] = CCV_UPD_NT ? __builtin_nontemporal_load(sq + i) : sq[i];
-        const u32x4_t *xq = reinterpret_cast<const u32x4_t *>(
-            static_cast<const uint16_t *>(a.x) + (b0 + r) * a.x_sb + c0);
-        xv[r] = CCV_UPD_NT ? __builtin_nontemporal_load(xq) : *xq;
-    }
-
-    float w[W][VEC], bias[VEC];
-#pragma unroll
-    for (int c = 0; c < VEC; ++c) {
+    for (int c = 0; c < 8; ++c) {
 #pragma unroll
         for (int k = 0; k < W; ++k) {
             const int e2 = c * W + k;
@@ -1441,47 +1409,201 @@ void k_update_vec(UpdArgs a) {
         if constexpr (WF32) bias[c] = __uint_as_float(bv[c / 4][c % 4]);
         else bias[c] = (c % 2) ? hi_bf16(bv[0][c / 2]) : lo_bf16(bv[0][c / 2]);
     }
+}
 
+// One row of 8 channels: y from the state (s_0 .. s_{W-2}) and the token x,
+// and the new state (s_1 .. s_{W-2}, x) as raw bits (a copy, never re-rounded).
+template <int W, bool SILU, bool WF32>
+__device__ __forceinline__ void upd_row(const float (&w)[W][8], const float (&bias)[8],
+                                        const u32x4_t (&sv)[UpdVecs<W, WF32>::kState],
+                                        const u32x4_t &xv, float (&out)[8],
+                                        u32x4_t (&nv)[UpdVecs<W, WF32>::kState]) {
+    constexpr int VEC = 8;
+    uint16_t st[VEC][W - 1], xr[VEC];
+#pragma unroll
+    for (int e2 = 0; e2 < VEC * (W - 1); ++e2)
+        st[e2 / (W - 1)][e2 % (W - 1)] =
+            static_cast<uint16_t>(sv[e2 / 8][(e2 % 8) / 2] >> (16 * (e2 % 2)));
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) xr[c] = static_cast<uint16_t>(xv[c / 2] >> (16 * (c % 2)));
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) {
+        float z = bias[c];
+#pragma unroll
+        for (int k = 0; k < W - 1; ++k) z = fmaf(w[k][c], bf16_bits_to_f32(st[c][k]), z);
+        z = fmaf(w[W - 1][c], bf16_bits_to_f32(xr[c]), z);
+        out[c] = act<SILU>(z);
+    }
+#pragma unroll
+    for (int i = 0; i < VEC * (W - 1) / 2; ++i) {
+        uint16_t h[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int e2 = 2 * i + q, c = e2 / (W - 1), j = e2 % (W - 1);
+            h[q] = j < W - 2 ? st[c][j + 1] : xr[c];
+        }
+        nv[i / 4][i % 4] = static_cast<uint32_t>(h[0]) | (static_cast<uint32_t>(h[1]) << 16);
+    }
+}
+
+// The register budget of up to CCV_UPD_MAX_WAVES waves per SIMD leaves room
+// for every load of a lane to be in flight at once.  With 8 channels per lane
+// the host has verified unit channel strides, a contiguous [B,D,W-1] state, a
+// contiguous [D,W] filter and bias, and 16-byte alignment: a lane's state is
+// 3 x 16 contiguous bytes.  A lane serves RPL batch rows of the same
+// channels, so their filter and bias are loaded once.
+template <int W, bool SILU, bool WF32, bool BIAS, int RPL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, CCV_UPD_MAX_WAVES)))
+void k_update_vec(UpdArgs a) {
+    using V = UpdVecs<W, WF32>;
+    constexpr int VEC = 8;
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t rg = gid / a.n_lane_per_row;
+    if (rg >= a.n_row_groups) return;
+    const int64_t c0 = (gid % a.n_lane_per_row) * VEC;
+    const int64_t b0 = rg * RPL;
+
+    // Every load first: filter, bias, then each row's state and token.
+    const u32x4_t *wq = reinterpret_cast<const u32x4_t *>(
+        static_cast<const char *>(a.w) + c0 * W * (WF32 ? 4 : 2));
+    u32x4_t wv[V::kFilter], bv[V::kBias];
+#pragma unroll
+    for (int i = 0; i < V::kFilter; ++i) wv[i] = wq[i];
+#pragma unroll
+    for (int i = 0; i < V::kBias; ++i) bv[i] = u32x4_t{0u, 0u, 0u, 0u};
+    if constexpr (BIAS) {
+        const u32x4_t *bq = reinterpret_cast<const u32x4_t *>(
+            static_cast<const char *>(a.bias) + c0 * (WF32 ? 4 : 2));
+#pragma unroll
+        for (int i = 0; i < V::kBias; ++i) bv[i] = bq[i];
+    }
+    u32x4_t sv[RPL][V::kState], xv[RPL];
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
         if (b0 + r >= a.B) break;
-        // Raw bits: the shifted state is a copy of them, never re-rounded.
-        uint16_t st[VEC][W - 1], xr[VEC];
+        const u32x4_t *sq = reinterpret_cast<const u32x4_t *>(
+            static_cast<const uint16_t *>(a.state) + (b0 + r) * a.s_sb + c0 * (W - 1));
 #pragma unroll
-        for (int e2 = 0; e2 < VEC * (W - 1); ++e2)
-            st[e2 / (W - 1)][e2 % (W - 1)] =
-                static_cast<uint16_t>(sv[r][e2 / 8][(e2 % 8) / 2] >> (16 * (e2 % 2)));
+        for (int i = 0; i < V::kState; ++i)
+            sv[r][i] = CCV_UPD_NT ? __builtin_nontemporal_load(sq + i) : sq[i];
+        const u32x4_t *xq = reinterpret_cast<const u32x4_t *>(
+            static_cast<const uint16_t *>(a.x) + (b0 + r) * a.x_sb + c0);
+        xv[r] = CCV_UPD_NT ? __builtin_nontemporal_load(xq) : *xq;
+    }
+
+    float w[W][VEC], bias[VEC];
+    upd_unpack_filter<W, WF32>(wv, bv, w, bias);
 #pragma unroll
-        for (int c = 0; c < VEC; ++c)
-            xr[c] = static_cast<uint16_t>(xv[r][c / 2] >> (16 * (c % 2)));
+    for (int r = 0; r < RPL; ++r) {
+        if (b0 + r >= a.B) break;
         float out[VEC];
-#pragma unroll
-        for (int c = 0; c < VEC; ++c) {
-            float z = bias[c];
-#pragma unroll
-            for (int k = 0; k < W - 1; ++k) z = fmaf(w[k][c], bf16_bits_to_f32(st[c][k]), z);
-            z = fmaf(w[W - 1][c], bf16_bits_to_f32(xr[c]), z);
-            out[c] = act<SILU>(z);
-        }
+        u32x4_t nv[V::kState];
+        upd_row<W, SILU, WF32>(w, bias, sv[r], xv[r], out, nv);
         store_vec<VEC, true>(static_cast<uint16_t *>(a.y) + (b0 + r) * a.y_sb + c0, 1, out);
-        // New state (s_1 .. s_{W-2}, x), packed back into 16-byte vectors.
-        u32x4_t nv[kStateVecs];
-#pragma unroll
-        for (int i = 0; i < VEC * (W - 1) / 2; ++i) {
-            uint16_t h[2];
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int e2 = 2 * i + q, c = e2 / (W - 1), j = e2 % (W - 1);
-                h[q] = j < W - 2 ? st[c][j + 1] : xr[c];
-            }
-            nv[i / 4][i % 4] = static_cast<uint32_t>(h[0]) | (static_cast<uint32_t>(h[1]) << 16);
-        }
         u32x4_t *sq = reinterpret_cast<u32x4_t *>(static_cast<uint16_t *>(a.state) +
                                                   (b0 + r) * a.s_sb + c0 * (W - 1));
 #pragma unroll
-        for (int i = 0; i < kStateVecs; ++i) {
+        for (int i = 0; i < V::kState; ++i) {
             if (CCV_UPD_NT) __builtin_nontemporal_store(nv[i], sq + i);
             else sq[i] = nv[i];
+        }
+    }
+}
+
+// The same update with every global access coalesced: a wave owns 512
+// consecutive channels (the host has verified D % 512 == 0, so a wave never
+// straddles two row groups), and its state rows and filter are contiguous
+// byte ranges.  Lane l loads the 16-byte vectors l, l + 64, ... of each range
+// (each wave-wide load is 1 KB contiguous), the vectors pass through the
+// wave's own LDS slice to the lane that owns their channels, and the new
+// state goes back the same way.  The strided per-lane form touches every
+// 128-byte line of the range with each of its loads.
+template <int W, bool SILU, bool WF32, bool BIAS, int RPL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, CCV_UPD_MAX_WAVES)))
+void k_update_staged(UpdArgs a) {
+    using V = UpdVecs<W, WF32>;
+    constexpr int VEC = 8;
+    __shared__ u32x4_t s_state[kWavesPerBlock][RPL][kWaveSize * V::kState];
+    __shared__ u32x4_t s_filt[kWavesPerBlock][kWaveSize * V::kFilter];
+    const int wave = threadIdx.x / kWaveSize, lane = threadIdx.x % kWaveSize;
+    const int64_t gw = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave;
+    const int64_t lanes_per_row = a.n_lane_per_row / kWaveSize;   // waves per row group
+    const int64_t rg = gw / lanes_per_row;
+    // Uniform over the wave; waves past the end still reach every barrier.
+    const bool live = rg < a.n_row_groups;
+    const int64_t cw = (gw % lanes_per_row) * (kWaveSize * VEC);  // the wave's first channel
+    const int64_t b0 = rg * RPL;
+
+    const u32x4_t *wq = reinterpret_cast<const u32x4_t *>(
+        static_cast<const char *>(a.w) + cw * W * (WF32 ? 4 : 2));
+    u32x4_t wv[V::kFilter], bv[V::kBias], sv[RPL][V::kState], xv[RPL];
+#pragma unroll
+    for (int i = 0; i < V::kBias; ++i) bv[i] = u32x4_t{0u, 0u, 0u, 0u};
+    if (live) {
+#pragma unroll
+        for (int i = 0; i < V::kFilter; ++i) wv[i] = wq[lane + kWaveSize * i];
+        if constexpr (BIAS) {
+            const u32x4_t *bq = reinterpret_cast<const u32x4_t *>(
+                static_cast<const char *>(a.bias) + (cw + lane * VEC) * (WF32 ? 4 : 2));
+#pragma unroll
+            for (int i = 0; i < V::kBias; ++i) bv[i] = bq[i];
+        }
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+            if (b0 + r >= a.B) break;
+            const u32x4_t *sq = reinterpret_cast<const u32x4_t *>(
+                static_cast<const uint16_t *>(a.state) + (b0 + r) * a.s_sb + cw * (W - 1));
+#pragma unroll
+            for (int i = 0; i < V::kState; ++i) sv[r][i] = sq[lane + kWaveSize * i];
+            xv[r] = *reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(a.x) +
+                                                       (b0 + r) * a.x_sb + cw + lane * VEC);
+        }
+#pragma unroll
+        for (int i = 0; i < V::kFilter; ++i) s_filt[wave][lane + kWaveSize * i] = wv[i];
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+            if (b0 + r >= a.B) break;
+#pragma unroll
+            for (int i = 0; i < V::kState; ++i) s_state[wave][r][lane + kWaveSize * i] = sv[r][i];
+        }
+    }
+    __syncthreads();
+    float w[W][VEC], bias[VEC];
+    u32x4_t nv[RPL][V::kState];
+    if (live) {
+#pragma unroll
+        for (int i = 0; i < V::kFilter; ++i) wv[i] = s_filt[wave][lane * V::kFilter + i];
+        upd_unpack_filter<W, WF32>(wv, bv, w, bias);
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+            if (b0 + r >= a.B) break;
+            u32x4_t own[V::kState];
+#pragma unroll
+            for (int i = 0; i < V::kState; ++i) own[i] = s_state[wave][r][lane * V::kState + i];
+            float out[VEC];
+            upd_row<W, SILU, WF32>(w, bias, own, xv[r], out, nv[r]);
+            store_vec<VEC, true>(static_cast<uint16_t *>(a.y) + (b0 + r) * a.y_sb + cw +
+                                     lane * VEC, 1, out);
+        }
+    }
+    __syncthreads();  // every lane has read its slice before it is overwritten
+    if (live) {
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+            if (b0 + r >= a.B) break;
+#pragma unroll
+            for (int i = 0; i < V::kState; ++i) s_state[wave][r][lane * V::kState + i] = nv[r][i];
+        }
+    }
+    __syncthreads();
+    if (live) {
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+            if (b0 + r >= a.B) break;
+            u32x4_t *sq = reinterpret_cast<u32x4_t *>(static_cast<uint16_t *>(a.state) +
+                                                      (b0 + r) * a.s_sb + cw * (W - 1));
+#pragma unroll
+            for (int i = 0; i < V::kState; ++i) sq[lane + kWaveSize * i] = s_state[wave][r][lane + kWaveSize * i];
         }
     }
 }

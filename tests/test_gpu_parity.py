@@ -268,6 +268,11 @@ UPDATE_CASES = [(4, 512, True, BF16, 4), (3, 40, True, BF16, 4), (2, 1024, False
 
 
 UPDATE_CASES += [(4, 512, True, F32, 4), (3, 40, True, F32, 3), (2, 64, True, F32, 2)]
+# Channel counts that are multiples of 512 take the coalesced (LDS-staged)
+# kernel: several waves per row group, an odd batch (a half-empty last row
+# group), every width and filter kind.
+UPDATE_CASES += [(5, 1536, True, BF16, 4), (7, 512, False, BF16, 4), (3, 1024, True, F32, 2),
+                 (1, 2048, True, BF16, 3), (9, 512, False, F32, 3), (2, 512, True, BF16, 2)]
 
 
 @pytest.mark.parametrize("B,D,bias,wdt,W", UPDATE_CASES)
@@ -288,6 +293,25 @@ def test_update_parity(B, D, bias, wdt, W):
         oy, st = oracle.update(f64(x), st, f64(w), f64(b), "silu")
         check_bf16("update y", y.view, oy)
         assert y.intact()
+        check_exact_bf16("conv_state", g_state, st)
+
+
+@pytest.mark.parametrize("D", [512, 1536])
+def test_update_no_activation(D):
+    print("update case act=none", D, flush=True)
+    gen = torch.Generator().manual_seed(900 + D)
+    B = 3
+    state = synth.state_tensor(gen, B, D, 4)
+    w = synth.weight_tensor(gen, D, 4, dtype=BF16)
+    b = synth.bias_tensor(gen, D, BF16)
+    g_state = dev(state)
+    st = f64(state)
+    for _ in range(3):
+        x = synth.activation_tensor(gen, B, D, 1, "tc")[:, :, 0].contiguous()
+        y = ops.update(dev(x), g_state, dev(w), dev(b), None)
+        torch.cuda.synchronize()
+        oy, st = oracle.update(f64(x), st, f64(w), f64(b), None)
+        check_bf16("update y", y, oy)
         check_exact_bf16("conv_state", g_state, st)
 
 
