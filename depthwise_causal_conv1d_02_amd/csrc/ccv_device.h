@@ -1379,6 +1379,14 @@ void k_bwd_tc(BwdArgs a) {
 #ifndef CCV_UPD_STAGED
 #define CCV_UPD_STAGED 1        // coalesced (LDS-staged) update when D % 512 == 0
 #endif
+// ... and from this many (row, channel) pairs (12 MiB of update traffic at
+// width 4).  Measured with cold states: the staged kernel loses about 0.5 us
+// to the plain one up to 1 MB, 0.1 us at 8 MB, and wins 0.15 us at 16 MB and
+// 0.7 us at 34 MB (its LDS round trips lengthen a launch-bound kernel, and
+// shorten the L2 request stream of a bandwidth-bound one).
+#ifndef CCV_UPD_STAGED_MIN_BD
+#define CCV_UPD_STAGED_MIN_BD (int64_t(3) << 18)
+#endif
 
 // Per-lane pieces of the 8-channel update, shared by both kernels below.
 // Filter taps and bias of 8 channels from their raw 16-byte vectors (the

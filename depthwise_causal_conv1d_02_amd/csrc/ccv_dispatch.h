@@ -135,8 +135,10 @@ hipError_t update_dispatch(const UpdArgs &a, int vec, int silu, hipStream_t s) {
         CCV_UPD(true, true, true) CCV_UPD(false, false, true) CCV_UPD(false, false, false)
         CCV_UPD(false, true, false) CCV_UPD(false, true, true)
 #undef CCV_UPD
-    } else if (vec == 8 && CCV_UPD_STAGED && a.n_lane_per_row % kWaveSize == 0) {
-        // Whole waves per row group (D % 512 == 0): the coalesced kernel.
+    } else if (vec == 8 && CCV_UPD_STAGED && a.n_lane_per_row % kWaveSize == 0 &&
+               a.B * a.D >= CCV_UPD_STAGED_MIN_BD) {
+        // Whole waves per row group (D % 512 == 0) and a large enough batch:
+        // the coalesced kernel.
         const int64_t waves = a.n_row_groups * (a.n_lane_per_row / kWaveSize);
         const int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
 #define CCV_UPD(S, F, B)                                                                      \

@@ -268,11 +268,14 @@ UPDATE_CASES = [(4, 512, True, BF16, 4), (3, 40, True, BF16, 4), (2, 1024, False
 
 
 UPDATE_CASES += [(4, 512, True, F32, 4), (3, 40, True, F32, 3), (2, 64, True, F32, 2)]
-# Channel counts that are multiples of 512 take the coalesced (LDS-staged)
-# kernel: several waves per row group, an odd batch (a half-empty last row
-# group), every width and filter kind.
 UPDATE_CASES += [(5, 1536, True, BF16, 4), (7, 512, False, BF16, 4), (3, 1024, True, F32, 2),
                  (1, 2048, True, BF16, 3), (9, 512, False, F32, 3), (2, 512, True, BF16, 2)]
+# Channel counts that are multiples of 512 with at least 786,432 (row,
+# channel) pairs take the coalesced (LDS-staged) kernel: several waves per
+# row group, odd batches (a half-empty last row group), a single row, the
+# size threshold itself, every width and filter kind.
+UPDATE_CASES += [(385, 2048, True, BF16, 4), (97, 8192, False, BF16, 4), (193, 4096, True, F32, 2),
+                 (1, 786432, True, BF16, 3), (257, 3072, False, F32, 3), (768, 1024, True, BF16, 2)]
 
 
 @pytest.mark.parametrize("B,D,bias,wdt,W", UPDATE_CASES)
@@ -296,11 +299,10 @@ def test_update_parity(B, D, bias, wdt, W):
         check_exact_bf16("conv_state", g_state, st)
 
 
-@pytest.mark.parametrize("D", [512, 1536])
-def test_update_no_activation(D):
-    print("update case act=none", D, flush=True)
+@pytest.mark.parametrize("B,D", [(3, 512), (513, 1536)])
+def test_update_no_activation(B, D):
+    print("update case act=none", B, D, flush=True)
     gen = torch.Generator().manual_seed(900 + D)
-    B = 3
     state = synth.state_tensor(gen, B, D, 4)
     w = synth.weight_tensor(gen, D, 4, dtype=BF16)
     b = synth.bias_tensor(gen, D, BF16)
