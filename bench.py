@@ -486,6 +486,8 @@ def main():
                     help="replay the step as a captured HIP graph in the timed region (default)")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="launch every op eagerly in the timed region")
+    ap.add_argument("--no-cycle-graph", dest="cycle_graph", action="store_false", default=True,
+                    help="replay one graph per step instead of one per rotation of R steps")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the workload, run a plain device copy of MIB MiB "
                          "(counter calibration for rocprofv3 --pmc)")
@@ -533,10 +535,13 @@ def main():
             st(quiet)
     torch.cuda.synchronize()
 
-    graphs = None
+    graphs = cycle = None
     if args.graph:
         # Each copy's step captured once and replayed: no host launch latency
-        # between kernels (HIP graphs under torch.cuda.CUDAGraph).
+        # between kernels (HIP graphs under torch.cuda.CUDAGraph).  A second
+        # graph holds one whole rotation (the R steps in order), so the timed
+        # loop launches one graph per R steps and a host launch never stands
+        # between two steps.
         graphs = []
         for st in steps:
             gr = torch.cuda.CUDAGraph()
@@ -544,20 +549,29 @@ def main():
                 st(quiet)
             gr.replay()
             graphs.append(gr)
+        if args.cycle_graph:
+            cycle = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(cycle):
+                for st in steps:
+                    st(quiet)
+            cycle.replay()
         torch.cuda.synchronize()
 
     # Timed region: exactly K steps between two synchronisations; step i runs
     # on operand copy i mod R.
-    step_ev = Events(torch, graphs is not None and not args.no_events)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        if graphs is not None:
-            step_ev.begin("step")
+    i = 0
+    while i < args.steps:
+        if cycle is not None and i + n_rot <= args.steps:
+            cycle.replay()          # steps i .. i+R-1 (i is a multiple of R here)
+            i += n_rot
+        elif graphs is not None:
             graphs[i % n_rot].replay()
-            step_ev.end("step")
+            i += 1
         else:
             steps[i % n_rot](quiet)
+            i += 1
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
@@ -614,7 +628,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.desc, "io_dtype": "bf16", **shape,
                    "ops_per_step": wl.counts, "step_algorithmic_bytes": step_bytes,
-                   "timing": ("graph replay" if graphs is not None else "eager launches") +
+                   "timing": ("graph replay, one graph per %d steps" % n_rot if cycle is not None
+                              else "graph replay, one graph per step" if graphs is not None
+                              else "eager launches") +
                              " rotating over %d operand copies (cold caches)" % n_rot},
         "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "token_channels_per_s": round(tc / (ms * 1e-3), 1),
