@@ -1522,34 +1522,39 @@ void k_update_vec(UpdArgs a) {
 // consecutive channels (the host has verified D % 512 == 0, so a wave never
 // straddles two row groups), and its state rows and filter are contiguous
 // byte ranges.  Lane l loads the 16-byte vectors l, l + 64, ... of each range
-// (each wave-wide load is 1 KB contiguous), the vectors pass through the
-// wave's own LDS slice to the lane that owns their channels, and the new
-// state goes back the same way.  The strided per-lane form touches every
-// 128-byte line of the range with each of its loads.
+// (each wave-wide load is 1 KB contiguous), the vectors pass through LDS to
+// the lane that owns their channels, and the new state goes back the same
+// way.  The four waves of a block take the same 512 channels of four
+// consecutive row groups, so the block loads their filter once.  (The
+// strided per-lane form touches every 128-byte line of a range with each of
+// its loads.)
 template <int W, bool SILU, bool WF32, bool BIAS, int RPL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, CCV_UPD_MAX_WAVES)))
 void k_update_staged(UpdArgs a) {
     using V = UpdVecs<W, WF32>;
     constexpr int VEC = 8;
+    constexpr int kFiltVecs = kWaveSize * V::kFilter;  // the block's filter, 16-byte vectors
     __shared__ u32x4_t s_state[kWavesPerBlock][RPL][kWaveSize * V::kState];
-    __shared__ u32x4_t s_filt[kWavesPerBlock][kWaveSize * V::kFilter];
+    __shared__ u32x4_t s_filt[kFiltVecs];
     const int wave = threadIdx.x / kWaveSize, lane = threadIdx.x % kWaveSize;
-    const int64_t gw = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave;
-    const int64_t lanes_per_row = a.n_lane_per_row / kWaveSize;   // waves per row group
-    const int64_t rg = gw / lanes_per_row;
+    const int64_t ranges = a.n_lane_per_row / kWaveSize;   // 512-channel ranges per row
+    const int64_t cb = blockIdx.x % ranges;
+    const int64_t rg = (blockIdx.x / ranges) * kWavesPerBlock + wave;
     // Uniform over the wave; waves past the end still reach every barrier.
     const bool live = rg < a.n_row_groups;
-    const int64_t cw = (gw % lanes_per_row) * (kWaveSize * VEC);  // the wave's first channel
+    const int64_t cw = cb * (kWaveSize * VEC);  // the block's first channel
     const int64_t b0 = rg * RPL;
 
     const u32x4_t *wq = reinterpret_cast<const u32x4_t *>(
         static_cast<const char *>(a.w) + cw * W * (WF32 ? 4 : 2));
-    u32x4_t wv[V::kFilter], bv[V::kBias], sv[RPL][V::kState], xv[RPL];
+    constexpr int kPerThread = (kFiltVecs + 255) / 256;
+    u32x4_t fv[kPerThread], bv[V::kBias], sv[RPL][V::kState], xv[RPL];
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i)
+        if (threadIdx.x + 256 * i < kFiltVecs) fv[i] = wq[threadIdx.x + 256 * i];
 #pragma unroll
     for (int i = 0; i < V::kBias; ++i) bv[i] = u32x4_t{0u, 0u, 0u, 0u};
     if (live) {
-#pragma unroll
-        for (int i = 0; i < V::kFilter; ++i) wv[i] = wq[lane + kWaveSize * i];
         if constexpr (BIAS) {
             const u32x4_t *bq = reinterpret_cast<const u32x4_t *>(
                 static_cast<const char *>(a.bias) + (cw + lane * VEC) * (WF32 ? 4 : 2));
@@ -1566,8 +1571,11 @@ void k_update_staged(UpdArgs a) {
             xv[r] = *reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(a.x) +
                                                        (b0 + r) * a.x_sb + cw + lane * VEC);
         }
+    }
 #pragma unroll
-        for (int i = 0; i < V::kFilter; ++i) s_filt[wave][lane + kWaveSize * i] = wv[i];
+    for (int i = 0; i < kPerThread; ++i)
+        if (threadIdx.x + 256 * i < kFiltVecs) s_filt[threadIdx.x + 256 * i] = fv[i];
+    if (live) {
 #pragma unroll
         for (int r = 0; r < RPL; ++r) {
             if (b0 + r >= a.B) break;
@@ -1579,8 +1587,9 @@ void k_update_staged(UpdArgs a) {
     float w[W][VEC], bias[VEC];
     u32x4_t nv[RPL][V::kState];
     if (live) {
+        u32x4_t wv[V::kFilter];
 #pragma unroll
-        for (int i = 0; i < V::kFilter; ++i) wv[i] = s_filt[wave][lane * V::kFilter + i];
+        for (int i = 0; i < V::kFilter; ++i) wv[i] = s_filt[lane * V::kFilter + i];
         upd_unpack_filter<W, WF32>(wv, bv, w, bias);
 #pragma unroll
         for (int r = 0; r < RPL; ++r) {
@@ -1611,7 +1620,8 @@ void k_update_staged(UpdArgs a) {
             u32x4_t *sq = reinterpret_cast<u32x4_t *>(static_cast<uint16_t *>(a.state) +
                                                       (b0 + r) * a.s_sb + cw * (W - 1));
 #pragma unroll
-            for (int i = 0; i < V::kState; ++i) sq[lane + kWaveSize * i] = s_state[wave][r][lane + kWaveSize * i];
+            for (int i = 0; i < V::kState; ++i)
+                sq[lane + kWaveSize * i] = s_state[wave][r][lane + kWaveSize * i];
         }
     }
 }

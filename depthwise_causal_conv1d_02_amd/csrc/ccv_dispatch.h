@@ -139,8 +139,9 @@ hipError_t update_dispatch(const UpdArgs &a, int vec, int silu, hipStream_t s) {
                a.B * a.D >= CCV_UPD_STAGED_MIN_BD) {
         // Whole waves per row group (D % 512 == 0) and a large enough batch:
         // the coalesced kernel.
-        const int64_t waves = a.n_row_groups * (a.n_lane_per_row / kWaveSize);
-        const int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+        // A block: one 512-channel range of kWavesPerBlock row groups.
+        const int64_t blocks = (a.n_lane_per_row / kWaveSize) *
+                               ((a.n_row_groups + kWavesPerBlock - 1) / kWavesPerBlock);
 #define CCV_UPD(S, F, B)                                                                      \
         if (!!silu == S && wf32 == F && bias == B)                                            \
             return launch(k_update_staged<W, S, F, B, CCV_UPD_ROWS>, blocks, a, s);
