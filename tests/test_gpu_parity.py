@@ -8,7 +8,7 @@ import torch
 
 import oracle
 from depthwise_causal_conv1d_02_amd import _abi, ops, synth
-from parity import (Guarded, check_bf16, check_exact_bf16, check_f32_rel, f64, guarded_act,
+from parity import (SENTINEL, Guarded, check_bf16, check_exact_bf16, check_f32_rel, f64, guarded_act,
                     guarded_flat)
 
 pytestmark = pytest.mark.gpu
@@ -332,6 +332,37 @@ def test_update_strided_state():
     check_exact_bf16("state", g_state, st)
     check_exact_bf16("untouched", g_big[:, :, 0], f64(big[:, :, 0]))
     check_exact_bf16("untouched", g_big[:, :, 4], f64(big[:, :, 4]))
+
+
+def test_update_staged_row_strided_views():
+    """The coalesced update (D % 512 == 0, above its size threshold) on
+    x, y and state that are row slices of wider buffers: row strides larger
+    than the row, and nothing outside the views written."""
+    gen = torch.Generator().manual_seed(78)
+    B, D, DW = 193, 4096, 4608
+    big_state = synth.state_tensor(gen, B, DW, 4)              # [B,4608,3]
+    w = synth.weight_tensor(gen, D)
+    b = synth.bias_tensor(gen, D, BF16)
+    g_big = dev(big_state)
+    g_state = g_big[:, :D, :]                                   # stride (13824, 3, 1)
+    st = f64(big_state[:, :D, :])
+    for step in range(3):
+        print("staged update on row-strided views, token", step, flush=True)
+        xbig = synth.activation_tensor(gen, B, DW, 1, "tc")[:, :, 0].contiguous()
+        g_xbig = dev(xbig)
+        x = g_xbig[:, :D]                                       # stride (4608, 1)
+        ybig = guarded_flat((B, DW), DEV)
+        y = ybig.view[:, :D]
+        ops.update(x, g_state, dev(w), dev(b), "silu", y=y)
+        torch.cuda.synchronize()
+        oy, st = oracle.update(f64(xbig[:, :D]), st, f64(w), f64(b), "silu")
+        check_bf16("update y", y, oy)
+        check_exact_bf16("conv_state", g_state, st)
+        check_exact_bf16("state outside the view", g_big[:, D:, :], f64(big_state[:, D:, :]))
+        # y's columns past D keep the sentinel
+        outside = ybig.view[:, D:].contiguous().view(torch.int16)
+        assert bool((outside == SENTINEL).all())
+        assert ybig.intact()
 
 
 def test_autograd_wrapper():
