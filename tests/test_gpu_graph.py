@@ -52,12 +52,16 @@ def test_graph_replay_matches_eager():
             assert torch.equal(_bits(v), _bits(ref[k])), (rep, k)
 
 
-def test_graph_decode_loop():
+# (8, 512): the per-lane update kernel; (192, 4096): the coalesced one
+# (786,432 (row, channel) pairs).
+@pytest.mark.parametrize("B,D", [(8, 512), (192, 4096)])
+def test_graph_decode_loop(B, D):
+    print("graph decode loop", B, D, flush=True)
     gen = torch.Generator().manual_seed(801)
-    state0 = synth.state_tensor(gen, 8, 512).to(DEV)
-    w = synth.weight_tensor(gen, 512).to(DEV)
-    b = synth.bias_tensor(gen, 512).to(DEV)
-    xs = torch.randn(16, 8, 512, generator=gen).to(torch.bfloat16).to(DEV)
+    state0 = synth.state_tensor(gen, B, D).to(DEV)
+    w = synth.weight_tensor(gen, D).to(DEV)
+    b = synth.bias_tensor(gen, D).to(DEV)
+    xs = torch.randn(16, B, D, generator=gen).to(torch.bfloat16).to(DEV)
     ys = torch.empty_like(xs)
     state = state0.clone()
     for s in range(16):
