@@ -312,6 +312,20 @@ def rotated_op_times(torch, steps, wl, rounds):
     return res
 
 
+def host_cpu():
+    """The host the oracle baseline ran on: logical CPU count and model name."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "model": model}
+
+
 def cpu_baseline(wl, budget_s=10.0):
     """The fp64 oracle, single-threaded, on a channel sample of the same workload."""
     import oracle
@@ -333,7 +347,8 @@ def cpu_baseline(wl, budget_s=10.0):
         return dict(value=nbytes / dt / 1e9, unit="GB/s", cores=1, kind="oracle",
                     sample="%d decode steps on %d of %d batch rows (all %d channels)"
                            % (steps, nb, B, D),
-                    seconds=dt, token_channels_per_s=steps * nb * D / dt)
+                    seconds=round(dt, 3), token_channels_per_s=round(steps * nb * D / dt, 1),
+                    host=host_cpu())
     x = w["x"]
     B, D, T = x.shape
     cu = w["cu_seqlens"]
@@ -372,7 +387,8 @@ def cpu_baseline(wl, budget_s=10.0):
     return dict(value=nbytes / dt / 1e9, unit="GB/s", cores=1, kind="oracle",
                 sample="fwd%s on channels 0..%d of %d (all %d rows x %d tokens), one thread"
                        % ("+bwd" if has_bwd else "", nch - 1, D, B, T),
-                seconds=round(dt, 3), token_channels_per_s=round(B * nch * T / dt, 1))
+                seconds=round(dt, 3), token_channels_per_s=round(B * nch * T / dt, 1),
+                host=host_cpu())
 
 
 def _kernel_rows(csv_path):
