@@ -194,7 +194,14 @@ __device__ __forceinline__ float act_slope(float z) {
 
 // Block id -> logical tile id such that XCD x (hardware dispatches block i
 // to XCD i % 8) receives one contiguous range of logical tiles.
+#ifndef CCV_XCD_REMAP
+#define CCV_XCD_REMAP 1
+#endif
+#ifndef CCV_BWD_PACKED_TILE_ORDER
+#define CCV_BWD_PACKED_TILE_ORDER 0
+#endif
 __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nb) {
+    if (!CCV_XCD_REMAP) return bid;
     constexpr int64_t X = 8;
     const int64_t q = nb / X, r = nb % X;
     const int64_t x = bid % X, j = bid / X;
@@ -202,9 +209,10 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nb) {
 }
 
 // Logical tile -> (row b, channel block, time block) in the CCV_TILE_ORDER.
+template <int ORDER = CCV_TILE_ORDER>
 __device__ __forceinline__ void decode_tile(int64_t tile, int64_t n_t, int64_t n_c, int64_t &b,
                                             int64_t &cb, int64_t &tb) {
-    if (CCV_TILE_ORDER == 0) {
+    if constexpr (ORDER == 0) {
         tb = tile % n_t;
         cb = (tile / n_t) % n_c;
     } else {
@@ -950,7 +958,10 @@ __global__ __launch_bounds__(256) CCV_BWD_ATTR void k_bwd_chan(BwdArgs a) {
     int32_t *s_cu = reinterpret_cast<int32_t *>(s_buf);
     float (*s_red)[W + 1][CH + 1] = reinterpret_cast<float (*)[W + 1][CH + 1]>(s_buf);
     int64_t b, g, bt;
-    decode_tile(xcd_remap(blockIdx.x, a.n_block), a.n_tblk, a.n_group, b, g, bt);
+    // Packed rows measured faster with time blocks innermost, the others
+    // with channel blocks innermost.
+    decode_tile<PACKED ? CCV_BWD_PACKED_TILE_ORDER : CCV_TILE_ORDER>(
+        xcd_remap(blockIdx.x, a.n_block), a.n_tblk, a.n_group, b, g, bt);
     // The wave index is uniform over the wave; readfirstlane tells the
     // compiler so, which keeps the time bounds and row offsets in scalars.
     // Measured: it frees the registers the seq_idx walk needs, but slows
