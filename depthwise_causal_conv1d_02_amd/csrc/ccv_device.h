@@ -59,6 +59,11 @@ constexpr uint32_t kFirstNonzero = 0x1u, kLastMismatch = 0x2u, kDecreasing = 0x4
 #ifndef CCV_BWD_PIPE
 #define CCV_BWD_PIPE 1
 #endif
+// Interior heads and tails of a backward chunk take a path without the
+// row-edge checks (dinit, final-state term, row end).
+#ifndef CCV_BWD_FAST_EDGES
+#define CCV_BWD_FAST_EDGES 1
+#endif
 // Lower bound on resident waves per SIMD (register budget), measured best:
 // the forward keeps 4 waves, or 3 when it software-pipelines its loads.
 #ifndef CCV_FWD_MIN_WAVES
@@ -779,8 +784,23 @@ __device__ __forceinline__ void bwd_piece(const BwdArgs &a, BwdLane<W, VEC, SILU
         Raw<VEC> rx[U], rd[U];
         load_batch(tau, rx, rd);
         finish_left_halo<W, VEC>(halo, a.init, r, s, ta, c0, xw);
+        if (CCV_BWD_FAST_EDGES && ta > s) {
+            // Interior head (this branch has tb >= ta + W-1 + U): every head
+            // token is in the row and counted, and its dx belongs to the
+            // chunk before, so nothing is emitted.
 #pragma unroll
-        for (int h = 0; h < W - 1; ++h) generic_step(ta + h, hx[h], hd[h]);
+            for (int h = 0; h < W - 1; ++h) {
+                float cur[VEC], dyv[VEC], gcur[VEC];
+                unpack<VEC>(hx[h], cur);
+                unpack<VEC>(hd[h], dyv);
+                grad_step(cur, dyv, gcur, true);
+                shift_in<W, VEC>(xw, cur);
+                shift_g(gcur);
+            }
+        } else {
+#pragma unroll
+            for (int h = 0; h < W - 1; ++h) generic_step(ta + h, hx[h], hd[h]);
+        }
         body_batch(tau, rx, rd);
         tau += U;
     } else {
@@ -829,9 +849,26 @@ __device__ __forceinline__ void bwd_piece(const BwdArgs &a, BwdLane<W, VEC, SILU
         const int64_t tt = tb > ta + (W - 1) ? tb : ta + (W - 1);
         Raw<VEC> rx[W - 1], rd[W - 1];
         load_steps(tt, rx, rd);
+        if (CCV_BWD_FAST_EDGES && tb >= ta + (W - 1) && tb + (W - 1) <= e) {
+            // Interior tail: the W-1 right-halo tokens are in the row and not
+            // counted, and the dx they complete (p < tb) carry no
+            // final-state term (p < e - (W-1)).
 #pragma unroll
-        for (int h = 0; h < W - 1; ++h)
-            if (tt + h < tb + (W - 1)) generic_step(tt + h, rx[h], rd[h]);
+            for (int h = 0; h < W - 1; ++h) {
+                float cur[VEC], dyv[VEC], gcur[VEC], v[VEC];
+                unpack<VEC>(rx[h], cur);
+                unpack<VEC>(rd[h], dyv);
+                grad_step(cur, dyv, gcur, false);
+                shift_in<W, VEC>(xw, cur);
+                emit_value(gcur, v);
+                store_vec<VEC, true>(dxb + (tb + h - (W - 1)) * ds_t, ds_d, v);
+                shift_g(gcur);
+            }
+        } else {
+#pragma unroll
+            for (int h = 0; h < W - 1; ++h)
+                if (tt + h < tb + (W - 1)) generic_step(tt + h, rx[h], rd[h]);
+        }
     }
 }
 
