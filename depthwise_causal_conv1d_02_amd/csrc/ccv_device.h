@@ -45,13 +45,17 @@ constexpr uint32_t kFirstNonzero = 0x1u, kLastMismatch = 0x2u, kDecreasing = 0x4
 #ifndef CCV_BWD_UNROLL
 #define CCV_BWD_UNROLL 4
 #endif
-// Measured per row mode: packed rows do best with batches of 2 (their
-// pieces restart often), seq_idx rows (not software-pipelined) with 8.
+// Measured per row mode: packed rows do best with batches of 2, seq_idx
+// rows with software-pipelined batches of 4 (1.2% faster than unpipelined
+// batches of 8; pipelined batches of 8 spill).
 #ifndef CCV_BWD_UNROLL_PACKED
 #define CCV_BWD_UNROLL_PACKED 2
 #endif
 #ifndef CCV_BWD_UNROLL_SEQ
-#define CCV_BWD_UNROLL_SEQ 8
+#define CCV_BWD_UNROLL_SEQ 4
+#endif
+#ifndef CCV_BWD_SEQ_PIPE
+#define CCV_BWD_SEQ_PIPE 1
 #endif
 #ifndef CCV_TC_BWD_WAVES
 #define CCV_TC_BWD_WAVES 6      // time-lane backward: waves per SIMD it must fit (8: 2.5% slower on 200 MB)
@@ -966,17 +970,48 @@ __device__ __forceinline__ void bwd_seq_piece(const BwdArgs &a, BwdLane<W, VEC, 
     const int64_t head_end = ta + (W - 1) < end ? ta + (W - 1) : end;
     int64_t tau = ta;
     for (; tau < head_end; ++tau) generic(tau);
-    for (; tau + U <= tb; tau += U) {
-        Raw<VEC> rx[U], rd[U];
-        int32_t ids[U];
+    auto load_seq_batch = [&](int64_t t, Raw<VEC> (&rx)[U], Raw<VEC> (&rd)[U],
+                              int32_t (&ids)[U]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            rx[u] = load_raw<VEC, NTL>(xb + (tau + u) * xs_t, xs_d);
-            rd[u] = load_raw<VEC, NTL>(dyb + (tau + u) * ys_t, ys_d);
-            ids[u] = sq[(tau + u) * st];
+            rx[u] = load_raw<VEC, NTL>(xb + (t + u) * xs_t, xs_d);
+            rd[u] = load_raw<VEC, NTL>(dyb + (t + u) * ys_t, ys_d);
+            ids[u] = sq[(t + u) * st];
         }
+    };
+    if constexpr (CCV_BWD_SEQ_PIPE) {
+        // The next batch's loads are in flight while the current one computes.
+        if (tau + U <= tb) {
+            Raw<VEC> rx[U], rd[U];
+            int32_t ids[U];
+            load_seq_batch(tau, rx, rd, ids);
+            for (; tau + 2 * U <= tb; tau += U) {
+                Raw<VEC> nx[U], nd[U];
+                int32_t nids[U];
+                load_seq_batch(tau + U, nx, nd, nids);
 #pragma unroll
-        for (int u = 0; u < U; ++u) step(tau + u, rx[u], rd[u], ids[u], true, true, true, true);
+                for (int u = 0; u < U; ++u)
+                    step(tau + u, rx[u], rd[u], ids[u], true, true, true, true);
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    rx[u] = nx[u];
+                    rd[u] = nd[u];
+                    ids[u] = nids[u];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) step(tau + u, rx[u], rd[u], ids[u], true, true, true, true);
+            tau += U;
+        }
+    } else {
+        for (; tau + U <= tb; tau += U) {
+            Raw<VEC> rx[U], rd[U];
+            int32_t ids[U];
+            load_seq_batch(tau, rx, rd, ids);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                step(tau + u, rx[u], rd[u], ids[u], true, true, true, true);
+        }
     }
     for (; tau < end; ++tau) generic(tau);
 }
