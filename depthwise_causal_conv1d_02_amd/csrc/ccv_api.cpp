@@ -584,7 +584,7 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     if (rc != CCV_OK) return rc;
     if (use_partials) {
         rc = hip_status(ccv::launch_dw_reduce(a.partial, n_part, p.D, static_cast<int>(p.W),
-                                              static_cast<int>(kp), a.dw, a.db, stream));
+                                              static_cast<int>(kp), a.dw, a.db, a.err, stream));
         if (rc != CCV_OK) return rc;
     }
     return status;

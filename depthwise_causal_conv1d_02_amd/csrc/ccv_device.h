@@ -1836,11 +1836,23 @@ __global__ __launch_bounds__(256) void k_validate(const int32_t *cu, int64_t n_s
 // group q sums p = q, q+16, q+32, ... in increasing p, then the 16 group sums
 // are added in increasing q.  The order depends on P only, never on
 // scheduling, so the result is the same bits run to run.
+//
+// `err` is the packed call's flag word (nullptr for dense rows).  When it is
+// non-zero the backward blocks wrote no partials, so the reduction adds
+// nothing either: dweight and dbias keep their values.  The word is read once
+// per block and shared through LDS, so the whole block takes one branch.
 __global__ __launch_bounds__(256) void k_dw_reduce(const float *part, int64_t n_part,
                                                    int64_t n_ch, int w, int kp, float *dw,
-                                                   float *db) {
+                                                   float *db, const uint32_t *err) {
     constexpr int kAcc = 4, kGroups = kWavesPerBlock * kAcc;
     __shared__ float s_acc[kGroups][kWaveSize];
+    __shared__ uint32_t s_err;
+    if (err != nullptr) {
+        if (threadIdx.x == 0)
+            s_err = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (s_err != 0u) return;  // uniform over the block
+    }
     const int lane = threadIdx.x % kWaveSize, wave = threadIdx.x / kWaveSize;
     const int64_t n_elem = n_ch * kp;
     const int64_t e = static_cast<int64_t>(blockIdx.x) * kWaveSize + lane;

@@ -125,8 +125,10 @@ int64_t fwd_resident_blocks(const FwdArgs &a, int vec, int silu, int rows);
 int64_t bwd_resident_blocks(const BwdArgs &a, int vec, int silu, int rows);
 hipError_t launch_validate(const int32_t *cu, int64_t n_seq, int64_t total, uint32_t *flags,
                            int overwrite, hipStream_t s);
+// `err`: the packed call's flag word, or nullptr; a non-zero word skips the
+// reduction (the backward wrote no partials).
 hipError_t launch_dw_reduce(const float *partial, int64_t n_part, int64_t n_ch, int w, int kp,
-                            float *dw, float *db, hipStream_t s);
+                            float *dw, float *db, const uint32_t *err, hipStream_t s);
 int64_t resident_blocks(const void *kernel, unsigned dyn_lds);
 
 // Per-width kernel selection (ccv_width.hip, built once per width).  With

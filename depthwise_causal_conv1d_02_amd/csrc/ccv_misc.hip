@@ -77,10 +77,10 @@ hipError_t launch_validate(const int32_t *cu, int64_t n_seq, int64_t total, uint
 }
 
 hipError_t launch_dw_reduce(const float *partial, int64_t n_part, int64_t n_ch, int w, int kp,
-                            float *dw, float *db, hipStream_t s) {
+                            float *dw, float *db, const uint32_t *err, hipStream_t s) {
     const int64_t blocks = (n_ch * kp + kWaveSize - 1) / kWaveSize;  // 64 elements per block
     hipLaunchKernelGGL(k_dw_reduce, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, partial,
-                       n_part, n_ch, w, kp, dw, db);
+                       n_part, n_ch, w, kp, dw, db, err);
     return hipGetLastError();
 }
 

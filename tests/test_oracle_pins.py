@@ -422,6 +422,25 @@ def test_O11_flags_brute_force():
     assert n == 5 * (7 ** 2 + 7 ** 3 + 7 ** 4)
 
 
+FLAG_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "cu_seqlens_flags.json")
+
+
+def test_O11_flags_hand_worked_table():
+    """The oracle's flag word against a table worked by hand from the four
+    malformed-metadata conditions of the cuDNN FE 'Causal Conv1d' page's
+    device-side validation paragraph (tests/golden/cu_seqlens_flags.json):
+    each condition alone, on several positions, and in combination."""
+    table = json.load(open(FLAG_GOLDEN))["cases"]
+    seen = 0
+    for row in table:
+        got = oracle.validate_cu_seqlens(row["cu"], row["total"])
+        assert got == row["flags"], (row, got)
+        seen |= row["flags"]
+    # every bit is exercised alone and the table holds the all-bits case
+    singles = {row["flags"] for row in table}
+    assert {1, 2, 4, 8, 15} <= singles and seen == 15
+
+
 # ---------------------------------------------------------------------------
 # O12 per-token sequence ids (seq_idx)
 # ---------------------------------------------------------------------------
@@ -573,6 +592,13 @@ MUTANTS = [
     ("update keeps the oldest token", "s[k] = v[k + 1];", "s[k] = v[k];"),
     ("equal offsets counted as decreasing",
      "if (cu[i + 1] < cu[i])", "if (cu[i + 1] <= cu[i])"),
+    ("first offset checked for negatives only", "if (cu[0] != 0)", "if (cu[0] < 0)"),
+    ("last offset read one early",
+     "if ((int64_t)cu[N] != total)", "if ((int64_t)cu[N - 1] != total)"),
+    ("empty sequences missed", "if (cu[i + 1] == cu[i])", "if (0)"),
+    ("first offset pair skipped",
+     "for (int64_t i = 0; i < N; ++i) {\n        if (cu[i + 1] < cu[i])",
+     "for (int64_t i = 1; i < N; ++i) {\n        if (cu[i + 1] < cu[i])"),
     ("dW uses the wrong tap",
      "dw[d * W + k] += g * x_ext(x, init, b, d, t - (W - 1) + k, row, D, T, W);",
      "dw[d * W + k] += g * x_ext(x, init, b, d, t - k, row, D, T, W);"),
@@ -603,6 +629,7 @@ PIN_BATTERY = [
     lambda: test_O3_packed_equals_dense([1, 2, 3, 5, 8], True),
     lambda: test_O4_update_steps_reproduce_forward(2, True),
     test_O11_flags_brute_force,
+    test_O11_flags_hand_worked_table,
     lambda: test_O12_contiguous_runs_are_the_packed_route([1, 2, 3, 5, 8]),
     lambda: test_O12_periodic_ids_reduce_to_a_sparse_filter(2, 4),
     lambda: test_O12_finite_differences_recurring_ids("silu"),
