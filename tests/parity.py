@@ -86,6 +86,29 @@ def check_f32_rel(name, g, o, rel=F32_REL):
                              % (name, len(bad), ok.size, rel, idx, gv[idx], o[idx]))
 
 
+def check_cast_bf16(name, g, o, rel=F32_REL):
+    """Parameter gradients handed back in BF16: the FP32 result (held to
+    check_f32_rel's bound) rounded to nearest even.  A value passes if it is
+    within one BF16 step of RNE(o) in ordinal order, or if it is within the
+    FP32 bound plus the cast's own rounding (half a BF16 step at g), which is
+    what entries much smaller than rms(o) can need."""
+    o = np.asarray(o, dtype=np.float64)
+    assert tuple(g.shape) == o.shape, (name, tuple(g.shape), o.shape)
+    assert g.dtype == torch.bfloat16, (name, g.dtype)
+    gv = g.detach().cpu().double().numpy()
+    rb = bf16_bits(torch.from_numpy(bf16_rne(o)).to(torch.bfloat16))
+    near = np.abs(bf16_ord(bf16_bits(g)) - bf16_ord(rb)) <= 1
+    rms = float(np.sqrt(np.mean(o * o))) if o.size else 0.0
+    half_step = np.ldexp(1.0, np.frexp(np.abs(gv))[1] - 9)
+    close = np.abs(gv - o) <= rel * np.maximum(np.abs(o), rms) + half_step
+    ok = near | close
+    if not ok.all():
+        bad = np.argwhere(~ok)
+        idx = tuple(bad[0])
+        raise AssertionError("%s: %d of %d BF16 gradients out of tolerance; first at %s: "
+                             "gpu=%r oracle=%r" % (name, len(bad), ok.size, idx, gv[idx], o[idx]))
+
+
 def f64(t):
     return None if t is None else t.detach().cpu().double().numpy()
 

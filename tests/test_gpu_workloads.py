@@ -1,26 +1,46 @@
 """Full-size parity of the five named workloads, in the launch configuration
 the benchmark times (the same calls, the same shapes and layouts).
 
-Channels are independent, so the oracle runs on a sample of channels (all
-rows and tokens of each); the sample covers both ends of every channel
-group boundary that the kernels use (groups of 512 channels).  The decode
-workload is compared in full, step by step.
+* Every output buffer starts filled with a sentinel (a BF16 NaN pattern no
+  finite input produces), so an element no launch wrote is caught anywhere
+  in the tensor, not only where the oracle is consulted.
+* The dense and packed workloads are compared with the oracle on every
+  channel: channels are independent, so the oracle runs over channel slices
+  in a thread pool (ctypes and numpy release the GIL).
+* The large workload is compared on a channel sample holding at least one
+  channel of every 256-channel group (the backward's channel groups; the
+  forward's are 512 wide), at an offset that changes from group to group,
+  plus both sides of the group edges at the ends and the middle.
+* The decode workload is compared in full, every one of its 64 steps.
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from depthwise_causal_conv1d_02_amd import ops, synth
-from parity import check_bf16, check_exact_bf16, check_f32_rel
+from parity import SENTINEL, check_bf16, check_exact_bf16, check_f32_rel
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda", 0)
 
 
-def sample_channels(D):
-    cand = [0, 1, 7, 8, 511, 512, 513, D // 2, D - 513, D - 512, D - 9, D - 8, D - 1]
-    return sorted({c for c in cand if 0 <= c < D})
+def sample_channels(D, group=256):
+    cand = {0, 1, 7, 8, 255, 256, 511, 512, 513, D // 2 - 1, D // 2, D - 513, D - 512, D - 257,
+            D - 256, D - 9, D - 8, D - 1}
+    for gi in range((D + group - 1) // group):
+        cand.add(gi * group + (gi * 37 + 3) % group)
+    return sorted(c for c in cand if 0 <= c < D)
+
+
+def test_sample_reaches_every_channel_group():
+    for D in (4096, 5120, 8192):
+        sel = sample_channels(D)
+        for group in (256, 512):
+            assert {c // group for c in sel} == set(range(D // group)), (D, group)
 
 
 def f(t):
@@ -33,6 +53,27 @@ def sub(t, sel):
     return t[:, sel] if t.dim() == 3 else t[sel]
 
 
+def n_workers():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 4
+    return max(1, min(16, n))
+
+
+def sentinel_like(t):
+    """An uninitialised-looking output with t's strides, every element the sentinel."""
+    out = torch.empty_like(t)
+    assert out.stride() == t.stride()
+    out.view(torch.int16).fill_(np.int16(SENTINEL))
+    return out
+
+
+def no_sentinel(name, t):
+    left = int((t.view(torch.int16) == np.int16(SENTINEL)).sum().item())
+    assert left == 0, "%s: %d elements never written" % (name, left)
+
+
 def run_workload(idx):
     w = synth.workload(idx)
     g = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in w.items()}
@@ -42,24 +83,37 @@ def run_workload(idx):
     R = B if w["cu_seqlens"] is None else w["cu_seqlens"].numel() - 1
     flag = torch.zeros(1, dtype=torch.int32, device=DEV)
     seq = g.get("seq_idx")
-    y, fin = ops.fwd(x, g["weight"], g["bias"], g["cu_seqlens"], g["initial_states"],
-                     g["activation"], return_final_states=w["return_final_states"], err_flag=flag,
-                     seq_idx=seq)
+    y = sentinel_like(x)
+    fin = None
+    if w["return_final_states"]:
+        fin = torch.empty(R, D, 3, dtype=x.dtype, device=DEV)
+        fin.view(torch.int16).fill_(np.int16(SENTINEL))
+    print("workload %d: forward" % idx, flush=True)
+    ops.fwd(x, g["weight"], g["bias"], g["cu_seqlens"], g["initial_states"], g["activation"],
+            final_states_out=fin, y=y, err_flag=flag, seq_idx=seq)
     out = {"y": y, "fin": fin}
     if g["dy"] is not None:
-        dx, dw, db, dinit = ops.bwd(x, g["weight"], g["dy"], g["bias"], g["cu_seqlens"],
-                                    g["initial_states"], None, g["activation"], g["deterministic"],
-                                    False, err_flag=flag, seq_idx=seq)
+        dx = sentinel_like(x)
+        dinit = None
+        if g["initial_states"] is not None:
+            dinit = sentinel_like(g["initial_states"])
+        print("workload %d: backward" % idx, flush=True)
+        _, dw, db, _ = ops.bwd(x, g["weight"], g["dy"], g["bias"], g["cu_seqlens"],
+                               g["initial_states"], None, g["activation"], g["deterministic"],
+                               False, dx=dx, err_flag=flag, seq_idx=seq, dinit=dinit)
         out.update(dx=dx, dw=dw, db=db, dinit=dinit)
     torch.cuda.synchronize()
     assert int(flag.item()) == 0
+    for name in ("y", "fin", "dx", "dinit"):
+        if out.get(name) is not None:
+            no_sentinel(name, out[name])
     return w, g, out
 
 
 def check_sample(w, out):
     D = w["x"].shape[1]
     sel = sample_channels(D)
-    print("sampled channels", sel, flush=True)
+    print("sampled channels (%d)" % len(sel), sel, flush=True)
     cu = None if w["cu_seqlens"] is None else w["cu_seqlens"].numpy()
     xs, ws, bs = f(sub(w["x"], sel)), f(sub(w["weight"], sel)), f(sub(w["bias"], sel))
     init = f(sub(w["initial_states"], sel))
@@ -76,7 +130,44 @@ def check_sample(w, out):
             check_f32_rel("dbias", out["db"][sel], odb)
         if odinit is not None:
             check_bf16("dinitial_states", out["dinit"][:, sel], odinit)
-    return oy
+
+
+def check_full(w, out, step):
+    """Every channel against the oracle, `step` channels per worker task."""
+    D = w["x"].shape[1]
+    cu = None if w["cu_seqlens"] is None else w["cu_seqlens"].numpy()
+    host = {k: (None if v is None else v.cpu()) for k, v in out.items()}
+    has_bwd = w["dy"] is not None
+    odw = np.zeros((D, w["weight"].shape[1])) if has_bwd else None
+    odb = np.zeros(D) if has_bwd and w["bias"] is not None else None
+
+    def job(c0):
+        sel = slice(c0, min(D, c0 + step))
+        xs, ws, bs = f(sub(w["x"], sel)), f(sub(w["weight"], sel)), f(sub(w["bias"], sel))
+        init = f(sub(w["initial_states"], sel))
+        oy, ofin = oracle.fwd(xs, ws, bs, cu, init, w["activation"])
+        check_bf16("y[:, %d:%d]" % (sel.start, sel.stop), host["y"][:, sel], oy)
+        if host["fin"] is not None:
+            check_exact_bf16("final_states", host["fin"][:, sel], ofin)
+        if not has_bwd:
+            return c0, None, None
+        gdx, gw, gb, gi = oracle.bwd(xs, ws, f(sub(w["dy"], sel)), bs, cu, init, None,
+                                     w["activation"])
+        check_bf16("dx[:, %d:%d]" % (sel.start, sel.stop), host["dx"][:, sel], gdx)
+        if gi is not None:
+            check_bf16("dinitial_states", host["dinit"][:, sel], gi)
+        return c0, gw, gb
+
+    with ThreadPoolExecutor(n_workers()) as ex:
+        for c0, gw, gb in ex.map(job, range(0, D, step)):
+            if gw is not None:
+                odw[c0:c0 + gw.shape[0]] = gw
+            if gb is not None:
+                odb[c0:c0 + gb.shape[0]] = gb
+    if has_bwd:
+        check_f32_rel("dweight", host["dw"], odw)
+        if odb is not None:
+            check_f32_rel("dbias", host["db"], odb)
 
 
 def test_workload_1_tiny_dense_fwd_full():
@@ -87,10 +178,10 @@ def test_workload_1_tiny_dense_fwd_full():
     assert out["fin"].shape == (1, 64, 3)
 
 
-def test_workload_2_dense_fwd_bwd_update():
+def test_workload_2_dense_fwd_bwd_update_full():
     w, g, out = run_workload(2)
-    check_sample(w, out)
-    # decode one token from the returned final states, as the benchmark does
+    check_full(w, out, 256)
+    # decode one token from the returned final states, as a decode loop would
     state = out["fin"].clone()
     xt = g["x"][:, :, -1].contiguous()
     yt = ops.update(xt, state, g["weight"], g["bias"], "silu")
@@ -101,10 +192,10 @@ def test_workload_2_dense_fwd_bwd_update():
     check_exact_bf16("update state", state, ost)
 
 
-def test_workload_3_packed_fwd_bwd():
+def test_workload_3_packed_fwd_bwd_full():
     w, g, out = run_workload(3)
     assert w["cu_seqlens"].numel() == 17 and int(w["cu_seqlens"][-1]) == 33280
-    check_sample(w, out)
+    check_full(w, out, 64)
 
 
 def test_workload_4_decode_64_steps_full():
@@ -112,16 +203,18 @@ def test_workload_4_decode_64_steps_full():
     state = w["conv_state"].to(DEV)
     wt, bt = w["weight"].to(DEV), w["bias"].to(DEV)
     xs = w["x_steps"].to(DEV)
+    ys = torch.empty_like(xs)
+    ys.view(torch.int16).fill_(np.int16(SENTINEL))
+    for s in range(xs.shape[0]):
+        ops.update(xs[s], state, wt, bt, "silu", y=ys[s])
+    torch.cuda.synchronize()
+    no_sentinel("y (64 steps)", ys)
+    host = ys.cpu()
     ost = f(w["conv_state"])
     wf, bf = f(w["weight"]), f(w["bias"])
-    y = torch.empty_like(xs[0])
     for s in range(xs.shape[0]):
-        ops.update(xs[s], state, wt, bt, "silu", y=y)
         oy, ost = oracle.update(f(w["x_steps"][s]), ost, wf, bf, "silu")
-        if s % 16 == 0 or s == xs.shape[0] - 1:
-            torch.cuda.synchronize()
-            check_bf16("update y step %d" % s, y, oy)
-    torch.cuda.synchronize()
+        check_bf16("update y step %d" % s, host[s], oy)
     check_exact_bf16("conv_state after 64 steps", state, ost)
 
 
@@ -136,6 +229,7 @@ def test_workload_5_large_deterministic():
                               True, False, dx=dx)
         torch.cuda.synchronize()
         assert torch.equal(dw.view(torch.int32), ref)
+    assert torch.equal(dx.view(torch.int16), out["dx"].view(torch.int16))
 
 
 def test_workload_6_seq_idx_fwd_bwd():
