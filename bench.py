@@ -1,23 +1,30 @@
 #!/usr/bin/env python3
 """Achieved HBM GB/s of the depthwise causal conv1d (fwd, bwd, update) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense|packed|decode|large|tiny]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 One step is one pass of the whole hot path over one batch of seeded synthetic
 input already resident in HBM:
 
-  dense  (default)  B=4 D=4096 T=2048, [B,T,D] storage behind a transpose view,
-                    BF16 weight + bias, initial states, SiLU:
-                    forward (returns final states) + backward (FP32 atomics,
-                    dinit) + one decode update from the final states.
+  large_decode (default)
+                    the largest one-GPU workload and the decode workload:
+                    B=8 D=8192 T=8192, [B,T,D] storage behind a transpose
+                    view, BF16 weight, no bias, SiLU: forward + backward with
+                    the deterministic (fixed-order) dweight; then the decode
+                    update B=256 D=8192, 64 single-token steps, BF16 weight +
+                    bias, SiLU, state mutated in place.  The dense and packed
+                    workloads' ops are timed after it and reported beside it.
+  dense             B=4 D=4096 T=2048, channel-last, BF16 weight + bias,
+                    initial states, SiLU: forward (returns final states) +
+                    backward (FP32 atomics, dinit).
   packed            16 sequences, T=33,280, D=5120, FP32 weight, no bias,
                     initial states: forward + backward.
-  decode            B=256 D=8192 single-token update; a step is one token
-                    (the 64 seeded tokens are cycled).
+  decode            B=256 D=8192 update; a step is the 64 seeded tokens.
   large             B=8 D=8192 T=8192, no bias: forward + deterministic backward.
   tiny              B=1 D=64 T=128 [B,D,T]: forward (launch-bound).
   seqidx            the dense shape with sequences of U[64,1024] tokens per row
                     marked by seq_idx (no states): forward + backward.
+  dense_tc, large_tc  the dense / large data in [B,D,T] time-contiguous storage.
 
 The value is algorithmic bytes (every compulsory input read once, every output
 written once) per step divided by the wall time per step.  Per-op times come
@@ -50,6 +57,15 @@ OP_KERNEL_TIME = {"fwd": "k_fwd_tc", "bwd": "k_bwd_tc", "update": "k_update"}
 def op_kernels(workload):
     """op -> kernel name prefix of a workload (time-lane kernels for *_tc)."""
     return OP_KERNEL_TIME if workload.endswith("_tc") else OP_KERNEL
+
+
+def profile_workload(workload, op):
+    """The workload name a committed profile of `op` is filed under (the
+    combined default workload runs the large workload's forward and backward
+    and the decode workload's update)."""
+    if workload == "large_decode":
+        return "decode" if op == "update" else "large"
+    return workload
 
 
 def source_hash():
@@ -111,6 +127,18 @@ class Workload:
         # "<workload>_tc": the same data in [B,D,T] storage (unit time stride)
         self.kind = name[:-3] if name.endswith("_tc") else name
         to = lambda t: None if t is None else t.to(dev)
+        if self.kind == "large_decode":
+            # the large workload's forward and backward, then the decode
+            # workload's 64 tokens, as one step
+            self.large = Workload("large", dev)
+            self.decode = Workload("decode", dev)
+            self.cpu, self.g = self.large.cpu, self.large.g
+            self.shape = dict(self.large.shape, decode_B=self.decode.shape["B"],
+                              decode_tokens=self.decode.shape["tokens"])
+            self.bytes = dict(self.large.bytes, update=self.decode.bytes["update"])
+            self.counts = dict(self.large.counts, update=self.decode.counts["update"])
+            self.desc = ("%s; then %s" % (self.large.desc, self.decode.desc))
+            return
         idx = {"tiny": 1, "dense": 2, "packed": 3, "decode": 4, "large": 5,
                "seqidx": 6}[self.kind]
         self.cpu = synth.workload(idx)
@@ -143,8 +171,6 @@ class Workload:
                       + seq}
         if w["dy"] is not None:
             self.bytes["bwd"] = bwd_bytes(B, D, T, R, init, False, wb, bias) + seq
-        if self.kind == "dense":
-            self.bytes["update"] = update_bytes(B, D, 2, bias)
         self.counts = {k: 1 for k in self.bytes}
         self.desc = synth.WORKLOADS[idx]
         if name.endswith("_tc"):
@@ -153,11 +179,22 @@ class Workload:
     def step_bytes(self):
         return sum(self.bytes[k] * self.counts[k] for k in self.bytes)
 
+    def token_channels(self):
+        """(token, channel) pairs one step processes."""
+        if self.kind == "large_decode":
+            return self.large.token_channels() + self.decode.token_channels()
+        sh = self.shape
+        return sh["B"] * sh["D"] * (sh["tokens"] if self.kind == "decode" else sh["T"])
+
     def clone(self):
         """The same workload on fresh device copies of its tensors (strides
         kept), for timing with operands that are not in any cache."""
         import copy
         c = copy.copy(self)
+        if self.kind == "large_decode":
+            c.large, c.decode = self.large.clone(), self.decode.clone()
+            c.g = c.large.g
+            return c
         c.g = {k: (v.clone() if getattr(v, "is_cuda", False) else v) for k, v in self.g.items()}
         return c
 
@@ -172,9 +209,10 @@ class Step:
     """One pass of the hot path: the ops of a step, run in order on the
     current stream."""
 
-    def __init__(self, ops, outputs):
+    def __init__(self, ops, outputs, flags):
         self.ops = ops            # [(op name, callable)]
         self.outputs = outputs
+        self.flags = flags        # cu_seqlens flag words of packed calls
 
     def __call__(self, ev):
         for name, fn in self.ops:
@@ -188,6 +226,10 @@ def make_step(wl, torch):
     from depthwise_causal_conv1d_02_amd import ops
 
     g, dev = wl.g, wl.dev
+    if wl.kind == "large_decode":
+        big, dec = make_step(wl.large, torch), make_step(wl.decode, torch)
+        outputs = dict(big.outputs, decode_y=dec.outputs["y"])
+        return Step(big.ops + dec.ops, outputs, big.flags + dec.flags)
     if wl.kind == "decode":
         states = [g["conv_state"].clone() for _ in range(DECODE_STATES)]
         xs = g["x_steps"]
@@ -198,12 +240,12 @@ def make_step(wl, torch):
                                                      g["weight"], g["bias"], g["activation"],
                                                      y=ys[s])))
                  for s in range(xs.shape[0])]
-        return Step(calls, {"y": ys})
+        return Step(calls, {"y": ys}, [])
 
     x = g["x"]
     y = torch.empty_like(x)
     fin = None
-    if g["return_final_states"] or wl.kind == "dense":
+    if g["return_final_states"]:
         fin = torch.empty(wl.shape["R"], x.shape[1], 3, dtype=x.dtype, device=dev)
     flag = torch.zeros(1, dtype=torch.int32, device=dev)
     seq = g.get("seq_idx")
@@ -227,14 +269,7 @@ def make_step(wl, torch):
                                              workspace=ws, dweight=dw, dbias=db, dinit=dinit,
                                              seq_idx=seq)))
         outputs.update(dx=dx, dw=dw)
-    if wl.kind == "dense":
-        # decode the next token straight from the returned final states
-        # (updated in place; the next step's forward rewrites them)
-        xt = g["x"][:, :, -1].contiguous()
-        yt = torch.empty_like(xt)
-        calls.append(("update", lambda: ops.update(xt, fin, g["weight"], g["bias"],
-                                                   g["activation"], y=yt)))
-    return Step(calls, outputs)
+    return Step(calls, outputs, [flag] if g["cu_seqlens"] is not None else [])
 
 
 class Events:
@@ -312,6 +347,60 @@ def rotated_op_times(torch, steps, wl, rounds):
     return res
 
 
+def check_flags(steps):
+    """Packed calls report malformed offsets through their flag word, and a
+    set word makes every later packed launch return early; a timing taken
+    with one set would not be a timing of the op."""
+    for st in steps:
+        for fl in st.flags:
+            v = int(fl.item())
+            if v:
+                raise RuntimeError("cu_seqlens flag word is %#x: the packed launches did no work"
+                                   % v)
+
+
+def op_kernel_label(wl, op):
+    """The kernels one launch of `op` runs (the deterministic backward adds
+    the fixed-order reduction of its partials)."""
+    k = op_kernels(wl.name)[op]
+    w = wl.large.cpu if wl.kind == "large_decode" else wl.cpu
+    if op == "bwd" and w.get("deterministic"):
+        k += " + k_dw_reduce"
+    return k
+
+
+def per_op_entry(wl, name, t, n_rot):
+    gbs = wl.bytes[name] / (t * 1e-3) / 1e9
+    return {"ms": round(t, 5), "algorithmic_bytes": wl.bytes[name],
+            "launches_per_step": wl.counts[name], "kernels": op_kernel_label(wl, name),
+            "GB_s": round(gbs, 1), "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "timing": "cold (rotating over %d operand copies)" % n_rot}
+
+
+def other_config_ops(torch, dev, names, reps):
+    """Cold per-op times of other workloads (their own operand copies), in
+    the same run: the dense and packed configurations' forward and backward."""
+    res = {}
+    for name in names:
+        print("bench: per-op times of workload %s" % name, file=sys.stderr, flush=True)
+        wl = Workload(name, dev)
+        n_rot = rotation_count(wl)
+        wls = [wl] + [wl.clone() for _ in range(n_rot - 1)]
+        steps = [make_step(w, torch) for w in wls]
+        quiet = Events(torch, False)
+        for st in steps:
+            st(quiet)
+        torch.cuda.synchronize()
+        cold = rotated_op_times(torch, steps, wl, reps)
+        check_flags(steps)
+        res[name] = {"workload": wl.desc,
+                     "ops": {k: per_op_entry(wl, k, t, n_rot) for k, t in cold.items()}}
+        del steps, wls, wl
+        torch.cuda.empty_cache()
+    return res
+
+
 def host_cpu():
     """The host the oracle baseline ran on: logical CPU count and model name."""
     model = None
@@ -326,29 +415,49 @@ def host_cpu():
     return {"nproc": os.cpu_count(), "model": model}
 
 
-def cpu_baseline(wl, budget_s=10.0):
-    """The fp64 oracle, single-threaded, on a channel sample of the same workload."""
-    import oracle
+class _OneCore:
+    """Pin the calling thread to one CPU for the duration (the oracle is
+    single-threaded C; pinning keeps the scheduler from moving it)."""
 
+    def __enter__(self):
+        self.prev = None
+        self.cpu = None
+        if hasattr(os, "sched_setaffinity"):
+            self.prev = os.sched_getaffinity(0)
+            self.cpu = min(self.prev)
+            os.sched_setaffinity(0, {self.cpu})
+        return self
+
+    def __exit__(self, *exc):
+        if self.prev is not None:
+            os.sched_setaffinity(0, self.prev)
+        return False
+
+
+def _oracle_decode(wl, budget_s):
+    """Oracle decode steps over every batch row, until the 64 tokens are done
+    or the budget is spent: (seconds, bytes, steps, rows)."""
+    import oracle
     w = wl.cpu
     f = lambda t: None if t is None else t.double().numpy()
-    if wl.kind == "decode":
-        B, D = w["conv_state"].shape[:2]
-        nb = B          # every row: the whole decode workload is about a second of oracle time
-        st = f(w["conv_state"][:nb])
-        t0 = time.perf_counter()
-        steps = 0
-        while steps < 64 and time.perf_counter() - t0 < budget_s:
-            _, st = oracle.update(f(w["x_steps"][steps][:nb]), st, f(w["weight"]), f(w["bias"]),
-                                  "silu")
-            steps += 1
-        dt = time.perf_counter() - t0
-        nbytes = steps * update_bytes(nb, D, 2, True)
-        return dict(value=nbytes / dt / 1e9, unit="GB/s", cores=1, kind="oracle",
-                    sample="%d decode steps on %d of %d batch rows (all %d channels)"
-                           % (steps, nb, B, D),
-                    seconds=round(dt, 3), token_channels_per_s=round(steps * nb * D / dt, 1),
-                    host=host_cpu())
+    B, D = w["conv_state"].shape[:2]
+    st = f(w["conv_state"])
+    t0 = time.perf_counter()
+    steps = 0
+    while steps < w["x_steps"].shape[0] and time.perf_counter() - t0 < budget_s:
+        _, st = oracle.update(f(w["x_steps"][steps]), st, f(w["weight"]), f(w["bias"]), "silu")
+        steps += 1
+    dt = time.perf_counter() - t0
+    return dt, steps * update_bytes(B, D, 2, True), steps, B, D
+
+
+def _oracle_rows(wl, budget_s):
+    """Oracle forward (+ backward) of a workload on a leading block of
+    channels (all rows and tokens), sized by a short pilot to about
+    `budget_s` seconds: (seconds, bytes, channels, D, has_bwd)."""
+    import oracle
+    w = wl.cpu
+    f = lambda t: None if t is None else t.double().numpy()
     x = w["x"]
     B, D, T = x.shape
     cu = w["cu_seqlens"]
@@ -358,8 +467,7 @@ def cpu_baseline(wl, budget_s=10.0):
     has_bwd = w["dy"] is not None
 
     # Channels are independent, so a block of channels over every row and
-    # token is the same workload, narrower.  A short pilot sizes the sample
-    # to about `budget_s` seconds of oracle time.
+    # token is the same workload, narrower.
     def run(nch):
         sub = lambda t: None if t is None else f(t[:, :nch] if t.dim() == 3 else t[:nch])
         xs, ws_, bs = sub(x), sub(w["weight"]), sub(w["bias"])
@@ -384,10 +492,34 @@ def cpu_baseline(wl, budget_s=10.0):
     pilot_dt, _ = run(min(D, 8))
     nch = int(min(D, max(8, budget_s / max(pilot_dt / min(D, 8), 1e-9))))
     dt, nbytes = run(nch)
+    return dt, nbytes, nch, D, has_bwd
+
+
+def cpu_baseline(wl, budget_s=10.0):
+    """The fp64 oracle, single-threaded and pinned to one CPU, on a bounded
+    sample of the same workload."""
+    with _OneCore() as core:
+        if wl.kind == "large_decode":
+            dt1, b1, nch, D, _ = _oracle_rows(wl.large, budget_s)
+            dt2, b2, steps, rows, Dd = _oracle_decode(wl.decode, budget_s / 2)
+            dt, nbytes = dt1 + dt2, b1 + b2
+            B, T = wl.large.shape["B"], wl.large.shape["T"]
+            sample = ("fwd+bwd on channels 0..%d of %d (all %d rows x %d tokens), then %d decode "
+                      "steps on all %d rows x %d channels" % (nch - 1, D, B, T, steps, rows, Dd))
+            tc = B * nch * T + steps * rows * Dd
+        elif wl.kind == "decode":
+            dt, nbytes, steps, rows, D = _oracle_decode(wl, budget_s)
+            sample = "%d decode steps on all %d rows x %d channels" % (steps, rows, D)
+            tc = steps * rows * D
+        else:
+            dt, nbytes, nch, D, has_bwd = _oracle_rows(wl, budget_s)
+            B, T = wl.shape["B"], wl.shape["T"]
+            sample = "fwd%s on channels 0..%d of %d (all %d rows x %d tokens)" % (
+                "+bwd" if has_bwd else "", nch - 1, D, B, T)
+            tc = B * nch * T
     return dict(value=nbytes / dt / 1e9, unit="GB/s", cores=1, kind="oracle",
-                sample="fwd%s on channels 0..%d of %d (all %d rows x %d tokens), one thread"
-                       % ("+bwd" if has_bwd else "", nch - 1, D, B, T),
-                seconds=round(dt, 3), token_channels_per_s=round(B * nch * T / dt, 1),
+                sample=sample + ", one thread pinned to CPU %s" % core.cpu,
+                seconds=round(dt, 3), token_channels_per_s=round(tc / dt, 1),
                 host=host_cpu())
 
 
@@ -488,9 +620,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="dense",
-                    choices=["dense", "packed", "decode", "large", "tiny", "seqidx", "dense_tc",
-                             "large_tc"])
+    ap.add_argument("--workload", default="large_decode",
+                    choices=["large_decode", "dense", "packed", "decode", "large", "tiny",
+                             "seqidx", "dense_tc", "large_tc"])
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="with large_decode: skip timing the dense and packed workloads' ops")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-events", action="store_true",
                     help="skip the per-op event pass")
@@ -590,6 +724,7 @@ def main():
             i += 1
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    check_flags(steps)
     ms = (t1 - t0) * 1e3 / args.steps
     step_bytes = wl.step_bytes()
     value = step_bytes / (ms * 1e-3) / 1e9
@@ -610,19 +745,16 @@ def main():
         cold = rotated_op_times(torch, steps, wl, args.op_reps)
         warm = {} if args.no_warm_pass else op_times(torch, steps[0], wl, args.op_reps)
         for k, t in cold.items():
-            gbs = wl.bytes[k] / (t * 1e-3) / 1e9
-            per_op[k] = {"ms": round(t, 5), "algorithmic_bytes": wl.bytes[k],
-                         "launches_per_step": wl.counts[k],
-                         "GB_s": round(gbs, 1), "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
-                         "timing": "cold (rotating over %d operand copies)" % n_rot}
+            per_op[k] = per_op_entry(wl, k, t, n_rot)
             if k in warm:
                 wg = wl.bytes[k] / (warm[k] * 1e-3) / 1e9
                 per_op[k].update(warm_ms=round(warm[k], 5), warm_GB_s=round(wg, 1),
                                  warm_pct_of_peak=round(100 * wg / PEAK_HBM_GBS, 2))
+        check_flags(steps)
         dom = max(cold, key=lambda k: cold[k] * wl.counts[k])
-        kernel = op_kernels(wl.name)[dom]
+        kernel = op_kernel_label(wl, dom)
         ach = wl.bytes[dom] / (cold[dom] * 1e-3) / 1e9
-        rec = recorded_traffic(kernel, wl.name)
+        rec = recorded_traffic(op_kernels(wl.name)[dom], profile_workload(wl.name, dom))
         roof = {"bound": "hbm", "kernel": kernel, "op": dom, "achieved": round(ach, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
                 "traffic": None if rec is None else rec["hbm_bytes_per_launch"],
@@ -636,7 +768,7 @@ def main():
                         avg_launch_ms_warm=round(warm[dom], 5))
 
     shape = wl.shape
-    tc = shape["B"] * shape["D"] * shape.get("T", shape.get("tokens", 1))
+    tc = wl.token_channels()
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
@@ -652,6 +784,8 @@ def main():
         "token_channels_per_s": round(tc / (ms * 1e-3), 1),
         "ops": per_op, "roofline": roof,
     }
+    if wl.kind == "large_decode" and not args.no_events and not args.no_other_configs:
+        out["other_configs"] = other_config_ops(torch, dev, ("dense", "packed"), args.op_reps)
     if not args.no_cpu_baseline:
         print("bench: timing the oracle on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl)
