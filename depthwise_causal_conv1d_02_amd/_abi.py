@@ -7,7 +7,7 @@ import ctypes
 import os
 import threading
 
-ABI_VERSION = 2  # CCV_ABI_VERSION of include/ccv.h
+ABI_VERSION = 3  # CCV_ABI_VERSION of include/ccv.h
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libccv.so")
 
 CCV_DTYPE_BF16, CCV_DTYPE_F32, CCV_DTYPE_I32 = 0, 1, 2
@@ -20,6 +20,9 @@ CCV_ERR_ALIAS = -2
 CCV_ERR_UNSUPPORTED = -3
 CCV_ERR_NONDETERMINISTIC = -4
 CCV_ERR_HIP = -5
+CCV_ERR_TOO_LARGE = -6
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # CCV_NOALLOC_SCRATCH_BYTES
 
 # option bits of ccv_fwd / ccv_bwd / ccv_update
 CCV_OPT_F32_FILTER_BIAS, CCV_OPT_DETERMINISTIC_DBIAS = 0x1, 0x2
@@ -30,8 +33,8 @@ CU_BIT_NAMES = {CU_FIRST_NONZERO: "first offset is not zero",
                 CU_DECREASING: "offsets decrease",
                 CU_EMPTY: "empty sequence"}
 
-EXPORTS = ("ccv_fwd", "ccv_bwd", "ccv_update", "ccv_validate_cu_seqlens", "ccv_abi_version",
-           "ccv_status_string")
+EXPORTS = ("ccv_fwd", "ccv_bwd", "ccv_bwd_noalloc", "ccv_update", "ccv_validate_cu_seqlens",
+           "ccv_abi_version", "ccv_status_string")
 
 
 class CcvTensor(ctypes.Structure):
@@ -55,6 +58,8 @@ def _declare(lib):
     lib.ccv_fwd.restype = i
     lib.ccv_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, i, i, i, u32, _vp, sz, _vp, _vp]
     lib.ccv_bwd.restype = i
+    lib.ccv_bwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, i, i, i, u32, _vp, _vp]
+    lib.ccv_bwd_noalloc.restype = i
     lib.ccv_update.argtypes = [P, P, P, P, P, i, u32, _vp]
     lib.ccv_update.restype = i
     lib.ccv_validate_cu_seqlens.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64, _vp, _vp]

@@ -379,6 +379,7 @@ const char *ccv_status_string(int status) {
     case CCV_ERR_UNSUPPORTED: return "CCV_ERR_UNSUPPORTED";
     case CCV_ERR_NONDETERMINISTIC: return "CCV_ERR_NONDETERMINISTIC";
     case CCV_ERR_HIP: return "CCV_ERR_HIP";
+    case CCV_ERR_TOO_LARGE: return "CCV_ERR_TOO_LARGE";
     default: return "CCV_UNKNOWN_STATUS";
     }
 }
@@ -461,14 +462,21 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     return hip_status(ccv::launch_fwd(a, vec, silu, p.rows(), stream));
 }
 
-int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bias,
-            const ccv_tensor *cu_seqlens, const ccv_tensor *seq_idx,
-            const ccv_tensor *initial_states, const ccv_tensor *dy,
-            const ccv_tensor *dfinal_states, const ccv_tensor *dx,
-            const ccv_tensor *dweight, const ccv_tensor *dbias,
-            const ccv_tensor *dinitial_states, int activation, int deterministic,
-            int warn_only, uint32_t options, void *workspace, size_t *workspace_bytes,
-            uint32_t *err_flag, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The backward behind ccv_bwd and ccv_bwd_noalloc.  With `noalloc` the
+// deterministic route's partials go to the library's per-device scratch
+// (no size query; calls that need more than it holds are refused before
+// any HIP call).
+int bwd_call(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bias,
+             const ccv_tensor *cu_seqlens, const ccv_tensor *seq_idx,
+             const ccv_tensor *initial_states, const ccv_tensor *dy,
+             const ccv_tensor *dfinal_states, const ccv_tensor *dx, const ccv_tensor *dweight,
+             const ccv_tensor *dbias, const ccv_tensor *dinitial_states, int activation,
+             int deterministic, int warn_only, uint32_t options, void *workspace,
+             size_t *workspace_bytes, uint32_t *err_flag, hipStream_t stream, bool noalloc) {
     Problem p;
     int rc = check_inputs(x, weight, bias, cu_seqlens, seq_idx, initial_states, activation,
                           err_flag, options, p);
@@ -517,11 +525,18 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     const size_t need = use_partials
                             ? static_cast<size_t>(n_part) * static_cast<size_t>(p.D * kp) * 4
                             : 0;
-    if (workspace == nullptr && workspace_bytes != nullptr) {  // size query
+    if (noalloc) {
+        // The partials go to the library's scratch (looked up after every
+        // host check below); it is private, so it takes no part in the
+        // alias test.
+        if (need > ccv::kNoallocScratchBytes) return CCV_ERR_TOO_LARGE;
+        workspace = nullptr;
+        workspace_bytes = nullptr;
+    } else if (workspace == nullptr && workspace_bytes != nullptr) {  // size query
         *workspace_bytes = need;
         return CCV_OK;
     }
-    if (need > 0) {
+    if (need > 0 && !noalloc) {
         if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
             return CCV_ERR_INVALID_ARG;
         if (workspace_bytes != nullptr && *workspace_bytes < need) return CCV_ERR_INVALID_ARG;
@@ -533,6 +548,11 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
                         span_of(initial_states), span_of(dy), span_of(dfinal_states),
                         span_of(seq_idx)};
     if (any_alias(outs, 6, ins, 8)) return CCV_ERR_ALIAS;
+
+    if (noalloc && need > 0) {
+        rc = hip_status(ccv::noalloc_scratch(&workspace));
+        if (rc != CCV_OK) return rc;
+    }
 
     ccv::BwdArgs a;
     memset(&a, 0, sizeof(a));
@@ -588,6 +608,35 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
         if (rc != CCV_OK) return rc;
     }
     return status;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bias,
+            const ccv_tensor *cu_seqlens, const ccv_tensor *seq_idx,
+            const ccv_tensor *initial_states, const ccv_tensor *dy,
+            const ccv_tensor *dfinal_states, const ccv_tensor *dx,
+            const ccv_tensor *dweight, const ccv_tensor *dbias,
+            const ccv_tensor *dinitial_states, int activation, int deterministic,
+            int warn_only, uint32_t options, void *workspace, size_t *workspace_bytes,
+            uint32_t *err_flag, hipStream_t stream) {
+    return bwd_call(x, weight, bias, cu_seqlens, seq_idx, initial_states, dy, dfinal_states, dx,
+                    dweight, dbias, dinitial_states, activation, deterministic, warn_only, options,
+                    workspace, workspace_bytes, err_flag, stream, false);
+}
+
+int ccv_bwd_noalloc(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bias,
+                    const ccv_tensor *cu_seqlens, const ccv_tensor *seq_idx,
+                    const ccv_tensor *initial_states, const ccv_tensor *dy,
+                    const ccv_tensor *dfinal_states, const ccv_tensor *dx,
+                    const ccv_tensor *dweight, const ccv_tensor *dbias,
+                    const ccv_tensor *dinitial_states, int activation, int deterministic,
+                    int warn_only, uint32_t options, uint32_t *err_flag, hipStream_t stream) {
+    return bwd_call(x, weight, bias, cu_seqlens, seq_idx, initial_states, dy, dfinal_states, dx,
+                    dweight, dbias, dinitial_states, activation, deterministic, warn_only, options,
+                    nullptr, nullptr, err_flag, stream, true);
 }
 
 int ccv_update(const ccv_tensor *x, const ccv_tensor *conv_state, const ccv_tensor *weight,

@@ -7,6 +7,8 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include "ccv.h"
+
 namespace ccv {
 
 constexpr int kMinWidth = 2, kMaxWidth = 4;  // filter widths the kernels are built for
@@ -130,6 +132,11 @@ hipError_t launch_validate(const int32_t *cu, int64_t n_seq, int64_t total, uint
 hipError_t launch_dw_reduce(const float *partial, int64_t n_part, int64_t n_ch, int w, int kp,
                             float *dw, float *db, const uint32_t *err, hipStream_t s);
 int64_t resident_blocks(const void *kernel, unsigned dyn_lds);
+
+// Bytes of the per-device scratch behind ccv_bwd_noalloc (CCV_NOALLOC_SCRATCH_BYTES),
+// and the device address of that scratch on the current device (ccv_misc.hip).
+constexpr size_t kNoallocScratchBytes = CCV_NOALLOC_SCRATCH_BYTES;
+hipError_t noalloc_scratch(void **ptr);
 
 // Per-width kernel selection (ccv_width.hip, built once per width).  With
 // `cap` set, the resident-block capacity of the selected kernel is stored

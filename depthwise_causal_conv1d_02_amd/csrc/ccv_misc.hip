@@ -1,9 +1,48 @@
 // ccv_misc.hip — width-independent launches (offset validation, the fixed-
 // order dW reduction) and the switch from a call's filter width to the
 // kernels built for it.
+#include <atomic>
+#include <mutex>
+
 #include "ccv_device.h"
 
 namespace ccv {
+
+// Scratch of the allocation-free backward (ccv_bwd_noalloc): the partials of
+// the deterministic dW/dB route live here instead of in a caller workspace.
+// Every device the library runs on holds its own copy, at its own address,
+// until the process ends.  Host code must never pass `scratch` itself to a
+// kernel or a copy (on the host the name is only a stand-in): it uses the
+// device address looked up below.
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+hipError_t noalloc_scratch(void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void *p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (p == nullptr) return hipErrorInvalidSymbol;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
+}
 
 // Resident blocks of a kernel on the current device (CUs x blocks per CU),
 // from the occupancy the compiled kernel allows; 0 when it cannot be told.

@@ -13,7 +13,7 @@ import torch
 from . import _abi
 
 __all__ = ["causal_conv1d", "causal_conv1d_update", "validate_cu_seqlens", "check_flag",
-           "reset_flag", "flag_tensor", "fwd", "bwd", "update", "CcvError"]
+           "reset_flag", "flag_tensor", "fwd", "bwd", "bwd_noalloc", "update", "CcvError"]
 
 _DTYPES = {torch.bfloat16: _abi.CCV_DTYPE_BF16, torch.float32: _abi.CCV_DTYPE_F32,
            torch.int32: _abi.CCV_DTYPE_I32}
@@ -71,6 +71,10 @@ def _check(rc, what):
     name = _abi.status_name(rc)
     if rc in (_abi.CCV_ERR_INVALID_ARG, _abi.CCV_ERR_ALIAS):
         raise ValueError("%s: %s" % (what, name))
+    if rc == _abi.CCV_ERR_TOO_LARGE:
+        raise ValueError("%s: %s: the deterministic partials of this call exceed the library's "
+                         "%d-byte device scratch; use the workspace form"
+                         % (what, name, _abi.NOALLOC_SCRATCH_BYTES))
     if rc == _abi.CCV_ERR_UNSUPPORTED:
         raise NotImplementedError("%s: %s (declined)" % (what, name))
     if rc == _abi.CCV_ERR_NONDETERMINISTIC:
@@ -192,6 +196,26 @@ def bwd(x, weight, dy, bias=None, cu_seqlens=None, initial_states=None, dfinal_s
                    None if ws is None else ctypes.byref(size), flag_ptr, _stream(x))
     _check(rc, "causal_conv1d backward")
     return dx, dw, db, dinit
+
+
+def bwd_noalloc(x, weight, dy, bias=None, cu_seqlens=None, initial_states=None,
+                dfinal_states=None, activation="silu", deterministic=False, warn_only=False, *,
+                dx, dweight, dbias=None, dinit=None, err_flag=None, seq_idx=None, options=0):
+    """One ccv_bwd_noalloc call: ccv_bwd with the deterministic partials in the
+    library's fixed device scratch, so nothing is allocated here or in the
+    library.  Every output is the caller's: dx, dweight (FP32, accumulated
+    into), dbias when a bias is given, dinit when wanted; packed calls need
+    ``err_flag``.  Calls that overlap on one device race (shared scratch)."""
+    if cu_seqlens is not None and err_flag is None:
+        raise ValueError("packed calls need err_flag (no flag word is allocated here)")
+    rc = _abi.lib().ccv_bwd_noalloc(
+        _ref(_desc(x)), _ref(_desc(weight)), _ref(_desc(bias)), _ref(_desc(cu_seqlens)),
+        _ref(_desc(seq_idx)), _ref(_desc(initial_states)), _ref(_desc(dy)),
+        _ref(_desc(dfinal_states)), _ref(_desc(dx)), _ref(_desc(dweight)), _ref(_desc(dbias)),
+        _ref(_desc(dinit)), _act(activation), int(bool(deterministic)), int(bool(warn_only)),
+        int(options), None if err_flag is None else err_flag.data_ptr(), _stream(x))
+    _check(rc, "causal_conv1d backward (no allocation)")
+    return dx, dweight, dbias, dinit
 
 
 def update(x, conv_state, weight, bias=None, activation="silu", y=None, options=0):

@@ -27,7 +27,9 @@
  * - An optional tensor is absent when its descriptor pointer is NULL or its
  *   data pointer is NULL.
  * - All memory is owned by the caller.  The library allocates nothing,
- *   keeps no pointer after returning, and holds no handle or state.
+ *   keeps no pointer after returning, and holds no handle or state; the
+ *   one exception is the fixed device scratch behind ccv_bwd_noalloc,
+ *   which is part of the loaded code and never allocated by a call.
  * - Every kernel is launched on `stream` (NULL = the default stream).
  *   Calls are asynchronous: no synchronisation, no device-to-host copy and
  *   no read of device memory on the host (cuDNN FE overview, the stream
@@ -51,7 +53,7 @@
 extern "C" {
 #endif
 
-#define CCV_ABI_VERSION 2
+#define CCV_ABI_VERSION 3
 
 typedef enum ccv_dtype {
     CCV_DTYPE_BF16 = 0,
@@ -84,7 +86,10 @@ typedef enum ccv_status {
      * without CCV_OPT_DETERMINISTIC_DBIAS. */
     CCV_ERR_NONDETERMINISTIC = -4,
     /* A HIP launch failed (hipGetLastError after the launch). */
-    CCV_ERR_HIP = -5
+    CCV_ERR_HIP = -5,
+    /* ccv_bwd_noalloc: the call needs more scratch than the library holds
+     * (CCV_NOALLOC_SCRATCH_BYTES); nothing was launched. */
+    CCV_ERR_TOO_LARGE = -6
 } ccv_status;
 
 /* Bits of the cu_seqlens flag word (cuDNN FE "Causal Conv1d", the paragraph
@@ -198,6 +203,33 @@ int ccv_bwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
             const ccv_tensor *dinitial_states, int activation, int deterministic,
             int warn_only, uint32_t options, void *workspace, size_t *workspace_bytes,
             uint32_t *err_flag, hipStream_t stream);
+
+/*
+ * ccv_bwd_noalloc — ccv_bwd for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The arguments and results are those of ccv_bwd without the
+ * workspace: the deterministic route writes its partials to a scratch array
+ * the library keeps in device memory, CCV_NOALLOC_SCRATCH_BYTES on each
+ * device it runs on, for the life of the process.  The call itself allocates
+ * nothing (its first call on a device looks up that device's scratch
+ * address).
+ *
+ *   Limit: a deterministic call whose partials exceed the scratch (ccv_bwd's
+ *   workspace query gives the size) returns CCV_ERR_TOO_LARGE before any
+ *   launch.  The atomic route uses no scratch and has no limit.
+ *   Sharing: every call on one device uses the same scratch; calls that
+ *   overlap in time on one device (two streams, two threads) race and must
+ *   be serialised by the caller.  Nothing in the scratch has to start at
+ *   zero: a call writes every partial it reads.
+ */
+#define CCV_NOALLOC_SCRATCH_BYTES (32u << 20)
+int ccv_bwd_noalloc(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bias,
+                    const ccv_tensor *cu_seqlens, const ccv_tensor *seq_idx,
+                    const ccv_tensor *initial_states, const ccv_tensor *dy,
+                    const ccv_tensor *dfinal_states, const ccv_tensor *dx,
+                    const ccv_tensor *dweight, const ccv_tensor *dbias,
+                    const ccv_tensor *dinitial_states, int activation, int deterministic,
+                    int warn_only, uint32_t options, uint32_t *err_flag, hipStream_t stream);
 
 /*
  * ccv_update — decode step (cuDNN FE "Causal Conv1d": the returned

@@ -73,9 +73,10 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.ccv_abi_version() == _abi.ABI_VERSION == 2
+    assert L.ccv_abi_version() == _abi.ABI_VERSION == 3
     assert _abi.status_name(0) == "CCV_OK"
     assert _abi.status_name(-2) == "CCV_ERR_ALIAS"
+    assert _abi.status_name(-6) == "CCV_ERR_TOO_LARGE"
     assert _abi.status_name(99) == "CCV_UNKNOWN_STATUS"
 
 
@@ -280,3 +281,49 @@ def test_python_surface_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         causal_conv1d(x, w, seq_idx=torch.zeros(1, 4, dtype=torch.int32),
                       cu_seqlens=torch.tensor([0, 4], dtype=torch.int32))
+
+
+def _bwd_noalloc(L, x, w, dy, dx, dw, b=None, db=None, det=1, opt=0):
+    return L.ccv_bwd_noalloc(R(x), R(w), R(b), None, None, None, R(dy), None, R(dx), R(dw),
+                             R(db), None, 1, det, 0, opt, None, None)
+
+
+def _bwd_query(L, x, w, dy, dx, dw, b=None, db=None, opt=0):
+    need = ctypes.c_size_t(0)
+    rc = L.ccv_bwd(R(x), R(w), R(b), None, None, None, R(dy), None, R(dx), R(dw), R(db), None,
+                   1, 1, 0, opt, None, ctypes.byref(need), None, None)
+    assert rc == 0
+    return need.value
+
+
+def test_bwd_noalloc_refuses_partials_beyond_its_scratch(L):
+    """The allocation-free backward's limit is the workspace ccv_bwd would ask
+    for: a deterministic call needing more than the scratch is refused with
+    CCV_ERR_TOO_LARGE before any HIP call (so on the CPU too)."""
+    B, D, Tn = 1, 16384, 1 << 20
+    x, dy, dx = T([B, D, Tn]), T([B, D, Tn]), T([B, D, Tn])
+    w, dw = T([D, 4]), T([D, 4], F32)
+    b, db = T([D]), T([D], F32)
+    need = _bwd_query(L, x, w, dy, dx, dw, b, db, DETDB)
+    assert need > _abi.NOALLOC_SCRATCH_BYTES
+    assert _bwd_noalloc(L, x, w, dy, dx, dw, b, db, 1, DETDB) == _abi.CCV_ERR_TOO_LARGE
+    # the argument checks and the determinism policy of ccv_bwd come first
+    assert _bwd_noalloc(L, x, w, dy, dx, dw, b, db, 1, 0) == NONDET
+    assert _bwd_noalloc(L, x, T([D, 4], F32), dy, dx, dw, b, db, 1, DETDB) == UNSUP
+    assert _bwd_noalloc(L, x, w, dy, dx, T([D, 3], F32)) == INVALID
+    xs, dys, dxs = T([2, 64, 100]), T([2, 64, 100]), T([2, 64, 100])
+    ws, dws = T([64, 4]), T([64, 4], F32)
+    assert _bwd_noalloc(L, xs, ws, dys, xs, dws) == ALIAS
+    assert _bwd_noalloc(L, xs, ws, dys, dxs, T([64, 4], F32, data=dys.data)) == ALIAS
+
+
+def test_bwd_noalloc_scratch_covers_the_large_workload(L):
+    """The deterministic partials of the largest named workload (B=8 D=8192
+    T=8192, no bias) fit the scratch, with room for a bias column."""
+    B, D, Tn = 8, 8192, 8192
+    cl = [Tn * D, 1, D]                       # [B,T,D] storage behind a transpose view
+    x, dy, dx = T([B, D, Tn], stride=cl), T([B, D, Tn], stride=cl), T([B, D, Tn], stride=cl)
+    w, dw = T([D, 4]), T([D, 4], F32)
+    need = _bwd_query(L, x, w, dy, dx, dw)
+    assert need == 128 * D * 4 * 4            # 8 rows x 16 time blocks of partials
+    assert need * 5 // 4 <= _abi.NOALLOC_SCRATCH_BYTES
