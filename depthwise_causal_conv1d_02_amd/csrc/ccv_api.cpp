@@ -36,6 +36,12 @@
 #ifndef CCV_FWD_PACKED_TARGET_WAVES
 #define CCV_FWD_PACKED_TARGET_WAVES CCV_FWD_TARGET_WAVES
 #endif
+// Inputs large enough for the pipelined forward: more waves of shorter
+// chunks (16 steps on the large and packed workloads) keep the dispatcher
+// refilling CUs until the end of the launch.
+#ifndef CCV_FWD_PIPE_TARGET_WAVES
+#define CCV_FWD_PIPE_TARGET_WAVES 65536
+#endif
 #ifndef CCV_BWD_PACKED_ROUNDS
 #define CCV_BWD_PACKED_ROUNDS CCV_BWD_ROUNDS
 #endif
@@ -80,6 +86,25 @@
 #endif
 #ifndef CCV_BWD_VEC
 #define CCV_BWD_VEC 4           // the backward kernels are built for 4 or 1
+#endif
+// Tail chunks (percent of each row's steps, and their length): the main
+// chunks shrink to cover the rest, and the tail chunks' blocks are numbered
+// after every main block, so the dispatcher hands them to whichever CUs
+// finish first.  0 = no tail.
+#ifndef CCV_FWD_TAIL_PCT
+#define CCV_FWD_TAIL_PCT 0
+#endif
+#ifndef CCV_FWD_TAIL_CHUNK
+#define CCV_FWD_TAIL_CHUNK 16
+#endif
+#ifndef CCV_FWD_TAIL_PIPE_ONLY
+#define CCV_FWD_TAIL_PIPE_ONLY 1  // only inputs large enough for the pipelined forward
+#endif
+#ifndef CCV_BWD_TAIL_PCT
+#define CCV_BWD_TAIL_PCT 0
+#endif
+#ifndef CCV_BWD_TAIL_CHUNK
+#define CCV_BWD_TAIL_CHUNK 16
 #endif
 
 namespace {
@@ -321,6 +346,7 @@ bool any_alias(const Span *outs, int n_out, const Span *ins, int n_in) {
 // A block holds `wt` waves along time times `wc` waves along channel groups.
 struct Geometry {
     int64_t L, n_chunk, n_tblk, n_group, n_gblk, n_block;
+    int64_t Tm, Lt, n_tblk_t, n_block_m;  // main / tail split (Tm == T: none)
 };
 
 Geometry geometry(const Problem &p, int vec, int wt, int wc, int64_t capacity, int rounds,
@@ -347,7 +373,33 @@ Geometry geometry(const Problem &p, int vec, int wt, int wc, int64_t capacity, i
     g.n_chunk = (p.T + L - 1) / L;
     g.n_tblk = (g.n_chunk + wt - 1) / wt;
     g.n_block = rows * g.n_gblk * g.n_tblk;
+    g.Tm = p.T;
+    g.Lt = 0;
+    g.n_tblk_t = 0;
+    g.n_block_m = g.n_block;
     return g;
+}
+
+// Split off tail chunks: the main chunks keep their number (whole blocks of
+// `wt`) and shrink to cover (100 - pct)% of the steps; the rest is cut into
+// chunks of `lt` steps.  No split when pct or lt is 0, or when the main
+// chunks would fall below `min_chunk` steps.
+void add_tail(Geometry &g, const Problem &p, int wt, int pct, int64_t lt, int64_t min_chunk) {
+    if (pct <= 0 || pct >= 100 || lt <= 0) return;
+    const int64_t n_chunk_m = g.n_tblk * wt;
+    const int64_t Lm = p.T * (100 - pct) / 100 / n_chunk_m;
+    if (Lm < min_chunk) return;
+    const int64_t Tm = Lm * n_chunk_m;
+    if (Tm >= p.T) return;
+    const int64_t per = (p.packed ? 1 : p.B) * g.n_gblk;
+    const int64_t n_chunk_t = (p.T - Tm + lt - 1) / lt;
+    g.L = Lm;
+    g.Tm = Tm;
+    g.Lt = lt;
+    g.n_tblk_t = (n_chunk_t + wt - 1) / wt;
+    g.n_chunk = n_chunk_m + n_chunk_t;
+    g.n_block_m = per * g.n_tblk;
+    g.n_block = g.n_block_m + per * g.n_tblk_t;
 }
 
 // Time-lane geometry: one wave per (row, chunk of kTcTiles tiles).
@@ -359,6 +411,10 @@ Geometry time_geometry(const Problem &p) {
     g.n_group = p.D;
     g.n_gblk = p.D;
     g.n_block = (p.B * p.D * g.n_chunk + ccv::kWavesPerBlock - 1) / ccv::kWavesPerBlock;
+    g.Tm = p.T;
+    g.Lt = 0;
+    g.n_tblk_t = 0;
+    g.n_block_m = g.n_block;
     return g;
 }
 
@@ -437,21 +493,30 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     const Geometry g = time_lanes ? time_geometry(p)
                                   : geometry(p, vec, ccv::kFwdWavesT, ccv::kFwdWavesC, cap,
                                              CCV_FWD_ROUNDS,
-                                             p.packed ? CCV_FWD_PACKED_TARGET_WAVES
-                                                      : CCV_FWD_TARGET_WAVES,
+                                             pipe && vec == 8 && !p.seq
+                                                 ? CCV_FWD_PIPE_TARGET_WAVES
+                                             : p.packed ? CCV_FWD_PACKED_TARGET_WAVES
+                                                        : CCV_FWD_TARGET_WAVES,
                                              p.packed ? CCV_FWD_PACKED_MIN_CHUNK
                                              : small_dense && vec == CCV_FWD_SMALL_VEC
                                                  ? CCV_FWD_SMALL_CHUNK
                                                  : CCV_FWD_MIN_CHUNK);
+    Geometry gs = g;
+    if (!time_lanes && (pipe || !CCV_FWD_TAIL_PIPE_ONLY))
+        add_tail(gs, p, ccv::kFwdWavesT, CCV_FWD_TAIL_PCT, CCV_FWD_TAIL_CHUNK, 1);
     a.B = p.B;
     a.D = p.D;
     a.T = p.T;
-    a.L = g.L;
-    a.n_chunk = g.n_chunk;
-    a.n_tblk = g.n_tblk;
-    a.n_group = g.n_group;
-    a.n_gblk = g.n_gblk;
-    a.n_block = g.n_block;
+    a.L = gs.L;
+    a.n_chunk = gs.n_chunk;
+    a.n_tblk = gs.n_tblk;
+    a.n_group = gs.n_group;
+    a.n_gblk = gs.n_gblk;
+    a.n_block = gs.n_block;
+    a.Tm = gs.Tm;
+    a.Lt = gs.Lt;
+    a.n_tblk_t = gs.n_tblk_t;
+    a.n_block_m = gs.n_block_m;
     a.cu_in_lds = p.packed && p.N + 1 <= ccv::kLdsCuMax;
     a.nt_load = p.B * p.D * p.T * 2 >=
                 (p.seq ? CCV_NT_LOAD_MIN_BYTES_SEQ : CCV_NT_LOAD_MIN_BYTES);
@@ -521,7 +586,9 @@ int bwd_call(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bi
     Geometry g = time_lanes ? time_geometry(p)
                             : geometry(p, vec, ccv::kWavesPerBlock, 1, 0, 0,
                                        CCV_BWD_TARGET_WAVES, CCV_BWD_MIN_CHUNK);
-    const int64_t n_part = (p.packed ? 1 : p.B) * g.n_tblk;
+    if (!time_lanes)
+        add_tail(g, p, ccv::kWavesPerBlock, CCV_BWD_TAIL_PCT, CCV_BWD_TAIL_CHUNK, 1);
+    const int64_t n_part = (p.packed ? 1 : p.B) * (g.n_tblk + g.n_tblk_t);
     const size_t need = use_partials
                             ? static_cast<size_t>(n_part) * static_cast<size_t>(p.D * kp) * 4
                             : 0;
@@ -582,9 +649,11 @@ int bwd_call(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bi
                 (p.seq ? CCV_NT_LOAD_MIN_BYTES_SEQ_BWD : CCV_NT_LOAD_MIN_BYTES);
     const int silu = activation == CCV_ACT_SILU;
     const int rounds = p.packed ? CCV_BWD_PACKED_ROUNDS : CCV_BWD_ROUNDS;
-    if (!use_partials && rounds > 0 && !time_lanes)
+    if (!use_partials && rounds > 0 && !time_lanes) {
         g = geometry(p, vec, ccv::kWavesPerBlock, 1, ccv::bwd_resident_blocks(a, vec, silu, p.rows()),
                      rounds, CCV_BWD_TARGET_WAVES, CCV_BWD_MIN_CHUNK);
+        add_tail(g, p, ccv::kWavesPerBlock, CCV_BWD_TAIL_PCT, CCV_BWD_TAIL_CHUNK, 1);
+    }
     a.B = p.B;
     a.D = p.D;
     a.T = p.T;
@@ -594,6 +663,10 @@ int bwd_call(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bi
     a.n_group = g.n_group;
     a.n_gblk = g.n_gblk;
     a.n_block = g.n_block;
+    a.Tm = g.Tm;
+    a.Lt = g.Lt;
+    a.n_tblk_t = g.n_tblk_t;
+    a.n_block_m = g.n_block_m;
     a.cu_in_lds = p.packed && p.N + 1 <= ccv::kLdsCuMax;
 
     if (p.packed && !a.cu_in_lds) {

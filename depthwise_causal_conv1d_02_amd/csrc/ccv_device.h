@@ -37,6 +37,15 @@ constexpr uint32_t kFirstNonzero = 0x1u, kLastMismatch = 0x2u, kDecreasing = 0x4
 #ifndef CCV_FWD_UNROLL
 #define CCV_FWD_UNROLL 4
 #endif
+// The software-pipelined forward (inputs of 256 MB and more, 16-step
+// chunks): two batches of 8 steps per chunk measured faster than four of 4
+// (large 350.8 -> 346.7 us, packed 127.9 -> 123.4 us).
+#ifndef CCV_FWD_PIPE_UNROLL
+#define CCV_FWD_PIPE_UNROLL 8
+#endif
+#ifndef CCV_FWD_PIPE_UNROLL_DENSE
+#define CCV_FWD_PIPE_UNROLL_DENSE CCV_FWD_PIPE_UNROLL
+#endif
 // Dense rows on 4-channel lanes (the small-input forward): longer batches,
 // more loads in flight from HBM (measured with cold caches).
 #ifndef CCV_FWD_SMALL_UNROLL
@@ -69,22 +78,29 @@ constexpr uint32_t kFirstNonzero = 0x1u, kLastMismatch = 0x2u, kDecreasing = 0x4
 #define CCV_BWD_FAST_EDGES 1
 #endif
 // Lower bound on resident waves per SIMD (register budget), measured best:
-// the forward keeps 4 waves, or 3 when it software-pipelines its loads.
+// the forward keeps 4 waves; the software-pipelined forward (two batches of
+// 8 steps) gets a 2-wave budget, within which its bias-free variants fit in
+// 164 registers (3 waves per SIMD) without spilling; a 3-wave budget spills.
 #ifndef CCV_FWD_MIN_WAVES
 #define CCV_FWD_MIN_WAVES 4
 #endif
 #ifndef CCV_FWD_PIPE_MIN_WAVES
-#define CCV_FWD_PIPE_MIN_WAVES 3
+#define CCV_FWD_PIPE_MIN_WAVES 2
+#endif
+// Variants that spilled under the 4-wave budget take the 3-wave one.
+#ifndef CCV_FWD_SPILL_MIN_WAVES
+#define CCV_FWD_SPILL_MIN_WAVES 3
 #endif
 #ifndef CCV_BWD_MIN_WAVES
 #define CCV_BWD_MIN_WAVES 2
 #endif
 // Variants that would spill under the 4-wave budget (no activation, seq_idx
-// rows, packed rows with a bias) take the pipelined budget instead.
+// rows, packed rows with a bias) take the 3-wave budget instead.
 #define CCV_FWD_ATTR                                                                 \
     __attribute__((amdgpu_waves_per_eu(                                              \
-        (PIPE || !SILU || ROWS == kRowsSeq || (ROWS == kRowsPacked && fk_bias(FK)))  \
-            ? CCV_FWD_PIPE_MIN_WAVES                                                 \
+        PIPE ? CCV_FWD_PIPE_MIN_WAVES                                                \
+        : (!SILU || ROWS == kRowsSeq || (ROWS == kRowsPacked && fk_bias(FK)))        \
+            ? CCV_FWD_SPILL_MIN_WAVES                                                \
             : CCV_FWD_MIN_WAVES)))
 #ifdef CCV_BWD_MIN_WAVES
 #define CCV_BWD_ATTR __attribute__((amdgpu_waves_per_eu(CCV_BWD_MIN_WAVES)))
@@ -102,6 +118,14 @@ constexpr uint32_t kFirstNonzero = 0x1u, kLastMismatch = 0x2u, kDecreasing = 0x4
 // Wave index through readfirstlane in the seq_idx kernels.
 #ifndef CCV_WAVE_UNIFORM
 #define CCV_WAVE_UNIFORM 1
+#endif
+// Row modes (bit 1 << mode) whose forward / backward take the wave index
+// through readfirstlane.
+#ifndef CCV_FWD_UNIFORM_ROWS
+#define CCV_FWD_UNIFORM_ROWS (1 << 2)
+#endif
+#ifndef CCV_BWD_UNIFORM_ROWS
+#define CCV_BWD_UNIFORM_ROWS (1 << 2)
 #endif
 
 // ---------------------------------------------------------------------------
@@ -229,6 +253,37 @@ __device__ __forceinline__ void decode_tile(int64_t tile, int64_t n_t, int64_t n
         tb = (tile / n_c) % n_t;
     }
     b = tile / (n_t * n_c);
+}
+
+// A block's place in a launch split into main and tail chunks (see
+// FwdArgs): the first n_block_m blocks tile [0, Tm) with chunks of L steps,
+// the rest tile [Tm, T) with chunks of Lt steps.  Each range is remapped over
+// the XCDs on its own, so both spread over every XCD.  `bt` comes back as
+// the time block among all n_tblk + n_tblk_t of a (row, channel block): a
+// fixed function of the block id, so per-block partials stay shape-determined.
+struct TileSpan {
+    int64_t b, c, bt;   // row, channel block, time block
+    int64_t t0, L, end; // first step of wave 0's chunk, chunk length, range end
+};
+template <int ORDER, typename A>
+__device__ __forceinline__ TileSpan split_tile(const A &a, int64_t n_c, int wt) {
+    TileSpan s;
+    const int64_t bid = blockIdx.x;
+    if (bid < a.n_block_m) {
+        decode_tile<ORDER>(xcd_remap(bid, a.n_block_m), a.n_tblk, n_c, s.b, s.c, s.bt);
+        s.L = a.L;
+        s.t0 = s.bt * wt * a.L;
+        s.end = a.Tm;
+    } else {
+        int64_t bt;
+        decode_tile<ORDER>(xcd_remap(bid - a.n_block_m, a.n_block - a.n_block_m), a.n_tblk_t, n_c,
+                           s.b, s.c, bt);
+        s.L = a.Lt;
+        s.t0 = a.Tm + bt * wt * a.Lt;
+        s.end = a.T;
+        s.bt = a.n_tblk + bt;
+    }
+    return s;
 }
 
 // Filter kinds: the weight dtype and whether a bias is present.  The bias
@@ -589,13 +644,13 @@ __global__ __launch_bounds__(256) CCV_FWD_ATTR void k_fwd_chan(FwdArgs a) {
     constexpr bool PACKED = ROWS == kRowsPacked;
     __shared__ int32_t s_cu[PACKED ? kLdsCuMax : 1];
     __shared__ uint32_t s_bad;
-    int64_t b, gb, bt;
-    decode_tile(xcd_remap(blockIdx.x, a.n_block), a.n_tblk, a.n_gblk, b, gb, bt);
+    const TileSpan ts = split_tile<CCV_TILE_ORDER>(a, a.n_gblk, kFwdWavesT);
+    const int64_t b = ts.b, gb = ts.c;
     // The wave index is uniform over the wave; readfirstlane tells the
     // compiler so, which keeps the time bounds and row offsets in scalars.
     // Measured: it frees the registers the seq_idx walk needs, but slows
     // the dense and packed streams on large inputs, so only seq_idx uses it.
-    const int wave = (ROWS == kRowsSeq && CCV_WAVE_UNIFORM)
+    const int wave = (((CCV_FWD_UNIFORM_ROWS >> ROWS) & 1) && CCV_WAVE_UNIFORM)
                          ? __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize)
                          : static_cast<int>(threadIdx.x / kWaveSize);
     const int lane = threadIdx.x % kWaveSize;
@@ -606,10 +661,10 @@ __global__ __launch_bounds__(256) CCV_FWD_ATTR void k_fwd_chan(FwdArgs a) {
             return;  // malformed or sticky: write nothing
     }
     const int64_t g = gb * kFwdWavesC + wave / kFwdWavesT;
-    const int64_t t0 = (bt * kFwdWavesT + wave % kFwdWavesT) * a.L;
+    const int64_t t0 = ts.t0 + (wave % kFwdWavesT) * ts.L;
     const int64_t c0 = g * (kWaveSize * VEC) + lane * VEC;
-    if (t0 >= a.T || c0 >= a.D) return;
-    const int64_t t1 = min(t0 + a.L, a.T);
+    if (t0 >= ts.end || c0 >= a.D) return;
+    const int64_t t1 = min(t0 + ts.L, ts.end);
 
     float w[W][VEC], bias[VEC];
     load_filter<W, VEC, FK>(a.w, a.w_sd, a.w_sk, a.bias, a.b_s, c0, w, bias);
@@ -621,14 +676,15 @@ __global__ __launch_bounds__(256) CCV_FWD_ATTR void k_fwd_chan(FwdArgs a) {
             constexpr int U = VEC == 4 ? CCV_FWD_SMALL_UNROLL : CCV_FWD_UNROLL;
             fwd_seq_piece<W, VEC, SILU, NTL, U>(a, b, t0, t1, c0, w, bias);
         } else if constexpr (!PACKED) {
-            constexpr int U = (VEC == 4 && !PIPE) ? CCV_FWD_SMALL_UNROLL : CCV_FWD_UNROLL;
+            constexpr int U = PIPE ? CCV_FWD_PIPE_UNROLL_DENSE
+                              : VEC == 4 ? CCV_FWD_SMALL_UNROLL : CCV_FWD_UNROLL;
             fwd_piece<W, VEC, SILU, NTL, PIPE, U>(a, b, b, 0, a.T, t0, t1, c0, w, bias);
         } else {
             const int32_t *cu = a.cu_in_lds ? s_cu : a.cu;
             for (int64_t i = find_row(cu, a.n_seq, t0); i < a.n_seq; ++i) {
                 const int64_t s = cu[i], e = cu[i + 1];
                 if (s >= t1) break;
-                fwd_piece<W, VEC, SILU, NTL, PIPE, CCV_FWD_UNROLL>(
+                fwd_piece<W, VEC, SILU, NTL, PIPE, PIPE ? CCV_FWD_PIPE_UNROLL : CCV_FWD_UNROLL>(
                     a, 0, i, s, e, s > t0 ? s : t0, e < t1 ? e : t1, c0, w, bias);
             }
         }
@@ -1029,16 +1085,16 @@ __global__ __launch_bounds__(256) CCV_BWD_ATTR void k_bwd_chan(BwdArgs a) {
     __shared__ uint32_t s_bad;
     int32_t *s_cu = reinterpret_cast<int32_t *>(s_buf);
     float (*s_red)[W + 1][CH + 1] = reinterpret_cast<float (*)[W + 1][CH + 1]>(s_buf);
-    int64_t b, g, bt;
     // Packed rows measured faster with time blocks innermost, the others
     // with channel blocks innermost.
-    decode_tile<PACKED ? CCV_BWD_PACKED_TILE_ORDER : CCV_TILE_ORDER>(
-        xcd_remap(blockIdx.x, a.n_block), a.n_tblk, a.n_group, b, g, bt);
+    const TileSpan ts = split_tile<PACKED ? CCV_BWD_PACKED_TILE_ORDER : CCV_TILE_ORDER>(
+        a, a.n_group, kWavesPerBlock);
+    const int64_t b = ts.b, g = ts.c, bt = ts.bt;
     // The wave index is uniform over the wave; readfirstlane tells the
     // compiler so, which keeps the time bounds and row offsets in scalars.
     // Measured: it frees the registers the seq_idx walk needs, but slows
     // the dense and packed streams on large inputs, so only seq_idx uses it.
-    const int wave = (ROWS == kRowsSeq && CCV_WAVE_UNIFORM)
+    const int wave = (((CCV_BWD_UNIFORM_ROWS >> ROWS) & 1) && CCV_WAVE_UNIFORM)
                          ? __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize)
                          : static_cast<int>(threadIdx.x / kWaveSize);
     const int lane = threadIdx.x % kWaveSize;
@@ -1048,7 +1104,7 @@ __global__ __launch_bounds__(256) CCV_BWD_ATTR void k_bwd_chan(BwdArgs a) {
                                blockIdx.x == 0))
             return;  // uniform over the block: no barrier is left waiting
     }
-    const int64_t t0 = (bt * kWavesPerBlock + wave) * a.L;
+    const int64_t t0 = ts.t0 + wave * ts.L;
     const int64_t c0 = g * CH + lane * VEC;
 
     BwdLane<W, VEC, SILU, BIAS> L;
@@ -1058,8 +1114,8 @@ __global__ __launch_bounds__(256) CCV_BWD_ATTR void k_bwd_chan(BwdArgs a) {
         for (int k = 0; k < W; ++k) L.dw[k][c] = 0.0f;
         L.db[c] = 0.0f;
     }
-    if (t0 < a.T && c0 < a.D) {
-        const int64_t t1 = min(t0 + a.L, a.T);
+    if (t0 < ts.end && c0 < a.D) {
+        const int64_t t1 = min(t0 + ts.L, ts.end);
         load_filter<W, VEC, FK>(a.w, a.w_sd, a.w_sk, a.bias, a.b_s, c0, L.w, L.bias);
         auto run = [&](auto ntl) {
             constexpr bool NTL = decltype(ntl)::value;
@@ -1093,7 +1149,7 @@ __global__ __launch_bounds__(256) CCV_BWD_ATTR void k_bwd_chan(BwdArgs a) {
     }
     __syncthreads();
     const int64_t ch0 = g * CH;
-    const int64_t pidx = b * a.n_tblk + bt;
+    const int64_t pidx = b * (a.n_tblk + a.n_tblk_t) + bt;
     if (a.partial) {
         // One unique partial row per block: [channel][tap] (+ the bias slot
         // when dbias goes through the deterministic route too).
@@ -1462,6 +1518,14 @@ void k_bwd_tc(BwdArgs a) {
 #ifndef CCV_UPD_STAGED
 #define CCV_UPD_STAGED 1        // coalesced (LDS-staged) update when D % 512 == 0
 #endif
+// Cache policy of the staged update's accesses (bits): 1 = non-temporal
+// state loads, 2 = non-temporal state stores, 4 = non-temporal token loads.
+// Measured on the decode shape with cold states (interleaved runs): all
+// three 6.8 us, state loads and stores 7.3 us, state stores alone 8.4 us,
+// none 8.6 us.
+#ifndef CCV_UPD_STAGED_NT
+#define CCV_UPD_STAGED_NT 7
+#endif
 // ... and from this many (row, channel) pairs (12 MiB of update traffic at
 // width 4).  Measured with cold states: the staged kernel loses about 0.5 us
 // to the plain one up to 1 MB, 0.1 us at 8 MB, and wins 0.15 us at 16 MB and
@@ -1650,9 +1714,16 @@ void k_update_staged(UpdArgs a) {
             const u32x4_t *sq = reinterpret_cast<const u32x4_t *>(
                 static_cast<const uint16_t *>(a.state) + (b0 + r) * a.s_sb + cw * (W - 1));
 #pragma unroll
-            for (int i = 0; i < V::kState; ++i) sv[r][i] = sq[lane + kWaveSize * i];
-            xv[r] = *reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(a.x) +
-                                                       (b0 + r) * a.x_sb + cw + lane * VEC);
+            for (int i = 0; i < V::kState; ++i) {
+                if constexpr (CCV_UPD_STAGED_NT & 1)
+                    sv[r][i] = __builtin_nontemporal_load(sq + lane + kWaveSize * i);
+                else
+                    sv[r][i] = sq[lane + kWaveSize * i];
+            }
+            const u32x4_t *xq = reinterpret_cast<const u32x4_t *>(
+                static_cast<const uint16_t *>(a.x) + (b0 + r) * a.x_sb + cw + lane * VEC);
+            if constexpr (CCV_UPD_STAGED_NT & 4) xv[r] = __builtin_nontemporal_load(xq);
+            else xv[r] = *xq;
         }
     }
 #pragma unroll
@@ -1703,8 +1774,13 @@ void k_update_staged(UpdArgs a) {
             u32x4_t *sq = reinterpret_cast<u32x4_t *>(static_cast<uint16_t *>(a.state) +
                                                       (b0 + r) * a.s_sb + cw * (W - 1));
 #pragma unroll
-            for (int i = 0; i < V::kState; ++i)
-                sq[lane + kWaveSize * i] = s_state[wave][r][lane + kWaveSize * i];
+            for (int i = 0; i < V::kState; ++i) {
+                if constexpr (CCV_UPD_STAGED_NT & 2)
+                    __builtin_nontemporal_store(s_state[wave][r][lane + kWaveSize * i],
+                                                sq + lane + kWaveSize * i);
+                else
+                    sq[lane + kWaveSize * i] = s_state[wave][r][lane + kWaveSize * i];
+            }
         }
     }
 }
@@ -1831,21 +1907,37 @@ __global__ __launch_bounds__(256) void k_validate(const int32_t *cu, int64_t n_s
 }
 
 // Fixed-order reduction of unique partials [P][D][kp] into dw[d][k] (k < W)
-// and, with kp = W+1, db[d].  A block takes 64 consecutive elements (one per
-// lane) and splits the P partials into 16 groups (4 waves x 4 accumulators):
-// group q sums p = q, q+16, q+32, ... in increasing p, then the 16 group sums
-// are added in increasing q.  The order depends on P only, never on
-// scheduling, so the result is the same bits run to run.
+// and, with kp = W+1, db[d].  The P partials of every element are split into
+// 16 groups (4 waves x 4 accumulators): group q sums p = q, q+16, q+32, ...
+// in increasing p, then the 16 group sums are added in increasing q.  The
+// order depends on P only, never on scheduling, so the result is the same
+// bits run to run.
+//
+// A lane owns V consecutive elements (V = 4: one 16-byte load per partial,
+// when the element count is a multiple of 4; else V = 1), a block 64 lanes'
+// columns.  Each lane issues the loads of 8 partials per group (32 loads)
+// before it adds any, so a block keeps its whole share of the partials in
+// flight at once.
 //
 // `err` is the packed call's flag word (nullptr for dense rows).  When it is
 // non-zero the backward blocks wrote no partials, so the reduction adds
 // nothing either: dweight and dbias keep their values.  The word is read once
 // per block and shared through LDS, so the whole block takes one branch.
-__global__ __launch_bounds__(256) void k_dw_reduce(const float *part, int64_t n_part,
+template <int V> struct RedVec;
+template <> struct RedVec<4> { typedef float T __attribute__((ext_vector_type(4))); };
+template <> struct RedVec<1> { typedef float T; };
+
+// The register budget of at most 2 waves per SIMD lets every load of a lane
+// be in flight together (a higher occupancy target makes the scheduler wait
+// on each load before the next).
+template <int V>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void k_dw_reduce(const float *part, int64_t n_part,
                                                    int64_t n_ch, int w, int kp, float *dw,
                                                    float *db, const uint32_t *err) {
-    constexpr int kAcc = 4, kGroups = kWavesPerBlock * kAcc;
-    __shared__ float s_acc[kGroups][kWaveSize];
+    using T = typename RedVec<V>::T;
+    constexpr int kAcc = 4, kGroups = kWavesPerBlock * kAcc, kUnroll = 8;
+    __shared__ T s_acc[kGroups][kWaveSize];
     __shared__ uint32_t s_err;
     if (err != nullptr) {
         if (threadIdx.x == 0)
@@ -1854,29 +1946,52 @@ __global__ __launch_bounds__(256) void k_dw_reduce(const float *part, int64_t n_
         if (s_err != 0u) return;  // uniform over the block
     }
     const int lane = threadIdx.x % kWaveSize, wave = threadIdx.x / kWaveSize;
-    const int64_t n_elem = n_ch * kp;
-    const int64_t e = static_cast<int64_t>(blockIdx.x) * kWaveSize + lane;
-    float acc[kAcc] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (e < n_elem) {
-        for (int64_t p0 = 0; p0 < n_part; p0 += kGroups) {
+    const int64_t n_vec = n_ch * kp / V;
+    const int64_t c = static_cast<int64_t>(blockIdx.x) * kWaveSize + lane;
+    T acc[kAcc];
+#pragma unroll
+    for (int j = 0; j < kAcc; ++j) acc[j] = T{};
+    if (c < n_vec) {
+        const T *col = reinterpret_cast<const T *>(part) + c;
+        int64_t p0 = 0;
+        for (; p0 + kGroups * kUnroll <= n_part; p0 += kGroups * kUnroll) {
+            T v[kUnroll][kAcc];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+                for (int j = 0; j < kAcc; ++j)
+                    v[u][j] = col[(p0 + u * kGroups + wave * kAcc + j) * n_vec];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+                for (int j = 0; j < kAcc; ++j) acc[j] += v[u][j];
+        }
+        for (; p0 < n_part; p0 += kGroups) {
 #pragma unroll
             for (int j = 0; j < kAcc; ++j) {
                 const int64_t p = p0 + wave * kAcc + j;
-                if (p < n_part) acc[j] += part[p * n_elem + e];
+                if (p < n_part) acc[j] += col[p * n_vec];
             }
         }
     }
 #pragma unroll
     for (int j = 0; j < kAcc; ++j) s_acc[wave * kAcc + j][lane] = acc[j];
     __syncthreads();
-    if (wave != 0 || e >= n_elem) return;
-    float sum = 0.0f;
+    if (wave != 0 || c >= n_vec) return;
+    T sum = T{};
 #pragma unroll
     for (int q = 0; q < kGroups; ++q) sum += s_acc[q][lane];
-    const int64_t ch = e / kp;
-    const int k = static_cast<int>(e % kp);
-    if (k < w) dw[ch * w + k] += sum;
-    else db[ch] += sum;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int64_t e = c * V + i;
+        const int64_t ch = e / kp;
+        const int k = static_cast<int>(e % kp);
+        float v;
+        if constexpr (V == 1) v = sum;
+        else v = sum[i];
+        if (k < w) dw[ch * w + k] += v;
+        else db[ch] += v;
+    }
 }
 
 // A stream value that never names a real stream: dispatch without launching.

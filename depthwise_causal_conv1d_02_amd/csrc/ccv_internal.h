@@ -67,6 +67,10 @@ struct FwdArgs {
     int64_t n_group;           // channel groups of 64*VEC channels
     int64_t n_gblk;            // blocks along channels: ceil(n_group / kFwdWavesC)
     int64_t n_block;           // grid size
+    // Main and tail chunks: the first n_block_m blocks take chunks of L steps
+    // over [0, Tm); the others take chunks of Lt steps over [Tm, T), n_tblk_t
+    // blocks along time per (row, channel block).  Tm == T: no tail.
+    int64_t Tm, Lt, n_tblk_t, n_block_m;
     int cu_in_lds;             // stage + validate cu_seqlens in LDS
     int nt_load;               // stream the bulk loads with the non-temporal policy
     int pipe;                  // software-pipelined body (8-channel lanes, large inputs)
@@ -90,6 +94,7 @@ struct BwdArgs {
     int64_t seq_sb, seq_st;
     uint32_t *err;
     int64_t B, D, T, L, n_chunk, n_tblk, n_group, n_gblk, n_block;
+    int64_t Tm, Lt, n_tblk_t, n_block_m;  // main and tail chunks, as in FwdArgs
     int cu_in_lds;
     int nt_load;
 };

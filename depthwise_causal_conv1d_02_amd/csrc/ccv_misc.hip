@@ -117,9 +117,18 @@ hipError_t launch_validate(const int32_t *cu, int64_t n_seq, int64_t total, uint
 
 hipError_t launch_dw_reduce(const float *partial, int64_t n_part, int64_t n_ch, int w, int kp,
                             float *dw, float *db, const uint32_t *err, hipStream_t s) {
-    const int64_t blocks = (n_ch * kp + kWaveSize - 1) / kWaveSize;  // 64 elements per block
-    hipLaunchKernelGGL(k_dw_reduce, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, partial,
-                       n_part, n_ch, w, kp, dw, db, err);
+    // 16-byte lanes when every partial row is a whole number of 16-byte
+    // vectors (the partials start 256-byte aligned); 64 lanes per block.
+    const int64_t n_elem = n_ch * kp;
+    if (n_elem % 4 == 0) {
+        const int64_t blocks = (n_elem / 4 + kWaveSize - 1) / kWaveSize;
+        hipLaunchKernelGGL(k_dw_reduce<4>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                           partial, n_part, n_ch, w, kp, dw, db, err);
+    } else {
+        const int64_t blocks = (n_elem + kWaveSize - 1) / kWaveSize;
+        hipLaunchKernelGGL(k_dw_reduce<1>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                           partial, n_part, n_ch, w, kp, dw, db, err);
+    }
     return hipGetLastError();
 }
 

@@ -500,6 +500,12 @@ DET_DBIAS_CASES = [
     (3, 3, 40, 77, "cl", None),
     (4, 2, 48, 50, "tc", None),
     (4, 1, 512, None, "cl", [1, 2, 3, 100, 17, 400, 5]),
+    # the reduction's paths: 625 partials per element on 16-byte lanes, and
+    # (D * (W+1) not a multiple of 4) single-element lanes with 282 partials
+    # and with a few partials of packed rows
+    (4, 1, 64, 40000, "cl", None),
+    (4, 2, 37, 9000, "cl", None),
+    (2, 1, 41, None, "cl", [5, 100, 2, 33]),
 ]
 
 
