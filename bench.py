@@ -179,6 +179,16 @@ class Workload:
     def step_bytes(self):
         return sum(self.bytes[k] * self.counts[k] for k in self.bytes)
 
+    def cpu_view(self):
+        """A copy of this workload without its device tensors (what the
+        oracle baseline needs)."""
+        import copy
+        c = copy.copy(self)
+        c.g = {}
+        if self.kind == "large_decode":
+            c.large, c.decode = self.large.cpu_view(), self.decode.cpu_view()
+        return c
+
     def token_channels(self):
         """(token, channel) pairs one step processes."""
         if self.kind == "large_decode":
@@ -378,9 +388,11 @@ def per_op_entry(wl, name, t, n_rot):
             "timing": "cold (rotating over %d operand copies)" % n_rot}
 
 
-def other_config_ops(torch, dev, names, reps):
+def other_config_ops(torch, dev, names, reps, warm_steps):
     """Cold per-op times of other workloads (their own operand copies), in
-    the same run: the dense and packed configurations' forward and backward."""
+    the same run: the dense and packed configurations' forward and backward.
+    Each workload first runs `warm_steps` whole steps, as a run of its own
+    would before its per-op pass."""
     res = {}
     for name in names:
         print("bench: per-op times of workload %s" % name, file=sys.stderr, flush=True)
@@ -389,8 +401,8 @@ def other_config_ops(torch, dev, names, reps):
         wls = [wl] + [wl.clone() for _ in range(n_rot - 1)]
         steps = [make_step(w, torch) for w in wls]
         quiet = Events(torch, False)
-        for st in steps:
-            st(quiet)
+        for i in range(max(1, warm_steps)):
+            steps[i % n_rot](quiet)
         torch.cuda.synchronize()
         cold = rotated_op_times(torch, steps, wl, reps)
         check_flags(steps)
@@ -575,8 +587,20 @@ def summarize(args):
         mine = [r for r in rows if r["_short"].startswith(kernel)]
         if not mine:
             continue
-        fetch, nf = _counter_per_launch(fetch_dir, "FETCH_SIZE", kernel)
-        write, nw = _counter_per_launch(write_dir, "WRITE_SIZE", kernel)
+        # the deterministic backward is two kernels: the walk and the
+        # fixed-order reduction of its partials; the op's time and traffic
+        # are their sums per launch
+        kernels = [kernel]
+        if op == "bwd" and any("k_dw_reduce" in r["_short"] for r in rows):
+            kernels.append("k_dw_reduce")
+        fetch = write = 0.0
+        nf = nw = 0
+        for k in kernels:
+            f_, n_ = _counter_per_launch(fetch_dir, "FETCH_SIZE", k)
+            w_, m_ = _counter_per_launch(write_dir, "WRITE_SIZE", k)
+            fetch += f_
+            write += w_
+            nf, nw = nf + n_, nw + m_
         hbm = int(fetch * 1024 * f_scale + write * 1024 * w_scale)
         alg = wl_bytes[op]
         lines = ["# %s on the %s workload" % (kernel, args.workload), "",
@@ -589,9 +613,13 @@ def summarize(args):
             lines.append("| `%s` | %s | %.2f | %.2f | %.2f |" % (
                 r["_short"][:70], r["Calls"], float(r["AverageNs"]) / 1e3,
                 float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
-        avg_us = sum(float(r["AverageNs"]) * int(r["Calls"]) for r in mine) / \
-            sum(int(r["Calls"]) for r in mine) / 1e3
-        lines += ["", "Counters per launch of `%s` (means over %d and %d dispatches):" % (kernel, nf, nw), "",
+        avg_us = 0.0
+        for k in kernels:
+            ks = [r for r in rows if k in r["_short"]]
+            avg_us += sum(float(r["AverageNs"]) * int(r["Calls"]) for r in ks) / \
+                sum(int(r["Calls"]) for r in ks) / 1e3
+        lines += ["", "Counters per launch of `%s` (means over %d and %d dispatches):"
+                  % (" + ".join(kernels), nf, nw), "",
                   "| quantity | value |", "|---|---|",
                   "| FETCH_SIZE (KiB) | %.1f |" % fetch, "| WRITE_SIZE (KiB) | %.1f |" % write,
                   "| copy calibration: %d MiB copy reads FETCH_SIZE KiB | %.1f (factor %.4f) |" % (
@@ -601,10 +629,11 @@ def summarize(args):
                   "| HBM bytes per launch (scaled) | %d |" % hbm,
                   "| algorithmic bytes per launch | %d |" % alg,
                   "| traffic / algorithmic | %.4f |" % (hbm / alg),
-                  "| average kernel duration (us) | %.2f |" % avg_us,
+                  "| average duration per launch of the op (us) | %.2f |" % avg_us,
                   "| algorithmic bytes / average duration (GB/s) | %.1f |" % (alg / (avg_us * 1e-6) / 1e9),
                   "",
-                  "<!-- traffic " + json.dumps({"kernel": kernel, "workload": args.workload,
+                  "<!-- traffic " + json.dumps({"kernel": kernel, "kernels": kernels,
+                                                 "workload": args.workload,
                                                  "hbm_bytes_per_launch": hbm,
                                                  "algorithmic_bytes": alg,
                                                  "avg_kernel_us": round(avg_us, 3),
@@ -785,7 +814,15 @@ def main():
         "ops": per_op, "roofline": roof,
     }
     if wl.kind == "large_decode" and not args.no_events and not args.no_other_configs:
-        out["other_configs"] = other_config_ops(torch, dev, ("dense", "packed"), args.op_reps)
+        # the large workload's operands and graphs are released first, so the
+        # smaller workloads are timed on a device holding only their own data
+        cpu_wl = wl.cpu_view()
+        del graphs, cycle, steps, wls, wl
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        out["other_configs"] = other_config_ops(torch, dev, ("dense", "packed"), args.op_reps,
+                                                args.warmup + args.steps)
+        wl = cpu_wl
     if not args.no_cpu_baseline:
         print("bench: timing the oracle on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl)
