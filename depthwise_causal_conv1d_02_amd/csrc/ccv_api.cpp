@@ -402,10 +402,10 @@ void add_tail(Geometry &g, const Problem &p, int wt, int pct, int64_t lt, int64_
     g.n_block = g.n_block_m + per * g.n_tblk_t;
 }
 
-// Time-lane geometry: one wave per (row, chunk of kTcTiles tiles).
-Geometry time_geometry(const Problem &p) {
+// Time-lane geometry: one wave per (row, chunk of `tiles` tiles).
+Geometry time_geometry(const Problem &p, int tiles) {
     Geometry g;
-    g.L = static_cast<int64_t>(ccv::kTcTiles) * ccv::kTcTile;
+    g.L = static_cast<int64_t>(tiles) * ccv::kTcTile;
     g.n_chunk = (p.T + g.L - 1) / g.L;
     g.n_tblk = g.n_chunk;  // partials per batch row: one per chunk
     g.n_group = p.D;
@@ -419,6 +419,17 @@ Geometry time_geometry(const Problem &p) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? CCV_OK : CCV_ERR_HIP; }
+
+// The time lanes decode their wave index in 32 bits when all B*D*n_chunk
+// wave indices fit.
+template <typename A>
+void set_tc_div(A &a) {
+    a.tc_div32 = a.B * a.D * a.n_chunk <= int64_t(UINT32_MAX);
+    if (a.tc_div32) {
+        a.tc_chunks = ccv::make_div32(static_cast<uint32_t>(a.n_chunk));
+        a.tc_rows = ccv::make_div32(static_cast<uint32_t>(a.D));
+    }
+}
 
 }  // namespace
 
@@ -490,7 +501,7 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     const int64_t cap = CCV_FWD_ROUNDS > 0 && !time_lanes
                             ? ccv::fwd_resident_blocks(a, vec, silu, p.rows())
                             : 0;
-    const Geometry g = time_lanes ? time_geometry(p)
+    const Geometry g = time_lanes ? time_geometry(p, ccv::kTcTilesFwd)
                                   : geometry(p, vec, ccv::kFwdWavesT, ccv::kFwdWavesC, cap,
                                              CCV_FWD_ROUNDS,
                                              pipe && vec == 8 && !p.seq
@@ -517,6 +528,7 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     a.Lt = gs.Lt;
     a.n_tblk_t = gs.n_tblk_t;
     a.n_block_m = gs.n_block_m;
+    if (time_lanes) set_tc_div(a);
     a.cu_in_lds = p.packed && p.N + 1 <= ccv::kLdsCuMax;
     a.nt_load = p.B * p.D * p.T * 2 >=
                 (p.seq ? CCV_NT_LOAD_MIN_BYTES_SEQ : CCV_NT_LOAD_MIN_BYTES);
@@ -583,7 +595,7 @@ int bwd_call(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bi
     // The partials of the deterministic route depend on the shape only (a
     // grid sized by target waves); the atomic route sizes its grid by the
     // device's resident capacity below.
-    Geometry g = time_lanes ? time_geometry(p)
+    Geometry g = time_lanes ? time_geometry(p, ccv::kTcTilesBwd)
                             : geometry(p, vec, ccv::kWavesPerBlock, 1, 0, 0,
                                        CCV_BWD_TARGET_WAVES, CCV_BWD_MIN_CHUNK);
     if (!time_lanes)
@@ -667,6 +679,7 @@ int bwd_call(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bi
     a.Lt = g.Lt;
     a.n_tblk_t = g.n_tblk_t;
     a.n_block_m = g.n_block_m;
+    if (time_lanes) set_tc_div(a);
     a.cu_in_lds = p.packed && p.N + 1 <= ccv::kLdsCuMax;
 
     if (p.packed && !a.cu_in_lds) {

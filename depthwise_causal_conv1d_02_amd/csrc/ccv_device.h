@@ -1188,22 +1188,44 @@ __global__ __launch_bounds__(256) CCV_BWD_ATTR void k_bwd_chan(BwdArgs a) {
 //
 // Lanes run along time: a lane owns kTcE = 8 consecutive tokens of one
 // (b, d) row (one 16-byte vector), a wave one tile of 512 consecutive tokens,
-// and a wave walks a chunk of kTcTiles tiles in order, all of whose loads are
-// issued before the first use.  The W-1 tokens before a lane's first token
-// come from the lane before (a cross-lane shift); lane 0 takes them from the
-// previous tile's lane 63, or at the chunk start from memory (the input, the
-// initial state, or zeros).  The filter taps and the bias belong to the row,
-// so they are wave-uniform.
+// and a wave walks a chunk of kTcTilesFwd (forward) or kTcTilesBwd tiles in
+// order, all of whose loads are issued before the first use.  The W-1 tokens
+// before a lane's first token come from the lane before (a cross-lane shift);
+// lane 0 takes them from the previous tile's lane 63, or at the chunk start
+// from memory (the input, the initial state, or zeros).  The filter taps and
+// the bias belong to the row, so they are wave-uniform.
 // ===========================================================================
-__device__ __forceinline__ float lane_up(float v) { return __shfl_up(v, 1, kWaveSize); }
-__device__ __forceinline__ float lane_down(float v) { return __shfl_down(v, 1, kWaveSize); }
+// Cross-lane moves on the VALU (DPP), not through the LDS crossbar.  With
+// `bound_ctrl` off, a lane whose source lies outside the wave (or, for the
+// row shifts, outside its row of 16 lanes) keeps `edge`.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float edge, float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(edge), __float_as_int(v),
+                                                      CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppWaveShr1 = 0x138;  // lane i <- lane i-1
+constexpr int kDppWaveShl1 = 0x130;  // lane i <- lane i+1
+constexpr int kDppRowShr = 0x110;    // + n: lane i <- lane i-n of the same row
+// Lane i gets lane i-1's v; lane 0 gets `first`.
+__device__ __forceinline__ float lane_up(float v, float first) {
+    return dpp_move<kDppWaveShr1>(first, v);
+}
+// Lane i gets lane i+1's v; lane 63 gets `last`.
+__device__ __forceinline__ float lane_down(float v, float last) {
+    return dpp_move<kDppWaveShl1>(last, v);
+}
 __device__ __forceinline__ float from_lane(float v, int l) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
+// Sum over the wave, in every lane: an inclusive scan within each row of 16
+// lanes (shifts of 1, 2, 4, 8), then the four row totals (lanes 15, 31, 47,
+// 63) added in a fixed order.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = kWaveSize / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWaveSize);
-    return v;
+    v += dpp_move<kDppRowShr + 1>(0.0f, v);
+    v += dpp_move<kDppRowShr + 2>(0.0f, v);
+    v += dpp_move<kDppRowShr + 4>(0.0f, v);
+    v += dpp_move<kDppRowShr + 8>(0.0f, v);
+    return (from_lane(v, 15) + from_lane(v, 31)) + (from_lane(v, 47) + from_lane(v, 63));
 }
 
 // A lane's kTcE tokens from t on a unit-stride row; the tokens at or past
@@ -1232,15 +1254,32 @@ __device__ __forceinline__ void tc_store(uint16_t *row, int64_t t, int64_t end,
     }
 }
 
-// x_ext at a position p < T of row (b, d): the input for p >= 0, else the
-// initial state slot p + W-1, else zero.
+// Single extended tokens of one row (b, d): x_ext at p < T is the input for
+// p >= 0, else the initial state's slot p + W-1, else zero.  The source is
+// picked by selects and every case has a valid address (a zero token reads
+// the row's first input and is dropped after the load), so these loads are
+// issued without a branch, before the bulk loads, and no wait comes between
+// them: the first tile can start as soon as its own data is in.
 template <int W>
-__device__ __forceinline__ float tc_x_ext(const uint16_t *xr, const Strided3 &init, int64_t b,
-                                          int64_t d, int64_t p) {
-    if (p >= 0) return bf16_bits_to_f32(xr[p]);
-    if (!init.ptr) return 0.0f;
-    return bf16_bits_to_f32(static_cast<const uint16_t *>(
-        init.ptr)[b * init.s0 + d * init.s1 + (p + W - 1) * init.s2]);
+struct TcRowExt {
+    const uint16_t *xr;  // the row's input, T >= 1 tokens
+    const uint16_t *ir;  // the row's initial state, or null
+    int64_t is2;         // its slot stride
+    __device__ __forceinline__ TcRowExt(const uint16_t *x_row, const Strided3 &init, int64_t b,
+                                        int64_t d)
+        : xr(x_row),
+          ir(init.ptr ? static_cast<const uint16_t *>(init.ptr) + b * init.s0 + d * init.s1
+                      : nullptr),
+          is2(init.s2) {}
+    // Raw bits of x_ext[p]; `keep` false where x_ext[p] is zero.
+    __device__ __forceinline__ uint16_t load(int64_t p, bool &keep) const {
+        keep = p >= 0 || ir;
+        const uint16_t *src = p >= 0 ? xr + p : ir ? ir + (p + W - 1) * is2 : xr;
+        return *src;
+    }
+};
+__device__ __forceinline__ float kept_f32(uint16_t bits, bool keep) {
+    return keep ? bf16_bits_to_f32(bits) : 0.0f;
 }
 
 // Work item of a time-lane wave: row (b, d) and chunk [t0, t1).
@@ -1252,10 +1291,19 @@ __device__ __forceinline__ bool tc_item(const A &a, TcItem &it) {
     const int64_t wid = xcd_remap(blockIdx.x, a.n_block) * kWavesPerBlock +
                         __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
     if (wid >= a.B * a.D * a.n_chunk) return false;
-    const int64_t row = wid / a.n_chunk;
-    it.chunk = wid % a.n_chunk;
-    it.b = row / a.D;
-    it.d = row % a.D;
+    if (a.tc_div32) {
+        const uint32_t w32 = static_cast<uint32_t>(wid);
+        const uint32_t row = div32(w32, a.tc_chunks);
+        const uint32_t b = div32(row, a.tc_rows);
+        it.chunk = w32 - row * static_cast<uint32_t>(a.n_chunk);
+        it.b = b;
+        it.d = row - b * static_cast<uint32_t>(a.D);
+    } else {
+        const int64_t row = wid / a.n_chunk;
+        it.chunk = wid % a.n_chunk;
+        it.b = row / a.D;
+        it.d = row % a.D;
+    }
     it.t0 = it.chunk * a.L;
     it.t1 = min(it.t0 + a.L, a.T);
     return true;
@@ -1267,30 +1315,36 @@ __device__ __forceinline__ void fwd_tc_chunk(const FwdArgs &a, const TcItem &it)
     const uint16_t *xr = static_cast<const uint16_t *>(a.x.ptr) + it.b * a.x.s0 + it.d * a.x.s1;
     uint16_t *yr = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.y.ptr)) +
                    it.b * a.y.s0 + it.d * a.y.s1;
-    Raw<8> raw[kTcTiles];
+    // Left halo, the final state's tokens (lanes 0..W-2 of the chunk that
+    // ends the row copy the row's last W-1 extended tokens bit for bit; the
+    // other lanes repeat lane W-2's address), the filter, then the tiles.
+    const TcRowExt<W> ext(xr, a.init, it.b, it.d);
+    uint16_t lh[W - 1];
+    bool lh_keep[W - 1], fin_keep;
 #pragma unroll
-    for (int c = 0; c < kTcTiles; ++c) {
+    for (int j = 0; j < W - 1; ++j) lh[j] = ext.load(it.t0 - (W - 1) + j, lh_keep[j]);
+    const uint16_t fin_bits = ext.load(a.T - (W - 1) + min(lane, W - 2), fin_keep);
+    float w[W][1], bias[1];
+    load_filter<W, 1, FK>(a.w, a.w_sd, a.w_sk, a.bias, a.b_s, it.d, w, bias);
+    Raw<8> raw[kTcTilesFwd];
+#pragma unroll
+    for (int c = 0; c < kTcTilesFwd; ++c) {
         const int64_t t = it.t0 + c * kTcTile + lane * kTcE;
         if (t < it.t1) raw[c] = tc_load<NTL>(xr, t, it.t1);
         else raw[c].v = u32x4_t{0u, 0u, 0u, 0u};
     }
-    float w[W][1], bias[1];
-    load_filter<W, 1, FK>(a.w, a.w_sd, a.w_sk, a.bias, a.b_s, it.d, w, bias);
     float carry[W - 1];  // x_ext of the W-1 tokens before the current tile
 #pragma unroll
-    for (int j = 0; j < W - 1; ++j) carry[j] = tc_x_ext<W>(xr, a.init, it.b, it.d, it.t0 - (W - 1) + j);
+    for (int j = 0; j < W - 1; ++j) carry[j] = kept_f32(lh[j], lh_keep[j]);
 
 #pragma unroll
-    for (int c = 0; c < kTcTiles; ++c) {
+    for (int c = 0; c < kTcTilesFwd; ++c) {
         const int64_t tt = it.t0 + c * kTcTile;
         if (tt >= it.t1) break;
         float v[kTcE], xe[W - 1 + kTcE], out[kTcE];
         unpack<8>(raw[c], v);
 #pragma unroll
-        for (int j = 0; j < W - 1; ++j) {
-            const float up = lane_up(v[kTcE - (W - 1) + j]);
-            xe[j] = lane == 0 ? carry[j] : up;
-        }
+        for (int j = 0; j < W - 1; ++j) xe[j] = lane_up(v[kTcE - (W - 1) + j], carry[j]);
 #pragma unroll
         for (int i = 0; i < kTcE; ++i) xe[W - 1 + i] = v[i];
 #pragma unroll
@@ -1305,18 +1359,9 @@ __device__ __forceinline__ void fwd_tc_chunk(const FwdArgs &a, const TcItem &it)
 #pragma unroll
         for (int j = 0; j < W - 1; ++j) carry[j] = from_lane(v[kTcE - (W - 1) + j], kWaveSize - 1);
     }
-    // The chunk that ends the row writes its final state: the last W-1
-    // extended tokens, copied bit for bit.
-    if (it.t1 == a.T && a.fin.ptr && lane < W - 1) {
-        const int64_t p = a.T - (W - 1) + lane;
-        uint16_t bits = 0;
-        if (p >= 0) bits = xr[p];
-        else if (a.init.ptr)
-            bits = static_cast<const uint16_t *>(a.init.ptr)[it.b * a.init.s0 + it.d * a.init.s1 +
-                                                             (p + W - 1) * a.init.s2];
+    if (it.t1 == a.T && a.fin.ptr && lane < W - 1)
         const_cast<uint16_t *>(static_cast<const uint16_t *>(a.fin.ptr))
-            [it.b * a.fin.s0 + it.d * a.fin.s1 + lane * a.fin.s2] = bits;
-    }
+            [it.b * a.fin.s0 + it.d * a.fin.s1 + lane * a.fin.s2] = fin_keep ? fin_bits : 0;
 }
 
 template <int W, bool SILU, int FK>
@@ -1342,9 +1387,28 @@ __device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it)
     const uint16_t *dyr = static_cast<const uint16_t *>(a.dy.ptr) + it.b * a.dy.s0 + it.d * a.dy.s1;
     uint16_t *dxr = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.dx.ptr)) +
                     it.b * a.dx.s0 + it.d * a.dx.s1;
-    Raw<8> rx[kTcTiles], rd[kTcTiles];
+    // Single-token loads first, without branches (as in the forward): the
+    // left halo; the right halo (lane j < W-1 reads token t1 + j of x and dy;
+    // the other lanes, and tokens past the row, read an in-row token that is
+    // dropped); the row's final-state gradient (every lane holds all W-1
+    // values; a row without one reads its first input token W-1 times).
+    const TcRowExt<W> ext(xr, a.init, it.b, it.d);
+    uint16_t lh[W - 1];
+    bool lh_keep[W - 1];
 #pragma unroll
-    for (int c = 0; c < kTcTiles; ++c) {
+    for (int j = 0; j < W - 1; ++j) lh[j] = ext.load(it.t0 - (W - 1) + j, lh_keep[j]);
+    const int64_t rq = min(it.t1 + lane, a.T - 1);
+    const uint16_t rh_x = xr[rq], rh_dy = dyr[rq];
+    const uint16_t *dfr = a.dfin.ptr ? static_cast<const uint16_t *>(a.dfin.ptr) +
+                                           it.b * a.dfin.s0 + it.d * a.dfin.s1
+                                     : xr;
+    const int64_t dfs = a.dfin.ptr ? a.dfin.s2 : 0;
+    uint16_t dfb[W - 1];
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) dfb[j] = dfr[j * dfs];
+    Raw<8> rx[kTcTilesBwd], rd[kTcTilesBwd];
+#pragma unroll
+    for (int c = 0; c < kTcTilesBwd; ++c) {
         const int64_t t = it.t0 + c * kTcTile + lane * kTcE;
         if (t < it.t1) {
             rx[c] = tc_load<NTL>(xr, t, it.t1);
@@ -1358,7 +1422,10 @@ __device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it)
     load_filter<W, 1, FK>(a.w, a.w_sd, a.w_sk, a.bias, a.b_s, it.d, w, bias);
     float carry[W - 1];
 #pragma unroll
-    for (int j = 0; j < W - 1; ++j) carry[j] = tc_x_ext<W>(xr, a.init, it.b, it.d, it.t0 - (W - 1) + j);
+    for (int j = 0; j < W - 1; ++j) carry[j] = kept_f32(lh[j], lh_keep[j]);
+    float dfv[W - 1];  // dfinal of the row (zeros without one)
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) dfv[j] = kept_f32(dfb[j], a.dfin.ptr != nullptr);
     float dwacc[W], dbacc = 0.0f;
 #pragma unroll
     for (int k = 0; k < W; ++k) dwacc[k] = 0.0f;
@@ -1371,10 +1438,7 @@ __device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it)
 #pragma unroll
         for (int i = 0; i < kTcE; ++i) ge[i] = g[i];
 #pragma unroll
-        for (int j = 0; j < W - 1; ++j) {
-            const float dn = lane_down(g[j]);
-            ge[kTcE + j] = lane == kWaveSize - 1 ? after[j] : dn;
-        }
+        for (int j = 0; j < W - 1; ++j) ge[kTcE + j] = lane_down(g[j], after[j]);
         const int64_t t = tt + lane * kTcE;
 #pragma unroll
         for (int i = 0; i < kTcE; ++i) {
@@ -1386,11 +1450,10 @@ __device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it)
         if (a.dfin.ptr && t + kTcE > fin0) {
 #pragma unroll
             for (int i = 0; i < kTcE; ++i) {
-                const int64_t p = t + i;
-                if (p >= fin0 && p < a.T)
-                    v[i] += bf16_bits_to_f32(static_cast<const uint16_t *>(a.dfin.ptr)
-                                                 [it.b * a.dfin.s0 + it.d * a.dfin.s1 +
-                                                  (p - fin0) * a.dfin.s2]);
+                const int64_t m = t + i - fin0;  // final-state slot of the token, if any
+#pragma unroll
+                for (int j = 0; j < W - 1; ++j)
+                    if (m == j) v[i] += dfv[j];
             }
         }
         if (t < it.t1) tc_store<true>(dxr, t, it.t1, v);
@@ -1399,17 +1462,14 @@ __device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it)
     float gprev[kTcE];
     int64_t tprev = -1;
 #pragma unroll
-    for (int c = 0; c < kTcTiles; ++c) {
+    for (int c = 0; c < kTcTilesBwd; ++c) {
         const int64_t tt = it.t0 + c * kTcTile;
         if (tt >= it.t1) break;
         float v[kTcE], dyv[kTcE], xe[W - 1 + kTcE], g[kTcE];
         unpack<8>(rx[c], v);
         unpack<8>(rd[c], dyv);
 #pragma unroll
-        for (int j = 0; j < W - 1; ++j) {
-            const float up = lane_up(v[kTcE - (W - 1) + j]);
-            xe[j] = lane == 0 ? carry[j] : up;
-        }
+        for (int j = 0; j < W - 1; ++j) xe[j] = lane_up(v[kTcE - (W - 1) + j], carry[j]);
 #pragma unroll
         for (int i = 0; i < kTcE; ++i) xe[W - 1 + i] = v[i];
 #pragma unroll
@@ -1438,10 +1498,11 @@ __device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it)
 #pragma unroll
                 for (int m = W - 2; m >= 0; --m)
                     acc = fmaf(w[W - 1 - m][0], p + m >= 0 ? g[p + m] : 0.0f, acc);
-                if (a.dfin.ptr && p >= fin0)
-                    acc += bf16_bits_to_f32(static_cast<const uint16_t *>(a.dfin.ptr)
-                                                [it.b * a.dfin.s0 + it.d * a.dfin.s1 +
-                                                 (p - fin0) * a.dfin.s2]);
+                if (a.dfin.ptr && p >= fin0) {
+#pragma unroll
+                    for (int m = 0; m < W - 1; ++m)
+                        if (p - fin0 == m) acc += dfv[m];
+                }
                 const_cast<uint16_t *>(static_cast<const uint16_t *>(a.dinit.ptr))
                     [it.b * a.dinit.s0 + it.d * a.dinit.s1 + j * a.dinit.s2] = to_bf16_bits(acc);
             }
@@ -1452,22 +1513,25 @@ __device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it)
 #pragma unroll
         for (int j = 0; j < W - 1; ++j) carry[j] = from_lane(v[kTcE - (W - 1) + j], kWaveSize - 1);
     }
-    // Right halo: g at t1 .. t1+W-2 (inside the row) for the last tile's
-    // lane 63; lane j computes position t1 + j.  (A chunk that does not end
-    // the row is a whole number of tiles, so t1 - (W-1) >= 0 here.)
+    // Right halo: g at t1 .. t1+W-2 (zero past the row) for the last tile's
+    // lane 63, computed in every lane from the prefetched tokens.  A chunk
+    // that does not end the row is a whole number of tiles, so `carry` now
+    // holds x at t1-(W-1) .. t1-1.
     {
-        float gh = 0.0f;
-        const int64_t p = it.t1 + lane;
-        if (lane < W - 1 && p < a.T) {
+        float xw[2 * (W - 1)], after[W - 1];
+        const float hx = bf16_bits_to_f32(rh_x), hd = bf16_bits_to_f32(rh_dy);
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) {
+            xw[j] = carry[j];
+            xw[W - 1 + j] = from_lane(hx, j);
+        }
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) {
             float z = bias[0];
 #pragma unroll
-            for (int k = 0; k < W; ++k)
-                z = fmaf(w[k][0], bf16_bits_to_f32(xr[p - (W - 1) + k]), z);
-            gh = bf16_bits_to_f32(dyr[p]) * act_slope<SILU>(z);
+            for (int k = 0; k < W; ++k) z = fmaf(w[k][0], xw[j + k], z);
+            after[j] = it.t1 + j < a.T ? from_lane(hd, j) * act_slope<SILU>(z) : 0.0f;
         }
-        float after[W - 1];
-#pragma unroll
-        for (int j = 0; j < W - 1; ++j) after[j] = from_lane(gh, j);
         emit(tprev, gprev, after);
     }
     // dW/dB of the chunk: a wave sum, then one atomic or one partial per tap.

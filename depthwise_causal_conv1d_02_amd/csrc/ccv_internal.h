@@ -30,15 +30,41 @@ constexpr int kFwdWavesC = kWavesPerBlock / kFwdWavesT;
 #endif
 constexpr int kLdsCuMax = 4096;    // cu_seqlens entries staged in LDS (16 KB)
 // Time-lane kernels (unit stride along T): tokens per lane, per wave step
-// (a tile), and tiles per wave chunk.
+// (a tile), and tiles per wave chunk in the forward and the backward (the
+// backward's per-chunk work, its right halo and its dW/dB sum, favours
+// longer chunks).
 constexpr int kTcE = 8;
 constexpr int kTcTile = kWaveSize * kTcE;
-#ifndef CCV_TC_TILES
-#define CCV_TC_TILES 4
+#ifndef CCV_TC_TILES_FWD
+#define CCV_TC_TILES_FWD 2
 #endif
-constexpr int kTcTiles = CCV_TC_TILES;
+#ifndef CCV_TC_TILES_BWD
+#define CCV_TC_TILES_BWD 4
+#endif
+constexpr int kTcTilesFwd = CCV_TC_TILES_FWD;
+constexpr int kTcTilesBwd = CCV_TC_TILES_BWD;
 // `vec` value that selects the time-lane kernels.
 constexpr int kVecTime = 0;
+
+// Unsigned 32-bit division by a divisor fixed for a launch, as a multiply
+// and two shifts, exact for every 0 <= n < 2^32 (Granlund and Montgomery,
+// "Division by Invariant Integers using Multiplication", PLDI 1994, section
+// 4: m = floor(2^32 (2^l - d) / d) + 1 with l = ceil(log2 d)).  The host
+// builds it; a kernel applies it to wave-uniform indices, where it replaces a
+// 64-bit division routine that would precede the wave's first load.
+struct Div32 {
+    uint32_t mul, sh1, sh2;
+};
+constexpr Div32 make_div32(uint32_t d) {
+    uint32_t l = 0;
+    while ((uint64_t(1) << l) < d) ++l;
+    const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1;
+    return Div32{static_cast<uint32_t>(m), l < 1 ? l : 1u, l > 1 ? l - 1 : 0u};
+}
+constexpr uint32_t div32(uint32_t n, const Div32 &v) {
+    const uint32_t t = static_cast<uint32_t>((static_cast<uint64_t>(v.mul) * n) >> 32);
+    return (t + ((n - t) >> v.sh1)) >> v.sh2;
+}
 
 // One BF16 activation-like tensor [B,D,T] (or [R,D,W-1] for states) in
 // element strides.  ptr == nullptr means absent.
@@ -74,6 +100,10 @@ struct FwdArgs {
     int cu_in_lds;             // stage + validate cu_seqlens in LDS
     int nt_load;               // stream the bulk loads with the non-temporal policy
     int pipe;                  // software-pipelined body (8-channel lanes, large inputs)
+    // Time lanes: wave index -> (row, chunk) -> (b, d) in 32 bits when the
+    // B*D*n_chunk waves fit (tc_div32), by these divisors (n_chunk, D).
+    int tc_div32;
+    Div32 tc_chunks, tc_rows;
 };
 
 struct BwdArgs {
@@ -97,6 +127,8 @@ struct BwdArgs {
     int64_t Tm, Lt, n_tblk_t, n_block_m;  // main and tail chunks, as in FwdArgs
     int cu_in_lds;
     int nt_load;
+    int tc_div32;                         // as in FwdArgs
+    Div32 tc_chunks, tc_rows;
 };
 
 struct UpdArgs {
