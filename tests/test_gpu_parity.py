@@ -740,6 +740,9 @@ TC_CASES = [
     (3, 2, 32, 2600, True, True, True, "silu", BF16, True, False),
     (2, 2, 32, 1000, False, True, True, "silu", F32, False, True),
     (4, 2, 32, 2056, True, True, False, "silu", F32, True, False),    # FP32 filter + bias
+    (4, 2, 16, 2049, True, True, True, "silu", BF16, False, False),   # right halo 1 token
+    (4, 1, 24, 2050, False, True, True, "silu", BF16, True, False),   # dfinal across chunks
+    (3, 2, 16, 1025, True, True, True, None, BF16, False, True),      # fwd chunk of 1 token
 ]
 
 
