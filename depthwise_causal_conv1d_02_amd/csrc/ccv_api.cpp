@@ -218,7 +218,7 @@ int pick_vec(int preferred, const ccv_tensor *weight, const ccv_tensor *bias,
 }
 
 // Time lanes (unit stride along T): every activation tensor has unit time
-// stride and 16-byte aligned row starts; dense rows only.
+// stride and 16-byte aligned row starts (dense, packed or seq_idx rows).
 bool time_lanes_ok(const ccv_tensor *a, const ccv_tensor *b, const ccv_tensor *c) {
     for (const ccv_tensor *t : {a, b, c}) {
         if (t == nullptr) continue;
@@ -326,6 +326,7 @@ void set_seq(A &a, const ccv_tensor *seq_idx, const Problem &p) {
     a.seq = p.seq ? static_cast<const int32_t *>(seq_idx->data) : nullptr;
     a.seq_sb = p.seq ? seq_idx->stride[0] : 0;
     a.seq_st = p.seq ? seq_idx->stride[1] : 0;
+    a.seq_vec = p.seq && a.seq_st == 1 && a.seq_sb % 4 == 0 && aligned16(seq_idx->data);
 }
 
 // Every output span against every input span and every other output span.
@@ -470,7 +471,7 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
                         span_of(initial_states), span_of(seq_idx)};
     if (any_alias(outs, 3, ins, 6)) return CCV_ERR_ALIAS;
 
-    const bool time_lanes = !p.packed && !p.seq && time_lanes_ok(x, y, nullptr);
+    const bool time_lanes = time_lanes_ok(x, y, nullptr);
     const bool pipe = p.B * p.D * p.T * 2 >= CCV_FWD_PIPE_MIN_BYTES;
     const int64_t groups8 = (p.D + ccv::kWaveSize * 8 - 1) / (ccv::kWaveSize * 8);
     const bool small_dense = !p.packed && (!p.seq || CCV_FWD_SMALL_SEQ) && !pipe &&
@@ -590,7 +591,7 @@ int bwd_call(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bi
         }
     }
     const int64_t kp = p.W + (present(bias) ? 1 : 0);  // partial columns per channel
-    const bool time_lanes = !p.packed && !p.seq && time_lanes_ok(x, dy, dx);
+    const bool time_lanes = time_lanes_ok(x, dy, dx);
     const int vec = time_lanes ? ccv::kVecTime : pick_vec(CCV_BWD_VEC, weight, bias, x, dy, dx);
     // The partials of the deterministic route depend on the shape only (a
     // grid sized by target waves); the atomic route sizes its grid by the

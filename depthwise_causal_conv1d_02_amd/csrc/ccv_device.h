@@ -430,12 +430,16 @@ __device__ __forceinline__ void finish_left_halo(const Raw<VEC> (&raw)[W - 1],
 // cu_seqlens staged in LDS and validated there (the whole array, by every
 // block, so no block depends on another).  Returns the violation bits of
 // this call ORed with the sticky flag word; block 0 publishes its bits.
+// s_bad[0] collects this call's bits, s_bad[1] receives the flag word, read
+// by one thread of the block: the word is one address that every block of
+// a launch reads at agent scope (past the XCDs' own L2s), so a read per wave
+// would queue a launch's waves on one memory channel.
 __device__ __forceinline__ uint32_t stage_and_validate(const int32_t *cu, int64_t n_seq,
                                                        int64_t total, uint32_t *err,
-                                                       int32_t *s_cu, uint32_t *s_bad,
+                                                       int32_t *s_cu, uint32_t (&s_bad)[2],
                                                        int in_lds, bool publish) {
     const int tid = threadIdx.x;
-    if (tid == 0) *s_bad = 0u;
+    if (tid == 0) s_bad[0] = 0u;
     if (in_lds) {
         for (int64_t i = tid; i <= n_seq; i += blockDim.x) s_cu[i] = cu[i];
     }
@@ -451,15 +455,15 @@ __device__ __forceinline__ uint32_t stage_and_validate(const int32_t *cu, int64_
             if (s_cu[0] != 0) bad |= kFirstNonzero;
             if (static_cast<int64_t>(s_cu[n_seq]) != total) bad |= kLastMismatch;
         }
-        if (bad) atomicOr(s_bad, bad);
+        if (bad) atomicOr(&s_bad[0], bad);
     }
-    __syncthreads();
-    bad = *s_bad;
-    if (publish && tid == 0 && bad) atomicOr(err, bad);
     // The word may hold bits of an earlier call (sticky) or, when the
     // offsets did not fit in LDS, of the validation kernel run just before.
-    const uint32_t prior = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return bad | prior;
+    if (tid == 0) s_bad[1] = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    bad = s_bad[0];
+    if (publish && tid == 0 && bad) atomicOr(err, bad);
+    return bad | s_bad[1];
 }
 
 // Largest i in [0, n) with cu[i] <= t, for offsets already validated
@@ -643,7 +647,7 @@ template <int W, int VEC, bool SILU, int ROWS, int FK, bool PIPE>
 __global__ __launch_bounds__(256) CCV_FWD_ATTR void k_fwd_chan(FwdArgs a) {
     constexpr bool PACKED = ROWS == kRowsPacked;
     __shared__ int32_t s_cu[PACKED ? kLdsCuMax : 1];
-    __shared__ uint32_t s_bad;
+    __shared__ uint32_t s_bad[2];
     const TileSpan ts = split_tile<CCV_TILE_ORDER>(a, a.n_gblk, kFwdWavesT);
     const int64_t b = ts.b, gb = ts.c;
     // The wave index is uniform over the wave; readfirstlane tells the
@@ -656,7 +660,7 @@ __global__ __launch_bounds__(256) CCV_FWD_ATTR void k_fwd_chan(FwdArgs a) {
     const int lane = threadIdx.x % kWaveSize;
 
     if constexpr (PACKED) {
-        if (stage_and_validate(a.cu, a.n_seq, a.T, a.err, s_cu, &s_bad, a.cu_in_lds,
+        if (stage_and_validate(a.cu, a.n_seq, a.T, a.err, s_cu, s_bad, a.cu_in_lds,
                                blockIdx.x == 0))
             return;  // malformed or sticky: write nothing
     }
@@ -1082,7 +1086,7 @@ __global__ __launch_bounds__(256) CCV_BWD_ATTR void k_bwd_chan(BwdArgs a) {
     constexpr int kRed = kWavesPerBlock * (W + 1) * (CH + 1);
     constexpr int kBuf = (PACKED && kLdsCuMax > kRed) ? kLdsCuMax : kRed;
     __shared__ float s_buf[kBuf];
-    __shared__ uint32_t s_bad;
+    __shared__ uint32_t s_bad[2];
     int32_t *s_cu = reinterpret_cast<int32_t *>(s_buf);
     float (*s_red)[W + 1][CH + 1] = reinterpret_cast<float (*)[W + 1][CH + 1]>(s_buf);
     // Packed rows measured faster with time blocks innermost, the others
@@ -1100,7 +1104,7 @@ __global__ __launch_bounds__(256) CCV_BWD_ATTR void k_bwd_chan(BwdArgs a) {
     const int lane = threadIdx.x % kWaveSize;
 
     if constexpr (PACKED) {
-        if (stage_and_validate(a.cu, a.n_seq, a.T, a.err, s_cu, &s_bad, a.cu_in_lds,
+        if (stage_and_validate(a.cu, a.n_seq, a.T, a.err, s_cu, s_bad, a.cu_in_lds,
                                blockIdx.x == 0))
             return;  // uniform over the block: no barrier is left waiting
     }
@@ -1560,6 +1564,595 @@ void k_bwd_tc(BwdArgs a) {
     if (!tc_item(a, it)) return;
     if (a.nt_load) bwd_tc_chunk<W, SILU, FK, true>(a, it);
     else bwd_tc_chunk<W, SILU, FK, false>(a, it);
+}
+
+// ===========================================================================
+// Time lanes for packed and seq_idx rows (unit stride along T)
+//
+// The lanes, tiles and chunks of the dense time-lane kernels, with one id
+// per token: the index of its sequence (packed rows, B = 1, from the offsets
+// staged in LDS) or its seq_idx entry.  A tap contributes the input only
+// when its token has the output token's id; otherwise it contributes zero,
+// or, on packed rows with initial states, the state slot of the output
+// token's sequence (the tap reaches before that sequence's start).  Ids move
+// across lanes with the same DPP shifts as the values.  Positions outside
+// the row carry kNoId: no sequence index is negative, and a seq_idx id equal
+// to it meets only zero inputs (before the row) or zero gradients (past it).
+// ===========================================================================
+constexpr int32_t kNoId = -1;
+
+__device__ __forceinline__ int32_t lane_up_id(int32_t v, int32_t first) {
+    return __builtin_amdgcn_update_dpp(first, v, kDppWaveShr1, 0xf, 0xf, false);
+}
+__device__ __forceinline__ int32_t lane_down_id(int32_t v, int32_t last) {
+    return __builtin_amdgcn_update_dpp(last, v, kDppWaveShl1, 0xf, 0xf, false);
+}
+__device__ __forceinline__ int32_t from_lane_id(int32_t v, int l) {
+    return __builtin_amdgcn_readlane(v, l);
+}
+
+// Token ids of one row.
+template <int ROWS>
+struct TcRowIds {
+    const int32_t *cu;  // packed: the offsets (validated), N + 1 entries
+    int64_t n;          // packed: N
+    const int32_t *sq;  // seq_idx: this row's ids
+    int64_t st;         // seq_idx: their stride
+    bool vec;           // seq_idx: unit stride, 16-byte aligned rows
+    int64_t T;
+    __device__ __forceinline__ int32_t at(int64_t p) const {
+        if (p < 0 || p >= T) return kNoId;
+        if constexpr (ROWS == kRowsPacked) return static_cast<int32_t>(find_row(cu, n, p));
+        else return sq[p * st];
+    }
+    // Packed rows: a lane's walk over the offsets, i = the sequence of the
+    // last token it has reached and nb = cu[i+1], the next offset.  A chunk
+    // starts every lane from one search (at the chunk's first halo token);
+    // the lanes then walk forward through their tiles and read the offsets
+    // only when they cross one.
+    struct Walk {
+        int64_t i, nb;
+    };
+    __device__ __forceinline__ Walk begin(int64_t p0) const {
+        Walk wk{0, 0};
+        if constexpr (ROWS == kRowsPacked) {
+            wk.i = find_row(cu, n, p0 > 0 ? p0 : 0);
+            wk.nb = cu[wk.i + 1];
+        }
+        return wk;
+    }
+    // The id of position p (kNoId outside the row), advancing a walk (p
+    // never decreases along it); seq_idx rows read it.
+    __device__ __forceinline__ int32_t walk_to(Walk &wk, int64_t p) const {
+        if constexpr (ROWS == kRowsPacked) {
+            if (p < 0 || p >= T) return kNoId;
+            while (p >= wk.nb) {
+                ++wk.i;
+                wk.nb = cu[wk.i + 1];
+            }
+            return static_cast<int32_t>(wk.i);
+        } else {
+            return at(p);
+        }
+    }
+    // The ids of the kTcE tokens from t (kNoId past the row); t never
+    // decreases along a walk.
+    __device__ __forceinline__ void lane_ids(int64_t t, int32_t (&id)[kTcE], Walk &wk) const {
+        if constexpr (ROWS == kRowsPacked) {
+#pragma unroll
+            for (int e = 0; e < kTcE; ++e) {
+                const int64_t p = t + e;
+                if (p < T) {
+                    // cu[n] = T > p ends the walk within the offsets
+                    while (p >= wk.nb) {
+                        ++wk.i;
+                        wk.nb = cu[wk.i + 1];
+                    }
+                    id[e] = static_cast<int32_t>(wk.i);
+                } else {
+                    id[e] = kNoId;
+                }
+            }
+        } else {
+            if (vec && t + kTcE <= T) {
+                // t is a multiple of kTcE: two 16-byte loads
+                const u32x4_t *q = reinterpret_cast<const u32x4_t *>(sq + t);
+                const u32x4_t lo = q[0], hi = q[1];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    id[e] = static_cast<int32_t>(lo[e]);
+                    id[4 + e] = static_cast<int32_t>(hi[e]);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < kTcE; ++e) id[e] = t + e < T ? sq[(t + e) * st] : kNoId;
+            }
+        }
+    }
+};
+
+// Tap values of output token i of a window (xe/ie: values and ids of the
+// W-1 tokens before the lane's first token, then its kTcE tokens): the input
+// where the ids match, else zero, or on packed rows with initial states the
+// slot r + k of the token's sequence, r being the token's offset in it.
+template <int W, int ROWS>
+__device__ __forceinline__ void tc_taps(const float (&xe)[W - 1 + kTcE],
+                                        const int32_t (&ie)[W - 1 + kTcE], int i, int64_t p,
+                                        const int32_t *cu, const uint16_t *ir,
+                                        const Strided3 &init, float (&xv)[W]) {
+    const int32_t own = ie[i + W - 1];
+#pragma unroll
+    for (int k = 0; k < W; ++k) xv[k] = ie[i + k] == own ? xe[i + k] : 0.0f;
+    if constexpr (ROWS == kRowsPacked) {
+        // Only the first W-1 tokens of a sequence reach before its start,
+        // and there the oldest tap's id differs.  Tokens past the row
+        // (kNoId) are never written and need no state.
+        if (ir && own != kNoId && ie[i] != own) {
+            const int64_t r = p - cu[own];
+#pragma unroll
+            for (int k = 0; k < W - 1; ++k)
+                if (ie[i + k] != own)
+                    xv[k] = bf16_bits_to_f32(ir[own * init.s0 + (r + k) * init.s2]);
+        }
+    }
+}
+
+template <int W, bool SILU, int FK, bool NTL, int ROWS>
+__device__ __forceinline__ void fwd_tcr_chunk(const FwdArgs &a, const TcItem &it,
+                                              const TcRowIds<ROWS> &ids) {
+    constexpr bool PACKED = ROWS == kRowsPacked;
+    const int lane = threadIdx.x % kWaveSize;
+    const uint16_t *xr = static_cast<const uint16_t *>(a.x.ptr) + it.b * a.x.s0 + it.d * a.x.s1;
+    uint16_t *yr = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.y.ptr)) +
+                   it.b * a.y.s0 + it.d * a.y.s1;
+    // The channel's initial-state column (packed rows: indexed by sequence).
+    const uint16_t *ir =
+        PACKED && a.init.ptr ? static_cast<const uint16_t *>(a.init.ptr) + it.d * a.init.s1
+                             : nullptr;
+    // Left halo (values and ids of the W-1 tokens before the chunk; before
+    // the row, zero and kNoId), the filter, then the tiles and their ids.
+    uint16_t lh[W - 1];
+    int32_t cid[W - 1];
+    auto wk = ids.begin(it.t0 - (W - 1));
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) {
+        const int64_t p = it.t0 - (W - 1) + j;
+        lh[j] = xr[p >= 0 ? p : 0];
+        cid[j] = ids.walk_to(wk, p);
+    }
+    float w[W][1], bias[1];
+    load_filter<W, 1, FK>(a.w, a.w_sd, a.w_sk, a.bias, a.b_s, it.d, w, bias);
+    Raw<8> raw[kTcTilesFwd];
+    // seq_idx ids are loads and go out with the tiles; packed ids come from
+    // the LDS offsets and are worked out tile by tile (fewer live registers)
+    int32_t tid[PACKED ? 1 : kTcTilesFwd][kTcE];
+#pragma unroll
+    for (int c = 0; c < kTcTilesFwd; ++c) {
+        const int64_t t = it.t0 + c * kTcTile + lane * kTcE;
+        if (t < it.t1) raw[c] = tc_load<NTL>(xr, t, it.t1);
+        else raw[c].v = u32x4_t{0u, 0u, 0u, 0u};
+        if constexpr (!PACKED) ids.lane_ids(t < it.t1 ? t : a.T, tid[c], wk);
+    }
+    float carry[W - 1];
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j)
+        carry[j] = it.t0 - (W - 1) + j >= 0 ? bf16_bits_to_f32(lh[j]) : 0.0f;
+
+#pragma unroll
+    for (int c = 0; c < kTcTilesFwd; ++c) {
+        const int64_t tt = it.t0 + c * kTcTile;
+        if (tt >= it.t1) break;
+        const int64_t t = tt + lane * kTcE;
+        float v[kTcE], xe[W - 1 + kTcE], out[kTcE];
+        int32_t ie[W - 1 + kTcE], cur[kTcE];
+        if constexpr (PACKED) {
+            ids.lane_ids(t < it.t1 ? t : a.T, cur, wk);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kTcE; ++i) cur[i] = tid[c][i];
+        }
+        unpack<8>(raw[c], v);
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) {
+            xe[j] = lane_up(v[kTcE - (W - 1) + j], carry[j]);
+            ie[j] = lane_up_id(cur[kTcE - (W - 1) + j], cid[j]);
+        }
+#pragma unroll
+        for (int i = 0; i < kTcE; ++i) {
+            xe[W - 1 + i] = v[i];
+            ie[W - 1 + i] = cur[i];
+        }
+#pragma unroll
+        for (int i = 0; i < kTcE; ++i) {
+            float xv[W];
+            tc_taps<W, ROWS>(xe, ie, i, t + i, ids.cu, ir, a.init, xv);
+            float z = bias[0];
+#pragma unroll
+            for (int k = 0; k < W; ++k) z = fmaf(w[k][0], xv[k], z);
+            out[i] = act<SILU>(z);
+        }
+        if (t < it.t1) tc_store<true>(yr, t, it.t1, out);
+        if constexpr (PACKED) {
+            // Each sequence that ends among the lane's tokens writes its
+            // final state: the last W-1 extended tokens, bit for bit.
+            if (a.fin.ptr && t < it.t1) {
+                const int64_t te = min(t + kTcE, it.t1);
+                for (int64_t i = cur[0]; i < ids.n; ++i) {
+                    const int64_t e = ids.cu[i + 1], s = ids.cu[i];
+                    if (e > te) break;
+#pragma unroll
+                    for (int j = 0; j < W - 1; ++j) {
+                        const int64_t q = e - (W - 1) + j;
+                        uint16_t bits = 0;
+                        if (q >= s) bits = xr[q];
+                        else if (ir) bits = ir[i * a.init.s0 + (q - s + W - 1) * a.init.s2];
+                        const_cast<uint16_t *>(static_cast<const uint16_t *>(a.fin.ptr))
+                            [i * a.fin.s0 + it.d * a.fin.s1 + j * a.fin.s2] = bits;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) {
+            carry[j] = from_lane(v[kTcE - (W - 1) + j], kWaveSize - 1);
+            cid[j] = from_lane_id(cur[kTcE - (W - 1) + j], kWaveSize - 1);
+        }
+    }
+}
+
+template <int W, bool SILU, int FK, bool NTL, int ROWS>
+__device__ __forceinline__ void bwd_tcr_chunk(const BwdArgs &a, const TcItem &it,
+                                              const TcRowIds<ROWS> &ids) {
+    constexpr bool PACKED = ROWS == kRowsPacked;
+    constexpr bool BIAS = fk_bias(FK);
+    const int lane = threadIdx.x % kWaveSize;
+    const uint16_t *xr = static_cast<const uint16_t *>(a.x.ptr) + it.b * a.x.s0 + it.d * a.x.s1;
+    const uint16_t *dyr = static_cast<const uint16_t *>(a.dy.ptr) + it.b * a.dy.s0 + it.d * a.dy.s1;
+    uint16_t *dxr = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.dx.ptr)) +
+                    it.b * a.dx.s0 + it.d * a.dx.s1;
+    const uint16_t *ir =
+        PACKED && a.init.ptr ? static_cast<const uint16_t *>(a.init.ptr) + it.d * a.init.s1
+                             : nullptr;
+    // Single tokens first: the left halo (values, ids); the right halo (lane
+    // j < W-1 reads token t1 + j of x and dy, the other lanes and tokens
+    // past the row an in-row token that is dropped) and its ids.
+    uint16_t lh[W - 1];
+    int32_t cid[W - 1];
+    auto wk = ids.begin(it.t0 - (W - 1));
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) {
+        const int64_t p = it.t0 - (W - 1) + j;
+        lh[j] = xr[p >= 0 ? p : 0];
+        cid[j] = ids.walk_to(wk, p);
+    }
+    const int64_t rq = min(it.t1 + lane, a.T - 1);
+    const uint16_t rh_x = xr[rq], rh_dy = dyr[rq];
+    float w[W][1], bias[1];
+    load_filter<W, 1, FK>(a.w, a.w_sd, a.w_sk, a.bias, a.b_s, it.d, w, bias);
+    Raw<8> rx[kTcTilesBwd], rd[kTcTilesBwd];
+    int32_t tid[PACKED ? 1 : kTcTilesBwd][kTcE];  // as in the forward
+#pragma unroll
+    for (int c = 0; c < kTcTilesBwd; ++c) {
+        const int64_t t = it.t0 + c * kTcTile + lane * kTcE;
+        if (t < it.t1) {
+            rx[c] = tc_load<NTL>(xr, t, it.t1);
+            rd[c] = tc_load<NTL>(dyr, t, it.t1);
+        } else {
+            rx[c].v = u32x4_t{0u, 0u, 0u, 0u};
+            rd[c].v = u32x4_t{0u, 0u, 0u, 0u};
+        }
+        if constexpr (!PACKED) ids.lane_ids(t < it.t1 ? t : a.T, tid[c], wk);
+    }
+    // lane j < W-1: the id of token t1 + j; packed rows walk to it after
+    // the tiles (past every token of them)
+    int32_t rh_id = 0;
+    if constexpr (!PACKED) rh_id = ids.walk_to(wk, it.t1 + lane);
+    float carry[W - 1];
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j)
+        carry[j] = it.t0 - (W - 1) + j >= 0 ? bf16_bits_to_f32(lh[j]) : 0.0f;
+    float dwacc[W], dbacc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < W; ++k) dwacc[k] = 0.0f;
+    const uint16_t *dfr = PACKED && a.dfin.ptr
+                              ? static_cast<const uint16_t *>(a.dfin.ptr) + it.d * a.dfin.s1
+                              : nullptr;
+
+    // dx of the lane's tokens of the tile at tt from its g's and ids, and
+    // the W-1 g's and ids that follow the lane (`after`: the next tile's, or
+    // the right halo's, for lane 63).  `before` is the id of the token before
+    // the tile (lane 0's left neighbour).  Packed rows add the final-state
+    // gradient to a sequence's last W-1 tokens and write dinit where a
+    // sequence starts.
+    auto emit = [&](int64_t tt, const float (&g)[kTcE], const int32_t (&id)[kTcE],
+                    const float (&after)[W - 1], const int32_t (&after_id)[W - 1],
+                    int32_t before) {
+        float ge[kTcE + W - 1], v[kTcE];
+        int32_t ige[kTcE + W - 1];
+#pragma unroll
+        for (int i = 0; i < kTcE; ++i) {
+            ge[i] = g[i];
+            ige[i] = id[i];
+        }
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) {
+            ge[kTcE + j] = lane_down(g[j], after[j]);
+            ige[kTcE + j] = lane_down_id(id[j], after_id[j]);
+        }
+        const int64_t t = tt + lane * kTcE;
+#pragma unroll
+        for (int i = 0; i < kTcE; ++i) {
+            const int32_t own = ige[i];
+            float acc = w[0][0] * (ige[i + W - 1] == own ? ge[i + W - 1] : 0.0f);
+#pragma unroll
+            for (int j = W - 2; j >= 0; --j)
+                acc = fmaf(w[W - 1 - j][0], ige[i + j] == own ? ge[i + j] : 0.0f, acc);
+            v[i] = acc;
+        }
+        if constexpr (PACKED) {
+            // A token q among the last W-1 of its sequence: position q+W-1
+            // is past the sequence's end.
+            if (dfr) {
+#pragma unroll
+                for (int i = 0; i < kTcE; ++i) {
+                    if (t + i < it.t1 && ige[i + W - 1] != ige[i]) {
+                        const int64_t jj = t + i - (ids.cu[ige[i] + 1] - (W - 1));
+                        v[i] += bf16_bits_to_f32(dfr[ige[i] * a.dfin.s0 + jj * a.dfin.s2]);
+                    }
+                }
+            }
+            if (a.dinit.ptr) {
+                const int32_t prev = lane_up_id(id[kTcE - 1], before);
+#pragma unroll
+                for (int i = 0; i < kTcE; ++i) {
+                    const int32_t own = ige[i];
+                    const int32_t left = i == 0 ? prev : ige[i - 1];
+                    if (t + i < it.t1 && left != own) {
+                        // dinit[own][j] = dx_ext at s-(W-1)+j (s = t+i): the
+                        // g's at s+j-k for k <= j that lie in the sequence,
+                        // plus the final-state gradient landing there.
+                        const int64_t s = t + i, e = ids.cu[own + 1];
+#pragma unroll
+                        for (int j = 0; j < W - 1; ++j) {
+                            float acc = w[0][0] * (ige[i + j] == own ? ge[i + j] : 0.0f);
+#pragma unroll
+                            for (int k = 1; k < W; ++k)
+                                acc = fmaf(w[k][0],
+                                           k <= j && ige[i + j - k] == own ? ge[i + j - k] : 0.0f,
+                                           acc);
+                            const int64_t jj = s - (W - 1) + j - (e - (W - 1));
+                            if (dfr && jj >= 0 && jj < W - 1)
+                                acc += bf16_bits_to_f32(dfr[own * a.dfin.s0 + jj * a.dfin.s2]);
+                            const_cast<uint16_t *>(static_cast<const uint16_t *>(a.dinit.ptr))
+                                [own * a.dinit.s0 + it.d * a.dinit.s1 + j * a.dinit.s2] =
+                                    to_bf16_bits(acc);
+                        }
+                    }
+                }
+            }
+        }
+        if (t < it.t1) tc_store<true>(dxr, t, it.t1, v);
+    };
+
+    float gprev[kTcE];
+    int32_t idprev[kTcE], before_prev = kNoId;
+    int64_t tprev = -1;
+#pragma unroll
+    for (int c = 0; c < kTcTilesBwd; ++c) {
+        const int64_t tt = it.t0 + c * kTcTile;
+        if (tt >= it.t1) break;
+        const int64_t t = tt + lane * kTcE;
+        float v[kTcE], dyv[kTcE], xe[W - 1 + kTcE], g[kTcE];
+        int32_t ie[W - 1 + kTcE], cur[kTcE];
+        if constexpr (PACKED) {
+            ids.lane_ids(t < it.t1 ? t : a.T, cur, wk);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kTcE; ++i) cur[i] = tid[c][i];
+        }
+        unpack<8>(rx[c], v);
+        unpack<8>(rd[c], dyv);
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) {
+            xe[j] = lane_up(v[kTcE - (W - 1) + j], carry[j]);
+            ie[j] = lane_up_id(cur[kTcE - (W - 1) + j], cid[j]);
+        }
+#pragma unroll
+        for (int i = 0; i < kTcE; ++i) {
+            xe[W - 1 + i] = v[i];
+            ie[W - 1 + i] = cur[i];
+        }
+#pragma unroll
+        for (int i = 0; i < kTcE; ++i) {
+            float xv[W];
+            tc_taps<W, ROWS>(xe, ie, i, t + i, ids.cu, ir, a.init, xv);
+            float z = bias[0];
+#pragma unroll
+            for (int k = 0; k < W; ++k) z = fmaf(w[k][0], xv[k], z);
+            g[i] = dyv[i] * act_slope<SILU>(z);  // zero past the chunk (dy reads 0)
+#pragma unroll
+            for (int k = 0; k < W; ++k) dwacc[k] = fmaf(g[i], xv[k], dwacc[k]);
+            if constexpr (BIAS) dbacc += g[i];
+        }
+        if (tprev >= 0) {
+            float after[W - 1];
+            int32_t after_id[W - 1];
+#pragma unroll
+            for (int j = 0; j < W - 1; ++j) {
+                after[j] = from_lane(g[j], 0);
+                after_id[j] = from_lane_id(cur[j], 0);
+            }
+            emit(tprev, gprev, idprev, after, after_id, before_prev);
+        }
+#pragma unroll
+        for (int i = 0; i < kTcE; ++i) {
+            gprev[i] = g[i];
+            idprev[i] = cur[i];
+        }
+        tprev = tt;
+        before_prev = cid[W - 2];
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) {
+            carry[j] = from_lane(v[kTcE - (W - 1) + j], kWaveSize - 1);
+            cid[j] = from_lane_id(cur[kTcE - (W - 1) + j], kWaveSize - 1);
+        }
+    }
+    if constexpr (PACKED) rh_id = ids.walk_to(wk, it.t1 + lane);
+    // Right halo: g at t1 .. t1+W-2 (zero past the row), in every lane.  A
+    // chunk that does not end the row is a whole number of tiles, so
+    // `carry`/`cid` hold the W-1 tokens before t1.
+    {
+        float xw[2 * (W - 1)], after[W - 1];
+        int32_t iw[2 * (W - 1)], after_id[W - 1];
+        const float hx = bf16_bits_to_f32(rh_x), hd = bf16_bits_to_f32(rh_dy);
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) {
+            xw[j] = carry[j];
+            iw[j] = cid[j];
+            xw[W - 1 + j] = from_lane(hx, j);
+            iw[W - 1 + j] = from_lane_id(rh_id, j);
+        }
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) {
+            const int32_t own = iw[j + W - 1];
+            const int64_t p = it.t1 + j;
+            float z = bias[0];
+#pragma unroll
+            for (int k = 0; k < W; ++k) {
+                float xv = iw[j + k] == own ? xw[j + k] : 0.0f;
+                if constexpr (PACKED) {
+                    if (ir && iw[j + k] != own && p < a.T)
+                        xv = bf16_bits_to_f32(ir[own * a.init.s0 + (p - ids.cu[own] + k) * a.init.s2]);
+                }
+                z = fmaf(w[k][0], xv, z);
+            }
+            after[j] = p < a.T ? from_lane(hd, j) * act_slope<SILU>(z) : 0.0f;
+            after_id[j] = iw[W - 1 + j];
+        }
+        emit(tprev, gprev, idprev, after, after_id, before_prev);
+    }
+    // dW/dB of the chunk: a wave sum, then one atomic or one partial per tap.
+#pragma unroll
+    for (int k = 0; k < W; ++k) dwacc[k] = wave_sum(dwacc[k]);
+    if constexpr (BIAS) dbacc = wave_sum(dbacc);
+    if (lane == 0) {
+        if (a.partial) {
+            const int64_t pidx = it.b * a.n_chunk + it.chunk;
+            float *pr = a.partial + (pidx * a.D + it.d) * a.part_stride;
+#pragma unroll
+            for (int k = 0; k < W; ++k) pr[k] = dwacc[k];
+            if (a.part_stride > W) pr[W] = dbacc;
+        } else {
+#pragma unroll
+            for (int k = 0; k < W; ++k) atomicAdd(a.dw + it.d * W + k, dwacc[k]);
+            if constexpr (BIAS) atomicAdd(a.db + it.d, dbacc);
+        }
+    }
+}
+
+// The row ids of a wave's row.  Packed rows read the offsets from `cu`:
+// the block's LDS copy or global memory; the caller passes the LDS array
+// itself (not a pointer chosen at run time), so that its reads compile to
+// LDS instructions rather than flat loads that would queue behind the bulk
+// global loads.
+template <int ROWS, typename A>
+__device__ __forceinline__ TcRowIds<ROWS> tc_row_ids(const A &a, const TcItem &it,
+                                                     const int32_t *cu) {
+    TcRowIds<ROWS> ids;
+    ids.T = a.T;
+    if constexpr (ROWS == kRowsPacked) {
+        ids.cu = cu;
+        ids.n = a.n_seq;
+        ids.sq = nullptr;
+        ids.st = 0;
+        ids.vec = false;
+    } else {
+        ids.cu = nullptr;
+        ids.n = 0;
+        ids.sq = a.seq + it.b * a.seq_sb;
+        ids.st = a.seq_st;
+        ids.vec = a.seq_vec != 0;
+    }
+    return ids;
+}
+
+// A packed chunk whose tokens and halos, [t0-(W-1), t1+(W-1)), lie inside
+// one sequence: no tap crosses a sequence start, no final state or state
+// gradient is written, and the dense rows' kernels compute it exactly
+// (wave-uniform).  seq_idx rows always take the id path.
+template <int W, int ROWS>
+__device__ __forceinline__ bool tc_interior(const TcRowIds<ROWS> &ids, const TcItem &it) {
+    if constexpr (ROWS == kRowsPacked) {
+        if (it.t0 < W - 1) return false;
+        const int64_t i = find_row(ids.cu, ids.n, it.t0 - (W - 1));
+        return it.t1 + (W - 1) <= ids.cu[i + 1];
+    } else {
+        return false;
+    }
+}
+
+// One chunk of a packed or seq_idx row: a packed chunk whose tokens and
+// halos lie inside one sequence takes the dense rows' code.
+template <int W, bool SILU, int FK, int ROWS>
+__device__ __forceinline__ void fwd_tcr_run(const FwdArgs &a, const TcItem &it,
+                                            const TcRowIds<ROWS> &ids) {
+    if (tc_interior<W, ROWS>(ids, it)) {
+        if (a.nt_load) fwd_tc_chunk<W, SILU, FK, true>(a, it);
+        else fwd_tc_chunk<W, SILU, FK, false>(a, it);
+        return;
+    }
+    if (a.nt_load) fwd_tcr_chunk<W, SILU, FK, true, ROWS>(a, it, ids);
+    else fwd_tcr_chunk<W, SILU, FK, false, ROWS>(a, it, ids);
+}
+
+template <int W, bool SILU, int FK, int ROWS>
+__device__ __forceinline__ void bwd_tcr_run(const BwdArgs &a, const TcItem &it,
+                                            const TcRowIds<ROWS> &ids) {
+    if (tc_interior<W, ROWS>(ids, it)) {
+        if (a.nt_load) bwd_tc_chunk<W, SILU, FK, true>(a, it);
+        else bwd_tc_chunk<W, SILU, FK, false>(a, it);
+        return;
+    }
+    if (a.nt_load) bwd_tcr_chunk<W, SILU, FK, true, ROWS>(a, it, ids);
+    else bwd_tcr_chunk<W, SILU, FK, false, ROWS>(a, it, ids);
+}
+
+// Packed rows pass the offsets' LDS array itself when they are staged (see
+// tc_row_ids), global memory otherwise.
+template <int W, bool SILU, int FK, int ROWS>
+__global__ __launch_bounds__(256) void k_fwd_tcr(FwdArgs a) {
+    constexpr bool PACKED = ROWS == kRowsPacked;
+    __shared__ int32_t s_cu[PACKED ? kLdsCuMax : 1];
+    __shared__ uint32_t s_bad[2];
+    if constexpr (PACKED) {
+        if (stage_and_validate(a.cu, a.n_seq, a.T, a.err, s_cu, s_bad, a.cu_in_lds,
+                               blockIdx.x == 0))
+            return;  // malformed or sticky: write nothing
+    }
+    TcItem it;
+    if (!tc_item(a, it)) return;
+    if (PACKED && a.cu_in_lds)
+        fwd_tcr_run<W, SILU, FK, ROWS>(a, it, tc_row_ids<ROWS>(a, it, s_cu));
+    else
+        fwd_tcr_run<W, SILU, FK, ROWS>(a, it, tc_row_ids<ROWS>(a, it, a.cu));
+}
+
+template <int W, bool SILU, int FK, int ROWS>
+__global__ __launch_bounds__(256) void k_bwd_tcr(BwdArgs a) {
+    constexpr bool PACKED = ROWS == kRowsPacked;
+    __shared__ int32_t s_cu[PACKED ? kLdsCuMax : 1];
+    __shared__ uint32_t s_bad[2];
+    if constexpr (PACKED) {
+        if (stage_and_validate(a.cu, a.n_seq, a.T, a.err, s_cu, s_bad, a.cu_in_lds,
+                               blockIdx.x == 0))
+            return;  // uniform over the block
+    }
+    TcItem it;
+    if (!tc_item(a, it)) return;
+    if (PACKED && a.cu_in_lds)
+        bwd_tcr_run<W, SILU, FK, ROWS>(a, it, tc_row_ids<ROWS>(a, it, s_cu));
+    else
+        bwd_tcr_run<W, SILU, FK, ROWS>(a, it, tc_row_ids<ROWS>(a, it, a.cu));
 }
 
 // ===========================================================================

@@ -50,11 +50,16 @@ hipError_t fwd_vec(const FwdArgs &a, int silu, int rows, int fk, hipStream_t s, 
 
 // The software-pipelined forward is built for 8-channel lanes of dense and
 // packed rows only.
-// Time-lane kernels: dense rows only.
+// Time-lane kernels: dense rows, and packed or seq_idx rows (per-token ids).
 template <int W>
-hipError_t fwd_tc(const FwdArgs &a, int silu, int fk, hipStream_t s) {
-#define CCV_TC(S, F) \
-    if (!!silu == S && fk == F) return launch(k_fwd_tc<W, S, F>, a.n_block, a, s);
+hipError_t fwd_tc(const FwdArgs &a, int silu, int fk, int rows, hipStream_t s) {
+#define CCV_TC(S, F)                                                                    \
+    if (!!silu == S && fk == F) {                                                       \
+        if (rows == kRowsDense) return launch(k_fwd_tc<W, S, F>, a.n_block, a, s);       \
+        if (rows == kRowsPacked)                                                        \
+            return launch(k_fwd_tcr<W, S, F, kRowsPacked>, a.n_block, a, s);            \
+        if (rows == kRowsSeq) return launch(k_fwd_tcr<W, S, F, kRowsSeq>, a.n_block, a, s); \
+    }
     CCV_TC(true, kBf16) CCV_TC(true, kBf16Bias) CCV_TC(true, kF32) CCV_TC(true, kF32Bias)
     CCV_TC(false, kBf16) CCV_TC(false, kBf16Bias) CCV_TC(false, kF32) CCV_TC(false, kF32Bias)
 #undef CCV_TC
@@ -62,9 +67,14 @@ hipError_t fwd_tc(const FwdArgs &a, int silu, int fk, hipStream_t s) {
 }
 
 template <int W>
-hipError_t bwd_tc(const BwdArgs &a, int silu, int fk, hipStream_t s) {
-#define CCV_TC(S, F) \
-    if (!!silu == S && fk == F) return launch(k_bwd_tc<W, S, F>, a.n_block, a, s);
+hipError_t bwd_tc(const BwdArgs &a, int silu, int fk, int rows, hipStream_t s) {
+#define CCV_TC(S, F)                                                                    \
+    if (!!silu == S && fk == F) {                                                       \
+        if (rows == kRowsDense) return launch(k_bwd_tc<W, S, F>, a.n_block, a, s);       \
+        if (rows == kRowsPacked)                                                        \
+            return launch(k_bwd_tcr<W, S, F, kRowsPacked>, a.n_block, a, s);            \
+        if (rows == kRowsSeq) return launch(k_bwd_tcr<W, S, F, kRowsSeq>, a.n_block, a, s); \
+    }
     CCV_TC(true, kBf16) CCV_TC(true, kBf16Bias) CCV_TC(true, kF32) CCV_TC(true, kF32Bias)
     CCV_TC(false, kBf16) CCV_TC(false, kBf16Bias) CCV_TC(false, kF32) CCV_TC(false, kF32Bias)
 #undef CCV_TC
@@ -78,7 +88,7 @@ hipError_t fwd_dispatch(const FwdArgs &a, int vec, int silu, int rows, hipStream
     if (vec == kVecTime) {
         if (cap) *cap = 0;
         if (s == kQueryStream) return hipSuccess;
-        return rows == kRowsDense ? fwd_tc<W>(a, silu, fk, s) : hipErrorInvalidValue;
+        return fwd_tc<W>(a, silu, fk, rows, s);
     }
     if (vec == 8 && a.pipe && rows != kRowsSeq)
         return fwd_vec<W, 8, true>(a, silu, rows, fk, s, cap);
@@ -117,7 +127,7 @@ hipError_t bwd_dispatch(const BwdArgs &a, int vec, int silu, int rows, hipStream
     if (vec == kVecTime) {
         if (cap) *cap = 0;
         if (s == kQueryStream) return hipSuccess;
-        return rows == kRowsDense ? bwd_tc<W>(a, silu, fk, s) : hipErrorInvalidValue;
+        return bwd_tc<W>(a, silu, fk, rows, s);
     }
     if (vec == 4) return bwd_vec<W, 4>(a, silu, rows, fk, s, cap);
     if (vec == 1) return bwd_vec<W, 1>(a, silu, rows, fk, s, cap);

@@ -85,6 +85,7 @@ struct FwdArgs {
     int64_t n_seq;             // N (packed) ; unused dense
     const int32_t *seq;        // seq_idx [B,T] or nullptr
     int64_t seq_sb, seq_st;
+    int seq_vec;               // unit id stride, 16-byte aligned id rows
     uint32_t *err;             // flag word (packed) or nullptr
     int64_t B, D, T;           // T = tokens per batch row (dense) or the packed total
     int64_t L;                 // time steps per wave
@@ -122,6 +123,7 @@ struct BwdArgs {
     int64_t n_seq;
     const int32_t *seq;        // seq_idx [B,T] or nullptr
     int64_t seq_sb, seq_st;
+    int seq_vec;               // as in FwdArgs
     uint32_t *err;
     int64_t B, D, T, L, n_chunk, n_tblk, n_group, n_gblk, n_block;
     int64_t Tm, Lt, n_tblk_t, n_block_m;  // main and tail chunks, as in FwdArgs

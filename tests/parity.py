@@ -149,7 +149,10 @@ def guarded_act(B, D, T, layout, device, dtype=torch.bfloat16):
         st = _fill(torch.empty(B, T + 2, D + 16, dtype=dtype, device=device))
         view = st[:, 1:1 + T, 8:8 + D].transpose(1, 2)
     else:
-        st = _fill(torch.empty(B, D + 2, T + 16, dtype=dtype, device=device))
+        # rows padded to a multiple of 8 tokens, so that every row starts on
+        # a 16-byte boundary (what the time-lane kernels need of an output)
+        Tp = (T + 7) // 8 * 8
+        st = _fill(torch.empty(B, D + 2, Tp + 16, dtype=dtype, device=device))
         view = st[:, 1:1 + D, 8:8 + T]
     return Guarded(st, view)
 

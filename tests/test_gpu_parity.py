@@ -825,13 +825,18 @@ def test_update_several_tokens(B, D, L, W, bias, wdt, layout):
     check_exact_bf16("conv_state after", g_state, ost)
 
 
-def test_packed_and_seq_idx_time_contiguous_layout():
-    """Packed offsets and seq_idx ids on a [B,D,T]-contiguous input (the
-    one-channel lanes): forward and backward against the oracle."""
+@pytest.mark.parametrize("padded", [False, True], ids=["unaligned-rows", "aligned-rows"])
+def test_packed_and_seq_idx_time_contiguous_layout(padded):
+    """Packed offsets and seq_idx ids on a [B,D,T]-contiguous input: rows
+    that do not start on 16-byte boundaries take the one-channel lanes, rows
+    that do (padded storage) the time lanes.  Forward and backward against
+    the oracle."""
     lengths = [5, 1, 40, 3, 77]
     cu = synth.cu_from_lengths(lengths)
     T = int(cu[-1])
     inp, g = inputs(2000, 1, 48, T, "tc", True, True, BF16, True, cu)
+    if padded:
+        g["x"], g["dy"] = padded_tc(inp["x"]), padded_tc(inp["dy"])
     ops.reset_flag(DEV)
     y, fin = run_fwd(g, "tc", "silu", True, cu)
     check_fwd(inp, y, fin, "silu")
@@ -839,11 +844,13 @@ def test_packed_and_seq_idx_time_contiguous_layout():
     check_bwd(inp, dx, dw, db, dinit, "silu")
     ops.check_flag(DEV)
 
-    inp, g = inputs(2001, 2, 40, 96, "tc", True, False, BF16)
-    seq = synth.seq_idx_tensor(torch.Generator().manual_seed(2002), 2, 96, "random")
-    y = guarded_act(2, 40, 96, "tc", DEV)
+    inp, g = inputs(2001, 2, 40, 93, "tc", True, False, BF16)
+    if padded:
+        g["x"], g["dy"] = padded_tc(inp["x"]), padded_tc(inp["dy"])
+    seq = synth.seq_idx_tensor(torch.Generator().manual_seed(2002), 2, 93, "random")
+    y = guarded_act(2, 40, 93, "tc", DEV)
     ops.fwd(g["x"], g["weight"], g["bias"], None, None, "silu", y=y.view, seq_idx=dev(seq))
-    dx = guarded_act(2, 40, 96, "tc", DEV)
+    dx = guarded_act(2, 40, 93, "tc", DEV)
     _, dw, db, _ = ops.bwd(g["x"], g["weight"], g["dy"], g["bias"], None, None, None, "silu",
                            False, False, dx=dx.view, seq_idx=dev(seq))
     torch.cuda.synchronize()
@@ -855,3 +862,35 @@ def test_packed_and_seq_idx_time_contiguous_layout():
     check_f32_rel("dweight", dw, odw)
     check_f32_rel("dbias", db, odb)
     assert y.intact() and dx.intact()
+
+
+TC_PACKED_CASES = [
+    # lengths, D, W, bias, init, dfinal, deterministic
+    ([1, 2, 3, 1, 1, 2, 3, 3, 2, 1] * 30 + [700, 1, 2], 24, 4, True, True, True, False),
+    ([2049, 1, 2, 1100, 7], 16, 4, False, True, True, True),
+    ([5, 1, 40, 3, 77, 513, 1, 1], 40, 3, True, True, False, False),
+    ([1000, 30, 1], 8, 2, False, False, True, True),
+    ([3] * 1500, 8, 4, True, True, True, False),
+    ([1, 2] * 2100, 8, 4, True, True, True, True),          # 4201 offsets: global path
+]
+
+
+@pytest.mark.parametrize("case", TC_PACKED_CASES, ids=lambda c: "N%d-D%d-W%d%s" % (
+    len(c[0]), c[1], c[2], "-det" if c[6] else ""))
+def test_packed_time_lanes(case):
+    """Packed rows on time lanes (rows aligned to 16 bytes): sequence starts
+    and ends inside a lane, several per lane, at tile and chunk edges, with
+    initial states, dfinal, dinit and both dW routes."""
+    lengths, D, W, bias, init, dfinal, det = case
+    print("packed time-lane case", len(lengths), D, W, bias, init, dfinal, det, flush=True)
+    cu = synth.cu_from_lengths(lengths)
+    T = int(cu[-1])
+    inp, g = inputs(2100 + len(lengths) + D, 1, D, T, "tc", bias, init, BF16, dfinal, cu, W=W)
+    g["x"], g["dy"] = padded_tc(inp["x"]), padded_tc(inp["dy"])
+    opts = OPT_DETDB if (bias and det) else 0
+    ops.reset_flag(DEV)
+    y, fin = run_fwd(g, "tc", "silu", True, cu, options=opts)
+    check_fwd(inp, y, fin, "silu")
+    dx, dw, db, dinit = run_bwd(g, "tc", "silu", det, cu, options=opts)
+    check_bwd(inp, dx, dw, db, dinit, "silu")
+    ops.check_flag(DEV)

@@ -53,7 +53,7 @@ def draw_case(i):
     c["init"] = states and r.random() < 0.6
     c["final"] = states and r.random() < 0.7
     c["dfinal"] = states and r.random() < 0.5
-    c["padded"] = c["layout"] == "tc" and mode == "dense" and r.random() < 0.3
+    c["padded"] = c["layout"] == "tc" and r.random() < 0.5
     return c
 
 
