@@ -24,7 +24,8 @@ input already resident in HBM:
   tiny              B=1 D=64 T=128 [B,D,T]: forward (launch-bound).
   seqidx            the dense shape with sequences of U[64,1024] tokens per row
                     marked by seq_idx (no states): forward + backward.
-  dense_tc, large_tc  the dense / large data in [B,D,T] time-contiguous storage.
+  dense_tc, large_tc, packed_tc, seqidx_tc
+                    the same data in [B,D,T] time-contiguous storage.
 
 The value is algorithmic bytes (every compulsory input read once, every output
 written once) per step divided by the wall time per step.  Per-op times come
@@ -52,11 +53,17 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "depthwise_causal_conv1d_02_amd", "csrc")
 OP_KERNEL = {"fwd": "k_fwd_chan", "bwd": "k_bwd_chan", "update": "k_update"}
 OP_KERNEL_TIME = {"fwd": "k_fwd_tc", "bwd": "k_bwd_tc", "update": "k_update"}
+OP_KERNEL_TIME_PACKED = {"fwd": "k_fwd_tcp", "bwd": "k_bwd_tcp", "update": "k_update"}
+OP_KERNEL_TIME_SEQ = {"fwd": "k_fwd_tcs", "bwd": "k_bwd_tcs", "update": "k_update"}
 
 
 def op_kernels(workload):
-    """op -> kernel name prefix of a workload (time-lane kernels for *_tc)."""
-    return OP_KERNEL_TIME if workload.endswith("_tc") else OP_KERNEL
+    """op -> kernel name prefix of a workload (time-lane kernels for *_tc;
+    the packed and seq_idx rows' own time-lane kernels for those rows)."""
+    if not workload.endswith("_tc"):
+        return OP_KERNEL
+    return {"packed_tc": OP_KERNEL_TIME_PACKED,
+            "seqidx_tc": OP_KERNEL_TIME_SEQ}.get(workload, OP_KERNEL_TIME)
 
 
 def profile_workload(workload, op):
@@ -564,14 +571,15 @@ def summarize(args):
              "bwd": bwd_bytes(4, 4096, 2048, 4, True, False, 2, True)}
     large = {"fwd": fwd_bytes(8, 8192, 8192, 8, False, False, 2, False),
              "bwd": bwd_bytes(8, 8192, 8192, 8, False, False, 2, False)}
-    wl_bytes = {"dense": dense, "dense_tc": dense, "large_tc": large,
+    wl_bytes = {"dense": dense,
                 "seqidx": {"fwd": fwd_bytes(4, 4096, 2048, 4, False, False, 2, True) + 4 * 2048 * 4,
                            "bwd": bwd_bytes(4, 4096, 2048, 4, False, False, 2, True) + 4 * 2048 * 4},
                 "packed": {"fwd": fwd_bytes(1, 5120, 33280, 16, True, True, 4, False),
                            "bwd": bwd_bytes(1, 5120, 33280, 16, True, False, 4, False)},
                 "large": {"fwd": fwd_bytes(8, 8192, 8192, 8, False, False, 2, False),
                           "bwd": bwd_bytes(8, 8192, 8192, 8, False, False, 2, False)},
-                "decode": {"update": update_bytes(256, 8192, 2, True)}}[args.workload]
+                "decode": {"update": update_bytes(256, 8192, 2, True)}}[
+                    args.workload[:-3] if args.workload.endswith("_tc") else args.workload]
     trace_dir, fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.summarize
     stats = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
     rows = _kernel_rows(stats)
@@ -651,7 +659,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="large_decode",
                     choices=["large_decode", "dense", "packed", "decode", "large", "tiny",
-                             "seqidx", "dense_tc", "large_tc"])
+                             "seqidx", "dense_tc", "large_tc", "packed_tc", "seqidx_tc"])
     ap.add_argument("--no-other-configs", action="store_true",
                     help="with large_decode: skip timing the dense and packed workloads' ops")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -530,9 +530,12 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     a.n_tblk_t = gs.n_tblk_t;
     a.n_block_m = gs.n_block_m;
     if (time_lanes) set_tc_div(a);
-    a.cu_in_lds = p.packed && p.N + 1 <= ccv::kLdsCuMax;
-    a.nt_load = p.B * p.D * p.T * 2 >=
-                (p.seq ? CCV_NT_LOAD_MIN_BYTES_SEQ : CCV_NT_LOAD_MIN_BYTES);
+    // packed rows on time lanes always take the validation launch first
+    a.cu_in_lds = p.packed && !time_lanes && p.N + 1 <= ccv::kLdsCuMax;
+    // packed rows on time lanes keep their inputs cached: the repair at the
+    // sequence boundaries reads some of them again
+    a.nt_load = !(p.packed && time_lanes) &&
+                p.B * p.D * p.T * 2 >= (p.seq ? CCV_NT_LOAD_MIN_BYTES_SEQ : CCV_NT_LOAD_MIN_BYTES);
     if (p.packed && !a.cu_in_lds) {
         rc = hip_status(ccv::launch_validate(a.cu, p.N, p.T, err_flag, 0, stream));
         if (rc != CCV_OK) return rc;
@@ -658,8 +661,9 @@ int bwd_call(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bi
     a.n_seq = p.N;
     a.err = p.packed ? err_flag : nullptr;
     set_seq(a, seq_idx, p);
-    a.nt_load = 2 * p.B * p.D * p.T * 2 >=
-                (p.seq ? CCV_NT_LOAD_MIN_BYTES_SEQ_BWD : CCV_NT_LOAD_MIN_BYTES);
+    a.nt_load = !(p.packed && time_lanes) &&
+                2 * p.B * p.D * p.T * 2 >=
+                    (p.seq ? CCV_NT_LOAD_MIN_BYTES_SEQ_BWD : CCV_NT_LOAD_MIN_BYTES);
     const int silu = activation == CCV_ACT_SILU;
     const int rounds = p.packed ? CCV_BWD_PACKED_ROUNDS : CCV_BWD_ROUNDS;
     if (!use_partials && rounds > 0 && !time_lanes) {
@@ -681,7 +685,8 @@ int bwd_call(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bi
     a.n_tblk_t = g.n_tblk_t;
     a.n_block_m = g.n_block_m;
     if (time_lanes) set_tc_div(a);
-    a.cu_in_lds = p.packed && p.N + 1 <= ccv::kLdsCuMax;
+    // packed rows on time lanes always take the validation launch first
+    a.cu_in_lds = p.packed && !time_lanes && p.N + 1 <= ccv::kLdsCuMax;
 
     if (p.packed && !a.cu_in_lds) {
         rc = hip_status(ccv::launch_validate(a.cu, p.N, p.T, err_flag, 0, stream));

@@ -1313,8 +1313,20 @@ __device__ __forceinline__ bool tc_item(const A &a, TcItem &it) {
     return true;
 }
 
-template <int W, bool SILU, int FK, bool NTL>
-__device__ __forceinline__ void fwd_tc_chunk(const FwdArgs &a, const TcItem &it) {
+// No repair: the dense rows' chunks.  A repair is told where its chunk is
+// once the chunk's loads are issued (`locate`), and runs after the tiles
+// (the forward) or before the dW/dB wave sums (the backward).
+struct TcNoFix {
+    __device__ __forceinline__ void locate() {}
+    template <int W>
+    __device__ __forceinline__ void operator()(const float (&)[W][1], const float (&)[1]) {}
+    template <int W>
+    __device__ __forceinline__ void operator()(const float (&)[W][1], const float (&)[1],
+                                               float (&)[W], float &) {}
+};
+
+template <int W, bool SILU, int FK, bool NTL, typename Fix>
+__device__ __forceinline__ void fwd_tc_chunk(const FwdArgs &a, const TcItem &it, Fix &fix) {
     const int lane = threadIdx.x % kWaveSize;
     const uint16_t *xr = static_cast<const uint16_t *>(a.x.ptr) + it.b * a.x.s0 + it.d * a.x.s1;
     uint16_t *yr = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.y.ptr)) +
@@ -1337,6 +1349,7 @@ __device__ __forceinline__ void fwd_tc_chunk(const FwdArgs &a, const TcItem &it)
         if (t < it.t1) raw[c] = tc_load<NTL>(xr, t, it.t1);
         else raw[c].v = u32x4_t{0u, 0u, 0u, 0u};
     }
+    fix.locate();
     float carry[W - 1];  // x_ext of the W-1 tokens before the current tile
 #pragma unroll
     for (int j = 0; j < W - 1; ++j) carry[j] = kept_f32(lh[j], lh_keep[j]);
@@ -1366,14 +1379,16 @@ __device__ __forceinline__ void fwd_tc_chunk(const FwdArgs &a, const TcItem &it)
     if (it.t1 == a.T && a.fin.ptr && lane < W - 1)
         const_cast<uint16_t *>(static_cast<const uint16_t *>(a.fin.ptr))
             [it.b * a.fin.s0 + it.d * a.fin.s1 + lane * a.fin.s2] = fin_keep ? fin_bits : 0;
+    fix(w, bias);
 }
 
 template <int W, bool SILU, int FK>
 __global__ __launch_bounds__(256) void k_fwd_tc(FwdArgs a) {
     TcItem it;
     if (!tc_item(a, it)) return;
-    if (a.nt_load) fwd_tc_chunk<W, SILU, FK, true>(a, it);
-    else fwd_tc_chunk<W, SILU, FK, false>(a, it);
+    TcNoFix fix;
+    if (a.nt_load) fwd_tc_chunk<W, SILU, FK, true>(a, it, fix);
+    else fwd_tc_chunk<W, SILU, FK, false>(a, it, fix);
 }
 
 // Backward on time lanes.  Per tile: z and g = dy * act'(z) for the lane's
@@ -1383,8 +1398,8 @@ __global__ __launch_bounds__(256) void k_fwd_tc(FwdArgs a) {
 // chunk's last tile the W-1 g's past the chunk are computed directly (the
 // right halo).  dW/dB: one wave sum per chunk, then an atomic or a unique
 // partial.
-template <int W, bool SILU, int FK, bool NTL>
-__device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it) {
+template <int W, bool SILU, int FK, bool NTL, typename Fix>
+__device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it, Fix &fix) {
     constexpr bool BIAS = fk_bias(FK);
     const int lane = threadIdx.x % kWaveSize;
     const uint16_t *xr = static_cast<const uint16_t *>(a.x.ptr) + it.b * a.x.s0 + it.d * a.x.s1;
@@ -1424,6 +1439,7 @@ __device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it)
     }
     float w[W][1], bias[1];
     load_filter<W, 1, FK>(a.w, a.w_sd, a.w_sk, a.bias, a.b_s, it.d, w, bias);
+    fix.locate();
     float carry[W - 1];
 #pragma unroll
     for (int j = 0; j < W - 1; ++j) carry[j] = kept_f32(lh[j], lh_keep[j]);
@@ -1538,6 +1554,7 @@ __device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it)
         }
         emit(tprev, gprev, after);
     }
+    fix(w, bias, dwacc, dbacc);
     // dW/dB of the chunk: a wave sum, then one atomic or one partial per tap.
 #pragma unroll
     for (int k = 0; k < W; ++k) dwacc[k] = wave_sum(dwacc[k]);
@@ -1562,22 +1579,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CCV_TC_BWD_
 void k_bwd_tc(BwdArgs a) {
     TcItem it;
     if (!tc_item(a, it)) return;
-    if (a.nt_load) bwd_tc_chunk<W, SILU, FK, true>(a, it);
-    else bwd_tc_chunk<W, SILU, FK, false>(a, it);
+    TcNoFix fix;
+    if (a.nt_load) bwd_tc_chunk<W, SILU, FK, true>(a, it, fix);
+    else bwd_tc_chunk<W, SILU, FK, false>(a, it, fix);
 }
 
 // ===========================================================================
-// Time lanes for packed and seq_idx rows (unit stride along T)
+// Time lanes for seq_idx rows (unit stride along T)
 //
-// The lanes, tiles and chunks of the dense time-lane kernels, with one id
-// per token: the index of its sequence (packed rows, B = 1, from the offsets
-// staged in LDS) or its seq_idx entry.  A tap contributes the input only
-// when its token has the output token's id; otherwise it contributes zero,
-// or, on packed rows with initial states, the state slot of the output
-// token's sequence (the tap reaches before that sequence's start).  Ids move
-// across lanes with the same DPP shifts as the values.  Positions outside
-// the row carry kNoId: no sequence index is negative, and a seq_idx id equal
-// to it meets only zero inputs (before the row) or zero gradients (past it).
+// The lanes, tiles and chunks of the dense time-lane kernels, with the
+// seq_idx entry of every token beside its value.  A tap contributes the input
+// only when its token has the output token's id, otherwise zero.  Ids move
+// across lanes with the same DPP shifts as the values.  Positions outside the
+// row carry kNoId; an entry equal to it meets only zero inputs (before the
+// row) or zero gradients (past it).
 // ===========================================================================
 constexpr int32_t kNoId = -1;
 
@@ -1591,147 +1606,81 @@ __device__ __forceinline__ int32_t from_lane_id(int32_t v, int l) {
     return __builtin_amdgcn_readlane(v, l);
 }
 
-// Token ids of one row.
-template <int ROWS>
-struct TcRowIds {
-    const int32_t *cu;  // packed: the offsets (validated), N + 1 entries
-    int64_t n;          // packed: N
-    const int32_t *sq;  // seq_idx: this row's ids
-    int64_t st;         // seq_idx: their stride
-    bool vec;           // seq_idx: unit stride, 16-byte aligned rows
+// The seq_idx entries of one row.
+struct TcSeqIds {
+    const int32_t *sq;  // this row's entries
+    int64_t st;         // their stride
+    bool vec;           // unit stride and 16-byte aligned rows
     int64_t T;
     __device__ __forceinline__ int32_t at(int64_t p) const {
-        if (p < 0 || p >= T) return kNoId;
-        if constexpr (ROWS == kRowsPacked) return static_cast<int32_t>(find_row(cu, n, p));
-        else return sq[p * st];
+        return p < 0 || p >= T ? kNoId : sq[p * st];
     }
-    // Packed rows: a lane's walk over the offsets, i = the sequence of the
-    // last token it has reached and nb = cu[i+1], the next offset.  A chunk
-    // starts every lane from one search (at the chunk's first halo token);
-    // the lanes then walk forward through their tiles and read the offsets
-    // only when they cross one.
-    struct Walk {
-        int64_t i, nb;
-    };
-    __device__ __forceinline__ Walk begin(int64_t p0) const {
-        Walk wk{0, 0};
-        if constexpr (ROWS == kRowsPacked) {
-            wk.i = find_row(cu, n, p0 > 0 ? p0 : 0);
-            wk.nb = cu[wk.i + 1];
-        }
-        return wk;
-    }
-    // The id of position p (kNoId outside the row), advancing a walk (p
-    // never decreases along it); seq_idx rows read it.
-    __device__ __forceinline__ int32_t walk_to(Walk &wk, int64_t p) const {
-        if constexpr (ROWS == kRowsPacked) {
-            if (p < 0 || p >= T) return kNoId;
-            while (p >= wk.nb) {
-                ++wk.i;
-                wk.nb = cu[wk.i + 1];
-            }
-            return static_cast<int32_t>(wk.i);
-        } else {
-            return at(p);
-        }
-    }
-    // The ids of the kTcE tokens from t (kNoId past the row); t never
-    // decreases along a walk.
-    __device__ __forceinline__ void lane_ids(int64_t t, int32_t (&id)[kTcE], Walk &wk) const {
-        if constexpr (ROWS == kRowsPacked) {
+    // The ids of the kTcE tokens from t (kNoId past the row).
+    __device__ __forceinline__ void lane_ids(int64_t t, int32_t (&id)[kTcE]) const {
+        if (vec && t + kTcE <= T) {
+            // t is a multiple of kTcE: two 16-byte loads
+            const u32x4_t *q = reinterpret_cast<const u32x4_t *>(sq + t);
+            const u32x4_t lo = q[0], hi = q[1];
 #pragma unroll
-            for (int e = 0; e < kTcE; ++e) {
-                const int64_t p = t + e;
-                if (p < T) {
-                    // cu[n] = T > p ends the walk within the offsets
-                    while (p >= wk.nb) {
-                        ++wk.i;
-                        wk.nb = cu[wk.i + 1];
-                    }
-                    id[e] = static_cast<int32_t>(wk.i);
-                } else {
-                    id[e] = kNoId;
-                }
+            for (int e = 0; e < 4; ++e) {
+                id[e] = static_cast<int32_t>(lo[e]);
+                id[4 + e] = static_cast<int32_t>(hi[e]);
             }
         } else {
-            if (vec && t + kTcE <= T) {
-                // t is a multiple of kTcE: two 16-byte loads
-                const u32x4_t *q = reinterpret_cast<const u32x4_t *>(sq + t);
-                const u32x4_t lo = q[0], hi = q[1];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    id[e] = static_cast<int32_t>(lo[e]);
-                    id[4 + e] = static_cast<int32_t>(hi[e]);
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < kTcE; ++e) id[e] = t + e < T ? sq[(t + e) * st] : kNoId;
-            }
+            for (int e = 0; e < kTcE; ++e) id[e] = t + e < T ? sq[(t + e) * st] : kNoId;
         }
     }
 };
 
+template <typename A>
+__device__ __forceinline__ TcSeqIds tc_seq_ids(const A &a, const TcItem &it) {
+    TcSeqIds ids;
+    ids.sq = a.seq + it.b * a.seq_sb;
+    ids.st = a.seq_st;
+    ids.vec = a.seq_vec != 0;
+    ids.T = a.T;
+    return ids;
+}
+
 // Tap values of output token i of a window (xe/ie: values and ids of the
-// W-1 tokens before the lane's first token, then its kTcE tokens): the input
-// where the ids match, else zero, or on packed rows with initial states the
-// slot r + k of the token's sequence, r being the token's offset in it.
-template <int W, int ROWS>
+// W-1 tokens before the lane's first token, then its kTcE tokens).
+template <int W>
 __device__ __forceinline__ void tc_taps(const float (&xe)[W - 1 + kTcE],
-                                        const int32_t (&ie)[W - 1 + kTcE], int i, int64_t p,
-                                        const int32_t *cu, const uint16_t *ir,
-                                        const Strided3 &init, float (&xv)[W]) {
+                                        const int32_t (&ie)[W - 1 + kTcE], int i,
+                                        float (&xv)[W]) {
     const int32_t own = ie[i + W - 1];
 #pragma unroll
     for (int k = 0; k < W; ++k) xv[k] = ie[i + k] == own ? xe[i + k] : 0.0f;
-    if constexpr (ROWS == kRowsPacked) {
-        // Only the first W-1 tokens of a sequence reach before its start,
-        // and there the oldest tap's id differs.  Tokens past the row
-        // (kNoId) are never written and need no state.
-        if (ir && own != kNoId && ie[i] != own) {
-            const int64_t r = p - cu[own];
-#pragma unroll
-            for (int k = 0; k < W - 1; ++k)
-                if (ie[i + k] != own)
-                    xv[k] = bf16_bits_to_f32(ir[own * init.s0 + (r + k) * init.s2]);
-        }
-    }
 }
 
-template <int W, bool SILU, int FK, bool NTL, int ROWS>
-__device__ __forceinline__ void fwd_tcr_chunk(const FwdArgs &a, const TcItem &it,
-                                              const TcRowIds<ROWS> &ids) {
-    constexpr bool PACKED = ROWS == kRowsPacked;
+template <int W, bool SILU, int FK, bool NTL>
+__device__ __forceinline__ void fwd_tcs_chunk(const FwdArgs &a, const TcItem &it,
+                                              const TcSeqIds &ids) {
     const int lane = threadIdx.x % kWaveSize;
     const uint16_t *xr = static_cast<const uint16_t *>(a.x.ptr) + it.b * a.x.s0 + it.d * a.x.s1;
     uint16_t *yr = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.y.ptr)) +
                    it.b * a.y.s0 + it.d * a.y.s1;
-    // The channel's initial-state column (packed rows: indexed by sequence).
-    const uint16_t *ir =
-        PACKED && a.init.ptr ? static_cast<const uint16_t *>(a.init.ptr) + it.d * a.init.s1
-                             : nullptr;
     // Left halo (values and ids of the W-1 tokens before the chunk; before
     // the row, zero and kNoId), the filter, then the tiles and their ids.
     uint16_t lh[W - 1];
     int32_t cid[W - 1];
-    auto wk = ids.begin(it.t0 - (W - 1));
 #pragma unroll
     for (int j = 0; j < W - 1; ++j) {
         const int64_t p = it.t0 - (W - 1) + j;
         lh[j] = xr[p >= 0 ? p : 0];
-        cid[j] = ids.walk_to(wk, p);
+        cid[j] = ids.at(p);
     }
     float w[W][1], bias[1];
     load_filter<W, 1, FK>(a.w, a.w_sd, a.w_sk, a.bias, a.b_s, it.d, w, bias);
     Raw<8> raw[kTcTilesFwd];
-    // seq_idx ids are loads and go out with the tiles; packed ids come from
-    // the LDS offsets and are worked out tile by tile (fewer live registers)
-    int32_t tid[PACKED ? 1 : kTcTilesFwd][kTcE];
+    int32_t tid[kTcTilesFwd][kTcE];
 #pragma unroll
     for (int c = 0; c < kTcTilesFwd; ++c) {
         const int64_t t = it.t0 + c * kTcTile + lane * kTcE;
         if (t < it.t1) raw[c] = tc_load<NTL>(xr, t, it.t1);
         else raw[c].v = u32x4_t{0u, 0u, 0u, 0u};
-        if constexpr (!PACKED) ids.lane_ids(t < it.t1 ? t : a.T, tid[c], wk);
+        ids.lane_ids(t < it.t1 ? t : a.T, tid[c]);
     }
     float carry[W - 1];
 #pragma unroll
@@ -1744,93 +1693,62 @@ __device__ __forceinline__ void fwd_tcr_chunk(const FwdArgs &a, const TcItem &it
         if (tt >= it.t1) break;
         const int64_t t = tt + lane * kTcE;
         float v[kTcE], xe[W - 1 + kTcE], out[kTcE];
-        int32_t ie[W - 1 + kTcE], cur[kTcE];
-        if constexpr (PACKED) {
-            ids.lane_ids(t < it.t1 ? t : a.T, cur, wk);
-        } else {
-#pragma unroll
-            for (int i = 0; i < kTcE; ++i) cur[i] = tid[c][i];
-        }
+        int32_t ie[W - 1 + kTcE];
         unpack<8>(raw[c], v);
 #pragma unroll
         for (int j = 0; j < W - 1; ++j) {
             xe[j] = lane_up(v[kTcE - (W - 1) + j], carry[j]);
-            ie[j] = lane_up_id(cur[kTcE - (W - 1) + j], cid[j]);
+            ie[j] = lane_up_id(tid[c][kTcE - (W - 1) + j], cid[j]);
         }
 #pragma unroll
         for (int i = 0; i < kTcE; ++i) {
             xe[W - 1 + i] = v[i];
-            ie[W - 1 + i] = cur[i];
+            ie[W - 1 + i] = tid[c][i];
         }
 #pragma unroll
         for (int i = 0; i < kTcE; ++i) {
             float xv[W];
-            tc_taps<W, ROWS>(xe, ie, i, t + i, ids.cu, ir, a.init, xv);
+            tc_taps<W>(xe, ie, i, xv);
             float z = bias[0];
 #pragma unroll
             for (int k = 0; k < W; ++k) z = fmaf(w[k][0], xv[k], z);
             out[i] = act<SILU>(z);
         }
         if (t < it.t1) tc_store<true>(yr, t, it.t1, out);
-        if constexpr (PACKED) {
-            // Each sequence that ends among the lane's tokens writes its
-            // final state: the last W-1 extended tokens, bit for bit.
-            if (a.fin.ptr && t < it.t1) {
-                const int64_t te = min(t + kTcE, it.t1);
-                for (int64_t i = cur[0]; i < ids.n; ++i) {
-                    const int64_t e = ids.cu[i + 1], s = ids.cu[i];
-                    if (e > te) break;
-#pragma unroll
-                    for (int j = 0; j < W - 1; ++j) {
-                        const int64_t q = e - (W - 1) + j;
-                        uint16_t bits = 0;
-                        if (q >= s) bits = xr[q];
-                        else if (ir) bits = ir[i * a.init.s0 + (q - s + W - 1) * a.init.s2];
-                        const_cast<uint16_t *>(static_cast<const uint16_t *>(a.fin.ptr))
-                            [i * a.fin.s0 + it.d * a.fin.s1 + j * a.fin.s2] = bits;
-                    }
-                }
-            }
-        }
 #pragma unroll
         for (int j = 0; j < W - 1; ++j) {
             carry[j] = from_lane(v[kTcE - (W - 1) + j], kWaveSize - 1);
-            cid[j] = from_lane_id(cur[kTcE - (W - 1) + j], kWaveSize - 1);
+            cid[j] = from_lane_id(tid[c][kTcE - (W - 1) + j], kWaveSize - 1);
         }
     }
 }
 
-template <int W, bool SILU, int FK, bool NTL, int ROWS>
-__device__ __forceinline__ void bwd_tcr_chunk(const BwdArgs &a, const TcItem &it,
-                                              const TcRowIds<ROWS> &ids) {
-    constexpr bool PACKED = ROWS == kRowsPacked;
+template <int W, bool SILU, int FK, bool NTL>
+__device__ __forceinline__ void bwd_tcs_chunk(const BwdArgs &a, const TcItem &it,
+                                              const TcSeqIds &ids) {
     constexpr bool BIAS = fk_bias(FK);
     const int lane = threadIdx.x % kWaveSize;
     const uint16_t *xr = static_cast<const uint16_t *>(a.x.ptr) + it.b * a.x.s0 + it.d * a.x.s1;
     const uint16_t *dyr = static_cast<const uint16_t *>(a.dy.ptr) + it.b * a.dy.s0 + it.d * a.dy.s1;
     uint16_t *dxr = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.dx.ptr)) +
                     it.b * a.dx.s0 + it.d * a.dx.s1;
-    const uint16_t *ir =
-        PACKED && a.init.ptr ? static_cast<const uint16_t *>(a.init.ptr) + it.d * a.init.s1
-                             : nullptr;
     // Single tokens first: the left halo (values, ids); the right halo (lane
     // j < W-1 reads token t1 + j of x and dy, the other lanes and tokens
     // past the row an in-row token that is dropped) and its ids.
     uint16_t lh[W - 1];
     int32_t cid[W - 1];
-    auto wk = ids.begin(it.t0 - (W - 1));
 #pragma unroll
     for (int j = 0; j < W - 1; ++j) {
         const int64_t p = it.t0 - (W - 1) + j;
         lh[j] = xr[p >= 0 ? p : 0];
-        cid[j] = ids.walk_to(wk, p);
+        cid[j] = ids.at(p);
     }
     const int64_t rq = min(it.t1 + lane, a.T - 1);
     const uint16_t rh_x = xr[rq], rh_dy = dyr[rq];
     float w[W][1], bias[1];
     load_filter<W, 1, FK>(a.w, a.w_sd, a.w_sk, a.bias, a.b_s, it.d, w, bias);
     Raw<8> rx[kTcTilesBwd], rd[kTcTilesBwd];
-    int32_t tid[PACKED ? 1 : kTcTilesBwd][kTcE];  // as in the forward
+    int32_t tid[kTcTilesBwd][kTcE];
 #pragma unroll
     for (int c = 0; c < kTcTilesBwd; ++c) {
         const int64_t t = it.t0 + c * kTcTile + lane * kTcE;
@@ -1841,12 +1759,9 @@ __device__ __forceinline__ void bwd_tcr_chunk(const BwdArgs &a, const TcItem &it
             rx[c].v = u32x4_t{0u, 0u, 0u, 0u};
             rd[c].v = u32x4_t{0u, 0u, 0u, 0u};
         }
-        if constexpr (!PACKED) ids.lane_ids(t < it.t1 ? t : a.T, tid[c], wk);
+        ids.lane_ids(t < it.t1 ? t : a.T, tid[c]);
     }
-    // lane j < W-1: the id of token t1 + j; packed rows walk to it after
-    // the tiles (past every token of them)
-    int32_t rh_id = 0;
-    if constexpr (!PACKED) rh_id = ids.walk_to(wk, it.t1 + lane);
+    const int32_t rh_id = ids.at(it.t1 + lane);  // lane j < W-1: the id of token t1 + j
     float carry[W - 1];
 #pragma unroll
     for (int j = 0; j < W - 1; ++j)
@@ -1854,19 +1769,12 @@ __device__ __forceinline__ void bwd_tcr_chunk(const BwdArgs &a, const TcItem &it
     float dwacc[W], dbacc = 0.0f;
 #pragma unroll
     for (int k = 0; k < W; ++k) dwacc[k] = 0.0f;
-    const uint16_t *dfr = PACKED && a.dfin.ptr
-                              ? static_cast<const uint16_t *>(a.dfin.ptr) + it.d * a.dfin.s1
-                              : nullptr;
 
     // dx of the lane's tokens of the tile at tt from its g's and ids, and
     // the W-1 g's and ids that follow the lane (`after`: the next tile's, or
-    // the right halo's, for lane 63).  `before` is the id of the token before
-    // the tile (lane 0's left neighbour).  Packed rows add the final-state
-    // gradient to a sequence's last W-1 tokens and write dinit where a
-    // sequence starts.
+    // the right halo's, for lane 63).
     auto emit = [&](int64_t tt, const float (&g)[kTcE], const int32_t (&id)[kTcE],
-                    const float (&after)[W - 1], const int32_t (&after_id)[W - 1],
-                    int32_t before) {
+                    const float (&after)[W - 1], const int32_t (&after_id)[W - 1]) {
         float ge[kTcE + W - 1], v[kTcE];
         int32_t ige[kTcE + W - 1];
 #pragma unroll
@@ -1889,83 +1797,34 @@ __device__ __forceinline__ void bwd_tcr_chunk(const BwdArgs &a, const TcItem &it
                 acc = fmaf(w[W - 1 - j][0], ige[i + j] == own ? ge[i + j] : 0.0f, acc);
             v[i] = acc;
         }
-        if constexpr (PACKED) {
-            // A token q among the last W-1 of its sequence: position q+W-1
-            // is past the sequence's end.
-            if (dfr) {
-#pragma unroll
-                for (int i = 0; i < kTcE; ++i) {
-                    if (t + i < it.t1 && ige[i + W - 1] != ige[i]) {
-                        const int64_t jj = t + i - (ids.cu[ige[i] + 1] - (W - 1));
-                        v[i] += bf16_bits_to_f32(dfr[ige[i] * a.dfin.s0 + jj * a.dfin.s2]);
-                    }
-                }
-            }
-            if (a.dinit.ptr) {
-                const int32_t prev = lane_up_id(id[kTcE - 1], before);
-#pragma unroll
-                for (int i = 0; i < kTcE; ++i) {
-                    const int32_t own = ige[i];
-                    const int32_t left = i == 0 ? prev : ige[i - 1];
-                    if (t + i < it.t1 && left != own) {
-                        // dinit[own][j] = dx_ext at s-(W-1)+j (s = t+i): the
-                        // g's at s+j-k for k <= j that lie in the sequence,
-                        // plus the final-state gradient landing there.
-                        const int64_t s = t + i, e = ids.cu[own + 1];
-#pragma unroll
-                        for (int j = 0; j < W - 1; ++j) {
-                            float acc = w[0][0] * (ige[i + j] == own ? ge[i + j] : 0.0f);
-#pragma unroll
-                            for (int k = 1; k < W; ++k)
-                                acc = fmaf(w[k][0],
-                                           k <= j && ige[i + j - k] == own ? ge[i + j - k] : 0.0f,
-                                           acc);
-                            const int64_t jj = s - (W - 1) + j - (e - (W - 1));
-                            if (dfr && jj >= 0 && jj < W - 1)
-                                acc += bf16_bits_to_f32(dfr[own * a.dfin.s0 + jj * a.dfin.s2]);
-                            const_cast<uint16_t *>(static_cast<const uint16_t *>(a.dinit.ptr))
-                                [own * a.dinit.s0 + it.d * a.dinit.s1 + j * a.dinit.s2] =
-                                    to_bf16_bits(acc);
-                        }
-                    }
-                }
-            }
-        }
         if (t < it.t1) tc_store<true>(dxr, t, it.t1, v);
     };
 
     float gprev[kTcE];
-    int32_t idprev[kTcE], before_prev = kNoId;
+    int32_t idprev[kTcE];
     int64_t tprev = -1;
 #pragma unroll
     for (int c = 0; c < kTcTilesBwd; ++c) {
         const int64_t tt = it.t0 + c * kTcTile;
         if (tt >= it.t1) break;
-        const int64_t t = tt + lane * kTcE;
         float v[kTcE], dyv[kTcE], xe[W - 1 + kTcE], g[kTcE];
-        int32_t ie[W - 1 + kTcE], cur[kTcE];
-        if constexpr (PACKED) {
-            ids.lane_ids(t < it.t1 ? t : a.T, cur, wk);
-        } else {
-#pragma unroll
-            for (int i = 0; i < kTcE; ++i) cur[i] = tid[c][i];
-        }
+        int32_t ie[W - 1 + kTcE];
         unpack<8>(rx[c], v);
         unpack<8>(rd[c], dyv);
 #pragma unroll
         for (int j = 0; j < W - 1; ++j) {
             xe[j] = lane_up(v[kTcE - (W - 1) + j], carry[j]);
-            ie[j] = lane_up_id(cur[kTcE - (W - 1) + j], cid[j]);
+            ie[j] = lane_up_id(tid[c][kTcE - (W - 1) + j], cid[j]);
         }
 #pragma unroll
         for (int i = 0; i < kTcE; ++i) {
             xe[W - 1 + i] = v[i];
-            ie[W - 1 + i] = cur[i];
+            ie[W - 1 + i] = tid[c][i];
         }
 #pragma unroll
         for (int i = 0; i < kTcE; ++i) {
             float xv[W];
-            tc_taps<W, ROWS>(xe, ie, i, t + i, ids.cu, ir, a.init, xv);
+            tc_taps<W>(xe, ie, i, xv);
             float z = bias[0];
 #pragma unroll
             for (int k = 0; k < W; ++k) z = fmaf(w[k][0], xv[k], z);
@@ -1980,24 +1839,22 @@ __device__ __forceinline__ void bwd_tcr_chunk(const BwdArgs &a, const TcItem &it
 #pragma unroll
             for (int j = 0; j < W - 1; ++j) {
                 after[j] = from_lane(g[j], 0);
-                after_id[j] = from_lane_id(cur[j], 0);
+                after_id[j] = from_lane_id(tid[c][j], 0);
             }
-            emit(tprev, gprev, idprev, after, after_id, before_prev);
+            emit(tprev, gprev, idprev, after, after_id);
         }
 #pragma unroll
         for (int i = 0; i < kTcE; ++i) {
             gprev[i] = g[i];
-            idprev[i] = cur[i];
+            idprev[i] = tid[c][i];
         }
         tprev = tt;
-        before_prev = cid[W - 2];
 #pragma unroll
         for (int j = 0; j < W - 1; ++j) {
             carry[j] = from_lane(v[kTcE - (W - 1) + j], kWaveSize - 1);
-            cid[j] = from_lane_id(cur[kTcE - (W - 1) + j], kWaveSize - 1);
+            cid[j] = from_lane_id(tid[c][kTcE - (W - 1) + j], kWaveSize - 1);
         }
     }
-    if constexpr (PACKED) rh_id = ids.walk_to(wk, it.t1 + lane);
     // Right halo: g at t1 .. t1+W-2 (zero past the row), in every lane.  A
     // chunk that does not end the row is a whole number of tiles, so
     // `carry`/`cid` hold the W-1 tokens before t1.
@@ -2015,21 +1872,13 @@ __device__ __forceinline__ void bwd_tcr_chunk(const BwdArgs &a, const TcItem &it
 #pragma unroll
         for (int j = 0; j < W - 1; ++j) {
             const int32_t own = iw[j + W - 1];
-            const int64_t p = it.t1 + j;
             float z = bias[0];
 #pragma unroll
-            for (int k = 0; k < W; ++k) {
-                float xv = iw[j + k] == own ? xw[j + k] : 0.0f;
-                if constexpr (PACKED) {
-                    if (ir && iw[j + k] != own && p < a.T)
-                        xv = bf16_bits_to_f32(ir[own * a.init.s0 + (p - ids.cu[own] + k) * a.init.s2]);
-                }
-                z = fmaf(w[k][0], xv, z);
-            }
-            after[j] = p < a.T ? from_lane(hd, j) * act_slope<SILU>(z) : 0.0f;
-            after_id[j] = iw[W - 1 + j];
+            for (int k = 0; k < W; ++k) z = fmaf(w[k][0], iw[j + k] == own ? xw[j + k] : 0.0f, z);
+            after[j] = it.t1 + j < a.T ? from_lane(hd, j) * act_slope<SILU>(z) : 0.0f;
+            after_id[j] = own;
         }
-        emit(tprev, gprev, idprev, after, after_id, before_prev);
+        emit(tprev, gprev, idprev, after, after_id);
     }
     // dW/dB of the chunk: a wave sum, then one atomic or one partial per tap.
 #pragma unroll
@@ -2050,109 +1899,455 @@ __device__ __forceinline__ void bwd_tcr_chunk(const BwdArgs &a, const TcItem &it
     }
 }
 
-// The row ids of a wave's row.  Packed rows read the offsets from `cu`:
-// the block's LDS copy or global memory; the caller passes the LDS array
-// itself (not a pointer chosen at run time), so that its reads compile to
-// LDS instructions rather than flat loads that would queue behind the bulk
-// global loads.
-template <int ROWS, typename A>
-__device__ __forceinline__ TcRowIds<ROWS> tc_row_ids(const A &a, const TcItem &it,
-                                                     const int32_t *cu) {
-    TcRowIds<ROWS> ids;
-    ids.T = a.T;
-    if constexpr (ROWS == kRowsPacked) {
-        ids.cu = cu;
-        ids.n = a.n_seq;
-        ids.sq = nullptr;
-        ids.st = 0;
-        ids.vec = false;
-    } else {
-        ids.cu = nullptr;
-        ids.n = 0;
-        ids.sq = a.seq + it.b * a.seq_sb;
-        ids.st = a.seq_st;
-        ids.vec = a.seq_vec != 0;
-    }
-    return ids;
-}
-
-// A packed chunk whose tokens and halos, [t0-(W-1), t1+(W-1)), lie inside
-// one sequence: no tap crosses a sequence start, no final state or state
-// gradient is written, and the dense rows' kernels compute it exactly
-// (wave-uniform).  seq_idx rows always take the id path.
-template <int W, int ROWS>
-__device__ __forceinline__ bool tc_interior(const TcRowIds<ROWS> &ids, const TcItem &it) {
-    if constexpr (ROWS == kRowsPacked) {
-        if (it.t0 < W - 1) return false;
-        const int64_t i = find_row(ids.cu, ids.n, it.t0 - (W - 1));
-        return it.t1 + (W - 1) <= ids.cu[i + 1];
-    } else {
-        return false;
-    }
-}
-
-// One chunk of a packed or seq_idx row: a packed chunk whose tokens and
-// halos lie inside one sequence takes the dense rows' code.
-template <int W, bool SILU, int FK, int ROWS>
-__device__ __forceinline__ void fwd_tcr_run(const FwdArgs &a, const TcItem &it,
-                                            const TcRowIds<ROWS> &ids) {
-    if (tc_interior<W, ROWS>(ids, it)) {
-        if (a.nt_load) fwd_tc_chunk<W, SILU, FK, true>(a, it);
-        else fwd_tc_chunk<W, SILU, FK, false>(a, it);
-        return;
-    }
-    if (a.nt_load) fwd_tcr_chunk<W, SILU, FK, true, ROWS>(a, it, ids);
-    else fwd_tcr_chunk<W, SILU, FK, false, ROWS>(a, it, ids);
-}
-
-template <int W, bool SILU, int FK, int ROWS>
-__device__ __forceinline__ void bwd_tcr_run(const BwdArgs &a, const TcItem &it,
-                                            const TcRowIds<ROWS> &ids) {
-    if (tc_interior<W, ROWS>(ids, it)) {
-        if (a.nt_load) bwd_tc_chunk<W, SILU, FK, true>(a, it);
-        else bwd_tc_chunk<W, SILU, FK, false>(a, it);
-        return;
-    }
-    if (a.nt_load) bwd_tcr_chunk<W, SILU, FK, true, ROWS>(a, it, ids);
-    else bwd_tcr_chunk<W, SILU, FK, false, ROWS>(a, it, ids);
-}
-
-// Packed rows pass the offsets' LDS array itself when they are staged (see
-// tc_row_ids), global memory otherwise.
-template <int W, bool SILU, int FK, int ROWS>
-__global__ __launch_bounds__(256) void k_fwd_tcr(FwdArgs a) {
-    constexpr bool PACKED = ROWS == kRowsPacked;
-    __shared__ int32_t s_cu[PACKED ? kLdsCuMax : 1];
-    __shared__ uint32_t s_bad[2];
-    if constexpr (PACKED) {
-        if (stage_and_validate(a.cu, a.n_seq, a.T, a.err, s_cu, s_bad, a.cu_in_lds,
-                               blockIdx.x == 0))
-            return;  // malformed or sticky: write nothing
-    }
+template <int W, bool SILU, int FK>
+__global__ __launch_bounds__(256) void k_fwd_tcs(FwdArgs a) {
     TcItem it;
     if (!tc_item(a, it)) return;
-    if (PACKED && a.cu_in_lds)
-        fwd_tcr_run<W, SILU, FK, ROWS>(a, it, tc_row_ids<ROWS>(a, it, s_cu));
-    else
-        fwd_tcr_run<W, SILU, FK, ROWS>(a, it, tc_row_ids<ROWS>(a, it, a.cu));
+    if (a.nt_load) fwd_tcs_chunk<W, SILU, FK, true>(a, it, tc_seq_ids(a, it));
+    else fwd_tcs_chunk<W, SILU, FK, false>(a, it, tc_seq_ids(a, it));
 }
 
-template <int W, bool SILU, int FK, int ROWS>
-__global__ __launch_bounds__(256) void k_bwd_tcr(BwdArgs a) {
-    constexpr bool PACKED = ROWS == kRowsPacked;
-    __shared__ int32_t s_cu[PACKED ? kLdsCuMax : 1];
-    __shared__ uint32_t s_bad[2];
-    if constexpr (PACKED) {
-        if (stage_and_validate(a.cu, a.n_seq, a.T, a.err, s_cu, s_bad, a.cu_in_lds,
-                               blockIdx.x == 0))
-            return;  // uniform over the block
-    }
+template <int W, bool SILU, int FK>
+__global__ __launch_bounds__(256) void k_bwd_tcs(BwdArgs a) {
     TcItem it;
     if (!tc_item(a, it)) return;
-    if (PACKED && a.cu_in_lds)
-        bwd_tcr_run<W, SILU, FK, ROWS>(a, it, tc_row_ids<ROWS>(a, it, s_cu));
-    else
-        bwd_tcr_run<W, SILU, FK, ROWS>(a, it, tc_row_ids<ROWS>(a, it, a.cu));
+    if (a.nt_load) bwd_tcs_chunk<W, SILU, FK, true>(a, it, tc_seq_ids(a, it));
+    else bwd_tcs_chunk<W, SILU, FK, false>(a, it, tc_seq_ids(a, it));
+}
+
+// ===========================================================================
+// Time lanes for packed rows (B = 1, unit stride along T)
+//
+// A packed chunk runs the dense rows' chunk code unchanged: the row's
+// initial state is sequence 0's, and it writes no final state and no state
+// gradient.  A repair then rewrites what the sequence boundaries near the
+// chunk change.  A boundary changes only the W-1 tokens on either side of
+// it, so the repair is a short pass with one lane per boundary, and the
+// tiles keep the dense code's registers, occupancy and speed.  The offsets
+// are validated by the launch before this one; a wave reads the flag word
+// first and writes nothing when it is set.  A chunk finds the sequences near
+// it from one offset per lane and two wave ballots when the row holds fewer
+// than 64 sequences (the offsets are loaded once the tiles are in flight and
+// looked at after them), else by a binary search with wave-uniform loads.
+//
+// Forward, for a sequence j = [s, e): the outputs at s .. s+W-2 take their
+// taps before s from the sequence's initial state (or zeros), and the chunk
+// holding e-1 writes the sequence's final state.
+//
+// Backward, at a boundary s between A = [sA, s) and B = [s, eB): A's last
+// W-1 tokens get dx without B's gradients and with A's final-state
+// gradient; B's first W-1 tokens get g, dx and their dW/dB terms from B's
+// own taps, and the dense pass's terms for them are taken out again; dinit
+// of B is worked out from those g's (plus, for a sequence shorter than W-1,
+// the final-state gradient slots that are initial-state slots).  The row's
+// end is a boundary with no B when a final-state gradient is given.
+//
+// The repair's stores to tokens of the chunk follow the dense pass's stores
+// of the same wave; a wave's vector memory operations complete in issue
+// order, and the repair waits for its own loads (issued after those stores)
+// before it stores, so its values are the ones that stay.
+// ===========================================================================
+
+// v[i] for 0 <= i < M, zero otherwise; i is known only at run time.
+template <int M>
+__device__ __forceinline__ float pick(const float (&v)[M], int64_t i) {
+    float r = 0.0f;
+#pragma unroll
+    for (int m = 0; m < M; ++m) r = i == m ? v[m] : r;
+    return r;
+}
+
+// Raw bits of token p of a row of T, zero outside [0, T) (the load reads
+// an in-row address either way).
+__device__ __forceinline__ uint16_t tcp_bits(const uint16_t *row, int64_t p, int64_t T) {
+    const uint16_t bits = row[p < 0 ? 0 : p >= T ? T - 1 : p];
+    return p >= 0 && p < T ? bits : uint16_t{0};
+}
+
+// Raw bits of the W-1 slots of sequence j, channel d, of a [N, D, W-1]
+// state tensor (zeros without one).
+template <int W>
+__device__ __forceinline__ void tcp_slot_bits(const Strided3 &st, int64_t j, int64_t d,
+                                              uint16_t (&v)[W - 1]) {
+    if (st.ptr) {
+        const uint16_t *r = static_cast<const uint16_t *>(st.ptr) + j * st.s0 + d * st.s1;
+#pragma unroll
+        for (int m = 0; m < W - 1; ++m) v[m] = r[m * st.s2];
+    } else {
+#pragma unroll
+        for (int m = 0; m < W - 1; ++m) v[m] = 0;
+    }
+}
+
+// The sticky flag word (this call's validation, or an earlier call's).
+__device__ __forceinline__ bool tcp_flag_set(const uint32_t *err) { return *err != 0u; }
+
+// One boundary's inputs for the forward repair: sequence j = [s, e), the
+// raw bits of its x_ext at s-(W-1) .. s+W-2 and of its final state.
+template <int W>
+struct FwdTcpIn {
+    int32_t s, e;
+    uint16_t xe[2 * (W - 1)];
+    uint16_t fin[W - 1];
+};
+
+// The forward repair, run by the dense chunk code after its tiles.
+template <int W, bool SILU, int FK>
+struct FwdTcpRepair {
+    const FwdArgs *a;  // the call's arguments, with the final states
+    const TcItem *it;
+    int64_t ja = 0, jb = -1;  // the sequences to look at (none: jb < ja)
+    bool few = false;         // fewer than 64 sequences: the offsets are in cl
+    int32_t cl = 0;           // lane l: cu[min(l, n)]
+
+    __device__ __forceinline__ FwdTcpIn<W> load(int64_t j, int32_t s, int32_t e) const {
+        const FwdArgs &A = *a;
+        const uint16_t *xr = static_cast<const uint16_t *>(A.x.ptr) + it->d * A.x.s1;
+        FwdTcpIn<W> r;
+        r.s = s;
+        r.e = e;
+        uint16_t st[W - 1];
+        tcp_slot_bits<W>(A.init, j, it->d, st);
+#pragma unroll
+        for (int i = 0; i < W - 1; ++i) {
+            r.xe[i] = st[i];
+            r.xe[W - 1 + i] = r.s + i < r.e ? tcp_bits(xr, r.s + i, A.T) : uint16_t{0};
+        }
+        // the last W-1 extended tokens, from the input or the initial state
+        // (every address valid; a zero token reads the input and is dropped)
+        const uint16_t *ir = A.init.ptr ? static_cast<const uint16_t *>(A.init.ptr) +
+                                              j * A.init.s0 + it->d * A.init.s1
+                                        : nullptr;
+#pragma unroll
+        for (int m = 0; m < W - 1; ++m) {
+            const int64_t p = static_cast<int64_t>(r.e) - (W - 1) + m;
+            const bool in_x = p >= r.s;
+            const uint16_t *src = in_x ? xr + p : ir ? ir + (p - r.s + W - 1) * A.init.s2 : xr;
+            const uint16_t bits = *src;
+            r.fin[m] = in_x || ir ? bits : uint16_t{0};
+        }
+        return r;
+    }
+
+    // Sequences whose first W-1 tokens or whose last token can fall in the
+    // chunk: from the one holding t0-(W-2) to the one holding t1-1
+    // (wave-uniform).
+    __device__ __forceinline__ void locate() {
+        const FwdArgs &A = *a;
+        const int64_t n = A.n_seq;
+        if (n < kWaveSize) {
+            // one offset per lane, looked at when the repair runs
+            few = true;
+            cl = A.cu[min(static_cast<int64_t>(threadIdx.x % kWaveSize), n)];
+            return;
+        }
+        const int32_t *cu = A.cu;
+        const int64_t lo = max(it->t0 - (W - 2), int64_t{0});
+        const int64_t j0 = find_row(cu, n, lo), j1 = find_row(cu, n, it->t1 - 1);
+        settle(j0, j1, cu[j0], cu[j1 + 1]);
+    }
+
+    __device__ __forceinline__ void settle(int64_t j0, int64_t j1, int64_t c0, int64_t c1) {
+        const bool starts = j1 > j0 || (j0 > 0 && c0 >= it->t0 - (W - 2));
+        const bool ends = a->fin.ptr && (j1 > j0 || c1 == it->t1);
+        if (starts || ends) {
+            ja = j0;
+            jb = j1;
+        }
+    }
+
+    __device__ __forceinline__ void operator()(const float (&w)[W][1], const float (&bias)[1]) {
+        if (few) {
+            const int64_t lo = max(it->t0 - (W - 2), int64_t{0});
+            const int64_t j0 = __popcll(__ballot(cl <= lo)) - 1;
+            const int64_t j1 = __popcll(__ballot(cl <= it->t1 - 1)) - 1;
+            settle(j0, j1, __builtin_amdgcn_readlane(cl, static_cast<int>(j0)),
+                   __builtin_amdgcn_readlane(cl, static_cast<int>(j1 + 1)));
+        }
+        if (jb < ja) return;
+        const FwdArgs &A = *a;
+        const int64_t t0 = it->t0, t1 = it->t1, d = it->d;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // after the dense pass's stores
+        uint16_t *yr = const_cast<uint16_t *>(static_cast<const uint16_t *>(A.y.ptr)) + d * A.y.s1;
+        for (int64_t j0 = ja; j0 <= jb; j0 += kWaveSize) {
+            const int64_t j = j0 + threadIdx.x % kWaveSize;
+            // few sequences: the offsets come from the lanes holding them, read
+            // while every lane is active (a lane moved from an inactive one
+            // reads zero)
+            int32_t fs = 0, fe = 0;
+            if (few) {
+                fs = __shfl(cl, static_cast<int>(j));
+                fe = __shfl(cl, static_cast<int>(j + 1));
+            }
+            if (j > jb) continue;
+            const FwdTcpIn<W> in = few ? load(j, fs, fe) : load(j, A.cu[j], A.cu[j + 1]);
+            const int64_t s = in.s, e = in.e;
+            if (j > 0 && s + (W - 2) >= t0 && s < t1) {
+#pragma unroll
+                for (int l = 0; l < W - 1; ++l) {
+                    const int64_t q = s + l;
+                    if (q < e && q >= t0 && q < t1) {
+                        float z = bias[0];
+#pragma unroll
+                        for (int k = 0; k < W; ++k)
+                            z = fmaf(w[k][0], bf16_bits_to_f32(in.xe[l + k]), z);
+                        yr[q] = to_bf16_bits(act<SILU>(z));
+                    }
+                }
+            }
+            if (A.fin.ptr && e - 1 >= t0 && e - 1 < t1) {
+                uint16_t *fr = const_cast<uint16_t *>(static_cast<const uint16_t *>(A.fin.ptr)) +
+                               j * A.fin.s0 + d * A.fin.s1;
+#pragma unroll
+                for (int m = 0; m < W - 1; ++m) fr[m * A.fin.s2] = in.fin[m];
+            }
+        }
+    }
+};
+
+template <int W, bool SILU, int FK>
+__global__ __launch_bounds__(256) void k_fwd_tcp(FwdArgs a) {
+    TcItem it;
+    if (!tc_item(a, it)) return;
+    if (tcp_flag_set(a.err)) return;  // malformed offsets: write nothing
+    FwdArgs da = a;
+    da.fin.ptr = nullptr;  // final states come from the repair
+    FwdTcpRepair<W, SILU, FK> fix{&a, &it};
+    if (a.nt_load) fwd_tc_chunk<W, SILU, FK, true>(da, it, fix);
+    else fwd_tc_chunk<W, SILU, FK, false>(da, it, fix);
+}
+
+// One boundary's inputs for the backward repair (boundary j, s = cu[j]):
+// the bounds of A = [sa, s) and B = [s, eb), x at s-2(W-1) .. s+2(W-1)-1,
+// dy at s-(W-1) .. s+2(W-1)-1, the initial-state slots of A, B and
+// sequence 0 and the final-state gradients of A and B (zeros for what the
+// call does not have), as raw bits.
+template <int W>
+struct BwdTcpIn {
+    int32_t s, sa, eb;
+    uint16_t X[4 * (W - 1)], Dy[3 * (W - 1)];
+    uint16_t ia[W - 1], ib[W - 1], i0[W - 1], fa[W - 1], fb[W - 1];
+};
+
+template <int M>
+__device__ __forceinline__ void tcp_widen(const uint16_t (&b)[M], float (&f)[M]) {
+#pragma unroll
+    for (int i = 0; i < M; ++i) f[i] = bf16_bits_to_f32(b[i]);
+}
+
+// The backward repair, run by the dense chunk code before its dW/dB wave
+// sums (so that its dW/dB terms join the chunk's).
+template <int W, bool SILU, int FK>
+struct BwdTcpRepair {
+    const BwdArgs *a;  // the call's arguments, with the state gradients
+    const TcItem *it;
+    int64_t ja = 0, jb = -1;  // the boundaries to look at (none: jb < ja)
+    bool few = false;         // fewer than 64 sequences: the offsets are in cl
+    int32_t cl = 0;           // lane l: cu[min(l, n)]
+
+    // Boundary j's inputs; s, sa and eb are cu[j] and its neighbours (or
+    // cu[j] where a neighbour does not exist).
+    __device__ __forceinline__ BwdTcpIn<W> load(int64_t j, int32_t s, int32_t sa,
+                                                int32_t eb) const {
+        const BwdArgs &A = *a;
+        const int64_t n = A.n_seq, T = A.T, d = it->d;
+        const uint16_t *xr = static_cast<const uint16_t *>(A.x.ptr) + d * A.x.s1;
+        const uint16_t *dyr = static_cast<const uint16_t *>(A.dy.ptr) + d * A.dy.s1;
+        const bool has_a = j > 0, has_b = j < n;
+        BwdTcpIn<W> r;
+        r.s = s;
+        r.sa = sa;
+        r.eb = eb;
+#pragma unroll
+        for (int i = 0; i < 4 * (W - 1); ++i) r.X[i] = tcp_bits(xr, r.s - 2 * (W - 1) + i, T);
+#pragma unroll
+        for (int i = 0; i < 3 * (W - 1); ++i) r.Dy[i] = tcp_bits(dyr, r.s - (W - 1) + i, T);
+        tcp_slot_bits<W>(A.init, has_a ? j - 1 : 0, d, r.ia);
+        tcp_slot_bits<W>(A.init, has_b ? j : 0, d, r.ib);
+        tcp_slot_bits<W>(A.init, 0, d, r.i0);
+        tcp_slot_bits<W>(A.dfin, has_a ? j - 1 : 0, d, r.fa);
+        tcp_slot_bits<W>(A.dfin, has_b ? j : 0, d, r.fb);
+        return r;
+    }
+
+    // The repair of boundary j (j = n is the row's end), in one lane.
+    __device__ __forceinline__ void boundary(int64_t j, const BwdTcpIn<W> &raw,
+                                             const float (&w)[W][1], const float (&bias)[1],
+                                             float (&dwacc)[W], float &dbacc) const {
+        constexpr bool BIAS = fk_bias(FK);
+        const BwdArgs &A = *a;
+        const int64_t n = A.n_seq, d = it->d, t0 = it->t0, t1 = it->t1;
+        uint16_t *dxr = const_cast<uint16_t *>(static_cast<const uint16_t *>(A.dx.ptr)) + d * A.dx.s1;
+        const bool has_a = j > 0, has_b = j < n;
+        const int64_t s = raw.s, sa = raw.sa, eb = raw.eb;
+        struct {
+            float X[4 * (W - 1)], Dy[3 * (W - 1)], ia[W - 1], ib[W - 1], i0[W - 1], fa[W - 1],
+                fb[W - 1];
+        } in;
+        tcp_widen(raw.X, in.X);
+        tcp_widen(raw.Dy, in.Dy);
+        tcp_widen(raw.ia, in.ia);
+        tcp_widen(raw.ib, in.ib);
+        tcp_widen(raw.i0, in.i0);
+        tcp_widen(raw.fa, in.fa);
+        tcp_widen(raw.fb, in.fb);
+
+        if (has_a) {
+            // A's last W-1 tokens u = s-(W-1)+i (those at or after sa)
+            float ga[W - 1];
+#pragma unroll
+            for (int i = 0; i < W - 1; ++i) {
+                const int64_t u = s - (W - 1) + i;
+                float z = bias[0];
+#pragma unroll
+                for (int k = 0; k < W; ++k) {
+                    const int64_t p = u - (W - 1) + k;
+                    z = fmaf(w[k][0], p >= sa ? in.X[i + k] : pick(in.ia, p - sa + W - 1), z);
+                }
+                ga[i] = u >= sa ? in.Dy[i] * act_slope<SILU>(z) : 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < W - 1; ++i) {
+                const int64_t u = s - (W - 1) + i;
+                if (u >= sa && u >= t0 && u < t1) {
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int m = W - 2; m >= 0; --m)
+                        if (i + m < W - 1) acc = fmaf(w[W - 1 - m][0], ga[i + m], acc);
+                    dxr[u] = to_bf16_bits(acc + in.fa[i]);
+                }
+            }
+        }
+        if (has_b) {
+            // B's first 2(W-1) tokens v = s+i, with B's taps (zero from eb on)
+            float gb[2 * (W - 1)];
+#pragma unroll
+            for (int i = 0; i < 2 * (W - 1); ++i) {
+                float z = bias[0];
+#pragma unroll
+                for (int k = 0; k < W; ++k)
+                    z = fmaf(w[k][0], i + k >= W - 1 ? in.X[i + k + W - 1] : in.ib[i + k], z);
+                gb[i] = s + i < eb ? in.Dy[i + W - 1] * act_slope<SILU>(z) : 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < W - 1; ++i) {
+                const int64_t v = s + i;
+                if (v < eb && v >= t0 && v < t1) {
+                    float acc = w[0][0] * gb[i + W - 1];
+#pragma unroll
+                    for (int m = W - 2; m >= 0; --m) acc = fmaf(w[W - 1 - m][0], gb[i + m], acc);
+                    dxr[v] = to_bf16_bits(acc + pick(in.fb, v - (eb - (W - 1))));
+                    if (has_a) {
+                        // take out the dense pass's dW/dB terms of v (its taps
+                        // were the row's tokens, or sequence 0's state before
+                        // the row) and put in B's
+                        float zd = bias[0], xd[W];
+#pragma unroll
+                        for (int k = 0; k < W; ++k) {
+                            const int64_t p = v - (W - 1) + k;
+                            xd[k] = p >= 0 ? in.X[i + k + W - 1] : pick(in.i0, p + W - 1);
+                            zd = fmaf(w[k][0], xd[k], zd);
+                        }
+                        const float gd = in.Dy[i + W - 1] * act_slope<SILU>(zd);
+#pragma unroll
+                        for (int k = 0; k < W; ++k) {
+                            const float xb = i + k >= W - 1 ? in.X[i + k + W - 1] : in.ib[i + k];
+                            dwacc[k] = fmaf(gb[i], xb, dwacc[k]);
+                            dwacc[k] = fmaf(-gd, xd[k], dwacc[k]);
+                        }
+                        if constexpr (BIAS) dbacc += gb[i] - gd;
+                    }
+                }
+            }
+            if (A.dinit.ptr && s >= t0 && s < t1) {
+                uint16_t *di = const_cast<uint16_t *>(static_cast<const uint16_t *>(A.dinit.ptr)) +
+                               j * A.dinit.s0 + d * A.dinit.s1;
+#pragma unroll
+                for (int m = 0; m < W - 1; ++m) {
+                    // dx_ext at s-(W-1)+m: the g's at s+m-k for k <= m, plus
+                    // a final-state slot that lands there
+                    float acc = w[0][0] * gb[m];
+#pragma unroll
+                    for (int k = W - 2; k >= 0; --k)
+                        if (m - (W - 1) + k >= 0) acc = fmaf(w[W - 1 - k][0], gb[m - (W - 1) + k], acc);
+                    di[m * A.dinit.s2] = to_bf16_bits(acc + pick(in.fb, m - (eb - s)));
+                }
+            }
+        }
+    }
+
+    // Boundaries s_j in [t0-(W-2), t1+W-2]: from the sequence holding
+    // t0-(W-2) to the one holding t1+W-2 or, when that is past the row and a
+    // final-state gradient is given, to the row's end (wave-uniform).
+    __device__ __forceinline__ void locate() {
+        const BwdArgs &A = *a;
+        const int64_t n = A.n_seq;
+        if (n < kWaveSize) {
+            // one offset per lane, looked at when the repair runs
+            few = true;
+            cl = A.cu[min(static_cast<int64_t>(threadIdx.x % kWaveSize), n)];
+            return;
+        }
+        const int32_t *cu = A.cu;
+        const int64_t j0 = find_row(cu, n, max(it->t0 - (W - 2), int64_t{0}));
+        const int64_t hi = it->t1 + (W - 2);
+        const int64_t j1 = hi >= A.T ? (A.dfin.ptr ? n : n - 1) : find_row(cu, n, hi);
+        settle(j0, j1, cu[j0]);
+    }
+
+    __device__ __forceinline__ void settle(int64_t j0, int64_t j1, int64_t c0) {
+        if (j1 > j0 || (j0 > 0 && c0 >= it->t0 - (W - 2)) ||
+            (j0 == 0 && it->t0 == 0 && a->dinit.ptr)) {
+            ja = j0;
+            jb = j1;
+        }
+    }
+
+    __device__ __forceinline__ void operator()(const float (&w)[W][1], const float (&bias)[1],
+                                               float (&dwacc)[W], float &dbacc) {
+        if (few) {
+            const BwdArgs &A = *a;
+            const int64_t n = A.n_seq;
+            const int64_t j0 = __popcll(__ballot(cl <= max(it->t0 - (W - 2), int64_t{0}))) - 1;
+            const int64_t hi = it->t1 + (W - 2);
+            const int64_t j1 =
+                hi >= A.T ? (A.dfin.ptr ? n : n - 1) : __popcll(__ballot(cl <= hi)) - 1;
+            settle(j0, j1, __builtin_amdgcn_readlane(cl, static_cast<int>(j0)));
+        }
+        if (jb < ja) return;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // after the dense pass's stores
+        const int64_t n = a->n_seq;
+        for (int64_t j0 = ja; j0 <= jb; j0 += kWaveSize) {
+            const int64_t j = j0 + threadIdx.x % kWaveSize;
+            const int64_t ia = j > 0 ? j - 1 : j, ib = j < n ? j + 1 : j;
+            // few sequences: the offsets come from the lanes holding them, read
+            // while every lane is active (a lane moved from an inactive one
+            // reads zero)
+            int32_t fs = 0, fa = 0, fb = 0;
+            if (few) {
+                fs = __shfl(cl, static_cast<int>(j));
+                fa = __shfl(cl, static_cast<int>(ia));
+                fb = __shfl(cl, static_cast<int>(ib));
+            }
+            if (j > jb) continue;
+            const BwdTcpIn<W> in = few ? load(j, fs, fa, fb) : load(j, a->cu[j], a->cu[ia], a->cu[ib]);
+            boundary(j, in, w, bias, dwacc, dbacc);
+        }
+    }
+};
+
+template <int W, bool SILU, int FK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CCV_TC_BWD_WAVES)))
+void k_bwd_tcp(BwdArgs a) {
+    TcItem it;
+    if (!tc_item(a, it)) return;
+    if (tcp_flag_set(a.err)) return;  // malformed offsets: write nothing
+    BwdArgs da = a;
+    da.dfin.ptr = nullptr;  // the state gradients come from the repair
+    da.dinit.ptr = nullptr;
+    BwdTcpRepair<W, SILU, FK> fix{&a, &it};
+    if (a.nt_load) bwd_tc_chunk<W, SILU, FK, true>(da, it, fix);
+    else bwd_tc_chunk<W, SILU, FK, false>(da, it, fix);
 }
 
 // ===========================================================================

@@ -50,15 +50,15 @@ hipError_t fwd_vec(const FwdArgs &a, int silu, int rows, int fk, hipStream_t s, 
 
 // The software-pipelined forward is built for 8-channel lanes of dense and
 // packed rows only.
-// Time-lane kernels: dense rows, and packed or seq_idx rows (per-token ids).
+// Time-lane kernels: dense rows, packed rows (the dense code plus a repair at
+// the sequence boundaries) and seq_idx rows (per-token ids).
 template <int W>
 hipError_t fwd_tc(const FwdArgs &a, int silu, int fk, int rows, hipStream_t s) {
 #define CCV_TC(S, F)                                                                    \
     if (!!silu == S && fk == F) {                                                       \
         if (rows == kRowsDense) return launch(k_fwd_tc<W, S, F>, a.n_block, a, s);       \
-        if (rows == kRowsPacked)                                                        \
-            return launch(k_fwd_tcr<W, S, F, kRowsPacked>, a.n_block, a, s);            \
-        if (rows == kRowsSeq) return launch(k_fwd_tcr<W, S, F, kRowsSeq>, a.n_block, a, s); \
+        if (rows == kRowsPacked) return launch(k_fwd_tcp<W, S, F>, a.n_block, a, s);     \
+        if (rows == kRowsSeq) return launch(k_fwd_tcs<W, S, F>, a.n_block, a, s);        \
     }
     CCV_TC(true, kBf16) CCV_TC(true, kBf16Bias) CCV_TC(true, kF32) CCV_TC(true, kF32Bias)
     CCV_TC(false, kBf16) CCV_TC(false, kBf16Bias) CCV_TC(false, kF32) CCV_TC(false, kF32Bias)
@@ -71,9 +71,8 @@ hipError_t bwd_tc(const BwdArgs &a, int silu, int fk, int rows, hipStream_t s) {
 #define CCV_TC(S, F)                                                                    \
     if (!!silu == S && fk == F) {                                                       \
         if (rows == kRowsDense) return launch(k_bwd_tc<W, S, F>, a.n_block, a, s);       \
-        if (rows == kRowsPacked)                                                        \
-            return launch(k_bwd_tcr<W, S, F, kRowsPacked>, a.n_block, a, s);            \
-        if (rows == kRowsSeq) return launch(k_bwd_tcr<W, S, F, kRowsSeq>, a.n_block, a, s); \
+        if (rows == kRowsPacked) return launch(k_bwd_tcp<W, S, F>, a.n_block, a, s);     \
+        if (rows == kRowsSeq) return launch(k_bwd_tcs<W, S, F>, a.n_block, a, s);        \
     }
     CCV_TC(true, kBf16) CCV_TC(true, kBf16Bias) CCV_TC(true, kF32) CCV_TC(true, kF32Bias)
     CCV_TC(false, kBf16) CCV_TC(false, kBf16Bias) CCV_TC(false, kF32) CCV_TC(false, kF32Bias)

@@ -1,5 +1,6 @@
-"""Full-size parity of the five named workloads, in the launch configuration
-the benchmark times (the same calls, the same shapes and layouts).
+"""Full-size parity of the named workloads, in the launch configuration the
+benchmark times (the same calls, the same shapes and layouts, and the
+[B,D,T]-contiguous variants of the dense, packed, large and seq_idx ones).
 
 * Every output buffer starts filled with a sentinel (a BF16 NaN pattern no
   finite input produces), so an element no launch wrote is caught anywhere
@@ -74,8 +75,13 @@ def no_sentinel(name, t):
     assert left == 0, "%s: %d elements never written" % (name, left)
 
 
-def run_workload(idx):
+def run_workload(idx, tc=False):
+    """tc: the workload's activations in [B,D,T] time-contiguous storage (the
+    benchmark's *_tc workloads) instead of its own layout."""
     w = synth.workload(idx)
+    if tc:
+        w = dict(w, x=w["x"].contiguous(),
+                 dy=None if w["dy"] is None else w["dy"].contiguous())
     g = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in w.items()}
     x = g["x"]
     assert x.stride() == w["x"].stride()
@@ -232,8 +238,7 @@ def test_workload_5_large_deterministic():
     assert torch.equal(dx.view(torch.int16), out["dx"].view(torch.int16))
 
 
-def test_workload_6_seq_idx_fwd_bwd():
-    w, g, out = run_workload(6)
+def check_seq_sample(w, out):
     D = w["x"].shape[1]
     sel = sample_channels(D)
     seq = w["seq_idx"].numpy()
@@ -244,6 +249,25 @@ def test_workload_6_seq_idx_fwd_bwd():
     check_bf16("dx", out["dx"][:, sel], odx)
     check_f32_rel("dweight", out["dw"][sel], odw)
     check_f32_rel("dbias", out["db"][sel], odb)
+
+
+def test_workload_6_seq_idx_fwd_bwd():
+    w, g, out = run_workload(6)
+    check_seq_sample(w, out)
+
+
+@pytest.mark.parametrize("idx", [2, 3, 5, 6])
+def test_workload_time_contiguous(idx):
+    """The dense, packed, large and seq_idx workloads with [B,D,T]-contiguous
+    activations, which run on the time-lane kernels."""
+    w, g, out = run_workload(idx, tc=True)
+    assert w["x"].stride(2) == 1
+    if idx == 6:
+        check_seq_sample(w, out)
+    elif idx == 5:
+        check_sample(w, out)
+    else:
+        check_full(w, out, 256 if idx == 2 else 64)
 
 
 def test_more_than_2_pow_31_elements():
