@@ -532,10 +532,8 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     if (time_lanes) set_tc_div(a);
     // packed rows on time lanes always take the validation launch first
     a.cu_in_lds = p.packed && !time_lanes && p.N + 1 <= ccv::kLdsCuMax;
-    // packed rows on time lanes keep their inputs cached: the repair at the
-    // sequence boundaries reads some of them again
-    a.nt_load = !(p.packed && time_lanes) &&
-                p.B * p.D * p.T * 2 >= (p.seq ? CCV_NT_LOAD_MIN_BYTES_SEQ : CCV_NT_LOAD_MIN_BYTES);
+    a.nt_load = p.B * p.D * p.T * 2 >=
+                (p.seq ? CCV_NT_LOAD_MIN_BYTES_SEQ : CCV_NT_LOAD_MIN_BYTES);
     if (p.packed && !a.cu_in_lds) {
         rc = hip_status(ccv::launch_validate(a.cu, p.N, p.T, err_flag, 0, stream));
         if (rc != CCV_OK) return rc;
@@ -604,7 +602,11 @@ int bwd_call(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bi
                                        CCV_BWD_TARGET_WAVES, CCV_BWD_MIN_CHUNK);
     if (!time_lanes)
         add_tail(g, p, ccv::kWavesPerBlock, CCV_BWD_TAIL_PCT, CCV_BWD_TAIL_CHUNK, 1);
-    const int64_t n_part = (p.packed ? 1 : p.B) * (g.n_tblk + g.n_tblk_t);
+    // packed rows on time lanes: the boundary repair's partial rows follow
+    // the chunks' (one per channel and group of 64 boundaries)
+    const int64_t n_part = (p.packed ? 1 : p.B) * (g.n_tblk + g.n_tblk_t) +
+                           (p.packed && time_lanes ? (p.N + 1 + ccv::kWaveSize - 1) / ccv::kWaveSize
+                                                   : 0);
     const size_t need = use_partials
                             ? static_cast<size_t>(n_part) * static_cast<size_t>(p.D * kp) * 4
                             : 0;
@@ -661,9 +663,8 @@ int bwd_call(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bi
     a.n_seq = p.N;
     a.err = p.packed ? err_flag : nullptr;
     set_seq(a, seq_idx, p);
-    a.nt_load = !(p.packed && time_lanes) &&
-                2 * p.B * p.D * p.T * 2 >=
-                    (p.seq ? CCV_NT_LOAD_MIN_BYTES_SEQ_BWD : CCV_NT_LOAD_MIN_BYTES);
+    a.nt_load = 2 * p.B * p.D * p.T * 2 >=
+                (p.seq ? CCV_NT_LOAD_MIN_BYTES_SEQ_BWD : CCV_NT_LOAD_MIN_BYTES);
     const int silu = activation == CCV_ACT_SILU;
     const int rounds = p.packed ? CCV_BWD_PACKED_ROUNDS : CCV_BWD_ROUNDS;
     if (!use_partials && rounds > 0 && !time_lanes) {

@@ -1313,20 +1313,8 @@ __device__ __forceinline__ bool tc_item(const A &a, TcItem &it) {
     return true;
 }
 
-// No repair: the dense rows' chunks.  A repair is told where its chunk is
-// once the chunk's loads are issued (`locate`), and runs after the tiles
-// (the forward) or before the dW/dB wave sums (the backward).
-struct TcNoFix {
-    __device__ __forceinline__ void locate() {}
-    template <int W>
-    __device__ __forceinline__ void operator()(const float (&)[W][1], const float (&)[1]) {}
-    template <int W>
-    __device__ __forceinline__ void operator()(const float (&)[W][1], const float (&)[1],
-                                               float (&)[W], float &) {}
-};
-
-template <int W, bool SILU, int FK, bool NTL, typename Fix>
-__device__ __forceinline__ void fwd_tc_chunk(const FwdArgs &a, const TcItem &it, Fix &fix) {
+template <int W, bool SILU, int FK, bool NTL>
+__device__ __forceinline__ void fwd_tc_chunk(const FwdArgs &a, const TcItem &it) {
     const int lane = threadIdx.x % kWaveSize;
     const uint16_t *xr = static_cast<const uint16_t *>(a.x.ptr) + it.b * a.x.s0 + it.d * a.x.s1;
     uint16_t *yr = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.y.ptr)) +
@@ -1349,7 +1337,6 @@ __device__ __forceinline__ void fwd_tc_chunk(const FwdArgs &a, const TcItem &it,
         if (t < it.t1) raw[c] = tc_load<NTL>(xr, t, it.t1);
         else raw[c].v = u32x4_t{0u, 0u, 0u, 0u};
     }
-    fix.locate();
     float carry[W - 1];  // x_ext of the W-1 tokens before the current tile
 #pragma unroll
     for (int j = 0; j < W - 1; ++j) carry[j] = kept_f32(lh[j], lh_keep[j]);
@@ -1379,16 +1366,14 @@ __device__ __forceinline__ void fwd_tc_chunk(const FwdArgs &a, const TcItem &it,
     if (it.t1 == a.T && a.fin.ptr && lane < W - 1)
         const_cast<uint16_t *>(static_cast<const uint16_t *>(a.fin.ptr))
             [it.b * a.fin.s0 + it.d * a.fin.s1 + lane * a.fin.s2] = fin_keep ? fin_bits : 0;
-    fix(w, bias);
 }
 
 template <int W, bool SILU, int FK>
 __global__ __launch_bounds__(256) void k_fwd_tc(FwdArgs a) {
     TcItem it;
     if (!tc_item(a, it)) return;
-    TcNoFix fix;
-    if (a.nt_load) fwd_tc_chunk<W, SILU, FK, true>(a, it, fix);
-    else fwd_tc_chunk<W, SILU, FK, false>(a, it, fix);
+    if (a.nt_load) fwd_tc_chunk<W, SILU, FK, true>(a, it);
+    else fwd_tc_chunk<W, SILU, FK, false>(a, it);
 }
 
 // Backward on time lanes.  Per tile: z and g = dy * act'(z) for the lane's
@@ -1398,8 +1383,8 @@ __global__ __launch_bounds__(256) void k_fwd_tc(FwdArgs a) {
 // chunk's last tile the W-1 g's past the chunk are computed directly (the
 // right halo).  dW/dB: one wave sum per chunk, then an atomic or a unique
 // partial.
-template <int W, bool SILU, int FK, bool NTL, typename Fix>
-__device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it, Fix &fix) {
+template <int W, bool SILU, int FK, bool NTL>
+__device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it) {
     constexpr bool BIAS = fk_bias(FK);
     const int lane = threadIdx.x % kWaveSize;
     const uint16_t *xr = static_cast<const uint16_t *>(a.x.ptr) + it.b * a.x.s0 + it.d * a.x.s1;
@@ -1439,7 +1424,6 @@ __device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it,
     }
     float w[W][1], bias[1];
     load_filter<W, 1, FK>(a.w, a.w_sd, a.w_sk, a.bias, a.b_s, it.d, w, bias);
-    fix.locate();
     float carry[W - 1];
 #pragma unroll
     for (int j = 0; j < W - 1; ++j) carry[j] = kept_f32(lh[j], lh_keep[j]);
@@ -1554,7 +1538,6 @@ __device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it,
         }
         emit(tprev, gprev, after);
     }
-    fix(w, bias, dwacc, dbacc);
     // dW/dB of the chunk: a wave sum, then one atomic or one partial per tap.
 #pragma unroll
     for (int k = 0; k < W; ++k) dwacc[k] = wave_sum(dwacc[k]);
@@ -1579,9 +1562,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CCV_TC_BWD_
 void k_bwd_tc(BwdArgs a) {
     TcItem it;
     if (!tc_item(a, it)) return;
-    TcNoFix fix;
-    if (a.nt_load) bwd_tc_chunk<W, SILU, FK, true>(a, it, fix);
-    else bwd_tc_chunk<W, SILU, FK, false>(a, it, fix);
+    if (a.nt_load) bwd_tc_chunk<W, SILU, FK, true>(a, it);
+    else bwd_tc_chunk<W, SILU, FK, false>(a, it);
 }
 
 // ===========================================================================
@@ -1918,34 +1900,29 @@ __global__ __launch_bounds__(256) void k_bwd_tcs(BwdArgs a) {
 // ===========================================================================
 // Time lanes for packed rows (B = 1, unit stride along T)
 //
-// A packed chunk runs the dense rows' chunk code unchanged: the row's
-// initial state is sequence 0's, and it writes no final state and no state
-// gradient.  A repair then rewrites what the sequence boundaries near the
-// chunk change.  A boundary changes only the W-1 tokens on either side of
-// it, so the repair is a short pass with one lane per boundary, and the
-// tiles keep the dense code's registers, occupancy and speed.  The offsets
-// are validated by the launch before this one; a wave reads the flag word
-// first and writes nothing when it is set.  A chunk finds the sequences near
-// it from one offset per lane and two wave ballots when the row holds fewer
-// than 64 sequences (the offsets are loaded once the tiles are in flight and
-// looked at after them), else by a binary search with wave-uniform loads.
+// Two launches after the validation launch.  The first is the dense rows'
+// chunk code unchanged: the row's initial state is sequence 0's, and it
+// writes no final state and no state gradient.  The second repairs what the
+// sequence boundaries change, with one lane per (channel, boundary): a
+// boundary changes only the W-1 tokens on either side of it.  So the tiles
+// run at the dense code's registers, occupancy and speed, and the repair's
+// stores come after the first launch's by stream order.  Both launches read
+// the flag word first and write nothing when it is set.
 //
 // Forward, for a sequence j = [s, e): the outputs at s .. s+W-2 take their
-// taps before s from the sequence's initial state (or zeros), and the chunk
-// holding e-1 writes the sequence's final state.
+// taps before s from the sequence's initial state (or zeros), and the
+// repair writes the sequence's final state.
 //
-// Backward, at a boundary s between A = [sA, s) and B = [s, eB): A's last
+// Backward, at a boundary s between A = [sa, s) and B = [s, eb): A's last
 // W-1 tokens get dx without B's gradients and with A's final-state
 // gradient; B's first W-1 tokens get g, dx and their dW/dB terms from B's
 // own taps, and the dense pass's terms for them are taken out again; dinit
 // of B is worked out from those g's (plus, for a sequence shorter than W-1,
-// the final-state gradient slots that are initial-state slots).  The row's
-// end is a boundary with no B when a final-state gradient is given.
-//
-// The repair's stores to tokens of the chunk follow the dense pass's stores
-// of the same wave; a wave's vector memory operations complete in issue
-// order, and the repair waits for its own loads (issued after those stores)
-// before it stores, so its values are the ones that stay.
+// the final-state gradient slots that are initial-state slots).  Boundary 0
+// is the row's start (dinit of sequence 0) and boundary N its end (the last
+// sequence's final-state gradient).  A wave's dW/dB terms are summed and
+// added like a chunk's: by atomics, or as partial rows after the first
+// launch's, in the order the fixed-order reduction reads them.
 // ===========================================================================
 
 // v[i] for 0 <= i < M, zero otherwise; i is known only at run time.
@@ -1957,153 +1934,45 @@ __device__ __forceinline__ float pick(const float (&v)[M], int64_t i) {
     return r;
 }
 
-// Raw bits of token p of a row of T, zero outside [0, T) (the load reads
-// an in-row address either way).
-__device__ __forceinline__ uint16_t tcp_bits(const uint16_t *row, int64_t p, int64_t T) {
+// Token p of a row of T, zero outside [0, T) (the load reads an in-row
+// address either way).
+__device__ __forceinline__ float tcp_tok(const uint16_t *row, int64_t p, int64_t T) {
     const uint16_t bits = row[p < 0 ? 0 : p >= T ? T - 1 : p];
-    return p >= 0 && p < T ? bits : uint16_t{0};
+    return p >= 0 && p < T ? bf16_bits_to_f32(bits) : 0.0f;
 }
 
-// Raw bits of the W-1 slots of sequence j, channel d, of a [N, D, W-1]
-// state tensor (zeros without one).
+// The W-1 slots of sequence j, channel d, of a [N, D, W-1] state tensor
+// (zeros without one).
 template <int W>
-__device__ __forceinline__ void tcp_slot_bits(const Strided3 &st, int64_t j, int64_t d,
-                                              uint16_t (&v)[W - 1]) {
+__device__ __forceinline__ void tcp_slots(const Strided3 &st, int64_t j, int64_t d,
+                                          float (&v)[W - 1]) {
     if (st.ptr) {
         const uint16_t *r = static_cast<const uint16_t *>(st.ptr) + j * st.s0 + d * st.s1;
 #pragma unroll
-        for (int m = 0; m < W - 1; ++m) v[m] = r[m * st.s2];
+        for (int m = 0; m < W - 1; ++m) v[m] = bf16_bits_to_f32(r[m * st.s2]);
     } else {
 #pragma unroll
-        for (int m = 0; m < W - 1; ++m) v[m] = 0;
+        for (int m = 0; m < W - 1; ++m) v[m] = 0.0f;
     }
 }
 
 // The sticky flag word (this call's validation, or an earlier call's).
 __device__ __forceinline__ bool tcp_flag_set(const uint32_t *err) { return *err != 0u; }
 
-// One boundary's inputs for the forward repair: sequence j = [s, e), the
-// raw bits of its x_ext at s-(W-1) .. s+W-2 and of its final state.
-template <int W>
-struct FwdTcpIn {
-    int32_t s, e;
-    uint16_t xe[2 * (W - 1)];
-    uint16_t fin[W - 1];
+// The repair launch's work item: channel d and the lanes' boundaries
+// j = 64 g + lane, g < groups.
+struct TcpItem {
+    int64_t d, g, j;
 };
-
-// The forward repair, run by the dense chunk code after its tiles.
-template <int W, bool SILU, int FK>
-struct FwdTcpRepair {
-    const FwdArgs *a;  // the call's arguments, with the final states
-    const TcItem *it;
-    int64_t ja = 0, jb = -1;  // the sequences to look at (none: jb < ja)
-    bool few = false;         // fewer than 64 sequences: the offsets are in cl
-    int32_t cl = 0;           // lane l: cu[min(l, n)]
-
-    __device__ __forceinline__ FwdTcpIn<W> load(int64_t j, int32_t s, int32_t e) const {
-        const FwdArgs &A = *a;
-        const uint16_t *xr = static_cast<const uint16_t *>(A.x.ptr) + it->d * A.x.s1;
-        FwdTcpIn<W> r;
-        r.s = s;
-        r.e = e;
-        uint16_t st[W - 1];
-        tcp_slot_bits<W>(A.init, j, it->d, st);
-#pragma unroll
-        for (int i = 0; i < W - 1; ++i) {
-            r.xe[i] = st[i];
-            r.xe[W - 1 + i] = r.s + i < r.e ? tcp_bits(xr, r.s + i, A.T) : uint16_t{0};
-        }
-        // the last W-1 extended tokens, from the input or the initial state
-        // (every address valid; a zero token reads the input and is dropped)
-        const uint16_t *ir = A.init.ptr ? static_cast<const uint16_t *>(A.init.ptr) +
-                                              j * A.init.s0 + it->d * A.init.s1
-                                        : nullptr;
-#pragma unroll
-        for (int m = 0; m < W - 1; ++m) {
-            const int64_t p = static_cast<int64_t>(r.e) - (W - 1) + m;
-            const bool in_x = p >= r.s;
-            const uint16_t *src = in_x ? xr + p : ir ? ir + (p - r.s + W - 1) * A.init.s2 : xr;
-            const uint16_t bits = *src;
-            r.fin[m] = in_x || ir ? bits : uint16_t{0};
-        }
-        return r;
-    }
-
-    // Sequences whose first W-1 tokens or whose last token can fall in the
-    // chunk: from the one holding t0-(W-2) to the one holding t1-1
-    // (wave-uniform).
-    __device__ __forceinline__ void locate() {
-        const FwdArgs &A = *a;
-        const int64_t n = A.n_seq;
-        if (n < kWaveSize) {
-            // one offset per lane, looked at when the repair runs
-            few = true;
-            cl = A.cu[min(static_cast<int64_t>(threadIdx.x % kWaveSize), n)];
-            return;
-        }
-        const int32_t *cu = A.cu;
-        const int64_t lo = max(it->t0 - (W - 2), int64_t{0});
-        const int64_t j0 = find_row(cu, n, lo), j1 = find_row(cu, n, it->t1 - 1);
-        settle(j0, j1, cu[j0], cu[j1 + 1]);
-    }
-
-    __device__ __forceinline__ void settle(int64_t j0, int64_t j1, int64_t c0, int64_t c1) {
-        const bool starts = j1 > j0 || (j0 > 0 && c0 >= it->t0 - (W - 2));
-        const bool ends = a->fin.ptr && (j1 > j0 || c1 == it->t1);
-        if (starts || ends) {
-            ja = j0;
-            jb = j1;
-        }
-    }
-
-    __device__ __forceinline__ void operator()(const float (&w)[W][1], const float (&bias)[1]) {
-        if (few) {
-            const int64_t lo = max(it->t0 - (W - 2), int64_t{0});
-            const int64_t j0 = __popcll(__ballot(cl <= lo)) - 1;
-            const int64_t j1 = __popcll(__ballot(cl <= it->t1 - 1)) - 1;
-            settle(j0, j1, __builtin_amdgcn_readlane(cl, static_cast<int>(j0)),
-                   __builtin_amdgcn_readlane(cl, static_cast<int>(j1 + 1)));
-        }
-        if (jb < ja) return;
-        const FwdArgs &A = *a;
-        const int64_t t0 = it->t0, t1 = it->t1, d = it->d;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // after the dense pass's stores
-        uint16_t *yr = const_cast<uint16_t *>(static_cast<const uint16_t *>(A.y.ptr)) + d * A.y.s1;
-        for (int64_t j0 = ja; j0 <= jb; j0 += kWaveSize) {
-            const int64_t j = j0 + threadIdx.x % kWaveSize;
-            // few sequences: the offsets come from the lanes holding them, read
-            // while every lane is active (a lane moved from an inactive one
-            // reads zero)
-            int32_t fs = 0, fe = 0;
-            if (few) {
-                fs = __shfl(cl, static_cast<int>(j));
-                fe = __shfl(cl, static_cast<int>(j + 1));
-            }
-            if (j > jb) continue;
-            const FwdTcpIn<W> in = few ? load(j, fs, fe) : load(j, A.cu[j], A.cu[j + 1]);
-            const int64_t s = in.s, e = in.e;
-            if (j > 0 && s + (W - 2) >= t0 && s < t1) {
-#pragma unroll
-                for (int l = 0; l < W - 1; ++l) {
-                    const int64_t q = s + l;
-                    if (q < e && q >= t0 && q < t1) {
-                        float z = bias[0];
-#pragma unroll
-                        for (int k = 0; k < W; ++k)
-                            z = fmaf(w[k][0], bf16_bits_to_f32(in.xe[l + k]), z);
-                        yr[q] = to_bf16_bits(act<SILU>(z));
-                    }
-                }
-            }
-            if (A.fin.ptr && e - 1 >= t0 && e - 1 < t1) {
-                uint16_t *fr = const_cast<uint16_t *>(static_cast<const uint16_t *>(A.fin.ptr)) +
-                               j * A.fin.s0 + d * A.fin.s1;
-#pragma unroll
-                for (int m = 0; m < W - 1; ++m) fr[m * A.fin.s2] = in.fin[m];
-            }
-        }
-    }
-};
+__device__ __forceinline__ bool tcp_item(int64_t D, int64_t groups, TcpItem &it) {
+    const int64_t wid = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock +
+                        __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
+    if (wid >= D * groups) return false;
+    it.d = wid / groups;
+    it.g = wid - it.d * groups;
+    it.j = it.g * kWaveSize + threadIdx.x % kWaveSize;
+    return true;
+}
 
 template <int W, bool SILU, int FK>
 __global__ __launch_bounds__(256) void k_fwd_tcp(FwdArgs a) {
@@ -2112,229 +1981,59 @@ __global__ __launch_bounds__(256) void k_fwd_tcp(FwdArgs a) {
     if (tcp_flag_set(a.err)) return;  // malformed offsets: write nothing
     FwdArgs da = a;
     da.fin.ptr = nullptr;  // final states come from the repair
-    FwdTcpRepair<W, SILU, FK> fix{&a, &it};
-    if (a.nt_load) fwd_tc_chunk<W, SILU, FK, true>(da, it, fix);
-    else fwd_tc_chunk<W, SILU, FK, false>(da, it, fix);
+    if (a.nt_load) fwd_tc_chunk<W, SILU, FK, true>(da, it);
+    else fwd_tc_chunk<W, SILU, FK, false>(da, it);
 }
 
-// One boundary's inputs for the backward repair (boundary j, s = cu[j]):
-// the bounds of A = [sa, s) and B = [s, eb), x at s-2(W-1) .. s+2(W-1)-1,
-// dy at s-(W-1) .. s+2(W-1)-1, the initial-state slots of A, B and
-// sequence 0 and the final-state gradients of A and B (zeros for what the
-// call does not have), as raw bits.
-template <int W>
-struct BwdTcpIn {
-    int32_t s, sa, eb;
-    uint16_t X[4 * (W - 1)], Dy[3 * (W - 1)];
-    uint16_t ia[W - 1], ib[W - 1], i0[W - 1], fa[W - 1], fb[W - 1];
-};
-
-template <int M>
-__device__ __forceinline__ void tcp_widen(const uint16_t (&b)[M], float (&f)[M]) {
-#pragma unroll
-    for (int i = 0; i < M; ++i) f[i] = bf16_bits_to_f32(b[i]);
-}
-
-// The backward repair, run by the dense chunk code before its dW/dB wave
-// sums (so that its dW/dB terms join the chunk's).
+// Forward repair: lane j is sequence j = [s, e).
 template <int W, bool SILU, int FK>
-struct BwdTcpRepair {
-    const BwdArgs *a;  // the call's arguments, with the state gradients
-    const TcItem *it;
-    int64_t ja = 0, jb = -1;  // the boundaries to look at (none: jb < ja)
-    bool few = false;         // fewer than 64 sequences: the offsets are in cl
-    int32_t cl = 0;           // lane l: cu[min(l, n)]
-
-    // Boundary j's inputs; s, sa and eb are cu[j] and its neighbours (or
-    // cu[j] where a neighbour does not exist).
-    __device__ __forceinline__ BwdTcpIn<W> load(int64_t j, int32_t s, int32_t sa,
-                                                int32_t eb) const {
-        const BwdArgs &A = *a;
-        const int64_t n = A.n_seq, T = A.T, d = it->d;
-        const uint16_t *xr = static_cast<const uint16_t *>(A.x.ptr) + d * A.x.s1;
-        const uint16_t *dyr = static_cast<const uint16_t *>(A.dy.ptr) + d * A.dy.s1;
-        const bool has_a = j > 0, has_b = j < n;
-        BwdTcpIn<W> r;
-        r.s = s;
-        r.sa = sa;
-        r.eb = eb;
+__global__ __launch_bounds__(256) void k_fwd_tcp_fix(FwdArgs a) {
+    TcpItem it;
+    if (!tcp_item(a.D, (a.n_seq + kWaveSize - 1) / kWaveSize, it)) return;
+    if (tcp_flag_set(a.err)) return;
+    const int64_t j = it.j, d = it.d;
+    if (j >= a.n_seq) return;
+    const uint16_t *xr = static_cast<const uint16_t *>(a.x.ptr) + d * a.x.s1;
+    uint16_t *yr = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.y.ptr)) + d * a.y.s1;
+    const int64_t s = a.cu[j], e = a.cu[j + 1];
+    float w[W][1], bias[1];
+    load_filter<W, 1, FK>(a.w, a.w_sd, a.w_sk, a.bias, a.b_s, d, w, bias);
+    if (j > 0) {
+        // x_ext of sequence j at s-(W-1) .. s+W-2
+        float st[W - 1], xe[2 * (W - 1)];
+        tcp_slots<W>(a.init, j, d, st);
 #pragma unroll
-        for (int i = 0; i < 4 * (W - 1); ++i) r.X[i] = tcp_bits(xr, r.s - 2 * (W - 1) + i, T);
+        for (int i = 0; i < W - 1; ++i) {
+            xe[i] = st[i];
+            xe[W - 1 + i] = s + i < e ? tcp_tok(xr, s + i, a.T) : 0.0f;
+        }
 #pragma unroll
-        for (int i = 0; i < 3 * (W - 1); ++i) r.Dy[i] = tcp_bits(dyr, r.s - (W - 1) + i, T);
-        tcp_slot_bits<W>(A.init, has_a ? j - 1 : 0, d, r.ia);
-        tcp_slot_bits<W>(A.init, has_b ? j : 0, d, r.ib);
-        tcp_slot_bits<W>(A.init, 0, d, r.i0);
-        tcp_slot_bits<W>(A.dfin, has_a ? j - 1 : 0, d, r.fa);
-        tcp_slot_bits<W>(A.dfin, has_b ? j : 0, d, r.fb);
-        return r;
-    }
-
-    // The repair of boundary j (j = n is the row's end), in one lane.
-    __device__ __forceinline__ void boundary(int64_t j, const BwdTcpIn<W> &raw,
-                                             const float (&w)[W][1], const float (&bias)[1],
-                                             float (&dwacc)[W], float &dbacc) const {
-        constexpr bool BIAS = fk_bias(FK);
-        const BwdArgs &A = *a;
-        const int64_t n = A.n_seq, d = it->d, t0 = it->t0, t1 = it->t1;
-        uint16_t *dxr = const_cast<uint16_t *>(static_cast<const uint16_t *>(A.dx.ptr)) + d * A.dx.s1;
-        const bool has_a = j > 0, has_b = j < n;
-        const int64_t s = raw.s, sa = raw.sa, eb = raw.eb;
-        struct {
-            float X[4 * (W - 1)], Dy[3 * (W - 1)], ia[W - 1], ib[W - 1], i0[W - 1], fa[W - 1],
-                fb[W - 1];
-        } in;
-        tcp_widen(raw.X, in.X);
-        tcp_widen(raw.Dy, in.Dy);
-        tcp_widen(raw.ia, in.ia);
-        tcp_widen(raw.ib, in.ib);
-        tcp_widen(raw.i0, in.i0);
-        tcp_widen(raw.fa, in.fa);
-        tcp_widen(raw.fb, in.fb);
-
-        if (has_a) {
-            // A's last W-1 tokens u = s-(W-1)+i (those at or after sa)
-            float ga[W - 1];
-#pragma unroll
-            for (int i = 0; i < W - 1; ++i) {
-                const int64_t u = s - (W - 1) + i;
+        for (int l = 0; l < W - 1; ++l) {
+            if (s + l < e) {
                 float z = bias[0];
 #pragma unroll
-                for (int k = 0; k < W; ++k) {
-                    const int64_t p = u - (W - 1) + k;
-                    z = fmaf(w[k][0], p >= sa ? in.X[i + k] : pick(in.ia, p - sa + W - 1), z);
-                }
-                ga[i] = u >= sa ? in.Dy[i] * act_slope<SILU>(z) : 0.0f;
-            }
-#pragma unroll
-            for (int i = 0; i < W - 1; ++i) {
-                const int64_t u = s - (W - 1) + i;
-                if (u >= sa && u >= t0 && u < t1) {
-                    float acc = 0.0f;
-#pragma unroll
-                    for (int m = W - 2; m >= 0; --m)
-                        if (i + m < W - 1) acc = fmaf(w[W - 1 - m][0], ga[i + m], acc);
-                    dxr[u] = to_bf16_bits(acc + in.fa[i]);
-                }
-            }
-        }
-        if (has_b) {
-            // B's first 2(W-1) tokens v = s+i, with B's taps (zero from eb on)
-            float gb[2 * (W - 1)];
-#pragma unroll
-            for (int i = 0; i < 2 * (W - 1); ++i) {
-                float z = bias[0];
-#pragma unroll
-                for (int k = 0; k < W; ++k)
-                    z = fmaf(w[k][0], i + k >= W - 1 ? in.X[i + k + W - 1] : in.ib[i + k], z);
-                gb[i] = s + i < eb ? in.Dy[i + W - 1] * act_slope<SILU>(z) : 0.0f;
-            }
-#pragma unroll
-            for (int i = 0; i < W - 1; ++i) {
-                const int64_t v = s + i;
-                if (v < eb && v >= t0 && v < t1) {
-                    float acc = w[0][0] * gb[i + W - 1];
-#pragma unroll
-                    for (int m = W - 2; m >= 0; --m) acc = fmaf(w[W - 1 - m][0], gb[i + m], acc);
-                    dxr[v] = to_bf16_bits(acc + pick(in.fb, v - (eb - (W - 1))));
-                    if (has_a) {
-                        // take out the dense pass's dW/dB terms of v (its taps
-                        // were the row's tokens, or sequence 0's state before
-                        // the row) and put in B's
-                        float zd = bias[0], xd[W];
-#pragma unroll
-                        for (int k = 0; k < W; ++k) {
-                            const int64_t p = v - (W - 1) + k;
-                            xd[k] = p >= 0 ? in.X[i + k + W - 1] : pick(in.i0, p + W - 1);
-                            zd = fmaf(w[k][0], xd[k], zd);
-                        }
-                        const float gd = in.Dy[i + W - 1] * act_slope<SILU>(zd);
-#pragma unroll
-                        for (int k = 0; k < W; ++k) {
-                            const float xb = i + k >= W - 1 ? in.X[i + k + W - 1] : in.ib[i + k];
-                            dwacc[k] = fmaf(gb[i], xb, dwacc[k]);
-                            dwacc[k] = fmaf(-gd, xd[k], dwacc[k]);
-                        }
-                        if constexpr (BIAS) dbacc += gb[i] - gd;
-                    }
-                }
-            }
-            if (A.dinit.ptr && s >= t0 && s < t1) {
-                uint16_t *di = const_cast<uint16_t *>(static_cast<const uint16_t *>(A.dinit.ptr)) +
-                               j * A.dinit.s0 + d * A.dinit.s1;
-#pragma unroll
-                for (int m = 0; m < W - 1; ++m) {
-                    // dx_ext at s-(W-1)+m: the g's at s+m-k for k <= m, plus
-                    // a final-state slot that lands there
-                    float acc = w[0][0] * gb[m];
-#pragma unroll
-                    for (int k = W - 2; k >= 0; --k)
-                        if (m - (W - 1) + k >= 0) acc = fmaf(w[W - 1 - k][0], gb[m - (W - 1) + k], acc);
-                    di[m * A.dinit.s2] = to_bf16_bits(acc + pick(in.fb, m - (eb - s)));
-                }
+                for (int k = 0; k < W; ++k) z = fmaf(w[k][0], xe[l + k], z);
+                yr[s + l] = to_bf16_bits(act<SILU>(z));
             }
         }
     }
-
-    // Boundaries s_j in [t0-(W-2), t1+W-2]: from the sequence holding
-    // t0-(W-2) to the one holding t1+W-2 or, when that is past the row and a
-    // final-state gradient is given, to the row's end (wave-uniform).
-    __device__ __forceinline__ void locate() {
-        const BwdArgs &A = *a;
-        const int64_t n = A.n_seq;
-        if (n < kWaveSize) {
-            // one offset per lane, looked at when the repair runs
-            few = true;
-            cl = A.cu[min(static_cast<int64_t>(threadIdx.x % kWaveSize), n)];
-            return;
-        }
-        const int32_t *cu = A.cu;
-        const int64_t j0 = find_row(cu, n, max(it->t0 - (W - 2), int64_t{0}));
-        const int64_t hi = it->t1 + (W - 2);
-        const int64_t j1 = hi >= A.T ? (A.dfin.ptr ? n : n - 1) : find_row(cu, n, hi);
-        settle(j0, j1, cu[j0]);
-    }
-
-    __device__ __forceinline__ void settle(int64_t j0, int64_t j1, int64_t c0) {
-        if (j1 > j0 || (j0 > 0 && c0 >= it->t0 - (W - 2)) ||
-            (j0 == 0 && it->t0 == 0 && a->dinit.ptr)) {
-            ja = j0;
-            jb = j1;
+    if (a.fin.ptr) {
+        // the sequence's last W-1 extended tokens, bit for bit
+        const uint16_t *ir = a.init.ptr ? static_cast<const uint16_t *>(a.init.ptr) +
+                                              j * a.init.s0 + d * a.init.s1
+                                        : nullptr;
+        uint16_t *fr = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.fin.ptr)) +
+                       j * a.fin.s0 + d * a.fin.s1;
+#pragma unroll
+        for (int m = 0; m < W - 1; ++m) {
+            const int64_t p = e - (W - 1) + m;
+            uint16_t bits = 0;
+            if (p >= s) bits = xr[p];
+            else if (ir) bits = ir[(p - s + W - 1) * a.init.s2];
+            fr[m * a.fin.s2] = bits;
         }
     }
-
-    __device__ __forceinline__ void operator()(const float (&w)[W][1], const float (&bias)[1],
-                                               float (&dwacc)[W], float &dbacc) {
-        if (few) {
-            const BwdArgs &A = *a;
-            const int64_t n = A.n_seq;
-            const int64_t j0 = __popcll(__ballot(cl <= max(it->t0 - (W - 2), int64_t{0}))) - 1;
-            const int64_t hi = it->t1 + (W - 2);
-            const int64_t j1 =
-                hi >= A.T ? (A.dfin.ptr ? n : n - 1) : __popcll(__ballot(cl <= hi)) - 1;
-            settle(j0, j1, __builtin_amdgcn_readlane(cl, static_cast<int>(j0)));
-        }
-        if (jb < ja) return;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // after the dense pass's stores
-        const int64_t n = a->n_seq;
-        for (int64_t j0 = ja; j0 <= jb; j0 += kWaveSize) {
-            const int64_t j = j0 + threadIdx.x % kWaveSize;
-            const int64_t ia = j > 0 ? j - 1 : j, ib = j < n ? j + 1 : j;
-            // few sequences: the offsets come from the lanes holding them, read
-            // while every lane is active (a lane moved from an inactive one
-            // reads zero)
-            int32_t fs = 0, fa = 0, fb = 0;
-            if (few) {
-                fs = __shfl(cl, static_cast<int>(j));
-                fa = __shfl(cl, static_cast<int>(ia));
-                fb = __shfl(cl, static_cast<int>(ib));
-            }
-            if (j > jb) continue;
-            const BwdTcpIn<W> in = few ? load(j, fs, fa, fb) : load(j, a->cu[j], a->cu[ia], a->cu[ib]);
-            boundary(j, in, w, bias, dwacc, dbacc);
-        }
-    }
-};
+}
 
 template <int W, bool SILU, int FK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CCV_TC_BWD_WAVES)))
@@ -2345,9 +2044,154 @@ void k_bwd_tcp(BwdArgs a) {
     BwdArgs da = a;
     da.dfin.ptr = nullptr;  // the state gradients come from the repair
     da.dinit.ptr = nullptr;
-    BwdTcpRepair<W, SILU, FK> fix{&a, &it};
-    if (a.nt_load) bwd_tc_chunk<W, SILU, FK, true>(da, it, fix);
-    else bwd_tc_chunk<W, SILU, FK, false>(da, it, fix);
+    if (a.nt_load) bwd_tc_chunk<W, SILU, FK, true>(da, it);
+    else bwd_tc_chunk<W, SILU, FK, false>(da, it);
+}
+
+// Backward repair of boundary j (s = cu[j]) in one lane, adding its dW/dB
+// terms to the lane's sums.
+template <int W, bool SILU, int FK>
+__device__ __forceinline__ void bwd_tcp_boundary(const BwdArgs &a, int64_t d, int64_t j,
+                                                 const float (&w)[W][1], const float (&bias)[1],
+                                                 float (&dwacc)[W], float &dbacc) {
+    constexpr bool BIAS = fk_bias(FK);
+    const int64_t n = a.n_seq, T = a.T;
+    const uint16_t *xr = static_cast<const uint16_t *>(a.x.ptr) + d * a.x.s1;
+    const uint16_t *dyr = static_cast<const uint16_t *>(a.dy.ptr) + d * a.dy.s1;
+    uint16_t *dxr = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.dx.ptr)) + d * a.dx.s1;
+    const bool has_a = j > 0, has_b = j < n;
+    const int64_t s = a.cu[j], sa = a.cu[has_a ? j - 1 : j], eb = a.cu[has_b ? j + 1 : j];
+    // x at s-2(W-1) .. s+2(W-1)-1, dy at s-(W-1) .. s+2(W-1)-1, the
+    // initial-state slots of A, B and sequence 0, the final-state gradients
+    // of A and B (zeros for what the call does not have)
+    float X[4 * (W - 1)], Dy[3 * (W - 1)];
+#pragma unroll
+    for (int i = 0; i < 4 * (W - 1); ++i) X[i] = tcp_tok(xr, s - 2 * (W - 1) + i, T);
+#pragma unroll
+    for (int i = 0; i < 3 * (W - 1); ++i) Dy[i] = tcp_tok(dyr, s - (W - 1) + i, T);
+    float ia[W - 1], ib[W - 1], i0[W - 1], fa[W - 1], fb[W - 1];
+    tcp_slots<W>(a.init, has_a ? j - 1 : 0, d, ia);
+    tcp_slots<W>(a.init, has_b ? j : 0, d, ib);
+    tcp_slots<W>(a.init, 0, d, i0);
+    tcp_slots<W>(a.dfin, has_a ? j - 1 : 0, d, fa);
+    tcp_slots<W>(a.dfin, has_b ? j : 0, d, fb);
+
+    if (has_a) {
+        // A's last W-1 tokens u = s-(W-1)+i (those at or after sa)
+        float ga[W - 1];
+#pragma unroll
+        for (int i = 0; i < W - 1; ++i) {
+            const int64_t u = s - (W - 1) + i;
+            float z = bias[0];
+#pragma unroll
+            for (int k = 0; k < W; ++k) {
+                const int64_t p = u - (W - 1) + k;
+                z = fmaf(w[k][0], p >= sa ? X[i + k] : pick(ia, p - sa + W - 1), z);
+            }
+            ga[i] = u >= sa ? Dy[i] * act_slope<SILU>(z) : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < W - 1; ++i) {
+            const int64_t u = s - (W - 1) + i;
+            if (u >= sa) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int m = W - 2; m >= 0; --m)
+                    if (i + m < W - 1) acc = fmaf(w[W - 1 - m][0], ga[i + m], acc);
+                dxr[u] = to_bf16_bits(acc + fa[i]);
+            }
+        }
+    }
+    if (has_b) {
+        // B's first 2(W-1) tokens v = s+i, with B's taps (zero from eb on)
+        float gb[2 * (W - 1)];
+#pragma unroll
+        for (int i = 0; i < 2 * (W - 1); ++i) {
+            float z = bias[0];
+#pragma unroll
+            for (int k = 0; k < W; ++k)
+                z = fmaf(w[k][0], i + k >= W - 1 ? X[i + k + W - 1] : ib[i + k], z);
+            gb[i] = s + i < eb ? Dy[i + W - 1] * act_slope<SILU>(z) : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < W - 1; ++i) {
+            const int64_t v = s + i;
+            if (v < eb) {
+                float acc = w[0][0] * gb[i + W - 1];
+#pragma unroll
+                for (int m = W - 2; m >= 0; --m) acc = fmaf(w[W - 1 - m][0], gb[i + m], acc);
+                dxr[v] = to_bf16_bits(acc + pick(fb, v - (eb - (W - 1))));
+                if (has_a) {
+                    // take out the dense pass's dW/dB terms of v (its taps were
+                    // the row's tokens, or sequence 0's state before the row)
+                    // and put in B's
+                    float zd = bias[0], xd[W];
+#pragma unroll
+                    for (int k = 0; k < W; ++k) {
+                        const int64_t p = v - (W - 1) + k;
+                        xd[k] = p >= 0 ? X[i + k + W - 1] : pick(i0, p + W - 1);
+                        zd = fmaf(w[k][0], xd[k], zd);
+                    }
+                    const float gd = Dy[i + W - 1] * act_slope<SILU>(zd);
+#pragma unroll
+                    for (int k = 0; k < W; ++k) {
+                        const float xb = i + k >= W - 1 ? X[i + k + W - 1] : ib[i + k];
+                        dwacc[k] = fmaf(gb[i], xb, dwacc[k]);
+                        dwacc[k] = fmaf(-gd, xd[k], dwacc[k]);
+                    }
+                    if constexpr (BIAS) dbacc += gb[i] - gd;
+                }
+            }
+        }
+        if (a.dinit.ptr) {
+            uint16_t *di = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.dinit.ptr)) +
+                           j * a.dinit.s0 + d * a.dinit.s1;
+#pragma unroll
+            for (int m = 0; m < W - 1; ++m) {
+                // dx_ext at s-(W-1)+m: the g's at s+m-k for k <= m, plus a
+                // final-state slot that lands there
+                float acc = w[0][0] * gb[m];
+#pragma unroll
+                for (int k = W - 2; k >= 0; --k)
+                    if (m - (W - 1) + k >= 0) acc = fmaf(w[W - 1 - k][0], gb[m - (W - 1) + k], acc);
+                di[m * a.dinit.s2] = to_bf16_bits(acc + pick(fb, m - (eb - s)));
+            }
+        }
+    }
+}
+
+// Backward repair: lane j is boundary j in [0, N].  Boundary 0 needs work
+// only for dinit, boundary N only for a final-state gradient.
+template <int W, bool SILU, int FK>
+__global__ __launch_bounds__(256) void k_bwd_tcp_fix(BwdArgs a) {
+    constexpr bool BIAS = fk_bias(FK);
+    TcpItem it;
+    if (!tcp_item(a.D, (a.n_seq + kWaveSize) / kWaveSize, it)) return;
+    if (tcp_flag_set(a.err)) return;
+    const int64_t j = it.j, d = it.d, n = a.n_seq;
+    float w[W][1], bias[1];
+    load_filter<W, 1, FK>(a.w, a.w_sd, a.w_sk, a.bias, a.b_s, d, w, bias);
+    float dwacc[W], dbacc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < W; ++k) dwacc[k] = 0.0f;
+    if (j <= n && (j > 0 || a.dinit.ptr) && (j < n || a.dfin.ptr))
+        bwd_tcp_boundary<W, SILU, FK>(a, d, j, w, bias, dwacc, dbacc);
+    // the wave's dW/dB terms, like a chunk's
+#pragma unroll
+    for (int k = 0; k < W; ++k) dwacc[k] = wave_sum(dwacc[k]);
+    if constexpr (BIAS) dbacc = wave_sum(dbacc);
+    if (threadIdx.x % kWaveSize == 0) {
+        if (a.partial) {
+            float *pr = a.partial + ((a.n_chunk + it.g) * a.D + d) * a.part_stride;
+#pragma unroll
+            for (int k = 0; k < W; ++k) pr[k] = dwacc[k];
+            if (a.part_stride > W) pr[W] = dbacc;
+        } else {
+#pragma unroll
+            for (int k = 0; k < W; ++k) atomicAdd(a.dw + d * W + k, dwacc[k]);
+            if constexpr (BIAS) atomicAdd(a.db + d, dbacc);
+        }
+    }
 }
 
 // ===========================================================================

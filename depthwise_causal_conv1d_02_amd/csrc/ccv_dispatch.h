@@ -50,14 +50,24 @@ hipError_t fwd_vec(const FwdArgs &a, int silu, int rows, int fk, hipStream_t s, 
 
 // The software-pipelined forward is built for 8-channel lanes of dense and
 // packed rows only.
-// Time-lane kernels: dense rows, packed rows (the dense code plus a repair at
-// the sequence boundaries) and seq_idx rows (per-token ids).
+// Time-lane kernels: dense rows, packed rows (the dense code, then a repair
+// at the sequence boundaries) and seq_idx rows (per-token ids).
+// Blocks of the packed rows' repair launch: a wave per channel and group of
+// 64 of the `items` boundaries (or sequences).
+inline int64_t tcp_blocks(int64_t D, int64_t items) {
+    return (D * ((items + kWaveSize - 1) / kWaveSize) + kWavesPerBlock - 1) / kWavesPerBlock;
+}
+
 template <int W>
 hipError_t fwd_tc(const FwdArgs &a, int silu, int fk, int rows, hipStream_t s) {
 #define CCV_TC(S, F)                                                                    \
     if (!!silu == S && fk == F) {                                                       \
         if (rows == kRowsDense) return launch(k_fwd_tc<W, S, F>, a.n_block, a, s);       \
-        if (rows == kRowsPacked) return launch(k_fwd_tcp<W, S, F>, a.n_block, a, s);     \
+        if (rows == kRowsPacked) {                                                      \
+            const hipError_t e = launch(k_fwd_tcp<W, S, F>, a.n_block, a, s);           \
+            if (e != hipSuccess) return e;                                              \
+            return launch(k_fwd_tcp_fix<W, S, F>, tcp_blocks(a.D, a.n_seq), a, s);       \
+        }                                                                               \
         if (rows == kRowsSeq) return launch(k_fwd_tcs<W, S, F>, a.n_block, a, s);        \
     }
     CCV_TC(true, kBf16) CCV_TC(true, kBf16Bias) CCV_TC(true, kF32) CCV_TC(true, kF32Bias)
@@ -71,7 +81,11 @@ hipError_t bwd_tc(const BwdArgs &a, int silu, int fk, int rows, hipStream_t s) {
 #define CCV_TC(S, F)                                                                    \
     if (!!silu == S && fk == F) {                                                       \
         if (rows == kRowsDense) return launch(k_bwd_tc<W, S, F>, a.n_block, a, s);       \
-        if (rows == kRowsPacked) return launch(k_bwd_tcp<W, S, F>, a.n_block, a, s);     \
+        if (rows == kRowsPacked) {                                                      \
+            const hipError_t e = launch(k_bwd_tcp<W, S, F>, a.n_block, a, s);           \
+            if (e != hipSuccess) return e;                                              \
+            return launch(k_bwd_tcp_fix<W, S, F>, tcp_blocks(a.D, a.n_seq + 1), a, s);   \
+        }                                                                               \
         if (rows == kRowsSeq) return launch(k_bwd_tcs<W, S, F>, a.n_block, a, s);        \
     }
     CCV_TC(true, kBf16) CCV_TC(true, kBf16Bias) CCV_TC(true, kF32) CCV_TC(true, kF32Bias)
