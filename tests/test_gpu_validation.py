@@ -1,8 +1,10 @@
 """Device-side validation of packed offsets, as the packed forward and
 backward run it (cuDNN FE "Causal Conv1d", the paragraph on device-side
 validation): every malformed-metadata condition alone and in combination,
-with the offsets staged and checked inside every block (N+1 <= 4096) and with
-the separate validation kernel ahead of the blocks (N+1 > 4096).
+with the offsets staged and checked inside every block (N+1 <= 4096), with
+the separate validation kernel ahead of the blocks (N+1 > 4096), and on
+[B,D,T]-contiguous rows, whose time-lane kernels (the chunks and the
+boundary repair) always follow the validation kernel.
 
 For each call, on a freshly cleared flag word:
   * the word equals the oracle's flag bits, bit for bit;
@@ -36,8 +38,8 @@ def _set(cu, i, v):
     return cu
 
 
-def _lds_cases():
-    good = _cu([5, 7, 9, 4, 6])                            # [0,5,12,21,25,31]
+def _lds_cases(lengths=(5, 7, 9, 4, 6)):
+    good = _cu(list(lengths))                              # [0,5,12,21,25,31]
     T = good[-1]
     swap = list(good)
     swap[2], swap[3] = swap[3], swap[2]
@@ -74,8 +76,23 @@ def _global_cases():
     ]
 
 
-def _inputs(T, seed, bias):
-    inp = synth.random_inputs(seed, 1, D, T, layout="cl", bias=bias, init=False)
+# time lanes: [B,D,T]-contiguous rows of T = 32, so every row starts on a
+# 16-byte boundary
+TIME_LENGTHS = (5, 7, 9, 4, 7)
+
+
+def _cases(path):
+    if path == "global":
+        return _global_cases()
+    return _lds_cases(TIME_LENGTHS if path == "time" else (5, 7, 9, 4, 6))
+
+
+def _layout(path):
+    return "tc" if path == "time" else "cl"
+
+
+def _inputs(T, seed, bias, layout):
+    inp = synth.random_inputs(seed, 1, D, T, layout=layout, bias=bias, init=False)
     return {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
 
 
@@ -89,18 +106,18 @@ class _Call:
     dweight/dbias, a garbage workspace) and returns every tensor the call
     may write; run(cu, flag) launches it on those buffers."""
 
-    def __init__(self, name, T, R, g, init, dfin, kind):
+    def __init__(self, name, T, R, g, init, dfin, kind, layout):
         self.name, self.T, self.R, self.g, self.init, self.dfin = name, T, R, g, init, dfin
-        self.kind = kind
+        self.kind, self.layout = kind, layout
 
     def alloc(self):
         T, R = self.T, self.R
         bias = self.g["bias"] is not None
         if self.kind == "fwd":
-            self.y = guarded_act(1, D, T, "cl", DEV)
+            self.y = guarded_act(1, D, T, self.layout, DEV)
             self.fin = guarded_flat((R, D, 3), DEV)
             return [self.y.storage, self.fin.storage]
-        self.dx = guarded_act(1, D, T, "cl", DEV)
+        self.dx = guarded_act(1, D, T, self.layout, DEV)
         self.dinit = guarded_flat((R, D, 3), DEV)
         self.dw = torch.full((D, 4), 1.5, dtype=F32, device=DEV)
         self.db = torch.full((D,), -2.25, dtype=F32, device=DEV) if bias else None
@@ -122,18 +139,17 @@ class _Call:
                 options=opts)
 
 
-def _calls(T, cu_len):
+def _calls(T, cu_len, layout):
     """fwd, atomic bwd, deterministic bwd (bias-free), and deterministic bwd
     with a bias whose dbias goes through the partials too."""
     R = cu_len - 1
-    gb = _inputs(T, 900 + T, True)
-    gn = _inputs(T, 901 + T, False)
+    gb = _inputs(T, 900 + T, True, layout)
+    gn = _inputs(T, 901 + T, False, layout)
     init = synth.state_tensor(torch.Generator().manual_seed(T), R, D, 4).to(DEV)
     dfin = synth.state_tensor(torch.Generator().manual_seed(T + 1), R, D, 4).to(DEV)
-    return [_Call("fwd", T, R, gb, init, dfin, "fwd"),
-            _Call("bwd_atomic", T, R, gb, init, dfin, "bwd_atomic"),
-            _Call("bwd_deterministic", T, R, gn, init, dfin, "bwd_deterministic"),
-            _Call("bwd_deterministic_dbias", T, R, gb, init, dfin, "bwd_deterministic_dbias")]
+    kinds = ("fwd", "bwd_atomic", "bwd_deterministic", "bwd_deterministic_dbias")
+    return [_Call(k, T, R, gn if k == "bwd_deterministic" else gb, init, dfin, k, layout)
+            for k in kinds]
 
 
 def _check_call(label, cu, T, call, flag_start=0, want=None):
@@ -153,10 +169,10 @@ def _check_call(label, cu, T, call, flag_start=0, want=None):
         assert torch.equal(_bits(b), s), "%s: buffer %d was written" % (label, i)
 
 
-@pytest.mark.parametrize("path", ["lds", "global"])
+@pytest.mark.parametrize("path", ["lds", "global", "time"])
 def test_malformed_offsets_flag_is_the_oracles_and_nothing_is_written(path):
-    T, cases = _lds_cases() if path == "lds" else _global_cases()
-    calls = _calls(T, len(cases[0][1]))
+    T, cases = _cases(path)
+    calls = _calls(T, len(cases[0][1]), _layout(path))
     for label, cu in cases:
         for call in calls:
             print("validation case", path, label, call.name, flush=True)
@@ -169,29 +185,30 @@ def test_malformed_offsets_flag_is_the_oracles_and_nothing_is_written(path):
 
 
 def _good(path):
-    return _cu([5, 7, 9, 4, 6] if path == "lds" else [3] * 5000 + [5, 7])
+    return _cu({"lds": [5, 7, 9, 4, 6], "global": [3] * 5000 + [5, 7],
+                "time": list(TIME_LENGTHS)}[path])
 
 
-@pytest.mark.parametrize("path", ["lds", "global"])
+@pytest.mark.parametrize("path", ["lds", "global", "time"])
 def test_sticky_flag_blocks_every_call_and_keeps_its_bits(path):
     """A word already non-zero (here a bit no validation produces) stops
     well-formed calls too and comes back unchanged."""
     good = _good(path)
     T = good[-1]
     assert oracle.validate_cu_seqlens(good, T) == 0
-    for call in _calls(T, len(good)):
+    for call in _calls(T, len(good), _layout(path)):
         print("sticky case", path, call.name, flush=True)
         _check_call("sticky/%s/%s" % (path, call.name), good, T, call, flag_start=0x40,
                     want=0x40)
 
 
-@pytest.mark.parametrize("path", ["lds", "global"])
+@pytest.mark.parametrize("path", ["lds", "global", "time"])
 def test_after_clearing_the_flag_packed_results_match_the_oracle(path):
     good = _good(path)
     T = good[-1]
     cu_cpu = torch.tensor(good, dtype=torch.int32)
-    inp = synth.random_inputs(950 + T, 1, D, T, layout="cl", bias=False, init=True, dfinal=True,
-                              cu_seqlens=cu_cpu)
+    inp = synth.random_inputs(950 + T, 1, D, T, layout=_layout(path), bias=False, init=True,
+                              dfinal=True, cu_seqlens=cu_cpu)
     g = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
     flag = torch.zeros(1, dtype=torch.int32, device=DEV)
     # a malformed call first sets the word ...

@@ -22,11 +22,11 @@ def _dev(inp):
     return {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
 
 
-def _pair(seed, B, D, T, bias, det, cu=None, init=False):
+def _pair(seed, B, D, T, bias, det, cu=None, init=False, layout="cl"):
     """ccv_bwd (workspace form) and ccv_bwd_noalloc on the same inputs."""
-    print("no-alloc case", seed, B, D, T, bias, det, None if cu is None else len(cu),
+    print("no-alloc case", seed, B, D, T, bias, det, None if cu is None else len(cu), layout,
           flush=True)
-    inp = synth.random_inputs(seed, B, D, T, layout="cl", bias=bias, init=init, dfinal=init,
+    inp = synth.random_inputs(seed, B, D, T, layout=layout, bias=bias, init=init, dfinal=init,
                               cu_seqlens=cu)
     g = _dev(inp)
     opts = DETDB if (det and bias) else 0
@@ -60,6 +60,9 @@ def test_noalloc_deterministic_matches_the_workspace_form_over_shrinking_calls()
         dict(seed=2001, B=8, D=8192, T=2048, bias=True),
         dict(seed=2002, B=2, D=1536, T=777, bias=False),
         dict(seed=2003, B=1, D=512, T=300, bias=True),
+        # packed rows on time lanes ([B,D,T] rows of 200 tokens): the boundary
+        # repair's partial rows follow the chunks'
+        dict(seed=2006, B=1, D=384, T=0, bias=True, lengths=[100, 3, 1, 60, 36], layout="tc"),
         dict(seed=2004, B=1, D=320, T=0, bias=False, lengths=[40, 1, 2, 300, 90]),
         dict(seed=2005, B=1, D=64, T=20, bias=False),
     ]
@@ -70,7 +73,7 @@ def test_noalloc_deterministic_matches_the_workspace_form_over_shrinking_calls()
             cu = synth.cu_from_lengths(c["lengths"])
             T = int(cu[-1])
         inp, ref, got = _pair(c["seed"], c["B"], c["D"], T, c["bias"], True, cu=cu,
-                              init=cu is not None)
+                              init=cu is not None, layout=c.get("layout", "cl"))
         for name, a, b in zip(("dx", "dweight", "dbias", "dinit"), ref, got):
             _same_bits(name, a, b)
         if c["D"] <= 1536:
