@@ -55,6 +55,7 @@ OP_KERNEL = {"fwd": "k_fwd_chan", "bwd": "k_bwd_chan", "update": "k_update"}
 OP_KERNEL_TIME = {"fwd": "k_fwd_tc", "bwd": "k_bwd_tc", "update": "k_update"}
 OP_KERNEL_TIME_PACKED = {"fwd": "k_fwd_tcp", "bwd": "k_bwd_tcp", "update": "k_update"}
 OP_KERNEL_TIME_SEQ = {"fwd": "k_fwd_tcs", "bwd": "k_bwd_tcs", "update": "k_update"}
+UPDATE_KERNELS = ("k_update_staged", "k_update_vec", "k_update_tokens", "k_update_any")
 
 
 def op_kernels(workload):
@@ -551,13 +552,24 @@ def _kernel_rows(csv_path):
     return rows
 
 
-def _counter_per_launch(pmc_dir, counter, name_part):
-    """Mean of a counter over the dispatches whose kernel name contains name_part."""
+def _is_kernel(short, kernel):
+    """Whether a kernel-trace name is `kernel` (any namespace, template
+    arguments or parameter list)."""
+    import re
+    short = short.replace("(anonymous namespace)::", "")
+    base = re.split(r"[<(]", short, maxsplit=1)[0].split("::")[-1].split(" ")[-1]
+    return base == kernel
+
+
+def _counter_per_launch(pmc_dir, counter, kernel=None, name_part=None):
+    """Mean of a counter over the dispatches of `kernel` (or, for library
+    kernels, of the names containing name_part)."""
     import glob
     vals = []
     for f in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
         for r in _kernel_rows(f):
-            if r["Counter_Name"] == counter and name_part in r["_short"]:
+            hit = _is_kernel(r["_short"], kernel) if kernel else name_part in r["_short"]
+            if r["Counter_Name"] == counter and hit:
                 vals.append(float(r["Counter_Value"]))
     return sum(vals) / len(vals) if vals else None, len(vals)
 
@@ -584,28 +596,32 @@ def summarize(args):
     stats = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
     rows = _kernel_rows(stats)
     copy_bytes = args.copy_calibration << 20
-    c_fetch, _ = _counter_per_launch(cfetch_dir, "FETCH_SIZE", "copyBuffer")
-    c_write, _ = _counter_per_launch(cwrite_dir, "WRITE_SIZE", "copyBuffer")
+    c_fetch, _ = _counter_per_launch(cfetch_dir, "FETCH_SIZE", name_part="copyBuffer")
+    c_write, _ = _counter_per_launch(cwrite_dir, "WRITE_SIZE", name_part="copyBuffer")
     f_scale = copy_bytes / (c_fetch * 1024.0)   # counter KiB -> bytes read
     w_scale = copy_bytes / (c_write * 1024.0)
     h = source_hash()
     for op, kernel in op_kernels(args.workload).items():
         if op not in wl_bytes:
             continue
-        mine = [r for r in rows if r["_short"].startswith(kernel)]
-        if not mine:
+        # the update op is whichever update kernel the workload's shape takes
+        family = (UPDATE_KERNELS if kernel == "k_update" else (kernel,))
+        kernels = [k for k in family if any(_is_kernel(r["_short"], k) for r in rows)]
+        if not kernels:
             continue
-        # the deterministic backward is two kernels: the walk and the
-        # fixed-order reduction of its partials; the op's time and traffic
-        # are their sums per launch
-        kernels = [kernel]
-        if op == "bwd" and any("k_dw_reduce" in r["_short"] for r in rows):
+        # An op of several launches counts all of them (time and traffic are
+        # their sums per launch): the deterministic backward's fixed-order
+        # reduction of its partials; on packed time lanes, the validation
+        # kernel before the chunks and the boundary repair after them.
+        if kernel in ("k_fwd_tcp", "k_bwd_tcp"):
+            kernels = ["k_validate", kernel, kernel + "_fix"]
+        if op == "bwd" and any(_is_kernel(r["_short"], "k_dw_reduce") for r in rows):
             kernels.append("k_dw_reduce")
         fetch = write = 0.0
         nf = nw = 0
         for k in kernels:
-            f_, n_ = _counter_per_launch(fetch_dir, "FETCH_SIZE", k)
-            w_, m_ = _counter_per_launch(write_dir, "WRITE_SIZE", k)
+            f_, n_ = _counter_per_launch(fetch_dir, "FETCH_SIZE", kernel=k)
+            w_, m_ = _counter_per_launch(write_dir, "WRITE_SIZE", kernel=k)
             fetch += f_
             write += w_
             nf, nw = nf + n_, nw + m_
@@ -623,7 +639,7 @@ def summarize(args):
                 float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
         avg_us = 0.0
         for k in kernels:
-            ks = [r for r in rows if k in r["_short"]]
+            ks = [r for r in rows if _is_kernel(r["_short"], k)]
             avg_us += sum(float(r["AverageNs"]) * int(r["Calls"]) for r in ks) / \
                 sum(int(r["Calls"]) for r in ks) / 1e3
         lines += ["", "Counters per launch of `%s` (means over %d and %d dispatches):"
