@@ -2698,6 +2698,7 @@ hipStream_t const kQueryStream = reinterpret_cast<hipStream_t>(~uintptr_t(0));
 template <typename K, typename A>
 hipError_t launch(K kernel, int64_t blocks, const A &args, hipStream_t s, unsigned lds = 0) {
     if (blocks <= 0) return hipSuccess;
+    if (blocks > int64_t(UINT32_MAX)) return hipErrorInvalidConfiguration;  // beyond one grid
     hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), lds, s, args);
     return hipGetLastError();
 }
