@@ -421,6 +421,17 @@ Geometry time_geometry(const Problem &p, int tiles) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? CCV_OK : CCV_ERR_HIP; }
 
+// Where packed offsets are validated: inside every block of the launch (in
+// LDS, channel lanes, N+1 <= 4096), by every wave (time lanes, one offset per
+// lane, N+1 <= 64), or by the validation launch before it.  The first two
+// need the launch to run at least one wave.
+template <typename A>
+void set_validation(A &a, const Problem &p, bool time_lanes) {
+    const bool waves = p.B * p.D * p.T > 0;
+    a.cu_in_lds = p.packed && !time_lanes && waves && p.N + 1 <= ccv::kLdsCuMax;
+    a.cu_in_wave = p.packed && time_lanes && waves && p.N + 1 <= ccv::kWaveSize;
+}
+
 // The time lanes decode their wave index in 32 bits when all B*D*n_chunk
 // wave indices fit.
 template <typename A>
@@ -530,11 +541,10 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     a.n_tblk_t = gs.n_tblk_t;
     a.n_block_m = gs.n_block_m;
     if (time_lanes) set_tc_div(a);
-    // packed rows on time lanes always take the validation launch first
-    a.cu_in_lds = p.packed && !time_lanes && p.N + 1 <= ccv::kLdsCuMax;
+    set_validation(a, p, time_lanes);
     a.nt_load = p.B * p.D * p.T * 2 >=
                 (p.seq ? CCV_NT_LOAD_MIN_BYTES_SEQ : CCV_NT_LOAD_MIN_BYTES);
-    if (p.packed && !a.cu_in_lds) {
+    if (p.packed && !a.cu_in_lds && !a.cu_in_wave) {
         rc = hip_status(ccv::launch_validate(a.cu, p.N, p.T, err_flag, 0, stream));
         if (rc != CCV_OK) return rc;
     }
@@ -686,10 +696,9 @@ int bwd_call(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bi
     a.n_tblk_t = g.n_tblk_t;
     a.n_block_m = g.n_block_m;
     if (time_lanes) set_tc_div(a);
-    // packed rows on time lanes always take the validation launch first
-    a.cu_in_lds = p.packed && !time_lanes && p.N + 1 <= ccv::kLdsCuMax;
+    set_validation(a, p, time_lanes);
 
-    if (p.packed && !a.cu_in_lds) {
+    if (p.packed && !a.cu_in_lds && !a.cu_in_wave) {
         rc = hip_status(ccv::launch_validate(a.cu, p.N, p.T, err_flag, 0, stream));
         if (rc != CCV_OK) return rc;
     }

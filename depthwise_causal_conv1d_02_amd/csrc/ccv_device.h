@@ -1313,8 +1313,15 @@ __device__ __forceinline__ bool tc_item(const A &a, TcItem &it) {
     return true;
 }
 
-template <int W, bool SILU, int FK, bool NTL>
-__device__ __forceinline__ void fwd_tc_chunk(const FwdArgs &a, const TcItem &it) {
+// No check: dense rows.  A packed chunk's check runs once the chunk's loads
+// are issued and says whether the chunk may write.
+struct TcNoCheck {
+    __device__ __forceinline__ bool ok() const { return true; }
+};
+
+template <int W, bool SILU, int FK, bool NTL, typename Check>
+__device__ __forceinline__ void fwd_tc_chunk(const FwdArgs &a, const TcItem &it,
+                                             const Check &check) {
     const int lane = threadIdx.x % kWaveSize;
     const uint16_t *xr = static_cast<const uint16_t *>(a.x.ptr) + it.b * a.x.s0 + it.d * a.x.s1;
     uint16_t *yr = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.y.ptr)) +
@@ -1337,6 +1344,7 @@ __device__ __forceinline__ void fwd_tc_chunk(const FwdArgs &a, const TcItem &it)
         if (t < it.t1) raw[c] = tc_load<NTL>(xr, t, it.t1);
         else raw[c].v = u32x4_t{0u, 0u, 0u, 0u};
     }
+    if (!check.ok()) return;
     float carry[W - 1];  // x_ext of the W-1 tokens before the current tile
 #pragma unroll
     for (int j = 0; j < W - 1; ++j) carry[j] = kept_f32(lh[j], lh_keep[j]);
@@ -1372,8 +1380,8 @@ template <int W, bool SILU, int FK>
 __global__ __launch_bounds__(256) void k_fwd_tc(FwdArgs a) {
     TcItem it;
     if (!tc_item(a, it)) return;
-    if (a.nt_load) fwd_tc_chunk<W, SILU, FK, true>(a, it);
-    else fwd_tc_chunk<W, SILU, FK, false>(a, it);
+    if (a.nt_load) fwd_tc_chunk<W, SILU, FK, true>(a, it, TcNoCheck{});
+    else fwd_tc_chunk<W, SILU, FK, false>(a, it, TcNoCheck{});
 }
 
 // Backward on time lanes.  Per tile: z and g = dy * act'(z) for the lane's
@@ -1383,8 +1391,9 @@ __global__ __launch_bounds__(256) void k_fwd_tc(FwdArgs a) {
 // chunk's last tile the W-1 g's past the chunk are computed directly (the
 // right halo).  dW/dB: one wave sum per chunk, then an atomic or a unique
 // partial.
-template <int W, bool SILU, int FK, bool NTL>
-__device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it) {
+template <int W, bool SILU, int FK, bool NTL, typename Check>
+__device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it,
+                                             const Check &check) {
     constexpr bool BIAS = fk_bias(FK);
     const int lane = threadIdx.x % kWaveSize;
     const uint16_t *xr = static_cast<const uint16_t *>(a.x.ptr) + it.b * a.x.s0 + it.d * a.x.s1;
@@ -1424,6 +1433,7 @@ __device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it)
     }
     float w[W][1], bias[1];
     load_filter<W, 1, FK>(a.w, a.w_sd, a.w_sk, a.bias, a.b_s, it.d, w, bias);
+    if (!check.ok()) return;
     float carry[W - 1];
 #pragma unroll
     for (int j = 0; j < W - 1; ++j) carry[j] = kept_f32(lh[j], lh_keep[j]);
@@ -1562,8 +1572,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CCV_TC_BWD_
 void k_bwd_tc(BwdArgs a) {
     TcItem it;
     if (!tc_item(a, it)) return;
-    if (a.nt_load) bwd_tc_chunk<W, SILU, FK, true>(a, it);
-    else bwd_tc_chunk<W, SILU, FK, false>(a, it);
+    if (a.nt_load) bwd_tc_chunk<W, SILU, FK, true>(a, it, TcNoCheck{});
+    else bwd_tc_chunk<W, SILU, FK, false>(a, it, TcNoCheck{});
 }
 
 // ===========================================================================
@@ -1900,14 +1910,16 @@ __global__ __launch_bounds__(256) void k_bwd_tcs(BwdArgs a) {
 // ===========================================================================
 // Time lanes for packed rows (B = 1, unit stride along T)
 //
-// Two launches after the validation launch.  The first is the dense rows'
-// chunk code unchanged: the row's initial state is sequence 0's, and it
-// writes no final state and no state gradient.  The second repairs what the
-// sequence boundaries change, with one lane per (channel, boundary): a
-// boundary changes only the W-1 tokens on either side of it.  So the tiles
-// run at the dense code's registers, occupancy and speed, and the repair's
-// stores come after the first launch's by stream order.  Both launches read
-// the flag word first and write nothing when it is set.
+// Two launches.  The first is the dense rows' chunk code unchanged: the
+// row's initial state is sequence 0's, and it writes no final state and no
+// state gradient.  The second repairs what the sequence boundaries change,
+// with one lane per (channel, boundary): a boundary changes only the W-1
+// tokens on either side of it.  So the tiles run at the dense code's
+// registers, occupancy and speed, and the repair's stores come after the
+// first launch's by stream order.  With at most 64 offsets the chunk launch
+// validates them itself (every wave, see TcpCheck); otherwise the validation
+// launch runs first.  The repair launch reads the flag word first and writes
+// nothing when it is set.
 //
 // Forward, for a sequence j = [s, e): the outputs at s .. s+W-2 take their
 // taps before s from the sequence's initial state (or zeros), and the
@@ -1974,15 +1986,53 @@ __device__ __forceinline__ bool tcp_item(int64_t D, int64_t groups, TcpItem &it)
     return true;
 }
 
+// The packed chunk launch's check.  With the validation launch before it, a
+// wave only reads the sticky flag word (and stops at once when it is set).
+// With at most 64 offsets (cu_in_wave) the wave validates them itself, one
+// per lane, loaded before the chunk's bulk loads and looked at after them:
+// the conditions of the validation kernel, by two ballots and two lane
+// reads; the launch's first wave publishes the bits into the word.  A wave
+// writes nothing when the offsets are malformed or the word was set.
+template <typename A>
+struct TcpCheck {
+    const A *a;
+    bool first;           // the launch's first wave
+    uint32_t sticky = 0;  // the flag word before the call
+    int32_t cl = 0;       // cu_in_wave: lane l holds cu[min(l, N)]
+
+    // false: stop now
+    __device__ __forceinline__ bool start() {
+        sticky = *a->err;
+        if (!a->cu_in_wave) return sticky == 0u;
+        cl = a->cu[min(static_cast<int64_t>(threadIdx.x % kWaveSize), a->n_seq)];
+        return true;
+    }
+
+    __device__ __forceinline__ bool ok() const {
+        if (!a->cu_in_wave) return true;
+        const int64_t lane = threadIdx.x % kWaveSize, n = a->n_seq;
+        const int32_t next = lane_down_id(cl, cl);  // lane l: cu[l+1]
+        uint32_t bad = 0u;
+        if (__ballot(lane < n && next < cl)) bad |= kDecreasing;
+        if (__ballot(lane < n && next == cl)) bad |= kEmpty;
+        if (__builtin_amdgcn_readlane(cl, 0) != 0) bad |= kFirstNonzero;
+        if (static_cast<int64_t>(__builtin_amdgcn_readlane(cl, static_cast<int>(n))) != a->T)
+            bad |= kLastMismatch;
+        if (bad && first && lane == 0) atomicOr(a->err, bad);
+        return (bad | sticky) == 0u;
+    }
+};
+
 template <int W, bool SILU, int FK>
 __global__ __launch_bounds__(256) void k_fwd_tcp(FwdArgs a) {
     TcItem it;
     if (!tc_item(a, it)) return;
-    if (tcp_flag_set(a.err)) return;  // malformed offsets: write nothing
+    TcpCheck<FwdArgs> check{&a, it.b == 0 && it.d == 0 && it.chunk == 0};
+    if (!check.start()) return;  // a set flag word: write nothing
     FwdArgs da = a;
     da.fin.ptr = nullptr;  // final states come from the repair
-    if (a.nt_load) fwd_tc_chunk<W, SILU, FK, true>(da, it);
-    else fwd_tc_chunk<W, SILU, FK, false>(da, it);
+    if (a.nt_load) fwd_tc_chunk<W, SILU, FK, true>(da, it, check);
+    else fwd_tc_chunk<W, SILU, FK, false>(da, it, check);
 }
 
 // Forward repair: lane j is sequence j = [s, e).
@@ -2040,12 +2090,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CCV_TC_BWD_
 void k_bwd_tcp(BwdArgs a) {
     TcItem it;
     if (!tc_item(a, it)) return;
-    if (tcp_flag_set(a.err)) return;  // malformed offsets: write nothing
+    TcpCheck<BwdArgs> check{&a, it.b == 0 && it.d == 0 && it.chunk == 0};
+    if (!check.start()) return;  // a set flag word: write nothing
     BwdArgs da = a;
     da.dfin.ptr = nullptr;  // the state gradients come from the repair
     da.dinit.ptr = nullptr;
-    if (a.nt_load) bwd_tc_chunk<W, SILU, FK, true>(da, it);
-    else bwd_tc_chunk<W, SILU, FK, false>(da, it);
+    if (a.nt_load) bwd_tc_chunk<W, SILU, FK, true>(da, it, check);
+    else bwd_tc_chunk<W, SILU, FK, false>(da, it, check);
 }
 
 // Backward repair of boundary j (s = cu[j]) in one lane, adding its dW/dB

@@ -99,6 +99,7 @@ struct FwdArgs {
     // blocks along time per (row, channel block).  Tm == T: no tail.
     int64_t Tm, Lt, n_tblk_t, n_block_m;
     int cu_in_lds;             // stage + validate cu_seqlens in LDS
+    int cu_in_wave;            // packed time lanes: every wave validates the N+1 <= 64 offsets
     int nt_load;               // stream the bulk loads with the non-temporal policy
     int pipe;                  // software-pipelined body (8-channel lanes, large inputs)
     // Time lanes: wave index -> (row, chunk) -> (b, d) in 32 bits when the
@@ -128,6 +129,7 @@ struct BwdArgs {
     int64_t B, D, T, L, n_chunk, n_tblk, n_group, n_gblk, n_block;
     int64_t Tm, Lt, n_tblk_t, n_block_m;  // main and tail chunks, as in FwdArgs
     int cu_in_lds;
+    int cu_in_wave;                       // as in FwdArgs
     int nt_load;
     int tc_div32;                         // as in FwdArgs
     Div32 tc_chunks, tc_rows;

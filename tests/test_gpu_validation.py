@@ -3,8 +3,8 @@ backward run it (cuDNN FE "Causal Conv1d", the paragraph on device-side
 validation): every malformed-metadata condition alone and in combination,
 with the offsets staged and checked inside every block (N+1 <= 4096), with
 the separate validation kernel ahead of the blocks (N+1 > 4096), and on
-[B,D,T]-contiguous rows, whose time-lane kernels (the chunks and the
-boundary repair) always follow the validation kernel.
+[B,D,T]-contiguous rows, whose time-lane chunk launch validates up to 64
+offsets in every wave and otherwise follows the validation kernel.
 
 For each call, on a freshly cleared flag word:
   * the word equals the oracle's flag bits, bit for bit;
@@ -59,8 +59,8 @@ def _lds_cases(lengths=(5, 7, 9, 4, 6)):
     ]
 
 
-def _global_cases():
-    good = _cu([3] * 5000 + [5, 7])                        # N = 5002 > 4095
+def _global_cases(lengths=None):
+    good = _cu(lengths or [3] * 5000 + [5, 7])             # N = 5002 > 4095
     T = good[-1]
     n = len(good)
     swap = list(good)
@@ -76,19 +76,24 @@ def _global_cases():
     ]
 
 
-# time lanes: [B,D,T]-contiguous rows of T = 32, so every row starts on a
-# 16-byte boundary
+# time lanes: [B,D,T]-contiguous rows whose length is a multiple of 8, so
+# that every row starts on a 16-byte boundary; 5 sequences (the chunk
+# launch validates them in every wave) and 5002 (the validation launch)
 TIME_LENGTHS = (5, 7, 9, 4, 7)
+TIME_MANY_LENGTHS = [3] * 5000 + [5, 11]
+PATHS = ["lds", "global", "time", "time_many"]
 
 
 def _cases(path):
     if path == "global":
         return _global_cases()
+    if path == "time_many":
+        return _global_cases(TIME_MANY_LENGTHS)
     return _lds_cases(TIME_LENGTHS if path == "time" else (5, 7, 9, 4, 6))
 
 
 def _layout(path):
-    return "tc" if path == "time" else "cl"
+    return "tc" if path.startswith("time") else "cl"
 
 
 def _inputs(T, seed, bias, layout):
@@ -169,7 +174,7 @@ def _check_call(label, cu, T, call, flag_start=0, want=None):
         assert torch.equal(_bits(b), s), "%s: buffer %d was written" % (label, i)
 
 
-@pytest.mark.parametrize("path", ["lds", "global", "time"])
+@pytest.mark.parametrize("path", PATHS)
 def test_malformed_offsets_flag_is_the_oracles_and_nothing_is_written(path):
     T, cases = _cases(path)
     calls = _calls(T, len(cases[0][1]), _layout(path))
@@ -186,10 +191,10 @@ def test_malformed_offsets_flag_is_the_oracles_and_nothing_is_written(path):
 
 def _good(path):
     return _cu({"lds": [5, 7, 9, 4, 6], "global": [3] * 5000 + [5, 7],
-                "time": list(TIME_LENGTHS)}[path])
+                "time": list(TIME_LENGTHS), "time_many": TIME_MANY_LENGTHS}[path])
 
 
-@pytest.mark.parametrize("path", ["lds", "global", "time"])
+@pytest.mark.parametrize("path", PATHS)
 def test_sticky_flag_blocks_every_call_and_keeps_its_bits(path):
     """A word already non-zero (here a bit no validation produces) stops
     well-formed calls too and comes back unchanged."""
@@ -202,7 +207,7 @@ def test_sticky_flag_blocks_every_call_and_keeps_its_bits(path):
                     want=0x40)
 
 
-@pytest.mark.parametrize("path", ["lds", "global", "time"])
+@pytest.mark.parametrize("path", PATHS)
 def test_after_clearing_the_flag_packed_results_match_the_oracle(path):
     good = _good(path)
     T = good[-1]
