@@ -1971,15 +1971,17 @@ __device__ __forceinline__ void tcp_slots(const Strided3 &st, int64_t j, int64_t
 // The sticky flag word (this call's validation, or an earlier call's).
 __device__ __forceinline__ bool tcp_flag_set(const uint32_t *err) { return *err != 0u; }
 
-// The repair launch's work item: channel d and the lanes' boundaries
-// j = 64 g + lane, g < groups.
+// The repair launches' work item: a wave per (row r < rows, group g of 64
+// lanes), and the lane's index j = 64 g + lane along the groups.  The
+// backward's rows are channels and its lanes boundaries; the forward's rows
+// are sequences and its lanes channels.
 struct TcpItem {
-    int64_t d, g, j;
+    int64_t d, g, j;  // row, group, lane index
 };
-__device__ __forceinline__ bool tcp_item(int64_t D, int64_t groups, TcpItem &it) {
+__device__ __forceinline__ bool tcp_item(int64_t rows, int64_t groups, TcpItem &it) {
     const int64_t wid = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock +
                         __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
-    if (wid >= D * groups) return false;
+    if (wid >= rows * groups) return false;
     it.d = wid / groups;
     it.g = wid - it.d * groups;
     it.j = it.g * kWaveSize + threadIdx.x % kWaveSize;
@@ -2035,14 +2037,16 @@ __global__ __launch_bounds__(256) void k_fwd_tcp(FwdArgs a) {
     else fwd_tc_chunk<W, SILU, FK, false>(da, it, check);
 }
 
-// Forward repair: lane j is sequence j = [s, e).
+// Forward repair: a wave per sequence j = [s, e) and group of 64 channels,
+// lane l channel 64 g + l (the state reads and final-state writes of a
+// wave are contiguous).
 template <int W, bool SILU, int FK>
 __global__ __launch_bounds__(256) void k_fwd_tcp_fix(FwdArgs a) {
     TcpItem it;
-    if (!tcp_item(a.D, (a.n_seq + kWaveSize - 1) / kWaveSize, it)) return;
+    if (!tcp_item(a.n_seq, (a.D + kWaveSize - 1) / kWaveSize, it)) return;
     if (tcp_flag_set(a.err)) return;
-    const int64_t j = it.j, d = it.d;
-    if (j >= a.n_seq) return;
+    const int64_t j = it.d, d = it.j;  // (item row, lane) = (sequence, channel)
+    if (d >= a.D) return;
     const uint16_t *xr = static_cast<const uint16_t *>(a.x.ptr) + d * a.x.s1;
     uint16_t *yr = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.y.ptr)) + d * a.y.s1;
     const int64_t s = a.cu[j], e = a.cu[j + 1];

@@ -52,10 +52,11 @@ hipError_t fwd_vec(const FwdArgs &a, int silu, int rows, int fk, hipStream_t s, 
 // packed rows only.
 // Time-lane kernels: dense rows, packed rows (the dense code, then a repair
 // at the sequence boundaries) and seq_idx rows (per-token ids).
-// Blocks of the packed rows' repair launch: a wave per channel and group of
-// 64 of the `items` boundaries (or sequences).
-inline int64_t tcp_blocks(int64_t D, int64_t items) {
-    return (D * ((items + kWaveSize - 1) / kWaveSize) + kWavesPerBlock - 1) / kWavesPerBlock;
+// Blocks of a packed rows' repair launch: a wave per row and group of 64
+// lanes over `items` (backward: channels x boundaries; forward: sequences x
+// channels).
+inline int64_t tcp_blocks(int64_t rows, int64_t items) {
+    return (rows * ((items + kWaveSize - 1) / kWaveSize) + kWavesPerBlock - 1) / kWavesPerBlock;
 }
 
 template <int W>
@@ -66,7 +67,7 @@ hipError_t fwd_tc(const FwdArgs &a, int silu, int fk, int rows, hipStream_t s) {
         if (rows == kRowsPacked) {                                                      \
             const hipError_t e = launch(k_fwd_tcp<W, S, F>, a.n_block, a, s);           \
             if (e != hipSuccess) return e;                                              \
-            return launch(k_fwd_tcp_fix<W, S, F>, tcp_blocks(a.D, a.n_seq), a, s);       \
+            return launch(k_fwd_tcp_fix<W, S, F>, tcp_blocks(a.n_seq, a.D), a, s);       \
         }                                                                               \
         if (rows == kRowsSeq) return launch(k_fwd_tcs<W, S, F>, a.n_block, a, s);        \
     }
