@@ -611,12 +611,14 @@ def summarize(args):
             continue
         # An op of several launches counts all of them (time and traffic are
         # their sums per launch): the deterministic backward's fixed-order
-        # reduction of its partials; on packed time lanes, the validation
-        # kernel before the chunks and the boundary repair after them.
+        # reduction of its partials; on packed time lanes, the boundary repair
+        # after the chunks, and the validation kernel before them when there
+        # are too many offsets for the chunk waves to check.
         if kernel in ("k_fwd_tcp", "k_bwd_tcp"):
             kernels = ["k_validate", kernel, kernel + "_fix"]
-        if op == "bwd" and any(_is_kernel(r["_short"], "k_dw_reduce") for r in rows):
+        if op == "bwd":
             kernels.append("k_dw_reduce")
+        kernels = [k for k in kernels if any(_is_kernel(r["_short"], k) for r in rows)]
         fetch = write = 0.0
         nf = nw = 0
         for k in kernels:
