@@ -872,6 +872,9 @@ TC_PACKED_CASES = [
     ([1000, 30, 1], 8, 2, False, False, True, True),
     # few sequences, the forward chunk [1024, 2048) meets sequences 10..13
     ([700, 1, 1, 2, 3, 5, 8, 13, 21, 34, 400, 2, 2, 900, 1], 16, 4, True, True, True, False),
+    # channel counts that leave part of the repair launches' last lane group idle
+    ([300, 1, 2, 77, 3, 640], 13, 4, True, True, True, True),
+    ([5, 1, 40, 3, 77, 513, 1, 1] * 9, 100, 3, False, True, True, False),
     ([3] * 1500, 8, 4, True, True, True, False),
     ([1, 2] * 2100, 8, 4, True, True, True, True),          # 4201 offsets: global path
 ]
