@@ -82,3 +82,33 @@ def test_committed_profiles_carry_a_traffic_record():
         assert 1.0 <= rec["hbm_bytes_per_launch"] / rec["algorithmic_bytes"] < 1.2, p
         assert "rocprofv3" in text and "bench.py" in text, p
     assert seen >= 7
+
+
+@pytest.mark.parametrize("name,kernel,want", [
+    ("k_fwd_tcp<4, true, 2>", "k_fwd_tcp", True),
+    ("k_fwd_tcp_fix<4, true, 2>", "k_fwd_tcp", False),
+    ("k_fwd_tcp_fix<4, true, 2>", "k_fwd_tcp_fix", True),
+    ("k_fwd_tc<4, true, 1>", "k_fwd_tcp", False),
+    ("k_fwd_tc<4, true, 1>", "k_fwd_tc", True),
+    ("ccv::(anonymous namespace)::k_validate(int const*, long, long, unsigned int*, int)",
+     "k_validate", True),
+    ("void ccv::(anonymous namespace)::k_dw_reduce<4>(float const*, long)", "k_dw_reduce", True),
+    ("k_update_staged<4, true, false, true, 2>", "k_update", False),
+    ("__amd_rocclr_copyBuffer", "k_update", False),
+])
+def test_trace_names_match_whole_kernel_names(name, kernel, want):
+    """Counter and trace rows are matched to a kernel by its whole name (a
+    kernel whose name extends another's is another kernel)."""
+    assert bench._is_kernel(name, kernel) is want
+
+
+def test_every_workload_maps_its_ops_to_a_kernel_family():
+    for wl in ("large_decode", "dense", "packed", "decode", "large", "tiny", "seqidx",
+               "dense_tc", "large_tc", "packed_tc", "seqidx_tc"):
+        ks = bench.op_kernels(wl)
+        assert set(ks) == {"fwd", "bwd", "update"}, wl
+    assert bench.op_kernels("packed_tc")["bwd"] == "k_bwd_tcp"
+    assert bench.op_kernels("seqidx_tc")["fwd"] == "k_fwd_tcs"
+    assert bench.op_kernels("dense_tc")["fwd"] == "k_fwd_tc"
+    assert bench.op_kernels("packed")["fwd"] == "k_fwd_chan"
+    assert "k_update_staged" in bench.UPDATE_KERNELS
