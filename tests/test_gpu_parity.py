@@ -899,3 +899,37 @@ def test_packed_time_lanes(case):
     dx, dw, db, dinit = run_bwd(g, "tc", "silu", det, cu, options=opts)
     check_bwd(inp, dx, dw, db, dinit, "silu")
     ops.check_flag(DEV)
+
+
+@pytest.mark.parametrize("layout", ["cl", "tc"])
+def test_large_magnitudes_saturate_like_the_oracle(layout):
+    """Activations and states scaled by 64 (exact in BF16), so that the
+    pre-activation spreads to |z| > 100: SiLU and its slope saturate (exp(-z)
+    overflows and its reciprocal flushes to zero, or exp(-z) underflows) and
+    must still match the oracle, forward, backward and update, with and
+    without the activation."""
+    B, D, T = 2, 64, 600
+    inp = synth.random_inputs(4100 + (layout == "tc"), B, D, T, layout=layout, bias=True,
+                              init=True, dfinal=True)
+    for k in ("x", "initial_states"):
+        inp[k] = inp[k] * 64
+    assert inp["x"].stride() == synth.random_inputs(1, B, D, T, layout=layout)["x"].stride()
+    g = {k: dev(v) for k, v in inp.items()}
+    z = oracle.fwd(f64(inp["x"]), f64(inp["weight"]), f64(inp["bias"]), None,
+                   f64(inp["initial_states"]), None)[0]
+    assert np.abs(z).max() > 100  # the case the test is for
+    for act in ("silu", None):
+        print("large magnitudes", layout, act, flush=True)
+        y, fin = run_fwd(g, layout, act, True)
+        check_fwd(inp, y, fin, act)
+        dx, dw, db, dinit = run_bwd(g, layout, act, False)
+        check_bwd(inp, dx, dw, db, dinit, act)
+    # the decode step from the same scaled states
+    state = inp["initial_states"].contiguous()
+    xt = inp["x"][:, :, 0].contiguous()
+    g_state = dev(state)
+    yt = ops.update(dev(xt), g_state, g["weight"], g["bias"], "silu")
+    torch.cuda.synchronize()
+    oyt, ost = oracle.update(f64(xt), f64(state), f64(inp["weight"]), f64(inp["bias"]), "silu")
+    check_bf16("update y", yt, oyt)
+    check_exact_bf16("conv_state", g_state, ost)
