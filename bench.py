@@ -705,8 +705,9 @@ def main():
         summarize(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the op shards with no communication over channels; see the design notes)",
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(the op shards over channels or batch rows with no communication, each "
+              "GPU running the same kernels on its share)",
               file=sys.stderr)
         sys.exit(2)
 
