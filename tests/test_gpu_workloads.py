@@ -22,7 +22,7 @@ import pytest
 import torch
 
 import oracle
-from depthwise_causal_conv1d_02_amd import ops, synth
+from depthwise_causal_conv1d_02_amd import _abi, ops, synth
 from parity import SENTINEL, check_bf16, check_exact_bf16, check_f32_rel
 
 pytestmark = pytest.mark.gpu
@@ -317,3 +317,144 @@ def test_more_than_2_pow_31_elements():
         ob += odb
     check_f32_rel("dweight", dwt, ow)
     check_f32_rel("dbias", dbt, ob)
+
+
+def _window_y(x, wf, bf, init, s, t):
+    """Oracle y at token t of a sequence that starts at s (init: its initial
+    state [1,D,W-1] or None), from the shortest window that determines it."""
+    lo = max(s, t - 3)
+    win = f(x[:, :, lo:t + 1])
+    oy, _ = oracle.fwd(win, wf, bf, None, init if lo == s else None, "silu")
+    return oy[:, :, -1:]
+
+
+def test_more_than_2_pow_31_elements_time_lanes():
+    """64-bit indexing on the time-lane kernels: [1, 10, 286,331,149] in
+    [B,D,T]-contiguous storage whose rows start on 16-byte boundaries (2.9 G
+    elements; rows 8 and 9 start past element 2^31, row 7 crosses it half
+    way along).
+    Dense rows with initial states and final-state gradients (deterministic
+    backward), packed rows with a sequence starting one token before the
+    crossing and a last sequence of two tokens, and seq_idx rows split at the
+    same place.  Outputs are checked on sampled tokens, each from its own
+    window through the oracle; the backward takes dy zero except at a few
+    tokens, so that dx, dW, dB and the state gradients have closed windows."""
+    D, T = 10, 286_331_149                      # T % 8 = 5, T % 2048 = 269: ragged tails
+    Tp = T + 3                                  # multiple of 8: aligned row starts
+    edge = (1 << 31) - 7 * Tp                   # row 7's token at element 2^31
+    assert 1000 < edge < T - 1000 and 8 * Tp > (1 << 31)
+    check_time_lanes_sampled(D, T, Tp, edge)
+
+
+def check_time_lanes_sampled(D, T, Tp, edge):
+    """The body of the test above for any [1, D, T] shape with row stride Tp
+    and a token `edge` (a sequence starts at edge - 1) well inside the row."""
+    gen = torch.Generator(device=DEV).manual_seed(2031)
+
+    def tc_buffer(fill=None):
+        st = torch.empty(1, D, Tp, dtype=torch.bfloat16, device=DEV)
+        if fill is None:
+            st.view(torch.int16).fill_(np.int16(SENTINEL))
+        else:
+            st.normal_(generator=gen)
+        return st[:, :, :T]
+
+    x = tc_buffer(fill="randn")
+    w = (torch.rand(D, 4, generator=gen, device=DEV) - 0.5).to(torch.bfloat16)
+    b = (torch.randn(D, generator=gen, device=DEV) * 0.1).to(torch.bfloat16)
+    wf, bf = f(w), f(b)
+    samples = sorted({0, 1, 2, 3, 7, 8, 511, 512, 1023, 1024, 1025, edge - 2, edge - 1, edge,
+                      edge + 1, edge + 4, T // 2, T - 38, T - 37, T - 36, T - 6, T - 2, T - 1})
+
+    # dense rows, initial and final states
+    init = torch.randn(1, D, 3, generator=gen, device=DEV).to(torch.bfloat16)
+    y = tc_buffer()
+    y, fin = ops.fwd(x, w, b, None, init, "silu", return_final_states=True, y=y)
+    torch.cuda.synchronize()
+    for t in samples:
+        check_bf16("dense y[%d]" % t, y[:, :, t:t + 1], _window_y(x, wf, bf, f(init), 0, t))
+    check_exact_bf16("dense final_states", fin, f(x[:, :, T - 3:]))
+    del y
+    dy = tc_buffer(fill="randn")
+    picks = (0, 1, edge, T - 1)
+    keep = {t: dy[:, :, t].clone() for t in picks}
+    dy.zero_()
+    for t, v in keep.items():
+        dy[:, :, t] = v
+    dfin = torch.randn(1, D, 3, generator=gen, device=DEV).to(torch.bfloat16)
+    dx = tc_buffer()
+    dx, dwt, dbt, dinit = ops.bwd(x, w, dy, b, None, init, dfin, "silu", deterministic=True,
+                                  dx=dx, options=_abi.CCV_OPT_DETERMINISTIC_DBIAS)
+    torch.cuda.synchronize()
+    # the row's head (picks 0, 1 and the initial state) and tail (pick T-1 and
+    # dfinal) through the oracle with the row's own states
+    hx, hdy = f(x[:, :, :8]), f(dy[:, :, :8])
+    # a window's final state sits at its end: zero dfinal for the head window
+    odx, odw_h, odb_h, odinit = oracle.bwd(hx, wf, hdy, bf, None, f(init), None, "silu")
+    check_bf16("dense dx head", dx[:, :, :5], odx[:, :, :5])
+    check_bf16("dense dinit", dinit, odinit)
+    tx, tdy = f(x[:, :, T - 11:]), f(dy[:, :, T - 8:])
+    odx, odw_t, odb_t, _ = oracle.bwd(tx[:, :, 3:], wf, tdy, bf, None, tx[:, :, :3], f(dfin),
+                                      "silu")
+    check_bf16("dense dx tail", dx[:, :, T - 8:], odx)
+    ex, edy = f(x[:, :, edge - 6:edge + 4]), f(dy[:, :, edge - 3:edge + 4])
+    odx, odw_e, odb_e, _ = oracle.bwd(ex[:, :, 3:], wf, edy, bf, None, ex[:, :, :3], None, "silu")
+    check_bf16("dense dx at the 2^31 crossing", dx[:, :, edge - 3:edge + 4], odx)
+    for t in (T // 2, edge - 700, edge + 700):
+        check_bf16("dense dx[%d] (dy zero nearby)" % t, dx[:, :, t:t + 1], np.zeros((1, D, 1)))
+    check_f32_rel("dense dweight", dwt, odw_h + odw_t + odw_e)
+    check_f32_rel("dense dbias", dbt, odb_h + odb_t + odb_e)
+    del dx
+
+    # packed rows: a sequence starts one token before row 7's crossing, the
+    # last one holds two tokens
+    s1, s2 = edge - 1, T - 2
+    cu = torch.tensor([0, s1, s2, T], dtype=torch.int32, device=DEV)
+    pinit = torch.randn(3, D, 3, generator=gen, device=DEV).to(torch.bfloat16)
+    starts = (0, s1, s2)
+    ops.reset_flag(DEV)
+    y = tc_buffer()
+    y, fin = ops.fwd(x, w, b, cu, pinit, "silu", return_final_states=True, y=y)
+    torch.cuda.synchronize()
+    for t in samples + [s1 + 1, s1 + 2, s1 + 3]:
+        s = max(v for v in starts if v <= t)
+        i = starts.index(s)
+        check_bf16("packed y[%d]" % t, y[:, :, t:t + 1],
+                   _window_y(x, wf, bf, f(pinit[i:i + 1]), s, t))
+    check_exact_bf16("packed final_states[0]", fin[0:1], f(x[:, :, s1 - 3:s1]))
+    check_exact_bf16("packed final_states[1]", fin[1:2], f(x[:, :, s2 - 3:s2]))
+    check_exact_bf16("packed final_states[2]", fin[2:3],
+                     np.concatenate([f(pinit[2:3])[:, :, 2:], f(x[:, :, s2:])], axis=2))
+    del y
+    picks = (s1, s1 + 2, T - 1)
+    dy.zero_()
+    for t in picks:
+        dy[:, :, t] = 1.0
+    dx = tc_buffer()
+    dx, dwt, dbt, dinit = ops.bwd(x, w, dy, b, cu, pinit, None, "silu", dx=dx)
+    torch.cuda.synchronize()
+    ops.check_flag(DEV)
+    check_bf16("packed dx before the start", dx[:, :, s1 - 3:s1], np.zeros((1, D, 3)))
+    odx1, odw1, odb1, odi1 = oracle.bwd(f(x[:, :, s1:s1 + 6]), wf, f(dy[:, :, s1:s1 + 6]), bf,
+                                        None, f(pinit[1:2]), None, "silu")
+    check_bf16("packed dx after the start", dx[:, :, s1:s1 + 6], odx1)
+    check_bf16("packed dinit[1]", dinit[1:2], odi1)
+    odx2, odw2, odb2, odi2 = oracle.bwd(f(x[:, :, s2:]), wf, f(dy[:, :, s2:]), bf, None,
+                                        f(pinit[2:3]), None, "silu")
+    check_bf16("packed dx, last sequence", dx[:, :, s2:], odx2)
+    check_bf16("packed dinit[2]", dinit[2:3], odi2)
+    check_bf16("packed dinit[0]", dinit[0:1], np.zeros((1, D, 3)))
+    check_f32_rel("packed dweight", dwt, odw1 + odw2)
+    check_f32_rel("packed dbias", dbt, odb1 + odb2)
+    del dx, dy
+
+    # seq_idx rows: ids 4 before s1, 9 from s1 on, 2 on the last two tokens
+    seq = torch.full((1, T), 4, dtype=torch.int32, device=DEV)
+    seq[:, s1:] = 9
+    seq[:, s2:] = 2
+    y = tc_buffer()
+    ops.fwd(x, w, b, None, None, "silu", y=y, seq_idx=seq)
+    torch.cuda.synchronize()
+    for t in samples + [s1 + 1, s1 + 2, s1 + 3]:
+        s = max(v for v in starts if v <= t)
+        check_bf16("seq_idx y[%d]" % t, y[:, :, t:t + 1], _window_y(x, wf, bf, None, s, t))
