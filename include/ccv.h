@@ -72,7 +72,9 @@ typedef enum ccv_status {
      * call ran with FP32 atomics (cuDNN FE "Causal Conv1d", determinism). */
     CCV_WARN_NONDETERMINISTIC = 1,
     /* Bad shape, stride, dtype or pointer; B != 1 with cu_seqlens; both
-     * seq_idx and cu_seqlens; T < 1; N < 1; a too-small workspace. */
+     * seq_idx and cu_seqlens; B, D, T or N < 1 (empty inputs: PyTorch hands
+     * an empty tensor a null data pointer, which reads as absent here); a
+     * too-small workspace. */
     CCV_ERR_INVALID_ARG = -1,
     /* An output's byte span overlaps an input's or another output's
      * (cuDNN FE "Causal Conv1d", the paragraph on final_states_out). */

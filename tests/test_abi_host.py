@@ -119,6 +119,12 @@ def test_fwd_rejects(L):
     x0, w0, _ = dense(T_=1)
     x0.shape[2] = 0
     assert fwd(L, x0, w0, y=T([2, 64, 0])) == INVALID              # T = 0
+    xb, wb, yb = dense()
+    xb.shape[0] = yb.shape[0] = 0
+    assert fwd(L, xb, wb, y=yb) == INVALID                         # B = 0
+    xd, wd, yd = dense()
+    xd.shape[1] = yd.shape[1] = wd.shape[0] = 0
+    assert fwd(L, xd, wd, y=yd) == INVALID                         # D = 0
     # an output that overlaps itself
     assert fwd(L, x, w, y=T([2, 64, 32], stride=[0, 32, 1])) == INVALID
     assert fwd(L, x, w, y=y, fin=T([2, 64, 3], stride=[3, 1, 1])) == INVALID
@@ -247,6 +253,9 @@ def test_update_rejects(L):
     assert up(w=T([64, 4], F32), b=T([64], F32)) == UNSUP
     assert up(w=T([64, 4], F32), b=T([64]), opt=F32FB) == INVALID
     assert up(opt=0x10) == INVALID
+    xe, ste, ye = T([1, 64]), T([1, 64, 3]), T([1, 64])
+    xe.shape[0] = ste.shape[0] = ye.shape[0] = 0
+    assert up(x=xe, st=ste, y=ye) == INVALID                       # B = 0
     assert up(act=7) == UNSUP
     assert up(y=T([4, 64], data=x.data)) == ALIAS
     assert up(y=T([4, 64], data=st.data + 2)) == ALIAS
