@@ -26,6 +26,12 @@ input already resident in HBM:
                     marked by seq_idx (no states): forward + backward.
   dense_tc, large_tc, packed_tc, seqidx_tc
                     the same data in [B,D,T] time-contiguous storage.
+  dense_w2, dense_w3, dense_noact, dense_f32bias
+                    the dense workload with filter width 2 or 3, without the
+                    activation, or with an FP32 weight and FP32 bias (opt-in)
+                    and the deterministic dweight and dbias (opt-in).
+  decode_tokens     the decode shape, 64 tokens as 8 multi-token updates of
+                    8 tokens each.
 
 The value is algorithmic bytes (every compulsory input read once, every output
 written once) per step divided by the wall time per step.  Per-op times come
@@ -49,6 +55,9 @@ SPACER_CYCLES = 200000      # GPU spin before each timed op in the per-op pass
 METRIC = "achieved HBM GB/s (% of MI355X peak) for fwd, bwd and update at 1 GPU"
 
 
+WORKLOADS = ["large_decode", "dense", "packed", "decode", "large", "tiny", "seqidx",
+             "dense_tc", "large_tc", "packed_tc", "seqidx_tc",
+             "dense_w2", "dense_w3", "dense_noact", "dense_f32bias", "decode_tokens"]
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "depthwise_causal_conv1d_02_amd", "csrc")
 OP_KERNEL = {"fwd": "k_fwd_chan", "bwd": "k_bwd_chan", "update": "k_update"}
@@ -110,18 +119,50 @@ def act_bytes(B, D, T):
     return B * D * T * 2
 
 
-def fwd_bytes(B, D, T, R, init, final, w_bytes, bias):
-    return (2 * act_bytes(B, D, T) + (R * D * 6 if init else 0) + (R * D * 6 if final else 0)
-            + D * 4 * w_bytes + (D * 2 if bias else 0))
+def fwd_bytes(B, D, T, R, init, final, w_bytes, bias, W=4, b_bytes=2):
+    st = R * D * (W - 1) * 2  # one BF16 state tensor
+    return (2 * act_bytes(B, D, T) + (st if init else 0) + (st if final else 0)
+            + D * W * w_bytes + (D * b_bytes if bias else 0))
 
 
-def bwd_bytes(B, D, T, R, init, dfinal, w_bytes, bias):
-    return (3 * act_bytes(B, D, T) + (2 * R * D * 6 if init else 0) + (R * D * 6 if dfinal else 0)
-            + D * 4 * w_bytes + D * 4 * 4 + ((D * 2 + D * 4) if bias else 0))
+def bwd_bytes(B, D, T, R, init, dfinal, w_bytes, bias, W=4, b_bytes=2):
+    st = R * D * (W - 1) * 2
+    return (3 * act_bytes(B, D, T) + (2 * st if init else 0) + (st if dfinal else 0)
+            + D * W * w_bytes + D * W * 4 + ((D * b_bytes + D * 4) if bias else 0))
 
 
 def update_bytes(B, D, w_bytes, bias):
     return B * D * 16 + D * 4 * w_bytes + (D * 2 if bias else 0)
+
+
+def update_tokens_bytes(B, D, L, w_bytes, bias):
+    """L tokens per call: the state read and written once, each token read
+    and its output written."""
+    return B * D * (12 + 4 * L) + D * 4 * w_bytes + (D * 2 if bias else 0)
+
+
+# Algorithmic bytes per launch of each op of every workload, from the shapes
+# alone (the summaries of rocprofv3 runs need them without a GPU).
+WORKLOAD_BYTES = {
+    "dense": {"fwd": fwd_bytes(4, 4096, 2048, 4, True, True, 2, True),
+              "bwd": bwd_bytes(4, 4096, 2048, 4, True, False, 2, True)},
+    "seqidx": {"fwd": fwd_bytes(4, 4096, 2048, 4, False, False, 2, True) + 4 * 2048 * 4,
+               "bwd": bwd_bytes(4, 4096, 2048, 4, False, False, 2, True) + 4 * 2048 * 4},
+    "packed": {"fwd": fwd_bytes(1, 5120, 33280, 16, True, True, 4, False),
+               "bwd": bwd_bytes(1, 5120, 33280, 16, True, False, 4, False)},
+    "large": {"fwd": fwd_bytes(8, 8192, 8192, 8, False, False, 2, False),
+              "bwd": bwd_bytes(8, 8192, 8192, 8, False, False, 2, False)},
+    "decode": {"update": update_bytes(256, 8192, 2, True)},
+    "dense_w2": {"fwd": fwd_bytes(4, 4096, 2048, 4, True, True, 2, True, W=2),
+                 "bwd": bwd_bytes(4, 4096, 2048, 4, True, False, 2, True, W=2)},
+    "dense_w3": {"fwd": fwd_bytes(4, 4096, 2048, 4, True, True, 2, True, W=3),
+                 "bwd": bwd_bytes(4, 4096, 2048, 4, True, False, 2, True, W=3)},
+    "dense_noact": {"fwd": fwd_bytes(4, 4096, 2048, 4, True, True, 2, True),
+                    "bwd": bwd_bytes(4, 4096, 2048, 4, True, False, 2, True)},
+    "dense_f32bias": {"fwd": fwd_bytes(4, 4096, 2048, 4, True, True, 4, True, b_bytes=4),
+                      "bwd": bwd_bytes(4, 4096, 2048, 4, True, False, 4, True, b_bytes=4)},
+    "decode_tokens": {"update": update_tokens_bytes(256, 8192, 8, 2, True)},
+}
 
 
 class Workload:
@@ -147,9 +188,13 @@ class Workload:
             self.counts = dict(self.large.counts, update=self.decode.counts["update"])
             self.desc = ("%s; then %s" % (self.large.desc, self.decode.desc))
             return
-        idx = {"tiny": 1, "dense": 2, "packed": 3, "decode": 4, "large": 5,
-               "seqidx": 6}[self.kind]
-        self.cpu = synth.workload(idx)
+        variant = self.kind in synth.VARIANTS
+        if variant:
+            self.cpu = synth.variant(self.kind)
+        else:
+            idx = {"tiny": 1, "dense": 2, "packed": 3, "decode": 4, "large": 5,
+                   "seqidx": 6}[self.kind]
+            self.cpu = synth.workload(idx)
         if name.endswith("_tc"):
             self.cpu = dict(self.cpu, x=self.cpu["x"].contiguous(),
                             dy=None if self.cpu["dy"] is None else self.cpu["dy"].contiguous())
@@ -166,21 +211,30 @@ class Workload:
                          "weight+bias, SiLU, state mutated in place (rotating over %d states)"
                          % (B, D, n_tok, DECODE_STATES))
             return
+        if self.kind == "decode_tokens":
+            n_call, B, D, L = w["x_calls"].shape
+            self.shape = dict(B=B, D=D, tokens=n_call * L, tokens_per_call=L)
+            self.bytes = {"update": update_tokens_bytes(B, D, L, 2, True)}
+            self.counts = {"update": n_call}
+            self.desc = synth.VARIANTS[self.kind] + " (rotating over %d states)" % DECODE_STATES
+            return
         x = w["x"]
         B, D, T = x.shape
         cu = w["cu_seqlens"]
         R = B if cu is None else cu.numel() - 1
         wb = 4 if w["weight"].dtype == torch.float32 else 2
         bias = w["bias"] is not None
+        bb = 4 if bias and w["bias"].dtype == torch.float32 else 2
         init = w["initial_states"] is not None
-        self.shape = dict(B=B, D=D, T=T, R=R)
+        W = w["weight"].shape[1]
+        self.shape = dict(B=B, D=D, T=T, R=R, W=W)
         seq = B * T * 4 if w.get("seq_idx") is not None else 0   # the int32 ids
-        self.bytes = {"fwd": fwd_bytes(B, D, T, R, init, w["return_final_states"], wb, bias)
-                      + seq}
+        self.bytes = {"fwd": fwd_bytes(B, D, T, R, init, w["return_final_states"], wb, bias,
+                                       W, bb) + seq}
         if w["dy"] is not None:
-            self.bytes["bwd"] = bwd_bytes(B, D, T, R, init, False, wb, bias) + seq
+            self.bytes["bwd"] = bwd_bytes(B, D, T, R, init, False, wb, bias, W, bb) + seq
         self.counts = {k: 1 for k in self.bytes}
-        self.desc = synth.WORKLOADS[idx]
+        self.desc = synth.VARIANTS[self.kind] if variant else synth.WORKLOADS[idx]
         if name.endswith("_tc"):
             self.desc = self.desc.replace("channel-last", "[B,D,T] time-contiguous")
 
@@ -202,7 +256,7 @@ class Workload:
         if self.kind == "large_decode":
             return self.large.token_channels() + self.decode.token_channels()
         sh = self.shape
-        return sh["B"] * sh["D"] * (sh["tokens"] if self.kind == "decode" else sh["T"])
+        return sh["B"] * sh["D"] * (sh["tokens"] if "tokens" in sh else sh["T"])
 
     def clone(self):
         """The same workload on fresh device copies of its tensors (strides
@@ -259,25 +313,37 @@ def make_step(wl, torch):
                                                      y=ys[s])))
                  for s in range(xs.shape[0])]
         return Step(calls, {"y": ys}, [])
+    if wl.kind == "decode_tokens":
+        states = [g["conv_state"].clone() for _ in range(DECODE_STATES)]
+        xs = g["x_calls"]                       # [calls, B, D, L], unit channel stride
+        ys = torch.empty_like(xs)
+        calls = [("update", (lambda s=s: ops.update(xs[s], states[s % DECODE_STATES],
+                                                     g["weight"], g["bias"], g["activation"],
+                                                     y=ys[s])))
+                 for s in range(xs.shape[0])]
+        return Step(calls, {"y": ys}, [])
 
     x = g["x"]
     y = torch.empty_like(x)
+    W = g["weight"].shape[1]
+    opts = ops._options(g.get("fp32_weight_bias", False), g.get("deterministic_dbias", False))
     fin = None
     if g["return_final_states"]:
-        fin = torch.empty(wl.shape["R"], x.shape[1], 3, dtype=x.dtype, device=dev)
+        fin = torch.empty(wl.shape["R"], x.shape[1], W - 1, dtype=x.dtype, device=dev)
     flag = torch.zeros(1, dtype=torch.int32, device=dev)
     seq = g.get("seq_idx")
     calls = [("fwd", lambda: ops.fwd(x, g["weight"], g["bias"], g["cu_seqlens"],
                                      g["initial_states"], g["activation"],
-                                     final_states_out=fin, y=y, err_flag=flag, seq_idx=seq))]
+                                     final_states_out=fin, y=y, err_flag=flag, seq_idx=seq,
+                                     options=opts))]
     outputs = {"y": y}
     if g["dy"] is not None:
         dx = torch.empty_like(x)
         D = x.shape[1]
         # dweight and dbias live in one buffer, cleared by a single fill per step
-        grads = torch.zeros(D * 5, dtype=torch.float32, device=dev)
-        dw = grads[:D * 4].view(D, 4)
-        db = grads[D * 4:] if g["bias"] is not None else None
+        grads = torch.zeros(D * (W + 1), dtype=torch.float32, device=dev)
+        dw = grads[:D * W].view(D, W)
+        db = grads[D * W:] if g["bias"] is not None else None
         dinit = torch.empty_like(g["initial_states"]) if g["initial_states"] is not None else None
         ws = torch.empty(1 << 26, dtype=torch.uint8, device=dev) if g["deterministic"] else None
         calls.append(("zero_grads", grads.zero_))
@@ -285,7 +351,7 @@ def make_step(wl, torch):
                                              g["initial_states"], None, g["activation"],
                                              g["deterministic"], False, dx=dx, err_flag=flag,
                                              workspace=ws, dweight=dw, dbias=db, dinit=dinit,
-                                             seq_idx=seq)))
+                                             seq_idx=seq, options=opts)))
         outputs.update(dx=dx, dw=dw)
     return Step(calls, outputs, [flag] if g["cu_seqlens"] is not None else [])
 
@@ -471,6 +537,25 @@ def _oracle_decode(wl, budget_s):
     return dt, steps * update_bytes(B, D, 2, True), steps, B, D
 
 
+def _oracle_decode_tokens(wl, budget_s):
+    """Oracle multi-token updates (each call's L tokens on every batch row),
+    until the calls are done or the budget is spent: (seconds, bytes, calls,
+    rows, D, L)."""
+    import oracle
+    w = wl.cpu
+    f = lambda t: None if t is None else t.double().numpy()
+    n_call, B, D, L = w["x_calls"].shape
+    st = f(w["conv_state"])
+    t0 = time.perf_counter()
+    calls = 0
+    while calls < n_call and time.perf_counter() - t0 < budget_s:
+        _, st = oracle.update_tokens(f(w["x_calls"][calls]), st, f(w["weight"]), f(w["bias"]),
+                                     w["activation"])
+        calls += 1
+    dt = time.perf_counter() - t0
+    return dt, calls * update_tokens_bytes(B, D, L, 2, True), calls, B, D, L
+
+
 def _oracle_rows(wl, budget_s):
     """Oracle forward (+ backward) of a workload on a leading block of
     channels (all rows and tokens), sized by a short pilot to about
@@ -493,20 +578,23 @@ def _oracle_rows(wl, budget_s):
         xs, ws_, bs = sub(x), sub(w["weight"]), sub(w["bias"])
         init, dy = sub(w["initial_states"]), sub(w["dy"])
         seq = w.get("seq_idx")
+        act = w["activation"]
         t0 = time.perf_counter()
         if seq is not None:
-            oracle.fwd_seq(xs, ws_, seq.numpy(), bs, "silu")
+            oracle.fwd_seq(xs, ws_, seq.numpy(), bs, act)
             if has_bwd:
-                oracle.bwd_seq(xs, ws_, dy, seq.numpy(), bs, "silu")
+                oracle.bwd_seq(xs, ws_, dy, seq.numpy(), bs, act)
         else:
-            oracle.fwd(xs, ws_, bs, cun, init, "silu", return_final_states=True)
+            oracle.fwd(xs, ws_, bs, cun, init, act, return_final_states=True)
             if has_bwd:
-                oracle.bwd(xs, ws_, dy, bs, cun, init, None, "silu")
+                oracle.bwd(xs, ws_, dy, bs, cun, init, None, act)
         dt = time.perf_counter() - t0
         fin = w["return_final_states"]
-        nbytes = fwd_bytes(B, nch, T, R, init is not None, fin, wb, bs is not None)
+        W = w["weight"].shape[1]
+        bb = 4 if bs is not None and w["bias"].dtype.itemsize == 4 else 2
+        nbytes = fwd_bytes(B, nch, T, R, init is not None, fin, wb, bs is not None, W, bb)
         if has_bwd:
-            nbytes += bwd_bytes(B, nch, T, R, init is not None, False, wb, bs is not None)
+            nbytes += bwd_bytes(B, nch, T, R, init is not None, False, wb, bs is not None, W, bb)
         return dt, nbytes
 
     pilot_dt, _ = run(min(D, 8))
@@ -531,6 +619,10 @@ def cpu_baseline(wl, budget_s=10.0):
             dt, nbytes, steps, rows, D = _oracle_decode(wl, budget_s)
             sample = "%d decode steps on all %d rows x %d channels" % (steps, rows, D)
             tc = steps * rows * D
+        elif wl.kind == "decode_tokens":
+            dt, nbytes, calls, rows, D, L = _oracle_decode_tokens(wl, budget_s)
+            sample = "%d calls of %d tokens on all %d rows x %d channels" % (calls, L, rows, D)
+            tc = calls * L * rows * D
         else:
             dt, nbytes, nch, D, has_bwd = _oracle_rows(wl, budget_s)
             B, T = wl.shape["B"], wl.shape["T"]
@@ -579,19 +671,8 @@ def summarize(args):
     (kernel trace, FETCH_SIZE pass, WRITE_SIZE pass, and the same two counters
     for a plain copy of known size)."""
     import glob
-    dense = {"fwd": fwd_bytes(4, 4096, 2048, 4, True, True, 2, True),
-             "bwd": bwd_bytes(4, 4096, 2048, 4, True, False, 2, True)}
-    large = {"fwd": fwd_bytes(8, 8192, 8192, 8, False, False, 2, False),
-             "bwd": bwd_bytes(8, 8192, 8192, 8, False, False, 2, False)}
-    wl_bytes = {"dense": dense,
-                "seqidx": {"fwd": fwd_bytes(4, 4096, 2048, 4, False, False, 2, True) + 4 * 2048 * 4,
-                           "bwd": bwd_bytes(4, 4096, 2048, 4, False, False, 2, True) + 4 * 2048 * 4},
-                "packed": {"fwd": fwd_bytes(1, 5120, 33280, 16, True, True, 4, False),
-                           "bwd": bwd_bytes(1, 5120, 33280, 16, True, False, 4, False)},
-                "large": {"fwd": fwd_bytes(8, 8192, 8192, 8, False, False, 2, False),
-                          "bwd": bwd_bytes(8, 8192, 8192, 8, False, False, 2, False)},
-                "decode": {"update": update_bytes(256, 8192, 2, True)}}[
-                    args.workload[:-3] if args.workload.endswith("_tc") else args.workload]
+    wl_bytes = WORKLOAD_BYTES[
+        args.workload[:-3] if args.workload.endswith("_tc") else args.workload]
     trace_dir, fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.summarize
     stats = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
     rows = _kernel_rows(stats)
@@ -676,8 +757,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="large_decode",
-                    choices=["large_decode", "dense", "packed", "decode", "large", "tiny",
-                             "seqidx", "dense_tc", "large_tc", "packed_tc", "seqidx_tc"])
+                    choices=WORKLOADS)
     ap.add_argument("--no-other-configs", action="store_true",
                     help="with large_decode: skip timing the dense and packed workloads' ops")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -184,3 +184,42 @@ def workload(idx):
                     seq_idx=seq_idx_tensor(g, B, T, "runs", max_run=1024, min_run=64),
                     activation="silu", return_final_states=False, deterministic=False)
     raise ValueError("workload index must be 1..6")
+
+
+# ---- variants of the dense and decode workloads (the optional features) -----
+
+VARIANTS = {
+    "dense_w2": "dense fwd+bwd with state, filter width 2: B=4 D=4096 T=2048, channel-last, "
+                "bf16 weight+bias, initial_states [B,D,1], SiLU, final_states returned",
+    "dense_w3": "dense fwd+bwd with state, filter width 3: B=4 D=4096 T=2048, channel-last, "
+                "bf16 weight+bias, initial_states [B,D,2], SiLU, final_states returned",
+    "dense_noact": "dense fwd+bwd with state, no activation: B=4 D=4096 T=2048, channel-last, "
+                   "bf16 weight+bias, initial_states, final_states returned",
+    "dense_f32bias": "dense fwd+bwd with state, fp32 weight + fp32 bias (opt-in): B=4 D=4096 "
+                     "T=2048, channel-last, initial_states, SiLU, final_states returned, "
+                     "deterministic dweight and dbias (opt-in)",
+    "decode_tokens": "multi-token decode update: B=256 D=8192, 64 tokens as 8 calls of 8 "
+                     "tokens ([B,D,8] over [B,8,D] storage), bf16 weight+bias, SiLU, state "
+                     "mutated in place",
+}
+
+
+def variant(name):
+    """Inputs of variant ``name`` (a key of VARIANTS) as CPU tensors; the seed
+    is 100 + the variant's position in VARIANTS."""
+    g = torch.Generator().manual_seed(100 + list(VARIANTS).index(name))
+    if name == "decode_tokens":
+        B, D, L, calls = 256, 8192, 8, 8
+        return dict(conv_state=_normal(g, (B, D, 3)),
+                    x_calls=_normal(g, (calls, B, L, D)).transpose(2, 3),
+                    weight=weight_tensor(g, D), bias=bias_tensor(g, D), activation="silu")
+    B, D, T = 4, 4096, 2048
+    W = {"dense_w2": 2, "dense_w3": 3}.get(name, 4)
+    f32 = name == "dense_f32bias"
+    dt = torch.float32 if f32 else BF16
+    return dict(x=activation_tensor(g, B, D, T, "cl"), weight=weight_tensor(g, D, W, dt),
+                bias=bias_tensor(g, D, dt), initial_states=state_tensor(g, B, D, W),
+                dy=activation_tensor(g, B, D, T, "cl"), cu_seqlens=None,
+                activation=None if name == "dense_noact" else "silu",
+                return_final_states=True, deterministic=f32,
+                fp32_weight_bias=f32, deterministic_dbias=f32)

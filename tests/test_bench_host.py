@@ -42,6 +42,19 @@ def test_more_than_one_gpu_exits_with_a_message():
     # B=8 D=8192 T=8192, no bias, no states
     ("large fwd", lambda: bench.fwd_bytes(8, 8192, 8192, 8, False, False, 2, False), 2147549184),
     ("large bwd", lambda: bench.bwd_bytes(8, 8192, 8192, 8, False, False, 2, False), 3221422080),
+    # the dense shape with a width-2 filter: one state slot, [D,2] filter and dW
+    ("dense_w2 fwd", lambda: bench.WORKLOAD_BYTES["dense_w2"]["fwd"],
+     2 * 4 * 4096 * 2048 * 2 + 2 * 4 * 4096 * 2 + 4096 * 2 * 2 + 4096 * 2),
+    ("dense_w2 bwd", lambda: bench.WORKLOAD_BYTES["dense_w2"]["bwd"],
+     3 * 4 * 4096 * 2048 * 2 + 2 * 4 * 4096 * 2 + 4096 * 2 * 2 + 4096 * 2 * 4 + 4096 * (2 + 4)),
+    # FP32 filter and FP32 bias
+    ("dense_f32bias fwd", lambda: bench.WORKLOAD_BYTES["dense_f32bias"]["fwd"],
+     2 * 4 * 4096 * 2048 * 2 + 2 * 4 * 4096 * 6 + 4096 * 4 * 4 + 4096 * 4),
+    ("dense_f32bias bwd", lambda: bench.WORKLOAD_BYTES["dense_f32bias"]["bwd"],
+     3 * 4 * 4096 * 2048 * 2 + 2 * 4 * 4096 * 6 + 4096 * 4 * 4 + 4096 * 4 * 4 + 4096 * (4 + 4)),
+    # 8 tokens per call: the state read and written once, 8 tokens in, 8 out
+    ("decode_tokens update", lambda: bench.WORKLOAD_BYTES["decode_tokens"]["update"],
+     256 * 8192 * (6 + 6 + 8 * 2 + 8 * 2) + 8192 * 4 * 2 + 8192 * 2),
 ])
 def test_algorithmic_bytes(name, got, want):
     assert got() == want, name
@@ -103,8 +116,7 @@ def test_trace_names_match_whole_kernel_names(name, kernel, want):
 
 
 def test_every_workload_maps_its_ops_to_a_kernel_family():
-    for wl in ("large_decode", "dense", "packed", "decode", "large", "tiny", "seqidx",
-               "dense_tc", "large_tc", "packed_tc", "seqidx_tc"):
+    for wl in bench.WORKLOADS:
         ks = bench.op_kernels(wl)
         assert set(ks) == {"fwd", "bwd", "update"}, wl
     assert bench.op_kernels("packed_tc")["bwd"] == "k_bwd_tcp"

@@ -82,6 +82,12 @@ def run_workload(idx, tc=False):
     if tc:
         w = dict(w, x=w["x"].contiguous(),
                  dy=None if w["dy"] is None else w["dy"].contiguous())
+    return run_inputs(w, "workload %d" % idx)
+
+
+def run_inputs(w, label, options=0):
+    """One forward (and backward) call on a workload's inputs, as the
+    benchmark makes it, into sentinel-filled outputs."""
     g = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in w.items()}
     x = g["x"]
     assert x.stride() == w["x"].stride()
@@ -92,21 +98,22 @@ def run_workload(idx, tc=False):
     y = sentinel_like(x)
     fin = None
     if w["return_final_states"]:
-        fin = torch.empty(R, D, 3, dtype=x.dtype, device=DEV)
+        fin = torch.empty(R, D, w["weight"].shape[1] - 1, dtype=x.dtype, device=DEV)
         fin.view(torch.int16).fill_(np.int16(SENTINEL))
-    print("workload %d: forward" % idx, flush=True)
+    print("%s: forward" % label, flush=True)
     ops.fwd(x, g["weight"], g["bias"], g["cu_seqlens"], g["initial_states"], g["activation"],
-            final_states_out=fin, y=y, err_flag=flag, seq_idx=seq)
+            final_states_out=fin, y=y, err_flag=flag, seq_idx=seq, options=options)
     out = {"y": y, "fin": fin}
     if g["dy"] is not None:
         dx = sentinel_like(x)
         dinit = None
         if g["initial_states"] is not None:
             dinit = sentinel_like(g["initial_states"])
-        print("workload %d: backward" % idx, flush=True)
+        print("%s: backward" % label, flush=True)
         _, dw, db, _ = ops.bwd(x, g["weight"], g["dy"], g["bias"], g["cu_seqlens"],
                                g["initial_states"], None, g["activation"], g["deterministic"],
-                               False, dx=dx, err_flag=flag, seq_idx=seq, dinit=dinit)
+                               False, dx=dx, err_flag=flag, seq_idx=seq, dinit=dinit,
+                               options=options)
         out.update(dx=dx, dw=dw, db=db, dinit=dinit)
     torch.cuda.synchronize()
     assert int(flag.item()) == 0
@@ -254,6 +261,49 @@ def check_seq_sample(w, out):
 def test_workload_6_seq_idx_fwd_bwd():
     w, g, out = run_workload(6)
     check_seq_sample(w, out)
+
+
+@pytest.mark.parametrize("name", ["dense_w2", "dense_w3", "dense_noact", "dense_f32bias"])
+def test_variant_workload_full(name):
+    """The benchmark's variants of the dense workload (filter widths 2 and 3,
+    no activation, FP32 weight with FP32 bias and the deterministic dweight
+    and dbias), every channel against the oracle."""
+    w = synth.variant(name)
+    opts = ops._options(w["fp32_weight_bias"], w["deterministic_dbias"])
+    w, g, out = run_inputs(w, name, opts)
+    check_full(w, out, 256)
+    if w["deterministic"]:
+        dx = torch.empty_like(g["x"])
+        for _ in range(3):
+            _, dw, db, _ = ops.bwd(g["x"], g["weight"], g["dy"], g["bias"], None,
+                                   g["initial_states"], None, g["activation"], True, False,
+                                   dx=dx, options=opts)
+            torch.cuda.synchronize()
+            assert torch.equal(dw.view(torch.int32), out["dw"].view(torch.int32))
+            assert torch.equal(db.view(torch.int32), out["db"].view(torch.int32))
+
+
+def test_variant_decode_tokens_full():
+    """The benchmark's multi-token decode: 64 tokens as 8 calls of 8 on the
+    decode shape, against the oracle's calls in the same order."""
+    w = synth.variant("decode_tokens")
+    state = w["conv_state"].to(DEV)
+    wt, bt = w["weight"].to(DEV), w["bias"].to(DEV)
+    xs = w["x_calls"].to(DEV)
+    assert xs.stride() == w["x_calls"].stride() and xs.stride(2) == 1
+    ys = torch.empty_like(xs)
+    ys.view(torch.int16).fill_(np.int16(SENTINEL))
+    for c in range(xs.shape[0]):
+        ops.update(xs[c], state, wt, bt, "silu", y=ys[c])
+    torch.cuda.synchronize()
+    no_sentinel("y (8 calls)", ys)
+    host = ys.cpu()
+    ost = f(w["conv_state"])
+    wf, bf = f(w["weight"]), f(w["bias"])
+    for c in range(xs.shape[0]):
+        oy, ost = oracle.update_tokens(f(w["x_calls"][c]), ost, wf, bf, "silu")
+        check_bf16("update y call %d" % c, host[c], oy)
+    check_exact_bf16("conv_state after 8 calls", state, ost)
 
 
 @pytest.mark.parametrize("idx", [2, 3, 5, 6])
