@@ -24,6 +24,26 @@
 #ifndef CCV_BWD_MIN_CHUNK
 #define CCV_BWD_MIN_CHUNK 16
 #endif
+// The deterministic backward's grid (and so its partials) depends on the
+// shape alone: a whole number of nominal rounds of CCV_BWD_DET_ROUND_WAVES
+// waves (the backward's resident waves on MI355X: two per SIMD; packed rows
+// three), with chunks of at most about CCV_BWD_DET_ROUND_STEPS steps.
+// Measured (interleaved, cold): against a plain 16384-wave target, the
+// dense shape 54.5 -> 46.3 us, seq_idx rows 67.0 -> 52.4 us, packed rows
+// 228 -> 216 us (one round of 256-step chunks), the large shape unchanged
+// (8 rounds of 128 steps either way).  0 waves: the plain target.
+#ifndef CCV_BWD_DET_ROUND_WAVES
+#define CCV_BWD_DET_ROUND_WAVES 2048
+#endif
+#ifndef CCV_BWD_DET_ROUND_STEPS
+#define CCV_BWD_DET_ROUND_STEPS 128
+#endif
+#ifndef CCV_BWD_DET_PACKED_ROUND_WAVES
+#define CCV_BWD_DET_PACKED_ROUND_WAVES 3072
+#endif
+#ifndef CCV_BWD_DET_PACKED_ROUND_STEPS
+#define CCV_BWD_DET_PACKED_ROUND_STEPS 256
+#endif
 #ifndef CCV_MAX_CHUNK
 #define CCV_MAX_CHUNK 1024
 #endif
@@ -381,6 +401,23 @@ Geometry geometry(const Problem &p, int vec, int wt, int wc, int64_t capacity, i
     return g;
 }
 
+// Target waves of the deterministic backward: as many nominal rounds as
+// chunks of at most the round's steps need, up to the plain target (the
+// large workload: 8 rounds of 128-step chunks, which is the plain target;
+// the dense one: 1 round of 64-step chunks; the packed one: 1 round of 3072
+// waves).
+int64_t det_target_waves(const Problem &p, int vec) {
+    const int64_t waves = p.packed ? CCV_BWD_DET_PACKED_ROUND_WAVES : CCV_BWD_DET_ROUND_WAVES;
+    const int64_t steps = p.packed ? CCV_BWD_DET_PACKED_ROUND_STEPS : CCV_BWD_DET_ROUND_STEPS;
+    if (waves <= 0) return CCV_BWD_TARGET_WAVES;
+    const int64_t groups = (p.D + ccv::kWaveSize * vec - 1) / (ccv::kWaveSize * vec);
+    const int64_t work = (p.packed ? 1 : p.B) * groups * p.T;
+    const int64_t per_round = waves * steps;
+    // never more waves (so never more partials) than the plain target
+    return std::min<int64_t>(std::max<int64_t>(1, (work + per_round - 1) / per_round) * waves,
+                             CCV_BWD_TARGET_WAVES);
+}
+
 // Split off tail chunks: the main chunks keep their number (whole blocks of
 // `wt`) and shrink to cover (100 - pct)% of the steps; the rest is cut into
 // chunks of `lt` steps.  No split when pct or lt is 0, or when the main
@@ -609,7 +646,7 @@ int bwd_call(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bi
     // device's resident capacity below.
     Geometry g = time_lanes ? time_geometry(p, ccv::kTcTilesBwd)
                             : geometry(p, vec, ccv::kWavesPerBlock, 1, 0, 0,
-                                       CCV_BWD_TARGET_WAVES, CCV_BWD_MIN_CHUNK);
+                                       det_target_waves(p, vec), CCV_BWD_MIN_CHUNK);
     if (!time_lanes)
         add_tail(g, p, ccv::kWavesPerBlock, CCV_BWD_TAIL_PCT, CCV_BWD_TAIL_CHUNK, 1);
     // packed rows on time lanes: the boundary repair's partial rows follow
