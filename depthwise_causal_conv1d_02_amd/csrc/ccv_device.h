@@ -2668,7 +2668,10 @@ __global__ __launch_bounds__(256) void k_validate(const int32_t *cu, int64_t n_s
 // when the element count is a multiple of 4; else V = 1), a block 64 lanes'
 // columns.  Each lane issues the loads of 8 partials per group (32 loads)
 // before it adds any, so a block keeps its whole share of the partials in
-// flight at once.
+// flight at once; a last partial round (P not a multiple of 128) loads from
+// indices clamped into range and adds only the partials that exist.  The
+// lane's dweight/dbias values are read before the partials, so that their
+// update does not wait for one more memory round trip.
 //
 // `err` is the packed call's flag word (nullptr for dense rows).  When it is
 // non-zero the backward blocks wrote no partials, so the reduction adds
@@ -2699,6 +2702,22 @@ void k_dw_reduce(const float *part, int64_t n_part,
     const int lane = threadIdx.x % kWaveSize, wave = threadIdx.x / kWaveSize;
     const int64_t n_vec = n_ch * kp / V;
     const int64_t c = static_cast<int64_t>(blockIdx.x) * kWaveSize + lane;
+    // wave 0 writes the sums: element e = c*V + i is (channel e / kp, tap e % kp)
+    float *dst[V];
+    float old[V];
+    if (wave == 0 && c < n_vec) {
+        int64_t ch = c * V / kp;
+        int k = static_cast<int>(c * V - ch * kp);
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            dst[i] = k < w ? dw + ch * w + k : db + ch;
+            old[i] = *dst[i];
+            if (++k == kp) {
+                k = 0;
+                ++ch;
+            }
+        }
+    }
     T acc[kAcc];
 #pragma unroll
     for (int j = 0; j < kAcc; ++j) acc[j] = T{};
@@ -2717,12 +2736,21 @@ void k_dw_reduce(const float *part, int64_t n_part,
 #pragma unroll
                 for (int j = 0; j < kAcc; ++j) acc[j] += v[u][j];
         }
-        for (; p0 < n_part; p0 += kGroups) {
+        if (p0 < n_part) {
+            // the last, partial round: same order, absent partials skipped
+            T v[kUnroll][kAcc];
 #pragma unroll
-            for (int j = 0; j < kAcc; ++j) {
-                const int64_t p = p0 + wave * kAcc + j;
-                if (p < n_part) acc[j] += col[p * n_vec];
-            }
+            for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+                for (int j = 0; j < kAcc; ++j) {
+                    const int64_t p = p0 + u * kGroups + wave * kAcc + j;
+                    v[u][j] = col[(p < n_part ? p : n_part - 1) * n_vec];
+                }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+                for (int j = 0; j < kAcc; ++j)
+                    if (p0 + u * kGroups + wave * kAcc + j < n_part) acc[j] += v[u][j];
         }
     }
 #pragma unroll
@@ -2734,14 +2762,10 @@ void k_dw_reduce(const float *part, int64_t n_part,
     for (int q = 0; q < kGroups; ++q) sum += s_acc[q][lane];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
-        const int64_t e = c * V + i;
-        const int64_t ch = e / kp;
-        const int k = static_cast<int>(e % kp);
         float v;
         if constexpr (V == 1) v = sum;
         else v = sum[i];
-        if (k < w) dw[ch * w + k] += v;
-        else db[ch] += v;
+        *dst[i] = old[i] + v;
     }
 }
 
