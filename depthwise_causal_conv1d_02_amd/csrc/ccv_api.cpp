@@ -68,6 +68,15 @@
 #ifndef CCV_BWD_ROUNDS
 #define CCV_BWD_ROUNDS 1
 #endif
+// Blocks per CU counted in the atomic backward's round (dense and seq_idx
+// rows; 0: as many as fit).  The width-4 kernels fit 2 (two waves per SIMD);
+// narrower filters need fewer registers and fit 3, and a round of 3 blocks
+// per CU (shorter chunks) measured slower: widths 3 and 2 on the dense
+// shape 41.9 -> 40.7 and 40.8 -> 39.8 us with the cap, seq_idx rows 46.7 ->
+// 45.8 us, width 4 unchanged.  Packed rows keep 3 (measured best there).
+#ifndef CCV_BWD_ROUND_BLOCKS_PER_CU
+#define CCV_BWD_ROUND_BLOCKS_PER_CU 2
+#endif
 #ifndef CCV_FWD_VEC
 #define CCV_FWD_VEC 8
 #endif
@@ -715,8 +724,11 @@ int bwd_call(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bi
     const int silu = activation == CCV_ACT_SILU;
     const int rounds = p.packed ? CCV_BWD_PACKED_ROUNDS : CCV_BWD_ROUNDS;
     if (!use_partials && rounds > 0 && !time_lanes) {
-        g = geometry(p, vec, ccv::kWavesPerBlock, 1, ccv::bwd_resident_blocks(a, vec, silu, p.rows()),
-                     rounds, CCV_BWD_TARGET_WAVES, CCV_BWD_MIN_CHUNK);
+        int64_t cap = ccv::bwd_resident_blocks(a, vec, silu, p.rows());
+        if (CCV_BWD_ROUND_BLOCKS_PER_CU > 0 && !p.packed)
+            cap = std::min<int64_t>(cap, ccv::device_cus() * CCV_BWD_ROUND_BLOCKS_PER_CU);
+        g = geometry(p, vec, ccv::kWavesPerBlock, 1, cap, rounds, CCV_BWD_TARGET_WAVES,
+                     CCV_BWD_MIN_CHUNK);
         add_tail(g, p, ccv::kWavesPerBlock, CCV_BWD_TAIL_PCT, CCV_BWD_TAIL_CHUNK, 1);
     }
     a.B = p.B;

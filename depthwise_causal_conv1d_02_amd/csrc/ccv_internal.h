@@ -173,6 +173,7 @@ hipError_t launch_validate(const int32_t *cu, int64_t n_seq, int64_t total, uint
 hipError_t launch_dw_reduce(const float *partial, int64_t n_part, int64_t n_ch, int w, int kp,
                             float *dw, float *db, const uint32_t *err, hipStream_t s);
 int64_t resident_blocks(const void *kernel, unsigned dyn_lds);
+int64_t device_cus();  // compute units of the current device (0 if unknown)
 
 // Bytes of the per-device scratch behind ccv_bwd_noalloc (CCV_NOALLOC_SCRATCH_BYTES),
 // and the device address of that scratch on the current device (ccv_misc.hip).

@@ -46,6 +46,14 @@ hipError_t noalloc_scratch(void **ptr) {
 
 // Resident blocks of a kernel on the current device (CUs x blocks per CU),
 // from the occupancy the compiled kernel allows; 0 when it cannot be told.
+int64_t device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    return cus;
+}
+
 int64_t resident_blocks(const void *kernel, unsigned dyn_lds) {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
