@@ -795,6 +795,12 @@ MULTI_CASES = [
     (3, 40, 6, 4, True, BF16, "cl"),       # D % 8 != 0: one-channel lanes
     (2, 64, 7, 4, True, BF16, "tc"),       # [B,D,L] contiguous: one-channel lanes
     (5, 256, 1, 4, True, BF16, "cl"),      # L = 1 through the [B,D,L] form
+    # token batches of 8 on 8-channel lanes: exactly one, two and a token,
+    # three with other widths and filters
+    (3, 512, 8, 4, True, BF16, "cl"),
+    (2, 256, 17, 4, True, BF16, "cl"),
+    (2, 128, 24, 3, False, F32, "cl"),
+    (4, 64, 8, 2, False, BF16, "cl"),
 ]
 
 
