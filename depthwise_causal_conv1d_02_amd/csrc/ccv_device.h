@@ -1233,12 +1233,40 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // A lane's kTcE tokens from t on a unit-stride row; the tokens at or past
-// `end` read as zeros.  Whole vectors when they fit (the host has checked
-// 16-byte aligned row starts).
+// `end` read as zeros.  `align` is the byte alignment (16, 8, 4 or 2) the
+// host found common to every row start of every tensor of the call; t is a
+// multiple of kTcE, so a lane's tokens start at that alignment too and are
+// moved in the widest pieces it allows: one 16-byte vector, two 8-byte or
+// four 4-byte pieces, or single tokens.
+template <typename V, bool NT>
+__device__ __forceinline__ V tc_piece_load(const uint16_t *p) {
+    const V *q = reinterpret_cast<const V *>(p);
+    if constexpr (NT && CCV_NT_LOAD) return __builtin_nontemporal_load(q);
+    else return *q;
+}
+template <typename V, bool NT>
+__device__ __forceinline__ void tc_piece_store(uint16_t *p, V v) {
+    V *q = reinterpret_cast<V *>(p);
+    if constexpr (NT && CCV_NT_STORE) __builtin_nontemporal_store(v, q);
+    else *q = v;
+}
+
 template <bool NTL>
-__device__ __forceinline__ Raw<8> tc_load(const uint16_t *row, int64_t t, int64_t end) {
-    if (t + kTcE <= end) return load_raw<8, NTL>(row + t, 1);
+__device__ __forceinline__ Raw<8> tc_load(const uint16_t *row, int64_t t, int64_t end,
+                                          int align) {
     Raw<8> r;
+    if (t + kTcE <= end && align >= 4) {
+        if (align >= 16) return load_raw<8, NTL>(row + t, 1);
+        if (align >= 8) {
+            const u32x2_t a = tc_piece_load<u32x2_t, NTL>(row + t);
+            const u32x2_t b = tc_piece_load<u32x2_t, NTL>(row + t + 4);
+            r.v = u32x4_t{a[0], a[1], b[0], b[1]};
+            return r;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.v[i] = tc_piece_load<uint32_t, NTL>(row + t + 2 * i);
+        return r;
+    }
     r.v = u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < kTcE; ++i)
@@ -1248,14 +1276,27 @@ __device__ __forceinline__ Raw<8> tc_load(const uint16_t *row, int64_t t, int64_
 
 template <bool STREAM>
 __device__ __forceinline__ void tc_store(uint16_t *row, int64_t t, int64_t end,
-                                         const float (&v)[kTcE]) {
-    if (t + kTcE <= end) {
-        store_vec<8, STREAM>(row + t, 1, v);
-    } else {
+                                         const float (&v)[kTcE], int align) {
+    if (t + kTcE <= end && align >= 4) {
+        if (align >= 16) {
+            store_vec<8, STREAM>(row + t, 1, v);
+            return;
+        }
+        uint32_t w[4];
 #pragma unroll
-        for (int i = 0; i < kTcE; ++i)
-            if (t + i < end) row[t + i] = to_bf16_bits(v[i]);
+        for (int i = 0; i < 4; ++i) w[i] = pack2_bf16(v[2 * i], v[2 * i + 1]);
+        if (align >= 8) {
+            tc_piece_store<u32x2_t, STREAM>(row + t, u32x2_t{w[0], w[1]});
+            tc_piece_store<u32x2_t, STREAM>(row + t + 4, u32x2_t{w[2], w[3]});
+            return;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tc_piece_store<uint32_t, STREAM>(row + t + 2 * i, w[i]);
+        return;
     }
+#pragma unroll
+    for (int i = 0; i < kTcE; ++i)
+        if (t + i < end) row[t + i] = to_bf16_bits(v[i]);
 }
 
 // Single extended tokens of one row (b, d): x_ext at p < T is the input for
@@ -1341,7 +1382,7 @@ __device__ __forceinline__ void fwd_tc_chunk(const FwdArgs &a, const TcItem &it,
 #pragma unroll
     for (int c = 0; c < kTcTilesFwd; ++c) {
         const int64_t t = it.t0 + c * kTcTile + lane * kTcE;
-        if (t < it.t1) raw[c] = tc_load<NTL>(xr, t, it.t1);
+        if (t < it.t1) raw[c] = tc_load<NTL>(xr, t, it.t1, a.tc_align);
         else raw[c].v = u32x4_t{0u, 0u, 0u, 0u};
     }
     if (!check.ok()) return;
@@ -1367,7 +1408,7 @@ __device__ __forceinline__ void fwd_tc_chunk(const FwdArgs &a, const TcItem &it,
             out[i] = act<SILU>(z);
         }
         const int64_t t = tt + lane * kTcE;
-        if (t < it.t1) tc_store<true>(yr, t, it.t1, out);
+        if (t < it.t1) tc_store<true>(yr, t, it.t1, out, a.tc_align);
 #pragma unroll
         for (int j = 0; j < W - 1; ++j) carry[j] = from_lane(v[kTcE - (W - 1) + j], kWaveSize - 1);
     }
@@ -1424,8 +1465,8 @@ __device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it,
     for (int c = 0; c < kTcTilesBwd; ++c) {
         const int64_t t = it.t0 + c * kTcTile + lane * kTcE;
         if (t < it.t1) {
-            rx[c] = tc_load<NTL>(xr, t, it.t1);
-            rd[c] = tc_load<NTL>(dyr, t, it.t1);
+            rx[c] = tc_load<NTL>(xr, t, it.t1, a.tc_align);
+            rd[c] = tc_load<NTL>(dyr, t, it.t1, a.tc_align);
         } else {
             rx[c].v = u32x4_t{0u, 0u, 0u, 0u};
             rd[c].v = u32x4_t{0u, 0u, 0u, 0u};
@@ -1470,7 +1511,7 @@ __device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it,
                     if (m == j) v[i] += dfv[j];
             }
         }
-        if (t < it.t1) tc_store<true>(dxr, t, it.t1, v);
+        if (t < it.t1) tc_store<true>(dxr, t, it.t1, v, a.tc_align);
     };
 
     float gprev[kTcE];
@@ -1670,7 +1711,7 @@ __device__ __forceinline__ void fwd_tcs_chunk(const FwdArgs &a, const TcItem &it
 #pragma unroll
     for (int c = 0; c < kTcTilesFwd; ++c) {
         const int64_t t = it.t0 + c * kTcTile + lane * kTcE;
-        if (t < it.t1) raw[c] = tc_load<NTL>(xr, t, it.t1);
+        if (t < it.t1) raw[c] = tc_load<NTL>(xr, t, it.t1, a.tc_align);
         else raw[c].v = u32x4_t{0u, 0u, 0u, 0u};
         ids.lane_ids(t < it.t1 ? t : a.T, tid[c]);
     }
@@ -1706,7 +1747,7 @@ __device__ __forceinline__ void fwd_tcs_chunk(const FwdArgs &a, const TcItem &it
             for (int k = 0; k < W; ++k) z = fmaf(w[k][0], xv[k], z);
             out[i] = act<SILU>(z);
         }
-        if (t < it.t1) tc_store<true>(yr, t, it.t1, out);
+        if (t < it.t1) tc_store<true>(yr, t, it.t1, out, a.tc_align);
 #pragma unroll
         for (int j = 0; j < W - 1; ++j) {
             carry[j] = from_lane(v[kTcE - (W - 1) + j], kWaveSize - 1);
@@ -1745,8 +1786,8 @@ __device__ __forceinline__ void bwd_tcs_chunk(const BwdArgs &a, const TcItem &it
     for (int c = 0; c < kTcTilesBwd; ++c) {
         const int64_t t = it.t0 + c * kTcTile + lane * kTcE;
         if (t < it.t1) {
-            rx[c] = tc_load<NTL>(xr, t, it.t1);
-            rd[c] = tc_load<NTL>(dyr, t, it.t1);
+            rx[c] = tc_load<NTL>(xr, t, it.t1, a.tc_align);
+            rd[c] = tc_load<NTL>(dyr, t, it.t1, a.tc_align);
         } else {
             rx[c].v = u32x4_t{0u, 0u, 0u, 0u};
             rd[c].v = u32x4_t{0u, 0u, 0u, 0u};
@@ -1789,7 +1830,7 @@ __device__ __forceinline__ void bwd_tcs_chunk(const BwdArgs &a, const TcItem &it
                 acc = fmaf(w[W - 1 - j][0], ige[i + j] == own ? ge[i + j] : 0.0f, acc);
             v[i] = acc;
         }
-        if (t < it.t1) tc_store<true>(dxr, t, it.t1, v);
+        if (t < it.t1) tc_store<true>(dxr, t, it.t1, v, a.tc_align);
     };
 
     float gprev[kTcE];

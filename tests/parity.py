@@ -142,16 +142,17 @@ def _fill(storage):
     return storage
 
 
-def guarded_act(B, D, T, layout, device, dtype=torch.bfloat16):
+def guarded_act(B, D, T, layout, device, dtype=torch.bfloat16, aligned=True):
     """[B,D,T] output with the given layout ('cl' = [B,T,D] storage viewed
-    through transpose, 'tc' = [B,D,T]); pads keep 16-byte alignment."""
+    through transpose, 'tc' = [B,D,T]); pads keep 16-byte alignment, unless
+    `aligned` is false ('tc' only: rows then start T + 16 tokens apart)."""
     if layout == "cl":
         st = _fill(torch.empty(B, T + 2, D + 16, dtype=dtype, device=device))
         view = st[:, 1:1 + T, 8:8 + D].transpose(1, 2)
     else:
         # rows padded to a multiple of 8 tokens, so that every row starts on
-        # a 16-byte boundary (what the time-lane kernels need of an output)
-        Tp = (T + 7) // 8 * 8
+        # a 16-byte boundary (the widest pieces the time lanes move)
+        Tp = (T + 7) // 8 * 8 if aligned else T
         st = _fill(torch.empty(B, D + 2, Tp + 16, dtype=dtype, device=device))
         view = st[:, 1:1 + D, 8:8 + T]
     return Guarded(st, view)

@@ -793,7 +793,7 @@ MULTI_CASES = [
     (2, 64, 2, 3, True, BF16, "cl"),
     (2, 64, 9, 2, True, F32, "cl"),
     (3, 40, 6, 4, True, BF16, "cl"),       # D % 8 != 0: one-channel lanes
-    (2, 64, 7, 4, True, BF16, "tc"),       # [B,D,L] contiguous: one-channel lanes
+    (2, 64, 7, 4, True, BF16, "tc"),       # [B,D,L] contiguous (unit token stride): one-channel lanes
     (5, 256, 1, 4, True, BF16, "cl"),      # L = 1 through the [B,D,L] form
     # token batches of 8 on 8-channel lanes: exactly one, two and a token,
     # three with other widths and filters
@@ -831,11 +831,68 @@ def test_update_several_tokens(B, D, L, W, bias, wdt, layout):
     check_exact_bf16("conv_state after", g_state, ost)
 
 
+@pytest.mark.parametrize("T,D", [(93, 24), (126, 16), (100, 40), (2049, 8), (1030, 16)],
+                         ids=["align2", "align4", "align8", "align2-long", "align4-long"])
+def test_time_lanes_unaligned_rows(T, D):
+    """[B,D,T]-contiguous activations whose rows start on 2-, 4- or 8-byte
+    boundaries (T odd, T = 2 mod 4, T = 4 mod 8), outputs in unpadded
+    storage too: the time lanes move a lane's 8 tokens in pieces of that
+    width.  Forward with initial and final states, backward with dfinal and
+    dinit, on both dW routes."""
+    for det in (False, True):
+        inp, g = inputs(2400 + T + det, 2, D, T, "tc", True, True, BF16, True)
+        assert g["x"].stride() == (D * T, T, 1)
+        opts = OPT_DETDB if det else 0
+        y = guarded_act(2, D, T, "tc", DEV, aligned=False)
+        fin = guarded_flat((2, D, 3), DEV)
+        ops.fwd(g["x"], g["weight"], g["bias"], None, g["initial_states"], "silu",
+                final_states_out=fin.view, y=y.view, options=opts)
+        torch.cuda.synchronize()
+        check_fwd(inp, y, fin, "silu")
+        dx = guarded_act(2, D, T, "tc", DEV, aligned=False)
+        _, dw, db, dinit = ops.bwd(g["x"], g["weight"], g["dy"], g["bias"], None,
+                                   g["initial_states"], g["dfinal_states"], "silu", det, False,
+                                   dx=dx.view, options=opts)
+        torch.cuda.synchronize()
+        check_bwd(inp, dx, dw, db, dinit, "silu")
+
+
+def test_one_channel_lanes_packed_and_seq_idx():
+    """Channel-last inputs with an odd channel count take the one-channel
+    lanes: packed rows and seq_idx rows, forward and backward."""
+    lengths = [5, 1, 40, 3, 77]
+    cu = synth.cu_from_lengths(lengths)
+    T = int(cu[-1])
+    inp, g = inputs(2300, 1, 13, T, "cl", True, True, BF16, True, cu)
+    ops.reset_flag(DEV)
+    y, fin = run_fwd(g, "cl", "silu", True, cu)
+    check_fwd(inp, y, fin, "silu")
+    dx, dw, db, dinit = run_bwd(g, "cl", "silu", False, cu)
+    check_bwd(inp, dx, dw, db, dinit, "silu")
+    ops.check_flag(DEV)
+    inp, g = inputs(2301, 2, 13, 93, "cl", True, False, BF16)
+    seq = synth.seq_idx_tensor(torch.Generator().manual_seed(2302), 2, 93, "random")
+    y = guarded_act(2, 13, 93, "cl", DEV)
+    ops.fwd(g["x"], g["weight"], g["bias"], None, None, "silu", y=y.view, seq_idx=dev(seq))
+    dx = guarded_act(2, 13, 93, "cl", DEV)
+    _, dw, db, _ = ops.bwd(g["x"], g["weight"], g["dy"], g["bias"], None, None, None, "silu",
+                           False, False, dx=dx.view, seq_idx=dev(seq))
+    torch.cuda.synchronize()
+    oy = oracle.fwd_seq(f64(inp["x"]), f64(inp["weight"]), seq.numpy(), f64(inp["bias"]), "silu")
+    odx, odw, odb = oracle.bwd_seq(f64(inp["x"]), f64(inp["weight"]), f64(inp["dy"]),
+                                   seq.numpy(), f64(inp["bias"]), "silu")
+    check_bf16("y", y.view, oy)
+    check_bf16("dx", dx.view, odx)
+    check_f32_rel("dweight", dw, odw)
+    check_f32_rel("dbias", db, odb)
+    assert y.intact() and dx.intact()
+
+
 @pytest.mark.parametrize("padded", [False, True], ids=["unaligned-rows", "aligned-rows"])
 def test_packed_and_seq_idx_time_contiguous_layout(padded):
     """Packed offsets and seq_idx ids on a [B,D,T]-contiguous input: rows
-    that do not start on 16-byte boundaries take the one-channel lanes, rows
-    that do (padded storage) the time lanes.  Forward and backward against
+    that start on 4- or 2-byte boundaries (T = 126, T = 93) and rows padded
+    to 16-byte boundaries, on the time lanes.  Forward and backward against
     the oracle."""
     lengths = [5, 1, 40, 3, 77]
     cu = synth.cu_from_lengths(lengths)
