@@ -32,6 +32,8 @@ input already resident in HBM:
                     and the deterministic dweight and dbias (opt-in).
   decode_tokens     the decode shape, 64 tokens as 8 multi-token updates of
                     8 tokens each.
+  dense_odd_tc      the dense workload at T=2047 in [B,D,T] storage: rows that
+                    start on 2-byte boundaries only.
 
 The value is algorithmic bytes (every compulsory input read once, every output
 written once) per step divided by the wall time per step.  Per-op times come
@@ -57,7 +59,8 @@ METRIC = "achieved HBM GB/s (% of MI355X peak) for fwd, bwd and update at 1 GPU"
 
 WORKLOADS = ["large_decode", "dense", "packed", "decode", "large", "tiny", "seqidx",
              "dense_tc", "large_tc", "packed_tc", "seqidx_tc",
-             "dense_w2", "dense_w3", "dense_noact", "dense_f32bias", "decode_tokens"]
+             "dense_w2", "dense_w3", "dense_noact", "dense_f32bias", "decode_tokens",
+             "dense_odd_tc"]
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "depthwise_causal_conv1d_02_amd", "csrc")
 OP_KERNEL = {"fwd": "k_fwd_chan", "bwd": "k_bwd_chan", "update": "k_update"}
@@ -161,6 +164,8 @@ WORKLOAD_BYTES = {
                     "bwd": bwd_bytes(4, 4096, 2048, 4, True, False, 2, True)},
     "dense_f32bias": {"fwd": fwd_bytes(4, 4096, 2048, 4, True, True, 4, True, b_bytes=4),
                       "bwd": bwd_bytes(4, 4096, 2048, 4, True, False, 4, True, b_bytes=4)},
+    "dense_odd": {"fwd": fwd_bytes(4, 4096, 2047, 4, True, True, 2, True),
+                  "bwd": bwd_bytes(4, 4096, 2047, 4, True, False, 2, True)},
     "decode_tokens": {"update": update_tokens_bytes(256, 8192, 8, 2, True)},
 }
 

@@ -198,6 +198,8 @@ VARIANTS = {
     "dense_f32bias": "dense fwd+bwd with state, fp32 weight + fp32 bias (opt-in): B=4 D=4096 "
                      "T=2048, channel-last, initial_states, SiLU, final_states returned, "
                      "deterministic dweight and dbias (opt-in)",
+    "dense_odd": "dense fwd+bwd with state, an odd length: B=4 D=4096 T=2047, channel-last, "
+                 "bf16 weight+bias, initial_states, SiLU, final_states returned",
     "decode_tokens": "multi-token decode update: B=256 D=8192, 64 tokens as 8 calls of 8 "
                      "tokens ([B,D,8] over [B,8,D] storage), bf16 weight+bias, SiLU, state "
                      "mutated in place",
@@ -213,7 +215,7 @@ def variant(name):
         return dict(conv_state=_normal(g, (B, D, 3)),
                     x_calls=_normal(g, (calls, B, L, D)).transpose(2, 3),
                     weight=weight_tensor(g, D), bias=bias_tensor(g, D), activation="silu")
-    B, D, T = 4, 4096, 2048
+    B, D, T = 4, 4096, 2047 if name == "dense_odd" else 2048
     W = {"dense_w2": 2, "dense_w3": 3}.get(name, 4)
     f32 = name == "dense_f32bias"
     dt = torch.float32 if f32 else BF16
