@@ -246,27 +246,27 @@ int pick_vec(int preferred, const ccv_tensor *weight, const ccv_tensor *bias,
     return 1;
 }
 
-// Byte alignment (16, 8, 4 or 2) common to every row start (b, d) of a
-// [B,D,T] BF16 tensor.
-int row_align(const ccv_tensor *t) {
-    uint64_t bits = static_cast<uint64_t>(reinterpret_cast<uintptr_t>(t->data)) | 16u;
-    if (t->shape[0] > 1) bits |= static_cast<uint64_t>(t->stride[0]) * 2;
-    if (t->shape[1] > 1) bits |= static_cast<uint64_t>(t->stride[1]) * 2;
-    return static_cast<int>(bits & (~bits + 1));  // the lowest set bit
-}
-
 // Time lanes (lanes along T): every activation tensor has unit time stride
-// and rows that are not channel-contiguous (dense, packed or seq_idx rows).
-// Returns the byte alignment common to all their row starts, the widest
-// piece a lane moves at once, or 0 for channel lanes.
-int time_lanes_align(const ccv_tensor *a, const ccv_tensor *b, const ccv_tensor *c) {
-    int align = 16;
+// and rows that are not channel-contiguous (dense, packed or seq_idx rows),
+// at any row alignment (each wave moves its rows' tokens in the widest
+// pieces their starts allow).
+bool time_lanes_ok(const ccv_tensor *a, const ccv_tensor *b, const ccv_tensor *c) {
     for (const ccv_tensor *t : {a, b, c}) {
         if (t == nullptr) continue;
-        if (t->stride[2] != 1 || (t->stride[1] == 1 && t->shape[1] > 1)) return 0;
-        align = std::min(align, row_align(t));
+        if (t->stride[2] != 1 || (t->stride[1] == 1 && t->shape[1] > 1)) return false;
     }
-    return align;
+    return true;
+}
+
+// Every row start of these tensors is 16-byte aligned.
+bool rows_aligned16(const ccv_tensor *a, const ccv_tensor *b, const ccv_tensor *c) {
+    for (const ccv_tensor *t : {a, b, c}) {
+        if (t == nullptr) continue;
+        if (!aligned16(t->data) || (t->shape[0] > 1 && t->stride[0] % 8 != 0) ||
+            (t->shape[1] > 1 && t->stride[1] % 8 != 0))
+            return false;
+    }
+    return true;
 }
 
 ccv::Strided3 s3(const ccv_tensor *t) {
@@ -539,8 +539,7 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
                         span_of(initial_states), span_of(seq_idx)};
     if (any_alias(outs, 3, ins, 6)) return CCV_ERR_ALIAS;
 
-    const int tc_align = time_lanes_align(x, y, nullptr);
-    const bool time_lanes = tc_align > 0;
+    const bool time_lanes = time_lanes_ok(x, y, nullptr);
     const bool pipe = p.B * p.D * p.T * 2 >= CCV_FWD_PIPE_MIN_BYTES;
     const int64_t groups8 = (p.D + ccv::kWaveSize * 8 - 1) / (ccv::kWaveSize * 8);
     const bool small_dense = !p.packed && (!p.seq || CCV_FWD_SMALL_SEQ) && !pipe &&
@@ -599,7 +598,7 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     a.n_tblk_t = gs.n_tblk_t;
     a.n_block_m = gs.n_block_m;
     if (time_lanes) set_tc_div(a);
-    a.tc_align = tc_align;
+    a.tc_vec16 = time_lanes && rows_aligned16(x, y, nullptr);
     set_validation(a, p, time_lanes);
     a.nt_load = p.B * p.D * p.T * 2 >=
                 (p.seq ? CCV_NT_LOAD_MIN_BYTES_SEQ : CCV_NT_LOAD_MIN_BYTES);
@@ -661,8 +660,7 @@ int bwd_call(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bi
         }
     }
     const int64_t kp = p.W + (present(bias) ? 1 : 0);  // partial columns per channel
-    const int tc_align = time_lanes_align(x, dy, dx);
-    const bool time_lanes = tc_align > 0;
+    const bool time_lanes = time_lanes_ok(x, dy, dx);
     const int vec = time_lanes ? ccv::kVecTime : pick_vec(CCV_BWD_VEC, weight, bias, x, dy, dx);
     // The partials of the deterministic route depend on the shape only (a
     // grid sized by target waves); the atomic route sizes its grid by the
@@ -759,7 +757,7 @@ int bwd_call(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bi
     a.n_tblk_t = g.n_tblk_t;
     a.n_block_m = g.n_block_m;
     if (time_lanes) set_tc_div(a);
-    a.tc_align = tc_align;
+    a.tc_vec16 = time_lanes && rows_aligned16(x, dy, dx);
     set_validation(a, p, time_lanes);
 
     if (p.packed && !a.cu_in_lds && !a.cu_in_wave) {

@@ -1233,22 +1233,21 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // A lane's kTcE tokens from t on a unit-stride row; the tokens at or past
-// `end` read as zeros.  `align` is the byte alignment (16, 8, 4 or 2) the
-// host found common to every row start of every tensor of the call; t is a
-// multiple of kTcE, so a lane's tokens start at that alignment too and are
-// moved in the widest pieces it allows: one 16-byte vector, two 8-byte or
-// four 4-byte pieces, or single tokens.
-template <typename V, bool NT>
-__device__ __forceinline__ V tc_piece_load(const uint16_t *p) {
-    const V *q = reinterpret_cast<const V *>(p);
-    if constexpr (NT && CCV_NT_LOAD) return __builtin_nontemporal_load(q);
-    else return *q;
-}
-template <typename V, bool NT>
-__device__ __forceinline__ void tc_piece_store(uint16_t *p, V v) {
-    V *q = reinterpret_cast<V *>(p);
-    if constexpr (NT && CCV_NT_STORE) __builtin_nontemporal_store(v, q);
-    else *q = v;
+// `end` read as zeros.  `align` is the byte alignment of the row's start
+// (tc_align: 16, 4 or 2); t is a multiple of kTcE, so a lane's tokens start
+// at that alignment too.  16: one aligned 16-byte
+// vector; 4: one 16-byte access at 4-byte alignment (the memory pipeline
+// takes dword-aligned vectors); 2: a load of the token before and the
+// first 7 (dword-aligned) plus one of the last token, shifted into place by
+// two bytes, and a store of the first token, the next six (three dwords)
+// and the last.  The lane that starts a row reads its tokens one by one (no
+// token before the row is read).
+typedef uint32_t u32x4_a4_t __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x3_a4_t __attribute__((ext_vector_type(3), aligned(4)));
+
+__device__ __forceinline__ int tc_align(const uint16_t *row) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(row);
+    return (a & 15u) == 0 ? 16 : (a & 3u) == 0 ? 4 : 2;
 }
 
 template <bool NTL>
@@ -1257,14 +1256,29 @@ __device__ __forceinline__ Raw<8> tc_load(const uint16_t *row, int64_t t, int64_
     Raw<8> r;
     if (t + kTcE <= end && align >= 4) {
         if (align >= 16) return load_raw<8, NTL>(row + t, 1);
-        if (align >= 8) {
-            const u32x2_t a = tc_piece_load<u32x2_t, NTL>(row + t);
-            const u32x2_t b = tc_piece_load<u32x2_t, NTL>(row + t + 4);
-            r.v = u32x4_t{a[0], a[1], b[0], b[1]};
-            return r;
+        const u32x4_a4_t *q = reinterpret_cast<const u32x4_a4_t *>(row + t);
+        u32x4_a4_t v;
+        if constexpr (NTL && CCV_NT_LOAD) v = __builtin_nontemporal_load(q);
+        else v = *q;
+        r.v = u32x4_t{v[0], v[1], v[2], v[3]};
+        return r;
+    }
+    if (t + kTcE <= end && t > 0) {
+        // 2-byte rows: tokens t-1 .. t+6 from the dword boundary before t
+        const u32x4_a4_t *q = reinterpret_cast<const u32x4_a4_t *>(row + t - 1);
+        u32x4_a4_t v;
+        uint32_t last;
+        if constexpr (NTL && CCV_NT_LOAD) {
+            v = __builtin_nontemporal_load(q);
+            last = __builtin_nontemporal_load(row + t + kTcE - 1);
+        } else {
+            v = *q;
+            last = row[t + kTcE - 1];
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) r.v[i] = tc_piece_load<uint32_t, NTL>(row + t + 2 * i);
+        r.v = u32x4_t{__builtin_amdgcn_alignbyte(v[1], v[0], 2),
+                      __builtin_amdgcn_alignbyte(v[2], v[1], 2),
+                      __builtin_amdgcn_alignbyte(v[3], v[2], 2),
+                      __builtin_amdgcn_alignbyte(last, v[3], 2)};
         return r;
     }
     r.v = u32x4_t{0u, 0u, 0u, 0u};
@@ -1282,16 +1296,28 @@ __device__ __forceinline__ void tc_store(uint16_t *row, int64_t t, int64_t end,
             store_vec<8, STREAM>(row + t, 1, v);
             return;
         }
-        uint32_t w[4];
+        u32x4_a4_t w;
 #pragma unroll
         for (int i = 0; i < 4; ++i) w[i] = pack2_bf16(v[2 * i], v[2 * i + 1]);
-        if (align >= 8) {
-            tc_piece_store<u32x2_t, STREAM>(row + t, u32x2_t{w[0], w[1]});
-            tc_piece_store<u32x2_t, STREAM>(row + t + 4, u32x2_t{w[2], w[3]});
-            return;
+        u32x4_a4_t *q = reinterpret_cast<u32x4_a4_t *>(row + t);
+        if constexpr (STREAM && CCV_NT_STORE) __builtin_nontemporal_store(w, q);
+        else *q = w;
+        return;
+    }
+    if (t + kTcE <= end) {
+        // 2-byte rows: token t, tokens t+1 .. t+6 (dword-aligned), token t+7
+        const u32x3_a4_t mid = {pack2_bf16(v[1], v[2]), pack2_bf16(v[3], v[4]),
+                                pack2_bf16(v[5], v[6])};
+        u32x3_a4_t *q = reinterpret_cast<u32x3_a4_t *>(row + t + 1);
+        if constexpr (STREAM && CCV_NT_STORE) {
+            __builtin_nontemporal_store(to_bf16_bits(v[0]), row + t);
+            __builtin_nontemporal_store(mid, q);
+            __builtin_nontemporal_store(to_bf16_bits(v[kTcE - 1]), row + t + kTcE - 1);
+        } else {
+            row[t] = to_bf16_bits(v[0]);
+            *q = mid;
+            row[t + kTcE - 1] = to_bf16_bits(v[kTcE - 1]);
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) tc_piece_store<uint32_t, STREAM>(row + t + 2 * i, w[i]);
         return;
     }
 #pragma unroll
@@ -1360,13 +1386,28 @@ struct TcNoCheck {
     __device__ __forceinline__ bool ok() const { return true; }
 };
 
-template <int W, bool SILU, int FK, bool NTL, typename Check>
+// Runs f(ntl, a16) with the call's cache policy for the bulk loads and
+// whether every row start of every tensor is 16-byte aligned (then the
+// tiles move as whole vectors with no alignment test in the kernel).
+template <typename A, typename F>
+__device__ __forceinline__ void tc_run(const A &a, F &&f) {
+    if (a.tc_vec16) {
+        if (a.nt_load) f(std::true_type{}, std::true_type{});
+        else f(std::false_type{}, std::true_type{});
+    } else {
+        if (a.nt_load) f(std::true_type{}, std::false_type{});
+        else f(std::false_type{}, std::false_type{});
+    }
+}
+
+template <int W, bool SILU, int FK, bool NTL, bool A16, typename Check>
 __device__ __forceinline__ void fwd_tc_chunk(const FwdArgs &a, const TcItem &it,
                                              const Check &check) {
     const int lane = threadIdx.x % kWaveSize;
     const uint16_t *xr = static_cast<const uint16_t *>(a.x.ptr) + it.b * a.x.s0 + it.d * a.x.s1;
     uint16_t *yr = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.y.ptr)) +
                    it.b * a.y.s0 + it.d * a.y.s1;
+    const int ax = A16 ? 16 : tc_align(xr), ay = A16 ? 16 : tc_align(yr);
     // Left halo, the final state's tokens (lanes 0..W-2 of the chunk that
     // ends the row copy the row's last W-1 extended tokens bit for bit; the
     // other lanes repeat lane W-2's address), the filter, then the tiles.
@@ -1382,7 +1423,7 @@ __device__ __forceinline__ void fwd_tc_chunk(const FwdArgs &a, const TcItem &it,
 #pragma unroll
     for (int c = 0; c < kTcTilesFwd; ++c) {
         const int64_t t = it.t0 + c * kTcTile + lane * kTcE;
-        if (t < it.t1) raw[c] = tc_load<NTL>(xr, t, it.t1, a.tc_align);
+        if (t < it.t1) raw[c] = tc_load<NTL>(xr, t, it.t1, ax);
         else raw[c].v = u32x4_t{0u, 0u, 0u, 0u};
     }
     if (!check.ok()) return;
@@ -1408,7 +1449,7 @@ __device__ __forceinline__ void fwd_tc_chunk(const FwdArgs &a, const TcItem &it,
             out[i] = act<SILU>(z);
         }
         const int64_t t = tt + lane * kTcE;
-        if (t < it.t1) tc_store<true>(yr, t, it.t1, out, a.tc_align);
+        if (t < it.t1) tc_store<true>(yr, t, it.t1, out, ay);
 #pragma unroll
         for (int j = 0; j < W - 1; ++j) carry[j] = from_lane(v[kTcE - (W - 1) + j], kWaveSize - 1);
     }
@@ -1421,8 +1462,9 @@ template <int W, bool SILU, int FK>
 __global__ __launch_bounds__(256) void k_fwd_tc(FwdArgs a) {
     TcItem it;
     if (!tc_item(a, it)) return;
-    if (a.nt_load) fwd_tc_chunk<W, SILU, FK, true>(a, it, TcNoCheck{});
-    else fwd_tc_chunk<W, SILU, FK, false>(a, it, TcNoCheck{});
+    tc_run(a, [&](auto ntl, auto a16) {
+        fwd_tc_chunk<W, SILU, FK, decltype(ntl)::value, decltype(a16)::value>(a, it, TcNoCheck{});
+    });
 }
 
 // Backward on time lanes.  Per tile: z and g = dy * act'(z) for the lane's
@@ -1432,7 +1474,7 @@ __global__ __launch_bounds__(256) void k_fwd_tc(FwdArgs a) {
 // chunk's last tile the W-1 g's past the chunk are computed directly (the
 // right halo).  dW/dB: one wave sum per chunk, then an atomic or a unique
 // partial.
-template <int W, bool SILU, int FK, bool NTL, typename Check>
+template <int W, bool SILU, int FK, bool NTL, bool A16, typename Check>
 __device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it,
                                              const Check &check) {
     constexpr bool BIAS = fk_bias(FK);
@@ -1441,6 +1483,8 @@ __device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it,
     const uint16_t *dyr = static_cast<const uint16_t *>(a.dy.ptr) + it.b * a.dy.s0 + it.d * a.dy.s1;
     uint16_t *dxr = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.dx.ptr)) +
                     it.b * a.dx.s0 + it.d * a.dx.s1;
+    const int ax = A16 ? 16 : tc_align(xr), ady = A16 ? 16 : tc_align(dyr),
+              adx = A16 ? 16 : tc_align(dxr);
     // Single-token loads first, without branches (as in the forward): the
     // left halo; the right halo (lane j < W-1 reads token t1 + j of x and dy;
     // the other lanes, and tokens past the row, read an in-row token that is
@@ -1465,8 +1509,8 @@ __device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it,
     for (int c = 0; c < kTcTilesBwd; ++c) {
         const int64_t t = it.t0 + c * kTcTile + lane * kTcE;
         if (t < it.t1) {
-            rx[c] = tc_load<NTL>(xr, t, it.t1, a.tc_align);
-            rd[c] = tc_load<NTL>(dyr, t, it.t1, a.tc_align);
+            rx[c] = tc_load<NTL>(xr, t, it.t1, ax);
+            rd[c] = tc_load<NTL>(dyr, t, it.t1, ady);
         } else {
             rx[c].v = u32x4_t{0u, 0u, 0u, 0u};
             rd[c].v = u32x4_t{0u, 0u, 0u, 0u};
@@ -1511,7 +1555,7 @@ __device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it,
                     if (m == j) v[i] += dfv[j];
             }
         }
-        if (t < it.t1) tc_store<true>(dxr, t, it.t1, v, a.tc_align);
+        if (t < it.t1) tc_store<true>(dxr, t, it.t1, v, adx);
     };
 
     float gprev[kTcE];
@@ -1613,8 +1657,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CCV_TC_BWD_
 void k_bwd_tc(BwdArgs a) {
     TcItem it;
     if (!tc_item(a, it)) return;
-    if (a.nt_load) bwd_tc_chunk<W, SILU, FK, true>(a, it, TcNoCheck{});
-    else bwd_tc_chunk<W, SILU, FK, false>(a, it, TcNoCheck{});
+    tc_run(a, [&](auto ntl, auto a16) {
+        bwd_tc_chunk<W, SILU, FK, decltype(ntl)::value, decltype(a16)::value>(a, it, TcNoCheck{});
+    });
 }
 
 // ===========================================================================
@@ -1687,13 +1732,14 @@ __device__ __forceinline__ void tc_taps(const float (&xe)[W - 1 + kTcE],
     for (int k = 0; k < W; ++k) xv[k] = ie[i + k] == own ? xe[i + k] : 0.0f;
 }
 
-template <int W, bool SILU, int FK, bool NTL>
+template <int W, bool SILU, int FK, bool NTL, bool A16>
 __device__ __forceinline__ void fwd_tcs_chunk(const FwdArgs &a, const TcItem &it,
                                               const TcSeqIds &ids) {
     const int lane = threadIdx.x % kWaveSize;
     const uint16_t *xr = static_cast<const uint16_t *>(a.x.ptr) + it.b * a.x.s0 + it.d * a.x.s1;
     uint16_t *yr = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.y.ptr)) +
                    it.b * a.y.s0 + it.d * a.y.s1;
+    const int ax = A16 ? 16 : tc_align(xr), ay = A16 ? 16 : tc_align(yr);
     // Left halo (values and ids of the W-1 tokens before the chunk; before
     // the row, zero and kNoId), the filter, then the tiles and their ids.
     uint16_t lh[W - 1];
@@ -1711,7 +1757,7 @@ __device__ __forceinline__ void fwd_tcs_chunk(const FwdArgs &a, const TcItem &it
 #pragma unroll
     for (int c = 0; c < kTcTilesFwd; ++c) {
         const int64_t t = it.t0 + c * kTcTile + lane * kTcE;
-        if (t < it.t1) raw[c] = tc_load<NTL>(xr, t, it.t1, a.tc_align);
+        if (t < it.t1) raw[c] = tc_load<NTL>(xr, t, it.t1, ax);
         else raw[c].v = u32x4_t{0u, 0u, 0u, 0u};
         ids.lane_ids(t < it.t1 ? t : a.T, tid[c]);
     }
@@ -1747,7 +1793,7 @@ __device__ __forceinline__ void fwd_tcs_chunk(const FwdArgs &a, const TcItem &it
             for (int k = 0; k < W; ++k) z = fmaf(w[k][0], xv[k], z);
             out[i] = act<SILU>(z);
         }
-        if (t < it.t1) tc_store<true>(yr, t, it.t1, out, a.tc_align);
+        if (t < it.t1) tc_store<true>(yr, t, it.t1, out, ay);
 #pragma unroll
         for (int j = 0; j < W - 1; ++j) {
             carry[j] = from_lane(v[kTcE - (W - 1) + j], kWaveSize - 1);
@@ -1756,7 +1802,7 @@ __device__ __forceinline__ void fwd_tcs_chunk(const FwdArgs &a, const TcItem &it
     }
 }
 
-template <int W, bool SILU, int FK, bool NTL>
+template <int W, bool SILU, int FK, bool NTL, bool A16>
 __device__ __forceinline__ void bwd_tcs_chunk(const BwdArgs &a, const TcItem &it,
                                               const TcSeqIds &ids) {
     constexpr bool BIAS = fk_bias(FK);
@@ -1765,6 +1811,8 @@ __device__ __forceinline__ void bwd_tcs_chunk(const BwdArgs &a, const TcItem &it
     const uint16_t *dyr = static_cast<const uint16_t *>(a.dy.ptr) + it.b * a.dy.s0 + it.d * a.dy.s1;
     uint16_t *dxr = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.dx.ptr)) +
                     it.b * a.dx.s0 + it.d * a.dx.s1;
+    const int ax = A16 ? 16 : tc_align(xr), ady = A16 ? 16 : tc_align(dyr),
+              adx = A16 ? 16 : tc_align(dxr);
     // Single tokens first: the left halo (values, ids); the right halo (lane
     // j < W-1 reads token t1 + j of x and dy, the other lanes and tokens
     // past the row an in-row token that is dropped) and its ids.
@@ -1786,8 +1834,8 @@ __device__ __forceinline__ void bwd_tcs_chunk(const BwdArgs &a, const TcItem &it
     for (int c = 0; c < kTcTilesBwd; ++c) {
         const int64_t t = it.t0 + c * kTcTile + lane * kTcE;
         if (t < it.t1) {
-            rx[c] = tc_load<NTL>(xr, t, it.t1, a.tc_align);
-            rd[c] = tc_load<NTL>(dyr, t, it.t1, a.tc_align);
+            rx[c] = tc_load<NTL>(xr, t, it.t1, ax);
+            rd[c] = tc_load<NTL>(dyr, t, it.t1, ady);
         } else {
             rx[c].v = u32x4_t{0u, 0u, 0u, 0u};
             rd[c].v = u32x4_t{0u, 0u, 0u, 0u};
@@ -1830,7 +1878,7 @@ __device__ __forceinline__ void bwd_tcs_chunk(const BwdArgs &a, const TcItem &it
                 acc = fmaf(w[W - 1 - j][0], ige[i + j] == own ? ge[i + j] : 0.0f, acc);
             v[i] = acc;
         }
-        if (t < it.t1) tc_store<true>(dxr, t, it.t1, v, a.tc_align);
+        if (t < it.t1) tc_store<true>(dxr, t, it.t1, v, adx);
     };
 
     float gprev[kTcE];
@@ -1936,16 +1984,18 @@ template <int W, bool SILU, int FK>
 __global__ __launch_bounds__(256) void k_fwd_tcs(FwdArgs a) {
     TcItem it;
     if (!tc_item(a, it)) return;
-    if (a.nt_load) fwd_tcs_chunk<W, SILU, FK, true>(a, it, tc_seq_ids(a, it));
-    else fwd_tcs_chunk<W, SILU, FK, false>(a, it, tc_seq_ids(a, it));
+    tc_run(a, [&](auto ntl, auto a16) {
+        fwd_tcs_chunk<W, SILU, FK, decltype(ntl)::value, decltype(a16)::value>(a, it, tc_seq_ids(a, it));
+    });
 }
 
 template <int W, bool SILU, int FK>
 __global__ __launch_bounds__(256) void k_bwd_tcs(BwdArgs a) {
     TcItem it;
     if (!tc_item(a, it)) return;
-    if (a.nt_load) bwd_tcs_chunk<W, SILU, FK, true>(a, it, tc_seq_ids(a, it));
-    else bwd_tcs_chunk<W, SILU, FK, false>(a, it, tc_seq_ids(a, it));
+    tc_run(a, [&](auto ntl, auto a16) {
+        bwd_tcs_chunk<W, SILU, FK, decltype(ntl)::value, decltype(a16)::value>(a, it, tc_seq_ids(a, it));
+    });
 }
 
 // ===========================================================================
@@ -2074,8 +2124,9 @@ __global__ __launch_bounds__(256) void k_fwd_tcp(FwdArgs a) {
     if (!check.start()) return;  // a set flag word: write nothing
     FwdArgs da = a;
     da.fin.ptr = nullptr;  // final states come from the repair
-    if (a.nt_load) fwd_tc_chunk<W, SILU, FK, true>(da, it, check);
-    else fwd_tc_chunk<W, SILU, FK, false>(da, it, check);
+    tc_run(a, [&](auto ntl, auto a16) {
+        fwd_tc_chunk<W, SILU, FK, decltype(ntl)::value, decltype(a16)::value>(da, it, check);
+    });
 }
 
 // Forward repair: a wave per sequence j = [s, e) and group of 64 channels,
@@ -2140,8 +2191,9 @@ void k_bwd_tcp(BwdArgs a) {
     BwdArgs da = a;
     da.dfin.ptr = nullptr;  // the state gradients come from the repair
     da.dinit.ptr = nullptr;
-    if (a.nt_load) bwd_tc_chunk<W, SILU, FK, true>(da, it, check);
-    else bwd_tc_chunk<W, SILU, FK, false>(da, it, check);
+    tc_run(a, [&](auto ntl, auto a16) {
+        bwd_tc_chunk<W, SILU, FK, decltype(ntl)::value, decltype(a16)::value>(da, it, check);
+    });
 }
 
 // Backward repair of boundary j (s = cu[j]) in one lane, adding its dW/dB

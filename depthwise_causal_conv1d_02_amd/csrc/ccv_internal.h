@@ -106,7 +106,7 @@ struct FwdArgs {
     // B*D*n_chunk waves fit (tc_div32), by these divisors (n_chunk, D).
     int tc_div32;
     Div32 tc_chunks, tc_rows;
-    int tc_align;              // time lanes: byte alignment common to every row start (16, 8, 4 or 2)
+    int tc_vec16;              // time lanes: every row start of every tensor is 16-byte aligned
 };
 
 struct BwdArgs {
@@ -134,7 +134,7 @@ struct BwdArgs {
     int nt_load;
     int tc_div32;                         // as in FwdArgs
     Div32 tc_chunks, tc_rows;
-    int tc_align;                         // as in FwdArgs
+    int tc_vec16;                         // as in FwdArgs
 };
 
 struct UpdArgs {
