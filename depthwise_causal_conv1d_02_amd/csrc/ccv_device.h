@@ -2676,6 +2676,9 @@ __global__ __launch_bounds__(256) void k_update_any(UpdArgs a) {
 // 8 tokens at B=256 D=8192 (cold), 20.3 us against 20.5 (state stores
 // cached too), 22.4 (all four non-temporal) and 23.8 (none); the scalar
 // state accesses and batches of 4 tokens before, 22.0 us.
+#ifndef CCV_UPD_TOK_STAGED
+#define CCV_UPD_TOK_STAGED 1
+#endif
 #ifndef CCV_UPD_TOK_NT
 #define CCV_UPD_TOK_NT 14  // non-temporal: 1 state loads, 2 state stores, 4 token loads, 8 outputs
 #endif
@@ -2691,10 +2694,22 @@ __global__ __launch_bounds__(256) void k_update_tokens(UpdArgs a) {
     uint16_t *yb = static_cast<uint16_t *>(a.y) + b * a.y_sb + c0;
     u32x4_t *sq = reinterpret_cast<u32x4_t *>(static_cast<uint16_t *>(a.state) + b * a.s_sb +
                                               c0 * (W - 1));
+    // With whole waves per row (D % 512 == 0) the wave's state is one
+    // contiguous range: lane l moves its vectors l, l + 64, ..., and the
+    // lanes swap them through the wave's LDS slice (LDS operations of a
+    // wave complete in order, so no barrier is needed).  8 calls of 8
+    // tokens at B=256 D=8192: 20.3 -> 19.5 us (state loads non-temporal
+    // too: 19.9 us).
+    __shared__ u32x4_t s_st[kWavesPerBlock][kWaveSize * V::kState];
+    const int wave = threadIdx.x / kWaveSize, lane = threadIdx.x % kWaveSize;
+    const bool staged = CCV_UPD_TOK_STAGED && a.n_lane_per_row % kWaveSize == 0;
+    u32x4_t *wsq = sq - lane * V::kState;  // the wave's first state vector (when staged)
     u32x4_t sv[V::kState];
 #pragma unroll
-    for (int i = 0; i < V::kState; ++i)
-        sv[i] = (CCV_UPD_TOK_NT & 1) ? __builtin_nontemporal_load(sq + i) : sq[i];
+    for (int i = 0; i < V::kState; ++i) {
+        u32x4_t *p = staged ? wsq + lane + kWaveSize * i : sq + i;
+        sv[i] = (CCV_UPD_TOK_NT & 1) ? __builtin_nontemporal_load(p) : *p;
+    }
     const u32x4_t *wq = reinterpret_cast<const u32x4_t *>(
         static_cast<const char *>(a.w) + c0 * W * (WF32 ? 4 : 2));
     u32x4_t wv[V::kFilter], bv[V::kBias];
@@ -2715,6 +2730,13 @@ __global__ __launch_bounds__(256) void k_update_tokens(UpdArgs a) {
 
     float w[W][VEC], bias[VEC];
     upd_unpack_filter<W, WF32>(wv, bv, w, bias);
+    if (staged) {
+#pragma unroll
+        for (int i = 0; i < V::kState; ++i) s_st[wave][lane + kWaveSize * i] = sv[i];
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < V::kState; ++i) sv[i] = s_st[wave][lane * V::kState + i];
+    }
     // state element (c, j) is 16-bit word c*(W-1) + j of the lane's vectors
     uint16_t st[VEC][W - 1];
 #pragma unroll
@@ -2766,10 +2788,18 @@ __global__ __launch_bounds__(256) void k_update_tokens(UpdArgs a) {
             const int e = c * (W - 1) + j;
             nv[e / 8][(e % 8) / 2] |= static_cast<uint32_t>(st[c][j]) << (16 * (e % 2));
         }
+    if (staged) {
+#pragma unroll
+        for (int i = 0; i < V::kState; ++i) s_st[wave][lane * V::kState + i] = nv[i];
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < V::kState; ++i) nv[i] = s_st[wave][lane + kWaveSize * i];
+    }
 #pragma unroll
     for (int i = 0; i < V::kState; ++i) {
-        if (CCV_UPD_TOK_NT & 2) __builtin_nontemporal_store(nv[i], sq + i);
-        else sq[i] = nv[i];
+        u32x4_t *p = staged ? wsq + lane + kWaveSize * i : sq + i;
+        if (CCV_UPD_TOK_NT & 2) __builtin_nontemporal_store(nv[i], p);
+        else *p = nv[i];
     }
 }
 
