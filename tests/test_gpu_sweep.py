@@ -6,7 +6,7 @@ states, the final-state gradient, the activation and the determinism route,
 then checks forward and backward against the fp64 oracle with every output
 inside a sentinel-filled guard band.  A second sweep does the same for the
 single- and multi-token update.  The draws are fixed by the case index, and
-each case prints itself before it runs (256 forward+backward cases, 64 updates)."""
+each case prints itself before it runs (512 forward+backward cases, 128 updates)."""
 import random
 
 import pytest
@@ -29,7 +29,7 @@ EDGE_T = [1, 2, 3, 4, 7, 8, 9, 15, 16, 17, 31, 33, 63, 64, 65, 127, 129, 511, 51
           1023, 1024, 1025, 2047, 2048, 2049, 2050, 4099]
 CHANNELS = [8, 16, 24, 40, 64, 72, 200, 256, 264, 512, 520, 1032, 1536, 2056]
 MAX_ELEMS = 2_500_000
-N_CASES = 256
+N_CASES = 512
 
 
 def draw_case(i):
@@ -115,7 +115,7 @@ def test_sweep_fwd_bwd(i):
         ops.check_flag(DEV)
 
 
-N_UPDATE = 64
+N_UPDATE = 128
 
 
 def draw_update(i):
