@@ -460,15 +460,26 @@ void add_tail(Geometry &g, const Problem &p, int wt, int pct, int64_t lt, int64_
     g.n_block = g.n_block_m + per * g.n_tblk_t;
 }
 
+// seq_idx rows on time lanes with block-shared tap masks: a block takes
+// kWavesPerBlock consecutive channels of one (batch row, chunk).
+bool seq_mask_blocks(const Problem &p, bool bwd) {
+    return (bwd ? CCV_TCS_MASKS_BWD : CCV_TCS_MASKS_FWD) && p.seq && !p.packed;
+}
+int64_t row_groups(const Problem &p) {
+    return (p.D + ccv::kWavesPerBlock - 1) / ccv::kWavesPerBlock;
+}
+
 // Time-lane geometry: one wave per (row, chunk of `tiles` tiles).
-Geometry time_geometry(const Problem &p, int tiles) {
+Geometry time_geometry(const Problem &p, int tiles, bool bwd) {
     Geometry g;
     g.L = static_cast<int64_t>(tiles) * ccv::kTcTile;
     g.n_chunk = (p.T + g.L - 1) / g.L;
     g.n_tblk = g.n_chunk;  // partials per batch row: one per chunk
     g.n_group = p.D;
     g.n_gblk = p.D;
-    g.n_block = (p.B * p.D * g.n_chunk + ccv::kWavesPerBlock - 1) / ccv::kWavesPerBlock;
+    g.n_block = seq_mask_blocks(p, bwd)
+                    ? p.B * g.n_chunk * row_groups(p)
+                    : (p.B * p.D * g.n_chunk + ccv::kWavesPerBlock - 1) / ccv::kWavesPerBlock;
     g.Tm = p.T;
     g.Lt = 0;
     g.n_tblk_t = 0;
@@ -490,13 +501,16 @@ void set_validation(A &a, const Problem &p, bool time_lanes) {
 }
 
 // The time lanes decode their wave index in 32 bits when all B*D*n_chunk
-// wave indices fit.
+// wave indices fit; with block-shared masks, their block index (B*n_chunk
+// blocks per row group, divided by the row groups, then by n_chunk).
 template <typename A>
-void set_tc_div(A &a) {
-    a.tc_div32 = a.B * a.D * a.n_chunk <= int64_t(UINT32_MAX);
+void set_tc_div(A &a, const Problem &p, bool bwd) {
+    const bool blocks = seq_mask_blocks(p, bwd);
+    const int64_t per = blocks ? row_groups(p) : a.D;
+    a.tc_div32 = a.B * per * a.n_chunk <= int64_t(UINT32_MAX);
     if (a.tc_div32) {
         a.tc_chunks = ccv::make_div32(static_cast<uint32_t>(a.n_chunk));
-        a.tc_rows = ccv::make_div32(static_cast<uint32_t>(a.D));
+        a.tc_rows = ccv::make_div32(static_cast<uint32_t>(per));
     }
 }
 
@@ -570,7 +584,7 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     const int64_t cap = CCV_FWD_ROUNDS > 0 && !time_lanes
                             ? ccv::fwd_resident_blocks(a, vec, silu, p.rows())
                             : 0;
-    const Geometry g = time_lanes ? time_geometry(p, ccv::kTcTilesFwd)
+    const Geometry g = time_lanes ? time_geometry(p, ccv::kTcTilesFwd, false)
                                   : geometry(p, vec, ccv::kFwdWavesT, ccv::kFwdWavesC, cap,
                                              CCV_FWD_ROUNDS,
                                              pipe && vec == 8 && !p.seq
@@ -597,7 +611,7 @@ int ccv_fwd(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bia
     a.Lt = gs.Lt;
     a.n_tblk_t = gs.n_tblk_t;
     a.n_block_m = gs.n_block_m;
-    if (time_lanes) set_tc_div(a);
+    if (time_lanes) set_tc_div(a, p, false);
     a.tc_vec16 = time_lanes && rows_aligned16(x, y, nullptr);
     set_validation(a, p, time_lanes);
     a.nt_load = p.B * p.D * p.T * 2 >=
@@ -665,7 +679,7 @@ int bwd_call(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bi
     // The partials of the deterministic route depend on the shape only (a
     // grid sized by target waves); the atomic route sizes its grid by the
     // device's resident capacity below.
-    Geometry g = time_lanes ? time_geometry(p, ccv::kTcTilesBwd)
+    Geometry g = time_lanes ? time_geometry(p, ccv::kTcTilesBwd, true)
                             : geometry(p, vec, ccv::kWavesPerBlock, 1, 0, 0,
                                        det_target_waves(p, vec), CCV_BWD_MIN_CHUNK);
     if (!time_lanes)
@@ -756,7 +770,7 @@ int bwd_call(const ccv_tensor *x, const ccv_tensor *weight, const ccv_tensor *bi
     a.Lt = g.Lt;
     a.n_tblk_t = g.n_tblk_t;
     a.n_block_m = g.n_block_m;
-    if (time_lanes) set_tc_div(a);
+    if (time_lanes) set_tc_div(a, p, true);
     a.tc_vec16 = time_lanes && rows_aligned16(x, dy, dx);
     set_validation(a, p, time_lanes);
 

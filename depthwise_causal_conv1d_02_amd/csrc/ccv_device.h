@@ -1980,22 +1980,375 @@ __device__ __forceinline__ void bwd_tcs_chunk(const BwdArgs &a, const TcItem &it
     }
 }
 
+// ---------------------------------------------------------------------------
+// The same lanes with block-shared tap masks (CCV_TCS_MASKS_FWD/_BWD).  A block's four
+// waves take four consecutive rows (b, d) of one chunk, so they share the
+// chunk's seq_idx entries: wave w reads the entries of tile w only and turns
+// them into one tap-mask word per lane (bit 3i + l-1: token i of the lane and
+// the token l places before it carry the same entry, l = 1..W-1), and the
+// block exchanges the words through LDS.  A wave past the last row only
+// builds masks.  The backward also needs the words of the W-1 tokens past the
+// chunk (the right halo), built by wave 0.
+// ---------------------------------------------------------------------------
+template <int W>
+__device__ __forceinline__ uint32_t tcm_word(const int32_t (&ie)[W - 1 + kTcE]) {
+    uint32_t m = 0u;
+#pragma unroll
+    for (int i = 0; i < kTcE; ++i)
+#pragma unroll
+        for (int l = 1; l < W; ++l)
+            if (ie[i + W - 1 - l] == ie[i + W - 1]) m |= 1u << (3 * i + l - 1);
+    return m;
+}
+// v where bit b of m is set, else +0 (an AND with the bit spread to 32).
+__device__ __forceinline__ float tcm_keep(float v, uint32_t m, int b) {
+    return __int_as_float(__float_as_int(v) &
+                          __builtin_amdgcn_sbfe(static_cast<int>(m), static_cast<unsigned>(b), 1u));
+}
+
+// Work item: block q = (b, chunk, row group), row groups innermost (32-bit
+// decode by tc_rows = n_rg and tc_chunks = n_chunk); wave w takes row
+// d = 4 rg + w, `live` when d < D (else d is clamped and nothing is loaded
+// or written for it).
+template <typename A>
+__device__ __forceinline__ void tcm_item(const A &a, TcItem &it, bool &live) {
+    const int64_t q = xcd_remap(blockIdx.x, a.n_block);
+    const int64_t n_rg = (a.D + kWavesPerBlock - 1) / kWavesPerBlock;
+    int64_t rg;
+    if (a.tc_div32) {
+        const uint32_t q32 = static_cast<uint32_t>(q);
+        const uint32_t bc = div32(q32, a.tc_rows);
+        rg = q32 - bc * static_cast<uint32_t>(n_rg);
+        const uint32_t b = div32(bc, a.tc_chunks);
+        it.chunk = bc - b * static_cast<uint32_t>(a.n_chunk);
+        it.b = b;
+    } else {
+        const int64_t bc = q / n_rg;
+        rg = q % n_rg;
+        it.chunk = bc % a.n_chunk;
+        it.b = bc / a.n_chunk;
+    }
+    it.d = rg * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
+    live = it.d < a.D;
+    if (!live) it.d = a.D - 1;
+    it.t0 = it.chunk * a.L;
+    it.t1 = min(it.t0 + a.L, a.T);
+}
+
+// Build the block's mask words (tile w by wave w; the right halo's by wave 0
+// when RH) and make them visible to the block.  Every wave of the block
+// calls it.
+template <int W, int TILES, bool RH>
+__device__ __forceinline__ void tcm_build(const TcItem &it, const TcSeqIds &ids, int64_t T,
+                                          uint32_t (&s_mask)[TILES][kWaveSize],
+                                          uint32_t &s_rh) {
+    static_assert(W <= 4, "3 mask bits per token");
+    static_assert(TILES <= kWavesPerBlock, "one tile per wave");
+    const int wave = threadIdx.x / kWaveSize, lane = threadIdx.x % kWaveSize;
+    const int64_t tt = it.t0 + static_cast<int64_t>(wave) * kTcTile;
+    if (wave < TILES && tt < it.t1) {
+        const int64_t t = tt + lane * kTcE;
+        int32_t id[kTcE], hid[W - 1], ie[W - 1 + kTcE];
+        ids.lane_ids(t < it.t1 ? t : T, id);
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) hid[j] = ids.at(tt - (W - 1) + j);
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) ie[j] = lane_up_id(id[kTcE - (W - 1) + j], hid[j]);
+#pragma unroll
+        for (int i = 0; i < kTcE; ++i) ie[W - 1 + i] = id[i];
+        s_mask[wave][lane] = tcm_word<W>(ie);
+    }
+    if (RH && wave == 0) {
+        // tokens t1 + j (j < W-1) against the W-1 tokens before each
+        int32_t iw[2 * (W - 1)];
+#pragma unroll
+        for (int k = 0; k < 2 * (W - 1); ++k) iw[k] = ids.at(it.t1 - (W - 1) + k);
+        uint32_t m = 0u;
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j)
+#pragma unroll
+            for (int l = 1; l < W; ++l)
+                if (iw[j + W - 1 - l] == iw[j + W - 1]) m |= 1u << (3 * j + l - 1);
+        if (lane == 0) s_rh = m;
+    }
+    __syncthreads();
+}
+
+template <int W, bool SILU, int FK, bool NTL, bool A16>
+__device__ __forceinline__ void fwd_tcm_chunk(const FwdArgs &a, const TcItem &it, bool live,
+                                              const TcSeqIds &ids,
+                                              uint32_t (&s_mask)[kTcTilesFwd][kWaveSize],
+                                              uint32_t &s_rh) {
+    const int lane = threadIdx.x % kWaveSize;
+    const uint16_t *xr = static_cast<const uint16_t *>(a.x.ptr) + it.b * a.x.s0 + it.d * a.x.s1;
+    uint16_t *yr = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.y.ptr)) +
+                   it.b * a.y.s0 + it.d * a.y.s1;
+    const int ax = A16 ? 16 : tc_align(xr), ay = A16 ? 16 : tc_align(yr);
+    uint16_t lh[W - 1];
+    float w[W][1], bias[1];
+    Raw<8> raw[kTcTilesFwd];
+    if (live) {
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) {
+            const int64_t p = it.t0 - (W - 1) + j;
+            lh[j] = xr[p >= 0 ? p : 0];
+        }
+        load_filter<W, 1, FK>(a.w, a.w_sd, a.w_sk, a.bias, a.b_s, it.d, w, bias);
+#pragma unroll
+        for (int c = 0; c < kTcTilesFwd; ++c) {
+            const int64_t t = it.t0 + c * kTcTile + lane * kTcE;
+            if (t < it.t1) raw[c] = tc_load<NTL>(xr, t, it.t1, ax);
+            else raw[c].v = u32x4_t{0u, 0u, 0u, 0u};
+        }
+    }
+    tcm_build<W, kTcTilesFwd, false>(it, ids, a.T, s_mask, s_rh);
+    if (!live) return;
+    float carry[W - 1];
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j)
+        carry[j] = it.t0 - (W - 1) + j >= 0 ? bf16_bits_to_f32(lh[j]) : 0.0f;
+#pragma unroll
+    for (int c = 0; c < kTcTilesFwd; ++c) {
+        const int64_t tt = it.t0 + c * kTcTile;
+        if (tt >= it.t1) break;
+        const int64_t t = tt + lane * kTcE;
+        const uint32_t mc = s_mask[c][lane];
+        float v[kTcE], xe[W - 1 + kTcE], out[kTcE];
+        unpack<8>(raw[c], v);
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) xe[j] = lane_up(v[kTcE - (W - 1) + j], carry[j]);
+#pragma unroll
+        for (int i = 0; i < kTcE; ++i) xe[W - 1 + i] = v[i];
+#pragma unroll
+        for (int i = 0; i < kTcE; ++i) {
+            float z = bias[0];
+#pragma unroll
+            for (int k = 0; k < W; ++k) {
+                const int lag = W - 1 - k;
+                z = fmaf(w[k][0], lag == 0 ? xe[i + k] : tcm_keep(xe[i + k], mc, 3 * i + lag - 1),
+                         z);
+            }
+            out[i] = act<SILU>(z);
+        }
+        if (t < it.t1) tc_store<true>(yr, t, it.t1, out, ay);
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) carry[j] = from_lane(v[kTcE - (W - 1) + j], kWaveSize - 1);
+    }
+}
+
+template <int W, bool SILU, int FK, bool NTL, bool A16>
+__device__ __forceinline__ void bwd_tcm_chunk(const BwdArgs &a, const TcItem &it, bool live,
+                                              const TcSeqIds &ids,
+                                              uint32_t (&s_mask)[kTcTilesBwd][kWaveSize],
+                                              uint32_t &s_rh) {
+    constexpr bool BIAS = fk_bias(FK);
+    const int lane = threadIdx.x % kWaveSize;
+    const uint16_t *xr = static_cast<const uint16_t *>(a.x.ptr) + it.b * a.x.s0 + it.d * a.x.s1;
+    const uint16_t *dyr = static_cast<const uint16_t *>(a.dy.ptr) + it.b * a.dy.s0 + it.d * a.dy.s1;
+    uint16_t *dxr = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.dx.ptr)) +
+                    it.b * a.dx.s0 + it.d * a.dx.s1;
+    const int ax = A16 ? 16 : tc_align(xr), ady = A16 ? 16 : tc_align(dyr),
+              adx = A16 ? 16 : tc_align(dxr);
+    uint16_t lh[W - 1], rh_x = 0, rh_dy = 0;
+    float w[W][1], bias[1];
+    Raw<8> rx[kTcTilesBwd], rd[kTcTilesBwd];
+    if (live) {
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) {
+            const int64_t p = it.t0 - (W - 1) + j;
+            lh[j] = xr[p >= 0 ? p : 0];
+        }
+        const int64_t rq = min(it.t1 + lane, a.T - 1);
+        rh_x = xr[rq];
+        rh_dy = dyr[rq];
+        load_filter<W, 1, FK>(a.w, a.w_sd, a.w_sk, a.bias, a.b_s, it.d, w, bias);
+#pragma unroll
+        for (int c = 0; c < kTcTilesBwd; ++c) {
+            const int64_t t = it.t0 + c * kTcTile + lane * kTcE;
+            if (t < it.t1) {
+                rx[c] = tc_load<NTL>(xr, t, it.t1, ax);
+                rd[c] = tc_load<NTL>(dyr, t, it.t1, ady);
+            } else {
+                rx[c].v = u32x4_t{0u, 0u, 0u, 0u};
+                rd[c].v = u32x4_t{0u, 0u, 0u, 0u};
+            }
+        }
+    }
+    tcm_build<W, kTcTilesBwd, true>(it, ids, a.T, s_mask, s_rh);
+    if (!live) return;
+    float carry[W - 1];
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j)
+        carry[j] = it.t0 - (W - 1) + j >= 0 ? bf16_bits_to_f32(lh[j]) : 0.0f;
+    float dwacc[W], dbacc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < W; ++k) dwacc[k] = 0.0f;
+
+    // dx of the lane's tokens of the tile at tt from its g's and mask word,
+    // and the W-1 g's and the mask word that follow the lane (`after`,
+    // `after_m`: the next tile's lane 0, or the right halo's, for lane 63).
+    // Term l of dx[i] is g of token i+l through its tap l, kept when token
+    // i+l has token i's entry: bit 3(i+l) + l-1 of this lane's word, or of
+    // the next lane's for i+l >= kTcE.
+    auto emit = [&](int64_t tt, const float (&g)[kTcE], uint32_t mw, const float (&after)[W - 1],
+                    uint32_t after_m) {
+        float ge[kTcE + W - 1], v[kTcE];
+#pragma unroll
+        for (int i = 0; i < kTcE; ++i) ge[i] = g[i];
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) ge[kTcE + j] = lane_down(g[j], after[j]);
+        const uint32_t mn = static_cast<uint32_t>(
+            lane_down_id(static_cast<int32_t>(mw), static_cast<int32_t>(after_m)));
+        const int64_t t = tt + lane * kTcE;
+#pragma unroll
+        for (int i = 0; i < kTcE; ++i) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int l = W - 1; l >= 0; --l) {
+                const int u = i + l;  // the output token whose tap l meets token i
+                float gv = ge[u];
+                if (l > 0) gv = u < kTcE ? tcm_keep(gv, mw, 3 * u + l - 1)
+                                         : tcm_keep(gv, mn, 3 * (u - kTcE) + l - 1);
+                acc = l == W - 1 ? w[0][0] * gv : fmaf(w[W - 1 - l][0], gv, acc);
+            }
+            v[i] = acc;
+        }
+        if (t < it.t1) tc_store<true>(dxr, t, it.t1, v, adx);
+    };
+
+    float gprev[kTcE];
+    uint32_t mprev = 0u;
+    int64_t tprev = -1;
+#pragma unroll
+    for (int c = 0; c < kTcTilesBwd; ++c) {
+        const int64_t tt = it.t0 + c * kTcTile;
+        if (tt >= it.t1) break;
+        const uint32_t mc = s_mask[c][lane];
+        float v[kTcE], dyv[kTcE], xe[W - 1 + kTcE], g[kTcE];
+        unpack<8>(rx[c], v);
+        unpack<8>(rd[c], dyv);
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) xe[j] = lane_up(v[kTcE - (W - 1) + j], carry[j]);
+#pragma unroll
+        for (int i = 0; i < kTcE; ++i) xe[W - 1 + i] = v[i];
+#pragma unroll
+        for (int i = 0; i < kTcE; ++i) {
+            float xv[W];
+#pragma unroll
+            for (int k = 0; k < W; ++k) {
+                const int lag = W - 1 - k;
+                xv[k] = lag == 0 ? xe[i + k] : tcm_keep(xe[i + k], mc, 3 * i + lag - 1);
+            }
+            float z = bias[0];
+#pragma unroll
+            for (int k = 0; k < W; ++k) z = fmaf(w[k][0], xv[k], z);
+            g[i] = dyv[i] * act_slope<SILU>(z);  // zero past the chunk (dy reads 0)
+#pragma unroll
+            for (int k = 0; k < W; ++k) dwacc[k] = fmaf(g[i], xv[k], dwacc[k]);
+            if constexpr (BIAS) dbacc += g[i];
+        }
+        if (tprev >= 0) {
+            float after[W - 1];
+#pragma unroll
+            for (int j = 0; j < W - 1; ++j) after[j] = from_lane(g[j], 0);
+            emit(tprev, gprev, mprev,
+                 after, static_cast<uint32_t>(from_lane_id(static_cast<int32_t>(mc), 0)));
+        }
+#pragma unroll
+        for (int i = 0; i < kTcE; ++i) gprev[i] = g[i];
+        mprev = mc;
+        tprev = tt;
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) carry[j] = from_lane(v[kTcE - (W - 1) + j], kWaveSize - 1);
+    }
+    // Right halo: g at t1 .. t1+W-2 (zero past the row), in every lane; a
+    // chunk that does not end the row is a whole number of tiles, so `carry`
+    // holds the W-1 tokens before t1.
+    {
+        const uint32_t rh = s_rh;
+        float xw[2 * (W - 1)], after[W - 1];
+        const float hx = bf16_bits_to_f32(rh_x), hd = bf16_bits_to_f32(rh_dy);
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) {
+            xw[j] = carry[j];
+            xw[W - 1 + j] = from_lane(hx, j);
+        }
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) {
+            float z = bias[0];
+#pragma unroll
+            for (int k = 0; k < W; ++k) {
+                const int lag = W - 1 - k;
+                z = fmaf(w[k][0], lag == 0 ? xw[j + k] : tcm_keep(xw[j + k], rh, 3 * j + lag - 1),
+                         z);
+            }
+            after[j] = it.t1 + j < a.T ? from_lane(hd, j) * act_slope<SILU>(z) : 0.0f;
+        }
+        emit(tprev, gprev, mprev, after, rh);
+    }
+    // dW/dB of the chunk: a wave sum, then one atomic or one partial per tap.
+#pragma unroll
+    for (int k = 0; k < W; ++k) dwacc[k] = wave_sum(dwacc[k]);
+    if constexpr (BIAS) dbacc = wave_sum(dbacc);
+    if (lane == 0) {
+        if (a.partial) {
+            const int64_t pidx = it.b * a.n_chunk + it.chunk;
+            float *pr = a.partial + (pidx * a.D + it.d) * a.part_stride;
+#pragma unroll
+            for (int k = 0; k < W; ++k) pr[k] = dwacc[k];
+            if (a.part_stride > W) pr[W] = dbacc;
+        } else {
+#pragma unroll
+            for (int k = 0; k < W; ++k) atomicAdd(a.dw + it.d * W + k, dwacc[k]);
+            if constexpr (BIAS) atomicAdd(a.db + it.d, dbacc);
+        }
+    }
+}
+
 template <int W, bool SILU, int FK>
 __global__ __launch_bounds__(256) void k_fwd_tcs(FwdArgs a) {
-    TcItem it;
-    if (!tc_item(a, it)) return;
-    tc_run(a, [&](auto ntl, auto a16) {
-        fwd_tcs_chunk<W, SILU, FK, decltype(ntl)::value, decltype(a16)::value>(a, it, tc_seq_ids(a, it));
-    });
+    if constexpr (CCV_TCS_MASKS_FWD) {
+        __shared__ uint32_t s_mask[kTcTilesFwd][kWaveSize];
+        __shared__ uint32_t s_rh;
+        TcItem it;
+        bool live;
+        tcm_item(a, it, live);
+        const TcSeqIds ids = tc_seq_ids(a, it);
+        tc_run(a, [&](auto ntl, auto a16) {
+            fwd_tcm_chunk<W, SILU, FK, decltype(ntl)::value, decltype(a16)::value>(
+                a, it, live, ids, s_mask, s_rh);
+        });
+    } else {
+        TcItem it;
+        if (!tc_item(a, it)) return;
+        tc_run(a, [&](auto ntl, auto a16) {
+            fwd_tcs_chunk<W, SILU, FK, decltype(ntl)::value, decltype(a16)::value>(
+                a, it, tc_seq_ids(a, it));
+        });
+    }
 }
 
 template <int W, bool SILU, int FK>
 __global__ __launch_bounds__(256) void k_bwd_tcs(BwdArgs a) {
-    TcItem it;
-    if (!tc_item(a, it)) return;
-    tc_run(a, [&](auto ntl, auto a16) {
-        bwd_tcs_chunk<W, SILU, FK, decltype(ntl)::value, decltype(a16)::value>(a, it, tc_seq_ids(a, it));
-    });
+    if constexpr (CCV_TCS_MASKS_BWD) {
+        __shared__ uint32_t s_mask[kTcTilesBwd][kWaveSize];
+        __shared__ uint32_t s_rh;
+        TcItem it;
+        bool live;
+        tcm_item(a, it, live);
+        const TcSeqIds ids = tc_seq_ids(a, it);
+        tc_run(a, [&](auto ntl, auto a16) {
+            bwd_tcm_chunk<W, SILU, FK, decltype(ntl)::value, decltype(a16)::value>(
+                a, it, live, ids, s_mask, s_rh);
+        });
+    } else {
+        TcItem it;
+        if (!tc_item(a, it)) return;
+        tc_run(a, [&](auto ntl, auto a16) {
+            bwd_tcs_chunk<W, SILU, FK, decltype(ntl)::value, decltype(a16)::value>(
+                a, it, tc_seq_ids(a, it));
+        });
+    }
 }
 
 // ===========================================================================

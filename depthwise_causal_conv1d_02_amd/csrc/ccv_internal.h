@@ -45,6 +45,17 @@ constexpr int kTcTilesFwd = CCV_TC_TILES_FWD;
 constexpr int kTcTilesBwd = CCV_TC_TILES_BWD;
 // `vec` value that selects the time-lane kernels.
 constexpr int kVecTime = 0;
+// seq_idx rows on time lanes: a block's four waves take four rows of one
+// chunk and share its tap masks through LDS (1), or every wave reads its own
+// seq_idx entries (0), per direction.  The host's grid follows the same
+// choice.  Measured on seqidx_tc (B4 D4096 T2048, 8 segments a row): the
+// backward 54.0 -> 49.9 us with shared masks, the forward 26.5 -> 26.7 us.
+#ifndef CCV_TCS_MASKS_FWD
+#define CCV_TCS_MASKS_FWD 0
+#endif
+#ifndef CCV_TCS_MASKS_BWD
+#define CCV_TCS_MASKS_BWD 1
+#endif
 
 // Unsigned 32-bit division by a divisor fixed for a launch, as a multiply
 // and two shifts, exact for every 0 <= n < 2^32 (Granlund and Montgomery,
