@@ -632,6 +632,14 @@ SEQ_CASES = [
     (3, 2, 520, 130, "cl", True, "silu", "random", BF16, False),
     (2, 2, 1024, 99, "cl", False, "silu", "runs", F32, True),
     (4, 2, 512, 64, "cl", False, "silu", "constant", F32, False),
+    # time lanes, a block per four channels of one chunk: channel counts that
+    # leave waves without a row, several 2048-token chunks with ragged tails
+    (4, 2, 5, 4100, "tc", True, "silu", "random", BF16, True),
+    (3, 3, 7, 2049, "tc", False, None, "runs", F32, False),
+    (2, 1, 1, 600, "tc", True, "silu", "periodic", BF16, True),
+    (4, 2, 66, 1030, "tc", True, "silu", "runs", BF16, False),
+    (4, 1, 3, 513, "tc", False, "silu", "constant", BF16, True),
+    (4, 2, 6, 2048, "tc", False, None, "periodic", F32, True),
 ]
 
 
@@ -652,8 +660,9 @@ def test_seq_idx_parity(case):
     check_bf16("y", y.view, oy)
     assert y.intact(), "write outside y"
     dx = guarded_act(B, D, T, layout, DEV)
+    opts = OPT_DETDB if (bias and det) else 0
     _, dw, db, _ = ops.bwd(g["x"], g["weight"], g["dy"], g["bias"], None, None, None, act, det,
-                           False, dx=dx.view, seq_idx=gseq)
+                           False, dx=dx.view, seq_idx=gseq, options=opts)
     torch.cuda.synchronize()
     odx, odw, odb = oracle.bwd_seq(f64(inp["x"]), f64(inp["weight"]), f64(inp["dy"]),
                                    seq.numpy(), f64(inp["bias"]), act)
@@ -663,10 +672,12 @@ def test_seq_idx_parity(case):
     if odb is not None:
         check_f32_rel("dbias", db, odb)
     if det:
-        _, dw2, _, _ = ops.bwd(g["x"], g["weight"], g["dy"], g["bias"], None, None, None, act,
-                               det, False, seq_idx=gseq)
+        _, dw2, db2, _ = ops.bwd(g["x"], g["weight"], g["dy"], g["bias"], None, None, None, act,
+                                 det, False, seq_idx=gseq, options=opts)
         torch.cuda.synchronize()
         assert torch.equal(dw2.view(torch.int32), dw.view(torch.int32))
+        if bias:
+            assert torch.equal(db2.view(torch.int32), db.view(torch.int32))
 
 
 def test_seq_idx_strided_ids_and_runs_equal_packed():
