@@ -1325,6 +1325,89 @@ __device__ __forceinline__ void tc_store(uint16_t *row, int64_t t, int64_t end,
         if (t + i < end) row[t + i] = to_bf16_bits(v[i]);
 }
 
+// Dwords q .. q+3 of the 8 in c, each moved down by `sh` bytes (0 or 2).
+template <int Q>
+__device__ __forceinline__ u32x4_t tc_funnel(const uint32_t (&c)[8], uint32_t sh) {
+    return u32x4_t{__builtin_amdgcn_alignbyte(c[Q + 1], c[Q], sh),
+                   __builtin_amdgcn_alignbyte(c[Q + 2], c[Q + 1], sh),
+                   __builtin_amdgcn_alignbyte(c[Q + 3], c[Q + 2], sh),
+                   __builtin_amdgcn_alignbyte(c[Q + 4], c[Q + 3], sh)};
+}
+// Lanes 0..62 take lane l+1's v, lane 63 takes `last`.
+__device__ __forceinline__ int32_t tc_lane_down_u32(int32_t v, int32_t last) {
+    return __builtin_amdgcn_update_dpp(last, v, kDppWaveShl1, 0xf, 0xf, false);
+}
+
+// Time-lane loads of rows that do not start on a 16-byte boundary.  A 16-byte
+// access that is only 4- or 2-byte aligned costs the memory pipeline about
+// as much again as an aligned one, so such rows are read in aligned blocks:
+// with s tokens between the 16-byte boundary at or before a lane's first
+// token t and t (s is the same for every lane of a row), the lane loads the
+// aligned block of tokens t-s .. t-s+7, takes the next lane's block (lane 63:
+// lane 0's block of the next tile, or the chunk's tail block) by a DPP shift,
+// and assembles t .. t+7 from the two with a byte shift.  Block tokens
+// outside [0, T) read as zero and are never accessed.
+template <bool NTL>
+__device__ __forceinline__ Raw<8> tc_block(const uint16_t *row, int64_t b0, int64_t T) {
+    if (b0 >= 0 && b0 + kTcE <= T) return load_raw<8, NTL>(row + b0, 1);  // 16-byte aligned
+    Raw<8> r;
+    r.v = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < kTcE; ++i)
+        if (b0 + i >= 0 && b0 + i < T)
+            r.v[i / 2] |= static_cast<uint32_t>(row[b0 + i]) << (16 * (i % 2));
+    return r;
+}
+
+template <bool NTL, bool A16>
+struct TcLoads {
+    const uint16_t *row;
+    int64_t T;  // the row's length
+    int s;      // 0: the row starts on a 16-byte boundary
+    __device__ __forceinline__ TcLoads(const uint16_t *r, int64_t row_len)
+        : row(r),
+          T(row_len),
+          s(A16 ? 0 : static_cast<int>((reinterpret_cast<uintptr_t>(r) & 15u) >> 1)) {}
+    // The lane's tokens t .. t+7 (aligned rows; zero from `end`), or its block.
+    __device__ __forceinline__ Raw<8> load(int64_t t, int64_t end) const {
+        if (A16 || s == 0) {
+            if (t < end) return tc_load<NTL>(row, t, end, 16);
+            Raw<8> z;
+            z.v = u32x4_t{0u, 0u, 0u, 0u};
+            return z;
+        }
+        return tc_block<NTL>(row, t - s, T);
+    }
+    // Lane 0's block of the tile at t (the chunk's tail; unused for aligned rows).
+    __device__ __forceinline__ Raw<8> tail(int64_t t) const {
+        if (A16 || s == 0) {
+            Raw<8> z;
+            z.v = u32x4_t{0u, 0u, 0u, 0u};
+            return z;
+        }
+        return tc_block<NTL>(row, t - s, T);
+    }
+    // Block -> tokens t .. t+7, given the next tile's blocks (lane 0's is
+    // used).  Every lane of the wave calls it.
+    __device__ __forceinline__ void fix(Raw<8> &r, const Raw<8> &next_tile) const {
+        if (A16 || s == 0) return;
+        uint32_t c[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            c[k] = r.v[k];
+            const int32_t first = __builtin_amdgcn_readlane(static_cast<int32_t>(next_tile.v[k]), 0);
+            c[4 + k] = static_cast<uint32_t>(tc_lane_down_u32(static_cast<int32_t>(r.v[k]), first));
+        }
+        const uint32_t sh = (s & 1) ? 2u : 0u;
+        switch (s >> 1) {
+            case 0: r.v = tc_funnel<0>(c, sh); break;
+            case 1: r.v = tc_funnel<1>(c, sh); break;
+            case 2: r.v = tc_funnel<2>(c, sh); break;
+            default: r.v = tc_funnel<3>(c, sh); break;
+        }
+    }
+};
+
 // Single extended tokens of one row (b, d): x_ext at p < T is the input for
 // p >= 0, else the initial state's slot p + W-1, else zero.  The source is
 // picked by selects and every case has a valid address (a zero token reads
@@ -1407,7 +1490,8 @@ __device__ __forceinline__ void fwd_tc_chunk(const FwdArgs &a, const TcItem &it,
     const uint16_t *xr = static_cast<const uint16_t *>(a.x.ptr) + it.b * a.x.s0 + it.d * a.x.s1;
     uint16_t *yr = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.y.ptr)) +
                    it.b * a.y.s0 + it.d * a.y.s1;
-    const int ax = A16 ? 16 : tc_align(xr), ay = A16 ? 16 : tc_align(yr);
+    const int ay = A16 ? 16 : tc_align(yr);
+    const TcLoads<NTL, A16> lx(xr, a.T);
     // Left halo, the final state's tokens (lanes 0..W-2 of the chunk that
     // ends the row copy the row's last W-1 extended tokens bit for bit; the
     // other lanes repeat lane W-2's address), the filter, then the tiles.
@@ -1423,9 +1507,9 @@ __device__ __forceinline__ void fwd_tc_chunk(const FwdArgs &a, const TcItem &it,
 #pragma unroll
     for (int c = 0; c < kTcTilesFwd; ++c) {
         const int64_t t = it.t0 + c * kTcTile + lane * kTcE;
-        if (t < it.t1) raw[c] = tc_load<NTL>(xr, t, it.t1, ax);
-        else raw[c].v = u32x4_t{0u, 0u, 0u, 0u};
+        raw[c] = lx.load(t, it.t1);
     }
+    const Raw<8> xtail = lx.tail(it.t0 + kTcTilesFwd * kTcTile);
     if (!check.ok()) return;
     float carry[W - 1];  // x_ext of the W-1 tokens before the current tile
 #pragma unroll
@@ -1436,6 +1520,7 @@ __device__ __forceinline__ void fwd_tc_chunk(const FwdArgs &a, const TcItem &it,
         const int64_t tt = it.t0 + c * kTcTile;
         if (tt >= it.t1) break;
         float v[kTcE], xe[W - 1 + kTcE], out[kTcE];
+        lx.fix(raw[c], c + 1 < kTcTilesFwd ? raw[c + 1 < kTcTilesFwd ? c + 1 : c] : xtail);
         unpack<8>(raw[c], v);
 #pragma unroll
         for (int j = 0; j < W - 1; ++j) xe[j] = lane_up(v[kTcE - (W - 1) + j], carry[j]);
@@ -1483,8 +1568,8 @@ __device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it,
     const uint16_t *dyr = static_cast<const uint16_t *>(a.dy.ptr) + it.b * a.dy.s0 + it.d * a.dy.s1;
     uint16_t *dxr = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.dx.ptr)) +
                     it.b * a.dx.s0 + it.d * a.dx.s1;
-    const int ax = A16 ? 16 : tc_align(xr), ady = A16 ? 16 : tc_align(dyr),
-              adx = A16 ? 16 : tc_align(dxr);
+    const int adx = A16 ? 16 : tc_align(dxr);
+    const TcLoads<NTL, A16> lx(xr, a.T), ld(dyr, a.T);
     // Single-token loads first, without branches (as in the forward): the
     // left halo; the right halo (lane j < W-1 reads token t1 + j of x and dy;
     // the other lanes, and tokens past the row, read an in-row token that is
@@ -1508,14 +1593,11 @@ __device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it,
 #pragma unroll
     for (int c = 0; c < kTcTilesBwd; ++c) {
         const int64_t t = it.t0 + c * kTcTile + lane * kTcE;
-        if (t < it.t1) {
-            rx[c] = tc_load<NTL>(xr, t, it.t1, ax);
-            rd[c] = tc_load<NTL>(dyr, t, it.t1, ady);
-        } else {
-            rx[c].v = u32x4_t{0u, 0u, 0u, 0u};
-            rd[c].v = u32x4_t{0u, 0u, 0u, 0u};
-        }
+        rx[c] = lx.load(t, it.t1);
+        rd[c] = ld.load(t, it.t1);
     }
+    const Raw<8> xtail = lx.tail(it.t0 + kTcTilesBwd * kTcTile),
+                 dtail = ld.tail(it.t0 + kTcTilesBwd * kTcTile);
     float w[W][1], bias[1];
     load_filter<W, 1, FK>(a.w, a.w_sd, a.w_sk, a.bias, a.b_s, it.d, w, bias);
     if (!check.ok()) return;
@@ -1565,6 +1647,8 @@ __device__ __forceinline__ void bwd_tc_chunk(const BwdArgs &a, const TcItem &it,
         const int64_t tt = it.t0 + c * kTcTile;
         if (tt >= it.t1) break;
         float v[kTcE], dyv[kTcE], xe[W - 1 + kTcE], g[kTcE];
+        lx.fix(rx[c], c + 1 < kTcTilesBwd ? rx[c + 1 < kTcTilesBwd ? c + 1 : c] : xtail);
+        ld.fix(rd[c], c + 1 < kTcTilesBwd ? rd[c + 1 < kTcTilesBwd ? c + 1 : c] : dtail);
         unpack<8>(rx[c], v);
         unpack<8>(rd[c], dyv);
 #pragma unroll
@@ -1739,7 +1823,8 @@ __device__ __forceinline__ void fwd_tcs_chunk(const FwdArgs &a, const TcItem &it
     const uint16_t *xr = static_cast<const uint16_t *>(a.x.ptr) + it.b * a.x.s0 + it.d * a.x.s1;
     uint16_t *yr = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.y.ptr)) +
                    it.b * a.y.s0 + it.d * a.y.s1;
-    const int ax = A16 ? 16 : tc_align(xr), ay = A16 ? 16 : tc_align(yr);
+    const int ay = A16 ? 16 : tc_align(yr);
+    const TcLoads<NTL, A16> lx(xr, a.T);
     // Left halo (values and ids of the W-1 tokens before the chunk; before
     // the row, zero and kNoId), the filter, then the tiles and their ids.
     uint16_t lh[W - 1];
@@ -1757,10 +1842,10 @@ __device__ __forceinline__ void fwd_tcs_chunk(const FwdArgs &a, const TcItem &it
 #pragma unroll
     for (int c = 0; c < kTcTilesFwd; ++c) {
         const int64_t t = it.t0 + c * kTcTile + lane * kTcE;
-        if (t < it.t1) raw[c] = tc_load<NTL>(xr, t, it.t1, ax);
-        else raw[c].v = u32x4_t{0u, 0u, 0u, 0u};
+        raw[c] = lx.load(t, it.t1);
         ids.lane_ids(t < it.t1 ? t : a.T, tid[c]);
     }
+    const Raw<8> xtail = lx.tail(it.t0 + kTcTilesFwd * kTcTile);
     float carry[W - 1];
 #pragma unroll
     for (int j = 0; j < W - 1; ++j)
@@ -1773,6 +1858,7 @@ __device__ __forceinline__ void fwd_tcs_chunk(const FwdArgs &a, const TcItem &it
         const int64_t t = tt + lane * kTcE;
         float v[kTcE], xe[W - 1 + kTcE], out[kTcE];
         int32_t ie[W - 1 + kTcE];
+        lx.fix(raw[c], c + 1 < kTcTilesFwd ? raw[c + 1 < kTcTilesFwd ? c + 1 : c] : xtail);
         unpack<8>(raw[c], v);
 #pragma unroll
         for (int j = 0; j < W - 1; ++j) {
@@ -1811,8 +1897,8 @@ __device__ __forceinline__ void bwd_tcs_chunk(const BwdArgs &a, const TcItem &it
     const uint16_t *dyr = static_cast<const uint16_t *>(a.dy.ptr) + it.b * a.dy.s0 + it.d * a.dy.s1;
     uint16_t *dxr = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.dx.ptr)) +
                     it.b * a.dx.s0 + it.d * a.dx.s1;
-    const int ax = A16 ? 16 : tc_align(xr), ady = A16 ? 16 : tc_align(dyr),
-              adx = A16 ? 16 : tc_align(dxr);
+    const int adx = A16 ? 16 : tc_align(dxr);
+    const TcLoads<NTL, A16> lx(xr, a.T), ld(dyr, a.T);
     // Single tokens first: the left halo (values, ids); the right halo (lane
     // j < W-1 reads token t1 + j of x and dy, the other lanes and tokens
     // past the row an in-row token that is dropped) and its ids.
@@ -1833,15 +1919,12 @@ __device__ __forceinline__ void bwd_tcs_chunk(const BwdArgs &a, const TcItem &it
 #pragma unroll
     for (int c = 0; c < kTcTilesBwd; ++c) {
         const int64_t t = it.t0 + c * kTcTile + lane * kTcE;
-        if (t < it.t1) {
-            rx[c] = tc_load<NTL>(xr, t, it.t1, ax);
-            rd[c] = tc_load<NTL>(dyr, t, it.t1, ady);
-        } else {
-            rx[c].v = u32x4_t{0u, 0u, 0u, 0u};
-            rd[c].v = u32x4_t{0u, 0u, 0u, 0u};
-        }
+        rx[c] = lx.load(t, it.t1);
+        rd[c] = ld.load(t, it.t1);
         ids.lane_ids(t < it.t1 ? t : a.T, tid[c]);
     }
+    const Raw<8> xtail = lx.tail(it.t0 + kTcTilesBwd * kTcTile),
+                 dtail = ld.tail(it.t0 + kTcTilesBwd * kTcTile);
     const int32_t rh_id = ids.at(it.t1 + lane);  // lane j < W-1: the id of token t1 + j
     float carry[W - 1];
 #pragma unroll
@@ -1890,6 +1973,8 @@ __device__ __forceinline__ void bwd_tcs_chunk(const BwdArgs &a, const TcItem &it
         if (tt >= it.t1) break;
         float v[kTcE], dyv[kTcE], xe[W - 1 + kTcE], g[kTcE];
         int32_t ie[W - 1 + kTcE];
+        lx.fix(rx[c], c + 1 < kTcTilesBwd ? rx[c + 1 < kTcTilesBwd ? c + 1 : c] : xtail);
+        ld.fix(rd[c], c + 1 < kTcTilesBwd ? rd[c + 1 < kTcTilesBwd ? c + 1 : c] : dtail);
         unpack<8>(rx[c], v);
         unpack<8>(rd[c], dyv);
 #pragma unroll
@@ -2083,10 +2168,11 @@ __device__ __forceinline__ void fwd_tcm_chunk(const FwdArgs &a, const TcItem &it
     const uint16_t *xr = static_cast<const uint16_t *>(a.x.ptr) + it.b * a.x.s0 + it.d * a.x.s1;
     uint16_t *yr = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.y.ptr)) +
                    it.b * a.y.s0 + it.d * a.y.s1;
-    const int ax = A16 ? 16 : tc_align(xr), ay = A16 ? 16 : tc_align(yr);
+    const int ay = A16 ? 16 : tc_align(yr);
+    const TcLoads<NTL, A16> lx(xr, a.T);
     uint16_t lh[W - 1];
     float w[W][1], bias[1];
-    Raw<8> raw[kTcTilesFwd];
+    Raw<8> raw[kTcTilesFwd], xtail;
     if (live) {
 #pragma unroll
         for (int j = 0; j < W - 1; ++j) {
@@ -2097,9 +2183,9 @@ __device__ __forceinline__ void fwd_tcm_chunk(const FwdArgs &a, const TcItem &it
 #pragma unroll
         for (int c = 0; c < kTcTilesFwd; ++c) {
             const int64_t t = it.t0 + c * kTcTile + lane * kTcE;
-            if (t < it.t1) raw[c] = tc_load<NTL>(xr, t, it.t1, ax);
-            else raw[c].v = u32x4_t{0u, 0u, 0u, 0u};
+            raw[c] = lx.load(t, it.t1);
         }
+        xtail = lx.tail(it.t0 + kTcTilesFwd * kTcTile);
     }
     tcm_build<W, kTcTilesFwd, false>(it, ids, a.T, s_mask, s_rh);
     if (!live) return;
@@ -2114,6 +2200,7 @@ __device__ __forceinline__ void fwd_tcm_chunk(const FwdArgs &a, const TcItem &it
         const int64_t t = tt + lane * kTcE;
         const uint32_t mc = s_mask[c][lane];
         float v[kTcE], xe[W - 1 + kTcE], out[kTcE];
+        lx.fix(raw[c], c + 1 < kTcTilesFwd ? raw[c + 1 < kTcTilesFwd ? c + 1 : c] : xtail);
         unpack<8>(raw[c], v);
 #pragma unroll
         for (int j = 0; j < W - 1; ++j) xe[j] = lane_up(v[kTcE - (W - 1) + j], carry[j]);
@@ -2147,11 +2234,11 @@ __device__ __forceinline__ void bwd_tcm_chunk(const BwdArgs &a, const TcItem &it
     const uint16_t *dyr = static_cast<const uint16_t *>(a.dy.ptr) + it.b * a.dy.s0 + it.d * a.dy.s1;
     uint16_t *dxr = const_cast<uint16_t *>(static_cast<const uint16_t *>(a.dx.ptr)) +
                     it.b * a.dx.s0 + it.d * a.dx.s1;
-    const int ax = A16 ? 16 : tc_align(xr), ady = A16 ? 16 : tc_align(dyr),
-              adx = A16 ? 16 : tc_align(dxr);
+    const int adx = A16 ? 16 : tc_align(dxr);
+    const TcLoads<NTL, A16> lx(xr, a.T), ld(dyr, a.T);
     uint16_t lh[W - 1], rh_x = 0, rh_dy = 0;
     float w[W][1], bias[1];
-    Raw<8> rx[kTcTilesBwd], rd[kTcTilesBwd];
+    Raw<8> rx[kTcTilesBwd], rd[kTcTilesBwd], xtail, dtail;
     if (live) {
 #pragma unroll
         for (int j = 0; j < W - 1; ++j) {
@@ -2165,14 +2252,11 @@ __device__ __forceinline__ void bwd_tcm_chunk(const BwdArgs &a, const TcItem &it
 #pragma unroll
         for (int c = 0; c < kTcTilesBwd; ++c) {
             const int64_t t = it.t0 + c * kTcTile + lane * kTcE;
-            if (t < it.t1) {
-                rx[c] = tc_load<NTL>(xr, t, it.t1, ax);
-                rd[c] = tc_load<NTL>(dyr, t, it.t1, ady);
-            } else {
-                rx[c].v = u32x4_t{0u, 0u, 0u, 0u};
-                rd[c].v = u32x4_t{0u, 0u, 0u, 0u};
-            }
+            rx[c] = lx.load(t, it.t1);
+            rd[c] = ld.load(t, it.t1);
         }
+        xtail = lx.tail(it.t0 + kTcTilesBwd * kTcTile);
+        dtail = ld.tail(it.t0 + kTcTilesBwd * kTcTile);
     }
     tcm_build<W, kTcTilesBwd, true>(it, ids, a.T, s_mask, s_rh);
     if (!live) return;
@@ -2225,6 +2309,8 @@ __device__ __forceinline__ void bwd_tcm_chunk(const BwdArgs &a, const TcItem &it
         if (tt >= it.t1) break;
         const uint32_t mc = s_mask[c][lane];
         float v[kTcE], dyv[kTcE], xe[W - 1 + kTcE], g[kTcE];
+        lx.fix(rx[c], c + 1 < kTcTilesBwd ? rx[c + 1 < kTcTilesBwd ? c + 1 : c] : xtail);
+        ld.fix(rd[c], c + 1 < kTcTilesBwd ? rd[c + 1 < kTcTilesBwd ? c + 1 : c] : dtail);
         unpack<8>(rx[c], v);
         unpack<8>(rd[c], dyv);
 #pragma unroll
