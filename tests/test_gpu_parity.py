@@ -1007,3 +1007,33 @@ def test_large_magnitudes_saturate_like_the_oracle(layout):
     oyt, ost = oracle.update(f64(xt), f64(state), f64(inp["weight"]), f64(inp["bias"]), "silu")
     check_bf16("update y", yt, oyt)
     check_exact_bf16("conv_state", g_state, ost)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 5, 7])
+def test_time_lanes_sliced_view_rows(k):
+    """x and dy as [B,D,T] views that drop the first k tokens of wider rows:
+    every row, the first included, starts k tokens past a 16-byte boundary
+    and the tokens before it hold data.  Outputs match the oracle on the
+    view alone, so nothing before a row's start is read into it."""
+    B, D, T = 2, 12, 1500
+    gen = torch.Generator().manual_seed(2600 + k)
+    xw = synth.activation_tensor(gen, B, D, T + k, "tc")
+    dyw = synth.activation_tensor(gen, B, D, T + k, "tc")
+    w = synth.weight_tensor(gen, D, 4, dtype=BF16)
+    b = synth.bias_tensor(gen, D, BF16)
+    gx, gdy = dev(xw)[:, :, k:], dev(dyw)[:, :, k:]
+    assert gx.stride() == (D * (T + k), T + k, 1)
+    y = guarded_act(B, D, T, "tc", DEV, aligned=False)
+    ops.fwd(gx, dev(w), dev(b), None, None, "silu", y=y.view)
+    dx = guarded_act(B, D, T, "tc", DEV, aligned=False)
+    _, dw, db, _ = ops.bwd(gx, dev(w), gdy, dev(b), None, None, None, "silu", False, False,
+                           dx=dx.view)
+    torch.cuda.synchronize()
+    x, dy = f64(xw)[:, :, k:], f64(dyw)[:, :, k:]
+    oy, _ = oracle.fwd(x, f64(w), f64(b), None, None, "silu", False)
+    odx, odw, odb, _ = oracle.bwd(x, f64(w), dy, f64(b), None, None, None, "silu")
+    check_bf16("y", y.view, oy)
+    check_bf16("dx", dx.view, odx)
+    check_f32_rel("dweight", dw, odw)
+    check_f32_rel("dbias", db, odb)
+    assert y.intact() and dx.intact()
